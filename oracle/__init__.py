@@ -1,0 +1,255 @@
+"""Plain fp64 CPU oracle for the SambaY cross-decoder step (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may use this package; the product library never does.  It
+shares no code with the HIP path.  The arithmetic lives in ``oracle.c``
+(plain double-precision loops, one function per definition on the pages);
+this module only builds it with gcc, marshals numpy/torch CPU arrays and
+returns float64 numpy arrays.
+
+Accepted input arrays: numpy float64 / float32, numpy uint16 holding raw
+bfloat16 bit patterns, or CPU torch tensors of dtype float64 / float32 /
+bfloat16.  bfloat16 and float32 values are widened exactly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F64, F32, BF16 = 0, 1, 2
+CATEGORIES = ("kv_cache", "state_in", "state_out", "weights")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so next to it (gcc, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+    lib.oracle_gmu.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i64, i64, i64, vp]
+    lib.oracle_gmu.restype = ctypes.c_int
+    lib.oracle_xattn.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i64, i64, i64, i64, i64, dbl, vp]
+    lib.oracle_xattn.restype = ctypes.c_int
+    lib.oracle_xattn_chunked.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i64, i64, i64, i64, i64, dbl,
+                                         i64]
+    lib.oracle_xattn_chunked.restype = ctypes.c_int
+    lib.oracle_crossdecoder.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i32,
+                                        i64, i64, i64, i64, i64, i64, i64, dbl, ctypes.c_int, vp, vp]
+    lib.oracle_crossdecoder.restype = ctypes.c_int
+    lib.oracle_round_bf16.argtypes = [dbl]
+    lib.oracle_round_bf16.restype = dbl
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def _as_input(a):
+    """Return (contiguous numpy array, dtype code) for an accepted input."""
+    if not isinstance(a, np.ndarray):
+        import torch  # only for CPU tensors handed in by the tests / bench
+
+        if not isinstance(a, torch.Tensor):
+            a = np.asarray(a, dtype=np.float64)
+        else:
+            t = a.detach()
+            if t.device.type != "cpu":
+                raise ValueError("oracle inputs must be CPU arrays")
+            t = t.contiguous()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view(np.uint16), BF16
+            if t.dtype == torch.float32:
+                return t.numpy(), F32
+            if t.dtype == torch.float64:
+                return t.numpy(), F64
+            raise TypeError("unsupported oracle input dtype %s" % t.dtype)
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float64:
+        return a, F64
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint16:
+        return a, BF16
+    raise TypeError("unsupported oracle input dtype %s" % a.dtype)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc == -1:
+        raise ValueError("oracle %s: invalid arguments" % what)
+    if rc != 0:
+        raise MemoryError("oracle %s: allocation failed (%d)" % (what, rc))
+
+
+def _bytes_dict(arr):
+    return {c: int(arr[i]) for i, c in enumerate(CATEGORIES)}
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round each value of x (float64) to the nearest bfloat16, ties to even."""
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    flat_in, flat_out = x.reshape(-1), out.reshape(-1)
+    for i in range(flat_in.size):
+        flat_out[i] = lib.oracle_round_bf16(float(flat_in[i]))
+    return out
+
+
+def gmu(M, X, W1, W2, count_bytes: bool = False):
+    """Y = (M ⊙ SiLU(X W1^T)) W2^T in fp64.  M [rows, d_inner], X [rows, d_model],
+    W1 [d_inner, d_model], W2 [d_model, d_inner].  M and X share a dtype."""
+    lib = _load()
+    m, dm = _as_input(M)
+    x, dx = _as_input(X)
+    w1, dw1 = _as_input(W1)
+    w2, dw2 = _as_input(W2)
+    if dm != dx or dw1 != dw2:
+        raise TypeError("M/X and W1/W2 must share dtypes")
+    rows, d_model = x.shape
+    d_inner = w1.shape[0]
+    if m.shape != (rows, d_inner) or w1.shape != (d_inner, d_model) or w2.shape != (d_model, d_inner):
+        raise ValueError("gmu shape mismatch")
+    y = np.empty((rows, d_model), dtype=np.float64)
+    nb = np.zeros(4, dtype=np.int64)
+    rc = lib.oracle_gmu(_ptr(m), _ptr(x), dm, _ptr(w1), _ptr(w2), dw1, _ptr(y), rows, d_model, d_inner,
+                        _ptr(nb) if count_bytes else None)
+    _check(rc, "gmu")
+    return (y, _bytes_dict(nb)) if count_bytes else y
+
+
+def _xattn_shapes(q, k, v):
+    B, Hq, D = q.shape
+    B2, Hkv, L, D2 = k.shape
+    if v.shape != k.shape or B2 != B or D2 != D:
+        raise ValueError("xattn shape mismatch")
+    return B, Hq, Hkv, D, L
+
+
+def xattn(q, K, V, scale: float | None = None, count_bytes: bool = False):
+    """out[B, Hq, D] = softmax(scale q K^T) V over all L positions; K, V [B, Hkv, L, D]."""
+    lib = _load()
+    qa, dq = _as_input(q)
+    ka, dk = _as_input(K)
+    va, dv = _as_input(V)
+    if dk != dv:
+        raise TypeError("K and V must share a dtype")
+    B, Hq, Hkv, D, L = _xattn_shapes(qa, ka, va)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    nb = np.zeros(4, dtype=np.int64)
+    rc = lib.oracle_xattn(_ptr(qa), dq, _ptr(ka), _ptr(va), dk, _ptr(out), B, Hq, Hkv, D, L, float(scale),
+                          _ptr(nb) if count_bytes else None)
+    _check(rc, "xattn")
+    return (out, _bytes_dict(nb)) if count_bytes else out
+
+
+def xattn_chunked(q, K, V, S: int, scale: float | None = None):
+    """The same attention as S key chunks merged by log-sum-exp."""
+    lib = _load()
+    qa, dq = _as_input(q)
+    ka, dk = _as_input(K)
+    va, dv = _as_input(V)
+    B, Hq, Hkv, D, L = _xattn_shapes(qa, ka, va)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    rc = lib.oracle_xattn_chunked(_ptr(qa), dq, _ptr(ka), _ptr(va), dk, _ptr(out), B, Hq, Hkv, D, L, float(scale),
+                                  int(S))
+    _check(rc, "xattn_chunked")
+    return out
+
+
+XATTN, GMU = 0, 1
+
+
+def crossdecoder(h, M, K, V, layers: Sequence, Hq: int, scale: float | None = None, round_bf16: bool = True,
+                 count_bytes: bool = False):
+    """One cross-decoder decode step.  layers: sequence of (kind, w_a, w_b) with
+    kind "xattn" (w_a = Wq, w_b = Wo, [d_model, d_model]) or "gmu"
+    (w_a = W1 [d_inner, d_model], w_b = W2 [d_model, d_inner]).
+    h [B, d_model], M [B, d_inner], K, V [B, Hkv, L, D]; Hq·D == d_model.
+    Returns the final h (float64) and, with count_bytes, a per-layer list of
+    byte dicts."""
+    lib = _load()
+    ha, dh = _as_input(h)
+    ma, dm = _as_input(M)
+    ka, dk = _as_input(K)
+    va, dv = _as_input(V)
+    if dh != dm or dk != dv:
+        raise TypeError("h/M and K/V must share dtypes")
+    B, d_model = ha.shape
+    d_inner = ma.shape[1]
+    B2, Hkv, L, D = ka.shape
+    if B2 != B or ma.shape[0] != B or va.shape != ka.shape or Hq * D != d_model:
+        raise ValueError("crossdecoder shape mismatch")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    n = len(layers)
+    kinds = np.zeros(max(n, 1), dtype=np.int32)
+    keep, wa_p, wb_p = [], (ctypes.c_void_p * max(n, 1))(), (ctypes.c_void_p * max(n, 1))()
+    dw = None
+    for i, (kind, wa, wb) in enumerate(layers):
+        if kind not in ("xattn", "gmu"):
+            raise ValueError("layer kind must be 'xattn' or 'gmu'")
+        kinds[i] = XATTN if kind == "xattn" else GMU
+        a, da = _as_input(wa)
+        b, db = _as_input(wb)
+        if dw is None:
+            dw = da
+        if da != dw or db != dw:
+            raise TypeError("all layer weights must share a dtype")
+        if kind == "xattn":
+            ok = a.shape == (d_model, d_model) and b.shape == (d_model, d_model)
+        else:
+            ok = a.shape == (d_inner, d_model) and b.shape == (d_model, d_inner)
+        if not ok:
+            raise ValueError("layer %d weight shape mismatch" % i)
+        keep += [a, b]
+        wa_p[i] = a.ctypes.data
+        wb_p[i] = b.ctypes.data
+    out = np.empty((B, d_model), dtype=np.float64)
+    nb = np.zeros((max(n, 1), 4), dtype=np.int64)
+    rc = lib.oracle_crossdecoder(_ptr(ha), _ptr(ma), dh, _ptr(ka), _ptr(va), dk, _ptr(kinds),
+                                 ctypes.cast(wa_p, ctypes.c_void_p), ctypes.cast(wb_p, ctypes.c_void_p),
+                                 dw if dw is not None else F64, n, B, d_model, d_inner, Hq, Hkv, D, L, float(scale),
+                                 1 if round_bf16 else 0, _ptr(out), _ptr(nb) if count_bytes else None)
+    _check(rc, "crossdecoder")
+    if count_bytes:
+        return out, [_bytes_dict(nb[i]) for i in range(n)]
+    return out

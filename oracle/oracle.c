@@ -1,0 +1,484 @@
+/*
+ * Plain fp64 CPU oracle for the SambaY cross-decoder step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker, not the product: only
+ * the tests, the smoke check and the benchmark's CPU-baseline leg may load it.
+ * It shares no source, header, table or helper with the HIP library under
+ * attention_decoding_amd/csrc, and it never touches a GPU.
+ *
+ * Every function below is the plain definition of what the method computes,
+ * written out as loops in double precision, in the order the pages state it.
+ * OpenMP splits only independent rows / (batch, head) pairs; no blocking,
+ * fusion or reordering of any single result's arithmetic.
+ *
+ * Sources (all are web pages about the paper "Decoder-Hybrid-Decoder
+ * Architecture for Efficient Reasoning with Long Generation"):
+ *   [Notes]    Paper-Notes reading notes page with that title; sections
+ *              "关键设计" (key designs: the GMU equation and the 3-D mixing
+ *              lift), "整体框架" (overall framework: self-/cross-decoder,
+ *              single KV cache, GMU/cross-attention alternation),
+ *              "现有痛点" (pain point: O(d_kv·N) decode I/O of cross-attention),
+ *              "关键发现" (findings: NoPE).
+ *   [Abstract] the authors' abstract (chatpaper.ai and fugumt.com pages).
+ *
+ * Inputs may be fp64, fp32 or bf16 (raw 16-bit patterns); bf16 and fp32 are
+ * widened exactly to fp64 before use.  Outputs are fp64.
+ *
+ * Byte-count mode: when a `bytes` array is passed, the call runs on one
+ * thread and records every distinct element it reads from each input tensor
+ * and writes to each output tensor; the sums (element count x nominal element
+ * size) are returned per category.  This makes the I/O claim of [Notes]
+ * "现有痛点"/"关键设计" (cross-attention decode reads O(d_kv·N); a GMU decode
+ * step reads state whose size does not depend on N) checkable by counting.
+ *
+ * Parity pins (the tests under tests/test_oracle_*.py): GMU against the
+ * brute-force 3-D mixing identity, closed forms and special cases; attention
+ * against torch's fp64 scaled_dot_product_attention, a brute-force two-pass
+ * softmax, closed forms and invariances; byte counts against the analytic
+ * formulas.  See the test files for which mistake each pin catches.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F64 = 0, OR_F32 = 1, OR_BF16 = 2 };
+enum { OR_CAT_KV = 0, OR_CAT_STATE_IN = 1, OR_CAT_STATE_OUT = 2, OR_CAT_WEIGHT = 3, OR_NCAT = 4 };
+
+/* ------------------------------------------------------------------ loads */
+
+static double widen(const void *p, int dt, int64_t i) {
+    if (dt == OR_F64) return ((const double *)p)[i];
+    if (dt == OR_F32) return (double)((const float *)p)[i];
+    /* bf16: the 16 stored bits are the top half of an IEEE binary32. */
+    uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int dt_bytes(int dt) { return dt == OR_F64 ? 8 : dt == OR_F32 ? 4 : 2; }
+
+/* --------------------------------------------------------------- tracking */
+
+typedef struct {
+    unsigned char *seen;
+    int64_t n;
+    int elem_bytes;
+    int cat;
+} trk_tensor;
+
+typedef struct {
+    trk_tensor t[8];
+} tracker;
+
+static int trk_add(tracker *tr, int slot, int64_t n, int elem_bytes, int cat) {
+    if (!tr) return 0;
+    tr->t[slot].seen = (unsigned char *)calloc((size_t)(n > 0 ? n : 1), 1);
+    tr->t[slot].n = n;
+    tr->t[slot].elem_bytes = elem_bytes;
+    tr->t[slot].cat = cat;
+    return tr->t[slot].seen ? 0 : -2;
+}
+
+static inline void trk_mark(tracker *tr, int slot, int64_t i) {
+    if (tr && tr->t[slot].seen) tr->t[slot].seen[i] = 1;
+}
+
+/* Adds the distinct-element byte sums into bytes[cat] and frees the maps. */
+static void trk_finish(tracker *tr, int64_t *bytes) {
+    if (!tr) return;
+    for (int s = 0; s < 8; ++s) {
+        if (!tr->t[s].seen) continue;
+        int64_t c = 0;
+        for (int64_t i = 0; i < tr->t[s].n; ++i) c += tr->t[s].seen[i];
+        if (bytes) bytes[tr->t[s].cat] += c * tr->t[s].elem_bytes;
+        free(tr->t[s].seen);
+        tr->t[s].seen = NULL;
+    }
+}
+
+/* ------------------------------------------------------------ bf16 round */
+
+/* Round a double to the nearest bfloat16 value, ties to even, directly (no
+ * detour through binary32, which could round twice).  bfloat16 keeps 8
+ * significant bits and binary32's exponent range. */
+double oracle_round_bf16(double x) {
+    if (!isfinite(x) || x == 0.0) return x;
+    int e;
+    (void)frexp(x, &e);          /* |x| = m * 2^e with 0.5 <= m < 1 */
+    int q = e - 8;               /* weight of the last kept bit */
+    if (q < -133) q = -133;      /* below the normal range: fixed quantum 2^-133 */
+    double r = nearbyint(ldexp(x, -q));  /* default mode: nearest, ties to even */
+    double y = ldexp(r, q);
+    if (fabs(y) > 3.3895313892515355e38) return copysign(INFINITY, x);
+    return y;
+}
+
+/* ------------------------------------------------------------------ GMU */
+
+/* One row of the Gated Memory Unit, [Notes] "关键设计":
+ *   Y = (M ⊙ SiLU(X W1^T)) W2, where SiLU(z) = z·sigmoid(z) = z / (1 + e^{-z}).
+ * Weights are stored as linear-layer matrices, W1 [d_inner, d_model] and
+ * W2 [d_model, d_inner], so the output projection is H · W2^T (the same
+ * linear map as the page's "H W2" with W2 stored transposed).  No bias. */
+static void gmu_row(const void *M, int dt_m, const void *X, int dt_x, const void *W1, const void *W2,
+                    int dt_w, double *y, int64_t r, int64_t d_model, int64_t d_inner, double *H,
+                    tracker *tr, int sM, int sX, int sW1, int sW2) {
+    for (int64_t k = 0; k < d_inner; ++k) {
+        double z = 0.0;                                  /* z = X[r,:] · W1[k,:] */
+        for (int64_t c = 0; c < d_model; ++c) {
+            trk_mark(tr, sX, r * d_model + c);
+            trk_mark(tr, sW1, k * d_model + c);
+            z += widen(X, dt_x, r * d_model + c) * widen(W1, dt_w, k * d_model + c);
+        }
+        double g = z / (1.0 + exp(-z));                  /* SiLU(z) */
+        trk_mark(tr, sM, r * d_inner + k);
+        H[k] = widen(M, dt_m, r * d_inner + k) * g;      /* memory gated channel-wise */
+    }
+    for (int64_t o = 0; o < d_model; ++o) {
+        double acc = 0.0;                                /* Y[r,o] = H · W2[o,:] */
+        for (int64_t k = 0; k < d_inner; ++k) {
+            trk_mark(tr, sW2, o * d_inner + k);
+            acc += H[k] * widen(W2, dt_w, o * d_inner + k);
+        }
+        y[o] = acc;
+    }
+}
+
+/* Y[rows, d_model] = (M[rows, d_inner] ⊙ SiLU(X[rows, d_model] W1^T)) W2^T.
+ * dt_act is the dtype of M and X, dt_w of W1 and W2.
+ * bytes (nullable, 4 entries, accumulated): distinct bytes per category. */
+int oracle_gmu(const void *M, const void *X, int dt_act, const void *W1, const void *W2, int dt_w,
+               double *Y, int64_t rows, int64_t d_model, int64_t d_inner, int64_t *bytes) {
+    if (!M || !X || !W1 || !W2 || !Y || rows < 0 || d_model <= 0 || d_inner <= 0) return -1;
+    tracker trs, *tr = NULL;
+    if (bytes) {
+        memset(&trs, 0, sizeof trs);
+        tr = &trs;
+        int ab = dt_bytes(dt_act), wb = dt_bytes(dt_w);
+        if (trk_add(tr, 0, rows * d_inner, ab, OR_CAT_STATE_IN) || trk_add(tr, 1, rows * d_model, ab, OR_CAT_STATE_IN) ||
+            trk_add(tr, 2, d_inner * d_model, wb, OR_CAT_WEIGHT) || trk_add(tr, 3, d_model * d_inner, wb, OR_CAT_WEIGHT) ||
+            trk_add(tr, 4, rows * d_model, ab, OR_CAT_STATE_OUT)) {
+            trk_finish(tr, NULL);
+            return -2;
+        }
+    }
+    int fail = 0;
+#pragma omp parallel if (!tr)
+    {
+        double *H = (double *)malloc((size_t)d_inner * sizeof(double));
+        if (!H) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < rows; ++r) {
+            if (!H) continue;
+            gmu_row(M, dt_act, X, dt_act, W1, W2, dt_w, Y + r * d_model, r, d_model, d_inner, H, tr, 0, 1, 2, 3);
+            for (int64_t o = 0; o < d_model; ++o) trk_mark(tr, 4, r * d_model + o);
+        }
+        free(H);
+    }
+    trk_finish(tr, bytes);
+    return fail ? -2 : 0;
+}
+
+/* ------------------------------------------------------ cross-attention */
+
+/* Decode-time softmax attention of one query head over all L cached
+ * positions of the single shared KV cache ([Notes] "整体框架": the
+ * self-decoder's final full-attention layer writes one KV cache that every
+ * cross-attention layer reuses).  No positional encoding is applied ([Notes]
+ * "关键发现", [Abstract]: no explicit positional encoding).  Grouped-query
+ * layout: query head h reads KV head h / (Hq / Hkv).
+ *   s_j = scale · q·k_j,  m = max_j s_j,  w_j = e^{s_j - m},
+ *   out = Σ_j w_j v_j / Σ_j w_j.                                        */
+static void xattn_head(const void *q, int dt_q, int64_t q_off, const void *K, const void *V, int dt_kv,
+                       int64_t kv_off, double *out, int64_t D, int64_t L, double scale, double *s,
+                       tracker *tr, int sQ, int sK, int sV) {
+    double m = -INFINITY;
+    for (int64_t j = 0; j < L; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            trk_mark(tr, sQ, q_off + d);
+            trk_mark(tr, sK, kv_off + j * D + d);
+            dot += widen(q, dt_q, q_off + d) * widen(K, dt_kv, kv_off + j * D + d);
+        }
+        s[j] = dot * scale;
+        if (s[j] > m) m = s[j];
+    }
+    double den = 0.0;
+    for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+    for (int64_t j = 0; j < L; ++j) {
+        double w = exp(s[j] - m);
+        den += w;
+        for (int64_t d = 0; d < D; ++d) {
+            trk_mark(tr, sV, kv_off + j * D + d);
+            out[d] += w * widen(V, dt_kv, kv_off + j * D + d);
+        }
+    }
+    for (int64_t d = 0; d < D; ++d) out[d] /= den;
+}
+
+static int xattn_args_ok(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L) {
+    return B >= 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && D > 0 && L > 0;
+}
+
+/* out[B, Hq, D] = softmax(scale · q K^T) V with q [B, Hq, D], K, V [B, Hkv, L, D].
+ * bytes (nullable, 4 entries, accumulated). */
+int oracle_xattn(const void *q, int dt_q, const void *K, const void *V, int dt_kv, double *out, int64_t B,
+                 int64_t Hq, int64_t Hkv, int64_t D, int64_t L, double scale, int64_t *bytes) {
+    if (!q || !K || !V || !out || !xattn_args_ok(B, Hq, Hkv, D, L)) return -1;
+    const int64_t G = Hq / Hkv;
+    tracker trs, *tr = NULL;
+    if (bytes) {
+        memset(&trs, 0, sizeof trs);
+        tr = &trs;
+        int qb = dt_bytes(dt_q), kb = dt_bytes(dt_kv);
+        if (trk_add(tr, 0, B * Hq * D, qb, OR_CAT_STATE_IN) || trk_add(tr, 1, B * Hkv * L * D, kb, OR_CAT_KV) ||
+            trk_add(tr, 2, B * Hkv * L * D, kb, OR_CAT_KV) || trk_add(tr, 3, B * Hq * D, qb, OR_CAT_STATE_OUT)) {
+            trk_finish(tr, NULL);
+            return -2;
+        }
+    }
+    int fail = 0;
+#pragma omp parallel if (!tr)
+    {
+        double *s = (double *)malloc((size_t)L * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * Hq; ++bh) {
+            if (!s) continue;
+            int64_t b = bh / Hq, h = bh % Hq, g = h / G;
+            xattn_head(q, dt_q, bh * D, K, V, dt_kv, (b * Hkv + g) * L * D, out + bh * D, D, L, scale, s, tr, 0, 1, 2);
+            for (int64_t d = 0; d < D; ++d) trk_mark(tr, 3, bh * D + d);
+        }
+        free(s);
+    }
+    trk_finish(tr, bytes);
+    return fail ? -2 : 0;
+}
+
+/* The same attention computed as S independent chunks of keys, each reduced
+ * to (m_c, l_c, o_c) = (max s, Σ e^{s-m_c}, Σ e^{s-m_c} v), then merged:
+ *   m = max_c m_c,  l = Σ_c l_c e^{m_c - m},  out = Σ_c o_c e^{m_c - m} / l.
+ * This is an exact rewriting of the softmax (split-K flash decoding); the
+ * pins check it against oracle_xattn.  Chunk c covers keys
+ * [c·ceil(L/S), min(L, (c+1)·ceil(L/S))); empty chunks are skipped. */
+int oracle_xattn_chunked(const void *q, int dt_q, const void *K, const void *V, int dt_kv, double *out,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L, double scale, int64_t S) {
+    if (!q || !K || !V || !out || !xattn_args_ok(B, Hq, Hkv, D, L) || S <= 0) return -1;
+    const int64_t G = Hq / Hkv, chunk = (L + S - 1) / S;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *mc = (double *)malloc((size_t)S * sizeof(double));
+        double *lc = (double *)malloc((size_t)S * sizeof(double));
+        double *oc = (double *)malloc((size_t)(S * D) * sizeof(double));
+        double *sv = (double *)malloc((size_t)(chunk > 0 ? chunk : 1) * sizeof(double));
+        int ok = mc && lc && oc && sv;
+        if (!ok) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * Hq; ++bh) {
+            if (!ok) continue;
+            int64_t b = bh / Hq, h = bh % Hq, g = h / G;
+            int64_t kv = (b * Hkv + g) * L * D;
+            int64_t nc = 0;
+            for (int64_t c = 0; c < S; ++c) {
+                int64_t j0 = c * chunk, j1 = j0 + chunk < L ? j0 + chunk : L;
+                if (j0 >= j1) continue;
+                double m = -INFINITY;
+                for (int64_t j = j0; j < j1; ++j) {
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += widen(q, dt_q, bh * D + d) * widen(K, dt_kv, kv + j * D + d);
+                    sv[j - j0] = dot * scale;
+                    if (sv[j - j0] > m) m = sv[j - j0];
+                }
+                double l = 0.0;
+                for (int64_t d = 0; d < D; ++d) oc[nc * D + d] = 0.0;
+                for (int64_t j = j0; j < j1; ++j) {
+                    double w = exp(sv[j - j0] - m);
+                    l += w;
+                    for (int64_t d = 0; d < D; ++d) oc[nc * D + d] += w * widen(V, dt_kv, kv + j * D + d);
+                }
+                mc[nc] = m;
+                lc[nc] = l;
+                ++nc;
+            }
+            double M = -INFINITY;
+            for (int64_t c = 0; c < nc; ++c) M = mc[c] > M ? mc[c] : M;
+            double l = 0.0;
+            for (int64_t c = 0; c < nc; ++c) l += lc[c] * exp(mc[c] - M);
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < nc; ++c) acc += oc[c * D + d] * exp(mc[c] - M);
+                out[bh * D + d] = acc / l;
+            }
+        }
+        free(mc);
+        free(lc);
+        free(oc);
+        free(sv);
+    }
+    return fail ? -2 : 0;
+}
+
+/* --------------------------------------------------------- cross-decoder */
+
+/* One decode step of the cross-decoder ([Notes] "整体框架": the second half
+ * of the layers alternates cross-attention over the single shared KV cache
+ * and GMUs that reuse the memory readout M of the self-decoder's last SSM
+ * layer).  Every layer is a residual branch:
+ *   cross-attention layer (weights Wq, Wo, each [d_model, d_model]):
+ *       q = h Wq^T (kept exact, viewed as [B, Hq, D]);  o = attention(q, K, V);
+ *       h = h + o Wo^T
+ *   GMU layer (weights W1 [d_inner, d_model], W2 [d_model, d_inner]):
+ *       h = h + GMU(M, h, W1, W2)
+ * When round_bf16 is set, h is rounded to bfloat16 after every residual add
+ * (the bf16 residual stream); nothing else is rounded.
+ * kinds[l]: 0 = cross-attention, 1 = GMU.  wa[l]/wb[l]: (Wq, Wo) or (W1, W2),
+ * all of dtype dt_w.  h0, M of dtype dt_act; K, V of dtype dt_kv.
+ * h_out [B, d_model] receives the final residual stream.
+ * bytes (nullable, n_layers x 4 entries, accumulated) counts each layer's
+ * distinct bytes with h and M counted at dt_act's size. */
+int oracle_crossdecoder(const void *h0, const void *M, int dt_act, const void *K, const void *V, int dt_kv,
+                        const int32_t *kinds, const void *const *wa, const void *const *wb, int dt_w, int32_t n_layers,
+                        int64_t B, int64_t d_model, int64_t d_inner, int64_t Hq, int64_t Hkv, int64_t D, int64_t L,
+                        double scale, int round_bf16, double *h_out, int64_t *bytes) {
+    if (!h0 || !M || !K || !V || !kinds || !wa || !wb || !h_out || n_layers < 0 || B < 0 || d_model <= 0 ||
+        d_inner <= 0 || !xattn_args_ok(B, Hq, Hkv, D, L) || Hq * D != d_model)
+        return -1;
+    const int64_t G = Hq / Hkv;
+    const int ab = dt_bytes(dt_act), wbyt = dt_bytes(dt_w), kb = dt_bytes(dt_kv);
+    double *h = (double *)malloc((size_t)(B * d_model) * sizeof(double));
+    double *y = (double *)malloc((size_t)(B * d_model) * sizeof(double));
+    double *qv = (double *)malloc((size_t)(B * d_model) * sizeof(double));
+    double *o = (double *)malloc((size_t)(B * d_model) * sizeof(double));
+    if (!h || !y || !qv || !o) {
+        free(h); free(y); free(qv); free(o);
+        return -2;
+    }
+    for (int64_t i = 0; i < B * d_model; ++i) h[i] = widen(h0, dt_act, i);
+    int fail = 0;
+    for (int32_t li = 0; li < n_layers && !fail; ++li) {
+        if (!wa[li] || !wb[li] || (kinds[li] != 0 && kinds[li] != 1)) {
+            fail = -1;
+            break;
+        }
+        tracker trs, *tr = NULL;
+        if (bytes) {
+            memset(&trs, 0, sizeof trs);
+            tr = &trs;
+            int e = trk_add(tr, 0, B * d_model, ab, OR_CAT_STATE_IN) | trk_add(tr, 1, B * d_model, ab, OR_CAT_STATE_OUT);
+            if (kinds[li] == 0)
+                e |= trk_add(tr, 2, d_model * d_model, wbyt, OR_CAT_WEIGHT) |
+                     trk_add(tr, 3, d_model * d_model, wbyt, OR_CAT_WEIGHT) |
+                     trk_add(tr, 4, B * Hkv * L * D, kb, OR_CAT_KV) | trk_add(tr, 5, B * Hkv * L * D, kb, OR_CAT_KV);
+            else
+                e |= trk_add(tr, 2, d_inner * d_model, wbyt, OR_CAT_WEIGHT) |
+                     trk_add(tr, 3, d_model * d_inner, wbyt, OR_CAT_WEIGHT) |
+                     trk_add(tr, 4, B * d_inner, ab, OR_CAT_STATE_IN);
+            if (e) {
+                trk_finish(tr, NULL);
+                fail = -2;
+                break;
+            }
+        }
+        if (kinds[li] == 0) {
+            /* q = h Wq^T, exact */
+#pragma omp parallel for schedule(static) if (!tr)
+            for (int64_t i = 0; i < B * d_model; ++i) {
+                int64_t b = i / d_model, n = i % d_model;
+                double acc = 0.0;
+                for (int64_t c = 0; c < d_model; ++c) {
+                    trk_mark(tr, 0, b * d_model + c);
+                    trk_mark(tr, 2, n * d_model + c);
+                    acc += h[b * d_model + c] * widen(wa[li], dt_w, n * d_model + c);
+                }
+                qv[i] = acc;
+            }
+            /* o = attention(q) over the shared cache */
+#pragma omp parallel if (!tr)
+            {
+                double *s = (double *)malloc((size_t)L * sizeof(double));
+                if (!s) {
+#pragma omp atomic write
+                    fail = -2;
+                }
+#pragma omp for schedule(dynamic, 1)
+                for (int64_t bh = 0; bh < B * Hq; ++bh) {
+                    if (!s) continue;
+                    int64_t b = bh / Hq, hh = bh % Hq, g = hh / G;
+                    xattn_head(qv, OR_F64, bh * D, K, V, dt_kv, (b * Hkv + g) * L * D, o + bh * D, D, L, scale, s,
+                               tr, 7, 4, 5);
+                }
+                free(s);
+            }
+            /* y = o Wo^T */
+#pragma omp parallel for schedule(static) if (!tr)
+            for (int64_t i = 0; i < B * d_model; ++i) {
+                int64_t b = i / d_model, n = i % d_model;
+                double acc = 0.0;
+                for (int64_t c = 0; c < d_model; ++c) {
+                    trk_mark(tr, 3, n * d_model + c);
+                    acc += o[b * d_model + c] * widen(wb[li], dt_w, n * d_model + c);
+                }
+                y[i] = acc;
+            }
+        } else {
+#pragma omp parallel if (!tr)
+            {
+                double *H = (double *)malloc((size_t)d_inner * sizeof(double));
+                if (!H) {
+#pragma omp atomic write
+                    fail = -2;
+                }
+#pragma omp for schedule(static)
+                for (int64_t r = 0; r < B; ++r) {
+                    if (!H) continue;
+                    gmu_row(M, dt_act, h, OR_F64, wa[li], wb[li], dt_w, y + r * d_model, r, d_model, d_inner, H, tr,
+                            4, 0, 2, 3);
+                }
+                free(H);
+            }
+        }
+        for (int64_t i = 0; i < B * d_model; ++i) {
+            trk_mark(tr, 0, i);
+            trk_mark(tr, 1, i);
+            double v = h[i] + y[i];
+            h[i] = round_bf16 ? oracle_round_bf16(v) : v;
+        }
+        trk_finish(tr, bytes ? bytes + (int64_t)li * OR_NCAT : NULL);
+    }
+    if (!fail) memcpy(h_out, h, (size_t)(B * d_model) * sizeof(double));
+    free(h); free(y); free(qv); free(o);
+    return fail;
+}
+
+/* --------------------------------------------------------------- threads */
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -1,0 +1,163 @@
+"""Seeded synthetic inputs for the SambaY cross-decoder step.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic (no GMU, no attention), so both the HIP path and the
+oracle can be fed from it.  Every tensor is drawn in float32 from its own
+seeded ``torch.Generator`` on the requested device and then rounded to the
+storage dtype (bfloat16: round-to-nearest-even).  The same seed on the same
+device type gives the same values.
+
+The shapes follow the pages' long-generation workload (2K-token prompt plus
+32K generated tokens, so a 34816-position shared KV cache) and the model
+widths below.  Values: activations and the KV cache ~ N(0, 1), weights
+~ N(0, 0.02^2).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+SEED_BASE = 20250716
+
+# ----------------------------------------------------------------- workloads
+
+TINY_GMU = dict(rows=64, d_model=64, d_inner=128)                       # fp32
+GMU_PREFILL = dict(batch=4, seq=2048, d_model=2560, d_inner=5120)        # bf16
+GMU_DECODE = dict(batches=(1, 8, 32, 64), d_model=3072, d_inner=6144)    # bf16
+XATTN_DECODE = dict(B=16, Hq=24, Hkv=8, D=128, L=34816)                  # bf16
+CROSSDECODER = dict(B=32, d_model=3072, d_inner=6144, Hq=24, Hkv=8, D=128, L=34816, n_layers=16)  # bf16
+WEIGHT_STD = 0.02
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(int(seed) & 0x7FFFFFFFFFFFFFFF)
+    return g
+
+
+def _seed(cfg: int, tensor: int, extra: int = 0) -> int:
+    return SEED_BASE + cfg + 1_000_003 * tensor + 7_919 * extra
+
+
+def normal(shape, *, std: float = 1.0, seed: int, device="cpu", dtype=torch.bfloat16) -> torch.Tensor:
+    """float32 N(0, std^2) draws from a generator seeded with `seed`, rounded to dtype."""
+    x = torch.randn(tuple(shape), generator=_gen(device, seed), device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x if dtype == torch.float32 else x.to(dtype)
+
+
+# ------------------------------------------------------------ tiny GMU (fp32)
+
+@dataclass
+class TinyGMU:
+    X: torch.Tensor    # [T, d_model] fp32
+    V: torch.Tensor    # [T, d_inner] fp32, token values mixed by A
+    A: torch.Tensor    # [T, T] float64, causal row-stochastic mixing matrix
+    M: torch.Tensor    # [T, d_inner] fp32, M = A·V rounded to fp32
+    W1: torch.Tensor   # [d_inner, d_model] fp32
+    W2: torch.Tensor   # [d_model, d_inner] fp32
+
+
+def tiny_gmu(seed: int = 0, rows: int = 64, d_model: int = 64, d_inner: int = 128) -> TinyGMU:
+    """The small fp32 GMU case: an explicit causal (lower-triangular) mixing
+    matrix A whose rows are softmax-normalised N(0,1) logits over j <= i, token
+    values V ~ N(0,1), and the memory M = A·V that a token-mixing layer would
+    produce; X ~ N(0,1); W1, W2 ~ N(0, 0.02^2).  CPU tensors."""
+    s = SEED_BASE + 1000 * seed
+    X = normal((rows, d_model), seed=s + 1, dtype=torch.float32)
+    V = normal((rows, d_inner), seed=s + 2, dtype=torch.float32)
+    logits = normal((rows, rows), seed=s + 3, dtype=torch.float32).double()
+    causal = torch.ones(rows, rows, dtype=torch.bool).tril()
+    logits = logits.masked_fill(~causal, float("-inf"))
+    A = torch.softmax(logits, dim=1)                # row i: weights over tokens j <= i
+    M = (A @ V.double()).float()
+    W1 = normal((d_inner, d_model), std=WEIGHT_STD, seed=s + 4, dtype=torch.float32)
+    W2 = normal((d_model, d_inner), std=WEIGHT_STD, seed=s + 5, dtype=torch.float32)
+    return TinyGMU(X=X, V=V, A=A, M=M, W1=W1, W2=W2)
+
+
+# -------------------------------------------------------------- GMU (bf16)
+
+@dataclass
+class GMUInputs:
+    M: torch.Tensor    # [rows, d_inner]
+    X: torch.Tensor    # [rows, d_model]
+    W1: torch.Tensor   # [d_inner, d_model]
+    W2: torch.Tensor   # [d_model, d_inner]
+
+
+def gmu_inputs(rows: int, d_model: int, d_inner: int, *, seed: int = 0, device="cpu",
+               dtype=torch.bfloat16, weight_set: int = 0) -> GMUInputs:
+    """M, X ~ N(0,1) rows; W1, W2 ~ N(0, 0.02^2).  `weight_set` selects one of
+    several independent weight draws (the benchmark rotates them so that the
+    weights are streamed from HBM rather than served from the last-level cache)."""
+    M = normal((rows, d_inner), seed=_seed(seed, 1), device=device, dtype=dtype)
+    X = normal((rows, d_model), seed=_seed(seed, 2), device=device, dtype=dtype)
+    W1 = normal((d_inner, d_model), std=WEIGHT_STD, seed=_seed(seed, 3, weight_set), device=device, dtype=dtype)
+    W2 = normal((d_model, d_inner), std=WEIGHT_STD, seed=_seed(seed, 4, weight_set), device=device, dtype=dtype)
+    return GMUInputs(M=M, X=X, W1=W1, W2=W2)
+
+
+# ------------------------------------------------- cross-attention (bf16)
+
+@dataclass
+class XAttnInputs:
+    q: torch.Tensor    # [B, Hq, D]
+    K: torch.Tensor    # [B, Hkv, L, D]
+    V: torch.Tensor    # [B, Hkv, L, D]
+
+
+def xattn_inputs(B: int, Hq: int, Hkv: int, D: int, L: int, *, seed: int = 0, device="cpu",
+                 dtype=torch.bfloat16) -> XAttnInputs:
+    """q, K, V ~ N(0,1): one decode query per sequence against a shared cache
+    of L positions (all positions visible)."""
+    q = normal((B, Hq, D), seed=_seed(seed, 11), device=device, dtype=dtype)
+    K = normal((B, Hkv, L, D), seed=_seed(seed, 12), device=device, dtype=dtype)
+    V = normal((B, Hkv, L, D), seed=_seed(seed, 13), device=device, dtype=dtype)
+    return XAttnInputs(q=q, K=K, V=V)
+
+
+# ------------------------------------------------------ cross-decoder step
+
+@dataclass
+class CrossDecoderInputs:
+    h: torch.Tensor                 # [B, d_model] residual stream entering the cross-decoder
+    M: torch.Tensor                 # [B, d_inner] memory readout shared by every GMU layer
+    K: torch.Tensor                 # [B, Hkv, L, D] the single shared KV cache
+    V: torch.Tensor
+    layers: list = field(default_factory=list)   # [(kind, w_a, w_b)]
+
+
+def layer_kinds(n_layers: int, first: str = "xattn") -> list:
+    """Alternating layer kinds, starting with `first` ("xattn" or "gmu")."""
+    other = "gmu" if first == "xattn" else "xattn"
+    return [first if i % 2 == 0 else other for i in range(n_layers)]
+
+
+def crossdecoder_inputs(B: int, d_model: int, d_inner: int, Hq: int, Hkv: int, D: int, L: int, n_layers: int, *,
+                        seed: int = 0, device="cpu", dtype=torch.bfloat16, kinds=None) -> CrossDecoderInputs:
+    """h, M, K, V ~ N(0,1); per-layer weights ~ N(0, 0.02^2): (Wq, Wo) of shape
+    [d_model, d_model] for cross-attention, (W1 [d_inner, d_model],
+    W2 [d_model, d_inner]) for GMU layers."""
+    if kinds is None:
+        kinds = layer_kinds(n_layers)
+    h = normal((B, d_model), seed=_seed(seed, 21), device=device, dtype=dtype)
+    M = normal((B, d_inner), seed=_seed(seed, 22), device=device, dtype=dtype)
+    K = normal((B, Hkv, L, D), seed=_seed(seed, 23), device=device, dtype=dtype)
+    V = normal((B, Hkv, L, D), seed=_seed(seed, 24), device=device, dtype=dtype)
+    layers = []
+    for i, kind in enumerate(kinds):
+        if kind == "xattn":
+            wa = normal((d_model, d_model), std=WEIGHT_STD, seed=_seed(seed, 30, 2 * i), device=device, dtype=dtype)
+            wb = normal((d_model, d_model), std=WEIGHT_STD, seed=_seed(seed, 30, 2 * i + 1), device=device,
+                        dtype=dtype)
+        elif kind == "gmu":
+            wa = normal((d_inner, d_model), std=WEIGHT_STD, seed=_seed(seed, 30, 2 * i), device=device, dtype=dtype)
+            wb = normal((d_model, d_inner), std=WEIGHT_STD, seed=_seed(seed, 30, 2 * i + 1), device=device,
+                        dtype=dtype)
+        else:
+            raise ValueError(kind)
+        layers.append((kind, wa, wb))
+    return CrossDecoderInputs(h=h, M=M, K=K, V=V, layers=layers)
