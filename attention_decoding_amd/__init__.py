@@ -1,0 +1,238 @@
+"""SambaY cross-decoder decode path for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libsambay.so`` (C ABI in ``include/sambay.h``).
+It only checks and marshals arguments — device, dtype, shape, contiguity —
+and passes torch's device memory and current HIP stream to the library;
+every step of the computation runs in the library's HIP kernels.  There is
+no CPU fallback: if the library is missing the import fails.
+
+Calls (same names as the C ABI):
+    gmu_forward(M, X, W1, W2, out=None)            -> Y
+    xattn_decode(q, kcache, vcache, out=None, scale=None) -> out
+    crossdecoder_step(h, M, kcache, vcache, layers, scale=None) -> h (in place)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsambay.so")
+
+SB_OK, SB_EINVAL, SB_EUNSUPPORTED, SB_EWORKSPACE, SB_EHIP = 0, 1, 2, 3, 4
+STATUS_NAMES = {0: "SB_OK", 1: "SB_EINVAL", 2: "SB_EUNSUPPORTED", 3: "SB_EWORKSPACE", 4: "SB_EHIP"}
+SB_F32, SB_BF16 = 0, 1
+SB_LAYER_XATTN, SB_LAYER_GMU = 0, 1
+
+# Every function the header declares, for load-time checking.
+EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", "xattn_workspace_bytes",
+           "xattn_decode", "crossdecoder_workspace_bytes", "crossdecoder_step")
+
+
+class SbLayer(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("w_a", ctypes.c_void_p), ("w_b", ctypes.c_void_p)]
+
+
+class SambayError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s: %s: %s" % (fn, STATUS_NAMES.get(status, str(status)), msg))
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libsambay.so not built at %s; run `python -m attention_decoding_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    lib.sb_last_error.restype = ctypes.c_char_p
+    lib.sb_version.restype = ctypes.c_char_p
+    lib.gmu_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+    lib.gmu_workspace_bytes.restype = sz
+    lib.gmu_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, sz, vp]
+    lib.gmu_forward.restype = ctypes.c_int
+    lib.xattn_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.xattn_workspace_bytes.restype = sz
+    lib.xattn_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, sz, vp]
+    lib.xattn_decode.restype = ctypes.c_int
+    lib.crossdecoder_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64]
+    lib.crossdecoder_workspace_bytes.restype = sz
+    lib.crossdecoder_step.argtypes = [vp, vp, vp, vp, ctypes.POINTER(SbLayer), i32, i64, i64, i64, i64, i64, i64,
+                                      i64, ctypes.c_float, vp, sz, vp]
+    lib.crossdecoder_step.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def version() -> str:
+    return lib.sb_version().decode()
+
+
+def _check(fn: str, status: int):
+    if status != SB_OK:
+        raise SambayError(fn, status, lib.sb_last_error().decode())
+
+
+def _dev_ptr(t: torch.Tensor, name: str, dtype: torch.dtype, device: torch.device) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A device byte buffer of at least nbytes, cached per device and stream
+    (reused only by calls ordered on that stream)."""
+    key = (device, _stream(device))
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _check_device(t: torch.Tensor, name: str) -> torch.device:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (the library has no CPU path)" % name)
+    return t.device
+
+
+def gmu_forward(M: torch.Tensor, X: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = (M ⊙ SiLU(X W1^T)) W2^T.  M [rows, d_inner], X [rows, d_model],
+    W1 [d_inner, d_model], W2 [d_model, d_inner]; all bf16 or all fp32."""
+    dev = _check_device(X, "X")
+    if X.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("X must be bfloat16 or float32")
+    dt = X.dtype
+    if X.dim() != 2 or M.dim() != 2 or W1.dim() != 2 or W2.dim() != 2:
+        raise ValueError("gmu_forward expects 2-D tensors")
+    rows, d_model = X.shape
+    d_inner = W1.shape[0]
+    if M.shape != (rows, d_inner) or W1.shape != (d_inner, d_model) or W2.shape != (d_model, d_inner):
+        raise ValueError("gmu_forward shape mismatch: M %s X %s W1 %s W2 %s" % (tuple(M.shape), tuple(X.shape),
+                                                                              tuple(W1.shape), tuple(W2.shape)))
+    if out is None:
+        out = torch.empty((rows, d_model), dtype=dt, device=dev)
+    elif out.shape != (rows, d_model):
+        raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), (rows, d_model)))
+    code = SB_BF16 if dt == torch.bfloat16 else SB_F32
+    nb = lib.gmu_workspace_bytes(rows, d_model, d_inner, code)
+    ws = _workspace(dev, nb)
+    st = lib.gmu_forward(_dev_ptr(M, "M", dt, dev), _dev_ptr(X, "X", dt, dev), _dev_ptr(W1, "W1", dt, dev),
+                         _dev_ptr(W2, "W2", dt, dev), _dev_ptr(out, "out", dt, dev), rows, d_model, d_inner, code,
+                         ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("gmu_forward", st)
+    return out
+
+
+def xattn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, out: torch.Tensor | None = None,
+                 scale: float | None = None) -> torch.Tensor:
+    """Decode attention of q [B, Hq, D] over the whole shared cache
+    kcache/vcache [B, Hkv, L, D]; bf16 in and out."""
+    dev = _check_device(q, "q")
+    bf = torch.bfloat16
+    if q.dim() != 3 or kcache.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and kcache [B, Hkv, L, D]")
+    B, Hq, D = q.shape
+    B2, Hkv, L, D2 = kcache.shape
+    if B2 != B or D2 != D or vcache.shape != kcache.shape:
+        raise ValueError("xattn_decode shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(kcache.shape),
+                                                                       tuple(vcache.shape)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=bf, device=dev)
+    elif out.shape != (B, Hq, D):
+        raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), (B, Hq, D)))
+    nb = lib.xattn_workspace_bytes(B, Hq, Hkv, D, L)
+    ws = _workspace(dev, nb)
+    st = lib.xattn_decode(_dev_ptr(q, "q", bf, dev), _dev_ptr(kcache, "kcache", bf, dev),
+                          _dev_ptr(vcache, "vcache", bf, dev), _dev_ptr(out, "out", bf, dev), B, Hq, Hkv, D, L,
+                          float(scale), ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("xattn_decode", st)
+    return out
+
+
+def _layer_array(layers: Sequence, dev: torch.device, d_model: int, d_inner: int):
+    arr = (SbLayer * max(len(layers), 1))()
+    bf = torch.bfloat16
+    for i, layer in enumerate(layers):
+        kind, wa, wb = layer
+        if kind in ("xattn", SB_LAYER_XATTN):
+            k, sa, sb = SB_LAYER_XATTN, (d_model, d_model), (d_model, d_model)
+        elif kind in ("gmu", SB_LAYER_GMU):
+            k, sa, sb = SB_LAYER_GMU, (d_inner, d_model), (d_model, d_inner)
+        else:
+            raise ValueError("layer %d: kind must be 'xattn' or 'gmu'" % i)
+        if tuple(wa.shape) != sa or tuple(wb.shape) != sb:
+            raise ValueError("layer %d (%s): weights %s, %s; expected %s, %s" % (i, kind, tuple(wa.shape),
+                                                                               tuple(wb.shape), sa, sb))
+        arr[i].kind = k
+        arr[i].w_a = _dev_ptr(wa, "layer %d w_a" % i, bf, dev)
+        arr[i].w_b = _dev_ptr(wb, "layer %d w_b" % i, bf, dev)
+    return arr
+
+
+class CrossDecoderStep:
+    """Prepared argument block for repeated cross-decoder steps on the same
+    tensors (what a decode loop or a HIP graph capture calls): the layer array
+    and workspace are built once; __call__ only enqueues."""
+
+    def __init__(self, h, M, kcache, vcache, layers: Sequence, scale: float | None = None):
+        dev = _check_device(h, "h")
+        bf = torch.bfloat16
+        if h.dim() != 2 or M.dim() != 2 or kcache.dim() != 4:
+            raise ValueError("h [B, d_model], M [B, d_inner], kcache [B, Hkv, L, D]")
+        B, d_model = h.shape
+        d_inner = M.shape[1]
+        B2, Hkv, L, D = kcache.shape
+        if M.shape[0] != B or B2 != B or vcache.shape != kcache.shape:
+            raise ValueError("crossdecoder_step shape mismatch")
+        if d_model % D != 0:
+            raise ValueError("d_model must be a multiple of the head dim")
+        self.Hq = d_model // D
+        self.dims = (B, d_model, d_inner, self.Hq, Hkv, D, L)
+        self.scale = float(1.0 / math.sqrt(D) if scale is None else scale)
+        self.tensors = (h, M, kcache, vcache, layers)
+        self.ptrs = (_dev_ptr(h, "h", bf, dev), _dev_ptr(M, "M", bf, dev), _dev_ptr(kcache, "kcache", bf, dev),
+                     _dev_ptr(vcache, "vcache", bf, dev))
+        self.arr = _layer_array(layers, dev, d_model, d_inner)
+        self.n_layers = len(layers)
+        nb = lib.crossdecoder_workspace_bytes(B, d_model, d_inner, self.Hq, Hkv, D, L)
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        self.device = dev
+
+    def __call__(self):
+        st = lib.crossdecoder_step(*self.ptrs, self.arr, self.n_layers, *self.dims, self.scale, self.ws.data_ptr(),
+                                   self.ws.numel(), _stream(self.device))
+        _check("crossdecoder_step", st)
+        return self.tensors[0]
+
+
+def crossdecoder_step(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                      layers: Sequence, scale: float | None = None) -> torch.Tensor:
+    """One cross-decoder decode step; h [B, d_model] bf16 is updated in place.
+    layers: sequence of (kind, w_a, w_b), kind "xattn" (Wq, Wo) or "gmu" (W1, W2)."""
+    return CrossDecoderStep(h, M, kcache, vcache, layers, scale)()
+
+
+__all__ = ["gmu_forward", "xattn_decode", "crossdecoder_step", "CrossDecoderStep", "SambayError", "version", "lib",
+           "EXPORTS", "LIB_PATH"]

@@ -1,0 +1,348 @@
+// C ABI of the library: argument validation, workspace layout, dispatch by
+// shape regime and cross-decoder sequencing.  Kernels live in the other
+// translation units; nothing here allocates, frees or synchronises.
+#include "sambay.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "launch.hpp"
+
+using namespace sambay;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sb_status fail(sb_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+sb_status ok() {
+    g_last_error.clear();
+    return SB_OK;
+}
+
+sb_status hip_fail(const char *where, hipError_t e) {
+    return fail(SB_EHIP, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range rng(const char *name, const void *p, size_t bytes) {
+    return Range{name, (uintptr_t)p, (uintptr_t)p + bytes};
+}
+
+bool overlaps(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// Workspace carving: sequential 256-byte-aligned sub-buffers.
+struct Carver {
+    char *base;
+    size_t used = 0;
+    void *take(size_t bytes) {
+        void *p = base ? base + used : nullptr;
+        used += round_up(bytes);
+        return p;
+    }
+};
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+// ----------------------------------------------------------------- GMU
+
+size_t gmu_ws(int64_t rows, int64_t d_model, int64_t d_inner, sb_dtype dt) {
+    if (rows <= 0 || d_model <= 0 || d_inner <= 0) return 0;
+    if (dt == SB_F32) return round_up((size_t)rows * d_inner * sizeof(float));
+    // bf16 H [rows, d_inner]; decode also needs room for k-split partials.
+    size_t bytes = round_up((size_t)rows * d_inner * sizeof(bf16_t));
+    if (rows <= kSkinnyMaxTokens) {
+        const SkinnyPlan p1 = skinny_plan((int)rows, (int)d_inner, (int)d_model);
+        const SkinnyPlan p2 = skinny_plan((int)rows, (int)d_model, (int)d_inner);
+        size_t part = skinny_partial_bytes((int)rows, (int)d_inner, p1);
+        const size_t part2 = skinny_partial_bytes((int)rows, (int)d_model, p2);
+        if (part2 > part) part = part2;
+        bytes += round_up(part);
+    }
+    return bytes;
+}
+
+// bf16 GMU on rows <= 64 tokens (decode): two weight-streaming launches.
+hipError_t gmu_decode_bf16(const bf16_t *M, const bf16_t *X, int ldx, const bf16_t *W1, const bf16_t *W2, void *Y,
+                           Epilogue out_epi, int T, int d_model, int d_inner, Carver &ws, hipStream_t stream) {
+    bf16_t *H = static_cast<bf16_t *>(ws.take((size_t)T * d_inner * sizeof(bf16_t)));
+    const SkinnyPlan p1 = skinny_plan(T, d_inner, d_model);
+    const SkinnyPlan p2 = skinny_plan(T, d_model, d_inner);
+    size_t part = skinny_partial_bytes(T, d_inner, p1);
+    if (skinny_partial_bytes(T, d_model, p2) > part) part = skinny_partial_bytes(T, d_model, p2);
+    float *partials = static_cast<float *>(ws.take(part));
+    hipError_t e = launch_skinny(X, ldx, W1, T, d_inner, d_model, EPI_GATE, H, d_inner, M, d_inner, p1, partials,
+                                 stream);
+    if (e != hipSuccess) return e;
+    return launch_skinny(H, d_inner, W2, T, d_model, d_inner, out_epi, Y, d_model, nullptr, 0, p2, partials, stream);
+}
+
+// ------------------------------------------------------- cross-attention
+
+sb_status check_xattn_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L) {
+    if (B < 0 || Hq < 0 || Hkv < 0 || D < 0 || L < 0) return fail(SB_EINVAL, "negative size");
+    if (Hq == 0 || Hkv == 0) return fail(SB_EINVAL, "Hq and Hkv must be positive");
+    if (L == 0) return fail(SB_EINVAL, "L == 0: the cache holds no position");
+    if (Hq % Hkv != 0) return fail(SB_EINVAL, "Hq (%lld) is not a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+    if (D != kHeadDim) return fail(SB_EUNSUPPORTED, "head dim %lld unsupported (only %d)", (long long)D, kHeadDim);
+    if (Hq / Hkv > kMaxGroup)
+        return fail(SB_EUNSUPPORTED, "group size Hq/Hkv = %lld exceeds %d", (long long)(Hq / Hkv), kMaxGroup);
+    if (L >= ((int64_t)1 << 31)) return fail(SB_EUNSUPPORTED, "L >= 2^31");
+    if (B > 65535 || Hkv > 65535) return fail(SB_EUNSUPPORTED, "B and Hkv must be <= 65535");
+    if (B * Hq > ((int64_t)1 << 31) - 1) return fail(SB_EUNSUPPORTED, "B*Hq too large");
+    return SB_OK;
+}
+
+size_t xattn_ws(int64_t B, int64_t Hq, int64_t Hkv, int64_t L) {
+    const XattnPlan p = xattn_plan(B, Hkv, L);
+    return round_up(xattn_partial_bytes(B, Hq, p.splits));
+}
+
+}  // namespace
+
+// =================================================================== ABI
+
+extern "C" const char *sb_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" const char *sb_version(void) { return "sambay-mi355x 0.1 (gfx950)"; }
+
+extern "C" size_t gmu_workspace_bytes(int64_t rows, int64_t d_model, int64_t d_inner, sb_dtype dt) {
+    return gmu_ws(rows, d_model, d_inner, dt);
+}
+
+extern "C" sb_status gmu_forward(const void *M, const void *X, const void *W1, const void *W2, void *Y, int64_t rows,
+                                 int64_t d_model, int64_t d_inner, sb_dtype dt, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    if (rows < 0 || d_model < 0 || d_inner < 0) return fail(SB_EINVAL, "negative size");
+    if (dt != SB_F32 && dt != SB_BF16) return fail(SB_EINVAL, "unknown dtype %d", (int)dt);
+    if (rows == 0) return ok();
+    if (d_model == 0 || d_inner == 0) return fail(SB_EINVAL, "d_model and d_inner must be positive");
+    if (!M || !X || !W1 || !W2 || !Y) return fail(SB_EINVAL, "null tensor pointer");
+    if (!aligned16(M) || !aligned16(X) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y))
+        return fail(SB_EINVAL, "tensor base pointers must be 16-byte aligned");
+    if (rows > kMaxDim || d_model > kMaxDim || d_inner > kMaxDim) return fail(SB_EUNSUPPORTED, "dimension >= 2^30");
+    if (rows * d_inner > ((int64_t)1 << 40) || rows * d_model > ((int64_t)1 << 40))
+        return fail(SB_EUNSUPPORTED, "tensor too large");
+    const size_t es = dt == SB_F32 ? 4 : 2;
+    const Range ry = rng("Y", Y, (size_t)rows * d_model * es);
+    const Range ins[] = {rng("M", M, (size_t)rows * d_inner * es), rng("X", X, (size_t)rows * d_model * es),
+                         rng("W1", W1, (size_t)d_inner * d_model * es), rng("W2", W2, (size_t)d_model * d_inner * es)};
+    for (const Range &r : ins)
+        if (overlaps(ry, r)) return fail(SB_EINVAL, "Y overlaps %s", r.name);
+    if (dt == SB_BF16 && (d_model % 64 != 0 || d_inner % 64 != 0))
+        return fail(SB_EUNSUPPORTED, "bf16 GMU needs d_model and d_inner multiples of 64");
+    const size_t need = gmu_ws(rows, d_model, d_inner, dt);
+    if (!workspace || workspace_bytes < need)
+        return fail(SB_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(SB_EINVAL, "workspace must be 16-byte aligned");
+    const Range rw = rng("workspace", workspace, need);
+    if (overlaps(rw, ry)) return fail(SB_EINVAL, "workspace overlaps Y");
+    for (const Range &r : ins)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+
+    Carver ws{static_cast<char *>(workspace)};
+    hipError_t e;
+    if (dt == SB_F32) {
+        float *H = static_cast<float *>(ws.take((size_t)rows * d_inner * sizeof(float)));
+        e = launch_gmu_f32((const float *)M, (const float *)X, (const float *)W1, (const float *)W2, (float *)Y, H,
+                           rows, d_model, d_inner, stream);
+    } else if (rows <= kSkinnyMaxTokens) {
+        e = gmu_decode_bf16((const bf16_t *)M, (const bf16_t *)X, (int)d_model, (const bf16_t *)W1,
+                            (const bf16_t *)W2, Y, EPI_BF16, (int)rows, (int)d_model, (int)d_inner, ws, stream);
+    } else {
+        bf16_t *H = static_cast<bf16_t *>(ws.take((size_t)rows * d_inner * sizeof(bf16_t)));
+        e = launch_gemm((const bf16_t *)X, (const bf16_t *)W1, (int)rows, (int)d_inner, (int)d_model, EPI_GATE, H,
+                        (const bf16_t *)M, stream);
+        if (e == hipSuccess)
+            e = launch_gemm(H, (const bf16_t *)W2, (int)rows, (int)d_model, (int)d_inner, EPI_BF16, (bf16_t *)Y,
+                            nullptr, stream);
+    }
+    if (e != hipSuccess) return hip_fail("gmu_forward launch", e);
+    return ok();
+}
+
+extern "C" size_t xattn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || D != kHeadDim || Hq % Hkv != 0) return 0;
+    return xattn_ws(B, Hq, Hkv, L);
+}
+
+extern "C" sb_status xattn_decode(const void *q, const void *kcache, const void *vcache, void *out, int64_t B,
+                                  int64_t Hq, int64_t Hkv, int64_t D, int64_t L, float scale, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || Hq < 0 || Hkv < 0 || D < 0 || L < 0) return fail(SB_EINVAL, "negative size");
+    if (B == 0) return ok();
+    sb_status st = check_xattn_shape(B, Hq, Hkv, D, L);
+    if (st != SB_OK) return st;
+    if (!q || !kcache || !vcache || !out) return fail(SB_EINVAL, "null tensor pointer");
+    if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out))
+        return fail(SB_EINVAL, "tensor base pointers must be 16-byte aligned");
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(SB_EINVAL, "scale must be finite");
+    const size_t qbytes = (size_t)B * Hq * D * 2, kvbytes = (size_t)B * Hkv * L * D * 2;
+    const Range ro = rng("out", out, qbytes);
+    const Range ins[] = {rng("q", q, qbytes), rng("kcache", kcache, kvbytes), rng("vcache", vcache, kvbytes)};
+    for (const Range &r : ins)
+        if (overlaps(ro, r)) return fail(SB_EINVAL, "out overlaps %s", r.name);
+    const size_t need = xattn_ws(B, Hq, Hkv, L);
+    if (!workspace || workspace_bytes < need)
+        return fail(SB_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(SB_EINVAL, "workspace must be 16-byte aligned");
+    const Range rw = rng("workspace", workspace, need);
+    if (overlaps(rw, ro)) return fail(SB_EINVAL, "workspace overlaps out");
+    for (const Range &r : ins)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+
+    const XattnPlan plan = xattn_plan(B, Hkv, L);
+    hipError_t e = launch_xattn(q, false, (const bf16_t *)kcache, (const bf16_t *)vcache, (bf16_t *)out, (int)B,
+                                (int)Hq, (int)Hkv, (int)L, scale, plan, workspace, stream);
+    if (e != hipSuccess) return hip_fail("xattn_decode launch", e);
+    return ok();
+}
+
+namespace {
+
+// Workspace layout of one cross-decoder step (all reused layer to layer).
+struct StepLayout {
+    size_t q, o, gmu, partials, total;
+};
+
+StepLayout step_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t Hq, int64_t Hkv, int64_t L) {
+    StepLayout s;
+    const int64_t T = B < kSkinnyMaxTokens ? B : kSkinnyMaxTokens;  // token group processed per product
+    s.q = round_up((size_t)B * d_model * sizeof(float));
+    s.o = round_up((size_t)B * d_model * sizeof(bf16_t));
+    // GMU: H for one token group plus k-split partials; projections share the partial space.
+    size_t part = 0;
+    const SkinnyPlan pa = skinny_plan((int)T, (int)d_inner, (int)d_model);
+    const SkinnyPlan pb = skinny_plan((int)T, (int)d_model, (int)d_inner);
+    const SkinnyPlan pq = skinny_plan((int)T, (int)d_model, (int)d_model);
+    const size_t cands[] = {skinny_partial_bytes((int)T, (int)d_inner, pa), skinny_partial_bytes((int)T, (int)d_model, pb),
+                            skinny_partial_bytes((int)T, (int)d_model, pq)};
+    for (size_t c : cands)
+        if (c > part) part = c;
+    s.gmu = round_up((size_t)T * d_inner * sizeof(bf16_t)) + round_up(part);
+    s.partials = round_up(xattn_partial_bytes(B, Hq, xattn_plan(B, Hkv, L).splits));
+    s.total = s.q + s.o + s.gmu + s.partials;
+    return s;
+}
+
+}  // namespace
+
+extern "C" size_t crossdecoder_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inner, int64_t Hq, int64_t Hkv,
+                                               int64_t D, int64_t L) {
+    if (B <= 0 || d_model <= 0 || d_inner <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || D != kHeadDim || Hq % Hkv != 0)
+        return 0;
+    return step_layout(B, d_model, d_inner, Hq, Hkv, L).total;
+}
+
+extern "C" sb_status crossdecoder_step(void *h, const void *M, const void *kcache, const void *vcache,
+                                       const sb_layer *layers, int32_t n_layers, int64_t B, int64_t d_model,
+                                       int64_t d_inner, int64_t Hq, int64_t Hkv, int64_t D, int64_t L, float scale,
+                                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || d_model < 0 || d_inner < 0 || Hq < 0 || Hkv < 0 || D < 0 || L < 0 || n_layers < 0)
+        return fail(SB_EINVAL, "negative size");
+    if (B == 0 || n_layers == 0) return ok();
+    sb_status st = check_xattn_shape(B, Hq, Hkv, D, L);
+    if (st != SB_OK) return st;
+    if (d_model == 0 || d_inner == 0) return fail(SB_EINVAL, "d_model and d_inner must be positive");
+    if (Hq * D != d_model)
+        return fail(SB_EINVAL, "Hq*D (%lld) != d_model (%lld)", (long long)(Hq * D), (long long)d_model);
+    if (d_model % 64 != 0 || d_inner % 64 != 0)
+        return fail(SB_EUNSUPPORTED, "d_model and d_inner must be multiples of 64");
+    if (d_model > kMaxDim || d_inner > kMaxDim) return fail(SB_EUNSUPPORTED, "dimension >= 2^30");
+    if (!h || !M || !kcache || !vcache) return fail(SB_EINVAL, "null tensor pointer");
+    if (!layers) return fail(SB_EINVAL, "null layer array");
+    if (!aligned16(h) || !aligned16(M) || !aligned16(kcache) || !aligned16(vcache))
+        return fail(SB_EINVAL, "tensor base pointers must be 16-byte aligned");
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(SB_EINVAL, "scale must be finite");
+    const size_t kvbytes = (size_t)B * Hkv * L * D * 2;
+    const Range rh = rng("h", h, (size_t)B * d_model * 2);
+    const Range fixed[] = {rng("M", M, (size_t)B * d_inner * 2), rng("kcache", kcache, kvbytes),
+                           rng("vcache", vcache, kvbytes)};
+    for (const Range &r : fixed)
+        if (overlaps(rh, r)) return fail(SB_EINVAL, "h overlaps %s", r.name);
+    for (int32_t i = 0; i < n_layers; ++i) {
+        const sb_layer &ly = layers[i];
+        if (ly.kind != SB_LAYER_XATTN && ly.kind != SB_LAYER_GMU)
+            return fail(SB_EINVAL, "layer %d: unknown kind %d", (int)i, (int)ly.kind);
+        if (!ly.w_a || !ly.w_b) return fail(SB_EINVAL, "layer %d: null weight", (int)i);
+        if (!aligned16(ly.w_a) || !aligned16(ly.w_b)) return fail(SB_EINVAL, "layer %d: misaligned weight", (int)i);
+        const size_t ba = (size_t)(ly.kind == SB_LAYER_GMU ? d_inner : d_model) * d_model * 2;
+        const size_t bb = (size_t)d_model * (ly.kind == SB_LAYER_GMU ? d_inner : d_model) * 2;
+        if (overlaps(rh, rng("w_a", ly.w_a, ba)) || overlaps(rh, rng("w_b", ly.w_b, bb)))
+            return fail(SB_EINVAL, "layer %d: weight overlaps h", (int)i);
+    }
+    const StepLayout lay = step_layout(B, d_model, d_inner, Hq, Hkv, L);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(SB_EWORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
+                    workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(SB_EINVAL, "workspace must be 16-byte aligned");
+    const Range rw = rng("workspace", workspace, lay.total);
+    if (overlaps(rw, rh)) return fail(SB_EINVAL, "workspace overlaps h");
+    for (const Range &r : fixed)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+
+    char *base = static_cast<char *>(workspace);
+    float *q = reinterpret_cast<float *>(base);
+    bf16_t *o = reinterpret_cast<bf16_t *>(base + lay.q);
+    char *gmu_ws_base = base + lay.q + lay.o;
+    void *partials = base + lay.q + lay.o + lay.gmu;
+    const XattnPlan plan = xattn_plan(B, Hkv, L);
+    bf16_t *hb = static_cast<bf16_t *>(h);
+    const int dm = (int)d_model, di = (int)d_inner;
+
+    for (int32_t li = 0; li < n_layers; ++li) {
+        const sb_layer &ly = layers[li];
+        hipError_t e = hipSuccess;
+        if (ly.kind == SB_LAYER_XATTN) {
+            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+                const SkinnyPlan pq = skinny_plan(T, dm, dm);
+                e = launch_skinny(hb + t0 * dm, dm, (const bf16_t *)ly.w_a, T, dm, dm, EPI_F32, q + t0 * dm, dm,
+                                  nullptr, 0, pq, reinterpret_cast<float *>(gmu_ws_base + round_up((size_t)T * di * 2)),
+                                  stream);
+            }
+            if (e == hipSuccess)
+                e = launch_xattn(q, true, (const bf16_t *)kcache, (const bf16_t *)vcache, o, (int)B, (int)Hq,
+                                 (int)Hkv, (int)L, scale, plan, partials, stream);
+            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+                const SkinnyPlan po = skinny_plan(T, dm, dm);
+                e = launch_skinny(o + t0 * dm, dm, (const bf16_t *)ly.w_b, T, dm, dm, EPI_RESID, hb + t0 * dm, dm,
+                                  nullptr, 0, po, reinterpret_cast<float *>(gmu_ws_base + round_up((size_t)T * di * 2)),
+                                  stream);
+            }
+        } else {
+            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+                Carver ws{gmu_ws_base};
+                e = gmu_decode_bf16((const bf16_t *)M + t0 * di, hb + t0 * dm, dm, (const bf16_t *)ly.w_a,
+                                    (const bf16_t *)ly.w_b, hb + t0 * dm, EPI_RESID, T, dm, di, ws, stream);
+            }
+        }
+        if (e != hipSuccess) return hip_fail("crossdecoder_step launch", e);
+    }
+    return ok();
+}

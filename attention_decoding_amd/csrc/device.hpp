@@ -1,0 +1,68 @@
+// Device-side building blocks shared by the gfx950 kernels: bf16 bit
+// conversions, 16-byte vector types, and the wave64 MFMA tile used by every
+// matrix product in the library.
+//
+// MFMA tile (v_mfma_f32_16x16x32_bf16, CDNA4): D[16x16] += A[16x32] · B[32x16].
+// Operand layout per lane l of the wave (row/col = l % 16, grp = l / 16):
+//   A: row (l % 16), k elements 8·grp .. 8·grp+7   (eight bf16, 16 bytes)
+//   B: col (l % 16), k elements 8·grp .. 8·grp+7
+//   D: col (l % 16), rows 4·grp .. 4·grp+3         (four fp32)
+// The kernels only rely on A and B pairing the same (grp, element) slots, so
+// any fixed assignment of the 32 contraction indices to those slots is valid;
+// they pick the one that lets every lane load 16 contiguous bytes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sambay {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// Round to nearest, ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Low / high bf16 of a packed pair, widened to fp32.
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// Streaming read of data used once (KV cache, weights): non-temporal hint.
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Orders this wave's LDS accesses across lanes without a workgroup barrier.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace sambay

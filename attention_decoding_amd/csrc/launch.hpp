@@ -1,0 +1,61 @@
+// Host-side launchers for the gfx950 kernels.  The C ABI (api.hip) validates
+// every argument first; these functions assume valid shapes and only enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sambay {
+
+typedef uint16_t bf16_t;
+
+// ------------------------------------------------------- cross-attention
+constexpr int kHeadDim = 128;     // supported head dimension
+constexpr int kMaxGroup = 16;     // query heads per KV head handled by one tile
+constexpr int kKeyBlock = 32;     // cache positions per wave iteration
+constexpr int kMaxSplits = 64;
+
+struct XattnPlan {
+    int splits;  // number of key chunks per (sequence, KV head)
+    int chunk;   // keys per chunk, a multiple of kKeyBlock; every chunk is non-empty
+};
+
+XattnPlan xattn_plan(int64_t B, int64_t Hkv, int64_t L);
+// Bytes of fp32 partials for `splits` chunks: (max, sum) pairs then D-wide sums.
+size_t xattn_partial_bytes(int64_t B, int64_t Hq, int splits);
+// q is fp32 ([B, Hq, D]) when q_f32, else bf16.  out: bf16 [B, Hq, D].
+hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, bf16_t *out, int B, int Hq,
+                        int Hkv, int L, float scale, const XattnPlan &plan, void *partials, hipStream_t stream);
+
+// ------------------------------------------------ skinny (decode) products
+// out[t, n] = epi( Σ_k X[t, k] · W[n, k] ) for t < T <= 64 tokens.
+enum Epilogue {
+    EPI_F32 = 0,    // out fp32
+    EPI_BF16 = 1,   // out bf16
+    EPI_GATE = 2,   // out bf16 = aux[t, n] · SiLU(acc)   (aux = M, bf16)
+    EPI_RESID = 3   // out bf16 = out[t, n] + acc         (in-place residual add)
+};
+constexpr int kSkinnyMaxTokens = 64;
+
+struct SkinnyPlan {
+    int rows_per_wg;   // weight rows per workgroup
+    int k_splits;      // workgroups along K (1 = epilogue fused)
+    int k_slice;       // K elements per split (multiple of 64)
+};
+SkinnyPlan skinny_plan(int T, int N, int K);
+size_t skinny_partial_bytes(int T, int N, const SkinnyPlan &p);
+hipError_t launch_skinny(const bf16_t *X, int ldx, const bf16_t *W, int T, int N, int K, Epilogue epi, void *out,
+                         int ldo, const bf16_t *aux, int ldaux, const SkinnyPlan &plan, float *partials,
+                         hipStream_t stream);
+
+// ------------------------------------------------------- prefill product
+// out[r, n] = epi( Σ_k X[r, k] · W[n, k] ), any row count, N % 64 == 0, K % 64 == 0.
+hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
+                       const bf16_t *aux, hipStream_t stream);
+
+// ------------------------------------------------------------- fp32 GMU
+hipError_t launch_gmu_f32(const float *M, const float *X, const float *W1, const float *W2, float *Y, float *H,
+                          int64_t rows, int64_t d_model, int64_t d_inner, hipStream_t stream);
+
+}  // namespace sambay

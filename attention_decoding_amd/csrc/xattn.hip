@@ -1,0 +1,276 @@
+// Split-K flash decoding over the single shared GQA KV cache (gfx950).
+//
+// What is computed: for each sequence b and query head h, the softmax
+// attention of the new token's query over all L cached positions of KV head
+// g = h / G (G = Hq / Hkv), with no positional encoding — the decode-time
+// cross-attention of the cross-decoder (Paper-Notes reading notes on
+// "Decoder-Hybrid-Decoder Architecture for Efficient Reasoning with Long
+// Generation", sections 整体框架 and 现有痛点; NoPE: section 关键发现).
+//
+// Design (HBM-bound: the cache is read once, ~3 FLOP per byte):
+//  * One workgroup per (chunk s, KV head g, sequence b); its four waves take
+//    32-position blocks of the chunk round-robin.  All G query heads of the
+//    group share every K/V byte loaded, so the cache is read exactly once.
+//  * Scores: one 16x16x32 MFMA tile per 16 positions and 32 dims, K rows as
+//    the A operand straight from HBM (each lane streams 64 contiguous bytes of
+//    one row), the group's queries as the B operand (padded to 16 heads).
+//    The query is pre-scaled by scale·log2(e) and split into bf16 hi + lo
+//    parts, so q·k keeps ~16 significant bits with exact bf16 keys.
+//  * Online softmax in the log2 domain per lane (each lane owns one head of
+//    8 positions); the block max is shared across the 4 lane groups.
+//  * P·V: the score tile's accumulator layout is already the B operand of
+//    the second product (each lane holds 8 probabilities of one head), so P
+//    never moves.  V is staged through a per-wave LDS tile and read back
+//    transposed (position-major per lane) as the A operand.
+//  * Partials (m, l, o) per (b, head, chunk) in fp32; a merge kernel combines
+//    the chunks by log-sum-exp in a fixed order (deterministic, no atomics).
+#include "device.hpp"
+#include "launch.hpp"
+
+#include <math.h>
+#include <stdlib.h>
+
+namespace sambay {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kVStride = kHeadDim + 8;  // bf16 per staged V row: 272-byte rows spread the transposed reads over banks
+
+template <bool QF32>
+__global__ __launch_bounds__(kThreads) void xattn_split_kernel(const void *__restrict__ qv,
+                                                               const bf16_t *__restrict__ K,
+                                                               const bf16_t *__restrict__ V,
+                                                               float2 *__restrict__ part_ml,
+                                                               float *__restrict__ part_o, int Hq, int Hkv, int L,
+                                                               int chunk, int S, float qscale) {
+    __shared__ __attribute__((aligned(16))) bf16_t vs[kWaves][kKeyBlock][kVStride];
+    __shared__ float red_m[kWaves][kMaxGroup];
+    __shared__ float red_l[kWaves][kMaxGroup];
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int G = Hq / Hkv;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+    const int j0 = s * chunk;
+    const int j1 = min(L, j0 + chunk);
+    const size_t kv0 = ((size_t)b * Hkv + g) * (size_t)L * kHeadDim;
+    const bf16_t *Kb = K + kv0;
+    const bf16_t *Vb = V + kv0;
+
+    // B operand of the score product: head `col` of this group, dims 32·grp + 8·t + e.
+    u32x4 qhi[4], qlo[4];
+    {
+        const int h = g * G + col;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float f[8];
+            const size_t off = ((size_t)b * Hq + h) * kHeadDim + 32 * grp + 8 * t;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x = 0.f;
+                if (col < G) x = QF32 ? ((const float *)qv)[off + e] : bf16_to_f32(((const bf16_t *)qv)[off + e]);
+                f[e] = x * qscale;
+            }
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16_t h0 = f32_to_bf16(f[2 * e]), h1 = f32_to_bf16(f[2 * e + 1]);
+                hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lo[e] = pack_bf16x2(f[2 * e] - bf16_to_f32(h0), f[2 * e + 1] - bf16_to_f32(h1));
+            }
+            qhi[t] = (u32x4){hi[0], hi[1], hi[2], hi[3]};
+            qlo[t] = (u32x4){lo[0], lo[1], lo[2], lo[3]};
+        }
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    bf16_t(*vw)[kVStride] = vs[wave];
+
+    const int nblk = (j1 - j0 + kKeyBlock - 1) / kKeyBlock;
+    for (int blk = wave; blk < nblk; blk += kWaves) {
+        const int base = j0 + blk * kKeyBlock;
+        // Rows past the chunk end are clamped to its last row (in bounds) and masked below.
+        const int ra = min(base + col, j1 - 1), rb = min(base + 16 + col, j1 - 1);
+        const bf16_t *kpa = Kb + (size_t)ra * kHeadDim + 32 * grp;
+        const bf16_t *kpb = Kb + (size_t)rb * kHeadDim + 32 * grp;
+        const bf16_t *vpa = Vb + (size_t)ra * kHeadDim + 32 * grp;
+        const bf16_t *vpb = Vb + (size_t)rb * kHeadDim + 32 * grp;
+        u32x4 k0[4], k1[4], v0[4], v1[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            k0[t] = ld16_stream(kpa + 8 * t);
+            k1[t] = ld16_stream(kpb + 8 * t);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            v0[t] = ld16_stream(vpa + 8 * t);
+            v1[t] = ld16_stream(vpb + 8 * t);
+        }
+
+        // Scores of positions base + 4·grp + r (s0) and base + 16 + 4·grp + r (s1) for head col.
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            s0 = mfma16x16x32(k0[t], qhi[t], s0);
+            s1 = mfma16x16x32(k1[t], qhi[t], s1);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            s0 = mfma16x16x32(k0[t], qlo[t], s0);
+            s1 = mfma16x16x32(k1[t], qlo[t], s1);
+        }
+
+        wave_lds_fence();  // the previous block's transposed reads are done
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            *reinterpret_cast<u32x4 *>(&vw[col][32 * grp + 8 * t]) = v0[t];
+            *reinterpret_cast<u32x4 *>(&vw[16 + col][32 * grp + 8 * t]) = v1[t];
+        }
+
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (base + 4 * grp + r >= j1) s0[r] = -INFINITY;
+            if (base + 16 + 4 * grp + r >= j1) s1[r] = -INFINITY;
+        }
+        float bm = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                         fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float m_new = fmaxf(m_run, bm);  // finite: every processed block has a live position
+        const float alpha = exp2_fast(m_run - m_new);
+        m_run = m_new;
+        float p[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p[r] = exp2_fast(s0[r] - m_new);
+            p[4 + r] = exp2_fast(s1[r] - m_new);
+        }
+        l_run = l_run * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+        const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                          pack_bf16x2(p[6], p[7])};
+
+        wave_lds_fence();  // the staged V rows are visible to every lane
+        // O^T[dim][head] += V^T[dim][pos] · P^T[pos][head]; lane reads dim 16·db + col at its 8 positions.
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const int d = 16 * db + col;
+            u32x4 va;
+            va[0] = (uint32_t)vw[4 * grp + 0][d] | ((uint32_t)vw[4 * grp + 1][d] << 16);
+            va[1] = (uint32_t)vw[4 * grp + 2][d] | ((uint32_t)vw[4 * grp + 3][d] << 16);
+            va[2] = (uint32_t)vw[16 + 4 * grp + 0][d] | ((uint32_t)vw[16 + 4 * grp + 1][d] << 16);
+            va[3] = (uint32_t)vw[16 + 4 * grp + 2][d] | ((uint32_t)vw[16 + 4 * grp + 3][d] << 16);
+            acc[db] = mfma16x16x32(va, pb, acc[db]);
+        }
+    }
+
+    // Row sums: each lane group summed different positions of the same head.
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+
+    // Combine the four waves' (m, l, o) in LDS, then write this chunk's partial.
+    __syncthreads();
+    float *ow = reinterpret_cast<float *>(&vs[0][0][0]);  // [kWaves][16 heads][128 dims] fp32 = 32 KB
+    if (grp == 0) {
+        red_m[wave][col] = m_run;
+        red_l[wave][col] = l_run;
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ow[(wave * kMaxGroup + col) * kHeadDim + 16 * db + 4 * grp + r] = acc[db][r];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
+        const int hh = idx / kHeadDim, d = idx % kHeadDim;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][hh]);
+        float lsum = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float e = exp2_fast(red_m[w][hh] - M);  // waves without positions carry m = -inf: weight 0
+            lsum += e * red_l[w][hh];
+            o += e * ow[(w * kMaxGroup + hh) * kHeadDim + d];
+        }
+        const size_t pi = ((size_t)b * Hq + (size_t)g * G + hh) * S + s;
+        part_o[pi * kHeadDim + d] = o;
+        if (d == 0) part_ml[pi] = make_float2(M, lsum);
+    }
+}
+
+// One workgroup per (sequence, query head): log-sum-exp merge of the chunks in
+// order, then normalisation and the bf16 store.
+__global__ __launch_bounds__(kHeadDim) void xattn_merge_kernel(const float2 *__restrict__ part_ml,
+                                                               const float *__restrict__ part_o,
+                                                               bf16_t *__restrict__ out, int S) {
+    const size_t bh = blockIdx.x;
+    const int d = threadIdx.x;
+    const float2 *ml = part_ml + bh * S;
+    const float *po = part_o + bh * S * kHeadDim;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s].x);
+    float lsum = 0.f, o = 0.f;
+    for (int s = 0; s < S; ++s) {
+        const float e = exp2_fast(ml[s].x - M);
+        lsum += e * ml[s].y;
+        o += e * po[(size_t)s * kHeadDim + d];
+    }
+    out[bh * kHeadDim + d] = f32_to_bf16(o / lsum);
+}
+
+int env_splits() {
+    const char *e = getenv("SAMBAY_XATTN_SPLITS");
+    if (!e || !*e) return 0;
+    const int v = atoi(e);
+    return v > 0 ? v : 0;
+}
+
+}  // namespace
+
+XattnPlan xattn_plan(int64_t B, int64_t Hkv, int64_t L) {
+    const int64_t nblk = (L + kKeyBlock - 1) / kKeyBlock;
+    const int64_t pairs = B * Hkv > 0 ? B * Hkv : 1;
+    // Aim for ~8 workgroups per CU over the 256 CUs so the tail is short.
+    int64_t S = env_splits();
+    if (S == 0) S = (2048 + pairs - 1) / pairs;
+    if (S > kMaxSplits) S = kMaxSplits;
+    if (S > nblk) S = nblk;
+    if (S < 1) S = 1;
+    const int64_t per = (nblk + S - 1) / S;
+    XattnPlan p;
+    p.chunk = (int)(per * kKeyBlock);
+    p.splits = (int)((L + p.chunk - 1) / p.chunk);  // every chunk non-empty
+    return p;
+}
+
+size_t xattn_partial_bytes(int64_t B, int64_t Hq, int splits) {
+    const size_t n = (size_t)B * Hq * splits;
+    return n * sizeof(float2) + n * kHeadDim * sizeof(float);
+}
+
+hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, bf16_t *out, int B, int Hq,
+                        int Hkv, int L, float scale, const XattnPlan &plan, void *partials, hipStream_t stream) {
+    const size_t n = (size_t)B * Hq * plan.splits;
+    float2 *ml = reinterpret_cast<float2 *>(partials);
+    float *po = reinterpret_cast<float *>(reinterpret_cast<char *>(partials) + n * sizeof(float2));
+    const dim3 grid(plan.splits, Hkv, B);
+    const float qscale = scale * kLog2e;
+    if (q_f32)
+        hipLaunchKernelGGL(xattn_split_kernel<true>, grid, dim3(kThreads), 0, stream, q, K, V, ml, po, Hq, Hkv, L,
+                           plan.chunk, plan.splits, qscale);
+    else
+        hipLaunchKernelGGL(xattn_split_kernel<false>, grid, dim3(kThreads), 0, stream, q, K, V, ml, po, Hq, Hkv, L,
+                           plan.chunk, plan.splits, qscale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(xattn_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kHeadDim), 0, stream, ml, po, out,
+                       plan.splits);
+    return hipGetLastError();
+}
+
+}  // namespace sambay

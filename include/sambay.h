@@ -1,0 +1,140 @@
+/*
+ * sambay.h — C ABI of the SambaY cross-decoder decode-path library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (web pages about "Decoder-Hybrid-Decoder Architecture for
+ * Efficient Reasoning with Long Generation"; the Paper-Notes reading-notes
+ * page is cited as [Notes], the authors' abstract as [Abstract]):
+ *   - the cross-decoder, the second half of the layers, alternates
+ *     cross-attention layers over the single KV cache written once by the
+ *     self-decoder's final full-attention layer, and Gated Memory Units that
+ *     reuse the memory readout M of the self-decoder's last SSM layer
+ *     ([Notes] section 整体框架);
+ *   - GMU: Y = (M ⊙ SiLU(X W1^T)) W2, SiLU(z) = z·sigmoid(z)
+ *     ([Notes] section 关键设计);
+ *   - at decode time a cross-attention layer reads the whole cache, O(d_kv·N)
+ *     bytes, while a GMU reads state whose size does not depend on N
+ *     ([Notes] sections 现有痛点 and 关键设计);
+ *   - no positional encoding is applied ([Notes] section 关键发现, [Abstract]).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, dense and
+ *     row-major, with a base address aligned to 16 bytes.  The library never
+ *     retains a pointer after the call returns.
+ *   - `workspace` is caller-owned device memory of at least the size the
+ *     matching *_workspace_bytes() query returns, aligned to 256 bytes; its
+ *     contents on entry are irrelevant and are clobbered.
+ *   - Calls only enqueue kernels on `stream` (0 = the null stream).  They never
+ *     allocate, free or synchronise.  Results are ready when `stream` is.
+ *   - All arguments are validated before anything is enqueued: on any
+ *     non-SB_OK status nothing was launched and sb_last_error() describes the
+ *     problem.  A zero batch (rows == 0, B == 0) is a successful no-op.
+ *   - Device faults inside a kernel are asynchronous: they surface at the
+ *     caller's next synchronisation on the stream, not as a status here.
+ *   - bf16 values are IEEE binary32 values truncated to their top 16 bits
+ *     (bfloat16); every conversion to bf16 rounds to nearest, ties to even.
+ *   - Entry points may be called from several host threads; sb_last_error()
+ *     is per thread.  Calls that overlap on one device share nothing.
+ */
+#ifndef SAMBAY_H
+#define SAMBAY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SB_OK = 0,
+    SB_EINVAL = 1,        /* null pointer, negative or inconsistent size, misaligned or aliased buffer */
+    SB_EUNSUPPORTED = 2,  /* a valid request outside what the kernels implement (see each call) */
+    SB_EWORKSPACE = 3,    /* workspace null or smaller than the matching query returns */
+    SB_EHIP = 4           /* the HIP runtime reported an error while enqueuing */
+} sb_status;
+
+typedef enum { SB_F32 = 0, SB_BF16 = 1 } sb_dtype;
+
+typedef enum { SB_LAYER_XATTN = 0, SB_LAYER_GMU = 1 } sb_layer_kind;
+
+/* One cross-decoder layer.  kind SB_LAYER_XATTN: w_a = Wq, w_b = Wo, both
+ * [d_model, d_model] bf16 (q = h Wq^T, branch = o Wo^T).  kind SB_LAYER_GMU:
+ * w_a = W1 [d_inner, d_model], w_b = W2 [d_model, d_inner], bf16. */
+typedef struct {
+    int32_t kind;       /* an sb_layer_kind value */
+    const void *w_a;
+    const void *w_b;
+} sb_layer;
+
+/* Text describing the last non-SB_OK status returned on this thread ("" if none). */
+const char *sb_last_error(void);
+
+/* Library version string. */
+const char *sb_version(void);
+
+/* ------------------------------------------------------------------ GMU --
+ * Gated Memory Unit, [Notes] section 关键设计:
+ *   Y[rows, d_model] = (M[rows, d_inner] ⊙ SiLU(X[rows, d_model] · W1^T)) · W2^T
+ * with W1 [d_inner, d_model] and W2 [d_model, d_inner] (linear-layer layout:
+ * the page's "· W2" with W2 stored transposed).  rows = batch·tokens for
+ * prefill, or batch for one decode step (one new token per sequence).  M is
+ * the memory readout of the earlier token-mixing layer, one row per token.
+ * All five tensors share `dt`:
+ *   SB_BF16: products accumulate in fp32; the gated hidden H = M ⊙ SiLU(·) is
+ *            rounded to bf16 before the second product; Y is stored as bf16.
+ *   SB_F32 : everything in fp32.
+ * Y must not overlap any input.  Errors: SB_EINVAL (null pointer, negative
+ * size, d_model or d_inner == 0 with rows > 0, overlap, misalignment),
+ * SB_EUNSUPPORTED (bf16 with d_model or d_inner not a multiple of 64),
+ * SB_EWORKSPACE, SB_EHIP. */
+size_t gmu_workspace_bytes(int64_t rows, int64_t d_model, int64_t d_inner, sb_dtype dt);
+sb_status gmu_forward(const void *M, const void *X, const void *W1, const void *W2, void *Y, int64_t rows,
+                      int64_t d_model, int64_t d_inner, sb_dtype dt, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* ------------------------------------------------------ cross-attention --
+ * Decode-time attention of one new token per sequence over the single shared
+ * KV cache ([Notes] sections 整体框架 and 现有痛点), no positional encoding:
+ *   out[b, h, :] = Σ_j softmax_j(scale · q[b, h, :] · K[b, g, j, :]) · V[b, g, j, :]
+ * over all L cached positions j, with g = h / (Hq / Hkv) (grouped-query
+ * heads, contiguous groups).  q, out: [B, Hq, D]; kcache, vcache: [B, Hkv, L, D];
+ * all bf16; logits, softmax and the weighted sum run in fp32 (q is scaled and
+ * split into two bf16 parts so that q·k keeps ~16 significant bits).
+ * Computed as split-K flash decoding: the L positions are cut into chunks whose
+ * (max, sum, weighted sum) partials are merged by log-sum-exp, an exact
+ * rewriting of the softmax.
+ * Errors: SB_EINVAL (null pointer, negative size, L == 0 with B > 0,
+ * Hq % Hkv != 0, out overlapping an input, misalignment), SB_EUNSUPPORTED
+ * (D != 128, Hq / Hkv > 16, L >= 2^31), SB_EWORKSPACE, SB_EHIP. */
+size_t xattn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L);
+sb_status xattn_decode(const void *q, const void *kcache, const void *vcache, void *out, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t D, int64_t L, float scale, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* ---------------------------------------------------- cross-decoder step --
+ * One decode step of the cross-decoder ([Notes] section 整体框架): for each
+ * layer in array order, a residual branch on the bf16 stream h [B, d_model]:
+ *   SB_LAYER_XATTN: q = h Wq^T (fp32, not rounded), o = attention of q over
+ *                   the shared kcache/vcache [B, Hkv, L, D] (as xattn_decode,
+ *                   o rounded to bf16), h = bf16(h + o Wo^T);
+ *   SB_LAYER_GMU:   h = bf16(h + GMU(M, h, W1, W2)) with the one memory
+ *                   readout M [B, d_inner] shared by every GMU layer.
+ * h is updated in place.  Requires Hq·D == d_model.  All tensors bf16.
+ * Errors: as gmu_forward and xattn_decode, plus SB_EINVAL for a null layer
+ * array with n_layers > 0, a null layer weight, an unknown kind, or
+ * Hq·D != d_model. */
+size_t crossdecoder_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inner, int64_t Hq, int64_t Hkv, int64_t D,
+                                    int64_t L);
+sb_status crossdecoder_step(void *h, const void *M, const void *kcache, const void *vcache, const sb_layer *layers,
+                            int32_t n_layers, int64_t B, int64_t d_model, int64_t d_inner, int64_t Hq, int64_t Hkv,
+                            int64_t D, int64_t L, float scale, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAMBAY_H */

@@ -1,0 +1,171 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every function include/sambay.h declares, and
+reject every invalid argument with the documented status before touching the
+device.  Fake device addresses are used only on paths that fail validation,
+so nothing is dereferenced or enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sambay.h")
+
+
+@pytest.fixture(scope="module")
+def sb():
+    path = os.path.join(ROOT, "attention_decoding_amd", "libsambay.so")
+    if not os.path.exists(path):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("sambay_build", os.path.join(ROOT, "attention_decoding_amd",
+                                                                                   "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    import attention_decoding_amd as sb
+    return sb
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared_functions()
+    for n in ("gmu_forward", "xattn_decode", "crossdecoder_step", "gmu_workspace_bytes", "xattn_workspace_bytes",
+              "crossdecoder_workspace_bytes", "sb_last_error", "sb_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(sb):
+    raw = ctypes.CDLL(sb.LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(raw, n), "symbol %s declared in sambay.h but not exported" % n
+    assert sorted(sb.EXPORTS) == _declared_functions()
+
+
+def test_version(sb):
+    assert "gfx950" in sb.version()
+
+
+A = 1 << 20  # fake, 16-byte aligned device addresses (never dereferenced)
+
+
+def _addr(i):
+    return A * (i + 1)
+
+
+def _gmu(sb, M=_addr(0), X=_addr(1), W1=_addr(2), W2=_addr(3), Y=_addr(4), rows=4, dm=64, di=128, dt=1,
+         ws=_addr(8), wsb=1 << 30):
+    return sb.lib.gmu_forward(M, X, W1, W2, Y, rows, dm, di, dt, ws, wsb, None)
+
+
+def test_gmu_validation(sb):
+    lib = sb.lib
+    assert _gmu(sb, rows=-1) == sb.SB_EINVAL
+    assert _gmu(sb, dm=-64) == sb.SB_EINVAL
+    assert _gmu(sb, dt=7) == sb.SB_EINVAL
+    assert _gmu(sb, M=None) == sb.SB_EINVAL
+    assert "null" in lib.sb_last_error().decode()
+    assert _gmu(sb, Y=None) == sb.SB_EINVAL
+    assert _gmu(sb, X=_addr(1) + 2) == sb.SB_EINVAL          # misaligned
+    assert _gmu(sb, dm=0) == sb.SB_EINVAL
+    assert _gmu(sb, Y=_addr(1)) == sb.SB_EINVAL              # Y aliases X
+    assert "overlap" in lib.sb_last_error().decode()
+    assert _gmu(sb, dm=96) == sb.SB_EUNSUPPORTED             # bf16 needs multiples of 64
+    assert _gmu(sb, di=100) == sb.SB_EUNSUPPORTED
+    assert _gmu(sb, ws=None) == sb.SB_EWORKSPACE
+    need = lib.gmu_workspace_bytes(4, 64, 128, 1)
+    assert need > 0
+    assert _gmu(sb, wsb=need - 1) == sb.SB_EWORKSPACE
+    assert _gmu(sb, ws=_addr(2), wsb=need) == sb.SB_EINVAL   # workspace overlaps W1
+    # rows == 0 is a successful no-op, even with null pointers.
+    assert _gmu(sb, rows=0, M=None, X=None) == sb.SB_OK
+    assert lib.sb_last_error().decode() == ""
+
+
+def test_gmu_workspace_sizes(sb):
+    lib = sb.lib
+    assert lib.gmu_workspace_bytes(0, 64, 128, 1) == 0
+    assert lib.gmu_workspace_bytes(64, 64, 128, 0) >= 64 * 128 * 4          # fp32 H
+    assert lib.gmu_workspace_bytes(8192, 2560, 5120, 1) >= 8192 * 5120 * 2  # bf16 H for prefill
+    assert lib.gmu_workspace_bytes(32, 3072, 6144, 1) >= 32 * 6144 * 2
+
+
+def _xa(sb, q=_addr(0), k=_addr(1) * 16, v=_addr(2) * 64, out=_addr(3), B=2, Hq=24, Hkv=8, D=128, L=300, scale=0.088,
+        ws=_addr(4) * 512, wsb=1 << 30):
+    return sb.lib.xattn_decode(q, k, v, out, B, Hq, Hkv, D, L, scale, ws, wsb, None)
+
+
+def test_xattn_validation(sb):
+    assert _xa(sb, B=-1) == sb.SB_EINVAL
+    assert _xa(sb, L=0) == sb.SB_EINVAL
+    assert _xa(sb, Hq=25) == sb.SB_EINVAL                     # Hq % Hkv != 0
+    assert _xa(sb, Hkv=0) == sb.SB_EINVAL
+    assert _xa(sb, D=64) == sb.SB_EUNSUPPORTED
+    assert _xa(sb, Hq=136, Hkv=8) == sb.SB_EUNSUPPORTED       # group of 17 heads
+    assert _xa(sb, L=1 << 31) == sb.SB_EUNSUPPORTED
+    assert _xa(sb, q=None) == sb.SB_EINVAL
+    assert _xa(sb, out=_addr(0)) == sb.SB_EINVAL              # out aliases q
+    assert _xa(sb, k=_addr(1) * 16 + 8) == sb.SB_EINVAL       # misaligned
+    assert _xa(sb, scale=float("nan")) == sb.SB_EINVAL
+    assert _xa(sb, scale=float("inf")) == sb.SB_EINVAL
+    assert _xa(sb, ws=None) == sb.SB_EWORKSPACE
+    need = sb.lib.xattn_workspace_bytes(2, 24, 8, 128, 300)
+    assert need > 0
+    assert _xa(sb, wsb=need - 1) == sb.SB_EWORKSPACE
+    assert _xa(sb, B=0, q=None, k=None) == sb.SB_OK
+
+
+def test_xattn_workspace_sizes(sb):
+    lib = sb.lib
+    assert lib.xattn_workspace_bytes(16, 24, 8, 128, 34816) >= 16 * 24 * (128 + 2) * 4
+    assert lib.xattn_workspace_bytes(16, 24, 8, 64, 34816) == 0
+    assert lib.xattn_workspace_bytes(0, 24, 8, 128, 34816) == 0
+
+
+def _step(sb, layers, n=None, h=_addr(0), M=_addr(1), k=_addr(2) * 16, v=_addr(3) * 64, B=2, dm=3072, di=6144, Hq=24,
+          Hkv=8, D=128, L=300, ws=_addr(5) * 512, wsb=1 << 34):
+    arr = (sb.SbLayer * max(len(layers), 1))()
+    for i, (kind, wa, wb) in enumerate(layers):
+        arr[i].kind, arr[i].w_a, arr[i].w_b = kind, wa, wb
+    return sb.lib.crossdecoder_step(h, M, k, v, arr if layers is not None else None, len(layers) if n is None else n,
+                                    B, dm, di, Hq, Hkv, D, L, 0.088, ws, wsb, None)
+
+
+def test_crossdecoder_validation(sb):
+    W = [(0, _addr(9) * 1024, _addr(10) * 1024), (1, _addr(11) * 1024, _addr(12) * 1024)]
+    assert _step(sb, W, B=-1) == sb.SB_EINVAL
+    assert _step(sb, W, n=-1) == sb.SB_EINVAL
+    assert _step(sb, W, dm=3000) == sb.SB_EINVAL              # Hq*D != d_model
+    assert _step(sb, W, di=6000) == sb.SB_EUNSUPPORTED
+    assert _step(sb, W, D=64, dm=24 * 64) == sb.SB_EUNSUPPORTED
+    assert _step(sb, [(2, _addr(9) * 1024, _addr(10) * 1024)]) == sb.SB_EINVAL   # unknown kind
+    assert _step(sb, [(0, None, _addr(10) * 1024)]) == sb.SB_EINVAL              # null weight
+    assert _step(sb, [(1, _addr(9) * 1024 + 4, _addr(10) * 1024)]) == sb.SB_EINVAL  # misaligned weight
+    assert _step(sb, [(1, _addr(0), _addr(10) * 1024)]) == sb.SB_EINVAL          # weight overlaps h
+    assert _step(sb, W, h=None) == sb.SB_EINVAL
+    assert _step(sb, W, M=_addr(0)) == sb.SB_EINVAL           # h overlaps M
+    assert _step(sb, W, ws=None) == sb.SB_EWORKSPACE
+    need = sb.lib.crossdecoder_workspace_bytes(2, 3072, 6144, 24, 8, 128, 300)
+    assert need > 0
+    assert _step(sb, W, wsb=need - 1) == sb.SB_EWORKSPACE
+    assert _step(sb, W, B=0) == sb.SB_OK
+    assert _step(sb, [], n=0) == sb.SB_OK
+
+
+def test_python_binding_refuses_cpu_tensors(sb):
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        sb.gmu_forward(torch.zeros(4, 128, dtype=torch.bfloat16), x, torch.zeros(128, 64, dtype=torch.bfloat16),
+                       torch.zeros(64, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU"):
+        sb.xattn_decode(torch.zeros(1, 3, 128, dtype=torch.bfloat16), torch.zeros(1, 1, 5, 128, dtype=torch.bfloat16),
+                        torch.zeros(1, 1, 5, 128, dtype=torch.bfloat16))
