@@ -30,7 +30,9 @@ SB_LAYER_XATTN, SB_LAYER_GMU = 0, 1
 
 # Every function the header declares, for load-time checking.
 EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", "xattn_workspace_bytes",
-           "xattn_decode", "crossdecoder_workspace_bytes", "crossdecoder_step")
+           "xattn_decode", "crossdecoder_workspace_bytes", "crossdecoder_step", "sb_timing_enable",
+           "sb_timing_collect")
+SB_TIME_XATTN_SPLIT, SB_TIME_XATTN_MERGE, SB_TIME_SKINNY, SB_TIME_GEMM, SB_TIME_GMU_F32 = 1, 2, 4, 8, 16
 
 
 class SbLayer(ctypes.Structure):
@@ -45,7 +47,7 @@ class SambayError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libsambay.so not built at %s; run `python -m attention_decoding_amd.build`" % LIB_PATH)
+        raise ImportError("libsambay.so not built at %s; run `python attention_decoding_amd/build.py`" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     lib.sb_last_error.restype = ctypes.c_char_p
@@ -63,6 +65,10 @@ def _load() -> ctypes.CDLL:
     lib.crossdecoder_step.argtypes = [vp, vp, vp, vp, ctypes.POINTER(SbLayer), i32, i64, i64, i64, i64, i64, i64,
                                       i64, ctypes.c_float, vp, sz, vp]
     lib.crossdecoder_step.restype = ctypes.c_int
+    lib.sb_timing_enable.argtypes = [ctypes.c_uint32]
+    lib.sb_timing_enable.restype = ctypes.c_int
+    lib.sb_timing_collect.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+    lib.sb_timing_collect.restype = ctypes.c_int
     return lib
 
 
@@ -71,6 +77,19 @@ lib = _load()
 
 def version() -> str:
     return lib.sb_version().decode()
+
+
+def timing_enable(mask: int) -> None:
+    """Bracket later launches of the kernel kinds in `mask` (SB_TIME_* bits)
+    with HIP events on their own stream; 0 turns recording off."""
+    _check("sb_timing_enable", lib.sb_timing_enable(int(mask)))
+
+
+def timing_collect(mask: int):
+    """(launches, total milliseconds) of the recorded launches of `mask`; forgets them."""
+    n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check("sb_timing_collect", lib.sb_timing_collect(int(mask), ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)
 
 
 def _check(fn: str, status: int):
@@ -235,4 +254,4 @@ def crossdecoder_step(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor, vc
 
 
 __all__ = ["gmu_forward", "xattn_decode", "crossdecoder_step", "CrossDecoderStep", "SambayError", "version", "lib",
-           "EXPORTS", "LIB_PATH"]
+           "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect"]

@@ -1,6 +1,6 @@
 """Build libsambay.so (the gfx950 HIP library) in-tree with hipcc.
 
-    python -m attention_decoding_amd.build        # compile every csrc/*.hip, link
+    python attention_decoding_amd/build.py        # compile every csrc/*.hip, link
 
 Objects go to _build/ at the repository root; the shared library is written
 next to this file so that the Python binding (and a copy of the tree on a GPU

@@ -51,10 +51,8 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// Streaming read of data used once (KV cache, weights): non-temporal hint.
-__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
+// Data read once per call (KV cache, weights) uses plain loads too: the
+// non-temporal hint measured ~8% slower on the attention kernel.
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -146,6 +146,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t *__restrict
 hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
                        const bf16_t *aux, hipStream_t stream) {
     const int tiles = ((rows + BM - 1) / BM) * ((N + BN - 1) / BN);
+    TimingScope ts(kTimeGemm, stream);
     if (epi == EPI_GATE)
         hipLaunchKernelGGL(gemm_kernel<EPI_GATE>, dim3(tiles), dim3(kThreads), 0, stream, X, W, rows, N, K, out, aux);
     else

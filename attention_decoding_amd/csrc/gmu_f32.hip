@@ -43,6 +43,7 @@ __global__ __launch_bounds__(256) void gmu_f32_out_kernel(const float *__restric
 hipError_t launch_gmu_f32(const float *M, const float *X, const float *W1, const float *W2, float *Y, float *H,
                           int64_t rows, int64_t d_model, int64_t d_inner, hipStream_t stream) {
     const int64_t n1 = rows * d_inner, n2 = rows * d_model;
+    TimingScope ts(kTimeGmuF32, stream);
     hipLaunchKernelGGL(gmu_f32_gate_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, stream, M, X, W1, H,
                        rows, d_model, d_inner);
     hipError_t e = hipGetLastError();

@@ -10,6 +10,22 @@ namespace sambay {
 
 typedef uint16_t bf16_t;
 
+// Optional HIP-event bracket around one kernel launch (sb_timing_enable).
+class TimingScope {
+  public:
+    TimingScope(uint32_t kind, hipStream_t stream);
+    ~TimingScope();
+    TimingScope(const TimingScope &) = delete;
+    TimingScope &operator=(const TimingScope &) = delete;
+
+  private:
+    uint32_t kind_;
+    hipStream_t stream_;
+    hipEvent_t start_ = nullptr, stop_ = nullptr;
+    bool active_ = false;
+};
+constexpr uint32_t kTimeXattnSplit = 1, kTimeXattnMerge = 2, kTimeSkinny = 4, kTimeGemm = 8, kTimeGmuF32 = 16;
+
 // ------------------------------------------------------- cross-attention
 constexpr int kHeadDim = 128;     // supported head dimension
 constexpr int kMaxGroup = 16;     // query heads per KV head handled by one tile

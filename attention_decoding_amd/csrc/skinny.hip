@@ -11,8 +11,10 @@
 //    so every CU streams the same number of bytes.  Eight waves per
 //    workgroup split the K dimension in 64-wide chunks; their 16x16x32 MFMA
 //    partial tiles are summed through LDS in a fixed order (deterministic).
-//  * A operand = 16 weight rows (each lane streams 32 contiguous bytes of a
-//    row per chunk); B operand = 16 tokens of X (read from L2: X is small).
+//  * A operand = 16 weight rows; MFMA k-step t of a chunk covers 32
+//    contiguous K elements, lane group grp holding elements 8·grp .. 8·grp+7,
+//    so each load instruction reads 64 contiguous bytes of 16 rows.  B operand
+//    = 16 tokens of X with the same K assignment (X is small and L2-resident).
 //    Tokens are padded to 16 per tile; rows past the range are zero operands.
 //  * Epilogues are fused: fp32 store, bf16 store, the GMU gate
 //    H = M ⊙ SiLU(acc) stored as bf16, or the residual add h = bf16(h + acc).
@@ -22,6 +24,7 @@
 #include "launch.hpp"
 
 #include <math.h>
+#include <stdlib.h>
 
 namespace sambay {
 
@@ -71,11 +74,11 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
     for (int rt = 0; rt < RT; ++rt) {
         const int rl = 16 * rt + col;
         rvalid[rt] = rl < R && n0 + rl < N;
-        wrow[rt] = W + (size_t)(rvalid[rt] ? n0 + rl : 0) * K + kbeg + 16 * grp;
+        wrow[rt] = W + (size_t)(rvalid[rt] ? n0 + rl : 0) * K + kbeg + 8 * grp;
     }
     const bf16_t *xrow[TB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) xrow[tb] = X + (size_t)min(16 * tb + col, T - 1) * ldx + kbeg + 16 * grp;
+    for (int tb = 0; tb < TB; ++tb) xrow[tb] = X + (size_t)min(16 * tb + col, T - 1) * ldx + kbeg + 8 * grp;
 
     f32x4 acc[RT][TB];
 #pragma unroll
@@ -83,22 +86,30 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    for (int c0 = wave * U; c0 < nchunks; c0 += kWaves * U) {
+    // Wave w owns chunks w, w + kWaves, w + 2·kWaves, ... (balanced); it keeps U
+    // of them in flight: all weight loads of a group are issued before any MFMA.
+    for (int j0 = 0; wave + kWaves * j0 < nchunks; j0 += U) {
         u32x4 wf[U][RT][2], xf[U][TB][2];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k = (c0 + u) * kChunk;
-            const bool live = c0 + u < nchunks;
+            const int c = wave + kWaves * (j0 + u);
+            const bool live = c < nchunks;
+            const int k = c * kChunk;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
-                    wf[u][rt][t] = (live && rvalid[rt]) ? ld16_stream(wrow[rt] + k + 8 * t) : (u32x4){0u, 0u, 0u, 0u};
+                    wf[u][rt][t] = (live && rvalid[rt]) ? ld16(wrow[rt] + k + 32 * t) : (u32x4){0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = wave + kWaves * (j0 + u);
+            const bool live = c < nchunks;
+            const int k = c * kChunk;
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    xf[u][tb][t] = live ? ld16(xrow[tb] + k + 8 * t) : (u32x4){0u, 0u, 0u, 0u};
+                for (int t = 0; t < 2; ++t) xf[u][tb][t] = live ? ld16(xrow[tb] + k + 32 * t) : (u32x4){0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -148,8 +159,10 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(const float *__restr
 template <int RT, int TB, int EPI>
 hipError_t launch3(const bf16_t *X, int ldx, const bf16_t *W, int T, int N, int K, void *out, int ldo,
                    const bf16_t *aux, int ldaux, const SkinnyPlan &p, float *partials, hipStream_t stream) {
-    constexpr int U = TB >= 4 ? 2 : 4;
+    // Chunks in flight per wave: operand registers U·8·(RT + TB) <= ~160.
+    constexpr int U = 20 / (RT + TB) < 1 ? 1 : 20 / (RT + TB);
     const dim3 grid((N + p.rows_per_wg - 1) / p.rows_per_wg, p.k_splits);
+    TimingScope ts(kTimeSkinny, stream);
     hipLaunchKernelGGL((skinny_kernel<RT, TB, U, EPI>), grid, dim3(kThreads), 0, stream, X, ldx, W, T, N, K,
                        p.rows_per_wg, p.k_slice, out, ldo, aux, ldaux, partials);
     hipError_t e = hipGetLastError();
@@ -182,14 +195,22 @@ hipError_t launch1(Epilogue epi, const bf16_t *X, int ldx, const bf16_t *W, int 
 }  // namespace
 
 SkinnyPlan skinny_plan(int T, int N, int K) {
-    (void)T;
+    // Every workgroup re-reads X[:, its K slice] from L2, T·K·2 bytes without a
+    // K split; splitting K across workgroups trades that for fp32 partials and
+    // a finishing launch.  Measured: a 2-way split pays off above 16 tokens.
+    int ks = T > 16 ? 2 : 1;
+    const char *e = getenv("SAMBAY_SKINNY_KSPLIT");
+    if (e && *e) ks = atoi(e);
+    if (ks < 1) ks = 1;
+    const int kc = K / kChunk;
+    while (ks > 1 && kc % ks != 0) --ks;
     SkinnyPlan p;
-    int R = (N + kTargetWGs - 1) / kTargetWGs;
+    int R = (int)(((int64_t)N * ks + kTargetWGs - 1) / kTargetWGs);
     if (R > 64) R = 64;
     if (R < 1) R = 1;
     p.rows_per_wg = R;
-    p.k_splits = 1;
-    p.k_slice = K;
+    p.k_splits = ks;
+    p.k_slice = K / ks;
     return p;
 }
 

@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the SambaY cross-decoder decode step on one MI355X.
+
+Workload (synthetic, seeded, shaped like the pages' 2K-prompt + 32K-generation
+decode): one step of a 16-layer cross-decoder — 8 cross-attention layers over
+the single shared KV cache alternating with 8 GMU layers — for B = 32
+sequences, d_model 3072, d_inner 6144, 24 query / 8 KV heads of 128, and
+34816 cached positions.  Every input is resident in HBM before timing.
+
+A step = refresh the residual stream h from the step's input (the token's
+self-decoder output) and run crossdecoder_step through the C ABI.  value =
+B / (seconds per step), in tokens/s.
+
+Also reported on the same JSON line:
+  roofline      the split-K attention kernel (the dominant one): algorithmic
+                bytes per launch (the KV cache it must read) / its mean launch
+                time, measured with HIP events on its own stream inside the
+                timed region; peak 8 TB/s; `traffic` = measured HBM bytes per
+                launch from the committed rocprofv3 counter summary when it
+                matches the current kernel source, else null.
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload
+                (a few whole sequences through all 16 layers), on the host.
+  kernels       per-kernel-kind times and rates from a short extra pass.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "cross-decoder decode tokens/s @34K ctx; GMU & XA achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "xattn_split_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "attention_decoding_amd", "csrc", f) for f in ("xattn.hip", "device.hpp")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def step_bytes(c) -> dict:
+    """Algorithmic HBM bytes of one step: what the method must read or write."""
+    B, dm, di, Hkv, D, L = c["B"], c["d_model"], c["d_inner"], c["Hkv"], c["D"], c["L"]
+    n_x = n_g = c["n_layers"] // 2
+    kv = B * Hkv * L * D * 2 * 2
+    xa_w, gmu_w = 2 * dm * dm * 2, 2 * dm * di * 2
+    xa_state, gmu_state = B * 2 * dm * 2, B * (dm + di + dm) * 2
+    return dict(kv=n_x * kv, kv_per_layer=kv, xattn_weights=n_x * xa_w, gmu_weights=n_g * gmu_w,
+                state=n_x * xa_state + n_g * gmu_state,
+                total=n_x * (kv + xa_w + xa_state) + n_g * (gmu_w + gmu_state))
+
+
+def traffic_for_current_kernel():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, c, n_seq: int):
+    import oracle
+
+    layers = [(k, a.cpu(), b.cpu()) for k, a, b in x.layers]
+    rows = slice(0, n_seq)
+    h, M, K, V = x.h[rows].cpu(), x.M[rows].cpu(), x.K[rows].cpu(), x.V[rows].cpu()
+    t0 = time.perf_counter()
+    oracle.crossdecoder(h, M, K, V, layers, c["Hq"])
+    dt = time.perf_counter() - t0
+    return {"value": n_seq / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "%d of %d sequences, one decode token each, through all %d layers at %d cached positions "
+                      "(fp64 oracle, sequences are independent); %.1f s" % (n_seq, c["B"], c["n_layers"], c["L"], dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle CPU sample")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for %d GPUs, world size %d)."
+              % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_decoding_amd as sb
+    import workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    c = dict(workload.CROSSDECODER)
+    log("bench: generating inputs (B=%d, L=%d, %d layers)" % (c["B"], c["L"], c["n_layers"]))
+    x = workload.crossdecoder_inputs(c["B"], c["d_model"], c["d_inner"], c["Hq"], c["Hkv"], c["D"], c["L"],
+                                     c["n_layers"], seed=0, device=dev)
+    h_in = x.h.clone()
+    step = sb.CrossDecoderStep(x.h, x.M, x.K, x.V, x.layers)
+    nbytes = step_bytes(c)
+
+    def run_step():
+        x.h.copy_(h_in)
+        step()
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    log("bench: warmup done, timing %d steps" % args.steps)
+
+    sb.timing_enable(sb.SB_TIME_XATTN_SPLIT)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        run_step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sb.timing_enable(0)
+    n_split, ms_split = sb.timing_collect(sb.SB_TIME_XATTN_SPLIT)
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = max(ms_step, 1e3 * wall / args.steps)
+    tokens_per_s = c["B"] / (ms_step / 1e3)
+    split_ms = ms_split / max(n_split, 1)
+    achieved = nbytes["kv_per_layer"] / (split_ms / 1e3) / 1e9
+    log("bench: %.3f ms/step, %.0f tokens/s; split kernel %.1f us/launch over %d launches" %
+        (ms_step, tokens_per_s, 1e3 * split_ms, n_split))
+
+    # Per-kernel breakdown on a few extra steps (not part of the timed value).
+    kinds = {"xattn_split": sb.SB_TIME_XATTN_SPLIT, "xattn_merge": sb.SB_TIME_XATTN_MERGE,
+             "skinny_products": sb.SB_TIME_SKINNY}
+    sb.timing_enable(sum(kinds.values()))
+    nb = 3
+    for _ in range(nb):
+        run_step()
+    torch.cuda.synchronize()
+    sb.timing_enable(0)
+    kern = {}
+    for name, bit in kinds.items():
+        n, ms = sb.timing_collect(bit)
+        kern[name] = {"launches_per_step": n // nb, "ms_per_step": round(ms / nb, 4)}
+    w_bytes = nbytes["xattn_weights"] + nbytes["gmu_weights"] + nbytes["state"]
+    sk = kern["skinny_products"]["ms_per_step"]
+    kern["skinny_products"]["gbps"] = round(w_bytes / (sk / 1e3) / 1e9, 1) if sk > 0 else None
+    kern["skinny_products"]["frac_of_peak"] = round(w_bytes / (sk / 1e3) / 1e9 / HBM_PEAK_GBS, 4) if sk > 0 else None
+    kern["xattn_split"]["gbps"] = round(nbytes["kv"] / (kern["xattn_split"]["ms_per_step"] / 1e3) / 1e9, 1)
+    kern["xattn_split"]["frac_of_peak"] = round(kern["xattn_split"]["gbps"] / HBM_PEAK_GBS, 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle on %d sequences" % args.cpu_seqs)
+        cpu = cpu_baseline(x, c, args.cpu_seqs)
+        log("bench: oracle %.3f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations and KV cache, N(0,0.02^2) weights)",
+        "config": {"workload": "cross-decoder decode step: 16 layers alternating cross-attention over one shared "
+                               "KV cache and GMU, one new token per sequence",
+                   "batch": c["B"], "layers": c["n_layers"], "layer_order": "xattn,gmu,...", "d_model": c["d_model"],
+                   "d_inner": c["d_inner"], "q_heads": c["Hq"], "kv_heads": c["Hkv"], "head_dim": c["D"],
+                   "kv_len": c["L"]},
+        "hbm_bytes_per_step": nbytes["total"],
+        "step_gbps": round(nbytes["total"] / (ms_step / 1e3) / 1e9, 1),
+        "step_frac_of_hbm_peak": round(nbytes["total"] / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"kernel": "xattn_split_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": nbytes["kv_per_layer"], "us_per_launch": round(1e3 * split_ms, 2),
+                     "traffic": traffic_for_current_kernel()},
+        "kernels": kern,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -133,6 +133,25 @@ sb_status crossdecoder_step(void *h, const void *M, const void *kcache, const vo
                             int64_t D, int64_t L, float scale, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/* ------------------------------------------------ benchmark instrumentation --
+ * For measuring kernels inside the calls above (benchmarks and profiling
+ * only; not meant for production loops).  While a kind's bit is enabled,
+ * every launch of that kernel kind is bracketed by a pair of HIP events
+ * recorded on the stream the kernel is launched on.  sb_timing_collect waits
+ * for the recorded events of the kinds in `mask`, returns the number of
+ * launches and their summed duration in milliseconds, and forgets them.
+ * These two calls may synchronise on the recorded events.  Errors: SB_EHIP. */
+typedef enum {
+    SB_TIME_XATTN_SPLIT = 1,   /* split-K attention partial kernel */
+    SB_TIME_XATTN_MERGE = 2,   /* log-sum-exp merge kernel */
+    SB_TIME_SKINNY = 4,        /* decode weight-streaming products (GMU, Wq, Wo) */
+    SB_TIME_GEMM = 8,          /* prefill MFMA GEMM */
+    SB_TIME_GMU_F32 = 16       /* fp32 GMU kernels */
+} sb_timing_kind;
+
+sb_status sb_timing_enable(uint32_t mask);
+sb_status sb_timing_collect(uint32_t mask, int64_t *launches, double *total_ms);
+
 #ifdef __cplusplus
 }
 #endif
