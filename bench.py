@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle CPU sample")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes 5 times (reference for HBM counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -115,6 +117,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * 1e6) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": 4 * n, "launches": 5}), flush=True)
+        return
     c = dict(workload.CROSSDECODER)
     log("bench: generating inputs (B=%d, L=%d, %d layers)" % (c["B"], c["L"], c["n_layers"]))
     x = workload.crossdecoder_inputs(c["B"], c["d_model"], c["d_inner"], c["Hq"], c["Hkv"], c["D"], c["L"],
