@@ -91,6 +91,67 @@ def cpu_baseline(x, c, n_seq: int):
                       "(fp64 oracle, sequences are independent); %.1f s" % (n_seq, c["B"], c["n_layers"], c["L"], dt)}
 
 
+def time_calls(fn, n: int, warmup: int = 3) -> float:
+    """Mean milliseconds per call of fn() over n calls (HIP events on the current stream)."""
+    import torch
+
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def other_workloads(sb, workload, dev) -> dict:
+    """Kernel-level rates of the other workloads (not part of `value`)."""
+    import torch
+
+    res = {}
+    # GMU prefill: 4 x 2048 rows, 2560 -> 5120 -> 2560.
+    c = workload.GMU_PREFILL
+    rows = c["batch"] * c["seq"]
+    g = workload.gmu_inputs(rows, c["d_model"], c["d_inner"], seed=1, device=dev)
+    Y = torch.empty(rows, c["d_model"], dtype=torch.bfloat16, device=dev)
+    ms = time_calls(lambda i: sb.gmu_forward(g.M, g.X, g.W1, g.W2, out=Y), 20)
+    flops = 4.0 * rows * c["d_model"] * c["d_inner"]
+    res["gmu_prefill_8192x2560x5120"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                                         "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4)}
+    del g, Y
+    # GMU decode: B in {1, 8, 32, 64}, 3072 -> 6144 -> 3072, 8 rotating weight sets (604 MB).
+    c = workload.GMU_DECODE
+    sets = [workload.gmu_inputs(1, c["d_model"], c["d_inner"], seed=2, device=dev, weight_set=k) for k in range(8)]
+    for B in c["batches"]:
+        gi = workload.gmu_inputs(B, c["d_model"], c["d_inner"], seed=3 + B, device=dev)
+        Y = torch.empty(B, c["d_model"], dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda i: sb.gmu_forward(gi.M, gi.X, sets[i % 8].W1, sets[i % 8].W2, out=Y), 64)
+        sb.timing_enable(sb.SB_TIME_SKINNY)
+        time_calls(lambda i: sb.gmu_forward(gi.M, gi.X, sets[i % 8].W1, sets[i % 8].W2, out=Y), 64, warmup=0)
+        sb.timing_enable(0)
+        n, kms = sb.timing_collect(sb.SB_TIME_SKINNY)
+        nbytes = 2 * c["d_model"] * c["d_inner"] * 2 + B * (2 * c["d_model"] + c["d_inner"]) * 2
+        kus = 1e3 * kms / 64
+        res["gmu_decode_B%d" % B] = {"us_per_call": round(1e3 * ms, 2), "us_kernels": round(kus, 2),
+                                     "gbps_kernels": round(nbytes / kus / 1e3, 1),
+                                     "frac_of_hbm_peak": round(nbytes / kus / 1e3 / HBM_PEAK_GBS, 4)}
+    del sets
+    # Attention alone: 16 x 24 q heads, 8 KV heads, 34816 positions.
+    c = workload.XATTN_DECODE
+    x = workload.xattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["L"], seed=4, device=dev)
+    out = torch.empty(c["B"], c["Hq"], c["D"], dtype=torch.bfloat16, device=dev)
+    ms = time_calls(lambda i: sb.xattn_decode(x.q, x.K, x.V, out=out), 20)
+    nbytes = c["B"] * c["Hkv"] * c["L"] * c["D"] * 4
+    res["xattn_decode_B16_L34816"] = {"us_per_call": round(1e3 * ms, 1), "gbps": round(nbytes / ms / 1e6, 1),
+                                      "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del x
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +159,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle CPU sample")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the other workloads (GMU prefill, GMU decode per batch, attention alone)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 5 times (reference for HBM counters) and exit")
     args = ap.parse_args()
@@ -183,6 +246,12 @@ def main():
     kern["xattn_split"]["gbps"] = round(nbytes["kv"] / (kern["xattn_split"]["ms_per_step"] / 1e3) / 1e9, 1)
     kern["xattn_split"]["frac_of_peak"] = round(kern["xattn_split"]["gbps"] / HBM_PEAK_GBS, 4)
 
+    workloads = None
+    if args.all:
+        log("bench: timing the other workloads")
+        del step
+        workloads = other_workloads(sb, workload, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on %d sequences" % args.cpu_seqs)
@@ -217,6 +286,8 @@ def main():
         "kernels": kern,
         "cpu_baseline": cpu,
     }
+    if workloads is not None:
+        out["workloads"] = workloads
     print(json.dumps(out), flush=True)
 
 
