@@ -70,9 +70,10 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;
 size_t gmu_ws(int64_t rows, int64_t d_model, int64_t d_inner, sb_dtype dt) {
     if (rows <= 0 || d_model <= 0 || d_inner <= 0) return 0;
     if (dt == SB_F32) return round_up((size_t)rows * d_inner * sizeof(float));
-    // bf16 H [rows, d_inner]; decode also needs room for k-split partials.
+    // bf16 H [rows, d_inner] (decode: a hi + lo pair, plus room for k-split partials).
     size_t bytes = round_up((size_t)rows * d_inner * sizeof(bf16_t));
     if (rows <= kSkinnyMaxTokens) {
+        bytes *= 2;
         const SkinnyPlan p1 = skinny_plan((int)rows, (int)d_inner, (int)d_model);
         const SkinnyPlan p2 = skinny_plan((int)rows, (int)d_model, (int)d_inner);
         size_t part = skinny_partial_bytes((int)rows, (int)d_inner, p1);
@@ -83,19 +84,30 @@ size_t gmu_ws(int64_t rows, int64_t d_model, int64_t d_inner, sb_dtype dt) {
     return bytes;
 }
 
-// bf16 GMU on rows <= 64 tokens (decode): two weight-streaming launches.
+// bf16 GMU on rows <= 64 tokens (decode): two weight-streaming launches.  With
+// h_lo the gated hidden H travels as a bf16 hi + lo pair between them (used in
+// the layer stack, where rounding errors compound; a single call's error is
+// dominated by its bf16 output, and the pair costs up to ~20% at 64 rows).
 hipError_t gmu_decode_bf16(const bf16_t *M, const bf16_t *X, int ldx, const bf16_t *W1, const bf16_t *W2, void *Y,
-                           Epilogue out_epi, int T, int d_model, int d_inner, Carver &ws, hipStream_t stream) {
+                           Epilogue out_epi, int T, int d_model, int d_inner, bool h_lo, Carver &ws,
+                           hipStream_t stream) {
     bf16_t *H = static_cast<bf16_t *>(ws.take((size_t)T * d_inner * sizeof(bf16_t)));
+    bf16_t *H_lo = static_cast<bf16_t *>(ws.take((size_t)T * d_inner * sizeof(bf16_t)));
+    if (!h_lo) H_lo = nullptr;
     const SkinnyPlan p1 = skinny_plan(T, d_inner, d_model);
     const SkinnyPlan p2 = skinny_plan(T, d_model, d_inner);
     size_t part = skinny_partial_bytes(T, d_inner, p1);
     if (skinny_partial_bytes(T, d_model, p2) > part) part = skinny_partial_bytes(T, d_model, p2);
     float *partials = static_cast<float *>(ws.take(part));
-    hipError_t e = launch_skinny(X, ldx, W1, T, d_inner, d_model, EPI_GATE, H, d_inner, M, d_inner, p1, partials,
-                                 stream);
+    SkinnyArgs a1;
+    a1.X = X; a1.ldx = ldx; a1.W = W1; a1.T = T; a1.N = d_inner; a1.K = d_model; a1.epi = EPI_GATE;
+    a1.out = H; a1.ldo = d_inner; a1.out_lo = H_lo; a1.aux = M; a1.ldaux = d_inner;
+    hipError_t e = launch_skinny(a1, p1, partials, stream);
     if (e != hipSuccess) return e;
-    return launch_skinny(H, d_inner, W2, T, d_model, d_inner, out_epi, Y, d_model, nullptr, 0, p2, partials, stream);
+    SkinnyArgs a2;
+    a2.X = H; a2.X_lo = H_lo; a2.ldx = d_inner; a2.W = W2; a2.T = T; a2.N = d_model; a2.K = d_inner;
+    a2.epi = out_epi; a2.out = Y; a2.ldo = d_model;
+    return launch_skinny(a2, p2, partials, stream);
 }
 
 // ------------------------------------------------------- cross-attention
@@ -169,7 +181,7 @@ extern "C" sb_status gmu_forward(const void *M, const void *X, const void *W1, c
                            rows, d_model, d_inner, stream);
     } else if (rows <= kSkinnyMaxTokens) {
         e = gmu_decode_bf16((const bf16_t *)M, (const bf16_t *)X, (int)d_model, (const bf16_t *)W1,
-                            (const bf16_t *)W2, Y, EPI_BF16, (int)rows, (int)d_model, (int)d_inner, ws, stream);
+                            (const bf16_t *)W2, Y, EPI_BF16, (int)rows, (int)d_model, (int)d_inner, false, ws, stream);
     } else {
         bf16_t *H = static_cast<bf16_t *>(ws.take((size_t)rows * d_inner * sizeof(bf16_t)));
         e = launch_gemm((const bf16_t *)X, (const bf16_t *)W1, (int)rows, (int)d_inner, (int)d_model, EPI_GATE, H,
@@ -214,8 +226,8 @@ extern "C" sb_status xattn_decode(const void *q, const void *kcache, const void 
         if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
 
     const XattnPlan plan = xattn_plan(B, Hkv, L);
-    hipError_t e = launch_xattn(q, false, (const bf16_t *)kcache, (const bf16_t *)vcache, (bf16_t *)out, (int)B,
-                                (int)Hq, (int)Hkv, (int)L, scale, plan, workspace, stream);
+    hipError_t e = launch_xattn(q, false, (const bf16_t *)kcache, (const bf16_t *)vcache, (bf16_t *)out, nullptr,
+                                (int)B, (int)Hq, (int)Hkv, (int)L, scale, plan, workspace, stream);
     if (e != hipSuccess) return hip_fail("xattn_decode launch", e);
     return ok();
 }
@@ -224,14 +236,14 @@ namespace {
 
 // Workspace layout of one cross-decoder step (all reused layer to layer).
 struct StepLayout {
-    size_t q, o, gmu, partials, total;
+    size_t q, o, gmu, partials, total;  // o holds the bf16 hi + lo pair of the attention output
 };
 
 StepLayout step_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t Hq, int64_t Hkv, int64_t L) {
     StepLayout s;
     const int64_t T = B < kSkinnyMaxTokens ? B : kSkinnyMaxTokens;  // token group processed per product
     s.q = round_up((size_t)B * d_model * sizeof(float));
-    s.o = round_up((size_t)B * d_model * sizeof(bf16_t));
+    s.o = 2 * round_up((size_t)B * d_model * sizeof(bf16_t));
     // GMU: H for one token group plus k-split partials; projections share the partial space.
     size_t part = 0;
     const SkinnyPlan pa = skinny_plan((int)T, (int)d_inner, (int)d_model);
@@ -241,7 +253,7 @@ StepLayout step_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t Hq, 
                             skinny_partial_bytes((int)T, (int)d_model, pq)};
     for (size_t c : cands)
         if (c > part) part = c;
-    s.gmu = round_up((size_t)T * d_inner * sizeof(bf16_t)) + round_up(part);
+    s.gmu = 2 * round_up((size_t)T * d_inner * sizeof(bf16_t)) + round_up(part);
     s.partials = round_up(xattn_partial_bytes(B, Hq, xattn_plan(B, Hkv, L).splits));
     s.total = s.q + s.o + s.gmu + s.partials;
     return s;
@@ -307,6 +319,7 @@ extern "C" sb_status crossdecoder_step(void *h, const void *M, const void *kcach
     char *base = static_cast<char *>(workspace);
     float *q = reinterpret_cast<float *>(base);
     bf16_t *o = reinterpret_cast<bf16_t *>(base + lay.q);
+    bf16_t *o_lo = reinterpret_cast<bf16_t *>(base + lay.q + lay.o / 2);
     char *gmu_ws_base = base + lay.q + lay.o;
     void *partials = base + lay.q + lay.o + lay.gmu;
     const XattnPlan plan = xattn_plan(B, Hkv, L);
@@ -317,29 +330,33 @@ extern "C" sb_status crossdecoder_step(void *h, const void *M, const void *kcach
         const sb_layer &ly = layers[li];
         hipError_t e = hipSuccess;
         if (ly.kind == SB_LAYER_XATTN) {
+            // Projection partials share the GMU region's partial space (after the H pair).
+            const int64_t Tm = B < kSkinnyMaxTokens ? B : kSkinnyMaxTokens;
+            float *proj_partials =
+                reinterpret_cast<float *>(gmu_ws_base + 2 * round_up((size_t)Tm * di * sizeof(bf16_t)));
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
-                const SkinnyPlan pq = skinny_plan(T, dm, dm);
-                e = launch_skinny(hb + t0 * dm, dm, (const bf16_t *)ly.w_a, T, dm, dm, EPI_F32, q + t0 * dm, dm,
-                                  nullptr, 0, pq, reinterpret_cast<float *>(gmu_ws_base + round_up((size_t)T * di * 2)),
-                                  stream);
+                SkinnyArgs aq;
+                aq.X = hb + t0 * dm; aq.ldx = dm; aq.W = (const bf16_t *)ly.w_a; aq.T = T; aq.N = dm; aq.K = dm;
+                aq.epi = EPI_F32; aq.out = q + t0 * dm; aq.ldo = dm;
+                e = launch_skinny(aq, skinny_plan(T, dm, dm), proj_partials, stream);
             }
             if (e == hipSuccess)
-                e = launch_xattn(q, true, (const bf16_t *)kcache, (const bf16_t *)vcache, o, (int)B, (int)Hq,
+                e = launch_xattn(q, true, (const bf16_t *)kcache, (const bf16_t *)vcache, o, o_lo, (int)B, (int)Hq,
                                  (int)Hkv, (int)L, scale, plan, partials, stream);
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
-                const SkinnyPlan po = skinny_plan(T, dm, dm);
-                e = launch_skinny(o + t0 * dm, dm, (const bf16_t *)ly.w_b, T, dm, dm, EPI_RESID, hb + t0 * dm, dm,
-                                  nullptr, 0, po, reinterpret_cast<float *>(gmu_ws_base + round_up((size_t)T * di * 2)),
-                                  stream);
+                SkinnyArgs ao;
+                ao.X = o + t0 * dm; ao.X_lo = o_lo + t0 * dm; ao.ldx = dm; ao.W = (const bf16_t *)ly.w_b; ao.T = T;
+                ao.N = dm; ao.K = dm; ao.epi = EPI_RESID; ao.out = hb + t0 * dm; ao.ldo = dm;
+                e = launch_skinny(ao, skinny_plan(T, dm, dm), proj_partials, stream);
             }
         } else {
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
                 Carver ws{gmu_ws_base};
                 e = gmu_decode_bf16((const bf16_t *)M + t0 * di, hb + t0 * dm, dm, (const bf16_t *)ly.w_a,
-                                    (const bf16_t *)ly.w_b, hb + t0 * dm, EPI_RESID, T, dm, di, ws, stream);
+                                    (const bf16_t *)ly.w_b, hb + t0 * dm, EPI_RESID, T, dm, di, true, ws, stream);
             }
         }
         if (e != hipSuccess) return hip_fail("crossdecoder_step launch", e);

@@ -40,9 +40,11 @@ struct XattnPlan {
 XattnPlan xattn_plan(int64_t B, int64_t Hkv, int64_t L);
 // Bytes of fp32 partials for `splits` chunks: (max, sum) pairs then D-wide sums.
 size_t xattn_partial_bytes(int64_t B, int64_t Hq, int splits);
-// q is fp32 ([B, Hq, D]) when q_f32, else bf16.  out: bf16 [B, Hq, D].
-hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, bf16_t *out, int B, int Hq,
-                        int Hkv, int L, float scale, const XattnPlan &plan, void *partials, hipStream_t stream);
+// q is fp32 ([B, Hq, D]) when q_f32, else bf16.  out: bf16 [B, Hq, D]; out_lo
+// (nullable) receives bf16(o - out), the low part of a bf16 hi + lo pair.
+hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, bf16_t *out, bf16_t *out_lo,
+                        int B, int Hq, int Hkv, int L, float scale, const XattnPlan &plan, void *partials,
+                        hipStream_t stream);
 
 // ------------------------------------------------ skinny (decode) products
 // out[t, n] = epi( Σ_k X[t, k] · W[n, k] ) for t < T <= 64 tokens.
@@ -61,9 +63,21 @@ struct SkinnyPlan {
 };
 SkinnyPlan skinny_plan(int T, int N, int K);
 size_t skinny_partial_bytes(int T, int N, const SkinnyPlan &p);
-hipError_t launch_skinny(const bf16_t *X, int ldx, const bf16_t *W, int T, int N, int K, Epilogue epi, void *out,
-                         int ldo, const bf16_t *aux, int ldaux, const SkinnyPlan &plan, float *partials,
-                         hipStream_t stream);
+
+struct SkinnyArgs {
+    const bf16_t *X = nullptr;     // [T, ldx] bf16
+    const bf16_t *X_lo = nullptr;  // optional low part: the product uses X + X_lo (a bf16 hi + lo pair)
+    int ldx = 0;
+    const bf16_t *W = nullptr;     // [N, K] bf16
+    int T = 0, N = 0, K = 0;
+    Epilogue epi = EPI_F32;
+    void *out = nullptr;           // [T, ldo]
+    int ldo = 0;
+    bf16_t *out_lo = nullptr;      // EPI_GATE only, optional: bf16(value - out)
+    const bf16_t *aux = nullptr;   // EPI_GATE: M [T, ldaux]
+    int ldaux = 0;
+};
+hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *partials, hipStream_t stream);
 
 // ------------------------------------------------------- prefill product
 // out[r, n] = epi( Σ_k X[r, k] · W[n, k] ), any row count, N % 64 == 0, K % 64 == 0.

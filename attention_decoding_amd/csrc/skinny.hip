@@ -11,13 +11,18 @@
 //    so every CU streams the same number of bytes.  Eight waves per
 //    workgroup split the K dimension in 64-wide chunks; their 16x16x32 MFMA
 //    partial tiles are summed through LDS in a fixed order (deterministic).
+//    For comparison, a plain 37.7 MB HBM read kernel takes ~7.2 us per
+//    launch back to back on MI355X; one GMU product here takes ~10-11 us.
 //  * A operand = 16 weight rows; MFMA k-step t of a chunk covers 32
 //    contiguous K elements, lane group grp holding elements 8·grp .. 8·grp+7,
 //    so each load instruction reads 64 contiguous bytes of 16 rows.  B operand
 //    = 16 tokens of X with the same K assignment (X is small and L2-resident).
 //    Tokens are padded to 16 per tile; rows past the range are zero operands.
 //  * Epilogues are fused: fp32 store, bf16 store, the GMU gate
-//    H = M ⊙ SiLU(acc) stored as bf16, or the residual add h = bf16(h + acc).
+//    H = M ⊙ SiLU(acc) stored as a bf16 hi + lo pair, or the residual add
+//    h = bf16(h + acc).  An X given as a hi + lo pair (the gated H, the
+//    attention output o) is multiplied as two MFMAs per operand, so rounding
+//    the intermediate to bf16 costs ~16 significant bits instead of 8.
 //  * For shapes whose row ranges would be too thin, K is also split across
 //    workgroups; fp32 partials then go through a small finishing kernel.
 #include "device.hpp"
@@ -36,8 +41,8 @@ constexpr int kChunk = 64;      // K per wave step: two MFMA k-steps
 constexpr int kTargetWGs = 256;
 
 template <int EPI>
-__device__ __forceinline__ void apply_epilogue(float v, int t, int n, void *out, int ldo, const bf16_t *aux,
-                                               int ldaux) {
+__device__ __forceinline__ void apply_epilogue(float v, int t, int n, void *out, int ldo, bf16_t *out_lo,
+                                               const bf16_t *aux, int ldaux) {
     const size_t o = (size_t)t * ldo + n;
     if (EPI == EPI_F32) {
         reinterpret_cast<float *>(out)[o] = v;
@@ -45,19 +50,23 @@ __device__ __forceinline__ void apply_epilogue(float v, int t, int n, void *out,
         reinterpret_cast<bf16_t *>(out)[o] = f32_to_bf16(v);
     } else if (EPI == EPI_GATE) {
         const float m = bf16_to_f32(aux[(size_t)t * ldaux + n]);
-        const float silu = v / (1.f + expf(-v));
-        reinterpret_cast<bf16_t *>(out)[o] = f32_to_bf16(m * silu);
+        const float g = m * (v / (1.f + expf(-v)));
+        const bf16_t hi = f32_to_bf16(g);
+        reinterpret_cast<bf16_t *>(out)[o] = hi;
+        if (out_lo) out_lo[o] = f32_to_bf16(g - bf16_to_f32(hi));
     } else {
         bf16_t *h = reinterpret_cast<bf16_t *>(out);
         h[o] = f32_to_bf16(bf16_to_f32(h[o]) + v);
     }
 }
 
-// RT row tiles of 16, TB token tiles of 16, U chunks in flight per wave.
-template <int RT, int TB, int U, int EPI>
-__global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restrict__ X, int ldx,
+// RT row tiles of 16, TB token tiles of 16, U chunks in flight per wave; XLO:
+// X arrives as a bf16 hi + lo pair (two MFMAs per operand pair).
+template <int RT, int TB, int U, int EPI, bool XLO>
+__global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restrict__ X,
+                                                          const bf16_t *__restrict__ X_lo, int ldx,
                                                           const bf16_t *__restrict__ W, int T, int N, int K, int R,
-                                                          int k_slice, void *out, int ldo,
+                                                          int k_slice, void *out, int ldo, bf16_t *out_lo,
                                                           const bf16_t *__restrict__ aux, int ldaux,
                                                           float *__restrict__ partials) {
     constexpr int TT = 16 * TB;
@@ -76,9 +85,9 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
         rvalid[rt] = rl < R && n0 + rl < N;
         wrow[rt] = W + (size_t)(rvalid[rt] ? n0 + rl : 0) * K + kbeg + 8 * grp;
     }
-    const bf16_t *xrow[TB];
+    size_t xoff[TB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) xrow[tb] = X + (size_t)min(16 * tb + col, T - 1) * ldx + kbeg + 8 * grp;
+    for (int tb = 0; tb < TB; ++tb) xoff[tb] = (size_t)min(16 * tb + col, T - 1) * ldx + kbeg + 8 * grp;
 
     f32x4 acc[RT][TB];
 #pragma unroll
@@ -86,30 +95,39 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // Wave w owns chunks w, w + kWaves, w + 2·kWaves, ... (balanced); it keeps U
-    // of them in flight: all weight loads of a group are issued before any MFMA.
-    for (int j0 = 0; wave + kWaves * j0 < nchunks; j0 += U) {
-        u32x4 wf[U][RT][2], xf[U][TB][2];
+    // Wave w owns a contiguous run of ceil(nchunks / kWaves) chunks and keeps U
+    // of them in flight: the (L2-resident) X loads of a group are issued first,
+    // then all its weight loads, then the MFMAs.  (Strided chunk ownership and
+    // weight-first ordering measured within 3%.)
+    const int per_wave = (nchunks + kWaves - 1) / kWaves;
+    auto chunk_of = [&](int j) { return wave * per_wave + j; };
+    auto live_of = [&](int j) { return j < per_wave && wave * per_wave + j < nchunks; };
+    for (int j0 = 0; live_of(j0); j0 += U) {
+        u32x4 wf[U][RT][2], xf[U][TB][2], xl[XLO ? U : 1][TB][2];
+        auto load_x = [&]() {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool live = live_of(j0 + u);
+                const int k = chunk_of(j0 + u) * kChunk;
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        xf[u][tb][t] = live ? ld16(X + xoff[tb] + k + 32 * t) : (u32x4){0u, 0u, 0u, 0u};
+                        if (XLO) xl[XLO ? u : 0][tb][t] = live ? ld16(X_lo + xoff[tb] + k + 32 * t) : (u32x4){0u, 0u, 0u, 0u};
+                    }
+            }
+        };
+        load_x();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = wave + kWaves * (j0 + u);
-            const bool live = c < nchunks;
-            const int k = c * kChunk;
+            const bool live = live_of(j0 + u);
+            const int k = chunk_of(j0 + u) * kChunk;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
                     wf[u][rt][t] = (live && rvalid[rt]) ? ld16(wrow[rt] + k + 32 * t) : (u32x4){0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = wave + kWaves * (j0 + u);
-            const bool live = c < nchunks;
-            const int k = c * kChunk;
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) xf[u][tb][t] = live ? ld16(xrow[tb] + k + 32 * t) : (u32x4){0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -118,7 +136,10 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                    for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = mfma16x16x32(wf[u][rt][t], xf[u][tb][t], acc[rt][tb]);
+                    for (int tb = 0; tb < TB; ++tb) {
+                        acc[rt][tb] = mfma16x16x32(wf[u][rt][t], xf[u][tb][t], acc[rt][tb]);
+                        if (XLO) acc[rt][tb] = mfma16x16x32(wf[u][rt][t], xl[XLO ? u : 0][tb][t], acc[rt][tb]);
+                    }
     }
 
     // acc[rt][tb][r] = partial of row n0 + 16·rt + 4·grp + r, token 16·tb + col.
@@ -138,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) v += red[w][rl][t];
         if (gridDim.y == 1)
-            apply_epilogue<EPI>(v, t, n, out, ldo, aux, ldaux);
+            apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, ldaux);
         else
             partials[((size_t)blockIdx.y * T + t) * N + n] = v;
     }
@@ -146,50 +167,53 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
 
 template <int EPI>
 __global__ __launch_bounds__(256) void skinny_finish_kernel(const float *__restrict__ partials, int splits, int T,
-                                                            int N, void *out, int ldo, const bf16_t *__restrict__ aux,
-                                                            int ldaux) {
+                                                            int N, void *out, int ldo, bf16_t *out_lo,
+                                                            const bf16_t *__restrict__ aux, int ldaux) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)T * N) return;
     const int t = (int)(idx / N), n = (int)(idx % N);
     float v = 0.f;
     for (int s = 0; s < splits; ++s) v += partials[((size_t)s * T + t) * N + n];
-    apply_epilogue<EPI>(v, t, n, out, ldo, aux, ldaux);
+    apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, ldaux);
 }
 
-template <int RT, int TB, int EPI>
-hipError_t launch3(const bf16_t *X, int ldx, const bf16_t *W, int T, int N, int K, void *out, int ldo,
-                   const bf16_t *aux, int ldaux, const SkinnyPlan &p, float *partials, hipStream_t stream) {
-    // Chunks in flight per wave: operand registers U·8·(RT + TB) <= ~160.
-    constexpr int U = 20 / (RT + TB) < 1 ? 1 : 20 / (RT + TB);
-    const dim3 grid((N + p.rows_per_wg - 1) / p.rows_per_wg, p.k_splits);
+template <int RT, int TB, int EPI, bool XLO>
+hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    // Chunks in flight per wave: operand registers U·8·(RT + TB·(1 + XLO)) <= ~160.
+    constexpr int U = 20 / (RT + TB * (XLO ? 2 : 1)) < 1 ? 1 : 20 / (RT + TB * (XLO ? 2 : 1));
+    const dim3 grid((a.N + p.rows_per_wg - 1) / p.rows_per_wg, p.k_splits);
     TimingScope ts(kTimeSkinny, stream);
-    hipLaunchKernelGGL((skinny_kernel<RT, TB, U, EPI>), grid, dim3(kThreads), 0, stream, X, ldx, W, T, N, K,
-                       p.rows_per_wg, p.k_slice, out, ldo, aux, ldaux, partials);
+    hipLaunchKernelGGL((skinny_kernel<RT, TB, U, EPI, XLO>), grid, dim3(kThreads), 0, stream, a.X, a.X_lo, a.ldx, a.W,
+                       a.T, a.N, a.K, p.rows_per_wg, p.k_slice, a.out, a.ldo, a.out_lo, a.aux, a.ldaux, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.k_splits == 1) return e;
-    const size_t total = (size_t)T * N;
+    const size_t total = (size_t)a.T * a.N;
     hipLaunchKernelGGL((skinny_finish_kernel<EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       partials, p.k_splits, T, N, out, ldo, aux, ldaux);
+                       partials, p.k_splits, a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.ldaux);
     return hipGetLastError();
 }
 
+template <int RT, int TB, int EPI>
+hipError_t launch3(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    if (a.X_lo) return launch4<RT, TB, EPI, true>(a, p, partials, stream);
+    return launch4<RT, TB, EPI, false>(a, p, partials, stream);
+}
+
 template <int RT, int TB>
-hipError_t launch2(Epilogue epi, const bf16_t *X, int ldx, const bf16_t *W, int T, int N, int K, void *out, int ldo,
-                   const bf16_t *aux, int ldaux, const SkinnyPlan &p, float *partials, hipStream_t stream) {
-    switch (epi) {
-        case EPI_F32: return launch3<RT, TB, EPI_F32>(X, ldx, W, T, N, K, out, ldo, aux, ldaux, p, partials, stream);
-        case EPI_BF16: return launch3<RT, TB, EPI_BF16>(X, ldx, W, T, N, K, out, ldo, aux, ldaux, p, partials, stream);
-        case EPI_GATE: return launch3<RT, TB, EPI_GATE>(X, ldx, W, T, N, K, out, ldo, aux, ldaux, p, partials, stream);
-        default: return launch3<RT, TB, EPI_RESID>(X, ldx, W, T, N, K, out, ldo, aux, ldaux, p, partials, stream);
+hipError_t launch2(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    switch (a.epi) {
+        case EPI_F32: return launch3<RT, TB, EPI_F32>(a, p, partials, stream);
+        case EPI_BF16: return launch3<RT, TB, EPI_BF16>(a, p, partials, stream);
+        case EPI_GATE: return launch3<RT, TB, EPI_GATE>(a, p, partials, stream);
+        default: return launch3<RT, TB, EPI_RESID>(a, p, partials, stream);
     }
 }
 
 template <int RT>
-hipError_t launch1(Epilogue epi, const bf16_t *X, int ldx, const bf16_t *W, int T, int N, int K, void *out, int ldo,
-                   const bf16_t *aux, int ldaux, const SkinnyPlan &p, float *partials, hipStream_t stream) {
-    if (T <= 16) return launch2<RT, 1>(epi, X, ldx, W, T, N, K, out, ldo, aux, ldaux, p, partials, stream);
-    if (T <= 32) return launch2<RT, 2>(epi, X, ldx, W, T, N, K, out, ldo, aux, ldaux, p, partials, stream);
-    return launch2<RT, 4>(epi, X, ldx, W, T, N, K, out, ldo, aux, ldaux, p, partials, stream);
+hipError_t launch1(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    if (a.T <= 16) return launch2<RT, 1>(a, p, partials, stream);
+    if (a.T <= 32) return launch2<RT, 2>(a, p, partials, stream);
+    return launch2<RT, 4>(a, p, partials, stream);
 }
 
 }  // namespace
@@ -218,13 +242,11 @@ size_t skinny_partial_bytes(int T, int N, const SkinnyPlan &p) {
     return p.k_splits > 1 ? (size_t)p.k_splits * T * N * sizeof(float) : 0;
 }
 
-hipError_t launch_skinny(const bf16_t *X, int ldx, const bf16_t *W, int T, int N, int K, Epilogue epi, void *out,
-                         int ldo, const bf16_t *aux, int ldaux, const SkinnyPlan &plan, float *partials,
-                         hipStream_t stream) {
+hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *partials, hipStream_t stream) {
     const int R = plan.rows_per_wg;
-    if (R <= 16) return launch1<1>(epi, X, ldx, W, T, N, K, out, ldo, aux, ldaux, plan, partials, stream);
-    if (R <= 32) return launch1<2>(epi, X, ldx, W, T, N, K, out, ldo, aux, ldaux, plan, partials, stream);
-    return launch1<4>(epi, X, ldx, W, T, N, K, out, ldo, aux, ldaux, plan, partials, stream);
+    if (R <= 16) return launch1<1>(a, plan, partials, stream);
+    if (R <= 32) return launch1<2>(a, plan, partials, stream);
+    return launch1<4>(a, plan, partials, stream);
 }
 
 }  // namespace sambay

@@ -23,7 +23,8 @@
 //    never moves.  V is staged through a per-wave LDS tile and read back
 //    transposed (position-major per lane) as the A operand.
 //  * Partials (m, l, o) per (b, head, chunk) in fp32; a merge kernel combines
-//    the chunks by log-sum-exp in a fixed order (deterministic, no atomics).
+//    the chunks by log-sum-exp in a fixed order (deterministic, no atomics)
+//    and stores bf16 (plus, on request, the bf16 low part of the fp32 value).
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -226,7 +227,8 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
 // order, then normalisation and the bf16 store.
 __global__ __launch_bounds__(kHeadDim) void xattn_merge_kernel(const float2 *__restrict__ part_ml,
                                                                const float *__restrict__ part_o,
-                                                               bf16_t *__restrict__ out, int S) {
+                                                               bf16_t *__restrict__ out, bf16_t *__restrict__ out_lo,
+                                                               int S) {
     const size_t bh = blockIdx.x;
     const int d = threadIdx.x;
     const float2 *ml = part_ml + bh * S;
@@ -239,7 +241,10 @@ __global__ __launch_bounds__(kHeadDim) void xattn_merge_kernel(const float2 *__r
         lsum += e * ml[s].y;
         o += e * po[(size_t)s * kHeadDim + d];
     }
-    out[bh * kHeadDim + d] = f32_to_bf16(o / lsum);
+    const float v = o / lsum;
+    const bf16_t hi = f32_to_bf16(v);
+    out[bh * kHeadDim + d] = hi;
+    if (out_lo) out_lo[bh * kHeadDim + d] = f32_to_bf16(v - bf16_to_f32(hi));
 }
 
 int env_splits() {
@@ -279,8 +284,9 @@ size_t xattn_partial_bytes(int64_t B, int64_t Hq, int splits) {
     return n * sizeof(float2) + n * kHeadDim * sizeof(float);
 }
 
-hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, bf16_t *out, int B, int Hq,
-                        int Hkv, int L, float scale, const XattnPlan &plan, void *partials, hipStream_t stream) {
+hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, bf16_t *out, bf16_t *out_lo,
+                        int B, int Hq, int Hkv, int L, float scale, const XattnPlan &plan, void *partials,
+                        hipStream_t stream) {
     const size_t n = (size_t)B * Hq * plan.splits;
     float2 *ml = reinterpret_cast<float2 *>(partials);
     float *po = reinterpret_cast<float *>(reinterpret_cast<char *>(partials) + n * sizeof(float2));
@@ -298,7 +304,7 @@ hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     TimingScope ts(kTimeXattnMerge, stream);
-    hipLaunchKernelGGL(xattn_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kHeadDim), 0, stream, ml, po, out,
+    hipLaunchKernelGGL(xattn_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kHeadDim), 0, stream, ml, po, out, out_lo,
                        plan.splits);
     return hipGetLastError();
 }

@@ -83,8 +83,9 @@ const char *sb_version(void);
  * prefill, or batch for one decode step (one new token per sequence).  M is
  * the memory readout of the earlier token-mixing layer, one row per token.
  * All five tensors share `dt`:
- *   SB_BF16: products accumulate in fp32; the gated hidden H = M ⊙ SiLU(·) is
- *            rounded to bf16 before the second product; Y is stored as bf16.
+ *   SB_BF16: products accumulate in fp32; the gated hidden H = M ⊙ SiLU(·)
+ *            is rounded to bf16 before the second product; Y is stored as
+ *            bf16.
  *   SB_F32 : everything in fp32.
  * Y must not overlap any input.  Errors: SB_EINVAL (null pointer, negative
  * size, d_model or d_inner == 0 with rows > 0, overlap, misalignment),
@@ -118,10 +119,11 @@ sb_status xattn_decode(const void *q, const void *kcache, const void *vcache, vo
  * One decode step of the cross-decoder ([Notes] section 整体框架): for each
  * layer in array order, a residual branch on the bf16 stream h [B, d_model]:
  *   SB_LAYER_XATTN: q = h Wq^T (fp32, not rounded), o = attention of q over
- *                   the shared kcache/vcache [B, Hkv, L, D] (as xattn_decode,
- *                   o rounded to bf16), h = bf16(h + o Wo^T);
+ *                   the shared kcache/vcache [B, Hkv, L, D] (as xattn_decode;
+ *                   o feeds Wo as a bf16 hi + lo pair), h = bf16(h + o Wo^T);
  *   SB_LAYER_GMU:   h = bf16(h + GMU(M, h, W1, W2)) with the one memory
- *                   readout M [B, d_inner] shared by every GMU layer.
+ *                   readout M [B, d_inner] shared by every GMU layer; H
+ *                   feeds W2 as a bf16 hi + lo pair (~16 significant bits).
  * h is updated in place.  Requires Hq·D == d_model.  All tensors bf16.
  * Errors: as gmu_forward and xattn_decode, plus SB_EINVAL for a null layer
  * array with n_layers > 0, a null layer weight, an unknown kind, or

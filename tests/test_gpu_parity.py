@@ -193,6 +193,17 @@ def test_crossdecoder_small(sb, B, Hq, Hkv, L, d_inner, n, first):
     report("crossdecoder B=%d Hq=%d L=%d n=%d %s-first" % (B, Hq, L, n, first), err(f64(hg), ref), TOL_BF16)
 
 
+def test_crossdecoder_batch_above_64(sb):
+    """More than 64 sequences: the decode products run in groups of 64 rows."""
+    x = _step_inputs(70, 3, 1, 50, 256, 4, seed=70)
+    h0 = x.h.clone()
+    sb.crossdecoder_step(x.h, x.M, x.K, x.V, x.layers)
+    torch.cuda.synchronize()
+    x.h, hg = h0, x.h
+    ref = _oracle_step(x, slice(None), 3)
+    report("crossdecoder B=70 (two row groups)", err(f64(hg), ref), TOL_BF16)
+
+
 def test_crossdecoder_full_sampled_sequences(sb):
     """16 layers (8 cross-attention + 8 GMU), 32 sequences, d_model 3072,
     d_inner 6144, 34816 shared cache positions; the oracle replays two whole
