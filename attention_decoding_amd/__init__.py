@@ -31,8 +31,9 @@ SB_LAYER_XATTN, SB_LAYER_GMU = 0, 1
 # Every function the header declares, for load-time checking.
 EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", "xattn_workspace_bytes",
            "xattn_decode", "crossdecoder_workspace_bytes", "crossdecoder_step", "sb_timing_enable",
-           "sb_timing_collect")
-SB_TIME_XATTN_SPLIT, SB_TIME_XATTN_MERGE, SB_TIME_SKINNY, SB_TIME_GEMM, SB_TIME_GMU_F32 = 1, 2, 4, 8, 16
+           "sb_timing_collect", "sb_probe_stream_read", "sb_probe_mfma", "sb_probe_mfma_flops")
+SB_TIME_XATTN_SPLIT, SB_TIME_XATTN_MERGE, SB_TIME_SKINNY, SB_TIME_GEMM, SB_TIME_GMU_F32, SB_TIME_PROBE = \
+    1, 2, 4, 8, 16, 32
 
 
 class SbLayer(ctypes.Structure):
@@ -69,6 +70,12 @@ def _load() -> ctypes.CDLL:
     lib.sb_timing_enable.restype = ctypes.c_int
     lib.sb_timing_collect.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
     lib.sb_timing_collect.restype = ctypes.c_int
+    lib.sb_probe_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.sb_probe_stream_read.restype = ctypes.c_int
+    lib.sb_probe_mfma.argtypes = [i64, vp, vp]
+    lib.sb_probe_mfma.restype = ctypes.c_int
+    lib.sb_probe_mfma_flops.argtypes = [i64]
+    lib.sb_probe_mfma_flops.restype = ctypes.c_double
     return lib
 
 
@@ -90,6 +97,35 @@ def timing_collect(mask: int):
     n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
     _check("sb_timing_collect", lib.sb_timing_collect(int(mask), ctypes.byref(n), ctypes.byref(ms)))
     return int(n.value), float(ms.value)
+
+
+def probe_stream_read_gbps(buf: torch.Tensor, reps: int = 5) -> float:
+    """Rate (GB/s) of a plain streaming read of `buf` (a GPU tensor) by the library's probe kernel."""
+    dev = _check_device(buf, "buf")
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    st = _stream(dev)
+    _check("sb_probe_stream_read", lib.sb_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), st))
+    timing_enable(SB_TIME_PROBE)
+    for _ in range(reps):
+        _check("sb_probe_stream_read", lib.sb_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), st))
+    timing_enable(0)
+    n, ms = timing_collect(SB_TIME_PROBE)
+    return nbytes / (ms / n / 1e3) / 1e9
+
+
+def probe_mfma_tflops(device, iters: int = 20000, reps: int = 3) -> float:
+    """Rate (TFLOP/s) of the library's register-only bf16 32x32x16 MFMA loop."""
+    dev = torch.device(device)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = _stream(dev)
+    _check("sb_probe_mfma", lib.sb_probe_mfma(100, sink.data_ptr(), st))
+    timing_enable(SB_TIME_PROBE)
+    for _ in range(reps):
+        _check("sb_probe_mfma", lib.sb_probe_mfma(iters, sink.data_ptr(), st))
+    timing_enable(0)
+    n, ms = timing_collect(SB_TIME_PROBE)
+    return lib.sb_probe_mfma_flops(iters) / (ms / n / 1e3) / 1e12
 
 
 def _check(fn: str, status: int):
@@ -254,4 +290,4 @@ def crossdecoder_step(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor, vc
 
 
 __all__ = ["gmu_forward", "xattn_decode", "crossdecoder_step", "CrossDecoderStep", "SambayError", "version", "lib",
-           "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect"]
+           "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect", "probe_stream_read_gbps", "probe_mfma_tflops"]

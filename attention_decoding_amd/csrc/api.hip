@@ -5,6 +5,7 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -64,6 +65,15 @@ struct Carver {
 };
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+// SAMBAY_LOG=1 prints each call's dispatch decisions (kernel path, plans) to stderr.
+bool log_enabled() {
+    static const bool on = [] {
+        const char *e = getenv("SAMBAY_LOG");
+        return e && *e && *e != '0';
+    }();
+    return on;
+}
 
 // ----------------------------------------------------------------- GMU
 
@@ -174,6 +184,23 @@ extern "C" sb_status gmu_forward(const void *M, const void *X, const void *W1, c
         if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
 
     Carver ws{static_cast<char *>(workspace)};
+    if (log_enabled()) {
+        if (dt == SB_F32) {
+            fprintf(stderr, "[sambay] gmu_forward rows=%lld %lldx%lld fp32 -> gmu_f32 kernels\n", (long long)rows,
+                    (long long)d_model, (long long)d_inner);
+        } else if (rows <= kSkinnyMaxTokens) {
+            const SkinnyPlan p1 = skinny_plan((int)rows, (int)d_inner, (int)d_model);
+            const SkinnyPlan p2 = skinny_plan((int)rows, (int)d_model, (int)d_inner);
+            fprintf(stderr,
+                    "[sambay] gmu_forward rows=%lld %lldx%lld bf16 -> decode products: gate rows/wg=%d ksplit=%d, "
+                    "out rows/wg=%d ksplit=%d\n",
+                    (long long)rows, (long long)d_model, (long long)d_inner, p1.rows_per_wg, p1.k_splits,
+                    p2.rows_per_wg, p2.k_splits);
+        } else {
+            fprintf(stderr, "[sambay] gmu_forward rows=%lld %lldx%lld bf16 -> prefill GEMMs (128x128 tiles)\n",
+                    (long long)rows, (long long)d_model, (long long)d_inner);
+        }
+    }
     hipError_t e;
     if (dt == SB_F32) {
         float *H = static_cast<float *>(ws.take((size_t)rows * d_inner * sizeof(float)));
@@ -226,6 +253,10 @@ extern "C" sb_status xattn_decode(const void *q, const void *kcache, const void 
         if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
 
     const XattnPlan plan = xattn_plan(B, Hkv, L);
+    if (log_enabled())
+        fprintf(stderr, "[sambay] xattn_decode B=%lld Hq=%lld Hkv=%lld L=%lld -> %d chunks of %d positions, grid %dx%lldx%lld\n",
+                (long long)B, (long long)Hq, (long long)Hkv, (long long)L, plan.splits, plan.chunk, plan.splits,
+                (long long)Hkv, (long long)B);
     hipError_t e = launch_xattn(q, false, (const bf16_t *)kcache, (const bf16_t *)vcache, (bf16_t *)out, nullptr,
                                 (int)B, (int)Hq, (int)Hkv, (int)L, scale, plan, workspace, stream);
     if (e != hipSuccess) return hip_fail("xattn_decode launch", e);
@@ -323,6 +354,11 @@ extern "C" sb_status crossdecoder_step(void *h, const void *M, const void *kcach
     char *gmu_ws_base = base + lay.q + lay.o;
     void *partials = base + lay.q + lay.o + lay.gmu;
     const XattnPlan plan = xattn_plan(B, Hkv, L);
+    if (log_enabled())
+        fprintf(stderr, "[sambay] crossdecoder_step B=%lld layers=%d d_model=%lld d_inner=%lld L=%lld -> attention "
+                        "%d chunks of %d positions; workspace %zu bytes\n",
+                (long long)B, (int)n_layers, (long long)d_model, (long long)d_inner, (long long)L, plan.splits,
+                plan.chunk, lay.total);
     bf16_t *hb = static_cast<bf16_t *>(h);
     const int dm = (int)d_model, di = (int)d_inner;
 

@@ -24,7 +24,8 @@ class TimingScope {
     hipEvent_t start_ = nullptr, stop_ = nullptr;
     bool active_ = false;
 };
-constexpr uint32_t kTimeXattnSplit = 1, kTimeXattnMerge = 2, kTimeSkinny = 4, kTimeGemm = 8, kTimeGmuF32 = 16;
+constexpr uint32_t kTimeXattnSplit = 1, kTimeXattnMerge = 2, kTimeSkinny = 4, kTimeGemm = 8, kTimeGmuF32 = 16,
+                   kTimeProbe = 32;
 
 // ------------------------------------------------------- cross-attention
 constexpr int kHeadDim = 128;     // supported head dimension

@@ -246,6 +246,12 @@ def main():
     kern["xattn_split"]["gbps"] = round(nbytes["kv"] / (kern["xattn_split"]["ms_per_step"] / 1e3) / 1e9, 1)
     kern["xattn_split"]["frac_of_peak"] = round(kern["xattn_split"]["gbps"] / HBM_PEAK_GBS, 4)
 
+    # Practical ceilings of this machine, by the library's probe kernels: a plain
+    # streaming read of the K cache and a register-only bf16 MFMA loop.
+    read_gbps = sb.probe_stream_read_gbps(x.K)
+    mfma_tf = sb.probe_mfma_tflops(dev, iters=10000)
+    log("bench: probes: streaming read %.0f GB/s, bf16 MFMA loop %.0f TFLOP/s" % (read_gbps, mfma_tf))
+
     workloads = None
     if args.all:
         log("bench: timing the other workloads")
@@ -283,6 +289,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": nbytes["kv_per_layer"], "us_per_launch": round(1e3 * split_ms, 2),
                      "traffic": traffic_for_current_kernel()},
+        "measured_ceilings": {"stream_read_gbps": round(read_gbps, 1), "bf16_mfma_tflops": round(mfma_tf, 1),
+                              "split_frac_of_stream_read": round(achieved / read_gbps, 4)},
         "kernels": kern,
         "cpu_baseline": cpu,
     }

@@ -148,11 +148,25 @@ typedef enum {
     SB_TIME_XATTN_MERGE = 2,   /* log-sum-exp merge kernel */
     SB_TIME_SKINNY = 4,        /* decode weight-streaming products (GMU, Wq, Wo) */
     SB_TIME_GEMM = 8,          /* prefill MFMA GEMM */
-    SB_TIME_GMU_F32 = 16       /* fp32 GMU kernels */
+    SB_TIME_GMU_F32 = 16,      /* fp32 GMU kernels */
+    SB_TIME_PROBE = 32         /* the two probes below */
 } sb_timing_kind;
 
 sb_status sb_timing_enable(uint32_t mask);
 sb_status sb_timing_collect(uint32_t mask, int64_t *launches, double *total_ms);
+
+/* Measured-ceiling probes (benchmarks only; not part of the method).
+ * sb_probe_stream_read reads `bytes` bytes of device memory `data` (16-byte
+ * aligned, bytes a multiple of 16) once with a plain grid-stride streaming
+ * read that does nothing else: its rate is a practical HBM read ceiling for
+ * this machine.  sb_probe_mfma runs `iters` dependent steps of the
+ * 32x32x16 bf16 MFMA on four independent accumulators per wave in 4096 waves
+ * (sb_probe_mfma_flops(iters) floating-point operations): a practical dense
+ * bf16 MFMA ceiling.  `sink` is 4 bytes of device memory the kernels may
+ * write.  Errors: SB_EINVAL, SB_EHIP. */
+sb_status sb_probe_stream_read(const void *data, size_t bytes, void *sink, hipStream_t stream);
+sb_status sb_probe_mfma(int64_t iters, void *sink, hipStream_t stream);
+double sb_probe_mfma_flops(int64_t iters);
 
 #ifdef __cplusplus
 }

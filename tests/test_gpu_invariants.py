@@ -147,3 +147,12 @@ def test_step_object_reuse_and_stream(sb):
     torch.cuda.current_stream().wait_stream(st)
     torch.cuda.synchronize()
     assert torch.equal(first, s.h)
+
+
+def test_ceiling_probes_run(sb):
+    """The benchmark probes run and report rates within physical limits."""
+    buf = torch.ones(64 << 20, dtype=torch.float32, device=DEV)
+    gbps = sb.probe_stream_read_gbps(buf)
+    tf = sb.probe_mfma_tflops(DEV, iters=200)
+    assert 100.0 < gbps < 8000.0 * 1.05
+    assert 10.0 < tf < 2500.0 * 1.05

@@ -221,3 +221,26 @@ def test_crossdecoder_full_sampled_sequences(sb):
         report("crossdecoder full seq b=%d" % b, err(f64(hg[b:b + 1]), ref), TOL_BF16)
     del x, hg
     torch.cuda.empty_cache()
+
+
+def test_crossdecoder_teacher_forced_layers(sb):
+    """Per-layer diagnostic at the full decode-step width: each GPU layer is fed
+    the GPU's own bf16 h of the previous layer and compared with the oracle's
+    single layer on that same input.  Every layer must meet the bar on its
+    own, so an end-to-end error is accumulated rounding, not a wrong layer."""
+    c = workload.CROSSDECODER
+    B, L = 2, 4096
+    x = workload.crossdecoder_inputs(B, c["d_model"], c["d_inner"], c["Hq"], c["Hkv"], c["D"], L, c["n_layers"],
+                                     seed=9, device=DEV)
+    h = x.h.clone()
+    worst = 0.0
+    for i, layer in enumerate(x.layers):
+        h_in = h.clone()
+        sb.crossdecoder_step(h, x.M, x.K, x.V, [layer])
+        torch.cuda.synchronize()
+        ref = oracle.crossdecoder(cpu(h_in), cpu(x.M), cpu(x.K), cpu(x.V), [(layer[0], cpu(layer[1]), cpu(layer[2]))],
+                                  c["Hq"])
+        e = err(f64(h), ref)
+        worst = max(worst, e)
+        assert e <= TOL_BF16, "layer %d (%s): err %.3e" % (i, layer[0], e)
+    report("crossdecoder teacher-forced, worst of 16 layers", worst, TOL_BF16)
