@@ -77,18 +77,31 @@ def traffic_for_current_kernel():
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, c, n_seq: int):
+def cpu_baseline(h_in, x, c, n_seq: int):
+    """Times the fp64 oracle on the first n_seq sequences of the step's input, on
+    all host threads and (one sequence) on one thread.  Returns the report and the
+    oracle's output for those sequences."""
     import oracle
 
     layers = [(k, a.cpu(), b.cpu()) for k, a, b in x.layers]
     rows = slice(0, n_seq)
-    h, M, K, V = x.h[rows].cpu(), x.M[rows].cpu(), x.K[rows].cpu(), x.V[rows].cpu()
+    h, M, K, V = h_in[rows].cpu(), x.M[rows].cpu(), x.K[rows].cpu(), x.V[rows].cpu()
+    cores = oracle.max_threads()
     t0 = time.perf_counter()
-    oracle.crossdecoder(h, M, K, V, layers, c["Hq"])
+    ref = oracle.crossdecoder(h, M, K, V, layers, c["Hq"])
     dt = time.perf_counter() - t0
-    return {"value": n_seq / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": "%d of %d sequences, one decode token each, through all %d layers at %d cached positions "
-                      "(fp64 oracle, sequences are independent); %.1f s" % (n_seq, c["B"], c["n_layers"], c["L"], dt)}
+    oracle.set_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.crossdecoder(h[:1], M[:1], K[:1], V[:1], layers, c["Hq"])
+        dt1 = time.perf_counter() - t1
+    finally:
+        oracle.set_threads(cores)
+    rep = {"value": n_seq / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": "%d of %d sequences, one decode token each, through all %d layers at %d cached positions "
+                     "(fp64 oracle, sequences are independent); %.1f s" % (n_seq, c["B"], c["n_layers"], c["L"], dt),
+           "single_core_value": 1.0 / dt1, "single_core_sample": "1 sequence on 1 thread; %.1f s" % dt1}
+    return rep, ref
 
 
 def time_calls(fn, n: int, warmup: int = 3) -> float:
@@ -107,7 +120,7 @@ def time_calls(fn, n: int, warmup: int = 3) -> float:
     return e0.elapsed_time(e1) / n
 
 
-def other_workloads(sb, workload, dev) -> dict:
+def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> dict:
     """Kernel-level rates of the other workloads (not part of `value`)."""
     import torch
 
@@ -120,7 +133,8 @@ def other_workloads(sb, workload, dev) -> dict:
     ms = time_calls(lambda i: sb.gmu_forward(g.M, g.X, g.W1, g.W2, out=Y), 20)
     flops = 4.0 * rows * c["d_model"] * c["d_inner"]
     res["gmu_prefill_8192x2560x5120"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
-                                         "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4)}
+                                         "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4),
+                                         "frac_of_measured_mfma_loop": round(flops / ms / 1e9 / mfma_tflops, 4)}
     del g, Y
     # GMU decode: B in {1, 8, 32, 64}, 3072 -> 6144 -> 3072, 8 rotating weight sets (604 MB).
     c = workload.GMU_DECODE
@@ -129,15 +143,11 @@ def other_workloads(sb, workload, dev) -> dict:
         gi = workload.gmu_inputs(B, c["d_model"], c["d_inner"], seed=3 + B, device=dev)
         Y = torch.empty(B, c["d_model"], dtype=torch.bfloat16, device=dev)
         ms = time_calls(lambda i: sb.gmu_forward(gi.M, gi.X, sets[i % 8].W1, sets[i % 8].W2, out=Y), 64)
-        sb.timing_enable(sb.SB_TIME_SKINNY)
-        time_calls(lambda i: sb.gmu_forward(gi.M, gi.X, sets[i % 8].W1, sets[i % 8].W2, out=Y), 64, warmup=0)
-        sb.timing_enable(0)
-        n, kms = sb.timing_collect(sb.SB_TIME_SKINNY)
         nbytes = 2 * c["d_model"] * c["d_inner"] * 2 + B * (2 * c["d_model"] + c["d_inner"]) * 2
-        kus = 1e3 * kms / 64
-        res["gmu_decode_B%d" % B] = {"us_per_call": round(1e3 * ms, 2), "us_kernels": round(kus, 2),
-                                     "gbps_kernels": round(nbytes / kus / 1e3, 1),
-                                     "frac_of_hbm_peak": round(nbytes / kus / 1e3 / HBM_PEAK_GBS, 4)}
+        gbps = nbytes / ms / 1e6
+        res["gmu_decode_B%d" % B] = {"us_per_call": round(1e3 * ms, 2), "gbps": round(gbps, 1),
+                                     "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
+                                     "frac_of_stream_read": round(gbps / read_gbps, 4)}
     del sets
     # Attention alone: 16 x 24 q heads, 8 KV heads, 34816 positions.
     c = workload.XATTN_DECODE
@@ -146,7 +156,8 @@ def other_workloads(sb, workload, dev) -> dict:
     ms = time_calls(lambda i: sb.xattn_decode(x.q, x.K, x.V, out=out), 20)
     nbytes = c["B"] * c["Hkv"] * c["L"] * c["D"] * 4
     res["xattn_decode_B16_L34816"] = {"us_per_call": round(1e3 * ms, 1), "gbps": round(nbytes / ms / 1e6, 1),
-                                      "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+                                      "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                      "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
     del x
     torch.cuda.empty_cache()
     return res
@@ -207,18 +218,22 @@ def main():
     log("bench: warmup done, timing %d steps" % args.steps)
 
     sb.timing_enable(sb.SB_TIME_XATTN_SPLIT)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         run_step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     sb.timing_enable(0)
     n_split, ms_split = sb.timing_collect(sb.SB_TIME_XATTN_SPLIT)
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+
+    def pct(q):
+        return per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
     ms_step = max(ms_step, 1e3 * wall / args.steps)
     tokens_per_s = c["B"] / (ms_step / 1e3)
     split_ms = ms_split / max(n_split, 1)
@@ -252,17 +267,33 @@ def main():
     mfma_tf = sb.probe_mfma_tflops(dev, iters=10000)
     log("bench: probes: streaming read %.0f GB/s, bf16 MFMA loop %.0f TFLOP/s" % (read_gbps, mfma_tf))
 
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+
+        log("bench: timing the fp64 oracle on %d sequences" % args.cpu_seqs)
+        cpu, ref = cpu_baseline(h_in, x, c, args.cpu_seqs)
+        log("bench: oracle %.3f tokens/s on %d threads, %.3f on one" %
+            (cpu["value"], cpu["cores"], cpu["single_core_value"]))
+        # The step's own output on the timed inputs against the oracle's.
+        run_step()
+        torch.cuda.synchronize()
+        got = x.h[:args.cpu_seqs].double().cpu().numpy()
+        err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+        big = np.abs(ref) > 1e-3 * np.max(np.abs(ref))
+        rel = np.abs(got - ref)[big] / np.abs(ref)[big]
+        parity = {"sequences": args.cpu_seqs, "max_abs_err_over_max_abs_ref": err, "tolerance": 2e-2,
+                  "pass": err <= 2e-2,
+                  "elementwise_rel_err_where_ref_above_1e-3_max": {"median": float(np.median(rel)),
+                                                                   "p99": float(np.quantile(rel, 0.99)),
+                                                                   "max": float(np.max(rel))}}
+        log("bench: parity of the timed step against the oracle: %.3e (tolerance 2e-2)" % err)
+
     workloads = None
     if args.all:
         log("bench: timing the other workloads")
         del step
-        workloads = other_workloads(sb, workload, dev)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("bench: timing the fp64 oracle on %d sequences" % args.cpu_seqs)
-        cpu = cpu_baseline(x, c, args.cpu_seqs)
-        log("bench: oracle %.3f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
+        workloads = other_workloads(sb, workload, dev, read_gbps, mfma_tf)
 
     out = {
         "metric": METRIC,
@@ -272,6 +303,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_p10_median_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -293,6 +325,7 @@ def main():
                               "split_frac_of_stream_read": round(achieved / read_gbps, 4)},
         "kernels": kern,
         "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
     }
     if workloads is not None:
         out["workloads"] = workloads
