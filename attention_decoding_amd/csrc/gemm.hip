@@ -51,7 +51,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     constexpr int INSTS = ROWS / 8;
     constexpr int IPW = INSTS / NWAVES;
     static_assert(IPW * NWAVES == INSTS && FM * 32 == TM && FN * 32 == TN, "tile shape");
-    __shared__ __attribute__((aligned(1024))) bf16_t lds[NS][ROWS * BK];
+    constexpr int SROW = TN + 4;                  // fp32 per staged epilogue row
+    constexpr int RING_BYTES = NS * ROWS * BK * 2, STAGE_BYTES = NWAVES * 32 * SROW * 4;
+    constexpr int LDS_BYTES = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) char lds_raw[LDS_BYTES];
+    bf16_t(*lds)[ROWS * BK] = reinterpret_cast<bf16_t(*)[ROWS * BK]>(lds_raw);
 
     const int tiles_m = (rows + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
@@ -121,23 +126,56 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
         }
     }
 
-    // acc[i][j][v]: row bm + TM·wm + 32·i + 8·(v/4) + 4·half + v%4, col bn + TN·wn + 32·j + l32.
+    // Epilogue through LDS: acc[i][j][v] holds row TM·wm + 32·i + 8·(v/4) +
+    // 4·half + v%4, col TN·wn + 32·j + l32 of the tile, so each lane owns one
+    // column.  Each wave parks 32 rows of its block in its own LDS area, then
+    // every lane handles 8 consecutive columns: one 16-byte load of M (gate)
+    // and one 16-byte store per vector instead of 2-byte accesses.
+    constexpr int VPR = TN / 8;                   // 8-column vectors per row
+    constexpr int VPL = 32 * VPR / 64;            // vectors per lane per 32 rows
+    static_assert(VPL * 64 == 32 * VPR, "epilogue shape");
+    float *stage = reinterpret_cast<float *>(lds_raw) + wave * 32 * SROW;
+    u32x4 mv[FM][VPL];
+    if (EPI == EPI_GATE) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int m = bm + wm * TM + 32 * i + 8 * (v / 4) + 4 * half + (v % 4);
-            if (m >= rows) continue;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = bn + wn * TN + 32 * j + l32;
-                if (n >= N) continue;
-                const size_t o = (size_t)m * N + n;
-                float x = acc[i][j][v];
-                if (EPI == EPI_GATE) x = bf16_to_f32(aux[o]) * (x / (1.f + expf(-x)));
-                out[o] = f32_to_bf16(x);
+            for (int u = 0; u < VPL; ++u) {
+                const int idx = u * 64 + lane, r = idx / VPR, c8 = idx % VPR;
+                const int m = bm + wm * TM + 32 * i + r, n = bn + wn * TN + 8 * c8;
+                mv[i][u] = (m < rows && n < N) ? ld16(aux + (size_t)m * N + n) : (u32x4){0u, 0u, 0u, 0u};
             }
+    }
+    __syncthreads();  // every wave is done with the operand ring
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) stage[(8 * (v / 4) + 4 * half + (v % 4)) * SROW + 32 * j + l32] = acc[i][j][v];
+        wave_lds_fence();
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+            const int idx = u * 64 + lane, r = idx / VPR, c8 = idx % VPR;
+            const int m = bm + wm * TM + 32 * i + r, n = bn + wn * TN + 8 * c8;
+            const f32x4 lo = *reinterpret_cast<const f32x4 *>(&stage[r * SROW + 8 * c8]);
+            const f32x4 hi = *reinterpret_cast<const f32x4 *>(&stage[r * SROW + 8 * c8 + 4]);
+            float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            if (EPI == EPI_GATE) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w = mv[i][u][e / 2];
+                    const float mm = (e & 1) ? hi_bf16(w) : lo_bf16(w);
+                    x[e] = mm * (x[e] / (1.f + expf(-x[e])));
+                }
+            }
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+            if (m < rows && n < N) *reinterpret_cast<u32x4 *>(out + (size_t)m * N + n) = o;
         }
+        wave_lds_fence();
+    }
 }
 
 template <int BM, int BN, int WGM, int WGN, int NS>
