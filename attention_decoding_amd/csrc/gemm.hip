@@ -9,7 +9,7 @@
 //  * 128x128 output tile per workgroup, 4 waves in a 2x2 grid, each wave a
 //    64x64 block of 2x2 32x32x16 MFMA tiles (on gfx950 the 32x32x16 bf16 form
 //    measured ~2.4 PFLOP/s in a register-only loop, the 16x16x32 form ~1.4).
-//  * K advances 64 at a time through a two-stage LDS ring filled by direct
+//  * K advances BK = 64 at a time through a two-stage LDS ring filled by direct
 //    global -> LDS loads (global_load_lds_dwordx4): no register staging, and
 //    the next stage's loads run under this stage's MFMAs.  A bare s_barrier
 //    plus an explicit vmcnt wait orders the stages (a __syncthreads fence
@@ -19,10 +19,15 @@
 //  * Two workgroups per CU; workgroup ids are remapped so each XCD (ids
 //    round-robin over 8) works on a contiguous band of tiles, grouped 8
 //    row-tiles at a time.
-//  * Measured at 8192 x 2560 x 5120 (both GMU products): ~0.60-0.70 ms per
-//    GMU call; tile size, stage depth, register vs LDS staging, MFMA shape and
-//    tile order all land within that band, so the limit is outside the MFMA
-//    and LDS rates (MFMA busy ~28%, LDS ~20%, no bank conflicts).
+//  * The epilogue parks each wave's accumulators in LDS (the ring is free by
+//    then) so that M is read and the output written as 16-byte vectors.
+//  * Measured at 8192 x 2560 x 5120 (both GMU products, random data): ~250 us
+//    for the gate product and ~227 us for the output product (850-950
+//    TFLOP/s).  A 3-5 deep ring (BK 64 or 32), 256-wide tiles with 8 or 16
+//    waves, 64x128 or 128x128 blocks per wave, and reading a whole slice's
+//    fragments before its MFMAs (forced with scheduling barriers) all
+//    measured equal or slower; MFMA busy stays near a third, LDS bank
+//    conflicts are zero.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -32,14 +37,21 @@ namespace sambay {
 
 namespace {
 
-constexpr int BK = 64;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+// LDS rows hold BK bf16 (CPR 16-byte chunks); chunk c of row r is stored at
+// c ^ ((r / RP) % CPR), RP = rows per 256 bytes, so the 32 rows of an operand
+// read are spread over all bank groups.
+template <int BK>
+__device__ __forceinline__ int swz(int row, int chunk) {
+    constexpr int CPR = BK / 8, RP = 256 / (2 * BK);
+    return chunk ^ ((row / RP) % CPR);
+}
 
-// BM x BN output tile per workgroup of WGM x WGN waves; NS-stage LDS ring.
-template <int BM, int BN, int WGM, int WGN, int NS, int EPI>
+// BM x BN output tile per workgroup of WGM x WGN waves; NS-stage LDS ring of
+// BK-deep operand slices.
+template <int BM, int BN, int WGM, int WGN, int NS, int BK, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__restrict__ X,
                                                                 const bf16_t *__restrict__ W, int rows, int N,
                                                                 int K, bf16_t *__restrict__ out,
@@ -48,7 +60,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int ROWS = BM + BN;
-    constexpr int INSTS = ROWS / 8;
+    constexpr int CPR = BK / 8;              // 16-byte chunks per LDS row
+    constexpr int IROWS = 64 / CPR;          // rows filled by one wave-wide 16-byte copy
+    constexpr int INSTS = ROWS / IROWS;
     constexpr int IPW = INSTS / NWAVES;
     static_assert(IPW * NWAVES == INSTS && FM * 32 == TM && FN * 32 == TN, "tile shape");
     constexpr int SROW = TN + 4;                  // fp32 per staged epilogue row
@@ -75,15 +89,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     const bf16_t *src[IPW];
 #pragma unroll
     for (int q = 0; q < IPW; ++q) {
-        const int r = (wave * IPW + q) * 8 + (lane >> 3);
-        const int logical = (lane & 7) ^ ((r >> 1) & 7);
+        const int r = (wave * IPW + q) * IROWS + lane / CPR;
+        const int logical = swz<BK>(r, lane % CPR);
         const bf16_t *base = r < BM ? X + (size_t)min(bm + r, rows - 1) * K
                                     : W + (size_t)min(bn + r - BM, N - 1) * K;
         src[q] = base + 8 * logical;
     }
     auto issue = [&](int kt, int slot) {
 #pragma unroll
-        for (int q = 0; q < IPW; ++q) lds_dma16(src[q] + (size_t)kt * BK, &lds[slot][(wave * IPW + q) * 8 * BK]);
+        for (int q = 0; q < IPW; ++q) lds_dma16(src[q] + (size_t)kt * BK, &lds[slot][(wave * IPW + q) * IROWS * BK]);
     };
 
     f32x16 acc[FM][FN];
@@ -112,12 +126,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int r = wm * TM + 32 * i + l32;
-                fa[i] = *reinterpret_cast<const u32x4 *>(&sA[r * BK + 8 * swz(r, 2 * ks + half)]);
+                fa[i] = *reinterpret_cast<const u32x4 *>(&sA[r * BK + 8 * swz<BK>(r, 2 * ks + half)]);
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int r = wn * TN + 32 * j + l32;
-                fb[j] = *reinterpret_cast<const u32x4 *>(&sB[r * BK + 8 * swz(BM + r, 2 * ks + half)]);
+                fb[j] = *reinterpret_cast<const u32x4 *>(&sB[r * BK + 8 * swz<BK>(BM + r, 2 * ks + half)]);
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -178,16 +192,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS>
+template <int BM, int BN, int WGM, int WGN, int NS, int BK>
 hipError_t launch_tile(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
                      const bf16_t *aux, hipStream_t stream) {
     const int tiles = ((rows + BM - 1) / BM) * ((N + BN - 1) / BN);
     TimingScope ts(kTimeGemm, stream);
     if (epi == EPI_GATE)
-        hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, EPI_GATE>), dim3(tiles), dim3(64 * WGM * WGN), 0,
+        hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_GATE>), dim3(tiles), dim3(64 * WGM * WGN), 0,
                            stream, X, W, rows, N, K, out, aux);
     else
-        hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, EPI_BF16>), dim3(tiles), dim3(64 * WGM * WGN), 0,
+        hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_BF16>), dim3(tiles), dim3(64 * WGM * WGN), 0,
                            stream, X, W, rows, N, K, out, aux);
     return hipGetLastError();
 }
@@ -196,7 +210,7 @@ hipError_t launch_tile(const bf16_t *X, const bf16_t *W, int rows, int N, int K,
 
 hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
                        const bf16_t *aux, hipStream_t stream) {
-    return launch_tile<128, 128, 2, 2, 2>(X, W, rows, N, K, epi, out, aux, stream);
+    return launch_tile<128, 128, 2, 2, 2, 64>(X, W, rows, N, K, epi, out, aux, stream);
 }
 
 }  // namespace sambay
