@@ -59,6 +59,16 @@ def _load():
     lib.oracle_crossdecoder.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i32,
                                         i64, i64, i64, i64, i64, i64, i64, dbl, ctypes.c_int, vp, vp]
     lib.oracle_crossdecoder.restype = ctypes.c_int
+    lib.oracle_xattn_varlen.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, i64, i64, i64, i64, i64, dbl]
+    lib.oracle_xattn_varlen.restype = ctypes.c_int
+    lib.oracle_rmsnorm.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, dbl, vp]
+    lib.oracle_rmsnorm.restype = ctypes.c_int
+    lib.oracle_swiglu.argtypes = [vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
+    lib.oracle_swiglu.restype = ctypes.c_int
+    lib.oracle_crossdecoder_ex.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
+                                           vp, vp, ctypes.c_int, i32, i64, i64, i64, i64, i64, i64, i64, i64, dbl,
+                                           dbl, ctypes.c_int, vp]
+    lib.oracle_crossdecoder_ex.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [dbl]
     lib.oracle_round_bf16.restype = dbl
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -252,4 +262,124 @@ def crossdecoder(h, M, K, V, layers: Sequence, Hq: int, scale: float | None = No
     _check(rc, "crossdecoder")
     if count_bytes:
         return out, [_bytes_dict(nb[i]) for i in range(n)]
+    return out
+
+
+def _lens_array(lens, B: int, L: int) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(lens.cpu() if hasattr(lens, "cpu") else lens), dtype=np.int32)
+    if a.shape != (B,):
+        raise ValueError("lens must have one entry per sequence")
+    if a.min(initial=0) < 0 or a.max(initial=0) > L:
+        raise ValueError("lens must lie in [0, L]")
+    return a
+
+
+def xattn_varlen(q, K, V, lens, scale: float | None = None):
+    """Ragged-batch attention: sequence b attends to its first lens[b] of the L
+    cached positions (lens[b] == 0 gives zeros).  K, V [B, Hkv, L, D]."""
+    lib = _load()
+    qa, dq = _as_input(q)
+    ka, dk = _as_input(K)
+    va, dv = _as_input(V)
+    if dk != dv:
+        raise TypeError("K and V must share a dtype")
+    B, Hq, Hkv, D, L = _xattn_shapes(qa, ka, va)
+    la = _lens_array(lens, B, L)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    rc = lib.oracle_xattn_varlen(_ptr(qa), dq, _ptr(ka), _ptr(va), dk, _ptr(la), _ptr(out), B, Hq, Hkv, D, L,
+                                 float(scale))
+    _check(rc, "xattn_varlen")
+    return out
+
+
+def rmsnorm(x, g, eps: float = 1e-5):
+    """Row-wise RMSNorm: x / sqrt(mean(x^2) + eps) * g over the last axis."""
+    lib = _load()
+    xa, dx = _as_input(x)
+    ga, dg = _as_input(g)
+    n = xa.shape[-1]
+    if ga.shape != (n,):
+        raise ValueError("gain shape mismatch")
+    out = np.empty(xa.shape, dtype=np.float64)
+    rc = lib.oracle_rmsnorm(_ptr(xa), dx, _ptr(ga), dg, xa.size // n, n, float(eps), _ptr(out))
+    _check(rc, "rmsnorm")
+    return out
+
+
+def swiglu(x, Wg, Wu, Wd):
+    """Row-wise SwiGLU MLP: (SiLU(x Wg^T) * (x Wu^T)) Wd^T."""
+    lib = _load()
+    xa, dx = _as_input(x)
+    ga, dg = _as_input(Wg)
+    ua, du = _as_input(Wu)
+    da, dd = _as_input(Wd)
+    if not (dg == du == dd):
+        raise TypeError("MLP weights must share a dtype")
+    rows, d_model = xa.shape
+    d_ff = ga.shape[0]
+    if ga.shape != (d_ff, d_model) or ua.shape != (d_ff, d_model) or da.shape != (d_model, d_ff):
+        raise ValueError("MLP weight shape mismatch")
+    out = np.empty((rows, d_model), dtype=np.float64)
+    rc = lib.oracle_swiglu(_ptr(xa), dx, _ptr(ga), _ptr(ua), _ptr(da), dg, rows, d_model, d_ff, _ptr(out))
+    _check(rc, "swiglu")
+    return out
+
+
+def crossdecoder_ex(h, M, K, V, layers: Sequence, Hq: int, lens=None, eps: float = 1e-5,
+                    scale: float | None = None, round_bf16: bool = True):
+    """One decode step of the complete cross-decoder (pre-RMSNorm mixer, optional
+    pre-RMSNorm SwiGLU MLP, ragged cache lengths).  layers: sequence of dicts with
+    keys kind ("xattn" or "gmu"), w_a, w_b and optional norm1, norm2, w_gate,
+    w_up, w_down (absent or None: no norm / no MLP).  lens: None or [B] ints in
+    [0, L].  Returns the final h (float64)."""
+    lib = _load()
+    ha, dh = _as_input(h)
+    ma, dm = _as_input(M)
+    ka, dk = _as_input(K)
+    va, dv = _as_input(V)
+    if dh != dm or dk != dv:
+        raise TypeError("h/M and K/V must share dtypes")
+    B, d_model = ha.shape
+    d_inner = ma.shape[1]
+    B2, Hkv, L, D = ka.shape
+    if B2 != B or ma.shape[0] != B or va.shape != ka.shape or Hq * D != d_model:
+        raise ValueError("crossdecoder shape mismatch")
+    la = _lens_array(lens, B, L) if lens is not None else None
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    n = len(layers)
+    N = max(n, 1)
+    kinds = np.zeros(N, dtype=np.int32)
+    ptrs = {k: (ctypes.c_void_p * N)() for k in ("w_a", "w_b", "norm1", "norm2", "w_gate", "w_up", "w_down")}
+    keep, dw, d_ff = [], None, 0
+    for i, ly in enumerate(layers):
+        kind = ly["kind"]
+        if kind not in ("xattn", "gmu"):
+            raise ValueError("layer kind must be 'xattn' or 'gmu'")
+        kinds[i] = XATTN if kind == "xattn" else GMU
+        for key in ptrs:
+            t = ly.get(key)
+            if t is None:
+                continue
+            a, da = _as_input(t)
+            if dw is None:
+                dw = da
+            if da != dw:
+                raise TypeError("all layer weights must share a dtype")
+            if key == "w_gate":
+                if d_ff and a.shape[0] != d_ff:
+                    raise ValueError("all MLPs must share d_ff")
+                d_ff = a.shape[0]
+            keep.append(a)
+            ptrs[key][i] = a.ctypes.data
+    out = np.empty((B, d_model), dtype=np.float64)
+    c = lambda k: ctypes.cast(ptrs[k], ctypes.c_void_p)
+    rc = lib.oracle_crossdecoder_ex(_ptr(ha), _ptr(ma), dh, _ptr(ka), _ptr(va), dk,
+                                    _ptr(la) if la is not None else None, _ptr(kinds), c("w_a"), c("w_b"),
+                                    c("norm1"), c("norm2"), c("w_gate"), c("w_up"), c("w_down"),
+                                    dw if dw is not None else F64, n, B, d_model, d_inner, d_ff, Hq, Hkv, D, L,
+                                    float(scale), float(eps), 1 if round_bf16 else 0, _ptr(out))
+    _check(rc, "crossdecoder_ex")
     return out

@@ -465,6 +465,247 @@ int oracle_crossdecoder(const void *h0, const void *M, int dt_act, const void *K
     return fail;
 }
 
+/* ------------------------------------- ragged batch and the complete layer
+ *
+ * The pages define the GMU and the shared-cache cross-attention but not the
+ * rest of a layer.  The complete cross-decoder layer below takes the plain
+ * Transformer reading: a pre-normalised residual mixer (cross-attention or
+ * GMU) followed by a pre-normalised residual SwiGLU MLP, RMSNorm as the norm.
+ * A serving batch holds sequences at different lengths: the cache has room
+ * for L positions per (sequence, KV head) and sequence b uses its first
+ * lens[b] of them. */
+
+/* Attention of a ragged batch.  K, V [B, Hkv, L, D] hold room for L
+ * positions; sequence b attends to positions 0 .. lens[b]-1 (0 <= lens[b] <=
+ * L).  lens[b] == 0 leaves the softmax without terms and is defined to give a
+ * zero output. */
+int oracle_xattn_varlen(const void *q, int dt_q, const void *K, const void *V, int dt_kv, const int32_t *lens,
+                        double *out, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L, double scale) {
+    if (!q || !K || !V || !lens || !out || !xattn_args_ok(B, Hq, Hkv, D, L)) return -1;
+    for (int64_t b = 0; b < B; ++b)
+        if (lens[b] < 0 || lens[b] > L) return -1;
+    const int64_t G = Hq / Hkv;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)L * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * Hq; ++bh) {
+            if (!s) continue;
+            int64_t b = bh / Hq, h = bh % Hq, g = h / G;
+            if (lens[b] == 0) {
+                for (int64_t d = 0; d < D; ++d) out[bh * D + d] = 0.0;
+                continue;
+            }
+            xattn_head(q, dt_q, bh * D, K, V, dt_kv, (b * Hkv + g) * L * D, out + bh * D, D, lens[b], scale, s, NULL,
+                       0, 0, 0);
+        }
+        free(s);
+    }
+    return fail ? -2 : 0;
+}
+
+/* RMSNorm of one row: y_i = x_i / sqrt(mean_j x_j^2 + eps) * g_i. */
+static void rmsnorm_row(const double *x, const void *g, int dt_g, int64_t n, double eps, double *y) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; ++i) ss += x[i] * x[i];
+    const double r = 1.0 / sqrt(ss / (double)n + eps);
+    for (int64_t i = 0; i < n; ++i) y[i] = x[i] * r * widen(g, dt_g, i);
+}
+
+/* SwiGLU MLP of one row: u_k = SiLU(x . Wg[k]) * (x . Wu[k]) for k < d_ff,
+ * y_n = u . Wd[n] for n < d_model (Wg, Wu [d_ff, d_model], Wd [d_model, d_ff]). */
+static void swiglu_row(const double *x, const void *Wg, const void *Wu, const void *Wd, int dt_w, int64_t d_model,
+                       int64_t d_ff, double *u, double *y) {
+    for (int64_t k = 0; k < d_ff; ++k) {
+        double a = 0.0, b = 0.0;
+        for (int64_t c = 0; c < d_model; ++c) {
+            a += x[c] * widen(Wg, dt_w, k * d_model + c);
+            b += x[c] * widen(Wu, dt_w, k * d_model + c);
+        }
+        u[k] = a / (1.0 + exp(-a)) * b;
+    }
+    for (int64_t n = 0; n < d_model; ++n) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < d_ff; ++k) acc += u[k] * widen(Wd, dt_w, n * d_ff + k);
+        y[n] = acc;
+    }
+}
+
+/* Row-wise RMSNorm of x [rows, n] (any input dtype) with gain g [n]. */
+int oracle_rmsnorm(const void *x, int dt_x, const void *g, int dt_g, int64_t rows, int64_t n, double eps,
+                   double *out) {
+    if (!x || !g || !out || rows < 0 || n <= 0 || !(eps >= 0.0)) return -1;
+    double *xr = (double *)malloc((size_t)n * sizeof(double));
+    if (!xr) return -2;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t i = 0; i < n; ++i) xr[i] = widen(x, dt_x, r * n + i);
+        rmsnorm_row(xr, g, dt_g, n, eps, out + r * n);
+    }
+    free(xr);
+    return 0;
+}
+
+/* Row-wise SwiGLU MLP of x [rows, d_model]. */
+int oracle_swiglu(const void *x, int dt_x, const void *Wg, const void *Wu, const void *Wd, int dt_w, int64_t rows,
+                  int64_t d_model, int64_t d_ff, double *out) {
+    if (!x || !Wg || !Wu || !Wd || !out || rows < 0 || d_model <= 0 || d_ff <= 0) return -1;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *xr = (double *)malloc((size_t)d_model * sizeof(double));
+        double *u = (double *)malloc((size_t)d_ff * sizeof(double));
+        if (!xr || !u) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < rows; ++r) {
+            if (!xr || !u) continue;
+            for (int64_t i = 0; i < d_model; ++i) xr[i] = widen(x, dt_x, r * d_model + i);
+            swiglu_row(xr, Wg, Wu, Wd, dt_w, d_model, d_ff, u, out + r * d_model);
+        }
+        free(xr);
+        free(u);
+    }
+    return fail ? -2 : 0;
+}
+
+/* One decode step of the complete cross-decoder.  For each layer l, with
+ * x = RMSNorm(h; norm1[l]) (x = h when norm1[l] is NULL):
+ *   cross-attention: q = x Wq^T; o = ragged attention(q, K, V, lens); y = o Wo^T
+ *   GMU:             y = GMU(M, x, W1, W2)
+ *   h = h + y                                  (rounded to bf16 if round_bf16)
+ * then, when wg[l] is not NULL, with x = RMSNorm(h; norm2[l]) (or h):
+ *   h = h + SwiGLU(x; Wg, Wu, Wd)              (rounded to bf16 if round_bf16)
+ * lens may be NULL (every sequence uses all L positions).  Norm gains and
+ * weights share dtype dt_w. */
+int oracle_crossdecoder_ex(const void *h0, const void *M, int dt_act, const void *K, const void *V, int dt_kv,
+                           const int32_t *lens, const int32_t *kinds, const void *const *wa, const void *const *wb,
+                           const void *const *norm1, const void *const *norm2, const void *const *wg,
+                           const void *const *wu, const void *const *wd, int dt_w, int32_t n_layers, int64_t B,
+                           int64_t d_model, int64_t d_inner, int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t D,
+                           int64_t L, double scale, double eps, int round_bf16, double *h_out) {
+    if (!h0 || !M || !K || !V || !kinds || !wa || !wb || !norm1 || !norm2 || !wg || !wu || !wd || !h_out ||
+        n_layers < 0 || B < 0 || d_model <= 0 || d_inner <= 0 || d_ff < 0 || !xattn_args_ok(B, Hq, Hkv, D, L) ||
+        Hq * D != d_model || !(eps >= 0.0))
+        return -1;
+    if (lens)
+        for (int64_t b = 0; b < B; ++b)
+            if (lens[b] < 0 || lens[b] > L) return -1;
+    const int64_t G = Hq / Hkv;
+    const size_t nbd = (size_t)(B * d_model) * sizeof(double);
+    double *h = (double *)malloc(nbd), *x = (double *)malloc(nbd), *y = (double *)malloc(nbd);
+    double *qv = (double *)malloc(nbd), *o = (double *)malloc(nbd);
+    if (!h || !x || !y || !qv || !o) {
+        free(h); free(x); free(y); free(qv); free(o);
+        return -2;
+    }
+    for (int64_t i = 0; i < B * d_model; ++i) h[i] = widen(h0, dt_act, i);
+    int fail = 0;
+    for (int32_t li = 0; li < n_layers && !fail; ++li) {
+        if (!wa[li] || !wb[li] || (kinds[li] != 0 && kinds[li] != 1) || (wg[li] && (!wu[li] || !wd[li] || d_ff == 0))) {
+            fail = -1;
+            break;
+        }
+        for (int64_t r = 0; r < B; ++r) {
+            if (norm1[li])
+                rmsnorm_row(h + r * d_model, norm1[li], dt_w, d_model, eps, x + r * d_model);
+            else
+                memcpy(x + r * d_model, h + r * d_model, (size_t)d_model * sizeof(double));
+        }
+        if (kinds[li] == 0) {
+#pragma omp parallel for schedule(static)
+            for (int64_t i = 0; i < B * d_model; ++i) {
+                int64_t b = i / d_model, n = i % d_model;
+                double acc = 0.0;
+                for (int64_t c = 0; c < d_model; ++c) acc += x[b * d_model + c] * widen(wa[li], dt_w, n * d_model + c);
+                qv[i] = acc;
+            }
+#pragma omp parallel
+            {
+                double *s = (double *)malloc((size_t)L * sizeof(double));
+                if (!s) {
+#pragma omp atomic write
+                    fail = -2;
+                }
+#pragma omp for schedule(dynamic, 1)
+                for (int64_t bh = 0; bh < B * Hq; ++bh) {
+                    if (!s) continue;
+                    int64_t b = bh / Hq, hh = bh % Hq, g = hh / G;
+                    int64_t Lb = lens ? lens[b] : L;
+                    if (Lb == 0) {
+                        for (int64_t d = 0; d < D; ++d) o[bh * D + d] = 0.0;
+                        continue;
+                    }
+                    xattn_head(qv, OR_F64, bh * D, K, V, dt_kv, (b * Hkv + g) * L * D, o + bh * D, D, Lb, scale, s,
+                               NULL, 0, 0, 0);
+                }
+                free(s);
+            }
+#pragma omp parallel for schedule(static)
+            for (int64_t i = 0; i < B * d_model; ++i) {
+                int64_t b = i / d_model, n = i % d_model;
+                double acc = 0.0;
+                for (int64_t c = 0; c < d_model; ++c) acc += o[b * d_model + c] * widen(wb[li], dt_w, n * d_model + c);
+                y[i] = acc;
+            }
+        } else {
+#pragma omp parallel
+            {
+                double *H = (double *)malloc((size_t)d_inner * sizeof(double));
+                if (!H) {
+#pragma omp atomic write
+                    fail = -2;
+                }
+#pragma omp for schedule(static)
+                for (int64_t r = 0; r < B; ++r) {
+                    if (!H) continue;
+                    gmu_row(M, dt_act, x, OR_F64, wa[li], wb[li], dt_w, y + r * d_model, r, d_model, d_inner, H, NULL,
+                            0, 0, 0, 0);
+                }
+                free(H);
+            }
+        }
+        for (int64_t i = 0; i < B * d_model; ++i) {
+            double v = h[i] + y[i];
+            h[i] = round_bf16 ? oracle_round_bf16(v) : v;
+        }
+        if (fail || !wg[li]) continue;
+        for (int64_t r = 0; r < B; ++r) {
+            if (norm2[li])
+                rmsnorm_row(h + r * d_model, norm2[li], dt_w, d_model, eps, x + r * d_model);
+            else
+                memcpy(x + r * d_model, h + r * d_model, (size_t)d_model * sizeof(double));
+        }
+#pragma omp parallel
+        {
+            double *u = (double *)malloc((size_t)d_ff * sizeof(double));
+            if (!u) {
+#pragma omp atomic write
+                fail = -2;
+            }
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < B; ++r) {
+                if (!u) continue;
+                swiglu_row(x + r * d_model, wg[li], wu[li], wd[li], dt_w, d_model, d_ff, u, y + r * d_model);
+            }
+            free(u);
+        }
+        for (int64_t i = 0; i < B * d_model; ++i) {
+            double v = h[i] + y[i];
+            h[i] = round_bf16 ? oracle_round_bf16(v) : v;
+        }
+    }
+    if (!fail) memcpy(h_out, h, nbd);
+    free(h); free(x); free(y); free(qv); free(o);
+    return fail;
+}
+
 /* --------------------------------------------------------------- threads */
 
 int oracle_max_threads(void) {

@@ -27,7 +27,15 @@ GMU_PREFILL = dict(batch=4, seq=2048, d_model=2560, d_inner=5120)        # bf16
 GMU_DECODE = dict(batches=(1, 8, 32, 64), d_model=3072, d_inner=6144)    # bf16
 XATTN_DECODE = dict(B=16, Hq=24, Hkv=8, D=128, L=34816)                  # bf16
 CROSSDECODER = dict(B=32, d_model=3072, d_inner=6144, Hq=24, Hkv=8, D=128, L=34816, n_layers=16)  # bf16
+# Ragged serving batch: every sequence has its 2048-token prompt and is somewhere
+# in its 32K-token generation, so cache lengths are uniform in [2048, 34816].
+XATTN_VARLEN = dict(B=32, Hq=24, Hkv=8, D=128, L=34816, min_len=2048)    # bf16
+# The complete layer adds a pre-RMSNorm SwiGLU MLP (d_ff = 8192, about 8/3 of
+# d_model) and pre-RMSNorms to the same stack, over the ragged batch.
+CROSSDECODER_EX = dict(B=32, d_model=3072, d_inner=6144, d_ff=8192, Hq=24, Hkv=8, D=128, L=34816, n_layers=16,
+                       min_len=2048)
 WEIGHT_STD = 0.02
+NORM_GAIN_STD = 0.1
 
 
 def _gen(device, seed: int) -> torch.Generator:
@@ -161,3 +169,57 @@ def crossdecoder_inputs(B: int, d_model: int, d_inner: int, Hq: int, Hkv: int, D
             raise ValueError(kind)
         layers.append((kind, wa, wb))
     return CrossDecoderInputs(h=h, M=M, K=K, V=V, layers=layers)
+
+
+# ------------------------------------------ ragged batch, complete layer
+
+def ragged_lens(B: int, L: int, *, seed: int = 0, min_len: int = 1, device="cpu") -> torch.Tensor:
+    """int32 cache lengths, uniform over [min_len, L] (seeded)."""
+    g = _gen("cpu", _seed(seed, 41))
+    lens = torch.randint(min_len, L + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+    return lens.to(device)
+
+
+@dataclass
+class CrossDecoderExInputs:
+    h: torch.Tensor
+    M: torch.Tensor
+    K: torch.Tensor
+    V: torch.Tensor
+    lens: torch.Tensor | None       # [B] int32 or None (all L positions)
+    layers: list = field(default_factory=list)   # dicts: kind, w_a, w_b, norm1, norm2, w_gate, w_up, w_down
+
+
+def crossdecoder_ex_inputs(B: int, d_model: int, d_inner: int, d_ff: int, Hq: int, Hkv: int, D: int, L: int,
+                           n_layers: int, *, seed: int = 0, device="cpu", dtype=torch.bfloat16, kinds=None,
+                           lens="ragged", min_len: int = 1, norms: bool = True, mlp: bool = True
+                           ) -> CrossDecoderExInputs:
+    """The cross-decoder inputs plus, per layer, RMSNorm gains 1 + N(0, 0.1^2)
+    (norm1 before the mixer, norm2 before the MLP) and SwiGLU weights
+    ~ N(0, 0.02^2): w_gate, w_up [d_ff, d_model], w_down [d_model, d_ff].
+    lens: "ragged" (uniform in [min_len, L]), None, or an explicit list."""
+    base = crossdecoder_inputs(B, d_model, d_inner, Hq, Hkv, D, L, n_layers, seed=seed, device=device, dtype=dtype,
+                               kinds=kinds)
+    if isinstance(lens, str):
+        lens_t = ragged_lens(B, L, seed=seed, min_len=min_len, device=device)
+    elif lens is None:
+        lens_t = None
+    else:
+        lens_t = torch.tensor(list(lens), dtype=torch.int32, device=device)
+    layers = []
+    for i, (kind, wa, wb) in enumerate(base.layers):
+        ly = dict(kind=kind, w_a=wa, w_b=wb, norm1=None, norm2=None, w_gate=None, w_up=None, w_down=None)
+        if norms:
+            for j, key in enumerate(("norm1", "norm2")):
+                gsd = normal((d_model,), std=NORM_GAIN_STD, seed=_seed(seed, 50, 2 * i + j), device=device,
+                             dtype=torch.float32)
+                ly[key] = (1.0 + gsd).to(dtype)
+        if mlp:
+            ly["w_gate"] = normal((d_ff, d_model), std=WEIGHT_STD, seed=_seed(seed, 60, 3 * i), device=device,
+                                  dtype=dtype)
+            ly["w_up"] = normal((d_ff, d_model), std=WEIGHT_STD, seed=_seed(seed, 60, 3 * i + 1), device=device,
+                                dtype=dtype)
+            ly["w_down"] = normal((d_model, d_ff), std=WEIGHT_STD, seed=_seed(seed, 60, 3 * i + 2), device=device,
+                                  dtype=dtype)
+        layers.append(ly)
+    return CrossDecoderExInputs(h=base.h, M=base.M, K=base.K, V=base.V, lens=lens_t, layers=layers)
