@@ -1,0 +1,75 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case below plants one mistake (a dropped term, a wrong sign, a swapped
+operand, a wrong index or stride) in a private copy of oracle.c, rebuilds it
+in a temporary directory and runs the pin file that should catch it; the
+case passes only if that pin run fails.  Nothing here touches the product
+library or a GPU.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (name, pin file, original text, planted text)
+MUTANTS = [
+    ("gmu_sigmoid_sign", "test_oracle_gmu.py",
+     "double g = z / (1.0 + exp(-z));", "double g = z / (1.0 + exp(z));"),
+    ("gmu_gate_without_memory", "test_oracle_gmu.py",
+     "H[k] = widen(M, dt_m, r * d_inner + k) * g;", "H[k] = g;"),
+    ("gmu_w2_transposed", "test_oracle_gmu.py",
+     "acc += H[k] * widen(W2, dt_w, o * d_inner + k);", "acc += H[k] * widen(W2, dt_w, k * d_model + o);"),
+    ("gmu_gate_on_wrong_channel", "test_oracle_gmu.py",
+     "H[k] = widen(M, dt_m, r * d_inner + k) * g;", "H[k] = widen(M, dt_m, r * d_inner + (d_inner - 1 - k)) * g;"),
+    ("xattn_scale_dropped", "test_oracle_xattn.py", "s[j] = dot * scale;", "s[j] = dot;"),
+    ("xattn_no_normalisation", "test_oracle_xattn.py", "for (int64_t d = 0; d < D; ++d) out[d] /= den;",
+     "for (int64_t d = 0; d < D; ++d) out[d] /= 1.0;"),
+    ("xattn_wrong_group_map", "test_oracle_xattn.py",
+     "int64_t b = bh / Hq, h = bh % Hq, g = h / G;\n            xattn_head(q, dt_q, bh * D, K, V, dt_kv, (b * Hkv + g) * L * D, out + bh * D, D, L, scale, s, tr, 0, 1, 2);",
+     "int64_t b = bh / Hq, h = bh % Hq, g = h % Hkv;\n            xattn_head(q, dt_q, bh * D, K, V, dt_kv, (b * Hkv + g) * L * D, out + bh * D, D, L, scale, s, tr, 0, 1, 2);"),
+    ("chunked_merge_without_rescale", "test_oracle_xattn.py",
+     "for (int64_t c = 0; c < nc; ++c) l += lc[c] * exp(mc[c] - M);", "for (int64_t c = 0; c < nc; ++c) l += lc[c];"),
+    ("round_bf16_truncates", "test_oracle_crossdecoder.py",
+     "double r = nearbyint(ldexp(x, -q));", "double r = trunc(ldexp(x, -q));"),
+    ("crossdecoder_no_residual", "test_oracle_crossdecoder.py",
+     "        for (int64_t i = 0; i < B * d_model; ++i) {\n            trk_mark(tr, 0, i);\n            trk_mark(tr, 1, i);\n            double v = h[i] + y[i];",
+     "        for (int64_t i = 0; i < B * d_model; ++i) {\n            trk_mark(tr, 0, i);\n            trk_mark(tr, 1, i);\n            double v = y[i];"),
+    ("rmsnorm_sum_not_mean", "test_oracle_ex.py", "ss / (double)n + eps", "ss + eps"),
+    ("rmsnorm_eps_outside_root", "test_oracle_ex.py", "1.0 / sqrt(ss / (double)n + eps)",
+     "1.0 / (sqrt(ss / (double)n) + eps)"),
+    ("swiglu_gate_up_swapped", "test_oracle_ex.py", "u[k] = a / (1.0 + exp(-a)) * b;",
+     "u[k] = b / (1.0 + exp(-b)) * a;"),
+    ("varlen_stride_uses_length", "test_oracle_ex.py",
+     "(b * Hkv + g) * L * D, out + bh * D, D, lens[b], scale, s, NULL,",
+     "(b * Hkv + g) * lens[b] * D, out + bh * D, D, lens[b], scale, s, NULL,"),
+    ("ex_gmu_takes_unnormalised_h", "test_oracle_ex.py",
+     "gmu_row(M, dt_act, x, OR_F64, wa[li], wb[li], dt_w, y + r * d_model, r, d_model, d_inner, H, NULL,",
+     "gmu_row(M, dt_act, h, OR_F64, wa[li], wb[li], dt_w, y + r * d_model, r, d_model, d_inner, H, NULL,"),
+    ("ex_mlp_uses_mixer_norm", "test_oracle_ex.py",
+     "rmsnorm_row(h + r * d_model, norm2[li], dt_w, d_model, eps, x + r * d_model);",
+     "rmsnorm_row(h + r * d_model, norm1[li], dt_w, d_model, eps, x + r * d_model);"),
+    ("ex_attention_ignores_lengths", "test_oracle_ex.py", "int64_t Lb = lens ? lens[b] : L;", "int64_t Lb = L;"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(os.path.join(ROOT, "oracle", "oracle.c")) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,pins,orig,planted", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, source, name, pins, orig, planted):
+    assert source.count(orig) >= 1, "mutation site for %s not found in oracle.c" % name
+    for d in ("oracle", "workload", "tests"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("*.so", "__pycache__", "*.tmp*"))
+    shutil.copy(os.path.join(ROOT, "pytest.ini"), tmp_path)
+    (tmp_path / "oracle" / "oracle.c").write_text(source.replace(orig, planted, 1))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-m", "not gpu", "-p", "no:cacheprovider",
+                        os.path.join("tests", pins)], cwd=tmp_path, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1, "planted mistake %r survived %s:\n%s" % (name, pins, r.stdout[-2000:])
