@@ -31,13 +31,20 @@ SB_LAYER_XATTN, SB_LAYER_GMU = 0, 1
 # Every function the header declares, for load-time checking.
 EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", "xattn_workspace_bytes",
            "xattn_decode", "crossdecoder_workspace_bytes", "crossdecoder_step", "sb_timing_enable",
-           "sb_timing_collect", "sb_probe_stream_read", "sb_probe_mfma", "sb_probe_mfma_flops")
+           "sb_timing_collect", "sb_probe_stream_read", "sb_probe_mfma", "sb_probe_mfma_flops",
+           "xattn_decode_varlen", "crossdecoder_ex_workspace_bytes", "crossdecoder_step_ex")
 SB_TIME_XATTN_SPLIT, SB_TIME_XATTN_MERGE, SB_TIME_SKINNY, SB_TIME_GEMM, SB_TIME_GMU_F32, SB_TIME_PROBE = \
     1, 2, 4, 8, 16, 32
 
 
 class SbLayer(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("w_a", ctypes.c_void_p), ("w_b", ctypes.c_void_p)]
+
+
+class SbLayerEx(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("w_a", ctypes.c_void_p), ("w_b", ctypes.c_void_p),
+                ("norm1", ctypes.c_void_p), ("norm2", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
 
 
 class SambayError(RuntimeError):
@@ -66,6 +73,13 @@ def _load() -> ctypes.CDLL:
     lib.crossdecoder_step.argtypes = [vp, vp, vp, vp, ctypes.POINTER(SbLayer), i32, i64, i64, i64, i64, i64, i64,
                                       i64, ctypes.c_float, vp, sz, vp]
     lib.crossdecoder_step.restype = ctypes.c_int
+    lib.xattn_decode_varlen.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, sz, vp]
+    lib.xattn_decode_varlen.restype = ctypes.c_int
+    lib.crossdecoder_ex_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64]
+    lib.crossdecoder_ex_workspace_bytes.restype = sz
+    lib.crossdecoder_step_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(SbLayerEx), i32, i64, i64, i64, i64, i64,
+                                         i64, i64, i64, ctypes.c_float, ctypes.c_float, vp, sz, vp]
+    lib.crossdecoder_step_ex.restype = ctypes.c_int
     lib.sb_timing_enable.argtypes = [ctypes.c_uint32]
     lib.sb_timing_enable.restype = ctypes.c_int
     lib.sb_timing_collect.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -199,9 +213,10 @@ def gmu_forward(M: torch.Tensor, X: torch.Tensor, W1: torch.Tensor, W2: torch.Te
 
 
 def xattn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, out: torch.Tensor | None = None,
-                 scale: float | None = None) -> torch.Tensor:
-    """Decode attention of q [B, Hq, D] over the whole shared cache
-    kcache/vcache [B, Hkv, L, D]; bf16 in and out."""
+                 scale: float | None = None, lens: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention of q [B, Hq, D] over the shared cache kcache/vcache
+    [B, Hkv, L, D]; bf16 in and out.  lens (optional, [B] int32 on the same
+    GPU): sequence b attends to its first lens[b] positions only."""
     dev = _check_device(q, "q")
     bf = torch.bfloat16
     if q.dim() != 3 or kcache.dim() != 4:
@@ -219,10 +234,15 @@ def xattn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, ou
         raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), (B, Hq, D)))
     nb = lib.xattn_workspace_bytes(B, Hq, Hkv, D, L)
     ws = _workspace(dev, nb)
-    st = lib.xattn_decode(_dev_ptr(q, "q", bf, dev), _dev_ptr(kcache, "kcache", bf, dev),
-                          _dev_ptr(vcache, "vcache", bf, dev), _dev_ptr(out, "out", bf, dev), B, Hq, Hkv, D, L,
-                          float(scale), ws.data_ptr(), ws.numel(), _stream(dev))
-    _check("xattn_decode", st)
+    args = (_dev_ptr(q, "q", bf, dev), _dev_ptr(kcache, "kcache", bf, dev), _dev_ptr(vcache, "vcache", bf, dev))
+    tail = (B, Hq, Hkv, D, L, float(scale), ws.data_ptr(), ws.numel(), _stream(dev))
+    if lens is None:
+        _check("xattn_decode", lib.xattn_decode(*args, _dev_ptr(out, "out", bf, dev), *tail))
+    else:
+        if lens.shape != (B,):
+            raise ValueError("lens must have shape [B]")
+        lp = _dev_ptr(lens, "lens", torch.int32, dev)
+        _check("xattn_decode_varlen", lib.xattn_decode_varlen(*args, lp, _dev_ptr(out, "out", bf, dev), *tail))
     return out
 
 
@@ -289,5 +309,75 @@ def crossdecoder_step(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor, vc
     return CrossDecoderStep(h, M, kcache, vcache, layers, scale)()
 
 
-__all__ = ["gmu_forward", "xattn_decode", "crossdecoder_step", "CrossDecoderStep", "SambayError", "version", "lib",
+_EX_KEYS = ("norm1", "norm2", "w_gate", "w_up", "w_down")
+
+
+class CrossDecoderStepEx:
+    """Prepared complete-layer decode step (pre-RMSNorm mixer, optional
+    pre-RMSNorm SwiGLU MLP, optional ragged cache lengths).  layers: sequence of
+    dicts with keys kind, w_a, w_b and optional norm1, norm2, w_gate, w_up,
+    w_down (None: absent).  lens: None or [B] int32 on the same GPU."""
+
+    def __init__(self, h, M, kcache, vcache, layers: Sequence, lens: torch.Tensor | None = None,
+                 eps: float = 1e-5, scale: float | None = None):
+        dev = _check_device(h, "h")
+        bf = torch.bfloat16
+        if h.dim() != 2 or M.dim() != 2 or kcache.dim() != 4:
+            raise ValueError("h [B, d_model], M [B, d_inner], kcache [B, Hkv, L, D]")
+        B, d_model = h.shape
+        d_inner = M.shape[1]
+        B2, Hkv, L, D = kcache.shape
+        if M.shape[0] != B or B2 != B or vcache.shape != kcache.shape:
+            raise ValueError("crossdecoder_step_ex shape mismatch")
+        if d_model % D != 0:
+            raise ValueError("d_model must be a multiple of the head dim")
+        Hq = d_model // D
+        d_ff = 0
+        for ly in layers:
+            if ly.get("w_gate") is not None:
+                d_ff = ly["w_gate"].shape[0]
+        arr = (SbLayerEx * max(len(layers), 1))()
+        base = _layer_array([(ly["kind"], ly["w_a"], ly["w_b"]) for ly in layers], dev, d_model, d_inner)
+        for i, ly in enumerate(layers):
+            arr[i].kind, arr[i].w_a, arr[i].w_b = base[i].kind, base[i].w_a, base[i].w_b
+            shapes = {"norm1": (d_model,), "norm2": (d_model,), "w_gate": (d_ff, d_model), "w_up": (d_ff, d_model),
+                      "w_down": (d_model, d_ff)}
+            for key in _EX_KEYS:
+                t = ly.get(key)
+                if t is None:
+                    continue
+                if tuple(t.shape) != shapes[key]:
+                    raise ValueError("layer %d %s has shape %s, expected %s" % (i, key, tuple(t.shape), shapes[key]))
+                setattr(arr[i], key, _dev_ptr(t, "layer %d %s" % (i, key), bf, dev))
+        if lens is not None and lens.shape != (B,):
+            raise ValueError("lens must have shape [B]")
+        self.lens_ptr = _dev_ptr(lens, "lens", torch.int32, dev) if lens is not None else None
+        self.dims = (B, d_model, d_inner, d_ff, Hq, Hkv, D, L)
+        self.scale = float(1.0 / math.sqrt(D) if scale is None else scale)
+        self.eps = float(eps)
+        self.tensors = (h, M, kcache, vcache, layers, lens)
+        self.ptrs = (_dev_ptr(h, "h", bf, dev), _dev_ptr(M, "M", bf, dev), _dev_ptr(kcache, "kcache", bf, dev),
+                     _dev_ptr(vcache, "vcache", bf, dev))
+        self.arr = arr
+        self.n_layers = len(layers)
+        nb = lib.crossdecoder_ex_workspace_bytes(*self.dims)
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        self.device = dev
+
+    def __call__(self):
+        st = lib.crossdecoder_step_ex(*self.ptrs, self.lens_ptr, self.arr, self.n_layers, *self.dims, self.scale,
+                                      self.eps, self.ws.data_ptr(), self.ws.numel(), _stream(self.device))
+        _check("crossdecoder_step_ex", st)
+        return self.tensors[0]
+
+
+def crossdecoder_step_ex(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                         layers: Sequence, lens: torch.Tensor | None = None, eps: float = 1e-5,
+                         scale: float | None = None) -> torch.Tensor:
+    """One complete-layer cross-decoder decode step; h is updated in place."""
+    return CrossDecoderStepEx(h, M, kcache, vcache, layers, lens, eps, scale)()
+
+
+__all__ = ["gmu_forward", "xattn_decode", "crossdecoder_step", "CrossDecoderStep", "crossdecoder_step_ex",
+           "CrossDecoderStepEx", "SambayError", "version", "lib",
            "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect", "probe_stream_read_gbps", "probe_mfma_tflops"]

@@ -98,9 +98,9 @@ size_t gmu_ws(int64_t rows, int64_t d_model, int64_t d_inner, sb_dtype dt) {
 // h_lo the gated hidden H travels as a bf16 hi + lo pair between them (used in
 // the layer stack, where rounding errors compound; a single call's error is
 // dominated by its bf16 output, and the pair costs up to ~20% at 64 rows).
-hipError_t gmu_decode_bf16(const bf16_t *M, const bf16_t *X, int ldx, const bf16_t *W1, const bf16_t *W2, void *Y,
-                           Epilogue out_epi, int T, int d_model, int d_inner, bool h_lo, Carver &ws,
-                           hipStream_t stream) {
+hipError_t gmu_decode_bf16(const bf16_t *M, const bf16_t *X, const bf16_t *X_lo, int ldx, const bf16_t *W1,
+                           const bf16_t *W2, void *Y, Epilogue out_epi, int T, int d_model, int d_inner, bool h_lo,
+                           Carver &ws, hipStream_t stream) {
     bf16_t *H = static_cast<bf16_t *>(ws.take((size_t)T * d_inner * sizeof(bf16_t)));
     bf16_t *H_lo = static_cast<bf16_t *>(ws.take((size_t)T * d_inner * sizeof(bf16_t)));
     if (!h_lo) H_lo = nullptr;
@@ -110,7 +110,7 @@ hipError_t gmu_decode_bf16(const bf16_t *M, const bf16_t *X, int ldx, const bf16
     if (skinny_partial_bytes(T, d_model, p2) > part) part = skinny_partial_bytes(T, d_model, p2);
     float *partials = static_cast<float *>(ws.take(part));
     SkinnyArgs a1;
-    a1.X = X; a1.ldx = ldx; a1.W = W1; a1.T = T; a1.N = d_inner; a1.K = d_model; a1.epi = EPI_GATE;
+    a1.X = X; a1.X_lo = X_lo; a1.ldx = ldx; a1.W = W1; a1.T = T; a1.N = d_inner; a1.K = d_model; a1.epi = EPI_GATE;
     a1.out = H; a1.ldo = d_inner; a1.out_lo = H_lo; a1.aux = M; a1.ldaux = d_inner;
     hipError_t e = launch_skinny(a1, p1, partials, stream);
     if (e != hipSuccess) return e;
@@ -207,7 +207,7 @@ extern "C" sb_status gmu_forward(const void *M, const void *X, const void *W1, c
         e = launch_gmu_f32((const float *)M, (const float *)X, (const float *)W1, (const float *)W2, (float *)Y, H,
                            rows, d_model, d_inner, stream);
     } else if (rows <= kSkinnyMaxTokens) {
-        e = gmu_decode_bf16((const bf16_t *)M, (const bf16_t *)X, (int)d_model, (const bf16_t *)W1,
+        e = gmu_decode_bf16((const bf16_t *)M, (const bf16_t *)X, nullptr, (int)d_model, (const bf16_t *)W1,
                             (const bf16_t *)W2, Y, EPI_BF16, (int)rows, (int)d_model, (int)d_inner, false, ws, stream);
     } else {
         bf16_t *H = static_cast<bf16_t *>(ws.take((size_t)rows * d_inner * sizeof(bf16_t)));
@@ -226,9 +226,11 @@ extern "C" size_t xattn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int6
     return xattn_ws(B, Hq, Hkv, L);
 }
 
-extern "C" sb_status xattn_decode(const void *q, const void *kcache, const void *vcache, void *out, int64_t B,
-                                  int64_t Hq, int64_t Hkv, int64_t D, int64_t L, float scale, void *workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+sb_status xattn_decode_impl(const char *fn, const void *q, const void *kcache, const void *vcache, const int32_t *lens,
+                            void *out, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L, float scale,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (B < 0 || Hq < 0 || Hkv < 0 || D < 0 || L < 0) return fail(SB_EINVAL, "negative size");
     if (B == 0) return ok();
     sb_status st = check_xattn_shape(B, Hq, Hkv, D, L);
@@ -240,7 +242,8 @@ extern "C" sb_status xattn_decode(const void *q, const void *kcache, const void 
         return fail(SB_EINVAL, "scale must be finite");
     const size_t qbytes = (size_t)B * Hq * D * 2, kvbytes = (size_t)B * Hkv * L * D * 2;
     const Range ro = rng("out", out, qbytes);
-    const Range ins[] = {rng("q", q, qbytes), rng("kcache", kcache, kvbytes), rng("vcache", vcache, kvbytes)};
+    const Range ins[] = {rng("q", q, qbytes), rng("kcache", kcache, kvbytes), rng("vcache", vcache, kvbytes),
+                         rng("lens", lens, lens ? (size_t)B * sizeof(int32_t) : 0)};
     for (const Range &r : ins)
         if (overlaps(ro, r)) return fail(SB_EINVAL, "out overlaps %s", r.name);
     const size_t need = xattn_ws(B, Hq, Hkv, L);
@@ -254,13 +257,31 @@ extern "C" sb_status xattn_decode(const void *q, const void *kcache, const void 
 
     const XattnPlan plan = xattn_plan(B, Hkv, L);
     if (log_enabled())
-        fprintf(stderr, "[sambay] xattn_decode B=%lld Hq=%lld Hkv=%lld L=%lld -> %d chunks of %d positions, grid %dx%lldx%lld\n",
-                (long long)B, (long long)Hq, (long long)Hkv, (long long)L, plan.splits, plan.chunk, plan.splits,
-                (long long)Hkv, (long long)B);
-    hipError_t e = launch_xattn(q, false, (const bf16_t *)kcache, (const bf16_t *)vcache, (bf16_t *)out, nullptr,
+        fprintf(stderr, "[sambay] %s B=%lld Hq=%lld Hkv=%lld L=%lld%s -> %d chunks of %d positions, grid %dx%lldx%lld\n",
+                fn, (long long)B, (long long)Hq, (long long)Hkv, (long long)L, lens ? " (ragged)" : "", plan.splits,
+                plan.chunk, plan.splits, (long long)Hkv, (long long)B);
+    hipError_t e = launch_xattn(q, false, (const bf16_t *)kcache, (const bf16_t *)vcache, lens, (bf16_t *)out, nullptr,
                                 (int)B, (int)Hq, (int)Hkv, (int)L, scale, plan, workspace, stream);
-    if (e != hipSuccess) return hip_fail("xattn_decode launch", e);
+    if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
+}
+
+}  // namespace
+
+extern "C" sb_status xattn_decode(const void *q, const void *kcache, const void *vcache, void *out, int64_t B,
+                                  int64_t Hq, int64_t Hkv, int64_t D, int64_t L, float scale, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    return xattn_decode_impl("xattn_decode", q, kcache, vcache, nullptr, out, B, Hq, Hkv, D, L, scale, workspace,
+                             workspace_bytes, stream);
+}
+
+extern "C" sb_status xattn_decode_varlen(const void *q, const void *kcache, const void *vcache, const int32_t *lens,
+                                         void *out, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L,
+                                         float scale, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B > 0 && !lens) return fail(SB_EINVAL, "null lens");
+    if (((uintptr_t)lens & 3u) != 0) return fail(SB_EINVAL, "lens must be 4-byte aligned");
+    return xattn_decode_impl("xattn_decode_varlen", q, kcache, vcache, lens, out, B, Hq, Hkv, D, L, scale, workspace,
+                             workspace_bytes, stream);
 }
 
 namespace {
@@ -378,7 +399,7 @@ extern "C" sb_status crossdecoder_step(void *h, const void *M, const void *kcach
                 e = launch_skinny(aq, skinny_plan(T, dm, dm), proj_partials, stream);
             }
             if (e == hipSuccess)
-                e = launch_xattn(q, true, (const bf16_t *)kcache, (const bf16_t *)vcache, o, o_lo, (int)B, (int)Hq,
+                e = launch_xattn(q, true, (const bf16_t *)kcache, (const bf16_t *)vcache, nullptr, o, o_lo, (int)B, (int)Hq,
                                  (int)Hkv, (int)L, scale, plan, partials, stream);
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
@@ -391,11 +412,210 @@ extern "C" sb_status crossdecoder_step(void *h, const void *M, const void *kcach
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
                 Carver ws{gmu_ws_base};
-                e = gmu_decode_bf16((const bf16_t *)M + t0 * di, hb + t0 * dm, dm, (const bf16_t *)ly.w_a,
+                e = gmu_decode_bf16((const bf16_t *)M + t0 * di, hb + t0 * dm, nullptr, dm, (const bf16_t *)ly.w_a,
                                     (const bf16_t *)ly.w_b, hb + t0 * dm, EPI_RESID, T, dm, di, true, ws, stream);
             }
         }
         if (e != hipSuccess) return hip_fail("crossdecoder_step launch", e);
+    }
+    return ok();
+}
+
+// ===================================================== complete cross-decoder
+
+namespace {
+
+// Workspace of one complete-layer step (all reused layer to layer).
+struct ExLayout {
+    size_t q, o, xn, gmu, mlp_g, mlp_u, part, attn, total;
+};
+
+ExLayout ex_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t L) {
+    ExLayout s;
+    const int64_t T = B < kSkinnyMaxTokens ? B : kSkinnyMaxTokens;
+    const int t = (int)T, dm = (int)d_model, di = (int)d_inner, df = (int)d_ff;
+    s.q = round_up((size_t)B * d_model * sizeof(float));
+    s.o = 2 * round_up((size_t)B * d_model * sizeof(bf16_t));
+    s.xn = 2 * round_up((size_t)B * d_model * sizeof(bf16_t));
+    s.gmu = 2 * round_up((size_t)T * d_inner * sizeof(bf16_t));
+    s.mlp_g = d_ff > 0 ? round_up((size_t)T * d_ff * sizeof(float)) : 0;
+    s.mlp_u = d_ff > 0 ? 2 * round_up((size_t)T * d_ff * sizeof(bf16_t)) : 0;
+    size_t part = 0;
+    const int shapes[][2] = {{di, dm}, {dm, di}, {dm, dm}, {df, dm}, {dm, df}};
+    for (const auto &nk : shapes) {
+        if (nk[0] <= 0 || nk[1] <= 0) continue;
+        const size_t c = skinny_partial_bytes(t, nk[0], skinny_plan(t, nk[0], nk[1]));
+        if (c > part) part = c;
+    }
+    s.part = round_up(part);
+    s.attn = round_up(xattn_partial_bytes(B, Hq, xattn_plan(B, Hkv, L).splits));
+    s.total = s.q + s.o + s.xn + s.gmu + s.mlp_g + s.mlp_u + s.part + s.attn;
+    return s;
+}
+
+}  // namespace
+
+extern "C" size_t crossdecoder_ex_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_ff,
+                                                  int64_t Hq, int64_t Hkv, int64_t D, int64_t L) {
+    if (B <= 0 || d_model <= 0 || d_inner <= 0 || d_ff < 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || D != kHeadDim ||
+        Hq % Hkv != 0)
+        return 0;
+    return ex_layout(B, d_model, d_inner, d_ff, Hq, Hkv, L).total;
+}
+
+extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kcache, const void *vcache,
+                                          const int32_t *lens, const sb_layer_ex *layers, int32_t n_layers, int64_t B,
+                                          int64_t d_model, int64_t d_inner, int64_t d_ff, int64_t Hq, int64_t Hkv,
+                                          int64_t D, int64_t L, float scale, float eps, void *workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || d_model < 0 || d_inner < 0 || d_ff < 0 || Hq < 0 || Hkv < 0 || D < 0 || L < 0 || n_layers < 0)
+        return fail(SB_EINVAL, "negative size");
+    if (B == 0 || n_layers == 0) return ok();
+    sb_status st = check_xattn_shape(B, Hq, Hkv, D, L);
+    if (st != SB_OK) return st;
+    if (d_model == 0 || d_inner == 0) return fail(SB_EINVAL, "d_model and d_inner must be positive");
+    if (Hq * D != d_model)
+        return fail(SB_EINVAL, "Hq*D (%lld) != d_model (%lld)", (long long)(Hq * D), (long long)d_model);
+    if (d_model % 64 != 0 || d_inner % 64 != 0 || d_ff % 64 != 0)
+        return fail(SB_EUNSUPPORTED, "d_model, d_inner and d_ff must be multiples of 64");
+    if (d_model > kMaxDim || d_inner > kMaxDim || d_ff > kMaxDim) return fail(SB_EUNSUPPORTED, "dimension >= 2^30");
+    if (!h || !M || !kcache || !vcache) return fail(SB_EINVAL, "null tensor pointer");
+    if (!layers) return fail(SB_EINVAL, "null layer array");
+    if (!aligned16(h) || !aligned16(M) || !aligned16(kcache) || !aligned16(vcache))
+        return fail(SB_EINVAL, "tensor base pointers must be 16-byte aligned");
+    if (((uintptr_t)lens & 3u) != 0) return fail(SB_EINVAL, "lens must be 4-byte aligned");
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(SB_EINVAL, "scale must be finite");
+    if (!(eps >= 0.f) || eps == __builtin_inff()) return fail(SB_EINVAL, "eps must be finite and >= 0");
+    const size_t kvbytes = (size_t)B * Hkv * L * D * 2;
+    const Range rh = rng("h", h, (size_t)B * d_model * 2);
+    const Range fixed[] = {rng("M", M, (size_t)B * d_inner * 2), rng("kcache", kcache, kvbytes),
+                           rng("vcache", vcache, kvbytes), rng("lens", lens, lens ? (size_t)B * 4 : 0)};
+    for (const Range &r : fixed)
+        if (overlaps(rh, r)) return fail(SB_EINVAL, "h overlaps %s", r.name);
+    for (int32_t i = 0; i < n_layers; ++i) {
+        const sb_layer_ex &ly = layers[i];
+        if (ly.kind != SB_LAYER_XATTN && ly.kind != SB_LAYER_GMU)
+            return fail(SB_EINVAL, "layer %d: unknown kind %d", (int)i, (int)ly.kind);
+        if (!ly.w_a || !ly.w_b) return fail(SB_EINVAL, "layer %d: null weight", (int)i);
+        const bool mlp = ly.w_gate != nullptr;
+        if (mlp && (!ly.w_up || !ly.w_down)) return fail(SB_EINVAL, "layer %d: incomplete MLP", (int)i);
+        if (mlp && d_ff == 0) return fail(SB_EINVAL, "layer %d has an MLP but d_ff == 0", (int)i);
+        const void *ptrs[] = {ly.w_a, ly.w_b, ly.norm1, ly.norm2, ly.w_gate, ly.w_up, ly.w_down};
+        for (const void *p : ptrs)
+            if (!aligned16(p)) return fail(SB_EINVAL, "layer %d: misaligned weight or gain", (int)i);
+        const size_t ba = (size_t)(ly.kind == SB_LAYER_GMU ? d_inner : d_model) * d_model * 2;
+        const size_t bb = (size_t)d_model * (ly.kind == SB_LAYER_GMU ? d_inner : d_model) * 2;
+        const Range wr[] = {rng("w_a", ly.w_a, ba), rng("w_b", ly.w_b, bb),
+                            rng("norm1", ly.norm1, ly.norm1 ? (size_t)d_model * 2 : 0),
+                            rng("norm2", ly.norm2, ly.norm2 ? (size_t)d_model * 2 : 0),
+                            rng("w_gate", ly.w_gate, mlp ? (size_t)d_ff * d_model * 2 : 0),
+                            rng("w_up", ly.w_up, mlp ? (size_t)d_ff * d_model * 2 : 0),
+                            rng("w_down", ly.w_down, mlp ? (size_t)d_model * d_ff * 2 : 0)};
+        for (const Range &r : wr)
+            if (overlaps(rh, r)) return fail(SB_EINVAL, "layer %d: %s overlaps h", (int)i, r.name);
+    }
+    const ExLayout lay = ex_layout(B, d_model, d_inner, d_ff, Hq, Hkv, L);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(SB_EWORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
+                    workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(SB_EINVAL, "workspace must be 16-byte aligned");
+    const Range rw = rng("workspace", workspace, lay.total);
+    if (overlaps(rw, rh)) return fail(SB_EINVAL, "workspace overlaps h");
+    for (const Range &r : fixed)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+
+    char *p = static_cast<char *>(workspace);
+    float *q = reinterpret_cast<float *>(p);
+    p += lay.q;
+    bf16_t *o = reinterpret_cast<bf16_t *>(p), *o_lo = reinterpret_cast<bf16_t *>(p + lay.o / 2);
+    p += lay.o;
+    bf16_t *xn = reinterpret_cast<bf16_t *>(p), *xn_lo = reinterpret_cast<bf16_t *>(p + lay.xn / 2);
+    p += lay.xn;
+    bf16_t *H = reinterpret_cast<bf16_t *>(p), *H_lo = reinterpret_cast<bf16_t *>(p + lay.gmu / 2);
+    p += lay.gmu;
+    float *G = reinterpret_cast<float *>(p);
+    p += lay.mlp_g;
+    bf16_t *U = reinterpret_cast<bf16_t *>(p), *U_lo = reinterpret_cast<bf16_t *>(p + lay.mlp_u / 2);
+    p += lay.mlp_u;
+    float *part = reinterpret_cast<float *>(p);
+    p += lay.part;
+    void *attn_part = p;
+    const XattnPlan plan = xattn_plan(B, Hkv, L);
+    if (log_enabled())
+        fprintf(stderr, "[sambay] crossdecoder_step_ex B=%lld layers=%d d_model=%lld d_inner=%lld d_ff=%lld L=%lld%s "
+                        "-> attention %d chunks of %d positions; workspace %zu bytes\n",
+                (long long)B, (int)n_layers, (long long)d_model, (long long)d_inner, (long long)d_ff, (long long)L,
+                lens ? " (ragged)" : "", plan.splits, plan.chunk, lay.total);
+    bf16_t *hb = static_cast<bf16_t *>(h);
+    const int dm = (int)d_model, di = (int)d_inner, df = (int)d_ff;
+
+    // One weight-streaming product of a token group of T <= 64 rows (pointers
+    // already at the group's first row).
+    auto product = [&](const bf16_t *X, const bf16_t *X_lo, int ldx, const void *W, int N, int K, Epilogue epi,
+                       void *out, int ldo, bf16_t *out_lo, const float *aux_f32, int T) -> hipError_t {
+        SkinnyArgs a;
+        a.X = X; a.X_lo = X_lo; a.ldx = ldx; a.W = (const bf16_t *)W; a.T = T; a.N = N; a.K = K; a.epi = epi;
+        a.out = out; a.ldo = ldo; a.out_lo = out_lo; a.aux_f32 = aux_f32; a.ldaux = N;
+        return launch_skinny(a, skinny_plan(T, N, K), part, stream);
+    };
+    auto rows = [](const bf16_t *p, int64_t t0, int ld) { return p ? p + t0 * ld : nullptr; };
+
+    for (int32_t li = 0; li < n_layers; ++li) {
+        const sb_layer_ex &ly = layers[li];
+        hipError_t e = hipSuccess;
+        // Mixer input: RMSNorm(h) as a bf16 hi + lo pair, or h itself.
+        const bf16_t *X = hb, *X_lo = nullptr;
+        if (ly.norm1) {
+            e = launch_rmsnorm(hb, (const bf16_t *)ly.norm1, (int)B, dm, eps, xn, xn_lo, stream);
+            X = xn;
+            X_lo = xn_lo;
+        }
+        if (e == hipSuccess && ly.kind == SB_LAYER_XATTN) {
+            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+                e = product(rows(X, t0, dm), rows(X_lo, t0, dm), dm, ly.w_a, dm, dm, EPI_F32, q + t0 * dm, dm, nullptr,
+                            nullptr, T);
+            }
+            if (e == hipSuccess)
+                e = launch_xattn(q, true, (const bf16_t *)kcache, (const bf16_t *)vcache, lens, o, o_lo, (int)B,
+                                 (int)Hq, (int)Hkv, (int)L, scale, plan, attn_part, stream);
+            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+                e = product(o + t0 * dm, o_lo + t0 * dm, dm, ly.w_b, dm, dm, EPI_RESID, hb + t0 * dm, dm, nullptr,
+                            nullptr, T);
+            }
+        } else if (e == hipSuccess) {
+            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+                SkinnyArgs a1;
+                a1.X = rows(X, t0, dm); a1.X_lo = rows(X_lo, t0, dm); a1.ldx = dm;
+                a1.W = (const bf16_t *)ly.w_a; a1.T = T; a1.N = di; a1.K = dm; a1.epi = EPI_GATE;
+                a1.out = H; a1.ldo = di; a1.out_lo = H_lo; a1.aux = (const bf16_t *)M + t0 * di; a1.ldaux = di;
+                e = launch_skinny(a1, skinny_plan(T, di, dm), part, stream);
+                if (e == hipSuccess)
+                    e = product(H, H_lo, di, ly.w_b, dm, di, EPI_RESID, hb + t0 * dm, dm, nullptr, nullptr, T);
+            }
+        }
+        if (e == hipSuccess && ly.w_gate) {
+            const bf16_t *X2 = hb, *X2_lo = nullptr;
+            if (ly.norm2) {
+                e = launch_rmsnorm(hb, (const bf16_t *)ly.norm2, (int)B, dm, eps, xn, xn_lo, stream);
+                X2 = xn;
+                X2_lo = xn_lo;
+            }
+            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+                e = product(rows(X2, t0, dm), rows(X2_lo, t0, dm), dm, ly.w_gate, df, dm, EPI_F32, G, df, nullptr,
+                            nullptr, T);
+                if (e == hipSuccess)
+                    e = product(rows(X2, t0, dm), rows(X2_lo, t0, dm), dm, ly.w_up, df, dm, EPI_SWIGLU, U, df, U_lo,
+                                G, T);
+                if (e == hipSuccess)
+                    e = product(U, U_lo, df, ly.w_down, dm, df, EPI_RESID, hb + t0 * dm, dm, nullptr, nullptr, T);
+            }
+        }
+        if (e != hipSuccess) return hip_fail("crossdecoder_step_ex launch", e);
     }
     return ok();
 }

@@ -43,9 +43,9 @@ XattnPlan xattn_plan(int64_t B, int64_t Hkv, int64_t L);
 size_t xattn_partial_bytes(int64_t B, int64_t Hq, int splits);
 // q is fp32 ([B, Hq, D]) when q_f32, else bf16.  out: bf16 [B, Hq, D]; out_lo
 // (nullable) receives bf16(o - out), the low part of a bf16 hi + lo pair.
-hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, bf16_t *out, bf16_t *out_lo,
-                        int B, int Hq, int Hkv, int L, float scale, const XattnPlan &plan, void *partials,
-                        hipStream_t stream);
+hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, const int32_t *lens,
+                        bf16_t *out, bf16_t *out_lo, int B, int Hq, int Hkv, int L, float scale, const XattnPlan &plan,
+                        void *partials, hipStream_t stream);
 
 // ------------------------------------------------ skinny (decode) products
 // out[t, n] = epi( Σ_k X[t, k] · W[n, k] ) for t < T <= 64 tokens.
@@ -53,7 +53,8 @@ enum Epilogue {
     EPI_F32 = 0,    // out fp32
     EPI_BF16 = 1,   // out bf16
     EPI_GATE = 2,   // out bf16 = aux[t, n] · SiLU(acc)   (aux = M, bf16)
-    EPI_RESID = 3   // out bf16 = out[t, n] + acc         (in-place residual add)
+    EPI_RESID = 3,  // out bf16 = out[t, n] + acc         (in-place residual add)
+    EPI_SWIGLU = 4  // out bf16 = SiLU(aux_f32[t, n]) · acc (aux_f32 = the gate product, fp32)
 };
 constexpr int kSkinnyMaxTokens = 64;
 
@@ -74,8 +75,9 @@ struct SkinnyArgs {
     Epilogue epi = EPI_F32;
     void *out = nullptr;           // [T, ldo]
     int ldo = 0;
-    bf16_t *out_lo = nullptr;      // EPI_GATE only, optional: bf16(value - out)
+    bf16_t *out_lo = nullptr;      // EPI_GATE / EPI_SWIGLU, optional: bf16(value - out)
     const bf16_t *aux = nullptr;   // EPI_GATE: M [T, ldaux]
+    const float *aux_f32 = nullptr; // EPI_SWIGLU: the gate product [T, ldaux]
     int ldaux = 0;
 };
 hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *partials, hipStream_t stream);
@@ -84,6 +86,11 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *par
 // out[r, n] = epi( Σ_k X[r, k] · W[n, k] ), any row count, N % 64 == 0, K % 64 == 0.
 hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
                        const bf16_t *aux, hipStream_t stream);
+
+// ------------------------------------------------------------- RMSNorm
+// out_hi + out_lo = h[r, :] / sqrt(mean(h[r, :]^2) + eps) * g, d % 8 == 0.
+hipError_t launch_rmsnorm(const bf16_t *h, const bf16_t *g, int rows, int d, float eps, bf16_t *out_hi,
+                          bf16_t *out_lo, hipStream_t stream);
 
 // ------------------------------------------------------------- fp32 GMU
 hipError_t launch_gmu_f32(const float *M, const float *X, const float *W1, const float *W2, float *Y, float *H,

@@ -19,8 +19,9 @@
 //    = 16 tokens of X with the same K assignment (X is small and L2-resident).
 //    Tokens are padded to 16 per tile; rows past the range are zero operands.
 //  * Epilogues are fused: fp32 store, bf16 store, the GMU gate
-//    H = M ⊙ SiLU(acc) stored as a bf16 hi + lo pair, or the residual add
-//    h = bf16(h + acc).  An X given as a hi + lo pair (the gated H, the
+//    H = M ⊙ SiLU(acc) stored as a bf16 hi + lo pair, the SwiGLU product
+//    SiLU(gate) ⊙ acc of the complete layer's MLP (same pair), or the
+//    residual add h = bf16(h + acc).  An X given as a hi + lo pair (the gated H, the
 //    attention output o) is multiplied as two MFMAs per operand, so rounding
 //    the intermediate to bf16 costs ~16 significant bits instead of 8.
 //  * For shapes whose row ranges would be too thin, K is also split across
@@ -42,7 +43,7 @@ constexpr int kTargetWGs = 256;
 
 template <int EPI>
 __device__ __forceinline__ void apply_epilogue(float v, int t, int n, void *out, int ldo, bf16_t *out_lo,
-                                               const bf16_t *aux, int ldaux) {
+                                               const bf16_t *aux, const float *aux_f32, int ldaux) {
     const size_t o = (size_t)t * ldo + n;
     if (EPI == EPI_F32) {
         reinterpret_cast<float *>(out)[o] = v;
@@ -54,6 +55,12 @@ __device__ __forceinline__ void apply_epilogue(float v, int t, int n, void *out,
         const bf16_t hi = f32_to_bf16(g);
         reinterpret_cast<bf16_t *>(out)[o] = hi;
         if (out_lo) out_lo[o] = f32_to_bf16(g - bf16_to_f32(hi));
+    } else if (EPI == EPI_SWIGLU) {
+        const float a = aux_f32[(size_t)t * ldaux + n];
+        const float u = (a / (1.f + expf(-a))) * v;
+        const bf16_t hi = f32_to_bf16(u);
+        reinterpret_cast<bf16_t *>(out)[o] = hi;
+        if (out_lo) out_lo[o] = f32_to_bf16(u - bf16_to_f32(hi));
     } else {
         bf16_t *h = reinterpret_cast<bf16_t *>(out);
         h[o] = f32_to_bf16(bf16_to_f32(h[o]) + v);
@@ -67,7 +74,8 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
                                                           const bf16_t *__restrict__ X_lo, int ldx,
                                                           const bf16_t *__restrict__ W, int T, int N, int K, int R,
                                                           int k_slice, void *out, int ldo, bf16_t *out_lo,
-                                                          const bf16_t *__restrict__ aux, int ldaux,
+                                                          const bf16_t *__restrict__ aux,
+                                                          const float *__restrict__ aux_f32, int ldaux,
                                                           float *__restrict__ partials) {
     constexpr int TT = 16 * TB;
     __shared__ float red[kWaves][16 * RT][TT + 4];
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) v += red[w][rl][t];
         if (gridDim.y == 1)
-            apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, ldaux);
+            apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, aux_f32, ldaux);
         else
             partials[((size_t)blockIdx.y * T + t) * N + n] = v;
     }
@@ -168,13 +176,14 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
 template <int EPI>
 __global__ __launch_bounds__(256) void skinny_finish_kernel(const float *__restrict__ partials, int splits, int T,
                                                             int N, void *out, int ldo, bf16_t *out_lo,
-                                                            const bf16_t *__restrict__ aux, int ldaux) {
+                                                            const bf16_t *__restrict__ aux,
+                                                            const float *__restrict__ aux_f32, int ldaux) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)T * N) return;
     const int t = (int)(idx / N), n = (int)(idx % N);
     float v = 0.f;
     for (int s = 0; s < splits; ++s) v += partials[((size_t)s * T + t) * N + n];
-    apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, ldaux);
+    apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, aux_f32, ldaux);
 }
 
 template <int RT, int TB, int EPI, bool XLO>
@@ -184,12 +193,13 @@ hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hi
     const dim3 grid((a.N + p.rows_per_wg - 1) / p.rows_per_wg, p.k_splits);
     TimingScope ts(kTimeSkinny, stream);
     hipLaunchKernelGGL((skinny_kernel<RT, TB, U, EPI, XLO>), grid, dim3(kThreads), 0, stream, a.X, a.X_lo, a.ldx, a.W,
-                       a.T, a.N, a.K, p.rows_per_wg, p.k_slice, a.out, a.ldo, a.out_lo, a.aux, a.ldaux, partials);
+                       a.T, a.N, a.K, p.rows_per_wg, p.k_slice, a.out, a.ldo, a.out_lo, a.aux, a.aux_f32, a.ldaux,
+                       partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.k_splits == 1) return e;
     const size_t total = (size_t)a.T * a.N;
     hipLaunchKernelGGL((skinny_finish_kernel<EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       partials, p.k_splits, a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.ldaux);
+                       partials, p.k_splits, a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.aux_f32, a.ldaux);
     return hipGetLastError();
 }
 
@@ -205,6 +215,7 @@ hipError_t launch2(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hi
         case EPI_F32: return launch3<RT, TB, EPI_F32>(a, p, partials, stream);
         case EPI_BF16: return launch3<RT, TB, EPI_BF16>(a, p, partials, stream);
         case EPI_GATE: return launch3<RT, TB, EPI_GATE>(a, p, partials, stream);
+        case EPI_SWIGLU: return launch3<RT, TB, EPI_SWIGLU>(a, p, partials, stream);
         default: return launch3<RT, TB, EPI_RESID>(a, p, partials, stream);
     }
 }

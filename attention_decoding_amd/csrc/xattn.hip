@@ -25,6 +25,11 @@
 //  * Partials (m, l, o) per (b, head, chunk) in fp32; a merge kernel combines
 //    the chunks by log-sum-exp in a fixed order (deterministic, no atomics)
 //    and stores bf16 (plus, on request, the bf16 low part of the fp32 value).
+//  * Ragged batches: with a lengths array, sequence b reads only its first
+//    lens[b] positions of a cache laid out with room for L; chunks past its
+//    end are empty (m = -inf, l = 0) and a sequence with no position gets a
+//    zero output.  The chunking follows L, so short sequences leave some
+//    workgroups idle.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -48,7 +53,8 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
                                                                const bf16_t *__restrict__ V,
                                                                float2 *__restrict__ part_ml,
                                                                float *__restrict__ part_o, int Hq, int Hkv, int L,
-                                                               int chunk, int S, float qscale) {
+                                                               const int32_t *__restrict__ lens, int chunk, int S,
+                                                               float qscale) {
     __shared__ __attribute__((aligned(16))) bf16_t vs[kWaves][kKeyBlock][kVStride];
     __shared__ float red_m[kWaves][kMaxGroup];
     __shared__ float red_l[kWaves][kMaxGroup];
@@ -56,8 +62,11 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int G = Hq / Hkv;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+    // Ragged batch: sequence b uses its first lens[b] positions (clamped to
+    // [0, L]); chunks past that end are empty and write an empty partial.
+    const int Lb = lens ? min(max(lens[b], 0), L) : L;
     const int j0 = s * chunk;
-    const int j1 = min(L, j0 + chunk);
+    const int j1 = max(j0, min(Lb, j0 + chunk));
     const size_t kv0 = ((size_t)b * Hkv + g) * (size_t)L * kHeadDim;
     const bf16_t *Kb = K + kv0;
     const bf16_t *Vb = V + kv0;
@@ -211,11 +220,13 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][hh]);
         float lsum = 0.f, o = 0.f;
+        if (M != -INFINITY) {  // else an empty chunk: (m, l, o) = (-inf, 0, 0)
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float e = exp2_fast(red_m[w][hh] - M);  // waves without positions carry m = -inf: weight 0
-            lsum += e * red_l[w][hh];
-            o += e * ow[(w * kMaxGroup + hh) * kHeadDim + d];
+            for (int w = 0; w < kWaves; ++w) {
+                const float e = exp2_fast(red_m[w][hh] - M);  // waves without positions carry m = -inf: weight 0
+                lsum += e * red_l[w][hh];
+                o += e * ow[(w * kMaxGroup + hh) * kHeadDim + d];
+            }
         }
         const size_t pi = ((size_t)b * Hq + (size_t)g * G + hh) * S + s;
         part_o[pi * kHeadDim + d] = o;
@@ -236,12 +247,14 @@ __global__ __launch_bounds__(kHeadDim) void xattn_merge_kernel(const float2 *__r
     float M = -INFINITY;
     for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s].x);
     float lsum = 0.f, o = 0.f;
-    for (int s = 0; s < S; ++s) {
-        const float e = exp2_fast(ml[s].x - M);
-        lsum += e * ml[s].y;
-        o += e * po[(size_t)s * kHeadDim + d];
+    if (M != -INFINITY) {  // else a sequence without visible positions: zero output
+        for (int s = 0; s < S; ++s) {
+            const float e = exp2_fast(ml[s].x - M);  // empty chunks carry m = -inf: weight 0
+            lsum += e * ml[s].y;
+            o += e * po[(size_t)s * kHeadDim + d];
+        }
     }
-    const float v = o / lsum;
+    const float v = lsum > 0.f ? o / lsum : 0.f;
     const bf16_t hi = f32_to_bf16(v);
     out[bh * kHeadDim + d] = hi;
     if (out_lo) out_lo[bh * kHeadDim + d] = f32_to_bf16(v - bf16_to_f32(hi));
@@ -284,9 +297,9 @@ size_t xattn_partial_bytes(int64_t B, int64_t Hq, int splits) {
     return n * sizeof(float2) + n * kHeadDim * sizeof(float);
 }
 
-hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, bf16_t *out, bf16_t *out_lo,
-                        int B, int Hq, int Hkv, int L, float scale, const XattnPlan &plan, void *partials,
-                        hipStream_t stream) {
+hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, const int32_t *lens,
+                        bf16_t *out, bf16_t *out_lo, int B, int Hq, int Hkv, int L, float scale, const XattnPlan &plan,
+                        void *partials, hipStream_t stream) {
     const size_t n = (size_t)B * Hq * plan.splits;
     float2 *ml = reinterpret_cast<float2 *>(partials);
     float *po = reinterpret_cast<float *>(reinterpret_cast<char *>(partials) + n * sizeof(float2));
@@ -296,10 +309,10 @@ hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t
     TimingScope ts(kTimeXattnSplit, stream);
     if (q_f32)
         hipLaunchKernelGGL(xattn_split_kernel<true>, grid, dim3(kThreads), 0, stream, q, K, V, ml, po, Hq, Hkv, L,
-                           plan.chunk, plan.splits, qscale);
+                           lens, plan.chunk, plan.splits, qscale);
     else
         hipLaunchKernelGGL(xattn_split_kernel<false>, grid, dim3(kThreads), 0, stream, q, K, V, ml, po, Hq, Hkv, L,
-                           plan.chunk, plan.splits, qscale);
+                           lens, plan.chunk, plan.splits, qscale);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

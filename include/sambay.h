@@ -135,6 +135,59 @@ sb_status crossdecoder_step(void *h, const void *M, const void *kcache, const vo
                             int64_t D, int64_t L, float scale, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/* ------------------------------------------------------ ragged batches --
+ * xattn_decode for a serving batch whose sequences are at different lengths.
+ * kcache/vcache [B, Hkv, L, D] have room for L positions per (sequence, KV
+ * head); sequence b attends to its first lens[b] positions only (lens: B
+ * int32 in device memory, 4-byte aligned, read by the kernels; values are
+ * clamped to [0, L], and a sequence with lens[b] == 0 gets a zero output: its
+ * softmax has no terms).  Positions at or past lens[b] are never read, so
+ * they may hold anything.  Same workspace as xattn_decode.  The pages define
+ * only the full-cache case; this is its plain per-sequence reading.
+ * Errors: as xattn_decode, plus SB_EINVAL for a null or misaligned lens with
+ * B > 0. */
+sb_status xattn_decode_varlen(const void *q, const void *kcache, const void *vcache, const int32_t *lens, void *out,
+                              int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L, float scale,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------- complete cross-decoder layer --
+ * The pages define the GMU and the shared-cache cross-attention but not the
+ * rest of a layer; this step takes the plain pre-norm Transformer reading.
+ * For each layer, with RMSNorm(x; g) = x / sqrt(mean(x^2) + eps) * g:
+ *   x = RMSNorm(h; norm1)            (x = h when norm1 is NULL)
+ *   SB_LAYER_XATTN: q = x Wq^T, o = attention over the first lens[b] cached
+ *                   positions (all L when lens is NULL), h = bf16(h + o Wo^T)
+ *   SB_LAYER_GMU:   h = bf16(h + GMU(M, x, W1, W2))
+ *   when w_gate is not NULL (a SwiGLU MLP):
+ *     x = RMSNorm(h; norm2)          (x = h when norm2 is NULL)
+ *     h = bf16(h + (SiLU(x Wg^T) ⊙ (x Wu^T)) Wd^T)
+ * The normalised x, the attention output, the GMU hidden and the SwiGLU
+ * product feed their next product as bf16 hi + lo pairs; everything else
+ * accumulates in fp32.  With every norm1, norm2, w_gate NULL and lens NULL
+ * this is crossdecoder_step.  Gains norm1, norm2 [d_model]; w_gate, w_up
+ * [d_ff, d_model]; w_down [d_model, d_ff]; all bf16, 16-byte aligned.
+ * d_ff may be 0 when no layer has an MLP.  h is updated in place.
+ * Errors: as crossdecoder_step and xattn_decode_varlen, plus SB_EINVAL for
+ * an MLP with a missing weight or d_ff == 0, a negative or non-finite eps,
+ * and SB_EUNSUPPORTED for d_ff not a multiple of 64. */
+typedef struct {
+    int32_t kind;          /* an sb_layer_kind value */
+    const void *w_a;       /* as sb_layer */
+    const void *w_b;
+    const void *norm1;     /* RMSNorm gain before the mixer, or NULL */
+    const void *norm2;     /* RMSNorm gain before the MLP, or NULL */
+    const void *w_gate;    /* SwiGLU MLP weights, or all NULL: no MLP */
+    const void *w_up;
+    const void *w_down;
+} sb_layer_ex;
+
+size_t crossdecoder_ex_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_ff, int64_t Hq,
+                                       int64_t Hkv, int64_t D, int64_t L);
+sb_status crossdecoder_step_ex(void *h, const void *M, const void *kcache, const void *vcache, const int32_t *lens,
+                               const sb_layer_ex *layers, int32_t n_layers, int64_t B, int64_t d_model,
+                               int64_t d_inner, int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t D, int64_t L,
+                               float scale, float eps, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------ benchmark instrumentation --
  * For measuring kernels inside the calls above (benchmarks and profiling
  * only; not meant for production loops).  While a kind's bit is enabled,

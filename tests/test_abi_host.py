@@ -169,3 +169,50 @@ def test_python_binding_refuses_cpu_tensors(sb):
     with pytest.raises(ValueError, match="GPU"):
         sb.xattn_decode(torch.zeros(1, 3, 128, dtype=torch.bfloat16), torch.zeros(1, 1, 5, 128, dtype=torch.bfloat16),
                         torch.zeros(1, 1, 5, 128, dtype=torch.bfloat16))
+
+
+def _xav(sb, lens=_addr(6) * 8, q=_addr(0), out=_addr(3), B=2, **kw):
+    k, v = kw.pop("k", _addr(1) * 16), kw.pop("v", _addr(2) * 64)
+    return sb.lib.xattn_decode_varlen(q, k, v, lens, out, B, 24, 8, 128, kw.pop("L", 300), 0.088, _addr(4) * 512,
+                                      1 << 30, None)
+
+
+def test_xattn_varlen_validation(sb):
+    assert _xav(sb, lens=None) == sb.SB_EINVAL                     # null lens
+    assert _xav(sb, lens=_addr(6) * 8 + 2) == sb.SB_EINVAL         # misaligned lens
+    assert _xav(sb, out=_addr(6) * 8) == sb.SB_EINVAL              # out overlaps lens
+    assert "lens" in sb.lib.sb_last_error().decode()
+    assert _xav(sb, L=0) == sb.SB_EINVAL
+    assert _xav(sb, B=0, lens=None, q=None) == sb.SB_OK
+
+
+def _step_ex(sb, layers, lens=None, B=2, dm=3072, di=6144, dff=8192, eps=1e-5, ws=_addr(5) * 512, wsb=1 << 36,
+             h=_addr(0)):
+    arr = (sb.SbLayerEx * max(len(layers), 1))()
+    for i, ly in enumerate(layers):
+        for key, val in ly.items():
+            setattr(arr[i], key, val)
+    return sb.lib.crossdecoder_step_ex(h, _addr(1), _addr(2) * 16, _addr(3) * 64, lens, arr, len(layers), B, dm, di,
+                                       dff, 24, 8, 128, 300, 0.088, eps, ws, wsb, None)
+
+
+def test_crossdecoder_ex_validation(sb):
+    base = dict(kind=0, w_a=_addr(9) * 1024, w_b=_addr(10) * 1024)
+    mlp = dict(base, norm1=_addr(13) * 1024, norm2=_addr(14) * 1024, w_gate=_addr(15) * 1024,
+               w_up=_addr(16) * 1024, w_down=_addr(17) * 1024)
+    assert _step_ex(sb, [mlp], dff=8040) == sb.SB_EUNSUPPORTED      # d_ff not a multiple of 64
+    assert _step_ex(sb, [mlp], dff=0) == sb.SB_EINVAL                # MLP without d_ff
+    assert _step_ex(sb, [dict(mlp, w_up=None)]) == sb.SB_EINVAL      # incomplete MLP
+    assert _step_ex(sb, [dict(mlp, norm1=_addr(13) * 1024 + 2)]) == sb.SB_EINVAL   # misaligned gain
+    assert _step_ex(sb, [dict(mlp, norm2=_addr(0))]) == sb.SB_EINVAL  # gain overlaps h
+    assert _step_ex(sb, [mlp], eps=-1.0) == sb.SB_EINVAL
+    assert _step_ex(sb, [mlp], eps=float("nan")) == sb.SB_EINVAL
+    assert _step_ex(sb, [mlp], lens=_addr(6) * 8 + 1) == sb.SB_EINVAL   # misaligned lens
+    assert _step_ex(sb, [mlp], lens=_addr(0)) == sb.SB_EINVAL        # lens overlaps h
+    assert _step_ex(sb, [dict(base, kind=3)]) == sb.SB_EINVAL
+    assert _step_ex(sb, [mlp], ws=None) == sb.SB_EWORKSPACE
+    need = sb.lib.crossdecoder_ex_workspace_bytes(2, 3072, 6144, 8192, 24, 8, 128, 300)
+    assert need > sb.lib.crossdecoder_workspace_bytes(2, 3072, 6144, 24, 8, 128, 300)
+    assert _step_ex(sb, [mlp], wsb=need - 1) == sb.SB_EWORKSPACE
+    assert _step_ex(sb, [mlp], B=0) == sb.SB_OK
+    assert sb.lib.crossdecoder_ex_workspace_bytes(2, 3072, 6144, 8192, 24, 8, 128, 0) == 0

@@ -1,0 +1,184 @@
+"""GPU parity of the ragged-batch attention and the complete cross-decoder
+layer against the fp64 oracle (through the C ABI), plus the invariants that
+tie them to the plain entry points.
+
+Tolerance: the bf16 bar, max |gpu - oracle| / max |oracle| <= 2e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL_BF16 = 2e-2
+
+
+@pytest.fixture(scope="module")
+def sb():
+    import attention_decoding_amd as sb
+    return sb
+
+
+def err(y, ref):
+    y, ref = np.asarray(y, np.float64), np.asarray(ref, np.float64)
+    return float(np.max(np.abs(y - ref)) / max(float(np.max(np.abs(ref))), 1e-300))
+
+
+def cpu(t):
+    return t.detach().cpu()
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def report(name, e, tol):
+    print("%-60s err %.3e (tol %.0e)" % (name, e, tol), flush=True)
+    assert e <= tol, "%s: %.3e > %.0e" % (name, e, tol)
+
+
+# ----------------------------------------------------------- ragged attention
+
+@pytest.mark.parametrize("B,L,lens", [
+    (6, 5000, [1, 4096, 4097, 5000, 33, 0]),      # one position, chunk boundaries, full, tail, empty
+    (3, 777, [777, 31, 32]),                       # block boundaries around 32
+    (2, 40000, [40000, 2048]),
+])
+def test_xattn_varlen_small(sb, B, L, lens):
+    x = workload.xattn_inputs(B, 24, 8, 128, L, seed=L, device=DEV)
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = sb.xattn_decode(x.q, x.K, x.V, lens=lt)
+    torch.cuda.synchronize()
+    ref = oracle.xattn_varlen(cpu(x.q), cpu(x.K), cpu(x.V), lens)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.count_nonzero(out[b]).item() == 0
+        else:
+            report("xattn varlen B=%d L=%d len=%d" % (B, L, n), err(f64(out[b]), ref[b]), TOL_BF16)
+
+
+def test_xattn_varlen_full_size_sampled(sb):
+    """32 sequences, room for 34816 positions, lengths uniform in [2048, 34816];
+    the oracle checks 6 sequences (the shortest, the longest, 4 more)."""
+    c = workload.XATTN_VARLEN
+    x = workload.xattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["L"], seed=5, device=DEV)
+    lens = workload.ragged_lens(c["B"], c["L"], seed=5, min_len=c["min_len"], device=DEV)
+    out = sb.xattn_decode(x.q, x.K, x.V, lens=lens)
+    torch.cuda.synchronize()
+    ln = cpu(lens).numpy()
+    pick = sorted(set([int(np.argmin(ln)), int(np.argmax(ln)), 0, 7, 19, 31]))
+    idx = torch.tensor(pick)
+    ref = oracle.xattn_varlen(cpu(x.q)[idx], cpu(x.K)[idx], cpu(x.V)[idx], ln[pick])
+    report("xattn varlen 32x34816 ragged (%d sequences)" % len(pick), err(f64(out[idx.to(DEV)]), ref), TOL_BF16)
+
+
+def test_xattn_varlen_full_lengths_equal_plain(sb):
+    x = workload.xattn_inputs(4, 24, 8, 128, 9000, seed=6, device=DEV)
+    lens = torch.full((4,), 9000, dtype=torch.int32, device=DEV)
+    a = sb.xattn_decode(x.q, x.K, x.V)
+    b = sb.xattn_decode(x.q, x.K, x.V, lens=lens)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_xattn_varlen_never_reads_past_the_length(sb):
+    x = workload.xattn_inputs(3, 24, 8, 128, 3000, seed=7, device=DEV)
+    lens_l = [100, 2999, 1]
+    lens = torch.tensor(lens_l, dtype=torch.int32, device=DEV)
+    a = sb.xattn_decode(x.q, x.K, x.V, lens=lens)
+    K, V = x.K.clone(), x.V.clone()
+    for b, n in enumerate(lens_l):
+        K[b, :, n:] = float("nan")
+        V[b, :, n:] = float("nan")
+    b2 = sb.xattn_decode(x.q, K, V, lens=lens)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b2)
+
+
+def test_xattn_varlen_clamps_lengths(sb):
+    """Lengths above L act as L, negative ones as 0 (documented clamping)."""
+    x = workload.xattn_inputs(2, 24, 8, 128, 500, seed=8, device=DEV)
+    a = sb.xattn_decode(x.q, x.K, x.V, lens=torch.tensor([1000, -5], dtype=torch.int32, device=DEV))
+    b = sb.xattn_decode(x.q, x.K, x.V, lens=torch.tensor([500, 0], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.count_nonzero(a[1]).item() == 0
+
+
+# ------------------------------------------------- complete cross-decoder
+
+def _ex_inputs(B, n_layers, lens, seed, kinds=None, norms=True, mlp=True, L=300, d_ff=512):
+    return workload.crossdecoder_ex_inputs(B, 384, 768, d_ff, 3, 1, 128, L, n_layers, seed=seed, device=DEV,
+                                           kinds=kinds, lens=lens, norms=norms, mlp=mlp)
+
+
+def _oracle_ex(x, rows=None):
+    rows = list(range(x.h.shape[0])) if rows is None else rows
+    idx = torch.tensor(rows)
+    layers = [{k: (cpu(v) if isinstance(v, torch.Tensor) else v) for k, v in ly.items()} for ly in x.layers]
+    lens = None if x.lens is None else cpu(x.lens).numpy()[rows]
+    return oracle.crossdecoder_ex(cpu(x.h)[idx], cpu(x.M)[idx], cpu(x.K)[idx], cpu(x.V)[idx], layers,
+                                  x.h.shape[1] // x.K.shape[3], lens=lens)
+
+
+@pytest.mark.parametrize("lens", [None, [300, 1, 129, 0]])
+@pytest.mark.parametrize("kinds", [None, ["gmu", "xattn", "gmu", "xattn"]])
+def test_step_ex_small(sb, lens, kinds):
+    x = _ex_inputs(4, 4, lens, seed=31, kinds=kinds)
+    ref = _oracle_ex(x)
+    sb.crossdecoder_step_ex(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+    torch.cuda.synchronize()
+    report("step_ex B=4 lens=%s kinds=%s" % (lens, kinds), err(f64(x.h), ref), TOL_BF16)
+
+
+def test_step_ex_two_token_groups_and_mixed_layers(sb):
+    """B = 70 (two groups of <= 64 rows); one layer without MLP, one without norms."""
+    x = _ex_inputs(70, 4, "ragged", seed=32)
+    x.layers[1].update(w_gate=None, w_up=None, w_down=None)
+    x.layers[2].update(norm1=None, norm2=None)
+    ref = _oracle_ex(x)
+    sb.crossdecoder_step_ex(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+    torch.cuda.synchronize()
+    report("step_ex B=70 mixed layers", err(f64(x.h), ref), TOL_BF16)
+
+
+def test_step_ex_without_extras_is_the_plain_step(sb):
+    """No norms, no MLP, no lengths: bit-identical to crossdecoder_step."""
+    x = _ex_inputs(5, 4, None, seed=33, norms=False, mlp=False)
+    h0 = x.h.clone()
+    sb.crossdecoder_step_ex(x.h, x.M, x.K, x.V, x.layers)
+    a = x.h.clone()
+    x.h.copy_(h0)
+    sb.crossdecoder_step(x.h, x.M, x.K, x.V, [(ly["kind"], ly["w_a"], ly["w_b"]) for ly in x.layers])
+    torch.cuda.synchronize()
+    assert torch.equal(a, x.h)
+
+
+def test_step_ex_full_size_sampled(sb):
+    """B = 32, 16 layers, d_model 3072, d_inner 6144, d_ff 8192, room for 34816
+    positions with lengths uniform in [2048, 34816]; the oracle checks 3
+    sequences (sequences are independent)."""
+    c = workload.CROSSDECODER_EX
+    x = workload.crossdecoder_ex_inputs(c["B"], c["d_model"], c["d_inner"], c["d_ff"], c["Hq"], c["Hkv"], c["D"],
+                                        c["L"], c["n_layers"], seed=34, device=DEV, lens="ragged",
+                                        min_len=c["min_len"])
+    rows = [0, 13, 31]
+    ref = _oracle_ex(x, rows)
+    sb.crossdecoder_step_ex(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+    torch.cuda.synchronize()
+    report("step_ex full size, 3 sampled sequences", err(f64(x.h[rows]), ref), TOL_BF16)
+
+
+def test_step_ex_prepared_replays_identically(sb):
+    x = _ex_inputs(3, 2, [5, 300, 77], seed=35)
+    h0 = x.h.clone()
+    step = sb.CrossDecoderStepEx(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+    step()
+    first = x.h.clone()
+    x.h.copy_(h0)
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(first, x.h)
