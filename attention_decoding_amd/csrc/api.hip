@@ -137,8 +137,7 @@ sb_status check_xattn_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64
 }
 
 size_t xattn_ws(int64_t B, int64_t Hq, int64_t Hkv, int64_t L) {
-    const XattnPlan p = xattn_plan(B, Hkv, L);
-    return round_up(xattn_partial_bytes(B, Hq, p.splits));
+    return round_up(xattn_workspace_need(B, Hq, Hkv, L));
 }
 
 }  // namespace
@@ -255,7 +254,7 @@ sb_status xattn_decode_impl(const char *fn, const void *q, const void *kcache, c
     for (const Range &r : ins)
         if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
 
-    const XattnPlan plan = xattn_plan(B, Hkv, L);
+    const XattnPlan plan = xattn_plan(B, Hkv, L, lens != nullptr);
     if (log_enabled())
         fprintf(stderr, "[sambay] %s B=%lld Hq=%lld Hkv=%lld L=%lld%s -> %d chunks of %d positions, grid %dx%lldx%lld\n",
                 fn, (long long)B, (long long)Hq, (long long)Hkv, (long long)L, lens ? " (ragged)" : "", plan.splits,
@@ -448,7 +447,7 @@ ExLayout ex_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_ff, in
         if (c > part) part = c;
     }
     s.part = round_up(part);
-    s.attn = round_up(xattn_partial_bytes(B, Hq, xattn_plan(B, Hkv, L).splits));
+    s.attn = round_up(xattn_workspace_need(B, Hq, Hkv, L));
     s.total = s.q + s.o + s.xn + s.gmu + s.mlp_g + s.mlp_u + s.part + s.attn;
     return s;
 }
@@ -541,7 +540,7 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
     float *part = reinterpret_cast<float *>(p);
     p += lay.part;
     void *attn_part = p;
-    const XattnPlan plan = xattn_plan(B, Hkv, L);
+    const XattnPlan plan = xattn_plan(B, Hkv, L, lens != nullptr);
     if (log_enabled())
         fprintf(stderr, "[sambay] crossdecoder_step_ex B=%lld layers=%d d_model=%lld d_inner=%lld d_ff=%lld L=%lld%s "
                         "-> attention %d chunks of %d positions; workspace %zu bytes\n",

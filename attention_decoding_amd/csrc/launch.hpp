@@ -38,9 +38,12 @@ struct XattnPlan {
     int chunk;   // keys per chunk, a multiple of kKeyBlock; every chunk is non-empty
 };
 
-XattnPlan xattn_plan(int64_t B, int64_t Hkv, int64_t L);
+// ragged: a lengths array limits each sequence to a prefix of the L positions.
+XattnPlan xattn_plan(int64_t B, int64_t Hkv, int64_t L, bool ragged = false);
 // Bytes of fp32 partials for `splits` chunks: (max, sum) pairs then D-wide sums.
 size_t xattn_partial_bytes(int64_t B, int64_t Hq, int splits);
+// Partial bytes for either plan (what a workspace must hold).
+size_t xattn_workspace_need(int64_t B, int64_t Hq, int64_t Hkv, int64_t L);
 // q is fp32 ([B, Hq, D]) when q_f32, else bf16.  out: bf16 [B, Hq, D]; out_lo
 // (nullable) receives bf16(o - out), the low part of a bf16 hi + lo pair.
 hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, const int32_t *lens,

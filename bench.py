@@ -159,6 +159,41 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> 
                                       "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
                                       "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
     del x
+    # Ragged batch: 32 sequences, room for 34816 positions, lengths uniform in [2048, 34816].
+    c = workload.XATTN_VARLEN
+    x = workload.xattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["L"], seed=6, device=dev)
+    lens = workload.ragged_lens(c["B"], c["L"], seed=6, min_len=c["min_len"], device=dev)
+    out = torch.empty(c["B"], c["Hq"], c["D"], dtype=torch.bfloat16, device=dev)
+    ms = time_calls(lambda i: sb.xattn_decode(x.q, x.K, x.V, out=out, lens=lens), 20)
+    nbytes = int(lens.sum().item()) * c["Hkv"] * c["D"] * 4
+    res["xattn_decode_varlen_B32_L34816_ragged"] = {
+        "us_per_call": round(1e3 * ms, 1), "cached_positions": int(lens.sum().item()),
+        "gbps": round(nbytes / ms / 1e6, 1), "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+        "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
+    del x
+    torch.cuda.empty_cache()
+    # Complete cross-decoder layer step (pre-RMSNorm mixer + pre-RMSNorm SwiGLU MLP, d_ff 8192) on that ragged batch.
+    c = workload.CROSSDECODER_EX
+    x = workload.crossdecoder_ex_inputs(c["B"], c["d_model"], c["d_inner"], c["d_ff"], c["Hq"], c["Hkv"], c["D"],
+                                        c["L"], c["n_layers"], seed=7, device=dev, lens="ragged",
+                                        min_len=c["min_len"])
+    h_in = x.h.clone()
+    step = sb.CrossDecoderStepEx(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+
+    def run(i):
+        x.h.copy_(h_in)
+        step()
+
+    ms = time_calls(run, 10)
+    n_x = c["n_layers"] // 2
+    dm, di, dff = c["d_model"], c["d_inner"], c["d_ff"]
+    kv = int(x.lens.sum().item()) * c["Hkv"] * c["D"] * 4
+    nbytes = (n_x * kv + n_x * 2 * dm * dm * 2 + (c["n_layers"] - n_x) * 2 * dm * di * 2
+              + c["n_layers"] * (3 * dm * dff + 2 * dm) * 2)
+    res["crossdecoder_ex_B32_ragged_dff8192"] = {
+        "ms_per_step": round(ms, 4), "tokens_per_s": round(c["B"] / (ms / 1e3), 1), "hbm_bytes_per_step": nbytes,
+        "gbps": round(nbytes / ms / 1e6, 1), "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del step, x
     torch.cuda.empty_cache()
     return res
 
