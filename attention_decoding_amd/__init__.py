@@ -128,6 +128,19 @@ def probe_stream_read_gbps(buf: torch.Tensor, reps: int = 5) -> float:
     return nbytes / (ms / n / 1e3) / 1e9
 
 
+_probe_sinks: dict = {}
+
+
+def probe_stream_read_raw(buf: torch.Tensor) -> None:
+    """Enqueue one plain streaming read of `buf` (no timing)."""
+    dev = _check_device(buf, "buf")
+    sink = _probe_sinks.get(dev)
+    if sink is None:
+        sink = _probe_sinks[dev] = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    _check("sb_probe_stream_read", lib.sb_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(dev)))
+
+
 def probe_mfma_tflops(device, iters: int = 20000, reps: int = 3) -> float:
     """Rate (TFLOP/s) of the library's register-only bf16 32x32x16 MFMA loop."""
     dev = torch.device(device)
@@ -380,4 +393,5 @@ def crossdecoder_step_ex(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor,
 
 __all__ = ["gmu_forward", "xattn_decode", "crossdecoder_step", "CrossDecoderStep", "crossdecoder_step_ex",
            "CrossDecoderStepEx", "SambayError", "version", "lib",
-           "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect", "probe_stream_read_gbps", "probe_mfma_tflops"]
+           "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect", "probe_stream_read_gbps", "probe_mfma_tflops",
+           "probe_stream_read_raw"]

@@ -558,19 +558,39 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
         a.out = out; a.ldo = ldo; a.out_lo = out_lo; a.aux_f32 = aux_f32; a.ldaux = N;
         return launch_skinny(a, skinny_plan(T, N, K), part, stream);
     };
+    // The residual product of a group; when `next_norm` is set the group's
+    // rows of the next sublayer's input RMSNorm(h; next_norm) are produced
+    // too, inside the K-split finishing pass or by a separate launch.
+    auto residual = [&](const bf16_t *X, const bf16_t *X_lo, int ldx, const void *W, int K, int64_t t0, int T,
+                        const void *next_norm) -> hipError_t {
+        SkinnyArgs a;
+        a.X = X; a.X_lo = X_lo; a.ldx = ldx; a.W = (const bf16_t *)W; a.T = T; a.N = dm; a.K = K;
+        a.epi = EPI_RESID; a.out = hb + t0 * dm; a.ldo = dm;
+        a.next_norm = (const bf16_t *)next_norm; a.next_x = xn + t0 * dm; a.next_x_lo = xn_lo + t0 * dm;
+        a.eps = eps;
+        const SkinnyPlan plan_r = skinny_plan(T, dm, K);
+        hipError_t e = launch_skinny(a, plan_r, part, stream);
+        if (e == hipSuccess && next_norm && !skinny_fuses_norm(a, plan_r))
+            e = launch_rmsnorm(hb + t0 * dm, (const bf16_t *)next_norm, T, dm, eps, xn + t0 * dm, xn_lo + t0 * dm,
+                               stream);
+        return e;
+    };
     auto rows = [](const bf16_t *p, int64_t t0, int ld) { return p ? p + t0 * ld : nullptr; };
 
+    // xn holds RMSNorm(h) for the sublayer about to run whenever its gain is set.
+    hipError_t e0 = layers[0].norm1
+                        ? launch_rmsnorm(hb, (const bf16_t *)layers[0].norm1, (int)B, dm, eps, xn, xn_lo, stream)
+                        : hipSuccess;
+    if (e0 != hipSuccess) return hip_fail("crossdecoder_step_ex launch", e0);
     for (int32_t li = 0; li < n_layers; ++li) {
         const sb_layer_ex &ly = layers[li];
+        const bool mlp = ly.w_gate != nullptr;
+        const void *after_mixer = mlp ? ly.norm2 : (li + 1 < n_layers ? layers[li + 1].norm1 : nullptr);
+        const void *after_mlp = li + 1 < n_layers ? layers[li + 1].norm1 : nullptr;
         hipError_t e = hipSuccess;
         // Mixer input: RMSNorm(h) as a bf16 hi + lo pair, or h itself.
-        const bf16_t *X = hb, *X_lo = nullptr;
-        if (ly.norm1) {
-            e = launch_rmsnorm(hb, (const bf16_t *)ly.norm1, (int)B, dm, eps, xn, xn_lo, stream);
-            X = xn;
-            X_lo = xn_lo;
-        }
-        if (e == hipSuccess && ly.kind == SB_LAYER_XATTN) {
+        const bf16_t *X = ly.norm1 ? xn : hb, *X_lo = ly.norm1 ? xn_lo : nullptr;
+        if (ly.kind == SB_LAYER_XATTN) {
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
                 e = product(rows(X, t0, dm), rows(X_lo, t0, dm), dm, ly.w_a, dm, dm, EPI_F32, q + t0 * dm, dm, nullptr,
@@ -581,10 +601,9 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
                                  (int)Hq, (int)Hkv, (int)L, scale, plan, attn_part, stream);
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
-                e = product(o + t0 * dm, o_lo + t0 * dm, dm, ly.w_b, dm, dm, EPI_RESID, hb + t0 * dm, dm, nullptr,
-                            nullptr, T);
+                e = residual(o + t0 * dm, o_lo + t0 * dm, dm, ly.w_b, dm, t0, T, after_mixer);
             }
-        } else if (e == hipSuccess) {
+        } else {
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
                 SkinnyArgs a1;
@@ -592,17 +611,11 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
                 a1.W = (const bf16_t *)ly.w_a; a1.T = T; a1.N = di; a1.K = dm; a1.epi = EPI_GATE;
                 a1.out = H; a1.ldo = di; a1.out_lo = H_lo; a1.aux = (const bf16_t *)M + t0 * di; a1.ldaux = di;
                 e = launch_skinny(a1, skinny_plan(T, di, dm), part, stream);
-                if (e == hipSuccess)
-                    e = product(H, H_lo, di, ly.w_b, dm, di, EPI_RESID, hb + t0 * dm, dm, nullptr, nullptr, T);
+                if (e == hipSuccess) e = residual(H, H_lo, di, ly.w_b, di, t0, T, after_mixer);
             }
         }
-        if (e == hipSuccess && ly.w_gate) {
-            const bf16_t *X2 = hb, *X2_lo = nullptr;
-            if (ly.norm2) {
-                e = launch_rmsnorm(hb, (const bf16_t *)ly.norm2, (int)B, dm, eps, xn, xn_lo, stream);
-                X2 = xn;
-                X2_lo = xn_lo;
-            }
+        if (e == hipSuccess && mlp) {
+            const bf16_t *X2 = ly.norm2 ? xn : hb, *X2_lo = ly.norm2 ? xn_lo : nullptr;
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
                 e = product(rows(X2, t0, dm), rows(X2_lo, t0, dm), dm, ly.w_gate, df, dm, EPI_F32, G, df, nullptr,
@@ -610,8 +623,7 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
                 if (e == hipSuccess)
                     e = product(rows(X2, t0, dm), rows(X2_lo, t0, dm), dm, ly.w_up, df, dm, EPI_SWIGLU, U, df, U_lo,
                                 G, T);
-                if (e == hipSuccess)
-                    e = product(U, U_lo, df, ly.w_down, dm, df, EPI_RESID, hb + t0 * dm, dm, nullptr, nullptr, T);
+                if (e == hipSuccess) e = residual(U, U_lo, df, ly.w_down, df, t0, T, after_mlp);
             }
         }
         if (e != hipSuccess) return hip_fail("crossdecoder_step_ex launch", e);

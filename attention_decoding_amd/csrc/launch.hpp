@@ -82,8 +82,15 @@ struct SkinnyArgs {
     const bf16_t *aux = nullptr;   // EPI_GATE: M [T, ldaux]
     const float *aux_f32 = nullptr; // EPI_SWIGLU: the gate product [T, ldaux]
     int ldaux = 0;
+    // EPI_RESID only: also produce the next sublayer's input RMSNorm(h_new;
+    // next_norm) as a bf16 hi + lo pair [T, ldo] — fused into the finishing
+    // pass when the plan splits K (skinny_fuses_norm), else left to the caller.
+    const bf16_t *next_norm = nullptr;
+    bf16_t *next_x = nullptr, *next_x_lo = nullptr;
+    float eps = 0.f;
 };
 hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *partials, hipStream_t stream);
+bool skinny_fuses_norm(const SkinnyArgs &a, const SkinnyPlan &plan);
 
 // ------------------------------------------------------- prefill product
 // out[r, n] = epi( Σ_k X[r, k] · W[n, k] ), any row count, N % 64 == 0, K % 64 == 0.

@@ -11,7 +11,11 @@ using namespace sambay;
 
 namespace {
 
-constexpr int kReadWGs = 256, kReadThreads = 256, kReadInFlight = 8;
+constexpr int kReadThreads = 256, kReadInFlight = 8;
+
+// Measured on MI355X: 256 workgroups saturate HBM on GB-sized buffers; reads
+// of tens of MB finish sooner with ~1024 (more requests in flight at once).
+int read_wgs(size_t bytes) { return bytes < ((size_t)256 << 20) ? 1024 : 256; }
 
 // Grid-stride read: each workgroup reads 32 KB contiguous per step (eight 16-byte
 // loads in flight per thread), the grid sweeps memory linearly.
@@ -62,7 +66,7 @@ extern "C" sb_status sb_probe_stream_read(const void *data, size_t bytes, void *
     if (!data || !sink || bytes % 16 != 0 || ((uintptr_t)data & 15u) != 0) return SB_EINVAL;
     if (bytes == 0) return SB_OK;
     TimingScope ts(kTimeProbe, stream);
-    hipLaunchKernelGGL(stream_read_kernel, dim3(kReadWGs), dim3(kReadThreads), 0, stream,
+    hipLaunchKernelGGL(stream_read_kernel, dim3(read_wgs(bytes)), dim3(kReadThreads), 0, stream,
                        static_cast<const u32x4 *>(data), bytes / 16, static_cast<unsigned *>(sink));
     return hipGetLastError() == hipSuccess ? SB_OK : SB_EHIP;
 }

@@ -186,6 +186,70 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(const float *__restr
     apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, aux_f32, ldaux);
 }
 
+// K-split finishing of a residual product fused with the next sublayer's
+// RMSNorm: one workgroup per token row sums the slices in slice order, stores
+// h_new = bf16(h + Σ) and writes RMSNorm(h_new; g) as a bf16 hi + lo pair.
+// The norm's loop structure and reduction order are those of the standalone
+// RMSNorm kernel, so both give the same bits.
+__global__ __launch_bounds__(256) void resid_norm_finish_kernel(const float *__restrict__ partials, int splits,
+                                                                 int T, int N, bf16_t *__restrict__ h, int ldo,
+                                                                 const bf16_t *__restrict__ g, float eps,
+                                                                 bf16_t *__restrict__ xn, bf16_t *__restrict__ xn_lo) {
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    bf16_t *hr = h + (size_t)t * ldo;
+    const int nvec = N / 8;
+    float ss = 0.f;
+    for (int v = threadIdx.x; v < nvec; v += 256) {
+        const int n = 8 * v;
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        for (int sl = 0; sl < splits; ++sl) {
+            const float *p = partials + ((size_t)sl * T + t) * N + n;
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] += a[e];
+                acc[4 + e] += b[e];
+            }
+        }
+        const u32x4 hv = ld16(hr + n);
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bf16_t h0 = f32_to_bf16(lo_bf16(hv[e]) + acc[2 * e]);
+            const bf16_t h1 = f32_to_bf16(hi_bf16(hv[e]) + acc[2 * e + 1]);
+            o[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            const float a = bf16_to_f32(h0), b = bf16_to_f32(h1);
+            ss += a * a + b * b;
+        }
+        *reinterpret_cast<u32x4 *>(hr + n) = o;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) tot += red[w];
+    const float r = 1.f / sqrtf(tot / (float)N + eps);
+    for (int v = threadIdx.x; v < nvec; v += 256) {
+        const u32x4 x = ld16(hr + 8 * v), gv = ld16(g + 8 * v);  // this thread's own stores above
+        u32x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float y0 = lo_bf16(x[e]) * r * lo_bf16(gv[e]);
+            const float y1 = hi_bf16(x[e]) * r * hi_bf16(gv[e]);
+            const bf16_t h0 = f32_to_bf16(y0), h1 = f32_to_bf16(y1);
+            hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lo[e] = pack_bf16x2(y0 - bf16_to_f32(h0), y1 - bf16_to_f32(h1));
+        }
+        *reinterpret_cast<u32x4 *>(xn + (size_t)t * ldo + 8 * v) = hi;
+        *reinterpret_cast<u32x4 *>(xn_lo + (size_t)t * ldo + 8 * v) = lo;
+    }
+}
+
 template <int RT, int TB, int EPI, bool XLO>
 hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
     // Chunks in flight per wave: operand registers U·8·(RT + TB·(1 + XLO)) <= ~160.
@@ -197,6 +261,12 @@ hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hi
                        partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.k_splits == 1) return e;
+    if (EPI == EPI_RESID && skinny_fuses_norm(a, p)) {
+        hipLaunchKernelGGL(resid_norm_finish_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, partials, p.k_splits,
+                           a.T, a.N, static_cast<bf16_t *>(a.out), a.ldo, a.next_norm, a.eps, a.next_x,
+                           a.next_x_lo);
+        return hipGetLastError();
+    }
     const size_t total = (size_t)a.T * a.N;
     hipLaunchKernelGGL((skinny_finish_kernel<EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
                        partials, p.k_splits, a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.aux_f32, a.ldaux);
@@ -247,6 +317,14 @@ SkinnyPlan skinny_plan(int T, int N, int K) {
     p.k_splits = ks;
     p.k_slice = K / ks;
     return p;
+}
+
+bool skinny_fuses_norm(const SkinnyArgs &a, const SkinnyPlan &p) {
+    // SAMBAY_NO_NORM_FUSION=1 selects the separate RMSNorm launch instead (same bits).
+    const char *env = getenv("SAMBAY_NO_NORM_FUSION");
+    const bool off = env && *env && *env != '0';
+    return !off && a.epi == EPI_RESID && p.k_splits > 1 && a.next_norm && a.next_x && a.next_x_lo &&
+           a.ldo == a.N && a.N % 8 == 0;
 }
 
 size_t skinny_partial_bytes(int T, int N, const SkinnyPlan &p) {

@@ -148,6 +148,18 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> 
         res["gmu_decode_B%d" % B] = {"us_per_call": round(1e3 * ms, 2), "gbps": round(gbps, 1),
                                      "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
                                      "frac_of_stream_read": round(gbps / read_gbps, 4)}
+    # Context: two plain streaming reads of the same two weight matrices (the
+    # library's read probe, same rotation), i.e. what a perfect kernel pair
+    # could approach at this size with two launches.
+    def plain_reads(i):
+        sb.probe_stream_read_raw(sets[i % 8].W1)
+        sb.probe_stream_read_raw(sets[i % 8].W2)
+
+    pr = time_calls(plain_reads, 64)
+    for B in c["batches"]:
+        res["gmu_decode_B%d" % B]["two_plain_reads_us"] = round(1e3 * pr, 2)
+        res["gmu_decode_B%d" % B]["frac_of_two_plain_reads"] = round(pr / (res["gmu_decode_B%d" % B]["us_per_call"]
+                                                                          / 1e3), 4)
     del sets
     # Attention alone: 16 x 24 q heads, 8 KV heads, 34816 positions.
     c = workload.XATTN_DECODE

@@ -212,7 +212,7 @@ sb_status sb_timing_collect(uint32_t mask, int64_t *launches, double *total_ms);
  * sb_probe_stream_read reads `bytes` bytes of device memory `data` (16-byte
  * aligned, bytes a multiple of 16) once with a plain grid-stride streaming
  * read that does nothing else: its rate is a practical HBM read ceiling for
- * this machine.  sb_probe_mfma runs `iters` dependent steps of the
+ * this machine at that size.  sb_probe_mfma runs `iters` dependent steps of the
  * 32x32x16 bf16 MFMA on four independent accumulators per wave in 4096 waves
  * (sb_probe_mfma_flops(iters) floating-point operations): a practical dense
  * bf16 MFMA ceiling.  `sink` is 4 bytes of device memory the kernels may

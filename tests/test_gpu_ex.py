@@ -2,7 +2,13 @@
 layer against the fp64 oracle (through the C ABI), plus the invariants that
 tie them to the plain entry points.
 
-Tolerance: the bf16 bar, max |gpu - oracle| / max |oracle| <= 2e-2.
+Tolerance: the bf16 bar, max |gpu - oracle| / max |oracle| <= 2e-2, except
+for whole multi-layer complete steps at full size, whose residual stream is
+rounded to bf16 at R = 2 points per layer: two implementations that agree to
+fp32 before each rounding can land one bf16 step (2^-8 relative) apart at any
+of them, and those disagreements add up along the stream like a random walk,
+so the bar there is 2·sqrt(R)·2^-8 (R = 32: 4.4e-2); every single layer is
+still held to 2e-2 (teacher-forced).
 """
 import numpy as np
 import pytest
@@ -14,6 +20,10 @@ import workload
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL_BF16 = 2e-2
+
+
+def tol_stream(roundings: int) -> float:
+    return 2.0 * np.sqrt(roundings) * 2.0 ** -8
 
 
 @pytest.fixture(scope="module")
@@ -125,10 +135,10 @@ def _ex_inputs(B, n_layers, lens, seed, kinds=None, norms=True, mlp=True, L=300,
 
 def _oracle_ex(x, rows=None):
     rows = list(range(x.h.shape[0])) if rows is None else rows
-    idx = torch.tensor(rows)
+    idx = torch.tensor(rows, device=x.h.device)   # select on the GPU, copy only those sequences
     layers = [{k: (cpu(v) if isinstance(v, torch.Tensor) else v) for k, v in ly.items()} for ly in x.layers]
     lens = None if x.lens is None else cpu(x.lens).numpy()[rows]
-    return oracle.crossdecoder_ex(cpu(x.h)[idx], cpu(x.M)[idx], cpu(x.K)[idx], cpu(x.V)[idx], layers,
+    return oracle.crossdecoder_ex(cpu(x.h[idx]), cpu(x.M[idx]), cpu(x.K[idx]), cpu(x.V[idx]), layers,
                                   x.h.shape[1] // x.K.shape[3], lens=lens)
 
 
@@ -175,9 +185,20 @@ def test_step_ex_full_size_sampled(sb):
                                         min_len=c["min_len"])
     rows = [0, 13, 31]
     ref = _oracle_ex(x, rows)
+    h0 = x.h.clone()
     sb.crossdecoder_step_ex(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
     torch.cuda.synchronize()
-    report("step_ex full size, 3 sampled sequences", err(f64(x.h[rows]), ref), TOL_BF16)
+    report("step_ex full size, 3 sampled sequences", err(f64(x.h[rows]), ref), tol_stream(2 * c["n_layers"]))
+    # Teacher-forced: every layer alone, from the GPU's own input to it.
+    h = h0.clone()
+    worst = 0.0
+    for ly in x.layers:
+        h_in = h.clone()
+        sb.crossdecoder_step_ex(h, x.M, x.K, x.V, [ly], lens=x.lens)
+        torch.cuda.synchronize()
+        one = workload.CrossDecoderExInputs(h=h_in, M=x.M, K=x.K, V=x.V, lens=x.lens, layers=[ly])
+        worst = max(worst, err(f64(h[rows]), _oracle_ex(one, rows)))
+    report("step_ex full size, teacher-forced, worst of 16 layers", worst, TOL_BF16)
 
 
 def test_step_ex_prepared_replays_identically(sb):
@@ -190,3 +211,18 @@ def test_step_ex_prepared_replays_identically(sb):
     step()
     torch.cuda.synchronize()
     assert torch.equal(first, x.h)
+
+
+def test_step_ex_fused_norm_matches_separate_norm(sb, monkeypatch):
+    """Above 16 tokens the next sublayer's RMSNorm is fused into the residual
+    product's finishing pass; it must give the same bits as the separate
+    RMSNorm launch."""
+    x = _ex_inputs(40, 4, "ragged", seed=36)
+    h0 = x.h.clone()
+    sb.crossdecoder_step_ex(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+    fused = x.h.clone()
+    x.h.copy_(h0)
+    monkeypatch.setenv("SAMBAY_NO_NORM_FUSION", "1")
+    sb.crossdecoder_step_ex(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, x.h)
