@@ -426,7 +426,7 @@ namespace {
 
 // Workspace of one complete-layer step (all reused layer to layer).
 struct ExLayout {
-    size_t q, o, xn, gmu, mlp_g, mlp_u, part, attn, total;
+    size_t q, o, xn, gmu, mlp_u, part, attn, total;
 };
 
 ExLayout ex_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t L) {
@@ -437,18 +437,21 @@ ExLayout ex_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_ff, in
     s.o = 2 * round_up((size_t)B * d_model * sizeof(bf16_t));
     s.xn = 2 * round_up((size_t)B * d_model * sizeof(bf16_t));
     s.gmu = 2 * round_up((size_t)T * d_inner * sizeof(bf16_t));
-    s.mlp_g = d_ff > 0 ? round_up((size_t)T * d_ff * sizeof(float)) : 0;
     s.mlp_u = d_ff > 0 ? 2 * round_up((size_t)T * d_ff * sizeof(bf16_t)) : 0;
     size_t part = 0;
-    const int shapes[][2] = {{di, dm}, {dm, di}, {dm, dm}, {df, dm}, {dm, df}};
+    const int shapes[][2] = {{di, dm}, {dm, di}, {dm, dm}, {dm, df}};
     for (const auto &nk : shapes) {
         if (nk[0] <= 0 || nk[1] <= 0) continue;
         const size_t c = skinny_partial_bytes(t, nk[0], skinny_plan(t, nk[0], nk[1]));
         if (c > part) part = c;
     }
+    if (df > 0) {
+        const size_t c = skinny_partial_bytes_dual(t, df, skinny_plan_dual(t, df, dm));
+        if (c > part) part = c;
+    }
     s.part = round_up(part);
     s.attn = round_up(xattn_workspace_need(B, Hq, Hkv, L));
-    s.total = s.q + s.o + s.xn + s.gmu + s.mlp_g + s.mlp_u + s.part + s.attn;
+    s.total = s.q + s.o + s.xn + s.gmu + s.mlp_u + s.part + s.attn;
     return s;
 }
 
@@ -533,8 +536,6 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
     p += lay.xn;
     bf16_t *H = reinterpret_cast<bf16_t *>(p), *H_lo = reinterpret_cast<bf16_t *>(p + lay.gmu / 2);
     p += lay.gmu;
-    float *G = reinterpret_cast<float *>(p);
-    p += lay.mlp_g;
     bf16_t *U = reinterpret_cast<bf16_t *>(p), *U_lo = reinterpret_cast<bf16_t *>(p + lay.mlp_u / 2);
     p += lay.mlp_u;
     float *part = reinterpret_cast<float *>(p);
@@ -552,10 +553,10 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
     // One weight-streaming product of a token group of T <= 64 rows (pointers
     // already at the group's first row).
     auto product = [&](const bf16_t *X, const bf16_t *X_lo, int ldx, const void *W, int N, int K, Epilogue epi,
-                       void *out, int ldo, bf16_t *out_lo, const float *aux_f32, int T) -> hipError_t {
+                       void *out, int ldo, int T) -> hipError_t {
         SkinnyArgs a;
         a.X = X; a.X_lo = X_lo; a.ldx = ldx; a.W = (const bf16_t *)W; a.T = T; a.N = N; a.K = K; a.epi = epi;
-        a.out = out; a.ldo = ldo; a.out_lo = out_lo; a.aux_f32 = aux_f32; a.ldaux = N;
+        a.out = out; a.ldo = ldo;
         return launch_skinny(a, skinny_plan(T, N, K), part, stream);
     };
     // The residual product of a group; when `next_norm` is set the group's
@@ -593,8 +594,7 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
         if (ly.kind == SB_LAYER_XATTN) {
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
-                e = product(rows(X, t0, dm), rows(X_lo, t0, dm), dm, ly.w_a, dm, dm, EPI_F32, q + t0 * dm, dm, nullptr,
-                            nullptr, T);
+                e = product(rows(X, t0, dm), rows(X_lo, t0, dm), dm, ly.w_a, dm, dm, EPI_F32, q + t0 * dm, dm, T);
             }
             if (e == hipSuccess)
                 e = launch_xattn(q, true, (const bf16_t *)kcache, (const bf16_t *)vcache, lens, o, o_lo, (int)B,
@@ -618,11 +618,11 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
             const bf16_t *X2 = ly.norm2 ? xn : hb, *X2_lo = ly.norm2 ? xn_lo : nullptr;
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
-                e = product(rows(X2, t0, dm), rows(X2_lo, t0, dm), dm, ly.w_gate, df, dm, EPI_F32, G, df, nullptr,
-                            nullptr, T);
-                if (e == hipSuccess)
-                    e = product(rows(X2, t0, dm), rows(X2_lo, t0, dm), dm, ly.w_up, df, dm, EPI_SWIGLU, U, df, U_lo,
-                                G, T);
+                SkinnyArgs a;  // gate and up weights streamed in one pass
+                a.X = rows(X2, t0, dm); a.X_lo = rows(X2_lo, t0, dm); a.ldx = dm;
+                a.W = (const bf16_t *)ly.w_gate; a.W_b = (const bf16_t *)ly.w_up; a.T = T; a.N = df; a.K = dm;
+                a.epi = EPI_SWIGLU; a.out = U; a.ldo = df; a.out_lo = U_lo;
+                e = launch_skinny(a, skinny_plan_dual(T, df, dm), part, stream);
                 if (e == hipSuccess) e = residual(U, U_lo, df, ly.w_down, df, t0, T, after_mlp);
             }
         }

@@ -57,7 +57,7 @@ enum Epilogue {
     EPI_BF16 = 1,   // out bf16
     EPI_GATE = 2,   // out bf16 = aux[t, n] · SiLU(acc)   (aux = M, bf16)
     EPI_RESID = 3,  // out bf16 = out[t, n] + acc         (in-place residual add)
-    EPI_SWIGLU = 4  // out bf16 = SiLU(aux_f32[t, n]) · acc (aux_f32 = the gate product, fp32)
+    EPI_SWIGLU = 4  // out bf16 = SiLU(X W^T) · (X W_b^T): gate and up in one pass (W_b required)
 };
 constexpr int kSkinnyMaxTokens = 64;
 
@@ -74,13 +74,14 @@ struct SkinnyArgs {
     const bf16_t *X_lo = nullptr;  // optional low part: the product uses X + X_lo (a bf16 hi + lo pair)
     int ldx = 0;
     const bf16_t *W = nullptr;     // [N, K] bf16
+    const bf16_t *W_b = nullptr;   // EPI_SWIGLU only: the up weights [N, K]; W is then the gate (one pass, plan
+                                   // with skinny_plan_dual)
     int T = 0, N = 0, K = 0;
     Epilogue epi = EPI_F32;
     void *out = nullptr;           // [T, ldo]
     int ldo = 0;
     bf16_t *out_lo = nullptr;      // EPI_GATE / EPI_SWIGLU, optional: bf16(value - out)
     const bf16_t *aux = nullptr;   // EPI_GATE: M [T, ldaux]
-    const float *aux_f32 = nullptr; // EPI_SWIGLU: the gate product [T, ldaux]
     int ldaux = 0;
     // EPI_RESID only: also produce the next sublayer's input RMSNorm(h_new;
     // next_norm) as a bf16 hi + lo pair [T, ldo] — fused into the finishing
@@ -91,6 +92,8 @@ struct SkinnyArgs {
 };
 hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *partials, hipStream_t stream);
 bool skinny_fuses_norm(const SkinnyArgs &a, const SkinnyPlan &plan);
+SkinnyPlan skinny_plan_dual(int T, int N, int K);
+size_t skinny_partial_bytes_dual(int T, int N, const SkinnyPlan &p);
 
 // ------------------------------------------------------- prefill product
 // out[r, n] = epi( Σ_k X[r, k] · W[n, k] ), any row count, N % 64 == 0, K % 64 == 0.

@@ -19,9 +19,10 @@
 //    = 16 tokens of X with the same K assignment (X is small and L2-resident).
 //    Tokens are padded to 16 per tile; rows past the range are zero operands.
 //  * Epilogues are fused: fp32 store, bf16 store, the GMU gate
-//    H = M ⊙ SiLU(acc) stored as a bf16 hi + lo pair, the SwiGLU product
-//    SiLU(gate) ⊙ acc of the complete layer's MLP (same pair), or the
-//    residual add h = bf16(h + acc).  An X given as a hi + lo pair (the gated H, the
+//    H = M ⊙ SiLU(acc) stored as a bf16 hi + lo pair, or the residual add
+//    h = bf16(h + acc).  The complete layer's SwiGLU MLP streams its gate
+//    and up weights in one pass (paired row tiles) and stores
+//    SiLU(gate) ⊙ up as a bf16 hi + lo pair.  An X given as a hi + lo pair (the gated H, the
 //    attention output o) is multiplied as two MFMAs per operand, so rounding
 //    the intermediate to bf16 costs ~16 significant bits instead of 8.
 //  * For shapes whose row ranges would be too thin, K is also split across
@@ -43,7 +44,7 @@ constexpr int kTargetWGs = 256;
 
 template <int EPI>
 __device__ __forceinline__ void apply_epilogue(float v, int t, int n, void *out, int ldo, bf16_t *out_lo,
-                                               const bf16_t *aux, const float *aux_f32, int ldaux) {
+                                               const bf16_t *aux, int ldaux) {
     const size_t o = (size_t)t * ldo + n;
     if (EPI == EPI_F32) {
         reinterpret_cast<float *>(out)[o] = v;
@@ -55,27 +56,33 @@ __device__ __forceinline__ void apply_epilogue(float v, int t, int n, void *out,
         const bf16_t hi = f32_to_bf16(g);
         reinterpret_cast<bf16_t *>(out)[o] = hi;
         if (out_lo) out_lo[o] = f32_to_bf16(g - bf16_to_f32(hi));
-    } else if (EPI == EPI_SWIGLU) {
-        const float a = aux_f32[(size_t)t * ldaux + n];
-        const float u = (a / (1.f + expf(-a))) * v;
-        const bf16_t hi = f32_to_bf16(u);
-        reinterpret_cast<bf16_t *>(out)[o] = hi;
-        if (out_lo) out_lo[o] = f32_to_bf16(u - bf16_to_f32(hi));
     } else {
         bf16_t *h = reinterpret_cast<bf16_t *>(out);
         h[o] = f32_to_bf16(bf16_to_f32(h[o]) + v);
     }
 }
 
+// The SwiGLU MLP's two products of the same input in one pass: u = SiLU(g) · v
+// with g from W and v from W_b (same rows), stored as a bf16 hi + lo pair.
+__device__ __forceinline__ void store_swiglu(float g, float v, int t, int n, void *out, int ldo, bf16_t *out_lo) {
+    const size_t o = (size_t)t * ldo + n;
+    const float u = (g / (1.f + expf(-g))) * v;
+    const bf16_t hi = f32_to_bf16(u);
+    reinterpret_cast<bf16_t *>(out)[o] = hi;
+    if (out_lo) out_lo[o] = f32_to_bf16(u - bf16_to_f32(hi));
+}
+
 // RT row tiles of 16, TB token tiles of 16, U chunks in flight per wave; XLO:
-// X arrives as a bf16 hi + lo pair (two MFMAs per operand pair).
-template <int RT, int TB, int U, int EPI, bool XLO>
+// X arrives as a bf16 hi + lo pair (two MFMAs per operand pair).  DUAL: the
+// first RT/2 row tiles come from W, the other RT/2 from W_b at the same rows
+// (the SwiGLU gate and up products); partials then hold [slice][T][2N].
+template <int RT, int TB, int U, int EPI, bool XLO, bool DUAL = false>
 __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restrict__ X,
                                                           const bf16_t *__restrict__ X_lo, int ldx,
-                                                          const bf16_t *__restrict__ W, int T, int N, int K, int R,
+                                                          const bf16_t *__restrict__ W,
+                                                          const bf16_t *__restrict__ W_b, int T, int N, int K, int R,
                                                           int k_slice, void *out, int ldo, bf16_t *out_lo,
-                                                          const bf16_t *__restrict__ aux,
-                                                          const float *__restrict__ aux_f32, int ldaux,
+                                                          const bf16_t *__restrict__ aux, int ldaux,
                                                           float *__restrict__ partials) {
     constexpr int TT = 16 * TB;
     __shared__ float red[kWaves][16 * RT][TT + 4];
@@ -85,13 +92,16 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
     const int kbeg = blockIdx.y * k_slice;
     const int nchunks = k_slice / kChunk;
 
+    constexpr int RH = DUAL ? RT / 2 : RT;  // row tiles per weight matrix
+    static_assert(!DUAL || RT % 2 == 0, "dual products take row tiles in pairs");
     const bf16_t *wrow[RT];
     bool rvalid[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const int rl = 16 * rt + col;
+        const int rl = 16 * (rt % RH) + col;
+        const bf16_t *Wm = (DUAL && rt >= RH) ? W_b : W;
         rvalid[rt] = rl < R && n0 + rl < N;
-        wrow[rt] = W + (size_t)(rvalid[rt] ? n0 + rl : 0) * K + kbeg + 8 * grp;
+        wrow[rt] = Wm + (size_t)(rvalid[rt] ? n0 + rl : 0) * K + kbeg + 8 * grp;
     }
     size_t xoff[TB];
 #pragma unroll
@@ -163,27 +173,48 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restri
     for (int idx = threadIdx.x; idx < total; idx += kThreads) {
         const int t = idx / R, rl = idx % R, n = n0 + rl;
         if (n >= N) continue;
-        float v = 0.f;
+        float v = 0.f, vb = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) v += red[w][rl][t];
-        if (gridDim.y == 1)
-            apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, aux_f32, ldaux);
-        else
-            partials[((size_t)blockIdx.y * T + t) * N + n] = v;
+        for (int w = 0; w < kWaves; ++w) {
+            v += red[w][rl][t];
+            if (DUAL) vb += red[w][16 * RH + rl][t];
+        }
+        if (gridDim.y == 1) {
+            if (DUAL)
+                store_swiglu(v, vb, t, n, out, ldo, out_lo);
+            else
+                apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, ldaux);
+        } else {
+            const int np = DUAL ? 2 * N : N;
+            partials[((size_t)blockIdx.y * T + t) * np + n] = v;
+            if (DUAL) partials[((size_t)blockIdx.y * T + t) * np + N + n] = vb;
+        }
     }
+}
+
+__global__ __launch_bounds__(256) void swiglu_finish_kernel(const float *__restrict__ partials, int splits, int T,
+                                                            int N, void *out, int ldo, bf16_t *out_lo) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)T * N) return;
+    const int t = (int)(idx / N), n = (int)(idx % N);
+    float g = 0.f, v = 0.f;
+    for (int s = 0; s < splits; ++s) {
+        g += partials[((size_t)s * T + t) * 2 * N + n];
+        v += partials[((size_t)s * T + t) * 2 * N + N + n];
+    }
+    store_swiglu(g, v, t, n, out, ldo, out_lo);
 }
 
 template <int EPI>
 __global__ __launch_bounds__(256) void skinny_finish_kernel(const float *__restrict__ partials, int splits, int T,
                                                             int N, void *out, int ldo, bf16_t *out_lo,
-                                                            const bf16_t *__restrict__ aux,
-                                                            const float *__restrict__ aux_f32, int ldaux) {
+                                                            const bf16_t *__restrict__ aux, int ldaux) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)T * N) return;
     const int t = (int)(idx / N), n = (int)(idx % N);
     float v = 0.f;
     for (int s = 0; s < splits; ++s) v += partials[((size_t)s * T + t) * N + n];
-    apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, aux_f32, ldaux);
+    apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, ldaux);
 }
 
 // K-split finishing of a residual product fused with the next sublayer's
@@ -250,17 +281,22 @@ __global__ __launch_bounds__(256) void resid_norm_finish_kernel(const float *__r
     }
 }
 
-template <int RT, int TB, int EPI, bool XLO>
+template <int RT, int TB, int EPI, bool XLO, bool DUAL = false>
 hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
     // Chunks in flight per wave: operand registers U·8·(RT + TB·(1 + XLO)) <= ~160.
     constexpr int U = 20 / (RT + TB * (XLO ? 2 : 1)) < 1 ? 1 : 20 / (RT + TB * (XLO ? 2 : 1));
     const dim3 grid((a.N + p.rows_per_wg - 1) / p.rows_per_wg, p.k_splits);
     TimingScope ts(kTimeSkinny, stream);
-    hipLaunchKernelGGL((skinny_kernel<RT, TB, U, EPI, XLO>), grid, dim3(kThreads), 0, stream, a.X, a.X_lo, a.ldx, a.W,
-                       a.T, a.N, a.K, p.rows_per_wg, p.k_slice, a.out, a.ldo, a.out_lo, a.aux, a.aux_f32, a.ldaux,
-                       partials);
+    hipLaunchKernelGGL((skinny_kernel<RT, TB, U, EPI, XLO, DUAL>), grid, dim3(kThreads), 0, stream, a.X, a.X_lo, a.ldx,
+                       a.W, a.W_b, a.T, a.N, a.K, p.rows_per_wg, p.k_slice, a.out, a.ldo, a.out_lo, a.aux, a.ldaux, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.k_splits == 1) return e;
+    if (DUAL) {
+        const size_t total = (size_t)a.T * a.N;
+        hipLaunchKernelGGL(swiglu_finish_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, partials,
+                           p.k_splits, a.T, a.N, a.out, a.ldo, a.out_lo);
+        return hipGetLastError();
+    }
     if (EPI == EPI_RESID && skinny_fuses_norm(a, p)) {
         hipLaunchKernelGGL(resid_norm_finish_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, partials, p.k_splits,
                            a.T, a.N, static_cast<bf16_t *>(a.out), a.ldo, a.next_norm, a.eps, a.next_x,
@@ -269,12 +305,19 @@ hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hi
     }
     const size_t total = (size_t)a.T * a.N;
     hipLaunchKernelGGL((skinny_finish_kernel<EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       partials, p.k_splits, a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.aux_f32, a.ldaux);
+                       partials, p.k_splits, a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.ldaux);
     return hipGetLastError();
 }
 
 template <int RT, int TB, int EPI>
 hipError_t launch3(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    if (EPI == EPI_SWIGLU) {  // always the dual gate + up pass
+        if constexpr (RT % 2 == 0) {
+            if (a.X_lo) return launch4<RT, TB, EPI, true, true>(a, p, partials, stream);
+            return launch4<RT, TB, EPI, false, true>(a, p, partials, stream);
+        }
+        return hipErrorInvalidValue;
+    }
     if (a.X_lo) return launch4<RT, TB, EPI, true>(a, p, partials, stream);
     return launch4<RT, TB, EPI, false>(a, p, partials, stream);
 }
@@ -319,6 +362,18 @@ SkinnyPlan skinny_plan(int T, int N, int K) {
     return p;
 }
 
+SkinnyPlan skinny_plan_dual(int T, int N, int K) {
+    // Plan the 2N weight rows together, then give each workgroup R/2 output
+    // rows (R/2 rows of each matrix).
+    SkinnyPlan p = skinny_plan(T, 2 * N, K);
+    p.rows_per_wg = p.rows_per_wg / 2 > 0 ? p.rows_per_wg / 2 : 1;
+    return p;
+}
+
+size_t skinny_partial_bytes_dual(int T, int N, const SkinnyPlan &p) {
+    return p.k_splits > 1 ? (size_t)p.k_splits * T * 2 * N * sizeof(float) : 0;
+}
+
 bool skinny_fuses_norm(const SkinnyArgs &a, const SkinnyPlan &p) {
     // SAMBAY_NO_NORM_FUSION=1 selects the separate RMSNorm launch instead (same bits).
     const char *env = getenv("SAMBAY_NO_NORM_FUSION");
@@ -333,6 +388,10 @@ size_t skinny_partial_bytes(int T, int N, const SkinnyPlan &p) {
 
 hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *partials, hipStream_t stream) {
     const int R = plan.rows_per_wg;
+    if (a.epi == EPI_SWIGLU) {  // dual: row tiles in pairs, R <= 32 (skinny_plan_dual)
+        if (!a.W_b || R > 32) return hipErrorInvalidValue;
+        return R <= 16 ? launch1<2>(a, plan, partials, stream) : launch1<4>(a, plan, partials, stream);
+    }
     if (R <= 16) return launch1<1>(a, plan, partials, stream);
     if (R <= 32) return launch1<2>(a, plan, partials, stream);
     return launch1<4>(a, plan, partials, stream);
