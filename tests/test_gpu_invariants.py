@@ -156,3 +156,48 @@ def test_ceiling_probes_run(sb):
     tf = sb.probe_mfma_tflops(DEV, iters=200)
     assert 100.0 < gbps < 8000.0 * 1.05
     assert 10.0 < tf < 2500.0 * 1.05
+
+
+def _capture(fn):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("complete", [False, True])
+def test_step_replays_from_a_hip_graph(sb, complete):
+    """The prepared steps enqueue only kernels (no memset, no allocation), so a
+    captured HIP graph replays them bit-identically, also with eager work and
+    synchronisations between replays."""
+    if complete:
+        x = workload.crossdecoder_ex_inputs(40, 384, 768, 512, 3, 1, 128, 300, 4, seed=13, device=DEV,
+                                            lens=[300, 1, 77] + [200] * 37)
+        step = sb.CrossDecoderStepEx(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+    else:
+        x = workload.crossdecoder_inputs(40, 384, 768, 3, 1, 128, 300, 4, seed=13, device=DEV)
+        step = sb.CrossDecoderStep(x.h, x.M, x.K, x.V, x.layers)
+    h_in = x.h.clone()
+
+    def run():
+        x.h.copy_(h_in)
+        step()
+
+    run()
+    torch.cuda.synchronize()
+    ref = x.h.clone()
+    g = _capture(run)
+    for _ in range(4):
+        x.h.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(x.h, ref)
+        run()
+        torch.cuda.synchronize()
+        assert torch.equal(x.h, ref)
