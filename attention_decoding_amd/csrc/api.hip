@@ -84,10 +84,8 @@ size_t gmu_ws(int64_t rows, int64_t d_model, int64_t d_inner, sb_dtype dt) {
     size_t bytes = round_up((size_t)rows * d_inner * sizeof(bf16_t));
     if (rows <= kSkinnyMaxTokens) {
         bytes *= 2;
-        const SkinnyPlan p1 = skinny_plan((int)rows, (int)d_inner, (int)d_model);
-        const SkinnyPlan p2 = skinny_plan((int)rows, (int)d_model, (int)d_inner);
-        size_t part = skinny_partial_bytes((int)rows, (int)d_inner, p1);
-        const size_t part2 = skinny_partial_bytes((int)rows, (int)d_model, p2);
+        size_t part = skinny_partial_bytes_max((int)rows, (int)d_inner, (int)d_model);
+        const size_t part2 = skinny_partial_bytes_max((int)rows, (int)d_model, (int)d_inner);
         if (part2 > part) part = part2;
         bytes += round_up(part);
     }
@@ -104,8 +102,8 @@ hipError_t gmu_decode_bf16(const bf16_t *M, const bf16_t *X, const bf16_t *X_lo,
     bf16_t *H = static_cast<bf16_t *>(ws.take((size_t)T * d_inner * sizeof(bf16_t)));
     bf16_t *H_lo = static_cast<bf16_t *>(ws.take((size_t)T * d_inner * sizeof(bf16_t)));
     if (!h_lo) H_lo = nullptr;
-    const SkinnyPlan p1 = skinny_plan(T, d_inner, d_model);
-    const SkinnyPlan p2 = skinny_plan(T, d_model, d_inner);
+    const SkinnyPlan p1 = skinny_plan(T, d_inner, d_model, X_lo != nullptr);
+    const SkinnyPlan p2 = skinny_plan(T, d_model, d_inner, H_lo != nullptr);
     size_t part = skinny_partial_bytes(T, d_inner, p1);
     if (skinny_partial_bytes(T, d_model, p2) > part) part = skinny_partial_bytes(T, d_model, p2);
     float *partials = static_cast<float *>(ws.take(part));
@@ -188,8 +186,8 @@ extern "C" sb_status gmu_forward(const void *M, const void *X, const void *W1, c
             fprintf(stderr, "[sambay] gmu_forward rows=%lld %lldx%lld fp32 -> gmu_f32 kernels\n", (long long)rows,
                     (long long)d_model, (long long)d_inner);
         } else if (rows <= kSkinnyMaxTokens) {
-            const SkinnyPlan p1 = skinny_plan((int)rows, (int)d_inner, (int)d_model);
-            const SkinnyPlan p2 = skinny_plan((int)rows, (int)d_model, (int)d_inner);
+            const SkinnyPlan p1 = skinny_plan((int)rows, (int)d_inner, (int)d_model, false);
+            const SkinnyPlan p2 = skinny_plan((int)rows, (int)d_model, (int)d_inner, false);
             fprintf(stderr,
                     "[sambay] gmu_forward rows=%lld %lldx%lld bf16 -> decode products: gate rows/wg=%d ksplit=%d, "
                     "out rows/wg=%d ksplit=%d\n",
@@ -297,11 +295,9 @@ StepLayout step_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t Hq, 
     s.o = 2 * round_up((size_t)B * d_model * sizeof(bf16_t));
     // GMU: H for one token group plus k-split partials; projections share the partial space.
     size_t part = 0;
-    const SkinnyPlan pa = skinny_plan((int)T, (int)d_inner, (int)d_model);
-    const SkinnyPlan pb = skinny_plan((int)T, (int)d_model, (int)d_inner);
-    const SkinnyPlan pq = skinny_plan((int)T, (int)d_model, (int)d_model);
-    const size_t cands[] = {skinny_partial_bytes((int)T, (int)d_inner, pa), skinny_partial_bytes((int)T, (int)d_model, pb),
-                            skinny_partial_bytes((int)T, (int)d_model, pq)};
+    const size_t cands[] = {skinny_partial_bytes_max((int)T, (int)d_inner, (int)d_model),
+                            skinny_partial_bytes_max((int)T, (int)d_model, (int)d_inner),
+                            skinny_partial_bytes_max((int)T, (int)d_model, (int)d_model)};
     for (size_t c : cands)
         if (c > part) part = c;
     s.gmu = 2 * round_up((size_t)T * d_inner * sizeof(bf16_t)) + round_up(part);
@@ -395,7 +391,7 @@ extern "C" sb_status crossdecoder_step(void *h, const void *M, const void *kcach
                 SkinnyArgs aq;
                 aq.X = hb + t0 * dm; aq.ldx = dm; aq.W = (const bf16_t *)ly.w_a; aq.T = T; aq.N = dm; aq.K = dm;
                 aq.epi = EPI_F32; aq.out = q + t0 * dm; aq.ldo = dm;
-                e = launch_skinny(aq, skinny_plan(T, dm, dm), proj_partials, stream);
+                e = launch_skinny(aq, skinny_plan(T, dm, dm, false), proj_partials, stream);
             }
             if (e == hipSuccess)
                 e = launch_xattn(q, true, (const bf16_t *)kcache, (const bf16_t *)vcache, nullptr, o, o_lo, (int)B, (int)Hq,
@@ -405,7 +401,7 @@ extern "C" sb_status crossdecoder_step(void *h, const void *M, const void *kcach
                 SkinnyArgs ao;
                 ao.X = o + t0 * dm; ao.X_lo = o_lo + t0 * dm; ao.ldx = dm; ao.W = (const bf16_t *)ly.w_b; ao.T = T;
                 ao.N = dm; ao.K = dm; ao.epi = EPI_RESID; ao.out = hb + t0 * dm; ao.ldo = dm;
-                e = launch_skinny(ao, skinny_plan(T, dm, dm), proj_partials, stream);
+                e = launch_skinny(ao, skinny_plan(T, dm, dm, true), proj_partials, stream);
             }
         } else {
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
@@ -442,7 +438,7 @@ ExLayout ex_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_ff, in
     const int shapes[][2] = {{di, dm}, {dm, di}, {dm, dm}, {dm, df}};
     for (const auto &nk : shapes) {
         if (nk[0] <= 0 || nk[1] <= 0) continue;
-        const size_t c = skinny_partial_bytes(t, nk[0], skinny_plan(t, nk[0], nk[1]));
+        const size_t c = skinny_partial_bytes_max(t, nk[0], nk[1]);
         if (c > part) part = c;
     }
     if (df > 0) {
@@ -557,7 +553,7 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
         SkinnyArgs a;
         a.X = X; a.X_lo = X_lo; a.ldx = ldx; a.W = (const bf16_t *)W; a.T = T; a.N = N; a.K = K; a.epi = epi;
         a.out = out; a.ldo = ldo;
-        return launch_skinny(a, skinny_plan(T, N, K), part, stream);
+        return launch_skinny(a, skinny_plan(T, N, K, X_lo != nullptr), part, stream);
     };
     // The residual product of a group; when `next_norm` is set the group's
     // rows of the next sublayer's input RMSNorm(h; next_norm) are produced
@@ -569,7 +565,7 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
         a.epi = EPI_RESID; a.out = hb + t0 * dm; a.ldo = dm;
         a.next_norm = (const bf16_t *)next_norm; a.next_x = xn + t0 * dm; a.next_x_lo = xn_lo + t0 * dm;
         a.eps = eps;
-        const SkinnyPlan plan_r = skinny_plan(T, dm, K);
+        const SkinnyPlan plan_r = skinny_plan(T, dm, K, X_lo != nullptr);
         hipError_t e = launch_skinny(a, plan_r, part, stream);
         if (e == hipSuccess && next_norm && !skinny_fuses_norm(a, plan_r))
             e = launch_rmsnorm(hb + t0 * dm, (const bf16_t *)next_norm, T, dm, eps, xn + t0 * dm, xn_lo + t0 * dm,
@@ -610,7 +606,7 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
                 a1.X = rows(X, t0, dm); a1.X_lo = rows(X_lo, t0, dm); a1.ldx = dm;
                 a1.W = (const bf16_t *)ly.w_a; a1.T = T; a1.N = di; a1.K = dm; a1.epi = EPI_GATE;
                 a1.out = H; a1.ldo = di; a1.out_lo = H_lo; a1.aux = (const bf16_t *)M + t0 * di; a1.ldaux = di;
-                e = launch_skinny(a1, skinny_plan(T, di, dm), part, stream);
+                e = launch_skinny(a1, skinny_plan(T, di, dm, a1.X_lo != nullptr), part, stream);
                 if (e == hipSuccess) e = residual(H, H_lo, di, ly.w_b, di, t0, T, after_mixer);
             }
         }

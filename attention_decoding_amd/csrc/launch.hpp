@@ -66,8 +66,10 @@ struct SkinnyPlan {
     int k_splits;      // workgroups along K (1 = epilogue fused)
     int k_slice;       // K elements per split (multiple of 64)
 };
-SkinnyPlan skinny_plan(int T, int N, int K);
+// xlo: the token operand is a bf16 hi + lo pair (twice the bytes per workgroup).
+SkinnyPlan skinny_plan(int T, int N, int K, bool xlo);
 size_t skinny_partial_bytes(int T, int N, const SkinnyPlan &p);
+size_t skinny_partial_bytes_max(int T, int N, int K);  // over both operand kinds (workspace sizing)
 
 struct SkinnyArgs {
     const bf16_t *X = nullptr;     // [T, ldx] bf16

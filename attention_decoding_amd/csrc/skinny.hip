@@ -25,8 +25,10 @@
 //    SiLU(gate) ⊙ up as a bf16 hi + lo pair.  An X given as a hi + lo pair (the gated H, the
 //    attention output o) is multiplied as two MFMAs per operand, so rounding
 //    the intermediate to bf16 costs ~16 significant bits instead of 8.
-//  * For shapes whose row ranges would be too thin, K is also split across
-//    workgroups; fp32 partials then go through a small finishing kernel.
+//  * When the token operand a workgroup must read is large (many tokens, a
+//    hi + lo pair, long K), K is also split across workgroups so that each
+//    takes ~48 rows and the grid stays at ~256 workgroups; fp32 partials then
+//    go through a small finishing kernel (skinny_plan gives the measured rule).
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -342,15 +344,23 @@ hipError_t launch1(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hi
 
 }  // namespace
 
-SkinnyPlan skinny_plan(int T, int N, int K) {
-    // Every workgroup re-reads X[:, its K slice] from L2, T·K·2 bytes without a
-    // K split; splitting K across workgroups trades that for fp32 partials and
-    // a finishing launch.  Measured: a 2-way split pays off above 16 tokens.
-    int ks = T > 16 ? 2 : 1;
+SkinnyPlan skinny_plan(int T, int N, int K, bool xlo) {
+    // Every workgroup reads the K slice of the token operand from L2: T·K·2
+    // bytes without a K split (twice that for a hi + lo pair).  Measured on
+    // MI355X (N, K in {3072, 6144}, 1-64 tokens, all epilogues): below ~190
+    // KB per workgroup, one workgroup per CU over ceil(N/256) rows and no
+    // split is fastest; above it, ~48 rows per workgroup with K split so that
+    // the grid stays at ~256 workgroups wins by up to 30% (e.g. the 3072 x
+    // 6144 product with a hi + lo operand at 32 tokens: 22.5 -> 18.6 us),
+    // finishing pass included.
+    const int64_t xbytes = (int64_t)T * K * 2 * (xlo ? 2 : 1);
+    int ks = 1;
+    if (xbytes >= (int64_t)192 * 1024) ks = (int)((256LL * 48 + N / 2) / N);
     const char *e = getenv("SAMBAY_SKINNY_KSPLIT");
     if (e && *e) ks = atoi(e);
-    if (ks < 1) ks = 1;
     const int kc = K / kChunk;
+    if (ks > kc) ks = kc;
+    if (ks < 1) ks = 1;
     while (ks > 1 && kc % ks != 0) --ks;
     SkinnyPlan p;
     int R = (int)(((int64_t)N * ks + kTargetWGs - 1) / kTargetWGs);
@@ -362,11 +372,25 @@ SkinnyPlan skinny_plan(int T, int N, int K) {
     return p;
 }
 
+size_t skinny_partial_bytes_max(int T, int N, int K) {
+    const size_t a = skinny_partial_bytes(T, N, skinny_plan(T, N, K, false));
+    const size_t b = skinny_partial_bytes(T, N, skinny_plan(T, N, K, true));
+    return a > b ? a : b;
+}
+
 SkinnyPlan skinny_plan_dual(int T, int N, int K) {
-    // Plan the 2N weight rows together, then give each workgroup R/2 output
-    // rows (R/2 rows of each matrix).
-    SkinnyPlan p = skinny_plan(T, 2 * N, K);
-    p.rows_per_wg = p.rows_per_wg / 2 > 0 ? p.rows_per_wg / 2 : 1;
+    // The 2N weight rows are planned together (a 2-way K split above 16
+    // tokens), then each workgroup takes R/2 output rows (R/2 rows of each
+    // matrix).
+    int ks = T > 16 ? 2 : 1;
+    const int kc = K / kChunk;
+    while (ks > 1 && kc % ks != 0) --ks;
+    SkinnyPlan p;
+    int R = (int)(((int64_t)2 * N * ks + kTargetWGs - 1) / kTargetWGs);
+    if (R > 64) R = 64;
+    p.rows_per_wg = R / 2 > 0 ? R / 2 : 1;
+    p.k_splits = ks;
+    p.k_slice = K / ks;
     return p;
 }
 
@@ -394,6 +418,7 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *par
     }
     if (R <= 16) return launch1<1>(a, plan, partials, stream);
     if (R <= 32) return launch1<2>(a, plan, partials, stream);
+    if (R <= 48) return launch1<3>(a, plan, partials, stream);
     return launch1<4>(a, plan, partials, stream);
 }
 
