@@ -244,3 +244,27 @@ def test_crossdecoder_teacher_forced_layers(sb):
         worst = max(worst, e)
         assert e <= TOL_BF16, "layer %d (%s): err %.3e" % (i, layer[0], e)
     report("crossdecoder teacher-forced, worst of 16 layers", worst, TOL_BF16)
+
+
+def test_crossdecoder_single_sequence_full_width(sb):
+    """B = 1 at the full widths (d_model 3072, d_inner 6144): every product of
+    the step takes the one-token dot-product path (fp32 query, hi + lo attention
+    output into Wo, GMU gate with hi + lo H, residual adds)."""
+    c = workload.CROSSDECODER
+    x = workload.crossdecoder_inputs(1, c["d_model"], c["d_inner"], c["Hq"], c["Hkv"], c["D"], 3000, 16, seed=17,
+                                     device=DEV)
+    h0 = x.h.clone()
+    sb.crossdecoder_step(x.h, x.M, x.K, x.V, x.layers)
+    torch.cuda.synchronize()
+    ref = oracle.crossdecoder(cpu(h0), cpu(x.M), cpu(x.K), cpu(x.V), [(k, cpu(a), cpu(b)) for k, a, b in x.layers],
+                              c["Hq"])
+    report("crossdecoder B=1 full width, 16 layers", err(f64(x.h), ref), TOL_BF16)
+    # The complete layer at one token: MLP down-projection has K = 8192.
+    e = workload.crossdecoder_ex_inputs(1, c["d_model"], c["d_inner"], 8192, c["Hq"], c["Hkv"], c["D"], 3000, 2,
+                                        seed=18, device=DEV, lens=[2500])
+    h0 = e.h.clone()
+    sb.crossdecoder_step_ex(e.h, e.M, e.K, e.V, e.layers, lens=e.lens)
+    torch.cuda.synchronize()
+    layers = [{k: (cpu(v) if isinstance(v, torch.Tensor) else v) for k, v in ly.items()} for ly in e.layers]
+    ref = oracle.crossdecoder_ex(cpu(h0), cpu(e.M), cpu(e.K), cpu(e.V), layers, c["Hq"], lens=[2500])
+    report("complete step B=1 full width, 2 layers", err(f64(e.h), ref), TOL_BF16)
