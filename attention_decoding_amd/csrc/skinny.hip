@@ -311,6 +311,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(const bf16_t *__restrict__ X,
 #pragma unroll
             for (int s = 0; s < KS; ++s)
                 wr[r][s] = n0 + r < N ? ld16(W + (size_t)(n0 + r) * K + s * 512 + 8 * lane) : (u32x4){0u, 0u, 0u, 0u};
+        // The epilogue's own input (M for the gate, h for the residual add) is
+        // fetched together with the weights so its latency overlaps theirs.
+        float pre[RPW];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            pre[r] = 0.f;
+            if ((EPI == EPI_GATE || EPI == EPI_RESID) && lane == 0 && n0 + r < N)
+                pre[r] = bf16_to_f32(EPI == EPI_GATE ? aux[n0 + r] : reinterpret_cast<const bf16_t *>(out)[n0 + r]);
+        }
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
             float acc = 0.f;
@@ -325,7 +334,20 @@ __global__ __launch_bounds__(256) void gemv_kernel(const bf16_t *__restrict__ X,
                 }
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-            if (lane == 0 && n0 + r < N) apply_epilogue<EPI>(acc, 0, n0 + r, out, N, out_lo, aux, N);
+            if (lane != 0 || n0 + r >= N) continue;
+            const int n = n0 + r;
+            if (EPI == EPI_F32) {
+                reinterpret_cast<float *>(out)[n] = acc;
+            } else if (EPI == EPI_BF16) {
+                reinterpret_cast<bf16_t *>(out)[n] = f32_to_bf16(acc);
+            } else if (EPI == EPI_GATE) {
+                const float g = pre[r] * (acc / (1.f + expf(-acc)));
+                const bf16_t hi = f32_to_bf16(g);
+                reinterpret_cast<bf16_t *>(out)[n] = hi;
+                if (out_lo) out_lo[n] = f32_to_bf16(g - bf16_to_f32(hi));
+            } else {
+                reinterpret_cast<bf16_t *>(out)[n] = f32_to_bf16(pre[r] + acc);
+            }
         }
     }
 }
