@@ -24,7 +24,8 @@
 //  * Measured at 8192 x 2560 x 5120 (both GMU products, random data): ~250 us
 //    for the gate product and ~227 us for the output product (850-950
 //    TFLOP/s).  A 3-5 deep ring (BK 64 or 32), 256-wide tiles with 8 or 16
-//    waves, 64x128 or 128x128 blocks per wave, and reading a whole slice's
+//    waves, 128x160 tiles (whole tile rounds on the output product), 64x128
+//    or 128x128 blocks per wave, and reading a whole slice's
 //    fragments before its MFMAs (forced with scheduling barriers) all
 //    measured equal or slower; MFMA busy stays near a third, LDS bank
 //    conflicts are zero.

@@ -11,8 +11,8 @@
 //    so every CU streams the same number of bytes.  Eight waves per
 //    workgroup split the K dimension in 64-wide chunks; their 16x16x32 MFMA
 //    partial tiles are summed through LDS in a fixed order (deterministic).
-//    For comparison, a plain 37.7 MB HBM read kernel takes ~7.2 us per
-//    launch back to back on MI355X; one GMU product here takes ~10-11 us.
+//    For comparison, a plain 37.7 MB HBM read kernel takes ~7.2-7.7 us per
+//    launch back to back on MI355X; one GMU product here takes ~9-12 us.
 //  * A operand = 16 weight rows; MFMA k-step t of a chunk covers 32
 //    contiguous K elements, lane group grp holding elements 8·grp .. 8·grp+7,
 //    so each load instruction reads 64 contiguous bytes of 16 rows.  B operand
@@ -22,9 +22,12 @@
 //    H = M ⊙ SiLU(acc) stored as a bf16 hi + lo pair, or the residual add
 //    h = bf16(h + acc).  The complete layer's SwiGLU MLP streams its gate
 //    and up weights in one pass (paired row tiles) and stores
-//    SiLU(gate) ⊙ up as a bf16 hi + lo pair.  An X given as a hi + lo pair (the gated H, the
-//    attention output o) is multiplied as two MFMAs per operand, so rounding
-//    the intermediate to bf16 costs ~16 significant bits instead of 8.
+//    SiLU(gate) ⊙ up as a bf16 hi + lo pair.  An X given as a hi + lo pair
+//    (the gated H, the attention output o, a normalised input) is multiplied
+//    as two MFMAs per operand, so rounding the intermediate to bf16 costs
+//    ~16 significant bits instead of 8.
+//  * One token: a VALU dot-product kernel (gemv_kernel) with row-contiguous
+//    loads replaces the MFMA tile, whose 16 token slots would be 15/16 padding.
 //  * When the token operand a workgroup must read is large (many tokens, a
 //    hi + lo pair, long K), K is also split across workgroups so that each
 //    takes ~48 rows and the grid stays at ~256 workgroups; fp32 partials then
