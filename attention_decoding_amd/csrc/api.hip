@@ -185,6 +185,10 @@ extern "C" sb_status gmu_forward(const void *M, const void *X, const void *W1, c
         if (dt == SB_F32) {
             fprintf(stderr, "[sambay] gmu_forward rows=%lld %lldx%lld fp32 -> gmu_f32 kernels\n", (long long)rows,
                     (long long)d_model, (long long)d_inner);
+        } else if (rows == 1 && (d_model == 3072 || d_model == 6144 || d_model == 8192) &&
+                   (d_inner == 3072 || d_inner == 6144 || d_inner == 8192)) {
+            fprintf(stderr, "[sambay] gmu_forward rows=1 %lldx%lld bf16 -> one-token dot-product products\n",
+                    (long long)d_model, (long long)d_inner);
         } else if (rows <= kSkinnyMaxTokens) {
             const SkinnyPlan p1 = skinny_plan((int)rows, (int)d_inner, (int)d_model, false);
             const SkinnyPlan p2 = skinny_plan((int)rows, (int)d_model, (int)d_inner, false);
