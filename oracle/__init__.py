@@ -69,6 +69,9 @@ def _load():
                                            vp, vp, ctypes.c_int, i32, i64, i64, i64, i64, i64, i64, i64, i64, dbl,
                                            dbl, ctypes.c_int, vp]
     lib.oracle_crossdecoder_ex.restype = ctypes.c_int
+    lib.oracle_diffattn.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i64, i64,
+                                    i64, i64, i64, dbl, dbl, dbl, dbl]
+    lib.oracle_diffattn.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [dbl]
     lib.oracle_round_bf16.restype = dbl
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -291,6 +294,35 @@ def xattn_varlen(q, K, V, lens, scale: float | None = None):
     rc = lib.oracle_xattn_varlen(_ptr(qa), dq, _ptr(ka), _ptr(va), dk, _ptr(la), _ptr(out), B, Hq, Hkv, D, L,
                                  float(scale))
     _check(rc, "xattn_varlen")
+    return out
+
+
+def diffattn(q, K, V, lam: float, lam_init: float, gamma=None, lens=None, eps: float = 1e-5,
+             scale: float | None = None):
+    """Differential attention decode over a shared GQA cache.
+
+    Each D-wide query / key row is two halves (q1 | q2), (k1 | k2); value rows
+    keep all D.  out = (1 - lam_init) * RMSNorm(softmax(scale q1 k1^T) V
+    - lam * softmax(scale q2 k2^T) V) * gamma per head; scale defaults to
+    1/sqrt(D/2); gamma None means ones; lens as in xattn_varlen."""
+    lib = _load()
+    qa, dq = _as_input(q)
+    ka, dk = _as_input(K)
+    va, dv = _as_input(V)
+    if dk != dv:
+        raise TypeError("K and V must share a dtype")
+    B, Hq, Hkv, D, L = _xattn_shapes(qa, ka, va)
+    la = None if lens is None else _lens_array(lens, B, L)
+    ga, dg = (None, F64) if gamma is None else _as_input(gamma)
+    if ga is not None and ga.shape != (D,):
+        raise ValueError("gamma must have D entries")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D // 2)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    rc = lib.oracle_diffattn(_ptr(qa), dq, _ptr(ka), _ptr(va), dk, None if la is None else _ptr(la),
+                             None if ga is None else _ptr(ga), dg, _ptr(out), B, Hq, Hkv, D, L, float(scale),
+                             float(lam), float(lam_init), float(eps))
+    _check(rc, "diffattn")
     return out
 
 

@@ -706,6 +706,94 @@ int oracle_crossdecoder_ex(const void *h0, const void *M, int dt_act, const void
     return fail;
 }
 
+/* ------------------------------------------------- differential attention
+ *
+ * The pages name Differential Attention as part of their largest model and
+ * note that its serving implementation runs four plain attention passes
+ * ([Notes] "局限性 / 可改进方向"), but do not define it.  The definition used
+ * here is the published one (Differential Transformer, Ye et al. 2024,
+ * section 2.1), read for decoding over the shared cache:
+ *   each query head row q [D] and each cached key row k [D] are two halves
+ *   of width d = D/2, (q1 | q2) and (k1 | k2); value rows v keep all D;
+ *   a1 = softmax_j(scale · q1·k1_j),  a2 = softmax_j(scale · q2·k2_j),
+ *   o = Σ_j a1_j v_j − λ Σ_j a2_j v_j                      (width D),
+ *   out = (1 − λ_init) · o / sqrt(mean_c o_c² + eps) · γ   (per head).
+ * λ and λ_init are inputs (the paper derives λ from learned vectors; that
+ * reparametrisation lives with the weights).  γ is one D-wide gain shared by
+ * all heads, or all ones when NULL.  A ragged batch (lens non-NULL) uses the
+ * first lens[b] positions; a sequence with none gives a zero output. */
+
+/* One attention map: softmax over positions j < n of scale · Σ_{c0<=c<c1}
+ * q[c]·k_j[c], applied to the full D-wide value rows. */
+static void diff_map(const void *q, int dt_q, int64_t q_off, const void *K, const void *V, int dt_kv,
+                     int64_t kv_off, int64_t D, int64_t c0, int64_t c1, int64_t n, double scale, double *s,
+                     double *o) {
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+        double dot = 0.0;
+        for (int64_t c = c0; c < c1; ++c)
+            dot += widen(q, dt_q, q_off + c) * widen(K, dt_kv, kv_off + j * D + c);
+        s[j] = dot * scale;
+        if (s[j] > m) m = s[j];
+    }
+    double den = 0.0;
+    for (int64_t c = 0; c < D; ++c) o[c] = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        double w = exp(s[j] - m);
+        den += w;
+        for (int64_t c = 0; c < D; ++c) o[c] += w * widen(V, dt_kv, kv_off + j * D + c);
+    }
+    for (int64_t c = 0; c < D; ++c) o[c] /= den;
+}
+
+/* out[B, Hq, D] from q [B, Hq, D], K, V [B, Hkv, L, D] (GQA: head h reads KV
+ * head h / (Hq / Hkv)), lens [B] or NULL, gamma [D] or NULL. */
+int oracle_diffattn(const void *q, int dt_q, const void *K, const void *V, int dt_kv, const int32_t *lens,
+                    const void *gamma, int dt_g, double *out, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                    int64_t L, double scale, double lambda, double lambda_init, double eps) {
+    if (!q || !K || !V || !out || !xattn_args_ok(B, Hq, Hkv, D, L) || D % 2 != 0 || !(eps >= 0.0)) return -1;
+    if (lens)
+        for (int64_t b = 0; b < B; ++b)
+            if (lens[b] < 0 || lens[b] > L) return -1;
+    const int64_t G = Hq / Hkv, d = D / 2;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)L * sizeof(double));
+        double *o1 = (double *)malloc((size_t)D * sizeof(double));
+        double *o2 = (double *)malloc((size_t)D * sizeof(double));
+        int ok = s && o1 && o2;
+        if (!ok) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * Hq; ++bh) {
+            if (!ok) continue;
+            int64_t b = bh / Hq, h = bh % Hq, g = h / G;
+            int64_t n = lens ? lens[b] : L, kv = (b * Hkv + g) * L * D;
+            double *y = out + bh * D;
+            if (n == 0) {
+                for (int64_t c = 0; c < D; ++c) y[c] = 0.0;
+                continue;
+            }
+            diff_map(q, dt_q, bh * D, K, V, dt_kv, kv, D, 0, d, n, scale, s, o1);
+            diff_map(q, dt_q, bh * D, K, V, dt_kv, kv, D, d, D, n, scale, s, o2);
+            double ss = 0.0;
+            for (int64_t c = 0; c < D; ++c) {
+                y[c] = o1[c] - lambda * o2[c];
+                ss += y[c] * y[c];
+            }
+            const double r = (1.0 - lambda_init) / sqrt(ss / (double)D + eps);
+            for (int64_t c = 0; c < D; ++c) y[c] *= r * (gamma ? widen(gamma, dt_g, c) : 1.0);
+        }
+        free(s);
+        free(o1);
+        free(o2);
+    }
+    return fail ? -2 : 0;
+}
+
 /* --------------------------------------------------------------- threads */
 
 int oracle_max_threads(void) {

@@ -53,6 +53,19 @@ MUTANTS = [
      "rmsnorm_row(h + r * d_model, norm2[li], dt_w, d_model, eps, x + r * d_model);",
      "rmsnorm_row(h + r * d_model, norm1[li], dt_w, d_model, eps, x + r * d_model);"),
     ("ex_attention_ignores_lengths", "test_oracle_ex.py", "int64_t Lb = lens ? lens[b] : L;", "int64_t Lb = L;"),
+    ("diffattn_lambda_sign", "test_oracle_diffattn.py", "y[c] = o1[c] - lambda * o2[c];",
+     "y[c] = o1[c] + lambda * o2[c];"),
+    ("diffattn_second_map_on_first_half", "test_oracle_diffattn.py",
+     "diff_map(q, dt_q, bh * D, K, V, dt_kv, kv, D, d, D, n, scale, s, o2);",
+     "diff_map(q, dt_q, bh * D, K, V, dt_kv, kv, D, 0, d, n, scale, s, o2);"),
+    ("diffattn_keys_half_swapped", "test_oracle_diffattn.py",
+     "dot += widen(q, dt_q, q_off + c) * widen(K, dt_kv, kv_off + j * D + c);",
+     "dot += widen(q, dt_q, q_off + c) * widen(K, dt_kv, kv_off + j * D + (c + D / 2) % D);"),
+    ("diffattn_norm_sum_not_mean", "test_oracle_diffattn.py", "sqrt(ss / (double)D + eps)", "sqrt(ss + eps)"),
+    ("diffattn_lambda_init_dropped", "test_oracle_diffattn.py", "const double r = (1.0 - lambda_init) /",
+     "const double r = 1.0 /"),
+    ("diffattn_reads_past_length", "test_oracle_diffattn.py", "int64_t n = lens ? lens[b] : L, kv",
+     "int64_t n = L, kv"),
 ]
 
 

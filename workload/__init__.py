@@ -223,3 +223,28 @@ def crossdecoder_ex_inputs(B: int, d_model: int, d_inner: int, d_ff: int, Hq: in
                                   dtype=dtype)
         layers.append(ly)
     return CrossDecoderExInputs(h=base.h, M=base.M, K=base.K, V=base.V, lens=lens_t, layers=layers)
+
+
+# ------------------------------------------------ differential attention (bf16)
+
+# The same cache and query shapes as the plain decode; each 128-wide query and
+# key row is two 64-wide halves, one per attention map.  lambda starts at
+# lambda_init in the published definition, and lambda_init tends to 0.8 in deep
+# layers; the per-head normalisation gain is 1 + N(0, 0.1^2).
+DIFFATTN_DECODE = dict(B=16, Hq=24, Hkv=8, D=128, L=34816, lam=0.8, lam_init=0.8, eps=1e-5)  # bf16
+
+
+@dataclass
+class DiffAttnInputs:
+    q: torch.Tensor      # [B, Hq, D], rows (q1 | q2)
+    K: torch.Tensor      # [B, Hkv, L, D], rows (k1 | k2)
+    V: torch.Tensor      # [B, Hkv, L, D]
+    gamma: torch.Tensor  # [D]
+
+
+def diffattn_inputs(B: int, Hq: int, Hkv: int, D: int, L: int, *, seed: int = 0, device="cpu",
+                    dtype=torch.bfloat16) -> DiffAttnInputs:
+    """q, K, V ~ N(0,1) as for the plain decode, plus the gain 1 + N(0, 0.1^2)."""
+    x = xattn_inputs(B, Hq, Hkv, D, L, seed=seed, device=device, dtype=dtype)
+    gsd = normal((D,), std=NORM_GAIN_STD, seed=_seed(seed, 70), device=device, dtype=torch.float32)
+    return DiffAttnInputs(q=x.q, K=x.K, V=x.V, gamma=(1.0 + gsd).to(dtype))
