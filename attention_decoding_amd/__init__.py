@@ -32,9 +32,11 @@ SB_LAYER_XATTN, SB_LAYER_GMU = 0, 1
 EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", "xattn_workspace_bytes",
            "xattn_decode", "crossdecoder_workspace_bytes", "crossdecoder_step", "sb_timing_enable",
            "sb_timing_collect", "sb_probe_stream_read", "sb_probe_mfma", "sb_probe_mfma_flops",
-           "xattn_decode_varlen", "crossdecoder_ex_workspace_bytes", "crossdecoder_step_ex")
+           "xattn_decode_varlen", "crossdecoder_ex_workspace_bytes", "crossdecoder_step_ex",
+           "diffattn_workspace_bytes", "diffattn_decode")
 SB_TIME_XATTN_SPLIT, SB_TIME_XATTN_MERGE, SB_TIME_SKINNY, SB_TIME_GEMM, SB_TIME_GMU_F32, SB_TIME_PROBE = \
     1, 2, 4, 8, 16, 32
+SB_TIME_DIFF_SPLIT, SB_TIME_DIFF_MERGE = 64, 128
 
 
 class SbLayer(ctypes.Structure):
@@ -80,6 +82,11 @@ def _load() -> ctypes.CDLL:
     lib.crossdecoder_step_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(SbLayerEx), i32, i64, i64, i64, i64, i64,
                                          i64, i64, i64, ctypes.c_float, ctypes.c_float, vp, sz, vp]
     lib.crossdecoder_step_ex.restype = ctypes.c_int
+    lib.diffattn_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.diffattn_workspace_bytes.restype = sz
+    lib.diffattn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, ctypes.c_float,
+                                    ctypes.c_float, ctypes.c_float, vp, sz, vp]
+    lib.diffattn_decode.restype = ctypes.c_int
     lib.sb_timing_enable.argtypes = [ctypes.c_uint32]
     lib.sb_timing_enable.restype = ctypes.c_int
     lib.sb_timing_collect.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -259,6 +266,43 @@ def xattn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, ou
     return out
 
 
+def diffattn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, lam: float, lam_init: float,
+                    gamma: torch.Tensor | None = None, lens: torch.Tensor | None = None, eps: float = 1e-5,
+                    out: torch.Tensor | None = None, scale: float | None = None) -> torch.Tensor:
+    """Differential attention decode: each D-wide row of q [B, Hq, D] and of
+    kcache [B, Hkv, L, D] is two halves, one per softmax map; out [B, Hq, D]
+    = (1 - lam_init) * RMSNorm(map1 @ V - lam * map2 @ V) * gamma per head.
+    scale defaults to 1/sqrt(D/2); gamma ([D] bf16) to all ones; lens as in
+    xattn_decode.  bf16 in and out."""
+    dev = _check_device(q, "q")
+    bf = torch.bfloat16
+    if q.dim() != 3 or kcache.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and kcache [B, Hkv, L, D]")
+    B, Hq, D = q.shape
+    B2, Hkv, L, D2 = kcache.shape
+    if B2 != B or D2 != D or vcache.shape != kcache.shape:
+        raise ValueError("diffattn_decode shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(kcache.shape),
+                                                                          tuple(vcache.shape)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D // 2)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=bf, device=dev)
+    elif out.shape != (B, Hq, D):
+        raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), (B, Hq, D)))
+    if lens is not None and lens.shape != (B,):
+        raise ValueError("lens must have shape [B]")
+    if gamma is not None and gamma.shape != (D,):
+        raise ValueError("gamma must have shape [D]")
+    ws = _workspace(dev, lib.diffattn_workspace_bytes(B, Hq, Hkv, D, L))
+    lp = None if lens is None else _dev_ptr(lens, "lens", torch.int32, dev)
+    gp = None if gamma is None else _dev_ptr(gamma, "gamma", bf, dev)
+    _check("diffattn_decode", lib.diffattn_decode(
+        _dev_ptr(q, "q", bf, dev), _dev_ptr(kcache, "kcache", bf, dev), _dev_ptr(vcache, "vcache", bf, dev), lp, gp,
+        _dev_ptr(out, "out", bf, dev), B, Hq, Hkv, D, L, float(scale), float(lam), float(lam_init), float(eps),
+        ws.data_ptr(), ws.numel(), _stream(dev)))
+    return out
+
+
 def _layer_array(layers: Sequence, dev: torch.device, d_model: int, d_inner: int):
     arr = (SbLayer * max(len(layers), 1))()
     bf = torch.bfloat16
@@ -391,7 +435,7 @@ def crossdecoder_step_ex(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor,
     return CrossDecoderStepEx(h, M, kcache, vcache, layers, lens, eps, scale)()
 
 
-__all__ = ["gmu_forward", "xattn_decode", "crossdecoder_step", "CrossDecoderStep", "crossdecoder_step_ex",
+__all__ = ["gmu_forward", "xattn_decode", "diffattn_decode", "crossdecoder_step", "CrossDecoderStep", "crossdecoder_step_ex",
            "CrossDecoderStepEx", "SambayError", "version", "lib",
            "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect", "probe_stream_read_gbps", "probe_mfma_tflops",
            "probe_stream_read_raw"]

@@ -285,6 +285,62 @@ extern "C" sb_status xattn_decode_varlen(const void *q, const void *kcache, cons
                              workspace_bytes, stream);
 }
 
+extern "C" size_t diffattn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || D != kHeadDim || Hq % Hkv != 0) return 0;
+    return round_up(xattn_workspace_need(B, 2 * Hq, Hkv, L));
+}
+
+extern "C" sb_status diffattn_decode(const void *q, const void *kcache, const void *vcache, const int32_t *lens,
+                                     const void *gamma, void *out, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                     int64_t L, float scale, float lambda, float lambda_init, float eps,
+                                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "diffattn_decode";
+    if (B < 0 || Hq < 0 || Hkv < 0 || D < 0 || L < 0) return fail(SB_EINVAL, "negative size");
+    if (B == 0) return ok();
+    sb_status st = check_xattn_shape(B, Hq, Hkv, D, L);
+    if (st != SB_OK) return st;
+    if (2 * (Hq / Hkv) > kMaxGroup)
+        return fail(SB_EUNSUPPORTED, "group size Hq/Hkv = %lld exceeds %d for two maps", (long long)(Hq / Hkv),
+                    kMaxGroup / 2);
+    if (B * 2 * Hq > ((int64_t)1 << 31) - 1) return fail(SB_EUNSUPPORTED, "B*Hq too large");
+    if (!q || !kcache || !vcache || !out) return fail(SB_EINVAL, "null tensor pointer");
+    if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out) || !aligned16(gamma))
+        return fail(SB_EINVAL, "tensor base pointers must be 16-byte aligned");
+    if (((uintptr_t)lens & 3u) != 0) return fail(SB_EINVAL, "lens must be 4-byte aligned");
+    const float inf = __builtin_inff();
+    if (!(scale == scale) || scale == inf || scale == -inf) return fail(SB_EINVAL, "scale must be finite");
+    if (!(lambda == lambda) || lambda == inf || lambda == -inf || !(lambda_init == lambda_init) ||
+        lambda_init == inf || lambda_init == -inf)
+        return fail(SB_EINVAL, "lambda and lambda_init must be finite");
+    if (!(eps >= 0.f) || eps == inf) return fail(SB_EINVAL, "eps must be finite and >= 0");
+    const size_t qbytes = (size_t)B * Hq * D * 2, kvbytes = (size_t)B * Hkv * L * D * 2;
+    const Range ro = rng("out", out, qbytes);
+    const Range ins[] = {rng("q", q, qbytes), rng("kcache", kcache, kvbytes), rng("vcache", vcache, kvbytes),
+                         rng("lens", lens, lens ? (size_t)B * sizeof(int32_t) : 0),
+                         rng("gamma", gamma, gamma ? (size_t)D * 2 : 0)};
+    for (const Range &r : ins)
+        if (overlaps(ro, r)) return fail(SB_EINVAL, "out overlaps %s", r.name);
+    const size_t need = diffattn_workspace_bytes(B, Hq, Hkv, D, L);
+    if (!workspace || workspace_bytes < need)
+        return fail(SB_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(SB_EINVAL, "workspace must be 16-byte aligned");
+    const Range rw = rng("workspace", workspace, need);
+    if (overlaps(rw, ro)) return fail(SB_EINVAL, "workspace overlaps out");
+    for (const Range &r : ins)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+
+    const XattnPlan plan = xattn_plan(B, Hkv, L, lens != nullptr);
+    if (log_enabled())
+        fprintf(stderr, "[sambay] %s B=%lld Hq=%lld Hkv=%lld L=%lld%s -> %d chunks of %d positions, %lld score "
+                "columns per group\n", fn, (long long)B, (long long)Hq, (long long)Hkv, (long long)L,
+                lens ? " (ragged)" : "", plan.splits, plan.chunk, (long long)(2 * (Hq / Hkv)));
+    hipError_t e = launch_diffattn((const bf16_t *)q, (const bf16_t *)kcache, (const bf16_t *)vcache, lens,
+                                   (const bf16_t *)gamma, (bf16_t *)out, (int)B, (int)Hq, (int)Hkv, (int)L, scale,
+                                   lambda, lambda_init, eps, plan, workspace, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
 namespace {
 
 // Workspace layout of one cross-decoder step (all reused layer to layer).

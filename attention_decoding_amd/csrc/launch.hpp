@@ -25,7 +25,7 @@ class TimingScope {
     bool active_ = false;
 };
 constexpr uint32_t kTimeXattnSplit = 1, kTimeXattnMerge = 2, kTimeSkinny = 4, kTimeGemm = 8, kTimeGmuF32 = 16,
-                   kTimeProbe = 32;
+                   kTimeProbe = 32, kTimeDiffSplit = 64, kTimeDiffMerge = 128;
 
 // ------------------------------------------------------- cross-attention
 constexpr int kHeadDim = 128;     // supported head dimension
@@ -49,6 +49,13 @@ size_t xattn_workspace_need(int64_t B, int64_t Hq, int64_t Hkv, int64_t L);
 hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t *V, const int32_t *lens,
                         bf16_t *out, bf16_t *out_lo, int B, int Hq, int Hkv, int L, float scale, const XattnPlan &plan,
                         void *partials, hipStream_t stream);
+
+// Differential attention decode: q, K, V bf16 with 128-wide rows split into
+// two 64-wide halves (one per map); partials hold 2·Hq score columns per
+// sequence (xattn_partial_bytes(B, 2·Hq, splits)); gamma [128] bf16 or null.
+hipError_t launch_diffattn(const bf16_t *q, const bf16_t *K, const bf16_t *V, const int32_t *lens, const bf16_t *gamma,
+                           bf16_t *out, int B, int Hq, int Hkv, int L, float scale, float lam, float lam_init,
+                           float eps, const XattnPlan &plan, void *partials, hipStream_t stream);
 
 // ------------------------------------------------ skinny (decode) products
 // out[t, n] = epi( Σ_k X[t, k] · W[n, k] ) for t < T <= 64 tokens.

@@ -31,6 +31,19 @@
 //    case), so every workgroup streams a full chunk except each sequence's
 //    last; the merge reads only those chunks and a sequence with no position
 //    gets a zero output.
+//
+// Differential attention (the same kernel, DIFF = true): each query and key
+// row is two 64-wide halves, one per attention map, and both maps weight the
+// full 128-wide value rows (Differential Transformer, section 2.1; the pages
+// name the method in the Paper-Notes page's section 局限性 / 可改进方向, where
+// its serving implementation makes four plain attention passes).  The score
+// tile's 16 columns hold the group's G heads twice: column i < G is map 1 of
+// head i (query half 2 zeroed), column G + i is map 2 (half 1 zeroed), so one
+// 128-deep contraction yields both maps' logits and each column keeps its own
+// online softmax and P·V accumulator.  The cache is still read once, with
+// the same MFMA count as the plain decode (2G <= 16 columns either way).  The
+// merge combines each head's two columns as o1 − λ·o2 and applies the
+// per-head RMS normalisation, its gain and the (1 − λ_init) factor.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -45,7 +58,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kVStride = kHeadDim + 8;  // bf16 per staged V row: 272-byte rows spread the transposed reads over banks
 
-template <bool QF32>
+template <bool QF32, bool DIFF>
 // Three waves per SIMD (12 per CU) keep enough block loads in flight; a
 // register-level prefetch of the next block measured slower (it forces one
 // wave per SIMD or spills).
@@ -105,6 +118,7 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
         s = item[1] % nch;
     }
     const int G = Hq / Hkv;
+    const int NC = DIFF ? 2 * G : G;  // score columns of this group
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
     // Ragged batch: sequence b uses its first lens[b] positions (clamped to
     // [0, L]); chunks past that end are empty and write an empty partial.
@@ -115,19 +129,22 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
     const bf16_t *Kb = K + kv0;
     const bf16_t *Vb = V + kv0;
 
-    // B operand of the score product: head `col` of this group; MFMA k-step t
+    // B operand of the score product: head `col` of this group (differential:
+    // map col / G of head col % G, the other map's half zeroed); MFMA k-step t
     // covers dims 32·t .. 32·t+31, lane group grp holding dims 32·t + 8·grp + e.
     u32x4 qhi[4], qlo[4];
     {
-        const int h = g * G + col;
+        const int map = DIFF && col >= G ? 1 : 0;
+        const int h = g * G + col - map * G;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             float f[8];
+            const bool live = col < NC && (!DIFF || (t >> 1) == map);
             const size_t off = ((size_t)b * Hq + h) * kHeadDim + 32 * t + 8 * grp;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float x = 0.f;
-                if (col < G) x = QF32 ? ((const float *)qv)[off + e] : bf16_to_f32(((const bf16_t *)qv)[off + e]);
+                if (live) x = QF32 ? ((const float *)qv)[off + e] : bf16_to_f32(((const bf16_t *)qv)[off + e]);
                 f[e] = x * qscale;
             }
             uint32_t hi[4], lo[4];
@@ -258,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
 #pragma unroll
         for (int r = 0; r < 4; ++r) ow[(wave * kMaxGroup + col) * kHeadDim + 16 * db + 4 * grp + r] = acc[db][r];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < NC * kHeadDim; idx += kThreads) {
         const int hh = idx / kHeadDim, d = idx % kHeadDim;
         float M = -INFINITY;
 #pragma unroll
@@ -272,25 +289,16 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
                 o += e * ow[(w * kMaxGroup + hh) * kHeadDim + d];
             }
         }
-        const size_t pi = ((size_t)b * Hq + (size_t)g * G + hh) * S + s;
+        const size_t pi = ((size_t)b * (DIFF ? 2 * Hq : Hq) + (size_t)g * NC + hh) * S + s;
         part_o[pi * kHeadDim + d] = o;
         if (d == 0) part_ml[pi] = make_float2(M, lsum);
     }
 }
 
-// One workgroup per (sequence, query head): log-sum-exp merge of the chunks in
-// order, then normalisation and the bf16 store.
-__global__ __launch_bounds__(kHeadDim) void xattn_merge_kernel(const float2 *__restrict__ part_ml,
-                                                               const float *__restrict__ part_o,
-                                                               bf16_t *__restrict__ out, bf16_t *__restrict__ out_lo,
-                                                               int S, int Hq, int L, const int32_t *__restrict__ lens,
-                                                               int chunk) {
-    const size_t bh = blockIdx.x;
-    const int d = threadIdx.x;
-    // Ragged batches: only the chunks that hold positions were written.
-    const int Sb = lens ? (min(max(lens[bh / Hq], 0), L) + chunk - 1) / chunk : S;
-    const float2 *ml = part_ml + bh * S;
-    const float *po = part_o + bh * S * kHeadDim;
+// Log-sum-exp merge of one score column's first Sb chunk partials, in order,
+// and the softmax normalisation: dimension d of that column's output.
+__device__ __forceinline__ float merge_column(const float2 *__restrict__ ml, const float *__restrict__ po, int Sb,
+                                              int d) {
     float M = -INFINITY;
     for (int s = 0; s < Sb; ++s) M = fmaxf(M, ml[s].x);
     float lsum = 0.f, o = 0.f;
@@ -301,10 +309,52 @@ __global__ __launch_bounds__(kHeadDim) void xattn_merge_kernel(const float2 *__r
             o += e * po[(size_t)s * kHeadDim + d];
         }
     }
-    const float v = lsum > 0.f ? o / lsum : 0.f;
+    return lsum > 0.f ? o / lsum : 0.f;
+}
+
+// One workgroup per (sequence, query head): the merge, then the bf16 store.
+__global__ __launch_bounds__(kHeadDim) void xattn_merge_kernel(const float2 *__restrict__ part_ml,
+                                                               const float *__restrict__ part_o,
+                                                               bf16_t *__restrict__ out, bf16_t *__restrict__ out_lo,
+                                                               int S, int Hq, int L, const int32_t *__restrict__ lens,
+                                                               int chunk) {
+    const size_t bh = blockIdx.x;
+    const int d = threadIdx.x;
+    // Ragged batches: only the chunks that hold positions were written.
+    const int Sb = lens ? (min(max(lens[bh / Hq], 0), L) + chunk - 1) / chunk : S;
+    const float v = merge_column(part_ml + bh * S, part_o + bh * S * kHeadDim, Sb, d);
     const bf16_t hi = f32_to_bf16(v);
     out[bh * kHeadDim + d] = hi;
     if (out_lo) out_lo[bh * kHeadDim + d] = f32_to_bf16(v - bf16_to_f32(hi));
+}
+
+// Differential attention, one workgroup per (sequence, query head): merge the
+// head's two map columns, y = o1 − λ·o2, then out = (1 − λ_init)·y / RMS(y)·γ
+// over the head's 128 dimensions (RMS with eps; γ all ones when null).  The
+// sum of squares is reduced in a fixed order (wave tree, then wave 0 + wave 1).
+__global__ __launch_bounds__(kHeadDim) void diffattn_merge_kernel(const float2 *__restrict__ part_ml,
+                                                                  const float *__restrict__ part_o,
+                                                                  const bf16_t *__restrict__ gamma,
+                                                                  bf16_t *__restrict__ out, int S, int Hq, int G,
+                                                                  int L, const int32_t *__restrict__ lens, int chunk,
+                                                                  float lam, float lam_init, float eps) {
+    __shared__ float red[kHeadDim / 64];
+    const size_t bh = blockIdx.x;
+    const int d = threadIdx.x;
+    const size_t b = bh / Hq;
+    const int h = (int)(bh % Hq), g = h / G;
+    const size_t c1 = b * 2 * Hq + (size_t)g * 2 * G + (h - g * G), c2 = c1 + G;  // map 1 and map 2 columns
+    const int Sb = lens ? (min(max(lens[b], 0), L) + chunk - 1) / chunk : S;
+    const float y = merge_column(part_ml + c1 * S, part_o + c1 * S * kHeadDim, Sb, d) -
+                    lam * merge_column(part_ml + c2 * S, part_o + c2 * S * kHeadDim, Sb, d);
+    float ss = y * y;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    if ((d & 63) == 0) red[d >> 6] = ss;
+    __syncthreads();
+    const float r = (1.f - lam_init) / sqrtf((red[0] + red[1]) / (float)kHeadDim + eps);
+    const float gm = gamma ? bf16_to_f32(gamma[d]) : 1.f;
+    out[bh * kHeadDim + d] = f32_to_bf16(Sb > 0 ? y * r * gm : 0.f);
 }
 
 int env_splits() {
@@ -366,17 +416,38 @@ hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t
     {
     TimingScope ts(kTimeXattnSplit, stream);
     if (q_f32)
-        hipLaunchKernelGGL(xattn_split_kernel<true>, grid, dim3(kThreads), 0, stream, q, K, V, ml, po, B, Hq, Hkv, L,
-                           lens, plan.chunk, plan.splits, qscale);
+        hipLaunchKernelGGL((xattn_split_kernel<true, false>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po, B, Hq,
+                           Hkv, L, lens, plan.chunk, plan.splits, qscale);
     else
-        hipLaunchKernelGGL(xattn_split_kernel<false>, grid, dim3(kThreads), 0, stream, q, K, V, ml, po, B, Hq, Hkv, L,
-                           lens, plan.chunk, plan.splits, qscale);
+        hipLaunchKernelGGL((xattn_split_kernel<false, false>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po, B, Hq,
+                           Hkv, L, lens, plan.chunk, plan.splits, qscale);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     TimingScope ts(kTimeXattnMerge, stream);
     hipLaunchKernelGGL(xattn_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kHeadDim), 0, stream, ml, po, out, out_lo,
                        plan.splits, Hq, L, lens, plan.chunk);
+    return hipGetLastError();
+}
+
+hipError_t launch_diffattn(const bf16_t *q, const bf16_t *K, const bf16_t *V, const int32_t *lens, const bf16_t *gamma,
+                           bf16_t *out, int B, int Hq, int Hkv, int L, float scale, float lam, float lam_init,
+                           float eps, const XattnPlan &plan, void *partials, hipStream_t stream) {
+    const size_t n = (size_t)B * 2 * Hq * plan.splits;  // two score columns per head
+    float2 *ml = reinterpret_cast<float2 *>(partials);
+    float *po = reinterpret_cast<float *>(reinterpret_cast<char *>(partials) + n * sizeof(float2));
+    if (lens && (size_t)B * Hkv * plan.splits > 0x7fffffffu) return hipErrorInvalidConfiguration;
+    const dim3 grid = lens ? dim3((unsigned)((size_t)B * Hkv * plan.splits)) : dim3(plan.splits, Hkv, B);
+    {
+        TimingScope ts(kTimeDiffSplit, stream);
+        hipLaunchKernelGGL((xattn_split_kernel<false, true>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po, B, Hq,
+                           Hkv, L, lens, plan.chunk, plan.splits, scale * kLog2e);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    TimingScope ts(kTimeDiffMerge, stream);
+    hipLaunchKernelGGL(diffattn_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kHeadDim), 0, stream, ml, po, gamma, out,
+                       plan.splits, Hq, Hq / Hkv, L, lens, plan.chunk, lam, lam_init, eps);
     return hipGetLastError();
 }
 

@@ -170,6 +170,24 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> 
     res["xattn_decode_B16_L34816"] = {"us_per_call": round(1e3 * ms, 1), "gbps": round(nbytes / ms / 1e6, 1),
                                       "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
                                       "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
+    # Differential attention on the same cache: both maps in one pass, against
+    # two plain decode passes over it (the cache bytes that an implementation
+    # running one attention pass per map reads).
+    c = workload.DIFFATTN_DECODE
+    gain = workload.diffattn_gain(c["D"], seed=4, device=dev)
+    ms_d = time_calls(lambda i: sb.diffattn_decode(x.q, x.K, x.V, c["lam"], c["lam_init"], gamma=gain,
+                                                   eps=c["eps"], out=out), 20)
+
+    def two_passes(i):
+        sb.xattn_decode(x.q, x.K, x.V, out=out)
+        sb.xattn_decode(x.q, x.K, x.V, out=out)
+
+    ms_2 = time_calls(two_passes, 10)
+    res["diffattn_decode_B16_L34816"] = {
+        "us_per_call": round(1e3 * ms_d, 1), "gbps": round(nbytes / ms_d / 1e6, 1),
+        "frac_of_hbm_peak": round(nbytes / ms_d / 1e6 / HBM_PEAK_GBS, 4),
+        "frac_of_stream_read": round(nbytes / ms_d / 1e6 / read_gbps, 4),
+        "two_plain_passes_us": round(1e3 * ms_2, 1), "speedup_vs_two_passes": round(ms_2 / ms_d, 3)}
     del x
     # Ragged batch: 32 sequences, room for 34816 positions, lengths uniform in [2048, 34816].
     c = workload.XATTN_VARLEN

@@ -150,6 +150,32 @@ sb_status xattn_decode_varlen(const void *q, const void *kcache, const void *vca
                               int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L, float scale,
                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------ differential attention --
+ * Decode-time Differential Attention over the shared cache.  The pages name
+ * the method for their largest model and note that its serving
+ * implementation makes four plain attention passes ([Notes] section
+ * 局限性 / 可改进方向) but do not define it; this is the published definition
+ * (Differential Transformer, section 2.1) read for one query per sequence:
+ * every D-wide query row q [B, Hq, D] and cached key row [B, Hkv, L, D] is two
+ * halves of width D/2, (q1 | q2) and (k1 | k2); value rows keep all D; for
+ * query head h (KV head h / (Hq / Hkv)):
+ *   a1 = softmax_j(scale · q1·k1_j),  a2 = softmax_j(scale · q2·k2_j)
+ *   o  = Σ_j a1_j v_j − lambda · Σ_j a2_j v_j
+ *   out[b, h] = (1 − lambda_init) · o / sqrt(mean(o²) + eps) · gamma
+ * gamma [D] bf16 (one gain for every head) or NULL for all ones.  lens as in
+ * xattn_decode_varlen (NULL: all L positions); a sequence with no position
+ * gets a zero output.  Callers usually pass scale = 1/sqrt(D/2).  Both maps
+ * are computed in one pass over the cache (it is read once).  All tensors
+ * bf16; out [B, Hq, D] must not overlap any input.
+ * Errors: as xattn_decode_varlen (lens may be NULL here), plus SB_EINVAL for
+ * a non-finite lambda or lambda_init, eps < 0 or non-finite, or a misaligned
+ * gamma, and SB_EUNSUPPORTED for 2·(Hq/Hkv) > 16. */
+size_t diffattn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L);
+sb_status diffattn_decode(const void *q, const void *kcache, const void *vcache, const int32_t *lens,
+                          const void *gamma, void *out, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L,
+                          float scale, float lambda, float lambda_init, float eps, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------- complete cross-decoder layer --
  * The pages define the GMU and the shared-cache cross-attention but not the
  * rest of a layer; this step takes the plain pre-norm Transformer reading.
@@ -202,7 +228,9 @@ typedef enum {
     SB_TIME_SKINNY = 4,        /* decode weight-streaming products (GMU, Wq, Wo) */
     SB_TIME_GEMM = 8,          /* prefill MFMA GEMM */
     SB_TIME_GMU_F32 = 16,      /* fp32 GMU kernels */
-    SB_TIME_PROBE = 32         /* the two probes below */
+    SB_TIME_PROBE = 32,        /* the two probes below */
+    SB_TIME_DIFF_SPLIT = 64,   /* differential-attention partial kernel */
+    SB_TIME_DIFF_MERGE = 128   /* differential-attention merge + normalisation */
 } sb_timing_kind;
 
 sb_status sb_timing_enable(uint32_t mask);

@@ -216,3 +216,35 @@ def test_crossdecoder_ex_validation(sb):
     assert _step_ex(sb, [mlp], wsb=need - 1) == sb.SB_EWORKSPACE
     assert _step_ex(sb, [mlp], B=0) == sb.SB_OK
     assert sb.lib.crossdecoder_ex_workspace_bytes(2, 3072, 6144, 8192, 24, 8, 128, 0) == 0
+
+
+def _diff(sb, B=2, Hq=24, Hkv=8, D=128, L=300, lens=_addr(6) * 8, gamma=_addr(7) * 8, out=_addr(3), lam=0.8,
+          lam_init=0.8, eps=1e-5, wsb=1 << 30):
+    return sb.lib.diffattn_decode(_addr(0), _addr(1) * 16, _addr(2) * 64, lens, gamma, out, B, Hq, Hkv, D, L, 0.125,
+                                  lam, lam_init, eps, _addr(4) * 512, wsb, None)
+
+
+def test_diffattn_validation(sb):
+    """Every call here fails validation (or is the B == 0 no-op), so the fake
+    addresses are never used."""
+    assert _diff(sb, Hkv=2) == sb.SB_EUNSUPPORTED                  # 2·G = 24 score columns > 16
+    assert "two maps" in sb.lib.sb_last_error().decode()
+    assert _diff(sb, D=64) == sb.SB_EUNSUPPORTED
+    assert _diff(sb, lam=float("nan")) == sb.SB_EINVAL
+    assert _diff(sb, lam_init=float("inf")) == sb.SB_EINVAL
+    assert _diff(sb, eps=-1.0) == sb.SB_EINVAL
+    assert _diff(sb, gamma=_addr(7) * 8 + 2) == sb.SB_EINVAL       # misaligned gamma
+    assert _diff(sb, lens=_addr(6) * 8 + 2) == sb.SB_EINVAL        # misaligned lens
+    assert _diff(sb, out=_addr(7) * 8) == sb.SB_EINVAL             # out overlaps gamma
+    assert "gamma" in sb.lib.sb_last_error().decode()
+    assert _diff(sb, wsb=16) == sb.SB_EWORKSPACE
+    assert _diff(sb, L=0) == sb.SB_EINVAL
+    assert _diff(sb, B=0) == sb.SB_OK
+
+
+def test_diffattn_workspace_sizes(sb):
+    lib = sb.lib
+    # Two score columns per head: the partials of a plain decode with twice the heads.
+    assert lib.diffattn_workspace_bytes(16, 24, 8, 128, 34816) == lib.xattn_workspace_bytes(16, 48, 8, 128, 34816)
+    assert lib.diffattn_workspace_bytes(16, 24, 8, 64, 34816) == 0
+    assert lib.diffattn_workspace_bytes(16, 24, 7, 128, 34816) == 0

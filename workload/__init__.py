@@ -242,9 +242,14 @@ class DiffAttnInputs:
     gamma: torch.Tensor  # [D]
 
 
+def diffattn_gain(D: int, *, seed: int = 0, device="cpu", dtype=torch.bfloat16) -> torch.Tensor:
+    """The per-head normalisation gain, 1 + N(0, 0.1^2)."""
+    gsd = normal((D,), std=NORM_GAIN_STD, seed=_seed(seed, 70), device=device, dtype=torch.float32)
+    return (1.0 + gsd).to(dtype)
+
+
 def diffattn_inputs(B: int, Hq: int, Hkv: int, D: int, L: int, *, seed: int = 0, device="cpu",
                     dtype=torch.bfloat16) -> DiffAttnInputs:
-    """q, K, V ~ N(0,1) as for the plain decode, plus the gain 1 + N(0, 0.1^2)."""
+    """q, K, V ~ N(0,1) as for the plain decode (same seed, same values), plus the gain."""
     x = xattn_inputs(B, Hq, Hkv, D, L, seed=seed, device=device, dtype=dtype)
-    gsd = normal((D,), std=NORM_GAIN_STD, seed=_seed(seed, 70), device=device, dtype=torch.float32)
-    return DiffAttnInputs(q=x.q, K=x.K, V=x.V, gamma=(1.0 + gsd).to(dtype))
+    return DiffAttnInputs(q=x.q, K=x.K, V=x.V, gamma=diffattn_gain(D, seed=seed, device=device, dtype=dtype))
