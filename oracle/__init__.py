@@ -72,6 +72,9 @@ def _load():
     lib.oracle_diffattn.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i64, i64,
                                     i64, i64, i64, dbl, dbl, dbl, dbl]
     lib.oracle_diffattn.restype = ctypes.c_int
+    lib.oracle_selfattn.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                    i64, i64, i64, i64, i64, i64, dbl]
+    lib.oracle_selfattn.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [dbl]
     lib.oracle_round_bf16.restype = dbl
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -324,6 +327,39 @@ def diffattn(q, K, V, lam: float, lam_init: float, gamma=None, lens=None, eps: f
                              float(lam), float(lam_init), float(eps))
     _check(rc, "diffattn")
     return out
+
+
+def selfattn(q, k_new, v_new, K, V, pos, window: int = 0, scale: float | None = None):
+    """One decode step of a self-decoder attention layer: store each active
+    sequence's new key/value rows (k_new, v_new [B, Hkv, D]) at position
+    pos[b] (window 0: cache [B, Hkv, L, D] with room for L positions) or in
+    ring slot pos[b] % window (cache of window slots), then attend over the
+    visible positions (0 .. pos[b], or the window most recent tokens).
+    pos[b] < 0: inactive (nothing stored, zero output).  Returns (out, K_out,
+    V_out), the updated cache in float64."""
+    lib = _load()
+    qa, dq = _as_input(q)
+    ka, dk = _as_input(K)
+    va, dv = _as_input(V)
+    kn, dn = _as_input(k_new)
+    vn, dn2 = _as_input(v_new)
+    if dk != dv or dn != dn2:
+        raise TypeError("K and V (and k_new and v_new) must share a dtype")
+    B, Hq, Hkv, D, L = _xattn_shapes(qa, ka, va)
+    if kn.shape != (B, Hkv, D) or vn.shape != (B, Hkv, D):
+        raise ValueError("k_new and v_new must be [B, Hkv, D]")
+    pa = np.ascontiguousarray(np.asarray(pos.cpu() if hasattr(pos, "cpu") else pos), dtype=np.int32)
+    if pa.shape != (B,):
+        raise ValueError("pos must have one entry per sequence")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    Ko = np.empty((B, Hkv, L, D), dtype=np.float64)
+    Vo = np.empty((B, Hkv, L, D), dtype=np.float64)
+    rc = lib.oracle_selfattn(_ptr(qa), dq, _ptr(kn), _ptr(vn), dn, _ptr(ka), _ptr(va), dk, _ptr(pa), _ptr(out),
+                             _ptr(Ko), _ptr(Vo), B, Hq, Hkv, D, L, int(window), float(scale))
+    _check(rc, "selfattn")
+    return out, Ko, Vo
 
 
 def rmsnorm(x, g, eps: float = 1e-5):

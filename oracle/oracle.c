@@ -794,6 +794,71 @@ int oracle_diffattn(const void *q, int dt_q, const void *K, const void *V, int d
     return fail ? -2 : 0;
 }
 
+/* ----------------------------------------- self-decoder attention decode
+ *
+ * The producer side of the cache ([Notes] "整体框架": the self-decoder's
+ * final full-attention layer writes the one KV cache that every
+ * cross-attention layer reads; its other attention layers use a sliding
+ * window, 256 positions in the model the pages favour, [Notes] "消融实验").
+ * One decode step of such a layer for a batch: sequence b's new token sits
+ * at position p = pos[b] (0-based; p < 0 marks an inactive sequence, which
+ * writes nothing and gets a zero output).  Its key and value rows (k_new,
+ * v_new [B, Hkv, D]) are stored, then its query attends:
+ *   window == 0: the cache [B, Hkv, L, D] holds positions 0 .. L-1; the new
+ *                row goes to position p (p < L) and positions 0 .. p are
+ *                visible;
+ *   window == W: the cache holds W slots (L == W) used as a ring, token t in
+ *                slot t mod W; the new row goes to slot p mod W and the W
+ *                most recent tokens (all of p + 1 when p < W) are visible.
+ * No positional encoding, so the order of the slots does not matter to the
+ * softmax.  K_out, V_out receive the whole updated cache (fp64). */
+int oracle_selfattn(const void *q, int dt_q, const void *k_new, const void *v_new, int dt_new, const void *K,
+                    const void *V, int dt_kv, const int32_t *pos, double *out, double *K_out, double *V_out,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L, int64_t window, double scale) {
+    if (!q || !k_new || !v_new || !K || !V || !pos || !out || !K_out || !V_out || !xattn_args_ok(B, Hq, Hkv, D, L) ||
+        window < 0 || (window > 0 && L != window))
+        return -1;
+    for (int64_t b = 0; b < B; ++b)
+        if (window == 0 && pos[b] >= L) return -1;
+    const int64_t G = Hq / Hkv, n_cache = B * Hkv * L * D;
+    for (int64_t i = 0; i < n_cache; ++i) {
+        K_out[i] = widen(K, dt_kv, i);
+        V_out[i] = widen(V, dt_kv, i);
+    }
+    for (int64_t b = 0; b < B; ++b) {
+        if (pos[b] < 0) continue;
+        const int64_t slot = window ? pos[b] % window : pos[b];
+        for (int64_t g = 0; g < Hkv; ++g)
+            for (int64_t d = 0; d < D; ++d) {
+                K_out[((b * Hkv + g) * L + slot) * D + d] = widen(k_new, dt_new, (b * Hkv + g) * D + d);
+                V_out[((b * Hkv + g) * L + slot) * D + d] = widen(v_new, dt_new, (b * Hkv + g) * D + d);
+            }
+    }
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)L * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * Hq; ++bh) {
+            if (!s) continue;
+            const int64_t b = bh / Hq, h = bh % Hq, g = h / G, p = pos[b];
+            const int64_t n = p < 0 ? 0 : (window && p + 1 > window ? window : p + 1);
+            if (n == 0) {
+                for (int64_t d = 0; d < D; ++d) out[bh * D + d] = 0.0;
+                continue;
+            }
+            xattn_head(q, dt_q, bh * D, K_out, V_out, OR_F64, (b * Hkv + g) * L * D, out + bh * D, D, n, scale, s,
+                       NULL, 0, 0, 0);
+        }
+        free(s);
+    }
+    return fail ? -2 : 0;
+}
+
 /* --------------------------------------------------------------- threads */
 
 int oracle_max_threads(void) {

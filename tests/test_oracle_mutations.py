@@ -66,6 +66,18 @@ MUTANTS = [
      "const double r = 1.0 /"),
     ("diffattn_reads_past_length", "test_oracle_diffattn.py", "int64_t n = lens ? lens[b] : L, kv",
      "int64_t n = L, kv"),
+    ("selfattn_ring_slot_is_position", "test_oracle_selfattn.py",
+     "const int64_t slot = window ? pos[b] % window : pos[b];",
+     "const int64_t slot = window ? (pos[b] < window ? pos[b] : window - 1) : pos[b];"),
+    ("selfattn_new_token_not_visible", "test_oracle_selfattn.py",
+     "const int64_t n = p < 0 ? 0 : (window && p + 1 > window ? window : p + 1);",
+     "const int64_t n = p < 0 ? 0 : (window && p > window ? window : p);"),
+    ("selfattn_unfilled_ring_slots_visible", "test_oracle_selfattn.py",
+     "const int64_t n = p < 0 ? 0 : (window && p + 1 > window ? window : p + 1);",
+     "const int64_t n = p < 0 ? 0 : (window ? window : p + 1);"),
+    ("selfattn_value_row_not_stored", "test_oracle_selfattn.py",
+     "V_out[((b * Hkv + g) * L + slot) * D + d] = widen(v_new, dt_new, (b * Hkv + g) * D + d);",
+     "V_out[((b * Hkv + g) * L + slot) * D + d] = widen(V, dt_kv, ((b * Hkv + g) * L + slot) * D + d);"),
 ]
 
 
