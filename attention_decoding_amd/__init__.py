@@ -33,7 +33,7 @@ EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", 
            "xattn_decode", "crossdecoder_workspace_bytes", "crossdecoder_step", "sb_timing_enable",
            "sb_timing_collect", "sb_probe_stream_read", "sb_probe_mfma", "sb_probe_mfma_flops",
            "xattn_decode_varlen", "crossdecoder_ex_workspace_bytes", "crossdecoder_step_ex",
-           "diffattn_workspace_bytes", "diffattn_decode")
+           "diffattn_workspace_bytes", "diffattn_decode", "selfattn_workspace_bytes", "selfattn_decode")
 SB_TIME_XATTN_SPLIT, SB_TIME_XATTN_MERGE, SB_TIME_SKINNY, SB_TIME_GEMM, SB_TIME_GMU_F32, SB_TIME_PROBE = \
     1, 2, 4, 8, 16, 32
 SB_TIME_DIFF_SPLIT, SB_TIME_DIFF_MERGE = 64, 128
@@ -87,6 +87,11 @@ def _load() -> ctypes.CDLL:
     lib.diffattn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, ctypes.c_float,
                                     ctypes.c_float, ctypes.c_float, vp, sz, vp]
     lib.diffattn_decode.restype = ctypes.c_int
+    lib.selfattn_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.selfattn_workspace_bytes.restype = sz
+    lib.selfattn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float, vp, sz,
+                                    vp]
+    lib.selfattn_decode.restype = ctypes.c_int
     lib.sb_timing_enable.argtypes = [ctypes.c_uint32]
     lib.sb_timing_enable.restype = ctypes.c_int
     lib.sb_timing_collect.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -303,6 +308,42 @@ def diffattn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
     return out
 
 
+def selfattn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, kcache: torch.Tensor,
+                    vcache: torch.Tensor, pos: torch.Tensor, window: int = 0, out: torch.Tensor | None = None,
+                    scale: float | None = None) -> torch.Tensor:
+    """One self-decoder attention decode step: store k_new, v_new [B, Hkv, D]
+    at position pos[b] of kcache/vcache [B, Hkv, L, D] (window 0) or in ring
+    slot pos[b] % window (a cache of window slots), then attend q [B, Hq, D]
+    over the visible positions.  The cache is updated in place; pos is [B]
+    int32 on the same GPU (pos[b] < 0: inactive)."""
+    dev = _check_device(q, "q")
+    bf = torch.bfloat16
+    if q.dim() != 3 or kcache.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and kcache [B, Hkv, L, D]")
+    B, Hq, D = q.shape
+    B2, Hkv, L, D2 = kcache.shape
+    if B2 != B or D2 != D or vcache.shape != kcache.shape:
+        raise ValueError("selfattn_decode shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(kcache.shape),
+                                                                          tuple(vcache.shape)))
+    if k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D):
+        raise ValueError("k_new and v_new must be [B, Hkv, D]")
+    if pos.shape != (B,):
+        raise ValueError("pos must have shape [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=bf, device=dev)
+    elif out.shape != (B, Hq, D):
+        raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), (B, Hq, D)))
+    ws = _workspace(dev, lib.selfattn_workspace_bytes(B, Hq, Hkv, D, L))
+    _check("selfattn_decode", lib.selfattn_decode(
+        _dev_ptr(q, "q", bf, dev), _dev_ptr(k_new, "k_new", bf, dev), _dev_ptr(v_new, "v_new", bf, dev),
+        _dev_ptr(kcache, "kcache", bf, dev), _dev_ptr(vcache, "vcache", bf, dev), _dev_ptr(pos, "pos", torch.int32, dev),
+        _dev_ptr(out, "out", bf, dev), B, Hq, Hkv, D, L, int(window), float(scale), ws.data_ptr(), ws.numel(),
+        _stream(dev)))
+    return out
+
+
 def _layer_array(layers: Sequence, dev: torch.device, d_model: int, d_inner: int):
     arr = (SbLayer * max(len(layers), 1))()
     bf = torch.bfloat16
@@ -435,7 +476,7 @@ def crossdecoder_step_ex(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor,
     return CrossDecoderStepEx(h, M, kcache, vcache, layers, lens, eps, scale)()
 
 
-__all__ = ["gmu_forward", "xattn_decode", "diffattn_decode", "crossdecoder_step", "CrossDecoderStep", "crossdecoder_step_ex",
+__all__ = ["gmu_forward", "xattn_decode", "diffattn_decode", "selfattn_decode", "crossdecoder_step", "CrossDecoderStep", "crossdecoder_step_ex",
            "CrossDecoderStepEx", "SambayError", "version", "lib",
            "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect", "probe_stream_read_gbps", "probe_mfma_tflops",
            "probe_stream_read_raw"]

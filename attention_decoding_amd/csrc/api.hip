@@ -341,6 +341,68 @@ extern "C" sb_status diffattn_decode(const void *q, const void *kcache, const vo
     return ok();
 }
 
+extern "C" size_t selfattn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || D != kHeadDim || Hq % Hkv != 0) return 0;
+    // The visible counts, then the attention partials of a ragged batch.
+    return round_up((size_t)B * sizeof(int32_t)) + round_up(xattn_partial_bytes(B, Hq, xattn_plan(B, Hkv, L, true).splits));
+}
+
+extern "C" sb_status selfattn_decode(const void *q, const void *k_new, const void *v_new, void *kcache, void *vcache,
+                                     const int32_t *pos, void *out, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                     int64_t L, int64_t window, float scale, void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+    const char *fn = "selfattn_decode";
+    if (B < 0 || Hq < 0 || Hkv < 0 || D < 0 || L < 0) return fail(SB_EINVAL, "negative size");
+    if (window < 0) return fail(SB_EINVAL, "window must be >= 0");
+    if (B == 0) return ok();
+    sb_status st = check_xattn_shape(B, Hq, Hkv, D, L);
+    if (st != SB_OK) return st;
+    if (window > 0 && L != window)
+        return fail(SB_EINVAL, "a sliding-window cache has exactly window slots (L %lld, window %lld)", (long long)L,
+                    (long long)window);
+    if (!q || !k_new || !v_new || !kcache || !vcache || !pos || !out) return fail(SB_EINVAL, "null pointer");
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(kcache) || !aligned16(vcache) ||
+        !aligned16(out))
+        return fail(SB_EINVAL, "tensor base pointers must be 16-byte aligned");
+    if (((uintptr_t)pos & 3u) != 0) return fail(SB_EINVAL, "pos must be 4-byte aligned");
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(SB_EINVAL, "scale must be finite");
+    const size_t qbytes = (size_t)B * Hq * D * 2, rowbytes = (size_t)B * Hkv * D * 2,
+                 kvbytes = (size_t)B * Hkv * L * D * 2;
+    const Range rk = rng("kcache", kcache, kvbytes), rv = rng("vcache", vcache, kvbytes), ro = rng("out", out, qbytes);
+    const Range ins[] = {rng("q", q, qbytes), rng("k_new", k_new, rowbytes), rng("v_new", v_new, rowbytes),
+                         rng("pos", pos, (size_t)B * sizeof(int32_t))};
+    if (overlaps(rk, rv)) return fail(SB_EINVAL, "kcache overlaps vcache");
+    for (const Range *w : {&rk, &rv, &ro})
+        for (const Range &r : ins)
+            if (overlaps(*w, r)) return fail(SB_EINVAL, "%s overlaps %s", w->name, r.name);
+    if (overlaps(ro, rk) || overlaps(ro, rv)) return fail(SB_EINVAL, "out overlaps the cache");
+    const size_t need = selfattn_workspace_bytes(B, Hq, Hkv, D, L);
+    if (!workspace || workspace_bytes < need)
+        return fail(SB_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(SB_EINVAL, "workspace must be 16-byte aligned");
+    const Range rw = rng("workspace", workspace, need);
+    for (const Range *w : {&rk, &rv, &ro})
+        if (overlaps(rw, *w)) return fail(SB_EINVAL, "workspace overlaps %s", w->name);
+    for (const Range &r : ins)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+
+    int32_t *lens = reinterpret_cast<int32_t *>(workspace);
+    void *partials = reinterpret_cast<char *>(workspace) + round_up((size_t)B * sizeof(int32_t));
+    const XattnPlan plan = xattn_plan(B, Hkv, L, true);
+    if (log_enabled())
+        fprintf(stderr, "[sambay] %s B=%lld Hq=%lld Hkv=%lld L=%lld window=%lld -> append, %d chunks of %d positions\n",
+                fn, (long long)B, (long long)Hq, (long long)Hkv, (long long)L, (long long)window, plan.splits,
+                plan.chunk);
+    hipError_t e = launch_kv_append((const bf16_t *)k_new, (const bf16_t *)v_new, (bf16_t *)kcache, (bf16_t *)vcache,
+                                    pos, lens, (int)B, (int)Hkv, (int)L, (int)window, stream);
+    if (e == hipSuccess)
+        e = launch_xattn(q, false, (const bf16_t *)kcache, (const bf16_t *)vcache, lens, (bf16_t *)out, nullptr,
+                         (int)B, (int)Hq, (int)Hkv, (int)L, scale, plan, partials, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
 namespace {
 
 // Workspace layout of one cross-decoder step (all reused layer to layer).

@@ -57,6 +57,14 @@ hipError_t launch_diffattn(const bf16_t *q, const bf16_t *K, const bf16_t *V, co
                            bf16_t *out, int B, int Hq, int Hkv, int L, float scale, float lam, float lam_init,
                            float eps, const XattnPlan &plan, void *partials, hipStream_t stream);
 
+// Self-decoder cache append: sequence b's new K/V rows ([B, Hkv, 128] each)
+// go to position pos[b] (window 0, cache of L positions; not stored when
+// pos[b] >= L) or ring slot pos[b] % window (cache of window == L slots);
+// nothing for pos[b] < 0.  lens_out (nullable, B int32) receives the visible
+// count: 0 for pos[b] < 0, else min(pos[b] + 1, L).
+hipError_t launch_kv_append(const bf16_t *k_new, const bf16_t *v_new, bf16_t *K, bf16_t *V, const int32_t *pos,
+                            int32_t *lens_out, int B, int Hkv, int L, int window, hipStream_t stream);
+
 // ------------------------------------------------ skinny (decode) products
 // out[t, n] = epi( Σ_k X[t, k] · W[n, k] ) for t < T <= 64 tokens.
 enum Epilogue {

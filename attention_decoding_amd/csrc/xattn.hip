@@ -25,12 +25,15 @@
 //  * Partials (m, l, o) per (b, head, chunk) in fp32; a merge kernel combines
 //    the chunks by log-sum-exp in a fixed order (deterministic, no atomics)
 //    and stores bf16 (plus, on request, the bf16 low part of the fp32 value).
+//    With a single chunk per head (short caches) the split kernel stores the
+//    normalised output itself, with the same arithmetic, and no merge runs.
 //  * Ragged batches: with a lengths array, sequence b reads only its first
 //    lens[b] positions of a cache laid out with room for L.  The workgroups
 //    enumerate only the chunks that hold positions (same order as the full
-//    case), so every workgroup streams a full chunk except each sequence's
-//    last; the merge reads only those chunks and a sequence with no position
-//    gets a zero output.
+//    case; a sequence without positions keeps one empty item so that its
+//    output is written), so every workgroup streams a full chunk except each
+//    sequence's last; the merge reads only the chunks that hold positions and
+//    a sequence with no position gets a zero output.
 //
 // Differential attention (the same kernel, DIFF = true): each query and key
 // row is two 64-wide halves, one per attention map, and both maps weight the
@@ -66,9 +69,11 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
                                                                const bf16_t *__restrict__ K,
                                                                const bf16_t *__restrict__ V,
                                                                float2 *__restrict__ part_ml,
-                                                               float *__restrict__ part_o, int B, int Hq, int Hkv,
-                                                               int L, const int32_t *__restrict__ lens, int chunk,
-                                                               int S, float qscale) {
+                                                               float *__restrict__ part_o,
+                                                               bf16_t *__restrict__ out, bf16_t *__restrict__ out_lo,
+                                                               int B, int Hq, int Hkv, int L,
+                                                               const int32_t *__restrict__ lens, int chunk, int S,
+                                                               float qscale) {
     __shared__ __attribute__((aligned(16))) bf16_t vs[kWaves][kKeyBlock][kVStride];
     __shared__ float red_m[kWaves][kMaxGroup];
     __shared__ float red_l[kWaves][kMaxGroup];
@@ -87,10 +92,13 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
         // counts the items of a contiguous run of sequences, a scan over the
         // runs locates the sequence of this workgroup's item.
         int *runs = reinterpret_cast<int *>(&vs[0][0][0]);  // kThreads ints, free until the first block
+        // Chunks of sequence i: those holding positions, at least one (an empty
+        // item still writes the sequence's zero result).
+        auto chunks_of = [&](int i) { return max(1, (min(max(lens[i], 0), L) + chunk - 1) / chunk); };
         const int per = (B + kThreads - 1) / kThreads;
         const int lo = min(B, (int)threadIdx.x * per), hi = min(B, lo + per);
         int cnt = 0;
-        for (int i = lo; i < hi; ++i) cnt += Hkv * ((min(max(lens[i], 0), L) + chunk - 1) / chunk);
+        for (int i = lo; i < hi; ++i) cnt += Hkv * chunks_of(i);
         runs[threadIdx.x] = cnt;
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
             item[0] = -1;
             if (t < kThreads) {
                 for (int i = min(B, t * per); i < min(B, t * per + per); ++i) {
-                    const int n = Hkv * ((min(max(lens[i], 0), L) + chunk - 1) / chunk);
+                    const int n = Hkv * chunks_of(i);
                     if (w < acc + n) {
                         item[0] = i;
                         item[1] = w - acc;
@@ -113,7 +121,7 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
         __syncthreads();
         if (item[0] < 0) return;  // uniform across the workgroup
         b = item[0];
-        const int nch = (min(max(lens[b], 0), L) + chunk - 1) / chunk;
+        const int nch = chunks_of(b);
         g = item[1] / nch;
         s = item[1] % nch;
     }
@@ -289,9 +297,17 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
                 o += e * ow[(w * kMaxGroup + hh) * kHeadDim + d];
             }
         }
-        const size_t pi = ((size_t)b * (DIFF ? 2 * Hq : Hq) + (size_t)g * NC + hh) * S + s;
-        part_o[pi * kHeadDim + d] = o;
-        if (d == 0) part_ml[pi] = make_float2(M, lsum);
+        if (!DIFF && S == 1) {  // the only chunk: normalise and store here (what the merge would do)
+            const float v = lsum > 0.f ? o / lsum : 0.f;
+            const size_t oi = ((size_t)b * Hq + (size_t)g * G + hh) * kHeadDim + d;
+            const bf16_t hi = f32_to_bf16(v);
+            out[oi] = hi;
+            if (out_lo) out_lo[oi] = f32_to_bf16(v - bf16_to_f32(hi));
+        } else {
+            const size_t pi = ((size_t)b * (DIFF ? 2 * Hq : Hq) + (size_t)g * NC + hh) * S + s;
+            part_o[pi * kHeadDim + d] = o;
+            if (d == 0) part_ml[pi] = make_float2(M, lsum);
+        }
     }
 }
 
@@ -376,12 +392,19 @@ XattnPlan xattn_plan(int64_t B, int64_t Hkv, int64_t L, bool ragged) {
     if (S == 0) {
         const int64_t fill = (512 + pairs - 1) / pairs, cap = (2048 + pairs - 1) / pairs;
         const int64_t by_len = L / 4096 > 1 ? L / 4096 : 1;
+        // Splitting to fill the GPU only while every chunk keeps >= 16 blocks
+        // (512 positions): below that a workgroup's fixed cost (item lookup,
+        // query split, cross-wave combine) outweighs its streaming, and one
+        // chunk per head lets the split kernel store the output itself
+        // (measured on a 256-position window, 32 x 8 KV heads: 4 chunks
+        // 32.4 us, 2 chunks 21.4 us, 1 chunk 20.7 us per call).
+        const int64_t fill_cap = nblk / 16;
         S = cap < by_len ? cap : by_len;
-        if (S < fill) S = fill;
+        if (S < fill && S < fill_cap) S = fill < fill_cap ? fill : fill_cap;
         // Ragged batches hold fewer positions than L per sequence: chunks half
         // as long keep the workgroup count up and the tail short (measured on
         // lengths uniform in [2048, 34816]: 8 -> 16 chunks, 5.1 -> 5.4 TB/s).
-        if (ragged) S *= 2;
+        if (ragged && nblk / (2 * S) >= 16) S *= 2;
     }
     if (S > kMaxSplits) S = kMaxSplits;
     if (S > nblk) S = nblk;
@@ -416,14 +439,14 @@ hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t
     {
     TimingScope ts(kTimeXattnSplit, stream);
     if (q_f32)
-        hipLaunchKernelGGL((xattn_split_kernel<true, false>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po, B, Hq,
-                           Hkv, L, lens, plan.chunk, plan.splits, qscale);
+        hipLaunchKernelGGL((xattn_split_kernel<true, false>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po, out,
+                           out_lo, B, Hq, Hkv, L, lens, plan.chunk, plan.splits, qscale);
     else
-        hipLaunchKernelGGL((xattn_split_kernel<false, false>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po, B, Hq,
-                           Hkv, L, lens, plan.chunk, plan.splits, qscale);
+        hipLaunchKernelGGL((xattn_split_kernel<false, false>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po, out,
+                           out_lo, B, Hq, Hkv, L, lens, plan.chunk, plan.splits, qscale);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || plan.splits == 1) return e;  // one chunk: the split kernel stored the output
     TimingScope ts(kTimeXattnMerge, stream);
     hipLaunchKernelGGL(xattn_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kHeadDim), 0, stream, ml, po, out, out_lo,
                        plan.splits, Hq, L, lens, plan.chunk);
@@ -440,8 +463,8 @@ hipError_t launch_diffattn(const bf16_t *q, const bf16_t *K, const bf16_t *V, co
     const dim3 grid = lens ? dim3((unsigned)((size_t)B * Hkv * plan.splits)) : dim3(plan.splits, Hkv, B);
     {
         TimingScope ts(kTimeDiffSplit, stream);
-        hipLaunchKernelGGL((xattn_split_kernel<false, true>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po, B, Hq,
-                           Hkv, L, lens, plan.chunk, plan.splits, scale * kLog2e);
+        hipLaunchKernelGGL((xattn_split_kernel<false, true>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po,
+                           nullptr, nullptr, B, Hq, Hkv, L, lens, plan.chunk, plan.splits, scale * kLog2e);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

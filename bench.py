@@ -120,6 +120,34 @@ def time_calls(fn, n: int, warmup: int = 3) -> float:
     return e0.elapsed_time(e1) / n
 
 
+def time_graph(fn, n: int, reps: int = 10) -> float:
+    """Mean milliseconds per call of fn() replayed from a HIP graph of n calls
+    (no host launch cost: for calls whose kernels take a few microseconds)."""
+    import torch
+
+    fn(0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)                      # the library's workspace for this stream is allocated outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * n)
+
+
 def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> dict:
     """Kernel-level rates of the other workloads (not part of `value`)."""
     import torch
@@ -200,8 +228,30 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> 
         "us_per_call": round(1e3 * ms, 1), "cached_positions": int(lens.sum().item()),
         "gbps": round(nbytes / ms / 1e6, 1), "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
         "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
+    # Self-decoder attention steps: the final full-attention layer appends each
+    # sequence's new row to the same cache at position lens - 1 and attends over
+    # lens positions; a sliding-window layer does the same on a 256-slot ring.
+    kn = workload.normal((c["B"], c["Hkv"], c["D"]), seed=60, device=dev)
+    vn = workload.normal((c["B"], c["Hkv"], c["D"]), seed=61, device=dev)
+    pos = (lens - 1).to(torch.int32)
+    ms = time_calls(lambda i: sb.selfattn_decode(x.q, kn, vn, x.K, x.V, pos, out=out), 20)
+    nbytes = int(lens.sum().item()) * c["Hkv"] * c["D"] * 4 + c["B"] * c["Hkv"] * c["D"] * 4
+    res["selfattn_decode_full_B32_L34816_ragged"] = {
+        "us_per_call": round(1e3 * ms, 1), "gbps": round(nbytes / ms / 1e6, 1),
+        "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
     del x
     torch.cuda.empty_cache()
+    W = workload.SELFATTN_SWA["window"]
+    r = workload.selfattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], W, seed=62, device=dev)
+    call = lambda i: sb.selfattn_decode(r.q, r.k_new, r.v_new, r.K, r.V, pos, window=W, out=out)
+    ms_eager = time_calls(call, 50)
+    ms = time_graph(call, 20)
+    nbytes = c["B"] * c["Hkv"] * W * c["D"] * 4 + c["B"] * c["Hkv"] * c["D"] * 4
+    res["selfattn_decode_window256_B32"] = {
+        "us_per_call": round(1e3 * ms, 2), "timing": "HIP graph replay of 20 calls",
+        "us_per_call_eager": round(1e3 * ms_eager, 2), "gbps": round(nbytes / ms / 1e6, 1),
+        "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del r
     # Complete cross-decoder layer step (pre-RMSNorm mixer + pre-RMSNorm SwiGLU MLP, d_ff 8192) on that ragged batch.
     c = workload.CROSSDECODER_EX
     x = workload.crossdecoder_ex_inputs(c["B"], c["d_model"], c["d_inner"], c["d_ff"], c["Hq"], c["Hkv"], c["D"],

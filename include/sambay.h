@@ -176,6 +176,32 @@ sb_status diffattn_decode(const void *q, const void *kcache, const void *vcache,
                           float scale, float lambda, float lambda_init, float eps, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------- self-decoder attention step --
+ * One decode step of a self-decoder attention layer, the producer side of
+ * the caches ([Notes] section 整体框架: the final full-attention layer writes
+ * the one KV cache that every cross-attention layer reads; section 消融实验:
+ * the other attention layers attend over a 256-position sliding window).
+ * Sequence b's new token is at position p = pos[b] (pos: B int32 in device
+ * memory, 4-byte aligned).  First its key and value rows k_new, v_new
+ * [B, Hkv, D] are stored into kcache/vcache [B, Hkv, L, D]:
+ *   window == 0: at position p (the cache has room for L positions);
+ *   window  > 0: in ring slot p mod window (the cache has L == window slots,
+ *                token t living in slot t mod window);
+ * then q [B, Hq, D] attends, as xattn_decode, over the visible positions:
+ * 0 .. p (window 0) or the min(p + 1, window) slots holding the window most
+ * recent tokens.  No positional encoding, so the ring order is irrelevant.
+ * p < 0 marks an inactive sequence: nothing stored, zero output.  With
+ * window 0 a position p >= L has no slot: nothing is stored and all L
+ * positions are visible (the device clamps; the host cannot check device
+ * values).  kcache/vcache are updated in place; out [B, Hq, D]; all bf16.
+ * Errors: as xattn_decode_varlen, plus SB_EINVAL for window < 0, window > 0
+ * with L != window, a null or misaligned pos, and overlaps between the cache,
+ * out and the other arguments. */
+size_t selfattn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L);
+sb_status selfattn_decode(const void *q, const void *k_new, const void *v_new, void *kcache, void *vcache,
+                          const int32_t *pos, void *out, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L,
+                          int64_t window, float scale, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------- complete cross-decoder layer --
  * The pages define the GMU and the shared-cache cross-attention but not the
  * rest of a layer; this step takes the plain pre-norm Transformer reading.

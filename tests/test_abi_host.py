@@ -248,3 +248,32 @@ def test_diffattn_workspace_sizes(sb):
     assert lib.diffattn_workspace_bytes(16, 24, 8, 128, 34816) == lib.xattn_workspace_bytes(16, 48, 8, 128, 34816)
     assert lib.diffattn_workspace_bytes(16, 24, 8, 64, 34816) == 0
     assert lib.diffattn_workspace_bytes(16, 24, 7, 128, 34816) == 0
+
+
+def _self(sb, B=2, Hq=24, Hkv=8, D=128, L=300, window=0, pos=_addr(6) * 8, out=_addr(3), knew=_addr(7) * 8,
+          kc=_addr(1) * 16, wsb=1 << 30):
+    return sb.lib.selfattn_decode(_addr(0), knew, _addr(7) * 8 + 65536, kc, _addr(2) * 64, pos, out, B, Hq, Hkv, D,
+                                  L, window, 0.088, _addr(4) * 512, wsb, None)
+
+
+def test_selfattn_validation(sb):
+    """Every call here fails validation (or is the B == 0 no-op)."""
+    assert _self(sb, window=-1) == sb.SB_EINVAL
+    assert _self(sb, window=8) == sb.SB_EINVAL                      # L (300) != window
+    assert "window" in sb.lib.sb_last_error().decode()
+    assert _self(sb, pos=None) == sb.SB_EINVAL
+    assert _self(sb, pos=_addr(6) * 8 + 2) == sb.SB_EINVAL          # misaligned pos
+    assert _self(sb, out=_addr(1) * 16 + 4096) == sb.SB_EINVAL      # out inside the cache
+    assert _self(sb, knew=_addr(1) * 16) == sb.SB_EINVAL            # new rows inside the cache
+    assert "k_new" in sb.lib.sb_last_error().decode()
+    assert _self(sb, wsb=16) == sb.SB_EWORKSPACE
+    assert _self(sb, D=64) == sb.SB_EUNSUPPORTED
+    assert _self(sb, L=0) == sb.SB_EINVAL
+    assert _self(sb, B=0) == sb.SB_OK
+
+
+def test_selfattn_workspace_sizes(sb):
+    lib = sb.lib
+    assert lib.selfattn_workspace_bytes(32, 24, 8, 128, 256) > 256
+    assert lib.selfattn_workspace_bytes(32, 24, 8, 128, 34816) >= lib.xattn_workspace_bytes(32, 24, 8, 128, 34816)
+    assert lib.selfattn_workspace_bytes(32, 24, 8, 64, 256) == 0

@@ -56,6 +56,7 @@ def report(name, e, tol):
     (6, 5000, [1, 4096, 4097, 5000, 33, 0]),      # one position, chunk boundaries, full, tail, empty
     (3, 777, [777, 31, 32]),                       # block boundaries around 32
     (2, 40000, [40000, 2048]),
+    (4, 300, [300, 0, 1, 17]),                     # one chunk per head (stored by the split kernel), an empty sequence
 ])
 def test_xattn_varlen_small(sb, B, L, lens):
     x = workload.xattn_inputs(B, 24, 8, 128, L, seed=L, device=DEV)

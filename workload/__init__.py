@@ -253,3 +253,31 @@ def diffattn_inputs(B: int, Hq: int, Hkv: int, D: int, L: int, *, seed: int = 0,
     """q, K, V ~ N(0,1) as for the plain decode (same seed, same values), plus the gain."""
     x = xattn_inputs(B, Hq, Hkv, D, L, seed=seed, device=device, dtype=dtype)
     return DiffAttnInputs(q=x.q, K=x.K, V=x.V, gamma=diffattn_gain(D, seed=seed, device=device, dtype=dtype))
+
+
+# ------------------------------------------- self-decoder attention (bf16)
+
+# The self-decoder's attention layers at decode: the final full-attention
+# layer appends to the shared cache (room for 34816 positions, the ragged
+# serving batch's positions), the sliding-window layers to a ring of 256
+# slots (full once 256 tokens have been generated).
+SELFATTN_FULL = dict(B=32, Hq=24, Hkv=8, D=128, L=34816, min_len=2048)   # bf16
+SELFATTN_SWA = dict(B=32, Hq=24, Hkv=8, D=128, window=256, min_len=2048)  # bf16
+
+
+@dataclass
+class SelfAttnInputs:
+    q: torch.Tensor      # [B, Hq, D]
+    k_new: torch.Tensor  # [B, Hkv, D]
+    v_new: torch.Tensor  # [B, Hkv, D]
+    K: torch.Tensor      # [B, Hkv, L, D] cache contents before the step
+    V: torch.Tensor
+
+
+def selfattn_inputs(B: int, Hq: int, Hkv: int, D: int, L: int, *, seed: int = 0, device="cpu",
+                    dtype=torch.bfloat16) -> SelfAttnInputs:
+    """q, the new key/value rows and the cache contents, all ~ N(0,1)."""
+    x = xattn_inputs(B, Hq, Hkv, D, L, seed=seed, device=device, dtype=dtype)
+    k_new = normal((B, Hkv, D), seed=_seed(seed, 80), device=device, dtype=dtype)
+    v_new = normal((B, Hkv, D), seed=_seed(seed, 81), device=device, dtype=dtype)
+    return SelfAttnInputs(q=x.q, k_new=k_new, v_new=v_new, K=x.K, V=x.V)
