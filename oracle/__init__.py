@@ -75,6 +75,9 @@ def _load():
     lib.oracle_selfattn.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp,
                                     i64, i64, i64, i64, i64, i64, dbl]
     lib.oracle_selfattn.restype = ctypes.c_int
+    lib.oracle_mamba_step.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp,
+                                      ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64]
+    lib.oracle_mamba_step.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [dbl]
     lib.oracle_round_bf16.restype = dbl
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -360,6 +363,52 @@ def selfattn(q, k_new, v_new, K, V, pos, window: int = 0, scale: float | None = 
                              _ptr(Ko), _ptr(Vo), B, Hq, Hkv, D, L, int(window), float(scale))
     _check(rc, "selfattn")
     return out, Ko, Vo
+
+
+MAMBA_KEYS = ("W_in", "W_x", "W_dt", "W_out", "conv_w", "conv_b", "dt_bias", "A_log", "D")
+
+
+def mamba_step(x, w: dict, conv_state, ssm_state):
+    """One decode step of a Mamba layer for B sequences.
+
+    x [B, d_model]; w: W_in [2 d_inner, d_model], W_x [R + 2N, d_inner],
+    W_dt [d_inner, R], W_out [d_model, d_inner] (one dtype), conv_w
+    [d_inner, K], conv_b, dt_bias, D [d_inner], A_log [d_inner, N] (one dtype);
+    conv_state [B, d_inner, K - 1], ssm_state [B, d_inner, N].
+    Returns (M [B, d_inner], y [B, d_model], conv_state', ssm_state'), float64."""
+    lib = _load()
+    xa, dx = _as_input(x)
+    arr = {k: _as_input(w[k]) for k in MAMBA_KEYS}
+    dw = {arr[k][1] for k in ("W_in", "W_x", "W_dt", "W_out")}
+    dp = {arr[k][1] for k in ("conv_w", "conv_b", "dt_bias", "A_log", "D")}
+    if len(dw) != 1 or len(dp) != 1:
+        raise TypeError("matrices must share a dtype, and so must the per-channel parameters")
+    ca, dc = _as_input(conv_state)
+    sa, ds = _as_input(ssm_state)
+    if dc != ds:
+        raise TypeError("states must share a dtype")
+    B, d_model = xa.shape
+    d_inner, K = arr["conv_w"][0].shape
+    N = arr["A_log"][0].shape[1]
+    R = arr["W_dt"][0].shape[1]
+    shapes = {"W_in": (2 * d_inner, d_model), "W_x": (R + 2 * N, d_inner), "W_dt": (d_inner, R),
+              "W_out": (d_model, d_inner), "conv_b": (d_inner,), "dt_bias": (d_inner,), "A_log": (d_inner, N),
+              "D": (d_inner,)}
+    for k, shp in shapes.items():
+        if arr[k][0].shape != shp:
+            raise ValueError("%s has shape %s, expected %s" % (k, arr[k][0].shape, shp))
+    if ca.shape != (B, d_inner, K - 1) or sa.shape != (B, d_inner, N):
+        raise ValueError("state shape mismatch")
+    M = np.empty((B, d_inner), dtype=np.float64)
+    y = np.empty((B, d_model), dtype=np.float64)
+    co = np.empty((B, d_inner, K - 1), dtype=np.float64)
+    so = np.empty((B, d_inner, N), dtype=np.float64)
+    a = {k: _ptr(arr[k][0]) for k in MAMBA_KEYS}
+    rc = lib.oracle_mamba_step(_ptr(xa), dx, a["W_in"], a["W_x"], a["W_dt"], a["W_out"], dw.pop(), a["conv_w"],
+                               a["conv_b"], a["dt_bias"], a["A_log"], a["D"], dp.pop(), _ptr(ca), _ptr(sa), dc,
+                               _ptr(co), _ptr(so), _ptr(M), _ptr(y), B, d_model, d_inner, N, R, K)
+    _check(rc, "mamba_step")
+    return M, y, co, so
 
 
 def rmsnorm(x, g, eps: float = 1e-5):

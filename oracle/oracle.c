@@ -859,6 +859,110 @@ int oracle_selfattn(const void *q, int dt_q, const void *k_new, const void *v_ne
     return fail ? -2 : 0;
 }
 
+/* ------------------------------------------- SSM decode step (memory M)
+ *
+ * The GMU layers reuse M, the token-mixing output of the self-decoder's last
+ * SSM layer ([Notes] "关键设计", "整体框架"; at decode time that layer keeps a
+ * state of constant size, [Notes] "关键设计").  The pages do not spell out
+ * the SSM; the self-decoder is Samba's, whose SSM layers are Mamba layers
+ * with per-channel state decay ([Notes] "消融实验": the scalar-decay Mamba-2
+ * variant loses).  This is one decode step of a Mamba layer (selective SSM
+ * with zero-order-hold decay and Euler input term, as published) for B
+ * sequences, in the order the layer computes it:
+ *   [xi | z] = W_in x                           (W_in [2·d_inner, d_model])
+ *   u_c  = SiLU(Σ_k conv_w[c,k] · win_c[k] + conv_b[c]),
+ *          win_c = (conv_state[c, 0 .. K-2], xi_c)   oldest first, K = d_conv
+ *   [δ | Bv | Cv] = W_x u                       (W_x [R + 2N, d_inner])
+ *   Δ_c  = softplus(W_dt[c] · δ + dt_bias[c]),  softplus(a) = log(1 + e^a)
+ *   s[c,n] <- exp(Δ_c · A[c,n]) · s[c,n] + Δ_c · Bv[n] · u_c,  A = -exp(A_log)
+ *   M_c  = Σ_n Cv[n] · s[c,n] + D[c] · u_c      (the memory readout)
+ *   y    = W_out (M ⊙ SiLU(z))                  (W_out [d_model, d_inner])
+ * conv_state shifts by one (the new xi enters last).  Matrices share dt_w,
+ * per-channel parameters (conv_w [d_inner, K], conv_b, dt_bias, D [d_inner],
+ * A_log [d_inner, N]) share dt_p; states arrive in any dtype and leave as
+ * fp64 (conv_state [B, d_inner, K-1], ssm_state [B, d_inner, N]). */
+static double softplus_def(double a) {
+    /* log(1 + e^a), written without overflowing e^a for large a */
+    return a > 30.0 ? a + log1p(exp(-a)) : log1p(exp(a));
+}
+
+int oracle_mamba_step(const void *x, int dt_x, const void *W_in, const void *W_x, const void *W_dt,
+                      const void *W_out, int dt_w, const void *conv_w, const void *conv_b, const void *dt_bias,
+                      const void *A_log, const void *Dp, int dt_p, const void *conv_state, const void *ssm_state,
+                      int dt_s, double *conv_state_out, double *ssm_state_out, double *M_out, double *y_out,
+                      int64_t B, int64_t d_model, int64_t d_inner, int64_t N, int64_t R, int64_t K) {
+    if (!x || !W_in || !W_x || !W_dt || !W_out || !conv_w || !conv_b || !dt_bias || !A_log || !Dp ||
+        !conv_state || !ssm_state || !conv_state_out || !ssm_state_out || !M_out || !y_out || B < 0 ||
+        d_model <= 0 || d_inner <= 0 || N <= 0 || R <= 0 || K < 1)
+        return -1;
+    const int64_t P = R + 2 * N, KS = K - 1;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *xi = (double *)malloc((size_t)d_inner * sizeof(double));
+        double *z = (double *)malloc((size_t)d_inner * sizeof(double));
+        double *u = (double *)malloc((size_t)d_inner * sizeof(double));
+        double *xd = (double *)malloc((size_t)P * sizeof(double));
+        double *gm = (double *)malloc((size_t)d_inner * sizeof(double));
+        int ok = xi && z && u && xd && gm;
+        if (!ok) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t b = 0; b < B; ++b) {
+            if (!ok) continue;
+            /* input projection: the x branch and the gate branch */
+            for (int64_t c = 0; c < 2 * d_inner; ++c) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < d_model; ++k) acc += widen(W_in, dt_w, c * d_model + k) * widen(x, dt_x, b * d_model + k);
+                if (c < d_inner) xi[c] = acc; else z[c - d_inner] = acc;
+            }
+            /* causal depthwise convolution over the last K inputs, SiLU; shift the window */
+            for (int64_t c = 0; c < d_inner; ++c) {
+                const int64_t so = (b * d_inner + c) * KS;
+                double acc = widen(conv_b, dt_p, c);
+                for (int64_t k = 0; k < KS; ++k) acc += widen(conv_w, dt_p, c * K + k) * widen(conv_state, dt_s, so + k);
+                acc += widen(conv_w, dt_p, c * K + KS) * xi[c];
+                u[c] = acc / (1.0 + exp(-acc));
+                for (int64_t k = 0; k + 1 < KS; ++k) conv_state_out[so + k] = widen(conv_state, dt_s, so + k + 1);
+                if (KS > 0) conv_state_out[so + KS - 1] = xi[c];
+            }
+            /* the data-dependent step, input and output vectors */
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < d_inner; ++c) acc += widen(W_x, dt_w, p * d_inner + c) * u[c];
+                xd[p] = acc;
+            }
+            const double *delta = xd, *Bv = xd + R, *Cv = xd + R + N;
+            for (int64_t c = 0; c < d_inner; ++c) {
+                double a = widen(dt_bias, dt_p, c);
+                for (int64_t r = 0; r < R; ++r) a += widen(W_dt, dt_w, c * R + r) * delta[r];
+                const double dlt = softplus_def(a);
+                double m = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const int64_t si = (b * d_inner + c) * N + n;
+                    const double A = -exp(widen(A_log, dt_p, c * N + n));
+                    const double st = exp(dlt * A) * widen(ssm_state, dt_s, si) + dlt * Bv[n] * u[c];
+                    ssm_state_out[si] = st;
+                    m += Cv[n] * st;
+                }
+                m += widen(Dp, dt_p, c) * u[c];
+                M_out[b * d_inner + c] = m;
+                gm[c] = m * (z[c] / (1.0 + exp(-z[c])));
+            }
+            /* output projection of the gated readout */
+            for (int64_t o = 0; o < d_model; ++o) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < d_inner; ++c) acc += widen(W_out, dt_w, o * d_inner + c) * gm[c];
+                y_out[b * d_model + o] = acc;
+            }
+        }
+        free(xi); free(z); free(u); free(xd); free(gm);
+    }
+    return fail ? -2 : 0;
+}
+
 /* --------------------------------------------------------------- threads */
 
 int oracle_max_threads(void) {

@@ -281,3 +281,51 @@ def selfattn_inputs(B: int, Hq: int, Hkv: int, D: int, L: int, *, seed: int = 0,
     k_new = normal((B, Hkv, D), seed=_seed(seed, 80), device=device, dtype=dtype)
     v_new = normal((B, Hkv, D), seed=_seed(seed, 81), device=device, dtype=dtype)
     return SelfAttnInputs(q=x.q, k_new=k_new, v_new=v_new, K=x.K, V=x.V)
+
+
+# --------------------------------------------- SSM decode step (Mamba layer)
+
+# The self-decoder's SSM layer at the model width: d_inner = 2 d_model, 16
+# states per channel, a 4-tap causal convolution, a step projection of rank
+# ceil(d_model / 16) = 192.
+MAMBA_DECODE = dict(B=32, d_model=3072, d_inner=6144, d_state=16, dt_rank=192, d_conv=4)
+
+
+@dataclass
+class MambaInputs:
+    x: torch.Tensor            # [B, d_model] layer input
+    w: dict                    # W_in, W_x, W_dt, W_out (dtype); conv_w, conv_b, dt_bias, A_log, D (float32)
+    conv_state: torch.Tensor   # [B, d_inner, d_conv - 1] float32
+    ssm_state: torch.Tensor    # [B, d_inner, d_state] float32
+
+
+def _uniform(shape, lo: float, hi: float, *, seed: int, device) -> torch.Tensor:
+    u = torch.rand(tuple(shape), generator=_gen(device, seed), device=device, dtype=torch.float32)
+    return u * (hi - lo) + lo
+
+
+def mamba_inputs(B: int, d_model: int, d_inner: int, d_state: int, dt_rank: int, d_conv: int, *, seed: int = 0,
+                 device="cpu", dtype=torch.bfloat16) -> MambaInputs:
+    """x ~ N(0,1); the four matrices ~ N(0, 0.02^2); the layer's usual
+    initialisation for the rest: conv taps and bias ~ U(-1/sqrt(d_conv),
+    1/sqrt(d_conv)), dt_bias = softplus^-1(dt) with log dt ~ U(log 1e-3,
+    log 1e-1), A_log[c, n] = log(n + 1), D = 1; conv_state ~ N(0, 1.2^2)
+    (past branch inputs), ssm_state ~ N(0, 1)."""
+    s = lambda t: _seed(seed, 90 + t)
+    x = normal((B, d_model), seed=s(0), device=device, dtype=dtype)
+    w = {
+        "W_in": normal((2 * d_inner, d_model), std=WEIGHT_STD, seed=s(1), device=device, dtype=dtype),
+        "W_x": normal((dt_rank + 2 * d_state, d_inner), std=WEIGHT_STD, seed=s(2), device=device, dtype=dtype),
+        "W_dt": normal((d_inner, dt_rank), std=WEIGHT_STD, seed=s(3), device=device, dtype=dtype),
+        "W_out": normal((d_model, d_inner), std=WEIGHT_STD, seed=s(4), device=device, dtype=dtype),
+    }
+    bound = 1.0 / d_conv ** 0.5
+    w["conv_w"] = _uniform((d_inner, d_conv), -bound, bound, seed=s(5), device=device)
+    w["conv_b"] = _uniform((d_inner,), -bound, bound, seed=s(6), device=device)
+    dt = torch.exp(_uniform((d_inner,), -6.907755278982137, -2.302585092994046, seed=s(7), device=device))
+    w["dt_bias"] = dt + torch.log(-torch.expm1(-dt))
+    w["A_log"] = torch.log(torch.arange(1, d_state + 1, device=device, dtype=torch.float32)).repeat(d_inner, 1)
+    w["D"] = torch.ones(d_inner, device=device, dtype=torch.float32)
+    conv_state = normal((B, d_inner, d_conv - 1), std=1.2, seed=s(8), device=device, dtype=torch.float32)
+    ssm_state = normal((B, d_inner, d_state), seed=s(9), device=device, dtype=torch.float32)
+    return MambaInputs(x=x, w=w, conv_state=conv_state, ssm_state=ssm_state)
