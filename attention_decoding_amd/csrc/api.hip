@@ -405,6 +405,166 @@ extern "C" sb_status selfattn_decode(const void *q, const void *k_new, const voi
 
 namespace {
 
+// Workspace of one Mamba decode step, per token group of <= 64 sequences
+// (groups run one after another and reuse it).
+struct MambaLayout {
+    size_t xz, u, u_hi, u_lo, xdbl, g_hi, g_lo, part, total;
+};
+
+MambaLayout mamba_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t N, int64_t R) {
+    const int T = (int)(B < kSkinnyMaxTokens ? B : kSkinnyMaxTokens);
+    const int64_t P = R + 2 * N;
+    MambaLayout l;
+    Carver c{nullptr};
+    l.xz = c.used; c.take((size_t)T * 2 * d_inner * sizeof(float));
+    l.u = c.used; c.take((size_t)T * d_inner * sizeof(float));
+    l.u_hi = c.used; c.take((size_t)T * d_inner * 2);
+    l.u_lo = c.used; c.take((size_t)T * d_inner * 2);
+    l.xdbl = c.used; c.take((size_t)T * P * sizeof(float));
+    l.g_hi = c.used; c.take((size_t)T * d_inner * 2);
+    l.g_lo = c.used; c.take((size_t)T * d_inner * 2);
+    size_t part = skinny_partial_bytes_max(T, (int)(2 * d_inner), (int)d_model);
+    const size_t p2 = skinny_partial_bytes_max(T, (int)P, (int)d_inner),
+                 p3 = skinny_partial_bytes_max(T, (int)d_model, (int)d_inner);
+    if (p2 > part) part = p2;
+    if (p3 > part) part = p3;
+    l.part = c.used; c.take(part);
+    l.total = c.used;
+    return l;
+}
+
+bool mamba_dims_ok(int64_t B, int64_t d_model, int64_t d_inner, int64_t N, int64_t R, int64_t K) {
+    return B > 0 && d_model > 0 && d_inner > 0 && d_model % 64 == 0 && d_inner % 64 == 0 && d_model <= kMaxDim &&
+           d_inner <= kMaxDim && (N == 8 || N == 16 || N == 32 || N == 64) && R >= 8 && R <= kMaxDtRank &&
+           R % 8 == 0 && K >= 1 && K <= kMaxConv;
+}
+
+}  // namespace
+
+extern "C" size_t mamba_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_state,
+                                        int64_t dt_rank, int64_t d_conv) {
+    if (!mamba_dims_ok(B, d_model, d_inner, d_state, dt_rank, d_conv)) return 0;
+    return mamba_layout(B, d_model, d_inner, d_state, dt_rank).total;
+}
+
+extern "C" sb_status mamba_decode_step(const void *x, const sb_mamba_weights *w, float *conv_state, float *ssm_state,
+                                       void *M_out, void *y_out, int64_t B, int64_t d_model, int64_t d_inner,
+                                       int64_t d_state, int64_t dt_rank, int64_t d_conv, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "mamba_decode_step";
+    if (B < 0 || d_model < 0 || d_inner < 0 || d_state < 0 || dt_rank < 0 || d_conv < 0)
+        return fail(SB_EINVAL, "negative size");
+    if (B == 0) return ok();
+    if (d_model == 0 || d_inner == 0 || d_state == 0 || dt_rank == 0 || d_conv == 0)
+        return fail(SB_EINVAL, "every dimension must be positive");
+    if (!mamba_dims_ok(B, d_model, d_inner, d_state, dt_rank, d_conv))
+        return fail(SB_EUNSUPPORTED,
+                    "unsupported Mamba shape (d_model, d_inner multiples of 64; d_state in {8, 16, 32, 64}; "
+                    "dt_rank a multiple of 8, <= %d; d_conv <= %d)", kMaxDtRank, kMaxConv);
+    if (!x || !w || (!conv_state && d_conv > 1) || !ssm_state || !M_out || !y_out)
+        return fail(SB_EINVAL, "null pointer");
+    if (!w->w_in || !w->conv_w || !w->conv_b || !w->w_x || !w->w_dt || !w->dt_bias || !w->a_log || !w->d_skip ||
+        !w->w_out)
+        return fail(SB_EINVAL, "null weight");
+    const void *al[] = {x, conv_state, ssm_state, M_out, y_out, w->w_in, w->conv_w, w->conv_b, w->w_x, w->w_dt,
+                        w->dt_bias, w->a_log, w->d_skip, w->w_out};
+    for (const void *p : al)
+        if (!aligned16(p)) return fail(SB_EINVAL, "tensor base pointers must be 16-byte aligned");
+    const int64_t P = dt_rank + 2 * d_state;
+    const Range outs[] = {rng("conv_state", conv_state, (size_t)B * d_inner * (d_conv - 1) * 4),
+                          rng("ssm_state", ssm_state, (size_t)B * d_inner * d_state * 4),
+                          rng("M", M_out, (size_t)B * d_inner * 2), rng("y", y_out, (size_t)B * d_model * 2)};
+    const Range ins[] = {rng("x", x, (size_t)B * d_model * 2), rng("w_in", w->w_in, (size_t)2 * d_inner * d_model * 2),
+                         rng("conv_w", w->conv_w, (size_t)d_inner * d_conv * 4),
+                         rng("conv_b", w->conv_b, (size_t)d_inner * 4), rng("w_x", w->w_x, (size_t)P * d_inner * 2),
+                         rng("w_dt", w->w_dt, (size_t)d_inner * dt_rank * 2),
+                         rng("dt_bias", w->dt_bias, (size_t)d_inner * 4),
+                         rng("a_log", w->a_log, (size_t)d_inner * d_state * 4),
+                         rng("d_skip", w->d_skip, (size_t)d_inner * 4),
+                         rng("w_out", w->w_out, (size_t)d_model * d_inner * 2)};
+    for (size_t i = 0; i < 4; ++i) {
+        for (size_t j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j])) return fail(SB_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (const Range &r : ins)
+            if (overlaps(outs[i], r)) return fail(SB_EINVAL, "%s overlaps %s", outs[i].name, r.name);
+    }
+    const MambaLayout lay = mamba_layout(B, d_model, d_inner, d_state, dt_rank);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(SB_EWORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
+                    workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(SB_EINVAL, "workspace must be 16-byte aligned");
+    const Range rw = rng("workspace", workspace, lay.total);
+    for (const Range &r : outs)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+    for (const Range &r : ins)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+
+    char *ws = reinterpret_cast<char *>(workspace);
+    float *xz = reinterpret_cast<float *>(ws + lay.xz), *u = reinterpret_cast<float *>(ws + lay.u);
+    float *xdbl = reinterpret_cast<float *>(ws + lay.xdbl), *part = reinterpret_cast<float *>(ws + lay.part);
+    bf16_t *u_hi = reinterpret_cast<bf16_t *>(ws + lay.u_hi), *u_lo = reinterpret_cast<bf16_t *>(ws + lay.u_lo);
+    bf16_t *g_hi = reinterpret_cast<bf16_t *>(ws + lay.g_hi), *g_lo = reinterpret_cast<bf16_t *>(ws + lay.g_lo);
+    const int di = (int)d_inner, dm = (int)d_model, Pi = (int)P;
+    hipError_t e = hipSuccess;
+    for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+        const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+        SkinnyArgs a;
+        a.X = (const bf16_t *)x + t0 * d_model;
+        a.ldx = dm;
+        a.W = (const bf16_t *)w->w_in;
+        a.T = T;
+        a.N = 2 * di;
+        a.K = dm;
+        a.epi = EPI_F32;
+        a.out = xz;
+        a.ldo = 2 * di;
+        const SkinnyPlan p_in = skinny_plan(T, 2 * di, dm, false);
+        if (log_enabled() && t0 == 0)
+            fprintf(stderr, "[sambay] %s B=%lld d_model=%d d_inner=%d N=%lld R=%lld K=%lld: in-proj %d k-splits\n",
+                    fn, (long long)B, dm, di, (long long)d_state, (long long)dt_rank, (long long)d_conv,
+                    p_in.k_splits);
+        e = launch_skinny(a, p_in, part, stream);
+        if (e != hipSuccess) break;
+        e = launch_mamba_conv(xz, 2 * di, conv_state + t0 * d_inner * (d_conv - 1), (const float *)w->conv_w,
+                              (const float *)w->conv_b, u, u_hi, u_lo, T, di, (int)d_conv, stream);
+        if (e != hipSuccess) break;
+        SkinnyArgs b;
+        b.X = u_hi;
+        b.X_lo = u_lo;
+        b.ldx = di;
+        b.W = (const bf16_t *)w->w_x;
+        b.T = T;
+        b.N = Pi;
+        b.K = di;
+        b.epi = EPI_F32;
+        b.out = xdbl;
+        b.ldo = Pi;
+        e = launch_skinny(b, skinny_plan(T, Pi, di, true), part, stream);
+        if (e != hipSuccess) break;
+        e = launch_mamba_scan(xz, 2 * di, u, xdbl, Pi, (int)dt_rank, (const bf16_t *)w->w_dt,
+                              (const float *)w->dt_bias, (const float *)w->a_log, (const float *)w->d_skip,
+                              ssm_state + t0 * d_inner * d_state, (bf16_t *)M_out + t0 * d_inner, g_hi, g_lo, T, di,
+                              (int)d_state, stream);
+        if (e != hipSuccess) break;
+        SkinnyArgs o;
+        o.X = g_hi;
+        o.X_lo = g_lo;
+        o.ldx = di;
+        o.W = (const bf16_t *)w->w_out;
+        o.T = T;
+        o.N = dm;
+        o.K = di;
+        o.epi = EPI_BF16;
+        o.out = (bf16_t *)y_out + t0 * d_model;
+        o.ldo = dm;
+        e = launch_skinny(o, skinny_plan(T, dm, di, true), part, stream);
+    }
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+namespace {
+
 // Workspace layout of one cross-decoder step (all reused layer to layer).
 struct StepLayout {
     size_t q, o, gmu, partials, total;  // o holds the bf16 hi + lo pair of the attention output

@@ -65,6 +65,21 @@ hipError_t launch_diffattn(const bf16_t *q, const bf16_t *K, const bf16_t *V, co
 hipError_t launch_kv_append(const bf16_t *k_new, const bf16_t *v_new, bf16_t *K, bf16_t *V, const int32_t *pos,
                             int32_t *lens_out, int B, int Hkv, int L, int window, hipStream_t stream);
 
+// ------------------------------------------------------ SSM decode step
+constexpr int kMaxConv = 8;      // convolution taps supported
+constexpr int kMaxDtRank = 256;  // step-projection rank supported (a multiple of 8)
+// u = SiLU(conv(window, xi)) per (token, channel); conv_state [T, d_inner, K-1]
+// fp32 shifted in place; u fp32 and as a bf16 hi + lo pair.
+hipError_t launch_mamba_conv(const float *xz, int ldxz, float *conv_state, const float *conv_w, const float *conv_b,
+                             float *u, bf16_t *u_hi, bf16_t *u_lo, int T, int d_inner, int K, hipStream_t stream);
+// Δ = softplus(W_dt δ + dt_bias), the NS-state update of ssm_state [T, d_inner,
+// NS] fp32 in place, M (bf16) and g = M·SiLU(z) (bf16 hi + lo).  xdbl [T, P]
+// holds δ [R] | B [NS] | C [NS]; z is xz[:, d_inner:].  NS in {8, 16, 32, 64}.
+hipError_t launch_mamba_scan(const float *xz, int ldxz, const float *u, const float *xdbl, int P, int R,
+                             const bf16_t *W_dt, const float *dt_bias, const float *A_log, const float *Dp,
+                             float *ssm_state, bf16_t *M_out, bf16_t *g_hi, bf16_t *g_lo, int T, int d_inner, int NS,
+                             hipStream_t stream);
+
 // ------------------------------------------------ skinny (decode) products
 // out[t, n] = epi( Σ_k X[t, k] · W[n, k] ) for t < T <= 64 tokens.
 enum Epilogue {

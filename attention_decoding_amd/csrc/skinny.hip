@@ -468,6 +468,11 @@ SkinnyPlan skinny_plan(int T, int N, int K, bool xlo) {
     const int64_t xbytes = (int64_t)T * K * 2 * (xlo ? 2 : 1);
     int ks = 1;
     if (xbytes >= (int64_t)192 * 1024) ks = (int)((256LL * 48 + N / 2) / N);
+    // Short outputs (N < 768, e.g. the SSM layer's 224-row step/B/C
+    // projection) would get dozens of splits whose finishing pass, one thread
+    // per output summing every split, dominates (48 splits: 13.9 us of
+    // finishing for a 6.9 us product); at most 8.
+    if (N < 768 && ks > 8) ks = 8;
     const char *e = getenv("SAMBAY_SKINNY_KSPLIT");
     if (e && *e) ks = atoi(e);
     const int kc = K / kChunk;

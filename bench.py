@@ -252,6 +252,25 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> 
         "us_per_call_eager": round(1e3 * ms_eager, 2), "gbps": round(nbytes / ms / 1e6, 1),
         "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
     del r
+    # SSM decode step (the Mamba layer producing M): 4 rotating weight sets
+    # (4 x 118 MB, more than the 256 MB last-level cache) so that the weights
+    # stream from HBM as they would layer after layer.
+    c = workload.MAMBA_DECODE
+    dm, di, N, R, K = c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"], c["d_conv"]
+    msets = [workload.mamba_inputs(1, dm, di, N, R, K, seed=70 + k, device=dev).w for k in range(4)]
+    wbytes = (2 * di * dm + (R + 2 * N) * di + di * R + dm * di) * 2 + (di * K + 3 * di + di * N) * 4
+    for B in (1, 32):
+        m = workload.mamba_inputs(B, dm, di, N, R, K, seed=80 + B, device=dev)
+        Mo = torch.empty(B, di, dtype=torch.bfloat16, device=dev)
+        yo = torch.empty(B, dm, dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda i: sb.mamba_decode_step(m.x, msets[i % 4], m.conv_state, m.ssm_state, Mo, yo), 40)
+        nbytes = wbytes + B * di * (N + K - 1) * 4 * 2 + B * (2 * dm + di) * 2
+        res["mamba_decode_B%d" % B] = {
+            "us_per_call": round(1e3 * ms, 2), "hbm_bytes": nbytes, "gbps": round(nbytes / ms / 1e6, 1),
+            "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
+        del m
+    del msets
     # Complete cross-decoder layer step (pre-RMSNorm mixer + pre-RMSNorm SwiGLU MLP, d_ff 8192) on that ragged batch.
     c = workload.CROSSDECODER_EX
     x = workload.crossdecoder_ex_inputs(c["B"], c["d_model"], c["d_inner"], c["d_ff"], c["Hq"], c["Hkv"], c["D"],

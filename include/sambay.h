@@ -202,6 +202,50 @@ sb_status selfattn_decode(const void *q, const void *k_new, const void *v_new, v
                           const int32_t *pos, void *out, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L,
                           int64_t window, float scale, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------- SSM decode step (M) --
+ * One decode step of the self-decoder's SSM layer, whose token-mixing output
+ * M is the memory that every GMU layer reuses ([Notes] sections 关键设计 and
+ * 整体框架: the GMU gates M of the last SSM layer, which keeps a state of
+ * constant size at decode time; the SSM is Mamba with per-channel decay,
+ * section 消融实验).  The pages do not spell the layer out; this is the
+ * published Mamba layer, for B sequences with input x [B, d_model]:
+ *   [xi | z] = x W_in^T                  W_in  [2·d_inner, d_model], bf16
+ *   u  = SiLU(conv_b + Σ_k conv_w[:, k] · window[k]),   window = the d_conv-1
+ *        stored inputs (oldest first) then xi; the stored window shifts by one
+ *   [δ | Bv | Cv] = u W_x^T              W_x   [dt_rank + 2·d_state, d_inner], bf16
+ *   Δ  = softplus(δ W_dt^T + dt_bias)    W_dt  [d_inner, dt_rank], bf16
+ *   s  = exp(Δ·A) ⊙ s + Δ·Bv·u,  A = -exp(a_log)   (per channel c and state n)
+ *   M  = Σ_n Cv[n] · s[:, n] + d_skip ⊙ u           -> M_out [B, d_inner], bf16
+ *   y  = (M ⊙ SiLU(z)) W_out^T           W_out [d_model, d_inner], bf16
+ *                                                   -> y_out [B, d_model], bf16
+ * conv_w [d_inner, d_conv], conv_b, dt_bias, d_skip [d_inner] and a_log
+ * [d_inner, d_state] are fp32.  conv_state [B, d_inner, d_conv-1] and
+ * ssm_state [B, d_inner, d_state] are fp32 and updated in place (conv_state
+ * may be NULL when d_conv == 1: there is no stored input).  u and the
+ * gated readout feed their products as bf16 hi + lo pairs; everything else
+ * accumulates in fp32.  Supported: d_model, d_inner multiples of 64; d_state
+ * in {8, 16, 32, 64}; dt_rank a multiple of 8, at most 256; d_conv <= 8.
+ * Errors: SB_EINVAL for null pointers or weights, misaligned pointers, a
+ * zero dimension, overlaps between an output (states, M, y) and anything
+ * else; SB_EUNSUPPORTED for other shapes; SB_EWORKSPACE. */
+typedef struct {
+    const void *w_in;     /* [2·d_inner, d_model] bf16: rows 0 .. d_inner-1 the x branch, then z */
+    const float *conv_w;  /* [d_inner, d_conv] fp32, tap d_conv-1 multiplies the newest input */
+    const float *conv_b;  /* [d_inner] fp32 */
+    const void *w_x;      /* [dt_rank + 2·d_state, d_inner] bf16: rows δ | B | C */
+    const void *w_dt;     /* [d_inner, dt_rank] bf16 */
+    const float *dt_bias; /* [d_inner] fp32 */
+    const float *a_log;   /* [d_inner, d_state] fp32 */
+    const float *d_skip;  /* [d_inner] fp32 */
+    const void *w_out;    /* [d_model, d_inner] bf16 */
+} sb_mamba_weights;
+size_t mamba_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank,
+                             int64_t d_conv);
+sb_status mamba_decode_step(const void *x, const sb_mamba_weights *w, float *conv_state, float *ssm_state,
+                            void *M_out, void *y_out, int64_t B, int64_t d_model, int64_t d_inner, int64_t d_state,
+                            int64_t dt_rank, int64_t d_conv, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* ------------------------------------------- complete cross-decoder layer --
  * The pages define the GMU and the shared-cache cross-attention but not the
  * rest of a layer; this step takes the plain pre-norm Transformer reading.

@@ -277,3 +277,41 @@ def test_selfattn_workspace_sizes(sb):
     assert lib.selfattn_workspace_bytes(32, 24, 8, 128, 256) > 256
     assert lib.selfattn_workspace_bytes(32, 24, 8, 128, 34816) >= lib.xattn_workspace_bytes(32, 24, 8, 128, 34816)
     assert lib.selfattn_workspace_bytes(32, 24, 8, 64, 256) == 0
+
+
+def _mamba(sb, B=4, dm=3072, di=6144, N=16, R=192, K=4, w_over=None, M=None, y=None, wsb=1 << 34, null=None):
+    G = 1 << 30          # fake, far-apart, 16-byte aligned addresses (never dereferenced)
+    w = sb.SbMambaWeights(*[(i + 10) * G for i in range(9)])
+    for k, v in (w_over or {}).items():
+        setattr(w, k, v)
+    if null:
+        setattr(w, null, None)
+    return sb.lib.mamba_decode_step(1 * G, ctypes.byref(w), 2 * G, 3 * G, M if M is not None else 4 * G,
+                                    y if y is not None else 5 * G, B, dm, di, N, R, K, 6 * G, wsb, None)
+
+
+def test_mamba_validation(sb):
+    """Every call here fails validation (or is the B == 0 no-op)."""
+    assert _mamba(sb, N=12) == sb.SB_EUNSUPPORTED
+    assert _mamba(sb, R=191) == sb.SB_EUNSUPPORTED
+    assert _mamba(sb, R=196) == sb.SB_EUNSUPPORTED                  # not a multiple of 8
+    assert _mamba(sb, R=320) == sb.SB_EUNSUPPORTED
+    assert _mamba(sb, K=9) == sb.SB_EUNSUPPORTED
+    assert _mamba(sb, dm=100) == sb.SB_EUNSUPPORTED
+    assert _mamba(sb, null="w_dt") == sb.SB_EINVAL
+    assert _mamba(sb, w_over={"a_log": (15 << 30) + 4}) == sb.SB_EINVAL          # misaligned
+    assert _mamba(sb, M=(3 << 30) + 256) == sb.SB_EINVAL                           # M inside ssm_state
+    assert "overlaps" in sb.lib.sb_last_error().decode()
+    assert _mamba(sb, y=(18 << 30) + 1024) == sb.SB_EINVAL                         # y inside w_out
+    assert _mamba(sb, wsb=16) == sb.SB_EWORKSPACE
+    assert _mamba(sb, dm=0) == sb.SB_EINVAL
+    assert _mamba(sb, B=0) == sb.SB_OK
+
+
+def test_mamba_workspace_sizes(sb):
+    lib = sb.lib
+    assert lib.mamba_workspace_bytes(32, 3072, 6144, 16, 192, 4) > 32 * 2 * 6144 * 4
+    # token groups of at most 64 sequences reuse one workspace
+    assert lib.mamba_workspace_bytes(200, 3072, 6144, 16, 192, 4) == lib.mamba_workspace_bytes(64, 3072, 6144, 16,
+                                                                                                  192, 4)
+    assert lib.mamba_workspace_bytes(32, 3072, 6144, 12, 192, 4) == 0
