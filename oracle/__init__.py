@@ -78,6 +78,9 @@ def _load():
     lib.oracle_mamba_step.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp,
                                       ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64]
     lib.oracle_mamba_step.restype = ctypes.c_int
+    lib.oracle_attn_prefill.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i64, i64, i64, i64, i64, i64,
+                                        dbl]
+    lib.oracle_attn_prefill.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [dbl]
     lib.oracle_round_bf16.restype = dbl
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -409,6 +412,29 @@ def mamba_step(x, w: dict, conv_state, ssm_state):
                                _ptr(co), _ptr(so), _ptr(M), _ptr(y), B, d_model, d_inner, N, R, K)
     _check(rc, "mamba_step")
     return M, y, co, so
+
+
+def attn_prefill(q, k, v, window: int = 0, scale: float | None = None):
+    """Causal (window 0) or sliding-window causal attention of T prompt
+    tokens: q [B, T, Hq, D], k, v [B, T, Hkv, D] -> out [B, T, Hq, D]; query i
+    sees keys j <= i (and j > i - window when window > 0)."""
+    lib = _load()
+    qa, dq = _as_input(q)
+    ka, dk = _as_input(k)
+    va, dv = _as_input(v)
+    if dk != dv:
+        raise TypeError("k and v must share a dtype")
+    B, T, Hq, D = qa.shape
+    if ka.shape[:2] != (B, T) or ka.shape[3] != D or va.shape != ka.shape:
+        raise ValueError("attn_prefill shape mismatch")
+    Hkv = ka.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, T, Hq, D), dtype=np.float64)
+    rc = lib.oracle_attn_prefill(_ptr(qa), dq, _ptr(ka), _ptr(va), dk, _ptr(out), B, T, Hq, Hkv, D, int(window),
+                                 float(scale))
+    _check(rc, "attn_prefill")
+    return out
 
 
 def rmsnorm(x, g, eps: float = 1e-5):

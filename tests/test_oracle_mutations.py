@@ -89,6 +89,15 @@ MUTANTS = [
     ("mamba_window_not_shifted", "test_oracle_mamba.py",
      "for (int64_t k = 0; k + 1 < KS; ++k) conv_state_out[so + k] = widen(conv_state, dt_s, so + k + 1);",
      "for (int64_t k = 0; k + 1 < KS; ++k) conv_state_out[so + k] = widen(conv_state, dt_s, so + k);"),
+    ("prefill_window_off_by_one", "test_oracle_prefill.py",
+     "const int64_t j0 = window > 0 && i + 1 > window ? i + 1 - window : 0, j1 = i;",
+     "const int64_t j0 = window > 0 && i > window ? i - window : 0, j1 = i;"),
+    ("prefill_not_causal", "test_oracle_prefill.py", "? i + 1 - window : 0, j1 = i;", "? i + 1 - window : 0, j1 = T - 1;"),
+    ("prefill_excludes_own_token", "test_oracle_prefill.py", "? i + 1 - window : 0, j1 = i;",
+     "? i + 1 - window : 0, j1 = i > j0 ? i - 1 : i;"),
+    ("prefill_wrong_group_map", "test_oracle_prefill.py",
+     "const int64_t b = r / (T * Hq), i = (r / Hq) % T, h = r % Hq, g = h / G;",
+     "const int64_t b = r / (T * Hq), i = (r / Hq) % T, h = r % Hq, g = h % Hkv;"),
     ("selfattn_value_row_not_stored", "test_oracle_selfattn.py",
      "V_out[((b * Hkv + g) * L + slot) * D + d] = widen(v_new, dt_new, (b * Hkv + g) * D + d);",
      "V_out[((b * Hkv + g) * L + slot) * D + d] = widen(V, dt_kv, ((b * Hkv + g) * L + slot) * D + d);"),
