@@ -34,10 +34,10 @@ EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", 
            "sb_timing_collect", "sb_probe_stream_read", "sb_probe_mfma", "sb_probe_mfma_flops",
            "xattn_decode_varlen", "crossdecoder_ex_workspace_bytes", "crossdecoder_step_ex",
            "diffattn_workspace_bytes", "diffattn_decode", "selfattn_workspace_bytes", "selfattn_decode",
-           "mamba_workspace_bytes", "mamba_decode_step")
+           "mamba_workspace_bytes", "mamba_decode_step", "attn_prefill_workspace_bytes", "attn_prefill")
 SB_TIME_XATTN_SPLIT, SB_TIME_XATTN_MERGE, SB_TIME_SKINNY, SB_TIME_GEMM, SB_TIME_GMU_F32, SB_TIME_PROBE = \
     1, 2, 4, 8, 16, 32
-SB_TIME_DIFF_SPLIT, SB_TIME_DIFF_MERGE = 64, 128
+SB_TIME_DIFF_SPLIT, SB_TIME_DIFF_MERGE, SB_TIME_PREFILL = 64, 128, 256
 
 
 class SbLayer(ctypes.Structure):
@@ -104,6 +104,10 @@ def _load() -> ctypes.CDLL:
     lib.mamba_decode_step.argtypes = [vp, ctypes.POINTER(SbMambaWeights), vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                       i64, vp, sz, vp]
     lib.mamba_decode_step.restype = ctypes.c_int
+    lib.attn_prefill_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.attn_prefill_workspace_bytes.restype = sz
+    lib.attn_prefill.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float, vp, sz, vp]
+    lib.attn_prefill.restype = ctypes.c_int
     lib.sb_timing_enable.argtypes = [ctypes.c_uint32]
     lib.sb_timing_enable.restype = ctypes.c_int
     lib.sb_timing_collect.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -401,6 +405,33 @@ def mamba_decode_step(x: torch.Tensor, w: dict, conv_state: torch.Tensor, ssm_st
     return M_out, y_out
 
 
+def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int = 0, out: torch.Tensor | None = None,
+                 scale: float | None = None) -> torch.Tensor:
+    """Causal prefill attention over the prompt: q [B, T, Hq, D], k, v
+    [B, T, Hkv, D] (bf16) -> out [B, T, Hq, D]; query i sees keys j <= i and,
+    with window > 0, j > i - window."""
+    dev = _check_device(q, "q")
+    bf = torch.bfloat16
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, T, Hq, D] and k [B, T, Hkv, D]")
+    B, T, Hq, D = q.shape
+    if k.shape[:2] != (B, T) or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError("attn_prefill shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                                       tuple(v.shape)))
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=bf, device=dev)
+    elif out.shape != (B, T, Hq, D):
+        raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), (B, T, Hq, D)))
+    ws = _workspace(dev, lib.attn_prefill_workspace_bytes(B, T, Hkv, D))
+    _check("attn_prefill", lib.attn_prefill(_dev_ptr(q, "q", bf, dev), _dev_ptr(k, "k", bf, dev),
+                                            _dev_ptr(v, "v", bf, dev), _dev_ptr(out, "out", bf, dev), B, T, Hq, Hkv,
+                                            D, int(window), float(scale), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return out
+
+
 def _layer_array(layers: Sequence, dev: torch.device, d_model: int, d_inner: int):
     arr = (SbLayer * max(len(layers), 1))()
     bf = torch.bfloat16
@@ -534,6 +565,7 @@ def crossdecoder_step_ex(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor,
 
 
 __all__ = ["gmu_forward", "xattn_decode", "diffattn_decode", "selfattn_decode", "mamba_decode_step",
+           "attn_prefill",
            "crossdecoder_step", "CrossDecoderStep", "crossdecoder_step_ex",
            "CrossDecoderStepEx", "SambayError", "version", "lib",
            "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect", "probe_stream_read_gbps", "probe_mfma_tflops",

@@ -403,6 +403,51 @@ extern "C" sb_status selfattn_decode(const void *q, const void *k_new, const voi
     return ok();
 }
 
+extern "C" size_t attn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t Hkv, int64_t D) {
+    if (B <= 0 || T <= 0 || Hkv <= 0 || D != kHeadDim) return 0;
+    return round_up(attn_prefill_workspace_need(B, T, Hkv));
+}
+
+extern "C" sb_status attn_prefill(const void *q, const void *k, const void *v, void *out, int64_t B, int64_t T,
+                                  int64_t Hq, int64_t Hkv, int64_t D, int64_t window, float scale, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "attn_prefill";
+    if (B < 0 || T < 0 || Hq < 0 || Hkv < 0 || D < 0 || window < 0) return fail(SB_EINVAL, "negative size");
+    if (B == 0 || T == 0) return ok();
+    if (Hq == 0 || Hkv == 0) return fail(SB_EINVAL, "Hq and Hkv must be positive");
+    if (Hq % Hkv != 0) return fail(SB_EINVAL, "Hq (%lld) is not a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+    if (D != kHeadDim) return fail(SB_EUNSUPPORTED, "head dim %lld unsupported (only %d)", (long long)D, kHeadDim);
+    if (B > 65535 || Hq > 65535 || T >= ((int64_t)1 << 31) || B * T * Hq * D >= ((int64_t)1 << 62))
+        return fail(SB_EUNSUPPORTED, "size out of range");
+    if (!q || !k || !v || !out) return fail(SB_EINVAL, "null tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(SB_EINVAL, "tensor base pointers must be 16-byte aligned");
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(SB_EINVAL, "scale must be finite");
+    const size_t qbytes = (size_t)B * T * Hq * D * 2, kvbytes = (size_t)B * T * Hkv * D * 2;
+    const Range ro = rng("out", out, qbytes);
+    const Range ins[] = {rng("q", q, qbytes), rng("k", k, kvbytes), rng("v", v, kvbytes)};
+    for (const Range &r : ins)
+        if (overlaps(ro, r)) return fail(SB_EINVAL, "out overlaps %s", r.name);
+    const size_t need = attn_prefill_workspace_bytes(B, T, Hkv, D);
+    if (!workspace || workspace_bytes < need)
+        return fail(SB_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(SB_EINVAL, "workspace must be 16-byte aligned");
+    const Range rw = rng("workspace", workspace, need);
+    if (overlaps(rw, ro)) return fail(SB_EINVAL, "workspace overlaps out");
+    for (const Range &r : ins)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+    if (log_enabled())
+        fprintf(stderr, "[sambay] %s B=%lld T=%lld Hq=%lld Hkv=%lld window=%lld -> %lld workgroups\n", fn,
+                (long long)B, (long long)T, (long long)Hq, (long long)Hkv, (long long)window,
+                (long long)(B * Hq * ((T + 63) / 64)));
+    const int W = window >= T ? 0 : (int)window;  // a window covering the prompt is plain causal attention
+    hipError_t e = launch_attn_prefill((const bf16_t *)q, (const bf16_t *)k, (const bf16_t *)v, (bf16_t *)out, (int)B,
+                                       (int)T, (int)Hq, (int)Hkv, W, scale, workspace, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
 namespace {
 
 // Workspace of one Mamba decode step, per token group of <= 64 sequences

@@ -25,7 +25,8 @@ class TimingScope {
     bool active_ = false;
 };
 constexpr uint32_t kTimeXattnSplit = 1, kTimeXattnMerge = 2, kTimeSkinny = 4, kTimeGemm = 8, kTimeGmuF32 = 16,
-                   kTimeProbe = 32, kTimeDiffSplit = 64, kTimeDiffMerge = 128;
+                   kTimeProbe = 32, kTimeDiffSplit = 64, kTimeDiffMerge = 128,
+                   kTimePrefill = 256;
 
 // ------------------------------------------------------- cross-attention
 constexpr int kHeadDim = 128;     // supported head dimension
@@ -64,6 +65,14 @@ hipError_t launch_diffattn(const bf16_t *q, const bf16_t *K, const bf16_t *V, co
 // count: 0 for pos[b] < 0, else min(pos[b] + 1, L).
 hipError_t launch_kv_append(const bf16_t *k_new, const bf16_t *v_new, bf16_t *K, bf16_t *V, const int32_t *pos,
                             int32_t *lens_out, int B, int Hkv, int L, int window, hipStream_t stream);
+
+// Prefill attention: q [B, T, Hq, 128], k, v [B, T, Hkv, 128] bf16 ->
+// out [B, T, Hq, 128] bf16; query i sees keys j <= i (and j > i - window when
+// window > 0).  Grid (ceil(T / 64), Hq, B).
+// workspace: attn_prefill_workspace_need(B, T, Hkv) bytes (V transposed).
+size_t attn_prefill_workspace_need(int64_t B, int64_t T, int64_t Hkv);
+hipError_t launch_attn_prefill(const bf16_t *q, const bf16_t *k, const bf16_t *v, bf16_t *out, int B, int T, int Hq,
+                               int Hkv, int window, float scale, void *workspace, hipStream_t stream);
 
 // ------------------------------------------------------ SSM decode step
 constexpr int kMaxConv = 8;      // convolution taps supported

@@ -271,6 +271,22 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> 
             "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
         del m
     del msets
+    # Prefill attention over the prompt: 4 x 2048 tokens, window 256 (the
+    # self-decoder's sliding-window layers), and plain causal at 1 x 2048.
+    c = workload.ATTN_PREFILL
+    for B, W in ((c["B"], c["window"]), (1, 0)):
+        x = workload.prefill_inputs(B, c["T"], c["Hq"], c["Hkv"], c["D"], seed=90 + W, device=dev)
+        o = torch.empty_like(x.q)
+        ms = time_calls(lambda i: sb.attn_prefill(x.q, x.k, x.v, window=W, out=o), 20)
+        T, D = c["T"], c["D"]
+        keys = sum(min(i + 1, W) if W else i + 1 for i in range(T))        # visible (query, key) pairs per head
+        flops = 4.0 * D * keys * c["Hq"] * B
+        nbytes = B * T * (2 * c["Hq"] + 2 * c["Hkv"]) * D * 2
+        res["attn_prefill_B%d_T%d_window%d" % (B, T, W)] = {
+            "us_per_call": round(1e3 * ms, 2), "tflops": round(flops / ms / 1e9, 1),
+            "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4), "gbps": round(nbytes / ms / 1e6, 1),
+            "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        del x, o
     # Complete cross-decoder layer step (pre-RMSNorm mixer + pre-RMSNorm SwiGLU MLP, d_ff 8192) on that ragged batch.
     c = workload.CROSSDECODER_EX
     x = workload.crossdecoder_ex_inputs(c["B"], c["d_model"], c["d_inner"], c["d_ff"], c["Hq"], c["Hkv"], c["D"],

@@ -202,6 +202,25 @@ sb_status selfattn_decode(const void *q, const void *k_new, const void *v_new, v
                           const int32_t *pos, void *out, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t L,
                           int64_t window, float scale, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------- prefill attention --
+ * Attention of the self-decoder's layers over the prompt during a YOCO-style
+ * prefill, which keeps pre-filling linear ([Notes] sections 领域现状 and
+ * 现有痛点; the sliding window of section 消融实验): q [B, T, Hq, D], k, v
+ * [B, T, Hkv, D] (token-major, as the projections write them), out
+ * [B, T, Hq, D]; query i of head h attends to keys j of KV head
+ * h / (Hq / Hkv) with j <= i and, when window > 0, j > i - window:
+ *   out[b, i, h] = Σ_j softmax_j(scale · q[b, i, h]·k[b, j, g]) v[b, j, g].
+ * window == 0 (or >= T) is plain causal attention.  No positional encoding.
+ * All bf16; fp32 accumulation.  The workspace holds V transposed.
+ * Errors: SB_EINVAL for null or misaligned pointers, Hq % Hkv != 0, a
+ * non-finite scale, out or the workspace overlapping an input;
+ * SB_EUNSUPPORTED for D != 128 or B, Hq > 65535; SB_EWORKSPACE.  B == 0 or
+ * T == 0 is a no-op. */
+size_t attn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t Hkv, int64_t D);
+sb_status attn_prefill(const void *q, const void *k, const void *v, void *out, int64_t B, int64_t T, int64_t Hq,
+                       int64_t Hkv, int64_t D, int64_t window, float scale, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
 /* ------------------------------------------------- SSM decode step (M) --
  * One decode step of the self-decoder's SSM layer, whose token-mixing output
  * M is the memory that every GMU layer reuses ([Notes] sections 关键设计 and
@@ -300,7 +319,8 @@ typedef enum {
     SB_TIME_GMU_F32 = 16,      /* fp32 GMU kernels */
     SB_TIME_PROBE = 32,        /* the two probes below */
     SB_TIME_DIFF_SPLIT = 64,   /* differential-attention partial kernel */
-    SB_TIME_DIFF_MERGE = 128   /* differential-attention merge + normalisation */
+    SB_TIME_DIFF_MERGE = 128,  /* differential-attention merge + normalisation */
+    SB_TIME_PREFILL = 256      /* prefill attention kernel */
 } sb_timing_kind;
 
 sb_status sb_timing_enable(uint32_t mask);

@@ -315,3 +315,25 @@ def test_mamba_workspace_sizes(sb):
     assert lib.mamba_workspace_bytes(200, 3072, 6144, 16, 192, 4) == lib.mamba_workspace_bytes(64, 3072, 6144, 16,
                                                                                                   192, 4)
     assert lib.mamba_workspace_bytes(32, 3072, 6144, 12, 192, 4) == 0
+
+
+def test_attn_prefill_validation(sb):
+    """Every call here fails validation (or is a no-op)."""
+    lib = sb.lib
+    G = 1 << 30
+    call = lambda **kw: lib.attn_prefill(kw.get("q", 1 * G), 2 * G, 3 * G, kw.get("out", 4 * G), kw.get("B", 2),
+                                         kw.get("T", 2048), kw.get("Hq", 24), kw.get("Hkv", 8), kw.get("D", 128),
+                                         kw.get("W", 256), kw.get("scale", 0.088), kw.get("ws", 5 * G),
+                                         kw.get("wsb", 1 << 30), None)
+    assert call(D=64) == sb.SB_EUNSUPPORTED
+    assert call(Hkv=7) == sb.SB_EINVAL
+    assert call(W=-1) == sb.SB_EINVAL
+    assert call(q=None) == sb.SB_EINVAL
+    assert call(out=1 * G + 1024) == sb.SB_EINVAL                  # out overlaps q
+    assert call(out=4 * G + 8) == sb.SB_EINVAL                     # misaligned
+    assert call(scale=float("inf")) == sb.SB_EINVAL
+    assert call(wsb=1024) == sb.SB_EWORKSPACE
+    assert call(ws=2 * G + 4096) == sb.SB_EINVAL                   # workspace overlaps k
+    assert call(T=0) == sb.SB_OK and call(B=0) == sb.SB_OK
+    assert lib.attn_prefill_workspace_bytes(4, 2048, 8, 128) == 4 * 8 * 128 * 2048 * 2
+    assert lib.attn_prefill_workspace_bytes(1, 33, 1, 128) == 128 * 64 * 2      # 33 keys padded to 64

@@ -329,3 +329,25 @@ def mamba_inputs(B: int, d_model: int, d_inner: int, d_state: int, dt_rank: int,
     conv_state = normal((B, d_inner, d_conv - 1), std=1.2, seed=s(8), device=device, dtype=torch.float32)
     ssm_state = normal((B, d_inner, d_state), seed=s(9), device=device, dtype=torch.float32)
     return MambaInputs(x=x, w=w, conv_state=conv_state, ssm_state=ssm_state)
+
+
+# ---------------------------------------------- prefill attention (bf16)
+
+# The pages' prompt length: 2048 tokens, four sequences, the model's head
+# shape; the self-decoder's sliding window of 256 tokens.
+ATTN_PREFILL = dict(B=4, T=2048, Hq=24, Hkv=8, D=128, window=256)   # bf16
+
+
+@dataclass
+class PrefillInputs:
+    q: torch.Tensor    # [B, T, Hq, D]
+    k: torch.Tensor    # [B, T, Hkv, D]
+    v: torch.Tensor
+
+
+def prefill_inputs(B: int, T: int, Hq: int, Hkv: int, D: int, *, seed: int = 0, device="cpu",
+                   dtype=torch.bfloat16) -> PrefillInputs:
+    """q, k, v ~ N(0, 1), token-major as the projections write them."""
+    return PrefillInputs(q=normal((B, T, Hq, D), seed=_seed(seed, 100), device=device, dtype=dtype),
+                         k=normal((B, T, Hkv, D), seed=_seed(seed, 101), device=device, dtype=dtype),
+                         v=normal((B, T, Hkv, D), seed=_seed(seed, 102), device=device, dtype=dtype))
