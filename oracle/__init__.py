@@ -437,6 +437,25 @@ def attn_prefill(q, k, v, window: int = 0, scale: float | None = None):
     return out
 
 
+def mamba_prefill(x, w: dict, conv_state, ssm_state):
+    """The Mamba layer over T tokens, x [B, T, d_model]: by definition T
+    successive mamba_step calls from the given states.  Returns (M [B, T,
+    d_inner], y [B, T, d_model], conv_state', ssm_state'), float64."""
+    xa, _ = _as_input(x)
+    if xa.ndim != 3:
+        raise ValueError("x must be [B, T, d_model]")
+    B, T, _ = xa.shape
+    conv, ssm = conv_state, ssm_state
+    Ms, ys = [], []
+    for t in range(T):
+        M, y, conv, ssm = mamba_step(np.ascontiguousarray(xa[:, t]), w, conv, ssm)
+        Ms.append(M)
+        ys.append(y)
+    if T == 0:
+        raise ValueError("T must be positive")
+    return np.stack(Ms, axis=1), np.stack(ys, axis=1), conv, ssm
+
+
 def rmsnorm(x, g, eps: float = 1e-5):
     """Row-wise RMSNorm: x / sqrt(mean(x^2) + eps) * g over the last axis."""
     lib = _load()

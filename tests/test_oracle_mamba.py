@@ -157,3 +157,49 @@ def test_rejects_bad_arguments():
     w["W_x"] = w["W_x"][:-1]
     with pytest.raises(ValueError):
         oracle.mamba_step(xs[0], w, m.conv_state, m.ssm_state)
+
+
+@pytest.mark.parametrize("T,K", [(1, 4), (7, 4), (12, 1)])
+def test_prefill_against_parallel_form(T, K):
+    """oracle.mamba_prefill over a [B, T, d_model] prompt against the
+    materialised mixing-matrix form, per sequence."""
+    B = 2
+    m, xs = _inputs(B, seed=30 + T + K, K=K, T=T)
+    x = np.ascontiguousarray(np.transpose(_f64(xs), (1, 0, 2)))
+    M, y, conv, ssm = oracle.mamba_prefill(x, m.w, m.conv_state, m.ssm_state)
+    for b in range(B):
+        Mp, yp, cp, sp = _parallel(xs[:, b], m.w, m.conv_state[b], m.ssm_state[b])
+        assert _rel(M[b], Mp) <= 1e-11
+        assert _rel(y[b], yp) <= 1e-11
+        if K > 1:
+            assert _rel(conv[b], cp) <= 1e-13
+        assert _rel(ssm[b], sp) <= 1e-11
+
+
+def test_prefill_pure_decay_closed_form():
+    """With a zero input projection, bias and window the convolution sees
+    zeros: u = SiLU(0) = 0, so δ = B = C = 0, M = y = 0, Δ = softplus(dt_bias)
+    at every step and the state after T tokens is exp(T·Δ·A)·s0."""
+    m, xs = _inputs(2, seed=40, T=5)
+    m.w["W_in"] = torch.zeros_like(m.w["W_in"])
+    m.w["conv_b"] = torch.zeros_like(m.w["conv_b"])
+    m.conv_state.zero_()
+    x = np.ascontiguousarray(np.transpose(_f64(xs), (1, 0, 2)))
+    M, y, conv, ssm = oracle.mamba_prefill(x, m.w, m.conv_state, m.ssm_state)
+    assert np.count_nonzero(M) == 0 and np.count_nonzero(y) == 0 and np.count_nonzero(conv) == 0
+    dt = np.log1p(np.exp(_f64(m.w["dt_bias"])))                         # [d_inner]
+    A = -np.exp(_f64(m.w["A_log"]))                                       # [d_inner, N]
+    expect = np.exp(5 * dt[:, None] * A)[None] * _f64(m.ssm_state)
+    assert _rel(ssm, expect) <= 1e-13
+
+
+def test_prefill_in_two_parts_equals_one():
+    """The states a prompt leaves carry it on exactly: prefill(x[:, :7]) then
+    prefill(x[:, 7:]) from the returned states equals prefill(x)."""
+    m, xs = _inputs(2, seed=41, T=11)
+    x = np.ascontiguousarray(np.transpose(_f64(xs), (1, 0, 2)))
+    M, y, conv, ssm = oracle.mamba_prefill(x, m.w, m.conv_state, m.ssm_state)
+    M1, y1, c1, s1 = oracle.mamba_prefill(np.ascontiguousarray(x[:, :7]), m.w, m.conv_state, m.ssm_state)
+    M2, y2, c2, s2 = oracle.mamba_prefill(np.ascontiguousarray(x[:, 7:]), m.w, c1, s1)
+    assert np.array_equal(np.concatenate([M1, M2], 1), M) and np.array_equal(np.concatenate([y1, y2], 1), y)
+    assert np.array_equal(c2, conv) and np.array_equal(s2, ssm)
