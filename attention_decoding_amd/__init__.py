@@ -34,7 +34,8 @@ EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", 
            "sb_timing_collect", "sb_probe_stream_read", "sb_probe_mfma", "sb_probe_mfma_flops",
            "xattn_decode_varlen", "crossdecoder_ex_workspace_bytes", "crossdecoder_step_ex",
            "diffattn_workspace_bytes", "diffattn_decode", "selfattn_workspace_bytes", "selfattn_decode",
-           "mamba_workspace_bytes", "mamba_decode_step", "attn_prefill_workspace_bytes", "attn_prefill")
+           "mamba_workspace_bytes", "mamba_decode_step", "attn_prefill_workspace_bytes", "attn_prefill",
+           "mamba_prefill_workspace_bytes", "mamba_prefill")
 SB_TIME_XATTN_SPLIT, SB_TIME_XATTN_MERGE, SB_TIME_SKINNY, SB_TIME_GEMM, SB_TIME_GMU_F32, SB_TIME_PROBE = \
     1, 2, 4, 8, 16, 32
 SB_TIME_DIFF_SPLIT, SB_TIME_DIFF_MERGE, SB_TIME_PREFILL = 64, 128, 256
@@ -108,6 +109,11 @@ def _load() -> ctypes.CDLL:
     lib.attn_prefill_workspace_bytes.restype = sz
     lib.attn_prefill.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float, vp, sz, vp]
     lib.attn_prefill.restype = ctypes.c_int
+    lib.mamba_prefill_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64]
+    lib.mamba_prefill_workspace_bytes.restype = sz
+    lib.mamba_prefill.argtypes = [vp, ctypes.POINTER(SbMambaWeights), vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                  i64, vp, sz, vp]
+    lib.mamba_prefill.restype = ctypes.c_int
     lib.sb_timing_enable.argtypes = [ctypes.c_uint32]
     lib.sb_timing_enable.restype = ctypes.c_int
     lib.sb_timing_collect.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -360,6 +366,53 @@ def selfattn_decode(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k
     return out
 
 
+def _mamba_weights(w: dict, dev, d_model: int):
+    bf, f32 = torch.bfloat16, torch.float32
+    if w["conv_w"].dim() != 2 or w["A_log"].dim() != 2 or w["W_dt"].dim() != 2:
+        raise ValueError("conv_w, A_log and W_dt must be 2-D")
+    d_inner, d_conv = w["conv_w"].shape
+    d_state, dt_rank = w["A_log"].shape[1], w["W_dt"].shape[1]
+    shapes = {"W_in": (2 * d_inner, d_model), "W_x": (dt_rank + 2 * d_state, d_inner), "W_dt": (d_inner, dt_rank),
+              "W_out": (d_model, d_inner), "conv_b": (d_inner,), "dt_bias": (d_inner,), "A_log": (d_inner, d_state),
+              "D": (d_inner,)}
+    for k, shp in shapes.items():
+        if tuple(w[k].shape) != shp:
+            raise ValueError("%s has shape %s, expected %s" % (k, tuple(w[k].shape), shp))
+    sw = SbMambaWeights(
+        _dev_ptr(w["W_in"], "W_in", bf, dev), _dev_ptr(w["conv_w"], "conv_w", f32, dev),
+        _dev_ptr(w["conv_b"], "conv_b", f32, dev), _dev_ptr(w["W_x"], "W_x", bf, dev),
+        _dev_ptr(w["W_dt"], "W_dt", bf, dev), _dev_ptr(w["dt_bias"], "dt_bias", f32, dev),
+        _dev_ptr(w["A_log"], "A_log", f32, dev), _dev_ptr(w["D"], "D", f32, dev), _dev_ptr(w["W_out"], "W_out", bf, dev))
+    return sw, d_inner, d_state, dt_rank, d_conv
+
+
+def mamba_prefill(x: torch.Tensor, w: dict, conv_state: torch.Tensor, ssm_state: torch.Tensor,
+                  M_out: torch.Tensor | None = None, y_out: torch.Tensor | None = None):
+    """The Mamba layer over T prompt tokens, x [B, T, d_model] (bf16), weights
+    as for mamba_decode_step; conv_state and ssm_state (float32) are read as
+    the states before the prompt and overwritten with those after it.
+    Returns (M [B, T, d_inner], y [B, T, d_model]), bf16."""
+    dev = _check_device(x, "x")
+    bf = torch.bfloat16
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, d_model]")
+    B, T, d_model = x.shape
+    sw, d_inner, d_state, dt_rank, d_conv = _mamba_weights(w, dev, d_model)
+    if conv_state.shape != (B, d_inner, d_conv - 1) or ssm_state.shape != (B, d_inner, d_state):
+        raise ValueError("state shape mismatch")
+    if M_out is None:
+        M_out = torch.empty((B, T, d_inner), dtype=bf, device=dev)
+    if y_out is None:
+        y_out = torch.empty((B, T, d_model), dtype=bf, device=dev)
+    ws = _workspace(dev, lib.mamba_prefill_workspace_bytes(B, T, d_model, d_inner, d_state, dt_rank, d_conv))
+    _check("mamba_prefill", lib.mamba_prefill(
+        _dev_ptr(x, "x", bf, dev), ctypes.byref(sw), _dev_ptr(conv_state, "conv_state", torch.float32, dev),
+        _dev_ptr(ssm_state, "ssm_state", torch.float32, dev), _dev_ptr(M_out, "M_out", bf, dev),
+        _dev_ptr(y_out, "y_out", bf, dev), B, T, d_model, d_inner, d_state, dt_rank, d_conv, ws.data_ptr(),
+        ws.numel(), _stream(dev)))
+    return M_out, y_out
+
+
 def mamba_decode_step(x: torch.Tensor, w: dict, conv_state: torch.Tensor, ssm_state: torch.Tensor,
                       M_out: torch.Tensor | None = None, y_out: torch.Tensor | None = None):
     """One decode step of the self-decoder's Mamba layer for x [B, d_model]
@@ -565,7 +618,7 @@ def crossdecoder_step_ex(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor,
 
 
 __all__ = ["gmu_forward", "xattn_decode", "diffattn_decode", "selfattn_decode", "mamba_decode_step",
-           "attn_prefill",
+           "attn_prefill", "mamba_prefill",
            "crossdecoder_step", "CrossDecoderStep", "crossdecoder_step_ex",
            "CrossDecoderStepEx", "SambayError", "version", "lib",
            "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect", "probe_stream_read_gbps", "probe_mfma_tflops",

@@ -608,6 +608,78 @@ extern "C" sb_status mamba_decode_step(const void *x, const sb_mamba_weights *w,
     return ok();
 }
 
+extern "C" size_t mamba_prefill_workspace_bytes(int64_t B, int64_t T, int64_t d_model, int64_t d_inner,
+                                                int64_t d_state, int64_t dt_rank, int64_t d_conv) {
+    if (T <= 0 || !mamba_dims_ok(B, d_model, d_inner, d_state, dt_rank, d_conv) || dt_rank % 64 != 0) return 0;
+    return round_up(mamba_prefill_workspace_need(B, T, d_inner, d_state, dt_rank));
+}
+
+extern "C" sb_status mamba_prefill(const void *x, const sb_mamba_weights *w, float *conv_state, float *ssm_state,
+                                   void *M_out, void *y_out, int64_t B, int64_t T, int64_t d_model, int64_t d_inner,
+                                   int64_t d_state, int64_t dt_rank, int64_t d_conv, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "mamba_prefill";
+    if (B < 0 || T < 0 || d_model < 0 || d_inner < 0 || d_state < 0 || dt_rank < 0 || d_conv < 0)
+        return fail(SB_EINVAL, "negative size");
+    if (B == 0 || T == 0) return ok();
+    if (d_model == 0 || d_inner == 0 || d_state == 0 || dt_rank == 0 || d_conv == 0)
+        return fail(SB_EINVAL, "every dimension must be positive");
+    if (!mamba_dims_ok(B, d_model, d_inner, d_state, dt_rank, d_conv) || dt_rank % 64 != 0)
+        return fail(SB_EUNSUPPORTED,
+                    "unsupported Mamba prefill shape (d_model, d_inner, dt_rank multiples of 64, dt_rank <= %d; "
+                    "d_state in {8, 16, 32, 64}; d_conv <= %d)", kMaxDtRank, kMaxConv);
+    if (B * T > ((int64_t)1 << 31) - 1 || B > 65535 || T > 65535)
+        return fail(SB_EUNSUPPORTED, "B, T <= 65535 and B*T < 2^31 required");
+    if (!x || !w || (!conv_state && d_conv > 1) || !ssm_state || !M_out || !y_out)
+        return fail(SB_EINVAL, "null pointer");
+    if (!w->w_in || !w->conv_w || !w->conv_b || !w->w_x || !w->w_dt || !w->dt_bias || !w->a_log || !w->d_skip ||
+        !w->w_out)
+        return fail(SB_EINVAL, "null weight");
+    const void *al[] = {x, conv_state, ssm_state, M_out, y_out, w->w_in, w->conv_w, w->conv_b, w->w_x, w->w_dt,
+                        w->dt_bias, w->a_log, w->d_skip, w->w_out};
+    for (const void *p : al)
+        if (!aligned16(p)) return fail(SB_EINVAL, "tensor base pointers must be 16-byte aligned");
+    const int64_t P = dt_rank + 2 * d_state, rows = B * T;
+    const Range outs[] = {rng("conv_state", conv_state, (size_t)B * d_inner * (d_conv - 1) * 4),
+                          rng("ssm_state", ssm_state, (size_t)B * d_inner * d_state * 4),
+                          rng("M", M_out, (size_t)rows * d_inner * 2), rng("y", y_out, (size_t)rows * d_model * 2)};
+    const Range ins[] = {rng("x", x, (size_t)rows * d_model * 2),
+                         rng("w_in", w->w_in, (size_t)2 * d_inner * d_model * 2),
+                         rng("conv_w", w->conv_w, (size_t)d_inner * d_conv * 4),
+                         rng("conv_b", w->conv_b, (size_t)d_inner * 4), rng("w_x", w->w_x, (size_t)P * d_inner * 2),
+                         rng("w_dt", w->w_dt, (size_t)d_inner * dt_rank * 2),
+                         rng("dt_bias", w->dt_bias, (size_t)d_inner * 4),
+                         rng("a_log", w->a_log, (size_t)d_inner * d_state * 4),
+                         rng("d_skip", w->d_skip, (size_t)d_inner * 4),
+                         rng("w_out", w->w_out, (size_t)d_model * d_inner * 2)};
+    for (size_t i = 0; i < 4; ++i) {
+        for (size_t j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j])) return fail(SB_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (const Range &r : ins)
+            if (overlaps(outs[i], r)) return fail(SB_EINVAL, "%s overlaps %s", outs[i].name, r.name);
+    }
+    const size_t need = mamba_prefill_workspace_bytes(B, T, d_model, d_inner, d_state, dt_rank, d_conv);
+    if (!workspace || workspace_bytes < need)
+        return fail(SB_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(SB_EINVAL, "workspace must be 16-byte aligned");
+    const Range rw = rng("workspace", workspace, need);
+    for (const Range &r : outs)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+    for (const Range &r : ins)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+    if (log_enabled())
+        fprintf(stderr, "[sambay] %s B=%lld T=%lld d_model=%lld d_inner=%lld N=%lld R=%lld K=%lld\n", fn,
+                (long long)B, (long long)T, (long long)d_model, (long long)d_inner, (long long)d_state,
+                (long long)dt_rank, (long long)d_conv);
+    hipError_t e = launch_mamba_prefill(
+        (const bf16_t *)x, (const bf16_t *)w->w_in, w->conv_w, w->conv_b, (const bf16_t *)w->w_x,
+        (const bf16_t *)w->w_dt, w->dt_bias, w->a_log, w->d_skip, (const bf16_t *)w->w_out, conv_state, ssm_state,
+        (bf16_t *)M_out, (bf16_t *)y_out, (int)B, (int)T, (int)d_model, (int)d_inner, (int)d_state, (int)dt_rank,
+        (int)d_conv, workspace, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
 namespace {
 
 // Workspace layout of one cross-decoder step (all reused layer to layer).

@@ -184,10 +184,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
                     x[e] = mm * (x[e] / (1.f + expf(-x[e])));
                 }
             }
-            u32x4 o;
+            if (EPI == EPI_SOFTPLUS) {  // softplus(acc + bias[n]), the SSM layer's step sizes
+                const float *bias = reinterpret_cast<const float *>(aux);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-            if (m < rows && n < N) *reinterpret_cast<u32x4 *>(out + (size_t)m * N + n) = o;
+                for (int e = 0; e < 8; ++e) {
+                    const float a = x[e] + (n + e < N ? bias[n + e] : 0.f);
+                    // log(1 + e^a) with the hardware exp/log: exact enough where it matters (|a| <= 20);
+                    // a itself above, e^a below -15 (1 + e^a would round to 1).
+                    x[e] = a > 20.f ? a : (a < -15.f ? __expf(a) : __logf(1.f + __expf(a)));
+                }
+            }
+            if (EPI == EPI_F32 || EPI == EPI_SOFTPLUS) {  // fp32 output: out is a float array
+                if (m < rows && n < N) {
+                    float *of = reinterpret_cast<float *>(out) + (size_t)m * N + n;
+                    *reinterpret_cast<f32x4 *>(of) = (f32x4){x[0], x[1], x[2], x[3]};
+                    *reinterpret_cast<f32x4 *>(of + 4) = (f32x4){x[4], x[5], x[6], x[7]};
+                }
+            } else {
+                u32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+                if (m < rows && n < N) *reinterpret_cast<u32x4 *>(out + (size_t)m * N + n) = o;
+            }
         }
         wave_lds_fence();
     }
@@ -201,6 +219,12 @@ hipError_t launch_tile(const bf16_t *X, const bf16_t *W, int rows, int N, int K,
     if (epi == EPI_GATE)
         hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_GATE>), dim3(tiles), dim3(64 * WGM * WGN), 0,
                            stream, X, W, rows, N, K, out, aux);
+    else if (epi == EPI_F32)
+        hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_F32>), dim3(tiles), dim3(64 * WGM * WGN), 0,
+                           stream, X, W, rows, N, K, out, aux);
+    else if (epi == EPI_SOFTPLUS)
+        hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_SOFTPLUS>), dim3(tiles),
+                           dim3(64 * WGM * WGN), 0, stream, X, W, rows, N, K, out, aux);
     else
         hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_BF16>), dim3(tiles), dim3(64 * WGM * WGN), 0,
                            stream, X, W, rows, N, K, out, aux);

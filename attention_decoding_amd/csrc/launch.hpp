@@ -89,6 +89,17 @@ hipError_t launch_mamba_scan(const float *xz, int ldxz, const float *u, const fl
                              float *ssm_state, bf16_t *M_out, bf16_t *g_hi, bf16_t *g_lo, int T, int d_inner, int NS,
                              hipStream_t stream);
 
+// The SSM layer over T prompt tokens (x [B·T, d_model] rows): GEMM
+// projections, the convolution and the selective scan over the sequence;
+// conv_state / ssm_state in and out; M [B·T, d_inner], y [B·T, d_model].
+// Requires d_model, d_inner, R multiples of 64, NS in {8, 16, 32, 64}.
+size_t mamba_prefill_workspace_need(int64_t B, int64_t T, int64_t d_inner, int64_t d_state, int64_t dt_rank);
+hipError_t launch_mamba_prefill(const bf16_t *x, const bf16_t *W_in, const float *conv_w, const float *conv_b,
+                                const bf16_t *W_x, const bf16_t *W_dt, const float *dt_bias, const float *A_log,
+                                const float *Dp, const bf16_t *W_out, float *conv_state, float *ssm_state,
+                                bf16_t *M_out, bf16_t *y_out, int B, int T, int d_model, int d_inner, int NS, int R,
+                                int K, void *workspace, hipStream_t stream);
+
 // ------------------------------------------------ skinny (decode) products
 // out[t, n] = epi( Σ_k X[t, k] · W[n, k] ) for t < T <= 64 tokens.
 enum Epilogue {
@@ -96,7 +107,8 @@ enum Epilogue {
     EPI_BF16 = 1,   // out bf16
     EPI_GATE = 2,   // out bf16 = aux[t, n] · SiLU(acc)   (aux = M, bf16)
     EPI_RESID = 3,  // out bf16 = out[t, n] + acc         (in-place residual add)
-    EPI_SWIGLU = 4  // out bf16 = SiLU(X W^T) · (X W_b^T): gate and up in one pass (W_b required)
+    EPI_SWIGLU = 4,  // out bf16 = SiLU(X W^T) · (X W_b^T): gate and up in one pass (W_b required)
+    EPI_SOFTPLUS = 5 // prefill GEMM only: out fp32 = softplus(acc + bias[n]), bias = aux as fp32 [N]
 };
 constexpr int kSkinnyMaxTokens = 64;
 
@@ -138,6 +150,8 @@ size_t skinny_partial_bytes_dual(int T, int N, const SkinnyPlan &p);
 
 // ------------------------------------------------------- prefill product
 // out[r, n] = epi( Σ_k X[r, k] · W[n, k] ), any row count, N % 64 == 0, K % 64 == 0.
+// epi: EPI_BF16, EPI_GATE (aux = M), EPI_F32 or EPI_SOFTPLUS (out is then a
+// float array; EPI_SOFTPLUS reads its fp32 bias [N] through aux).
 hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
                        const bf16_t *aux, hipStream_t stream);
 

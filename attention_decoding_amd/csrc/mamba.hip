@@ -190,6 +190,199 @@ __global__ __launch_bounds__(64 * TW) void mamba_scan_kernel(
     store_pair(g_hi, g_lo, tc, m * silu(xz[(size_t)t * ldxz + d_inner + c]));
 }
 
+// ------------------------------------------------------------------ prefill
+// The same layer over T prompt tokens: the projections are MFMA GEMMs over
+// all B·T rows (bf16 operands), the convolution and the scan run over the
+// sequence.
+
+// Grid (channel blocks, token blocks of kConvRun, b): each thread runs the
+// convolution over kConvRun consecutive tokens of one channel with the
+// window in registers: u = SiLU(conv_b + Σ_k conv_w[k] · x̃[t - K + 1 + k]),
+// x̃ the x branch of the input projection, positions before the prompt
+// taken from the stored window (read only here).
+constexpr int kConvRun = 8;
+__global__ __launch_bounds__(kConvThreads) void mamba_conv_seq_kernel(const bf16_t *__restrict__ xz, int ldxz,
+                                                                      const float *__restrict__ conv_state,
+                                                                      const float *__restrict__ conv_w,
+                                                                      const float *__restrict__ conv_b,
+                                                                      bf16_t *__restrict__ u, int T, int d_inner,
+                                                                      int K) {
+    const int c = blockIdx.x * kConvThreads + threadIdx.x, t0 = blockIdx.y * kConvRun, b = blockIdx.z;
+    if (c >= d_inner) return;
+    float w[kMaxConv], win[kMaxConv + kConvRun];
+#pragma unroll
+    for (int k = 0; k < kMaxConv; ++k) w[k] = k < K ? conv_w[(size_t)c * K + k] : 0.f;
+    // win[j] = x̃[t0 - (K - 1) + j] for j < K - 1 + kConvRun
+#pragma unroll
+    for (int j = 0; j < kMaxConv - 1 + kConvRun; ++j) {
+        if (j >= K - 1 + kConvRun) break;
+        const int i = t0 - (K - 1) + j;
+        float x = 0.f;
+        if (i >= 0 && i < T) x = bf16_to_f32(xz[((size_t)b * T + i) * ldxz + c]);
+        else if (i < 0) x = conv_state[((size_t)b * d_inner + c) * (K - 1) + (K - 1 + i)];
+        win[j] = x;
+    }
+    const float bias = conv_b[c];
+#pragma unroll
+    for (int e = 0; e < kConvRun; ++e) {
+        if (t0 + e >= T) break;
+        float acc = bias;
+#pragma unroll
+        for (int k = 0; k < kMaxConv; ++k)
+            if (k < K) acc += w[k] * win[e + k];
+        u[((size_t)b * T + t0 + e) * d_inner + c] = f32_to_bf16(acc / (1.f + __expf(-acc)));
+    }
+}
+
+// One thread per (b, channel): the stored window after the prompt (its last
+// K - 1 inputs, or older stored ones when T < K - 1), updated in place.
+__global__ __launch_bounds__(kConvThreads) void mamba_conv_state_kernel(const bf16_t *__restrict__ xz, int ldxz,
+                                                                        float *__restrict__ conv_state, int B, int T,
+                                                                        int d_inner, int K) {
+    const size_t idx = (size_t)blockIdx.x * kConvThreads + threadIdx.x;
+    if (idx >= (size_t)B * d_inner || K < 2) return;
+    const int b = (int)(idx / d_inner), c = (int)(idx % d_inner);
+    float *st = conv_state + idx * (K - 1);
+    float old[kMaxConv], nw[kMaxConv];
+#pragma unroll
+    for (int k = 0; k < kMaxConv - 1; ++k)
+        if (k < K - 1) old[k] = st[k];
+#pragma unroll
+    for (int k = 0; k < kMaxConv - 1; ++k)
+        if (k < K - 1) {
+            const int i = T - (K - 1) + k;  // position of the k-th kept input
+            nw[k] = i >= 0 ? bf16_to_f32(xz[((size_t)b * T + i) * ldxz + c]) : old[K - 1 + i];
+        }
+#pragma unroll
+    for (int k = 0; k < kMaxConv - 1; ++k)
+        if (k < K - 1) st[k] = nw[k];
+}
+
+// dst[r, :cols] = src[r, :cols] for r < rows_src, zeros for rows_src <= r < rows_dst
+// (rows of ld_src / ld_dst bf16; 16-byte pieces, cols % 8 == 0).
+__global__ __launch_bounds__(256) void copy_rows_kernel(const bf16_t *__restrict__ src, int ld_src,
+                                                        bf16_t *__restrict__ dst, int ld_dst, int rows_src,
+                                                        int rows_dst, int cols) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x, per = (size_t)cols / 8;
+    if (idx >= (size_t)rows_dst * per) return;
+    const size_t r = idx / per, c8 = 8 * (idx % per);
+    const u32x4 v = r < (size_t)rows_src ? ld16(src + r * ld_src + c8) : (u32x4){0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4 *>(dst + r * ld_dst + c8) = v;
+}
+
+// The selective scan over the prompt, in chunks of Lc tokens so that every
+// chunk of every channel runs in parallel:
+//   A: each chunk from a zero state: its end state S and its total decay
+//      P = exp(A · ΣΔ) per (channel, state);
+//   B: per (channel, state), in chunk order: the state entering each chunk
+//      (init_k = s; s = P_k·s + S_k) and the state after the prompt;
+//   C: each chunk again from its entering state, with the readout
+//      M_t = Σ_n C_n s_n + D·u_t and the gate g_t = M_t·SiLU(z_t).
+// A lane holds NPL states of one channel in registers (G = NS / NPL lanes per
+// channel, adjacent, their readouts summed by shuffles); a one-wave
+// workgroup covers 64 / G channels of one chunk.  Δ, u, z are read per lane
+// (consecutive channels: coalesced); B and C of a token are the same for the
+// whole wave when G == 1 (scalar loads).  Steps past the prompt's end run
+// with Δ = 0, which leaves the state as it is, so the loop has no tail.
+constexpr int kScanUnroll = 8;
+
+__host__ __device__ constexpr int scan_lanes_per_channel(int NS) { return NS > 16 ? NS / 16 : 1; }
+
+template <int NPL, int G, bool OUT>
+__global__ __launch_bounds__(64) void mamba_chunk_scan_kernel(
+    const bf16_t *__restrict__ xz, int ldxz, const bf16_t *__restrict__ u, const bf16_t *__restrict__ xdbl, int P,
+    int R, const float *__restrict__ delta, const float *__restrict__ A_log, const float *__restrict__ Dp,
+    float *__restrict__ SP,  // [B, nchunks, d_inner, NS] x2: S (A) / entering state (C), then P (A)
+    bf16_t *__restrict__ M_out, bf16_t *__restrict__ g_out, int T, int Lc, int d_inner) {
+    constexpr int NS = NPL * G, U = kScanUnroll;
+    const int k = blockIdx.x, b = blockIdx.z, nchunks = gridDim.x;
+    const int gi = threadIdx.x % G, c = blockIdx.y * (64 / G) + threadIdx.x / G;
+    const int t0 = k * Lc, len = min(Lc, T - t0);
+    const size_t row0 = (size_t)b * T + t0;
+    const size_t spi = (((size_t)b * nchunks + k) * d_inner + c) * NS + NPL * gi;
+    const size_t half = (size_t)gridDim.z * nchunks * d_inner * NS;  // offset of the P array
+    float a2[NPL], st[NPL];
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) {
+        a2[q] = -expf(A_log[(size_t)c * NS + NPL * gi + q]) * kLog2e;
+        st[q] = OUT ? SP[spi + q] : 0.f;
+    }
+    const float dsk = OUT ? Dp[c] : 0.f;
+    float dsum = 0.f;
+    for (int tb = 0; tb < len; tb += U) {
+        float dl[U], uu[U], zz[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int t = min(tb + i, len - 1);
+            const size_t row = row0 + t;
+            const float d = delta[row * d_inner + c];
+            dl[i] = tb + i < len ? d : 0.f;
+            uu[i] = bf16_to_f32(u[row * d_inner + c]);
+            if (OUT) zz[i] = bf16_to_f32(xz[row * ldxz + d_inner + c]);
+        }
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int t = min(tb + i, len - 1);
+            const bf16_t *bc = xdbl + (row0 + t) * P + R + NPL * gi;
+            const float du = dl[i] * uu[i];
+            float m = 0.f;
+#pragma unroll
+            for (int q2 = 0; q2 < NPL; q2 += 8) {
+                const u32x4 bw = ld16(bc + q2);
+                const float bq[8] = {lo_bf16(bw[0]), hi_bf16(bw[0]), lo_bf16(bw[1]), hi_bf16(bw[1]),
+                                     lo_bf16(bw[2]), hi_bf16(bw[2]), lo_bf16(bw[3]), hi_bf16(bw[3])};
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    st[q2 + q] = exp2_fast(dl[i] * a2[q2 + q]) * st[q2 + q] + du * bq[q];
+                if (OUT) {
+                    const u32x4 cw = ld16(bc + NS + q2);
+                    const float cq[8] = {lo_bf16(cw[0]), hi_bf16(cw[0]), lo_bf16(cw[1]), hi_bf16(cw[1]),
+                                         lo_bf16(cw[2]), hi_bf16(cw[2]), lo_bf16(cw[3]), hi_bf16(cw[3])};
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) m += cq[q] * st[q2 + q];
+                }
+            }
+            if (OUT) {
+#pragma unroll
+                for (int x = 1; x < G; x <<= 1) m += __shfl_xor(m, x);
+                if (gi == 0 && tb + i < len) {
+                    const size_t o = (row0 + tb + i) * d_inner + c;
+                    const float mm = m + dsk * uu[i];
+                    M_out[o] = f32_to_bf16(mm);
+                    g_out[o] = f32_to_bf16(mm * (zz[i] / (1.f + __expf(-zz[i]))));
+                }
+            } else {
+                dsum += dl[i];
+            }
+        }
+    }
+    if (!OUT) {
+#pragma unroll
+        for (int q = 0; q < NPL; ++q) {
+            SP[spi + q] = st[q];
+            SP[half + spi + q] = exp2_fast(a2[q] * dsum);
+        }
+    }
+}
+
+// One thread per (b, channel, state): the state entering each chunk, in
+// order, written over that chunk's S; the state after the prompt.
+__global__ __launch_bounds__(256) void mamba_chunk_combine_kernel(float *__restrict__ SP,
+                                                                  float *__restrict__ ssm_state, int B, int nchunks,
+                                                                  int d_inner, int NS) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x, per = (size_t)d_inner * NS;
+    if (idx >= (size_t)B * per) return;
+    const size_t b = idx / per, cn = idx % per, half = (size_t)B * nchunks * per;
+    float s = ssm_state[idx];
+    for (int k = 0; k < nchunks; ++k) {
+        const size_t i = (b * nchunks + k) * per + cn;
+        const float S = SP[i], Pk = SP[half + i];
+        SP[i] = s;
+        s = Pk * s + S;
+    }
+    ssm_state[idx] = s;
+}
+
 }  // namespace
 
 hipError_t launch_mamba_conv(const float *xz, int ldxz, float *conv_state, const float *conv_w, const float *conv_b,
@@ -224,6 +417,98 @@ hipError_t launch_mamba_scan(const float *xz, int ldxz, const float *u, const fl
 #undef SB_SCAN_TW
 #undef SB_SCAN
     return hipGetLastError();
+}
+
+// Tokens per scan chunk: 64, halved (to 16 at least) while the scan would
+// have fewer than 8192 waves (32 per CU).
+static int mamba_scan_chunk(int64_t B, int64_t T, int64_t d_inner, int64_t NS) {
+    int Lc = 64;
+    const int64_t waves = B * d_inner * scan_lanes_per_channel((int)NS) / 64;
+    while (Lc > 16 && waves * ((T + Lc - 1) / Lc) < 8192) Lc /= 2;
+    return Lc;
+}
+
+size_t mamba_prefill_workspace_need(int64_t B, int64_t T, int64_t d_inner, int64_t d_state, int64_t dt_rank) {
+    const int64_t rows = B * T, P = dt_rank + 2 * d_state, Pp = (P + 63) / 64 * 64;
+    auto r = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const int64_t Lc = mamba_scan_chunk(B, T, d_inner, d_state), nch = (T + Lc - 1) / Lc;
+    return r((size_t)rows * 2 * d_inner * 2) + r((size_t)rows * d_inner * 2) + r((size_t)Pp * d_inner * 2) +
+           r((size_t)rows * Pp * 2) + r((size_t)rows * dt_rank * 2) + r((size_t)rows * d_inner * 4) +
+           r((size_t)rows * d_inner * 2) + r((size_t)2 * B * nch * d_inner * d_state * 4);
+}
+
+hipError_t launch_mamba_prefill(const bf16_t *x, const bf16_t *W_in, const float *conv_w, const float *conv_b,
+                                const bf16_t *W_x, const bf16_t *W_dt, const float *dt_bias, const float *A_log,
+                                const float *Dp, const bf16_t *W_out, float *conv_state, float *ssm_state,
+                                bf16_t *M_out, bf16_t *y_out, int B, int T, int d_model, int d_inner, int NS, int R,
+                                int K, void *workspace, hipStream_t stream) {
+    const int rows = B * T, P = R + 2 * NS, Pp = (P + 63) / 64 * 64, di2 = 2 * d_inner;
+    auto r = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    char *ws = reinterpret_cast<char *>(workspace);
+    bf16_t *xz = reinterpret_cast<bf16_t *>(ws);
+    ws += r((size_t)rows * di2 * 2);
+    bf16_t *u = reinterpret_cast<bf16_t *>(ws);
+    ws += r((size_t)rows * d_inner * 2);
+    bf16_t *wxp = reinterpret_cast<bf16_t *>(ws);
+    ws += r((size_t)Pp * d_inner * 2);
+    bf16_t *xdbl = reinterpret_cast<bf16_t *>(ws);
+    ws += r((size_t)rows * Pp * 2);
+    bf16_t *delta = reinterpret_cast<bf16_t *>(ws);
+    ws += r((size_t)rows * R * 2);
+    float *dpre = reinterpret_cast<float *>(ws);
+    ws += r((size_t)rows * d_inner * 4);
+    bf16_t *g = reinterpret_cast<bf16_t *>(ws);
+    ws += r((size_t)rows * d_inner * 2);
+    float *sp = reinterpret_cast<float *>(ws);
+
+    auto blocks = [](size_t n, int per) { return dim3((unsigned)((n + per - 1) / per)); };
+    hipError_t e = launch_gemm(x, W_in, rows, di2, d_model, EPI_BF16, xz, nullptr, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mamba_conv_seq_kernel, dim3((unsigned)((d_inner + kConvThreads - 1) / kConvThreads),
+                                                   (unsigned)((T + kConvRun - 1) / kConvRun), (unsigned)B),
+                       dim3(kConvThreads), 0, stream, xz, di2, conv_state, conv_w, conv_b, u, T, d_inner, K);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(mamba_conv_state_kernel, blocks((size_t)B * d_inner, kConvThreads), dim3(kConvThreads), 0,
+                       stream, xz, di2, conv_state, B, T, d_inner, K);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // W_x padded to a multiple of 64 rows (zeros), then [δ | B | C | 0] = u W_x^T.
+    hipLaunchKernelGGL(copy_rows_kernel, blocks((size_t)Pp * d_inner / 8, 256), dim3(256), 0, stream, W_x, d_inner,
+                       wxp, d_inner, P, Pp, d_inner);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_gemm(u, wxp, rows, Pp, d_inner, EPI_BF16, xdbl, nullptr, stream)) != hipSuccess) return e;
+    // δ gathered into its own rows, then the step projection in fp32.
+    hipLaunchKernelGGL(copy_rows_kernel, blocks((size_t)rows * R / 8, 256), dim3(256), 0, stream, xdbl, Pp, delta, R,
+                       rows, rows, R);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // Δ = softplus(δ W_dt^T + dt_bias) in the GEMM's epilogue (fp32).
+    e = launch_gemm(delta, W_dt, rows, d_inner, R, EPI_SOFTPLUS, reinterpret_cast<bf16_t *>(dpre),
+                    reinterpret_cast<const bf16_t *>(dt_bias), stream);
+    if (e != hipSuccess) return e;
+    // The chunked scan (dpre now holds Δ; SP after g in the workspace).
+    const int Lc = mamba_scan_chunk(B, T, d_inner, NS), nch = (T + Lc - 1) / Lc;
+    const dim3 cgrid((unsigned)nch, (unsigned)(d_inner * scan_lanes_per_channel(NS) / 64), (unsigned)B);
+#define SB_CHUNK(N_, OUT_)                                                                                          \
+    hipLaunchKernelGGL((mamba_chunk_scan_kernel<N_ / scan_lanes_per_channel(N_), scan_lanes_per_channel(N_), OUT_>), \
+                       cgrid, dim3(64), 0, stream, xz, di2, u, xdbl, Pp, R, dpre, A_log, Dp, sp, M_out, g, T, Lc,    \
+                       d_inner)
+#define SB_CHUNK_NS(OUT_)                  \
+    switch (NS) {                          \
+        case 8: SB_CHUNK(8, OUT_); break;  \
+        case 16: SB_CHUNK(16, OUT_); break; \
+        case 32: SB_CHUNK(32, OUT_); break; \
+        case 64: SB_CHUNK(64, OUT_); break; \
+        default: return hipErrorInvalidValue; \
+    }
+    SB_CHUNK_NS(false);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(mamba_chunk_combine_kernel, blocks((size_t)B * d_inner * NS, 256), dim3(256), 0, stream, sp,
+                       ssm_state, B, nch, d_inner, NS);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    SB_CHUNK_NS(true);
+#undef SB_CHUNK_NS
+#undef SB_CHUNK
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_gemm(g, W_out, rows, d_model, d_inner, EPI_BF16, y_out, nullptr, stream);
 }
 
 }  // namespace sambay

@@ -271,6 +271,21 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> 
             "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
         del m
     del msets
+    # SSM layer over the prompt: 4 x 2048 tokens at the model width.
+    c = workload.MAMBA_DECODE
+    dm, di, N, R, K = c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"], c["d_conv"]
+    Bp, Tp = workload.ATTN_PREFILL["B"], workload.ATTN_PREFILL["T"]
+    m = workload.mamba_inputs(Bp, dm, di, N, R, K, seed=95, device=dev)
+    xs = workload.normal((Bp, Tp, dm), seed=96, device=dev)
+    Mo = torch.empty(Bp, Tp, di, dtype=torch.bfloat16, device=dev)
+    yo = torch.empty(Bp, Tp, dm, dtype=torch.bfloat16, device=dev)
+    ms = time_calls(lambda i: sb.mamba_prefill(xs, m.w, m.conv_state, m.ssm_state, Mo, yo), 10)
+    rows = Bp * Tp
+    flops = 2.0 * rows * (2 * di * dm + ((R + 2 * N + 63) // 64 * 64) * di + di * R + dm * di)
+    res["mamba_prefill_B%d_T%d" % (Bp, Tp)] = {
+        "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+        "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4)}
+    del m, xs, Mo, yo
     # Prefill attention over the prompt: 4 x 2048 tokens, window 256 (the
     # self-decoder's sliding-window layers), and plain causal at 1 x 2048.
     c = workload.ATTN_PREFILL

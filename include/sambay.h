@@ -265,6 +265,25 @@ sb_status mamba_decode_step(const void *x, const sb_mamba_weights *w, float *con
                             int64_t dt_rank, int64_t d_conv, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/* --------------------------------------------- SSM layer over the prompt --
+ * The same layer as mamba_decode_step over T prompt tokens in one call (the
+ * self-decoder's SSM layers in a YOCO-style prefill, which stays linear in T,
+ * [Notes] sections 领域现状 and 现有痛点): equal, up to rounding, to T
+ * successive mamba_decode_step calls on x[:, 0], ..., x[:, T-1] starting from
+ * the given states.  x [B, T, d_model]; M_out [B, T, d_inner] and y_out
+ * [B, T, d_model] for every token; conv_state and ssm_state in and out.  The
+ * projections are MFMA GEMMs over the B·T rows with bf16 operands (xz, u,
+ * [δ | B | C] and the gated readout are stored bf16; the step projection
+ * and the scan are fp32); the convolution and the selective scan run over
+ * the sequence.  Additionally requires dt_rank % 64 == 0.
+ * Errors: as mamba_decode_step, plus SB_EUNSUPPORTED for T > 65535 or
+ * B·T >= 2^31.  B == 0 or T == 0 is a no-op. */
+size_t mamba_prefill_workspace_bytes(int64_t B, int64_t T, int64_t d_model, int64_t d_inner, int64_t d_state,
+                                     int64_t dt_rank, int64_t d_conv);
+sb_status mamba_prefill(const void *x, const sb_mamba_weights *w, float *conv_state, float *ssm_state, void *M_out,
+                        void *y_out, int64_t B, int64_t T, int64_t d_model, int64_t d_inner, int64_t d_state,
+                        int64_t dt_rank, int64_t d_conv, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------- complete cross-decoder layer --
  * The pages define the GMU and the shared-cache cross-attention but not the
  * rest of a layer; this step takes the plain pre-norm Transformer reading.

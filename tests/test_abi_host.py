@@ -337,3 +337,17 @@ def test_attn_prefill_validation(sb):
     assert call(T=0) == sb.SB_OK and call(B=0) == sb.SB_OK
     assert lib.attn_prefill_workspace_bytes(4, 2048, 8, 128) == 4 * 8 * 128 * 2048 * 2
     assert lib.attn_prefill_workspace_bytes(1, 33, 1, 128) == 128 * 64 * 2      # 33 keys padded to 64
+
+
+def test_mamba_prefill_validation(sb):
+    """Every call here fails validation (or is a no-op)."""
+    G = 1 << 30
+    w = sb.SbMambaWeights(*[(i + 10) * G for i in range(9)])
+    call = lambda **kw: sb.lib.mamba_prefill(1 * G, ctypes.byref(w), 2 * G, 3 * G, kw.get("M", 4 * G), 5 * G,
+                                             kw.get("B", 4), kw.get("T", 2048), 3072, 6144, 16, kw.get("R", 192), 4,
+                                             6 * G, kw.get("wsb", 1 << 34), None)
+    assert call(R=184) == sb.SB_EUNSUPPORTED           # a multiple of 8 but not of 64
+    assert call(M=5 * G + 64) == sb.SB_EINVAL           # M overlaps y
+    assert call(wsb=1 << 20) == sb.SB_EWORKSPACE
+    assert call(T=0) == sb.SB_OK and call(B=0) == sb.SB_OK
+    assert sb.lib.mamba_prefill_workspace_bytes(4, 2048, 3072, 6144, 16, 192, 4) > 4 * 2048 * 6144 * 8
