@@ -56,7 +56,7 @@ template <int BM, int BN, int WGM, int WGN, int NS, int BK, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__restrict__ X,
                                                                 const bf16_t *__restrict__ W, int rows, int N,
                                                                 int K, bf16_t *__restrict__ out,
-                                                                const bf16_t *__restrict__ aux) {
+                                                                const bf16_t *__restrict__ aux, int ksplit) {
     constexpr int NWAVES = WGM * WGN;
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -75,7 +75,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
 
     const int tiles_m = (rows + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
-    int pid = blockIdx.x;
+    // Split K (EPI_F32 only): slice blockIdx.x / ntiles of K / ksplit, its
+    // partial sums to the slice's own [rows, N] block of out.
+    const int kslice = blockIdx.x / ntiles, Ks = K / ksplit;
+    int pid = blockIdx.x % ntiles;
     if (ntiles % kXcds == 0) pid = (pid % kXcds) * (ntiles / kXcds) + pid / kXcds;
     const int group = pid / (kGroupM * tiles_n);
     const int first_m = group * kGroupM;
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
         const int logical = swz<BK>(r, lane % CPR);
         const bf16_t *base = r < BM ? X + (size_t)min(bm + r, rows - 1) * K
                                     : W + (size_t)min(bn + r - BM, N - 1) * K;
-        src[q] = base + 8 * logical;
+        src[q] = base + (size_t)kslice * Ks + 8 * logical;
     }
     auto issue = [&](int kt, int slot) {
 #pragma unroll
@@ -109,7 +112,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    const int KT = K / BK;
+    // The lane's 8 output columns in the epilogue (the same for every vector
+    // it stores): their softplus biases are loaded before the main loop.
+    constexpr int VPR = TN / 8;                   // 8-column vectors per row
+    static_assert(64 % VPR == 0, "epilogue columns");
+    const int n_lane = bn + wn * TN + 8 * (lane % VPR);
+    float bias[8];
+    if (EPI == EPI_SOFTPLUS) {
+        f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
+        if (n_lane < N) {
+            b0 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(aux) + n_lane);
+            b1 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(aux) + n_lane + 4);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bias[e] = b0[e], bias[4 + e] = b1[e];
+    }
+
+    const int KT = Ks / BK;
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
         if (s < KT) issue(s, s);
@@ -146,7 +165,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     // column.  Each wave parks 32 rows of its block in its own LDS area, then
     // every lane handles 8 consecutive columns: one 16-byte load of M (gate)
     // and one 16-byte store per vector instead of 2-byte accesses.
-    constexpr int VPR = TN / 8;                   // 8-column vectors per row
     constexpr int VPL = 32 * VPR / 64;            // vectors per lane per 32 rows
     static_assert(VPL * 64 == 32 * VPR, "epilogue shape");
     float *stage = reinterpret_cast<float *>(lds_raw) + wave * 32 * SROW;
@@ -185,10 +203,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
                 }
             }
             if (EPI == EPI_SOFTPLUS) {  // softplus(acc + bias[n]), the SSM layer's step sizes
-                const float *bias = reinterpret_cast<const float *>(aux);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float a = x[e] + (n + e < N ? bias[n + e] : 0.f);
+                    const float a = x[e] + bias[e];
                     // log(1 + e^a) with the hardware exp/log: exact enough where it matters (|a| <= 20);
                     // a itself above, e^a below -15 (1 + e^a would round to 1).
                     x[e] = a > 20.f ? a : (a < -15.f ? __expf(a) : __logf(1.f + __expf(a)));
@@ -196,7 +213,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
             }
             if (EPI == EPI_F32 || EPI == EPI_SOFTPLUS) {  // fp32 output: out is a float array
                 if (m < rows && n < N) {
-                    float *of = reinterpret_cast<float *>(out) + (size_t)m * N + n;
+                    float *of = reinterpret_cast<float *>(out) + ((size_t)kslice * rows + m) * N + n;
                     *reinterpret_cast<f32x4 *>(of) = (f32x4){x[0], x[1], x[2], x[3]};
                     *reinterpret_cast<f32x4 *>(of + 4) = (f32x4){x[4], x[5], x[6], x[7]};
                 }
@@ -213,29 +230,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
 
 template <int BM, int BN, int WGM, int WGN, int NS, int BK>
 hipError_t launch_tile(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
-                     const bf16_t *aux, hipStream_t stream) {
-    const int tiles = ((rows + BM - 1) / BM) * ((N + BN - 1) / BN);
+                     const bf16_t *aux, int ksplit, hipStream_t stream) {
+    const int tiles = ((rows + BM - 1) / BM) * ((N + BN - 1) / BN) * ksplit;
     TimingScope ts(kTimeGemm, stream);
     if (epi == EPI_GATE)
         hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_GATE>), dim3(tiles), dim3(64 * WGM * WGN), 0,
-                           stream, X, W, rows, N, K, out, aux);
+                           stream, X, W, rows, N, K, out, aux, ksplit);
     else if (epi == EPI_F32)
         hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_F32>), dim3(tiles), dim3(64 * WGM * WGN), 0,
-                           stream, X, W, rows, N, K, out, aux);
+                           stream, X, W, rows, N, K, out, aux, ksplit);
     else if (epi == EPI_SOFTPLUS)
         hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_SOFTPLUS>), dim3(tiles),
-                           dim3(64 * WGM * WGN), 0, stream, X, W, rows, N, K, out, aux);
+                           dim3(64 * WGM * WGN), 0, stream, X, W, rows, N, K, out, aux, ksplit);
     else
         hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_BF16>), dim3(tiles), dim3(64 * WGM * WGN), 0,
-                           stream, X, W, rows, N, K, out, aux);
+                           stream, X, W, rows, N, K, out, aux, ksplit);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
-                       const bf16_t *aux, hipStream_t stream) {
-    return launch_tile<128, 128, 2, 2, 2, 64>(X, W, rows, N, K, epi, out, aux, stream);
+                       const bf16_t *aux, hipStream_t stream, int ksplit) {
+    if (ksplit < 1 || K % (64 * ksplit) != 0 || (ksplit > 1 && epi != EPI_F32)) return hipErrorInvalidValue;
+    return launch_tile<128, 128, 2, 2, 2, 64>(X, W, rows, N, K, epi, out, aux, ksplit, stream);
 }
 
 }  // namespace sambay

@@ -149,11 +149,13 @@ SkinnyPlan skinny_plan_dual(int T, int N, int K);
 size_t skinny_partial_bytes_dual(int T, int N, const SkinnyPlan &p);
 
 // ------------------------------------------------------- prefill product
-// out[r, n] = epi( Σ_k X[r, k] · W[n, k] ), any row count, N % 64 == 0, K % 64 == 0.
+// out[r, n] = epi( Σ_k X[r, k] · W[n, k] ), any row count, N % 8 == 0, K % 64 == 0.
 // epi: EPI_BF16, EPI_GATE (aux = M), EPI_F32 or EPI_SOFTPLUS (out is then a
-// float array; EPI_SOFTPLUS reads its fp32 bias [N] through aux).
+// float array; EPI_SOFTPLUS reads its fp32 bias [N] through aux).  ksplit > 1
+// (EPI_F32 only, K % (64·ksplit) == 0): slice s of K writes its partial sums
+// to out + s·rows·N.
 hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
-                       const bf16_t *aux, hipStream_t stream);
+                       const bf16_t *aux, hipStream_t stream, int ksplit = 1);
 
 // ------------------------------------------------------------- RMSNorm
 // out_hi + out_lo = h[r, :] / sqrt(mean(h[r, :]^2) + eps) * g, d % 8 == 0.

@@ -195,43 +195,87 @@ __global__ __launch_bounds__(64 * TW) void mamba_scan_kernel(
 // all B·T rows (bf16 operands), the convolution and the scan run over the
 // sequence.
 
-// Grid (channel blocks, token blocks of kConvRun, b): each thread runs the
-// convolution over kConvRun consecutive tokens of one channel with the
-// window in registers: u = SiLU(conv_b + Σ_k conv_w[k] · x̃[t - K + 1 + k]),
-// x̃ the x branch of the input projection, positions before the prompt
-// taken from the stored window (read only here).
+// Grid (blocks of 8·256 channels, token blocks of kConvRun, b): each thread
+// runs the convolution over kConvRun consecutive tokens of 8 adjacent
+// channels with the window in registers (16-byte loads and stores):
+// u = SiLU(conv_b + Σ_k conv_w[k] · x̃[t - K + 1 + k]), x̃ the x branch of
+// the input projection, positions before the prompt taken from the stored
+// window (read only here).
 constexpr int kConvRun = 8;
+template <int K>
 __global__ __launch_bounds__(kConvThreads) void mamba_conv_seq_kernel(const bf16_t *__restrict__ xz, int ldxz,
                                                                       const float *__restrict__ conv_state,
                                                                       const float *__restrict__ conv_w,
                                                                       const float *__restrict__ conv_b,
-                                                                      bf16_t *__restrict__ u, int T, int d_inner,
-                                                                      int K) {
-    const int c = blockIdx.x * kConvThreads + threadIdx.x, t0 = blockIdx.y * kConvRun, b = blockIdx.z;
+                                                                      bf16_t *__restrict__ u, int T, int d_inner) {
+    const int c = 8 * (blockIdx.x * kConvThreads + threadIdx.x), t0 = blockIdx.y * kConvRun, b = blockIdx.z;
     if (c >= d_inner) return;
-    float w[kMaxConv], win[kMaxConv + kConvRun];
+    constexpr int NW = K - 1 + kConvRun;
+    u32x4 raw[NW];  // raw[j]: the 8 channels of x̃ at position t0 - (K - 1) + j (bf16)
 #pragma unroll
-    for (int k = 0; k < kMaxConv; ++k) w[k] = k < K ? conv_w[(size_t)c * K + k] : 0.f;
-    // win[j] = x̃[t0 - (K - 1) + j] for j < K - 1 + kConvRun
+    for (int j = 0; j < NW; ++j) {
+        const int i = min(max(t0 - (K - 1) + j, 0), T - 1);
+        raw[j] = ld16(xz + ((size_t)b * T + i) * ldxz + c);
+    }
+    float w[K][8], bias[8];
 #pragma unroll
-    for (int j = 0; j < kMaxConv - 1 + kConvRun; ++j) {
-        if (j >= K - 1 + kConvRun) break;
+    for (int e = 0; e < 8; ++e) {
+        bias[e] = conv_b[c + e];
+#pragma unroll
+        for (int k = 0; k < K; ++k) w[k][e] = conv_w[(size_t)(c + e) * K + k];
+    }
+    float win[NW][8];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
         const int i = t0 - (K - 1) + j;
-        float x = 0.f;
-        if (i >= 0 && i < T) x = bf16_to_f32(xz[((size_t)b * T + i) * ldxz + c]);
-        else if (i < 0) x = conv_state[((size_t)b * d_inner + c) * (K - 1) + (K - 1 + i)];
-        win[j] = x;
-    }
-    const float bias = conv_b[c];
 #pragma unroll
-    for (int e = 0; e < kConvRun; ++e) {
-        if (t0 + e >= T) break;
-        float acc = bias;
-#pragma unroll
-        for (int k = 0; k < kMaxConv; ++k)
-            if (k < K) acc += w[k] * win[e + k];
-        u[((size_t)b * T + t0 + e) * d_inner + c] = f32_to_bf16(acc / (1.f + __expf(-acc)));
+        for (int e = 0; e < 8; ++e) {
+            float x = (e & 1) ? hi_bf16(raw[j][e / 2]) : lo_bf16(raw[j][e / 2]);
+            if (i < 0) x = conv_state[((size_t)b * d_inner + c + e) * (K - 1) + (K - 1 + i)];
+            win[j][e] = x;
+        }
     }
+#pragma unroll
+    for (int r = 0; r < kConvRun; ++r) {
+        if (t0 + r >= T) break;
+        u32x4 o;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            float y[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int e = 2 * e2 + h;
+                float acc = bias[e];
+#pragma unroll
+                for (int k = 0; k < K; ++k) acc += w[k][e] * win[r + k][e];
+                y[h] = acc / (1.f + __expf(-acc));
+            }
+            o[e2] = pack_bf16x2(y[0], y[1]);
+        }
+        *reinterpret_cast<u32x4 *>(u + ((size_t)b * T + t0 + r) * d_inner + c) = o;
+    }
+}
+
+// Sum of the step/B/C projection's K-slices (fp32 [ks, rows, P]): δ to its own
+// rows [rows, R] (the step projection's operand), B | C to [rows, 2·NS], bf16.
+__global__ __launch_bounds__(256) void xproj_reduce_kernel(const float *__restrict__ part, int ks, int rows, int P,
+                                                           int R, bf16_t *__restrict__ delta, bf16_t *__restrict__ bc) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x, per = (size_t)P / 8;
+    if (idx >= (size_t)rows * per) return;
+    const size_t r = idx / per;
+    const int c = 8 * (int)(idx % per);
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ks; ++s) {
+        const float *p = part + ((size_t)s * rows + r) * P + c;
+        const f32x4 lo = *reinterpret_cast<const f32x4 *>(p), hi = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] += lo[e], a[4 + e] += hi[e];
+    }
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(a[2 * e], a[2 * e + 1]);
+    bf16_t *dst = c < R ? delta + r * R + c : bc + r * (P - R) + (c - R);
+    *reinterpret_cast<u32x4 *>(dst) = o;
 }
 
 // One thread per (b, channel): the stored window after the prompt (its last
@@ -256,18 +300,6 @@ __global__ __launch_bounds__(kConvThreads) void mamba_conv_state_kernel(const bf
 #pragma unroll
     for (int k = 0; k < kMaxConv - 1; ++k)
         if (k < K - 1) st[k] = nw[k];
-}
-
-// dst[r, :cols] = src[r, :cols] for r < rows_src, zeros for rows_src <= r < rows_dst
-// (rows of ld_src / ld_dst bf16; 16-byte pieces, cols % 8 == 0).
-__global__ __launch_bounds__(256) void copy_rows_kernel(const bf16_t *__restrict__ src, int ld_src,
-                                                        bf16_t *__restrict__ dst, int ld_dst, int rows_src,
-                                                        int rows_dst, int cols) {
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x, per = (size_t)cols / 8;
-    if (idx >= (size_t)rows_dst * per) return;
-    const size_t r = idx / per, c8 = 8 * (idx % per);
-    const u32x4 v = r < (size_t)rows_src ? ld16(src + r * ld_src + c8) : (u32x4){0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4 *>(dst + r * ld_dst + c8) = v;
 }
 
 // The selective scan over the prompt, in chunks of Lc tokens so that every
@@ -428,13 +460,44 @@ static int mamba_scan_chunk(int64_t B, int64_t T, int64_t d_inner, int64_t NS) {
     return Lc;
 }
 
+// K-slices of the step/B/C projection (rows × (R + 2·NS) × d_inner: few
+// output tiles, a long K): up to 512 workgroups, slices of >= 512.
+static int xproj_splits(int64_t rows, int64_t P, int64_t d_inner) {
+    const int64_t tiles = ((rows + 127) / 128) * ((P + 127) / 128);
+    int ks = 1;
+    while (ks < 8 && tiles * ks * 2 <= 512 && d_inner % (64 * ks * 2) == 0 && d_inner / (ks * 2) >= 512) ks *= 2;
+    return ks;
+}
+
+namespace {
+struct PrefillLayout {
+    bf16_t *xz, *u, *bc, *delta, *g;
+    float *part, *dpre, *sp;
+    size_t bytes;
+};
+PrefillLayout prefill_layout(void *base, int64_t B, int64_t T, int64_t d_inner, int64_t NS, int64_t R) {
+    const int64_t rows = B * T, P = R + 2 * NS;
+    const int64_t Lc = mamba_scan_chunk(B, T, d_inner, NS), nch = (T + Lc - 1) / Lc;
+    auto r = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    char *b = reinterpret_cast<char *>(base);
+    size_t off = 0;
+    auto take = [&](size_t n) { char *q = b ? b + off : nullptr; off += r(n); return q; };
+    PrefillLayout L;
+    L.xz = reinterpret_cast<bf16_t *>(take((size_t)rows * 2 * d_inner * 2));
+    L.u = reinterpret_cast<bf16_t *>(take((size_t)rows * d_inner * 2));
+    L.part = reinterpret_cast<float *>(take((size_t)xproj_splits(rows, P, d_inner) * rows * P * 4));
+    L.bc = reinterpret_cast<bf16_t *>(take((size_t)rows * 2 * NS * 2));
+    L.delta = reinterpret_cast<bf16_t *>(take((size_t)rows * R * 2));
+    L.dpre = reinterpret_cast<float *>(take((size_t)rows * d_inner * 4));
+    L.g = reinterpret_cast<bf16_t *>(take((size_t)rows * d_inner * 2));
+    L.sp = reinterpret_cast<float *>(take((size_t)2 * B * nch * d_inner * NS * 4));
+    L.bytes = off;
+    return L;
+}
+}  // namespace
+
 size_t mamba_prefill_workspace_need(int64_t B, int64_t T, int64_t d_inner, int64_t d_state, int64_t dt_rank) {
-    const int64_t rows = B * T, P = dt_rank + 2 * d_state, Pp = (P + 63) / 64 * 64;
-    auto r = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const int64_t Lc = mamba_scan_chunk(B, T, d_inner, d_state), nch = (T + Lc - 1) / Lc;
-    return r((size_t)rows * 2 * d_inner * 2) + r((size_t)rows * d_inner * 2) + r((size_t)Pp * d_inner * 2) +
-           r((size_t)rows * Pp * 2) + r((size_t)rows * dt_rank * 2) + r((size_t)rows * d_inner * 4) +
-           r((size_t)rows * d_inner * 2) + r((size_t)2 * B * nch * d_inner * d_state * 4);
+    return prefill_layout(nullptr, B, T, d_inner, d_state, dt_rank).bytes;
 }
 
 hipError_t launch_mamba_prefill(const bf16_t *x, const bf16_t *W_in, const float *conv_w, const float *conv_b,
@@ -442,43 +505,37 @@ hipError_t launch_mamba_prefill(const bf16_t *x, const bf16_t *W_in, const float
                                 const float *Dp, const bf16_t *W_out, float *conv_state, float *ssm_state,
                                 bf16_t *M_out, bf16_t *y_out, int B, int T, int d_model, int d_inner, int NS, int R,
                                 int K, void *workspace, hipStream_t stream) {
-    const int rows = B * T, P = R + 2 * NS, Pp = (P + 63) / 64 * 64, di2 = 2 * d_inner;
-    auto r = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    char *ws = reinterpret_cast<char *>(workspace);
-    bf16_t *xz = reinterpret_cast<bf16_t *>(ws);
-    ws += r((size_t)rows * di2 * 2);
-    bf16_t *u = reinterpret_cast<bf16_t *>(ws);
-    ws += r((size_t)rows * d_inner * 2);
-    bf16_t *wxp = reinterpret_cast<bf16_t *>(ws);
-    ws += r((size_t)Pp * d_inner * 2);
-    bf16_t *xdbl = reinterpret_cast<bf16_t *>(ws);
-    ws += r((size_t)rows * Pp * 2);
-    bf16_t *delta = reinterpret_cast<bf16_t *>(ws);
-    ws += r((size_t)rows * R * 2);
-    float *dpre = reinterpret_cast<float *>(ws);
-    ws += r((size_t)rows * d_inner * 4);
-    bf16_t *g = reinterpret_cast<bf16_t *>(ws);
-    ws += r((size_t)rows * d_inner * 2);
-    float *sp = reinterpret_cast<float *>(ws);
+    const int rows = B * T, P = R + 2 * NS, di2 = 2 * d_inner;
+    const PrefillLayout L = prefill_layout(workspace, B, T, d_inner, NS, R);
+    bf16_t *xz = L.xz, *u = L.u, *bc = L.bc, *delta = L.delta, *g = L.g;
+    float *dpre = L.dpre, *sp = L.sp;
 
     auto blocks = [](size_t n, int per) { return dim3((unsigned)((n + per - 1) / per)); };
     hipError_t e = launch_gemm(x, W_in, rows, di2, d_model, EPI_BF16, xz, nullptr, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mamba_conv_seq_kernel, dim3((unsigned)((d_inner + kConvThreads - 1) / kConvThreads),
-                                                   (unsigned)((T + kConvRun - 1) / kConvRun), (unsigned)B),
-                       dim3(kConvThreads), 0, stream, xz, di2, conv_state, conv_w, conv_b, u, T, d_inner, K);
+    const dim3 conv_grid((unsigned)((d_inner / 8 + kConvThreads - 1) / kConvThreads),
+                         (unsigned)((T + kConvRun - 1) / kConvRun), (unsigned)B);
+#define SB_CONV(K_)                                                                                                  \
+    case K_:                                                                                                         \
+        hipLaunchKernelGGL(mamba_conv_seq_kernel<K_>, conv_grid, dim3(kConvThreads), 0, stream, xz, di2, conv_state, \
+                           conv_w, conv_b, u, T, d_inner);                                                           \
+        break
+    switch (K) {
+        SB_CONV(1); SB_CONV(2); SB_CONV(3); SB_CONV(4); SB_CONV(5); SB_CONV(6); SB_CONV(7); SB_CONV(8);
+        default: return hipErrorInvalidValue;
+    }
+#undef SB_CONV
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(mamba_conv_state_kernel, blocks((size_t)B * d_inner, kConvThreads), dim3(kConvThreads), 0,
                        stream, xz, di2, conv_state, B, T, d_inner, K);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // W_x padded to a multiple of 64 rows (zeros), then [δ | B | C | 0] = u W_x^T.
-    hipLaunchKernelGGL(copy_rows_kernel, blocks((size_t)Pp * d_inner / 8, 256), dim3(256), 0, stream, W_x, d_inner,
-                       wxp, d_inner, P, Pp, d_inner);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_gemm(u, wxp, rows, Pp, d_inner, EPI_BF16, xdbl, nullptr, stream)) != hipSuccess) return e;
-    // δ gathered into its own rows, then the step projection in fp32.
-    hipLaunchKernelGGL(copy_rows_kernel, blocks((size_t)rows * R / 8, 256), dim3(256), 0, stream, xdbl, Pp, delta, R,
-                       rows, rows, R);
+    // [δ | B | C] = u W_x^T in K-slices (fp32 partials), then summed into δ
+    // rows and B | C rows (bf16).
+    const int ks = xproj_splits(rows, P, d_inner);
+    e = launch_gemm(u, W_x, rows, P, d_inner, EPI_F32, reinterpret_cast<bf16_t *>(L.part), nullptr, stream, ks);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(xproj_reduce_kernel, blocks((size_t)rows * P / 8, 256), dim3(256), 0, stream, L.part, ks, rows,
+                       P, R, delta, bc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // Δ = softplus(δ W_dt^T + dt_bias) in the GEMM's epilogue (fp32).
     e = launch_gemm(delta, W_dt, rows, d_inner, R, EPI_SOFTPLUS, reinterpret_cast<bf16_t *>(dpre),
@@ -489,7 +546,7 @@ hipError_t launch_mamba_prefill(const bf16_t *x, const bf16_t *W_in, const float
     const dim3 cgrid((unsigned)nch, (unsigned)(d_inner * scan_lanes_per_channel(NS) / 64), (unsigned)B);
 #define SB_CHUNK(N_, OUT_)                                                                                          \
     hipLaunchKernelGGL((mamba_chunk_scan_kernel<N_ / scan_lanes_per_channel(N_), scan_lanes_per_channel(N_), OUT_>), \
-                       cgrid, dim3(64), 0, stream, xz, di2, u, xdbl, Pp, R, dpre, A_log, Dp, sp, M_out, g, T, Lc,    \
+                       cgrid, dim3(64), 0, stream, xz, di2, u, bc, 2 * NS, 0, dpre, A_log, Dp, sp, M_out, g, T, Lc,  \
                        d_inner)
 #define SB_CHUNK_NS(OUT_)                  \
     switch (NS) {                          \
