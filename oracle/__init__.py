@@ -545,3 +545,85 @@ def crossdecoder_ex(h, M, K, V, layers: Sequence, Hq: int, lens=None, eps: float
                                     float(scale), float(eps), 1 if round_bf16 else 0, _ptr(out))
     _check(rc, "crossdecoder_ex")
     return out
+
+
+def round_bf16_array(x) -> np.ndarray:
+    """round_bf16 for whole arrays: the nearest value with an 8-bit
+    significand (1 + 7 stored bits), ties to even; for the O(1) magnitudes of
+    activations (no bfloat16 overflow or subnormal range)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m · 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def _f64(a) -> np.ndarray:
+    """An accepted input widened exactly to float64 (bfloat16 bit patterns
+    become the values they encode: the high half of a float32)."""
+    arr, code = _as_input(a)
+    if code == BF16:
+        return (arr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.array(arr, dtype=np.float64)
+
+
+def sambay_prefill(x, self_layers: Sequence, cross_layers: Sequence, Hq: int, Hkv: int, window: int = 0,
+                   eps: float = 1e-5, scale: float | None = None, round_h: bool = True) -> dict:
+    """YOCO-style prefill ([Notes] 整体框架): the self-decoder over the prompt
+    x [B, T, d_model], its final full-attention layer's keys and values as
+    the shared cache, then the cross-decoder on the last prompt token.
+
+    Self-decoder layer (plain pre-norm reading, as the complete
+    cross-decoder layer): x = RMSNorm(h; norm1) or h; kind "mamba": (M, y)
+    = mamba_prefill(x) from the layer's states, h = h + y; "swa" / "attn":
+    q, k, v = x Wq^T, x Wk^T, x Wv^T, o = attn_prefill(q, k, v, window or
+    0), h = h + o Wo^T; then, with an MLP, h = h + swiglu(RMSNorm(h; norm2)).
+    round_h: round h to bfloat16 after every residual add (the bf16
+    residual stream), also inside the cross-decoder.  Dict keys of the
+    layers as in the library's binding (tensors on the CPU); D = d_model /
+    Hq.
+
+    Returns a dict: h_out [B, d_model] (the last token after the
+    cross-decoder), h_last (the same token after the self-decoder), M_last
+    [B, d_inner] (the last SSM layer's memory at that token), K, V [B, Hkv,
+    T, D] (the cache rows the last full-attention layer writes), per layer
+    "layers": {"k", "v"} token-major for attention layers or {"conv_state",
+    "ssm_state"} for SSM layers, all float64."""
+    h = _f64(x)
+    if h.ndim != 3:
+        raise ValueError("x must be [B, T, d_model]")
+    B, T, dm = h.shape
+    D = dm // Hq
+    if Hq * D != dm or Hq % Hkv != 0:
+        raise ValueError("head shape mismatch")
+    rnd = round_bf16_array if round_h else (lambda a: a)
+    h = rnd(h)
+    M_mem, K, V, per_layer = None, None, None, []
+    for ly in self_layers:
+        kind = ly["kind"]
+        xin = rmsnorm(h.reshape(B * T, dm), ly["norm1"], eps).reshape(B, T, dm) if ly.get("norm1") is not None else h
+        if kind == "mamba":
+            M, y, conv, ssm = mamba_prefill(xin, ly["w"], ly["conv_state"], ly["ssm_state"])
+            h = rnd(h + y)
+            M_mem = M
+            per_layer.append({"conv_state": conv, "ssm_state": ssm})
+        elif kind in ("swa", "attn"):
+            q = (xin @ _f64(ly["wq"]).T).reshape(B, T, Hq, D)
+            k = (xin @ _f64(ly["wk"]).T).reshape(B, T, Hkv, D)
+            v = (xin @ _f64(ly["wv"]).T).reshape(B, T, Hkv, D)
+            o = attn_prefill(q, k, v, window if kind == "swa" else 0, scale)
+            h = rnd(h + o.reshape(B, T, dm) @ _f64(ly["wo"]).T)
+            per_layer.append({"k": k, "v": v})
+            if kind == "attn":
+                K, V = np.ascontiguousarray(k.transpose(0, 2, 1, 3)), np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+        else:
+            raise ValueError("self layer kind must be 'mamba', 'swa' or 'attn'")
+        if ly.get("w_gate") is not None:
+            xm = rmsnorm(h.reshape(B * T, dm), ly["norm2"], eps) if ly.get("norm2") is not None \
+                else h.reshape(B * T, dm)
+            h = rnd(h + swiglu(xm, ly["w_gate"], ly["w_up"], ly["w_down"]).reshape(B, T, dm))
+    h_last = np.ascontiguousarray(h[:, T - 1])
+    M_last = np.ascontiguousarray(M_mem[:, T - 1]) if M_mem is not None else None
+    h_out = h_last
+    if cross_layers:
+        h_out = crossdecoder_ex(h_last, M_last if M_last is not None else np.zeros((B, 1)), K, V, cross_layers, Hq,
+                                eps=eps, scale=scale, round_bf16=round_h)
+    return {"h_out": h_out, "h_last": h_last, "M_last": M_last, "K": K, "V": V, "layers": per_layer}

@@ -351,3 +351,82 @@ def prefill_inputs(B: int, T: int, Hq: int, Hkv: int, D: int, *, seed: int = 0, 
     return PrefillInputs(q=normal((B, T, Hq, D), seed=_seed(seed, 100), device=device, dtype=dtype),
                          k=normal((B, T, Hkv, D), seed=_seed(seed, 101), device=device, dtype=dtype),
                          v=normal((B, T, Hkv, D), seed=_seed(seed, 102), device=device, dtype=dtype))
+
+
+# ------------------------------------------------- YOCO-style prefill (bf16)
+
+# The whole prefill of the pages' model shape: a 2048-token prompt for four
+# sequences through a 16-layer Samba self-decoder (SSM layers alternating with
+# 256-token sliding-window attention, the last layer full attention, each
+# with a SwiGLU MLP) and the 16-layer cross-decoder on the last token; the
+# shared cache has room for the 2K prompt + 32K generated tokens.
+SAMBAY_PREFILL = dict(B=4, T=2048, d_model=3072, d_inner=6144, d_state=16, dt_rank=192, d_conv=4, d_ff=8192,
+                      Hq=24, Hkv=8, D=128, window=256, L=34816, n_self=16, n_cross=16)
+
+
+def self_layer_kinds(n: int) -> list:
+    """Samba order: SSM, sliding window, SSM, ... with the last layer full attention."""
+    return ["attn" if i == n - 1 else ("mamba" if i % 2 == 0 else "swa") for i in range(n)]
+
+
+@dataclass
+class SambayPrefillInputs:
+    x: torch.Tensor                  # [B, T, d_model]
+    self_layers: list                # dicts as the binding takes them
+    cross_layers: list
+    kcache: torch.Tensor             # [B, Hkv, L, D]
+    vcache: torch.Tensor
+
+
+def sambay_prefill_inputs(B: int, T: int, d_model: int, d_inner: int, d_state: int, dt_rank: int, d_conv: int,
+                          d_ff: int, Hq: int, Hkv: int, D: int, window: int, L: int, self_kinds: list,
+                          cross_kinds: list, *, seed: int = 0, device="cpu", fresh: bool = True,
+                          mlp: bool = True, norms: bool = True, dtype=torch.bfloat16) -> SambayPrefillInputs:
+    """x ~ N(0, 1); every matrix ~ N(0, 0.02^2); RMSNorm gains 1 + N(0, 0.1^2);
+    the SSM layers' own parameters as mamba_inputs (one seed per layer);
+    fresh: zero SSM states (a new prompt), else mamba_inputs' states.  The
+    caches start as zeros."""
+    x = normal((B, T, d_model), seed=_seed(seed, 120), device=device, dtype=dtype)
+    w = lambda shape, t, i: normal(shape, std=WEIGHT_STD, seed=_seed(seed, t, i), device=device, dtype=dtype)
+
+    def norms_mlp(ly, i, base):
+        if norms:
+            for j, key in enumerate(("norm1", "norm2")):
+                gsd = normal((d_model,), std=NORM_GAIN_STD, seed=_seed(seed, base, 2 * i + j), device=device,
+                             dtype=torch.float32)
+                ly[key] = (1.0 + gsd).to(dtype)
+        if mlp:
+            ly["w_gate"] = w((d_ff, d_model), base + 1, 3 * i)
+            ly["w_up"] = w((d_ff, d_model), base + 1, 3 * i + 1)
+            ly["w_down"] = w((d_model, d_ff), base + 1, 3 * i + 2)
+        return ly
+
+    self_layers = []
+    for i, kind in enumerate(self_kinds):
+        ly = {"kind": kind}
+        if kind == "mamba":
+            m = mamba_inputs(B, d_model, d_inner, d_state, dt_rank, d_conv, seed=_seed(seed, 121, i), device=device,
+                             dtype=dtype)
+            ly["w"] = m.w
+            ly["conv_state"] = torch.zeros_like(m.conv_state) if fresh else m.conv_state
+            ly["ssm_state"] = torch.zeros_like(m.ssm_state) if fresh else m.ssm_state
+        else:
+            ly["wq"] = w((Hq * D, d_model), 122, 4 * i)
+            ly["wk"] = w((Hkv * D, d_model), 122, 4 * i + 1)
+            ly["wv"] = w((Hkv * D, d_model), 122, 4 * i + 2)
+            ly["wo"] = w((d_model, Hq * D), 122, 4 * i + 3)
+            if kind == "swa":
+                ly["kring"] = torch.zeros((B, Hkv, window, D), device=device, dtype=dtype)
+                ly["vring"] = torch.zeros((B, Hkv, window, D), device=device, dtype=dtype)
+        self_layers.append(norms_mlp(ly, i, 123))
+    cross_layers = []
+    for i, kind in enumerate(cross_kinds):
+        ly = {"kind": kind}
+        if kind == "xattn":
+            ly["w_a"], ly["w_b"] = w((d_model, d_model), 125, 2 * i), w((d_model, d_model), 125, 2 * i + 1)
+        else:
+            ly["w_a"], ly["w_b"] = w((d_inner, d_model), 125, 2 * i), w((d_model, d_inner), 125, 2 * i + 1)
+        cross_layers.append(norms_mlp(ly, i, 126))
+    kc = torch.zeros((B, Hkv, L, D), device=device, dtype=dtype)
+    return SambayPrefillInputs(x=x, self_layers=self_layers, cross_layers=cross_layers, kcache=kc,
+                               vcache=torch.zeros_like(kc))
