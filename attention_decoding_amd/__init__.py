@@ -27,6 +27,7 @@ SB_OK, SB_EINVAL, SB_EUNSUPPORTED, SB_EWORKSPACE, SB_EHIP = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "SB_OK", 1: "SB_EINVAL", 2: "SB_EUNSUPPORTED", 3: "SB_EWORKSPACE", 4: "SB_EHIP"}
 SB_F32, SB_BF16 = 0, 1
 SB_LAYER_XATTN, SB_LAYER_GMU = 0, 1
+SB_SELF_MAMBA, SB_SELF_SWA, SB_SELF_ATTN = 0, 1, 2
 
 # Every function the header declares, for load-time checking.
 EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", "xattn_workspace_bytes",
@@ -35,7 +36,7 @@ EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", 
            "xattn_decode_varlen", "crossdecoder_ex_workspace_bytes", "crossdecoder_step_ex",
            "diffattn_workspace_bytes", "diffattn_decode", "selfattn_workspace_bytes", "selfattn_decode",
            "mamba_workspace_bytes", "mamba_decode_step", "attn_prefill_workspace_bytes", "attn_prefill",
-           "mamba_prefill_workspace_bytes", "mamba_prefill")
+           "mamba_prefill_workspace_bytes", "mamba_prefill", "sambay_prefill_workspace_bytes", "sambay_prefill")
 SB_TIME_XATTN_SPLIT, SB_TIME_XATTN_MERGE, SB_TIME_SKINNY, SB_TIME_GEMM, SB_TIME_GMU_F32, SB_TIME_PROBE = \
     1, 2, 4, 8, 16, 32
 SB_TIME_DIFF_SPLIT, SB_TIME_DIFF_MERGE, SB_TIME_PREFILL = 64, 128, 256
@@ -55,6 +56,14 @@ class SbLayerEx(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("w_a", ctypes.c_void_p), ("w_b", ctypes.c_void_p),
                 ("norm1", ctypes.c_void_p), ("norm2", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
                 ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
+
+
+class SbSelfLayer(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("mamba", SbMambaWeights), ("conv_state", ctypes.c_void_p),
+                ("ssm_state", ctypes.c_void_p), ("wq", ctypes.c_void_p), ("wk", ctypes.c_void_p),
+                ("wv", ctypes.c_void_p), ("wo", ctypes.c_void_p), ("kring", ctypes.c_void_p),
+                ("vring", ctypes.c_void_p), ("norm1", ctypes.c_void_p), ("norm2", ctypes.c_void_p),
+                ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
 
 
 class SambayError(RuntimeError):
@@ -114,6 +123,11 @@ def _load() -> ctypes.CDLL:
     lib.mamba_prefill.argtypes = [vp, ctypes.POINTER(SbMambaWeights), vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                   i64, vp, sz, vp]
     lib.mamba_prefill.restype = ctypes.c_int
+    lib.sambay_prefill_workspace_bytes.argtypes = [i64] * 12
+    lib.sambay_prefill_workspace_bytes.restype = sz
+    lib.sambay_prefill.argtypes = [vp, vp, vp, ctypes.POINTER(SbSelfLayer), i32, ctypes.POINTER(SbLayerEx), i32, vp,
+                                   vp] + [i64] * 13 + [ctypes.c_float, ctypes.c_float, vp, sz, vp]
+    lib.sambay_prefill.restype = ctypes.c_int
     lib.sb_timing_enable.argtypes = [ctypes.c_uint32]
     lib.sb_timing_enable.restype = ctypes.c_int
     lib.sb_timing_collect.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -551,6 +565,35 @@ def crossdecoder_step(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor, vc
 _EX_KEYS = ("norm1", "norm2", "w_gate", "w_up", "w_down")
 
 
+def _mlp_width(layers: Sequence) -> int:
+    d_ff = 0
+    for ly in layers:
+        if ly.get("w_gate") is not None:
+            d_ff = ly["w_gate"].shape[0]
+    return d_ff
+
+
+def _set_norms_mlp(arr_i, ly: dict, i: int, dev, d_model: int, d_ff: int, what: str) -> None:
+    shapes = {"norm1": (d_model,), "norm2": (d_model,), "w_gate": (d_ff, d_model), "w_up": (d_ff, d_model),
+              "w_down": (d_model, d_ff)}
+    for key in _EX_KEYS:
+        t = ly.get(key)
+        if t is None:
+            continue
+        if tuple(t.shape) != shapes[key]:
+            raise ValueError("%s %d %s has shape %s, expected %s" % (what, i, key, tuple(t.shape), shapes[key]))
+        setattr(arr_i, key, _dev_ptr(t, "%s %d %s" % (what, i, key), torch.bfloat16, dev))
+
+
+def _layer_ex_array(layers: Sequence, dev, d_model: int, d_inner: int, d_ff: int):
+    arr = (SbLayerEx * max(len(layers), 1))()
+    base = _layer_array([(ly["kind"], ly["w_a"], ly["w_b"]) for ly in layers], dev, d_model, d_inner)
+    for i, ly in enumerate(layers):
+        arr[i].kind, arr[i].w_a, arr[i].w_b = base[i].kind, base[i].w_a, base[i].w_b
+        _set_norms_mlp(arr[i], ly, i, dev, d_model, d_ff, "layer")
+    return arr
+
+
 class CrossDecoderStepEx:
     """Prepared complete-layer decode step (pre-RMSNorm mixer, optional
     pre-RMSNorm SwiGLU MLP, optional ragged cache lengths).  layers: sequence of
@@ -571,23 +614,8 @@ class CrossDecoderStepEx:
         if d_model % D != 0:
             raise ValueError("d_model must be a multiple of the head dim")
         Hq = d_model // D
-        d_ff = 0
-        for ly in layers:
-            if ly.get("w_gate") is not None:
-                d_ff = ly["w_gate"].shape[0]
-        arr = (SbLayerEx * max(len(layers), 1))()
-        base = _layer_array([(ly["kind"], ly["w_a"], ly["w_b"]) for ly in layers], dev, d_model, d_inner)
-        for i, ly in enumerate(layers):
-            arr[i].kind, arr[i].w_a, arr[i].w_b = base[i].kind, base[i].w_a, base[i].w_b
-            shapes = {"norm1": (d_model,), "norm2": (d_model,), "w_gate": (d_ff, d_model), "w_up": (d_ff, d_model),
-                      "w_down": (d_model, d_ff)}
-            for key in _EX_KEYS:
-                t = ly.get(key)
-                if t is None:
-                    continue
-                if tuple(t.shape) != shapes[key]:
-                    raise ValueError("layer %d %s has shape %s, expected %s" % (i, key, tuple(t.shape), shapes[key]))
-                setattr(arr[i], key, _dev_ptr(t, "layer %d %s" % (i, key), bf, dev))
+        d_ff = _mlp_width(layers)
+        arr = _layer_ex_array(layers, dev, d_model, d_inner, d_ff)
         if lens is not None and lens.shape != (B,):
             raise ValueError("lens must have shape [B]")
         self.lens_ptr = _dev_ptr(lens, "lens", torch.int32, dev) if lens is not None else None
@@ -617,8 +645,106 @@ def crossdecoder_step_ex(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor,
     return CrossDecoderStepEx(h, M, kcache, vcache, layers, lens, eps, scale)()
 
 
+_SELF_KINDS = {"mamba": SB_SELF_MAMBA, "swa": SB_SELF_SWA, "attn": SB_SELF_ATTN}
+
+
+class SambayPrefill:
+    """Prepared YOCO-style prefill: the self-decoder over the prompt x [B, T,
+    d_model] (bf16), its final full-attention layer writing the shared cache
+    kcache / vcache [B, Hkv, L, D] at positions 0 .. T-1, then the
+    cross-decoder on the last prompt token.
+
+    self_layers: sequence of dicts, kind "mamba" (key "w": the weights dict of
+    mamba_decode_step; "conv_state", "ssm_state": float32 states, in and
+    out), "swa" (wq, wk, wv, wo; "kring", "vring": [B, Hkv, window, D] ring
+    caches, written) or "attn" (wq, wk, wv, wo); each with optional norm1,
+    norm2, w_gate, w_up, w_down.  cross_layers: as crossdecoder_step_ex.
+    Calling it returns (h_out [B, d_model], M_last [B, d_inner]), bf16."""
+
+    def __init__(self, x, self_layers: Sequence, cross_layers: Sequence, kcache, vcache, window: int = 0,
+                 eps: float = 1e-5, scale: float | None = None, h_out=None, M_out=None):
+        dev = _check_device(x, "x")
+        bf, f32 = torch.bfloat16, torch.float32
+        if x.dim() != 3 or kcache.dim() != 4 or vcache.shape != kcache.shape:
+            raise ValueError("x [B, T, d_model], kcache and vcache [B, Hkv, L, D]")
+        B, T, d_model = x.shape
+        B2, Hkv, L, D = kcache.shape
+        if B2 != B or d_model % D != 0:
+            raise ValueError("sambay_prefill shape mismatch")
+        Hq = d_model // D
+        mamba = [ly for ly in self_layers if ly["kind"] == "mamba"]
+        if mamba:
+            _, d_inner, d_state, dt_rank, d_conv = _mamba_weights(mamba[0]["w"], dev, d_model)
+        else:  # no SSM layer: any supported SSM shape sizes the (unused) memory
+            d_inner, d_state, dt_rank, d_conv = 64, 8, 64, 1
+            for ly in cross_layers:
+                if ly["kind"] == "gmu":
+                    d_inner = ly["w_a"].shape[0]
+        d_ff = max(_mlp_width(self_layers), _mlp_width(cross_layers))
+        arr = (SbSelfLayer * max(len(self_layers), 1))()
+        for i, ly in enumerate(self_layers):
+            kind = ly["kind"]
+            if kind not in _SELF_KINDS:
+                raise ValueError("self layer kind must be 'mamba', 'swa' or 'attn'")
+            arr[i].kind = _SELF_KINDS[kind]
+            if kind == "mamba":
+                sw, di, ds, dr, dc = _mamba_weights(ly["w"], dev, d_model)
+                if (di, ds, dr, dc) != (d_inner, d_state, dt_rank, d_conv):
+                    raise ValueError("every SSM layer must have the same shape")
+                if ly["ssm_state"].shape != (B, d_inner, d_state) or \
+                        (d_conv > 1 and ly["conv_state"].shape != (B, d_inner, d_conv - 1)):
+                    raise ValueError("self layer %d: state shape mismatch" % i)
+                arr[i].mamba = sw
+                arr[i].ssm_state = _dev_ptr(ly["ssm_state"], "ssm_state", f32, dev)
+                if d_conv > 1:
+                    arr[i].conv_state = _dev_ptr(ly["conv_state"], "conv_state", f32, dev)
+            else:
+                shapes = {"wq": (d_model, d_model), "wk": (Hkv * D, d_model), "wv": (Hkv * D, d_model),
+                          "wo": (d_model, d_model)}
+                for key, shp in shapes.items():
+                    if tuple(ly[key].shape) != shp:
+                        raise ValueError("self layer %d %s has shape %s, expected %s" %
+                                         (i, key, tuple(ly[key].shape), shp))
+                    setattr(arr[i], key, _dev_ptr(ly[key], "self layer %d %s" % (i, key), bf, dev))
+                if kind == "swa":
+                    for key in ("kring", "vring"):
+                        if tuple(ly[key].shape) != (B, Hkv, window, D):
+                            raise ValueError("self layer %d %s must be [B, Hkv, window, D]" % (i, key))
+                        setattr(arr[i], key, _dev_ptr(ly[key], "self layer %d %s" % (i, key), bf, dev))
+            _set_norms_mlp(arr[i], ly, i, dev, d_model, d_ff, "self layer")
+        self.cross = _layer_ex_array(cross_layers, dev, d_model, d_inner, d_ff)
+        self.self_arr = arr
+        self.h_out = h_out if h_out is not None else torch.empty((B, d_model), dtype=bf, device=dev)
+        self.M_out = M_out if M_out is not None else torch.empty((B, d_inner), dtype=bf, device=dev)
+        self.tensors = (x, self_layers, cross_layers, kcache, vcache)
+        self.ptrs = (_dev_ptr(x, "x", bf, dev), _dev_ptr(self.h_out, "h_out", bf, dev),
+                     _dev_ptr(self.M_out, "M_out", bf, dev))
+        self.kv = (_dev_ptr(kcache, "kcache", bf, dev), _dev_ptr(vcache, "vcache", bf, dev))
+        self.n = (len(self_layers), len(cross_layers))
+        self.dims = (B, T, d_model, d_inner, d_state, dt_rank, d_conv, d_ff, Hq, Hkv, D, L)
+        self.window = int(window)
+        self.scale = float(1.0 / math.sqrt(D) if scale is None else scale)
+        self.eps = float(eps)
+        nb = lib.sambay_prefill_workspace_bytes(*self.dims)
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        self.device = dev
+
+    def __call__(self):
+        st = lib.sambay_prefill(*self.ptrs, self.self_arr, self.n[0], self.cross, self.n[1], *self.kv, *self.dims,
+                                self.window, self.scale, self.eps, self.ws.data_ptr(), self.ws.numel(),
+                                _stream(self.device))
+        _check("sambay_prefill", st)
+        return self.h_out, self.M_out
+
+
+def sambay_prefill(x, self_layers: Sequence, cross_layers: Sequence, kcache, vcache, window: int = 0,
+                   eps: float = 1e-5, scale: float | None = None):
+    """YOCO-style prefill (see SambayPrefill); returns (h_out, M_last)."""
+    return SambayPrefill(x, self_layers, cross_layers, kcache, vcache, window, eps, scale)()
+
+
 __all__ = ["gmu_forward", "xattn_decode", "diffattn_decode", "selfattn_decode", "mamba_decode_step",
-           "attn_prefill", "mamba_prefill",
+           "attn_prefill", "mamba_prefill", "sambay_prefill", "SambayPrefill",
            "crossdecoder_step", "CrossDecoderStep", "crossdecoder_step_ex",
            "CrossDecoderStepEx", "SambayError", "version", "lib",
            "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect", "probe_stream_read_gbps", "probe_mfma_tflops",

@@ -12,6 +12,8 @@
 
 #include "launch.hpp"
 
+#include <vector>
+
 using namespace sambay;
 
 namespace {
@@ -1024,4 +1026,182 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
         if (e != hipSuccess) return hip_fail("crossdecoder_step_ex launch", e);
     }
     return ok();
+}
+
+// ===================================================== YOCO-style prefill
+
+namespace {
+
+size_t sambay_prefill_ws(int64_t B, int64_t T, int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank,
+                         int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t L, bool cross) {
+    const size_t self = round_up(self_decoder_layout(nullptr, B, T, d_model, d_inner, d_state, dt_rank, d_ff, Hq,
+                                                     Hkv).bytes);
+    return self + (cross ? round_up(ex_layout(B, d_model, d_inner, d_ff, Hq, Hkv, L).total) : 0);
+}
+
+bool prefill_dims_ok(int64_t B, int64_t T, int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank,
+                     int64_t d_conv, int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t D, int64_t L) {
+    return B > 0 && T > 0 && T <= L && B <= 65535 && T <= 65535 && B * T < ((int64_t)1 << 31) && D == kHeadDim &&
+           Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && Hq * D == d_model && d_ff >= 0 && d_ff % 64 == 0 &&
+           d_ff <= kMaxDim && L <= kMaxDim && mamba_dims_ok(B, d_model, d_inner, d_state, dt_rank, d_conv) &&
+           dt_rank % 64 == 0;
+}
+
+}  // namespace
+
+extern "C" size_t sambay_prefill_workspace_bytes(int64_t B, int64_t T, int64_t d_model, int64_t d_inner,
+                                                 int64_t d_state, int64_t dt_rank, int64_t d_conv, int64_t d_ff,
+                                                 int64_t Hq, int64_t Hkv, int64_t D, int64_t L) {
+    if (!prefill_dims_ok(B, T, d_model, d_inner, d_state, dt_rank, d_conv, d_ff, Hq, Hkv, D, L)) return 0;
+    return sambay_prefill_ws(B, T, d_model, d_inner, d_state, dt_rank, d_ff, Hq, Hkv, L, true);
+}
+
+extern "C" sb_status sambay_prefill(const void *x, void *h_out, void *M_out, const sb_self_layer *self_layers,
+                                    int32_t n_self, const sb_layer_ex *cross_layers, int32_t n_cross, void *kcache,
+                                    void *vcache, int64_t B, int64_t T, int64_t d_model, int64_t d_inner,
+                                    int64_t d_state, int64_t dt_rank, int64_t d_conv, int64_t d_ff, int64_t Hq,
+                                    int64_t Hkv, int64_t D, int64_t L, int64_t window, float scale, float eps,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "sambay_prefill";
+    if (B < 0 || T < 0 || d_model < 0 || d_inner < 0 || d_state < 0 || dt_rank < 0 || d_conv < 0 || d_ff < 0 ||
+        Hq < 0 || Hkv < 0 || D < 0 || L < 0 || window < 0 || n_self < 0 || n_cross < 0)
+        return fail(SB_EINVAL, "negative size");
+    if (B == 0) return ok();
+    if (T == 0) return fail(SB_EINVAL, "an empty prompt has no last token");
+    if (!prefill_dims_ok(B, T, d_model, d_inner, d_state, dt_rank, d_conv, d_ff, Hq, Hkv, D, L))
+        return fail(SB_EUNSUPPORTED,
+                    "unsupported prefill shape (D == 128, Hq %% Hkv == 0, Hq*D == d_model; d_model, d_inner, d_ff, "
+                    "dt_rank multiples of 64, dt_rank <= %d; d_state in {8, 16, 32, 64}; d_conv <= %d; "
+                    "1 <= T <= L; B, T <= 65535)", kMaxDtRank, kMaxConv);
+    if (!x || !h_out || !kcache || !vcache) return fail(SB_EINVAL, "null tensor pointer");
+    if (n_self > 0 && !self_layers) return fail(SB_EINVAL, "null self-decoder layer array");
+    if (n_cross > 0 && !cross_layers) return fail(SB_EINVAL, "null cross-decoder layer array");
+    if (!aligned16(x) || !aligned16(h_out) || !aligned16(M_out) || !aligned16(kcache) || !aligned16(vcache))
+        return fail(SB_EINVAL, "tensor base pointers must be 16-byte aligned");
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(SB_EINVAL, "scale must be finite");
+    if (!(eps >= 0.f) || eps == __builtin_inff()) return fail(SB_EINVAL, "eps must be finite and >= 0");
+    const int64_t rows = B * T, kvd = Hkv * D;
+    const size_t kvbytes = (size_t)B * Hkv * L * D * 2;
+    // Everything the call writes, against each other and everything it reads.
+    std::vector<Range> outs = {rng("h_out", h_out, (size_t)B * d_model * 2),
+                               rng("M_out", M_out, M_out ? (size_t)B * d_inner * 2 : 0),
+                               rng("kcache", kcache, kvbytes), rng("vcache", vcache, kvbytes)};
+    std::vector<Range> ins = {rng("x", x, (size_t)rows * d_model * 2)};
+    bool has_attn = false, has_mamba = false, has_swa = false;
+    for (int32_t i = 0; i < n_self; ++i) {
+        const sb_self_layer &ly = self_layers[i];
+        const bool mlp = ly.w_gate != nullptr;
+        if (mlp && (!ly.w_up || !ly.w_down)) return fail(SB_EINVAL, "self layer %d: incomplete MLP", (int)i);
+        if (mlp && d_ff == 0) return fail(SB_EINVAL, "self layer %d has an MLP but d_ff == 0", (int)i);
+        const void *common[] = {ly.norm1, ly.norm2, ly.w_gate, ly.w_up, ly.w_down};
+        for (const void *p : common)
+            if (!aligned16(p)) return fail(SB_EINVAL, "self layer %d: misaligned weight or gain", (int)i);
+        ins.push_back(rng("norm1", ly.norm1, ly.norm1 ? (size_t)d_model * 2 : 0));
+        ins.push_back(rng("norm2", ly.norm2, ly.norm2 ? (size_t)d_model * 2 : 0));
+        ins.push_back(rng("w_gate", ly.w_gate, mlp ? (size_t)d_ff * d_model * 2 : 0));
+        ins.push_back(rng("w_up", ly.w_up, mlp ? (size_t)d_ff * d_model * 2 : 0));
+        ins.push_back(rng("w_down", ly.w_down, mlp ? (size_t)d_model * d_ff * 2 : 0));
+        if (ly.kind == SB_SELF_MAMBA) {
+            has_mamba = true;
+            const sb_mamba_weights &w = ly.mamba;
+            if (!w.w_in || !w.conv_w || !w.conv_b || !w.w_x || !w.w_dt || !w.dt_bias || !w.a_log || !w.d_skip ||
+                !w.w_out)
+                return fail(SB_EINVAL, "self layer %d: null SSM weight", (int)i);
+            if (!ly.ssm_state || (!ly.conv_state && d_conv > 1))
+                return fail(SB_EINVAL, "self layer %d: null SSM state", (int)i);
+            const void *al[] = {w.w_in, w.conv_w, w.conv_b, w.w_x, w.w_dt, w.dt_bias, w.a_log, w.d_skip, w.w_out,
+                                ly.conv_state, ly.ssm_state};
+            for (const void *p : al)
+                if (!aligned16(p)) return fail(SB_EINVAL, "self layer %d: misaligned SSM tensor", (int)i);
+            const int64_t P = dt_rank + 2 * d_state;
+            outs.push_back(rng("conv_state", ly.conv_state, (size_t)B * d_inner * (d_conv - 1) * 4));
+            outs.push_back(rng("ssm_state", ly.ssm_state, (size_t)B * d_inner * d_state * 4));
+            ins.push_back(rng("w_in", w.w_in, (size_t)2 * d_inner * d_model * 2));
+            ins.push_back(rng("conv_w", w.conv_w, (size_t)d_inner * d_conv * 4));
+            ins.push_back(rng("conv_b", w.conv_b, (size_t)d_inner * 4));
+            ins.push_back(rng("w_x", w.w_x, (size_t)P * d_inner * 2));
+            ins.push_back(rng("w_dt", w.w_dt, (size_t)d_inner * dt_rank * 2));
+            ins.push_back(rng("dt_bias", w.dt_bias, (size_t)d_inner * 4));
+            ins.push_back(rng("a_log", w.a_log, (size_t)d_inner * d_state * 4));
+            ins.push_back(rng("d_skip", w.d_skip, (size_t)d_inner * 4));
+            ins.push_back(rng("w_out", w.w_out, (size_t)d_model * d_inner * 2));
+        } else if (ly.kind == SB_SELF_SWA || ly.kind == SB_SELF_ATTN) {
+            if (!ly.wq || !ly.wk || !ly.wv || !ly.wo)
+                return fail(SB_EINVAL, "self layer %d: null attention weight", (int)i);
+            const void *al[] = {ly.wq, ly.wk, ly.wv, ly.wo, ly.kring, ly.vring};
+            for (const void *p : al)
+                if (!aligned16(p)) return fail(SB_EINVAL, "self layer %d: misaligned attention tensor", (int)i);
+            ins.push_back(rng("wq", ly.wq, (size_t)d_model * d_model * 2));
+            ins.push_back(rng("wk", ly.wk, (size_t)kvd * d_model * 2));
+            ins.push_back(rng("wv", ly.wv, (size_t)kvd * d_model * 2));
+            ins.push_back(rng("wo", ly.wo, (size_t)d_model * d_model * 2));
+            if (ly.kind == SB_SELF_SWA) {
+                has_swa = true;
+                if (!ly.kring || !ly.vring) return fail(SB_EINVAL, "self layer %d: null ring cache", (int)i);
+                const size_t rb = (size_t)B * Hkv * (window > 0 ? window : 0) * D * 2;
+                outs.push_back(rng("kring", ly.kring, rb));
+                outs.push_back(rng("vring", ly.vring, rb));
+            } else {
+                has_attn = true;
+            }
+        } else {
+            return fail(SB_EINVAL, "self layer %d: unknown kind %d", (int)i, (int)ly.kind);
+        }
+    }
+    if (has_swa && (window < 1 || window > 65535))
+        return fail(SB_EUNSUPPORTED, "a sliding-window layer needs 1 <= window <= 65535");
+    for (int32_t i = 0; i < n_cross; ++i) {
+        if (cross_layers[i].kind == SB_LAYER_XATTN && !has_attn)
+            return fail(SB_EINVAL, "cross layer %d attends to a cache no self-decoder layer writes", (int)i);
+        if (cross_layers[i].kind == SB_LAYER_GMU && !has_mamba)
+            return fail(SB_EINVAL, "cross layer %d gates a memory no SSM layer produces", (int)i);
+    }
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlaps(outs[i], outs[j])) return fail(SB_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (const Range &r : ins)
+            if (overlaps(outs[i], r)) return fail(SB_EINVAL, "%s overlaps %s", outs[i].name, r.name);
+    }
+    // A final full-attention layer finishes on the last token only, as the
+    // first layer of the cross-decoder step.
+    const bool last_kv_only = n_self > 0 && self_layers[n_self - 1].kind == SB_SELF_ATTN;
+    const size_t need =
+        sambay_prefill_ws(B, T, d_model, d_inner, d_state, dt_rank, d_ff, Hq, Hkv, L, n_cross > 0 || last_kv_only);
+    if (!workspace || workspace_bytes < need)
+        return fail(SB_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(SB_EINVAL, "workspace must be 16-byte aligned");
+    const Range rw = rng("workspace", workspace, need);
+    for (const Range &r : outs)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+    for (const Range &r : ins)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+    if (log_enabled())
+        fprintf(stderr, "[sambay] %s B=%lld T=%lld self=%d cross=%d d_model=%lld window=%lld workspace %zu bytes\n",
+                fn, (long long)B, (long long)T, (int)n_self, (int)n_cross, (long long)d_model, (long long)window,
+                need);
+
+    const SelfDecoderLayout lay = self_decoder_layout(workspace, B, T, d_model, d_inner, d_state, dt_rank, d_ff, Hq,
+                                                      Hkv);
+    // M_last for the cross-decoder: the caller's M_out, else workspace rows.
+    bf16_t *m_last = M_out ? static_cast<bf16_t *>(M_out) : lay.m_last;
+    SelfDecoderArgs a;
+    a.x = (const bf16_t *)x; a.layers = self_layers; a.n = n_self;
+    a.B = (int)B; a.T = (int)T; a.d_model = (int)d_model; a.d_inner = (int)d_inner; a.d_state = (int)d_state;
+    a.dt_rank = (int)dt_rank; a.d_conv = (int)d_conv; a.d_ff = (int)d_ff; a.Hq = (int)Hq; a.Hkv = (int)Hkv;
+    a.L = (int)L; a.window = (int)window; a.scale = scale; a.eps = eps; a.kcache = kcache; a.vcache = vcache;
+    a.h_out = static_cast<bf16_t *>(h_out); a.M_out = m_last; a.last_kv_only = last_kv_only;
+    hipError_t e = launch_self_decoder(a, lay, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    std::vector<sb_layer_ex> cross;
+    if (last_kv_only) {
+        const sb_self_layer &ly = self_layers[n_self - 1];
+        cross.push_back(sb_layer_ex{SB_LAYER_XATTN, ly.wq, ly.wo, ly.norm1, ly.norm2, ly.w_gate, ly.w_up, ly.w_down});
+    }
+    for (int32_t i = 0; i < n_cross; ++i) cross.push_back(cross_layers[i]);
+    if (cross.empty()) return ok();
+    char *cws = static_cast<char *>(workspace) + round_up(lay.bytes);
+    const size_t cbytes = need - round_up(lay.bytes);
+    return crossdecoder_step_ex(h_out, m_last, kcache, vcache, lay.lens, cross.data(), (int32_t)cross.size(), B,
+                                d_model, d_inner, d_ff, Hq, Hkv, D, L, scale, eps, cws, cbytes, stream);
 }

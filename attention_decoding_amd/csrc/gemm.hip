@@ -20,7 +20,8 @@
 //    round-robin over 8) works on a contiguous band of tiles, grouped 8
 //    row-tiles at a time.
 //  * The epilogue parks each wave's accumulators in LDS (the ring is free by
-//    then) so that M is read and the output written as 16-byte vectors.
+//    then) so that M (or, for the residual add, h itself) is read and the
+//    output written as 16-byte vectors.
 //  * Measured at 8192 x 2560 x 5120 (both GMU products, random data): ~250 us
 //    for the gate product and ~227 us for the output product (850-950
 //    TFLOP/s).  A 3-5 deep ring (BK 64 or 32), 256-wide tiles with 8 or 16
@@ -169,14 +170,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     static_assert(VPL * 64 == 32 * VPR, "epilogue shape");
     float *stage = reinterpret_cast<float *>(lds_raw) + wave * 32 * SROW;
     u32x4 mv[FM][VPL];
-    if (EPI == EPI_GATE) {
+    if (EPI == EPI_GATE || EPI == EPI_RESID) {  // M (gate) or the residual h itself (out)
+        const bf16_t *src = EPI == EPI_GATE ? aux : out;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int u = 0; u < VPL; ++u) {
                 const int idx = u * 64 + lane, r = idx / VPR, c8 = idx % VPR;
                 const int m = bm + wm * TM + 32 * i + r, n = bn + wn * TN + 8 * c8;
-                mv[i][u] = (m < rows && n < N) ? ld16(aux + (size_t)m * N + n) : (u32x4){0u, 0u, 0u, 0u};
+                mv[i][u] = (m < rows && n < N) ? ld16(src + (size_t)m * N + n) : (u32x4){0u, 0u, 0u, 0u};
             }
     }
     __syncthreads();  // every wave is done with the operand ring
@@ -200,6 +202,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
                     const uint32_t w = mv[i][u][e / 2];
                     const float mm = (e & 1) ? hi_bf16(w) : lo_bf16(w);
                     x[e] = mm * (x[e] / (1.f + expf(-x[e])));
+                }
+            }
+            if (EPI == EPI_RESID) {  // h = bf16(h + acc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w = mv[i][u][e / 2];
+                    x[e] += (e & 1) ? hi_bf16(w) : lo_bf16(w);
                 }
             }
             if (EPI == EPI_SOFTPLUS) {  // softplus(acc + bias[n]), the SSM layer's step sizes
@@ -238,6 +247,9 @@ hipError_t launch_tile(const bf16_t *X, const bf16_t *W, int rows, int N, int K,
                            stream, X, W, rows, N, K, out, aux, ksplit);
     else if (epi == EPI_F32)
         hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_F32>), dim3(tiles), dim3(64 * WGM * WGN), 0,
+                           stream, X, W, rows, N, K, out, aux, ksplit);
+    else if (epi == EPI_RESID)
+        hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_RESID>), dim3(tiles), dim3(64 * WGM * WGN), 0,
                            stream, X, W, rows, N, K, out, aux, ksplit);
     else if (epi == EPI_SOFTPLUS)
         hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_SOFTPLUS>), dim3(tiles),

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "sambay.h"
+
 namespace sambay {
 
 typedef uint16_t bf16_t;
@@ -91,14 +93,15 @@ hipError_t launch_mamba_scan(const float *xz, int ldxz, const float *u, const fl
 
 // The SSM layer over T prompt tokens (x [B·T, d_model] rows): GEMM
 // projections, the convolution and the selective scan over the sequence;
-// conv_state / ssm_state in and out; M [B·T, d_inner], y [B·T, d_model].
+// conv_state / ssm_state in and out; M [B·T, d_inner], y [B·T, d_model]
+// (resid: y_out holds h and receives bf16(h + y) instead).
 // Requires d_model, d_inner, R multiples of 64, NS in {8, 16, 32, 64}.
 size_t mamba_prefill_workspace_need(int64_t B, int64_t T, int64_t d_inner, int64_t d_state, int64_t dt_rank);
 hipError_t launch_mamba_prefill(const bf16_t *x, const bf16_t *W_in, const float *conv_w, const float *conv_b,
                                 const bf16_t *W_x, const bf16_t *W_dt, const float *dt_bias, const float *A_log,
                                 const float *Dp, const bf16_t *W_out, float *conv_state, float *ssm_state,
                                 bf16_t *M_out, bf16_t *y_out, int B, int T, int d_model, int d_inner, int NS, int R,
-                                int K, void *workspace, hipStream_t stream);
+                                int K, void *workspace, hipStream_t stream, bool resid = false);
 
 // ------------------------------------------------ skinny (decode) products
 // out[t, n] = epi( Σ_k X[t, k] · W[n, k] ) for t < T <= 64 tokens.
@@ -150,17 +153,50 @@ size_t skinny_partial_bytes_dual(int T, int N, const SkinnyPlan &p);
 
 // ------------------------------------------------------- prefill product
 // out[r, n] = epi( Σ_k X[r, k] · W[n, k] ), any row count, N % 8 == 0, K % 64 == 0.
-// epi: EPI_BF16, EPI_GATE (aux = M), EPI_F32 or EPI_SOFTPLUS (out is then a
-// float array; EPI_SOFTPLUS reads its fp32 bias [N] through aux).  ksplit > 1
+// epi: EPI_BF16, EPI_GATE (aux = M), EPI_RESID (out = bf16(out + acc), in
+// place), EPI_F32 or EPI_SOFTPLUS (out is then a float array; EPI_SOFTPLUS
+// reads its fp32 bias [N] through aux).  ksplit > 1
 // (EPI_F32 only, K % (64·ksplit) == 0): slice s of K writes its partial sums
 // to out + s·rows·N.
 hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
                        const bf16_t *aux, hipStream_t stream, int ksplit = 1);
 
 // ------------------------------------------------------------- RMSNorm
-// out_hi + out_lo = h[r, :] / sqrt(mean(h[r, :]^2) + eps) * g, d % 8 == 0.
+// out_hi + out_lo = h[r, :] / sqrt(mean(h[r, :]^2) + eps) * g, d % 8 == 0
+// (out_lo may be null: plain bf16 output).
 hipError_t launch_rmsnorm(const bf16_t *h, const bf16_t *g, int rows, int d, float eps, bf16_t *out_hi,
                           bf16_t *out_lo, hipStream_t stream);
+
+// ------------------------------------------------- YOCO-style prefill
+// The self-decoder over B·T prompt rows (sambay_prefill's first part): the
+// caches and states written, h and M of position T-1 gathered into h_out
+// ([B, d_model]) and M_out ([B, d_inner]; the layout's m_last when null),
+// and lens ([B] int32 in the workspace) set to T for the cross-decoder step
+// that follows.
+struct SelfDecoderArgs {
+    const bf16_t *x = nullptr;          // [B, T, d_model]
+    const sb_self_layer *layers = nullptr;
+    int n = 0;
+    int B = 0, T = 0, d_model = 0, d_inner = 0, d_state = 0, dt_rank = 0, d_conv = 0, d_ff = 0;
+    int Hq = 0, Hkv = 0, L = 0, window = 0;
+    float scale = 0.f, eps = 0.f;
+    void *kcache = nullptr, *vcache = nullptr;
+    bf16_t *h_out = nullptr, *M_out = nullptr;
+    bool last_kv_only = false;          // a last SB_SELF_ATTN layer computes only its cache rows
+};
+struct SelfDecoderLayout {
+    bf16_t *h, *xn, *M;
+    int32_t *lens;
+    bf16_t *m_last;                      // [B, d_inner]: M at position T-1 when the caller keeps none
+    void *scratch;                       // shared by the attention, MLP and SSM layers in turn
+    bf16_t *q, *k, *v, *o, *up, *hid;    // views into scratch
+    void *attn_ws;
+    size_t bytes;
+};
+// base == nullptr: sizes only (bytes).
+SelfDecoderLayout self_decoder_layout(void *base, int64_t B, int64_t T, int64_t d_model, int64_t d_inner,
+                                      int64_t d_state, int64_t dt_rank, int64_t d_ff, int64_t Hq, int64_t Hkv);
+hipError_t launch_self_decoder(const SelfDecoderArgs &a, const SelfDecoderLayout &L, hipStream_t stream);
 
 // ------------------------------------------------------------- fp32 GMU
 hipError_t launch_gmu_f32(const float *M, const float *X, const float *W1, const float *W2, float *Y, float *H,

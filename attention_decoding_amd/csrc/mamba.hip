@@ -504,7 +504,7 @@ hipError_t launch_mamba_prefill(const bf16_t *x, const bf16_t *W_in, const float
                                 const bf16_t *W_x, const bf16_t *W_dt, const float *dt_bias, const float *A_log,
                                 const float *Dp, const bf16_t *W_out, float *conv_state, float *ssm_state,
                                 bf16_t *M_out, bf16_t *y_out, int B, int T, int d_model, int d_inner, int NS, int R,
-                                int K, void *workspace, hipStream_t stream) {
+                                int K, void *workspace, hipStream_t stream, bool resid) {
     const int rows = B * T, P = R + 2 * NS, di2 = 2 * d_inner;
     const PrefillLayout L = prefill_layout(workspace, B, T, d_inner, NS, R);
     bf16_t *xz = L.xz, *u = L.u, *bc = L.bc, *delta = L.delta, *g = L.g;
@@ -565,7 +565,7 @@ hipError_t launch_mamba_prefill(const bf16_t *x, const bf16_t *W_in, const float
 #undef SB_CHUNK_NS
 #undef SB_CHUNK
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return launch_gemm(g, W_out, rows, d_model, d_inner, EPI_BF16, y_out, nullptr, stream);
+    return launch_gemm(g, W_out, rows, d_model, d_inner, resid ? EPI_RESID : EPI_BF16, y_out, nullptr, stream);
 }
 
 }  // namespace sambay

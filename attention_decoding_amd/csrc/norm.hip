@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const bf16_t *__restr
             lo[e] = pack_bf16x2(y0 - bf16_to_f32(h0), y1 - bf16_to_f32(h1));
         }
         *reinterpret_cast<u32x4 *>(out_hi + row + 8 * v) = hi;
-        *reinterpret_cast<u32x4 *>(out_lo + row + 8 * v) = lo;
+        if (out_lo) *reinterpret_cast<u32x4 *>(out_lo + row + 8 * v) = lo;
     }
 }
 

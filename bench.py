@@ -160,9 +160,18 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> 
     Y = torch.empty(rows, c["d_model"], dtype=torch.bfloat16, device=dev)
     ms = time_calls(lambda i: sb.gmu_forward(g.M, g.X, g.W1, g.W2, out=Y), 20)
     flops = 4.0 * rows * c["d_model"] * c["d_inner"]
+    # Context only: the same two products through torch's bf16 matmul (the
+    # vendor BLAS), unfused, with the SiLU·M product as separate elementwise
+    # work — what a caller without this library would run.
+    F = torch.nn.functional
+    ms_lib = time_calls(lambda i: F.linear(g.M * F.silu(F.linear(g.X, g.W1)), g.W2), 20)
+    ms_lib_gemms = time_calls(lambda i: (F.linear(g.X, g.W1), F.linear(g.M, g.W2)), 20)
     res["gmu_prefill_8192x2560x5120"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
                                          "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4),
-                                         "frac_of_measured_mfma_loop": round(flops / ms / 1e9 / mfma_tflops, 4)}
+                                         "frac_of_measured_mfma_loop": round(flops / ms / 1e9 / mfma_tflops, 4),
+                                         "context_torch_gmu_ms": round(ms_lib, 4),
+                                         "context_torch_two_matmuls_ms": round(ms_lib_gemms, 4),
+                                         "context_torch_two_matmuls_tflops": round(flops / ms_lib_gemms / 1e9, 1)}
     del g, Y
     # GMU decode: B in {1, 8, 32, 64}, 3072 -> 6144 -> 3072, 8 rotating weight sets (604 MB).
     c = workload.GMU_DECODE
@@ -286,6 +295,26 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> 
         "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
         "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4)}
     del m, xs, Mo, yo
+    # YOCO-style prefill of the whole model: 4 x 2048 prompt tokens through the
+    # 16-layer self-decoder, then the 16-layer cross-decoder on the last token;
+    # the self-decoder alone timed beside it (the cross-decoder's share is the
+    # difference).
+    c = workload.SAMBAY_PREFILL
+    yp = workload.sambay_prefill_inputs(c["B"], c["T"], c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"],
+                                        c["d_conv"], c["d_ff"], c["Hq"], c["Hkv"], c["D"], c["window"], c["L"],
+                                        workload.self_layer_kinds(c["n_self"]), workload.layer_kinds(c["n_cross"]),
+                                        seed=97, device=dev)
+    full = sb.SambayPrefill(yp.x, yp.self_layers, yp.cross_layers, yp.kcache, yp.vcache, window=c["window"])
+    selfonly = sb.SambayPrefill(yp.x, yp.self_layers, [], yp.kcache, yp.vcache, window=c["window"])
+    ms_full = time_calls(lambda i: full(), 5, warmup=2)
+    ms_self = time_calls(lambda i: selfonly(), 5, warmup=1)
+    rows = c["B"] * c["T"]
+    res["sambay_prefill_B%d_T%d" % (c["B"], c["T"])] = {
+        "ms": round(ms_full, 3), "prompt_tokens_per_s": round(rows / ms_full * 1e3, 1),
+        "self_decoder_ms": round(ms_self, 3), "cross_decoder_last_token_ms": round(ms_full - ms_self, 3),
+        "layers": "16 self (8 SSM, 7 sliding-window 256, 1 full attention) + 16 cross (8 attention, 8 GMU), "
+                  "SwiGLU d_ff 8192 in every layer"}
+    del yp, full, selfonly
     # Prefill attention over the prompt: 4 x 2048 tokens, window 256 (the
     # self-decoder's sliding-window layers), and plain causal at 1 x 2048.
     c = workload.ATTN_PREFILL

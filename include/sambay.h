@@ -322,6 +322,71 @@ sb_status crossdecoder_step_ex(void *h, const void *M, const void *kcache, const
                                int64_t d_inner, int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t D, int64_t L,
                                float scale, float eps, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------ YOCO-style prefill --
+ * The SambaY prefill ([Notes] section 整体框架: only the self-decoder runs
+ * over the prompt, so pre-filling stays linear; [Summary] key claims): the
+ * self-decoder over the T prompt tokens of B sequences, its final
+ * full-attention layer writing the shared KV cache once, then the
+ * cross-decoder on the last prompt token only.  The self-decoder is Samba
+ * (SSM layers alternating with sliding-window attention layers) followed by
+ * one full-attention layer; no positional encoding ([Summary] abstract).
+ * Each self-decoder layer takes the same plain pre-norm reading as the
+ * complete cross-decoder layer:
+ *   x = RMSNorm(h; norm1)                      (x = h when norm1 is NULL)
+ *   SB_SELF_MAMBA: h = bf16(h + y), (M, y) = mamba_prefill(x) with the
+ *                  layer's states (in and out); M is kept for the GMUs
+ *   SB_SELF_SWA:   q, k, v = x Wq^T, x Wk^T, x Wv^T; o = attn_prefill(q, k, v,
+ *                  window); h = bf16(h + o Wo^T); the last min(T, window)
+ *                  positions p of k, v go to ring slot p % window of
+ *                  kring / vring [B, Hkv, window, D]
+ *   SB_SELF_ATTN:  the same with plain causal attention; k, v of positions
+ *                  0 .. T-1 go to the shared cache kcache / vcache
+ *                  [B, Hkv, L, D] (the cache the cross-decoder reads)
+ *   when w_gate is not NULL: x = RMSNorm(h; norm2);
+ *                  h = bf16(h + (SiLU(x Wg^T) ⊙ (x Wu^T)) Wd^T)
+ * Then h_last = h at position T-1 and M_last = M (of the last SSM layer) at
+ * position T-1 run through crossdecoder_step_ex(cross_layers) with every
+ * sequence's cache length T; h_out [B, d_model] receives the result and
+ * M_out [B, d_inner] (nullable) receives M_last, the memory the GMUs used.
+ * Prefill activations (x, q, k, v, o, M, the MLP hidden) are bf16 with fp32
+ * accumulation; the residual stream h is bf16.  The prompt starts at
+ * position 0 (the caches are written from there); the SSM states start from
+ * the values given (zero for a fresh prompt).
+ * Shapes: x [B, T, d_model] bf16; Wq, Wo [d_model, d_model] (Hq·D ==
+ * d_model), Wk, Wv [Hkv·D, d_model]; MLP and norms as in sb_layer_ex; the
+ * SSM layer as mamba_prefill.  Requires D == 128, Hq % Hkv == 0, d_model,
+ * d_inner, d_ff, dt_rank multiples of 64, 1 <= T <= L, B, T <= 65535,
+ * window >= 1 when an SB_SELF_SWA layer is present, at least one
+ * SB_SELF_ATTN layer when a cross layer is SB_LAYER_XATTN and at least one
+ * SB_SELF_MAMBA layer when a cross layer is SB_LAYER_GMU.
+ * Errors: SB_EINVAL for null or misaligned pointers, unknown kinds, missing
+ * weights or states, a non-finite scale or eps, h_out / M_out / the caches /
+ * the workspace overlapping another argument; SB_EUNSUPPORTED for other
+ * shapes; SB_EWORKSPACE.  B == 0 is a no-op. */
+typedef enum { SB_SELF_MAMBA = 0, SB_SELF_SWA = 1, SB_SELF_ATTN = 2 } sb_self_kind;
+typedef struct {
+    int32_t kind;             /* an sb_self_kind value */
+    sb_mamba_weights mamba;   /* SB_SELF_MAMBA */
+    float *conv_state;        /* SB_SELF_MAMBA: [B, d_inner, d_conv-1] fp32, in and out (NULL when d_conv == 1) */
+    float *ssm_state;         /* SB_SELF_MAMBA: [B, d_inner, d_state] fp32, in and out */
+    const void *wq, *wk, *wv, *wo;  /* SB_SELF_SWA, SB_SELF_ATTN */
+    void *kring, *vring;      /* SB_SELF_SWA: [B, Hkv, window, D] bf16, written */
+    const void *norm1;        /* RMSNorm gain before the mixer, or NULL */
+    const void *norm2;        /* RMSNorm gain before the MLP, or NULL */
+    const void *w_gate;       /* SwiGLU MLP weights, or all NULL: no MLP */
+    const void *w_up;
+    const void *w_down;
+} sb_self_layer;
+
+size_t sambay_prefill_workspace_bytes(int64_t B, int64_t T, int64_t d_model, int64_t d_inner, int64_t d_state,
+                                      int64_t dt_rank, int64_t d_conv, int64_t d_ff, int64_t Hq, int64_t Hkv,
+                                      int64_t D, int64_t L);
+sb_status sambay_prefill(const void *x, void *h_out, void *M_out, const sb_self_layer *self_layers, int32_t n_self,
+                         const sb_layer_ex *cross_layers, int32_t n_cross, void *kcache, void *vcache, int64_t B,
+                         int64_t T, int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank,
+                         int64_t d_conv, int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t D, int64_t L, int64_t window,
+                         float scale, float eps, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------ benchmark instrumentation --
  * For measuring kernels inside the calls above (benchmarks and profiling
  * only; not meant for production loops).  While a kind's bit is enabled,

@@ -351,3 +351,42 @@ def test_mamba_prefill_validation(sb):
     assert call(wsb=1 << 20) == sb.SB_EWORKSPACE
     assert call(T=0) == sb.SB_OK and call(B=0) == sb.SB_OK
     assert sb.lib.mamba_prefill_workspace_bytes(4, 2048, 3072, 6144, 16, 192, 4) > 4 * 2048 * 6144 * 8
+
+
+def test_sambay_prefill_validation(sb):
+    """Every call here fails validation (or is a no-op); no pointer is touched."""
+    G = 1 << 30
+    mw = sb.SbMambaWeights(*[(i + 10) * G for i in range(9)])
+    mam = sb.SbSelfLayer(kind=sb.SB_SELF_MAMBA, mamba=mw, conv_state=30 * G, ssm_state=31 * G)
+    att = sb.SbSelfLayer(kind=sb.SB_SELF_ATTN, wq=32 * G, wk=33 * G, wv=34 * G, wo=35 * G)
+    swa = sb.SbSelfLayer(kind=sb.SB_SELF_SWA, wq=36 * G, wk=37 * G, wv=38 * G, wo=39 * G, kring=40 * G,
+                         vring=41 * G)
+    cross = (sb.SbLayerEx * 2)()
+    cross[0].kind, cross[0].w_a, cross[0].w_b = sb.SB_LAYER_XATTN, 42 * G, 43 * G
+    cross[1].kind, cross[1].w_a, cross[1].w_b = sb.SB_LAYER_GMU, 44 * G, 45 * G
+
+    def call(layers=(mam, swa, att), ncross=2, T=2048, L=4096, window=256, kc=4 * G, hout=2 * G, wsb=1 << 36,
+             B=4, R=192):
+        arr = (sb.SbSelfLayer * max(len(layers), 1))(*layers)
+        return sb.lib.sambay_prefill(1 * G, hout, 3 * G, arr, len(layers), cross, ncross, kc, 6 * G, B, T, 3072, 6144,
+                                     16, R, 4, 0, 24, 8, 128, L, window, 0.088, 1e-5, 50 * G, wsb, None)
+
+    assert call(B=0) == sb.SB_OK
+    assert call(T=0) == sb.SB_EINVAL                      # no last token
+    assert call(T=5000) == sb.SB_EUNSUPPORTED             # T > L
+    assert call(R=184) == sb.SB_EUNSUPPORTED              # dt_rank not a multiple of 64
+    assert call(window=0) == sb.SB_EUNSUPPORTED           # a sliding-window layer needs a window
+    assert call(layers=(mam, swa)) == sb.SB_EINVAL        # cross-attention without a cache writer
+    assert call(layers=(swa, att)) == sb.SB_EINVAL        # a GMU without an SSM layer
+    assert call(hout=1 * G + 64) == sb.SB_EINVAL          # h_out overlaps x
+    assert call(kc=6 * G) == sb.SB_EINVAL                 # the two caches overlap
+    assert call(wsb=1 << 20) == sb.SB_EWORKSPACE
+    bad = sb.SbSelfLayer(kind=7)
+    assert call(layers=(mam, bad, att)) == sb.SB_EINVAL
+    noring = sb.SbSelfLayer(kind=sb.SB_SELF_SWA, wq=36 * G, wk=37 * G, wv=38 * G, wo=39 * G)
+    assert call(layers=(mam, noring, att)) == sb.SB_EINVAL
+    lib = sb.lib
+    need = lib.sambay_prefill_workspace_bytes(4, 2048, 3072, 6144, 16, 192, 4, 8192, 24, 8, 128, 36864)
+    assert need > 4 * 2048 * (2 * 3072 + 6144) * 2       # h, x-norm and M rows at least
+    assert lib.sambay_prefill_workspace_bytes(4, 0, 3072, 6144, 16, 192, 4, 0, 24, 8, 128, 36864) == 0
+    assert lib.sambay_prefill_workspace_bytes(4, 2048, 3072, 6144, 16, 192, 4, 0, 24, 8, 64, 36864) == 0

@@ -1,0 +1,142 @@
+"""GPU parity of the YOCO-style prefill (sambay_prefill) against the oracle's
+composition (oracle.sambay_prefill with the bf16 residual stream).
+
+Everything the call leaves behind is compared: the last token's hidden
+state after the cross-decoder, the memory M the GMUs used, the shared cache
+rows the final full-attention layer wrote, the sliding-window rings and the
+SSM states.  Tolerance: the bf16 bar (2e-2, max-abs normalised) for all of
+them; the prefill's activations are bf16 with fp32 accumulation, and the
+states integrate those roundings over the prompt.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def sb():
+    import attention_decoding_amd as sb
+    return sb
+
+
+def err(y, ref):
+    y, ref = np.asarray(y, np.float64), np.asarray(ref, np.float64)
+    return float(np.max(np.abs(y - ref)) / max(float(np.max(np.abs(ref))), 1e-300))
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def report(name, e, tol=TOL):
+    print("%-64s err %.3e (tol %.0e)" % (name, e, tol), flush=True)
+    assert e <= tol, "%s: %.3e > %.0e" % (name, e, tol)
+
+
+def _cpu(layers):
+    out = []
+    for ly in layers:
+        c = {}
+        for k, v in ly.items():
+            if isinstance(v, torch.Tensor):
+                c[k] = v.cpu()
+            elif isinstance(v, dict):
+                c[k] = {kk: vv.cpu() for kk, vv in v.items()}
+            else:
+                c[k] = v
+        out.append(c)
+    return out
+
+
+def _run(sb, B, T, dm, di, NS, R, K, dff, Hq, Hkv, W, L, self_kinds, cross_kinds, seed, name):
+    D = 128
+    inp = workload.sambay_prefill_inputs(B, T, dm, di, NS, R, K, dff, Hq, Hkv, D, W, L, self_kinds, cross_kinds,
+                                         seed=seed, device=DEV, fresh=False)
+    cpu_self = _cpu(inp.self_layers)              # the states before the prompt
+    cpu_cross = _cpu(inp.cross_layers)
+    print("case %s: B=%d T=%d d_model=%d layers %s | %s" % (name, B, T, dm, self_kinds, cross_kinds), flush=True)
+    h_out, M_last = sb.sambay_prefill(inp.x, inp.self_layers, inp.cross_layers, inp.kcache, inp.vcache, window=W)
+    torch.cuda.synchronize()
+    ref = oracle.sambay_prefill(inp.x.cpu(), cpu_self, cpu_cross, Hq, Hkv, window=W)
+    report("%s h_out" % name, err(f64(h_out), ref["h_out"]))
+    if ref["M_last"] is not None:
+        report("%s M_last" % name, err(f64(M_last), ref["M_last"]))
+    if ref["K"] is not None:
+        report("%s cache K rows" % name, err(f64(inp.kcache[:, :, :T]), ref["K"]))
+        report("%s cache V rows" % name, err(f64(inp.vcache[:, :, :T]), ref["V"]))
+        assert torch.count_nonzero(inp.kcache[:, :, T:]) == 0, "positions past the prompt were written"
+    for i, ly in enumerate(inp.self_layers):
+        r = ref["layers"][i]
+        if ly["kind"] == "mamba":
+            report("%s layer %d ssm_state" % (name, i), err(f64(ly["ssm_state"]), r["ssm_state"]))
+            if K > 1:
+                report("%s layer %d conv_state" % (name, i), err(f64(ly["conv_state"]), r["conv_state"]))
+        elif ly["kind"] == "swa":
+            ps = list(range(max(0, T - W), T))
+            slots = [p % W for p in ps]
+            report("%s layer %d ring K" % (name, i), err(f64(ly["kring"][:, :, slots]), r["k"][:, ps].transpose(0, 2, 1, 3)))
+            report("%s layer %d ring V" % (name, i), err(f64(ly["vring"][:, :, slots]), r["v"][:, ps].transpose(0, 2, 1, 3)))
+    return inp
+
+
+SELF = ["mamba", "swa", "mamba", "attn"]
+
+
+@pytest.mark.parametrize("B,T,W", [
+    (2, 100, 32),      # ragged prompt (100 = 64 + 36), ring wraps
+    (3, 20, 32),       # a prompt shorter than the window
+    (1, 1, 8),         # a one-token prompt
+])
+def test_sambay_prefill_small(sb, B, T, W):
+    _run(sb, B, T, 256, 512, 16, 64, 4, 512, 2, 1, W, T + 40, SELF, ["xattn", "gmu"], seed=B * T + W,
+         name="small B=%d T=%d W=%d" % (B, T, W))
+
+
+def test_sambay_prefill_without_mlps_or_cross_layers(sb):
+    inp = workload.sambay_prefill_inputs(2, 70, 256, 512, 16, 64, 4, 0, 2, 2, 128, 16, 80, ["mamba", "attn"], [],
+                                         seed=9, device=DEV, fresh=True, mlp=False, norms=False)
+    cpu_self = _cpu(inp.self_layers)
+    h_out, _ = sb.sambay_prefill(inp.x, inp.self_layers, [], inp.kcache, inp.vcache, window=16)
+    torch.cuda.synchronize()
+    ref = oracle.sambay_prefill(inp.x.cpu(), cpu_self, [], 2, 2, window=16)
+    report("no MLP, no cross layers: h_last", err(f64(h_out), ref["h_out"]))
+
+
+def test_sambay_prefill_full_width(sb):
+    """The model's widths (d_model 3072, d_inner 6144, 24/8 heads, d_ff
+    8192) over a 70-token prompt (a ragged second tile, a 64-slot ring that
+    wraps), 4 self-decoder and 2 cross-decoder layers."""
+    c = workload.SAMBAY_PREFILL
+    _run(sb, 1, 70, c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"], c["d_conv"], c["d_ff"], c["Hq"],
+         c["Hkv"], 64, 512, SELF, ["xattn", "gmu"], seed=11, name="full width 1 x 70")
+
+
+def test_sambay_prefill_full_size_properties(sb):
+    """The benchmark's whole prefill (4 x 2048 tokens, 16 + 16 layers): two
+    runs give the same bits, every output is finite, exactly the prompt's
+    cache positions are written."""
+    c = workload.SAMBAY_PREFILL
+    inp = workload.sambay_prefill_inputs(c["B"], c["T"], c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"],
+                                         c["d_conv"], c["d_ff"], c["Hq"], c["Hkv"], c["D"], c["window"], c["L"],
+                                         workload.self_layer_kinds(c["n_self"]), workload.layer_kinds(c["n_cross"]),
+                                         seed=12, device=DEV)
+    states0 = [(ly["conv_state"].clone(), ly["ssm_state"].clone()) for ly in inp.self_layers if ly["kind"] == "mamba"]
+    run = sb.SambayPrefill(inp.x, inp.self_layers, inp.cross_layers, inp.kcache, inp.vcache, window=c["window"])
+    h1, m1 = (t.clone() for t in run())
+    k1 = inp.kcache[:, :, :c["T"]].clone()
+    for (cs, ss), ly in zip(states0, [ly for ly in inp.self_layers if ly["kind"] == "mamba"]):
+        ly["conv_state"].copy_(cs)
+        ly["ssm_state"].copy_(ss)
+    h2, m2 = run()
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2) and torch.equal(m1, m2) and torch.equal(k1, inp.kcache[:, :, :c["T"]])
+    assert torch.isfinite(h1.float()).all() and torch.isfinite(m1.float()).all()
+    assert torch.count_nonzero(inp.kcache[:, :, c["T"]:]) == 0
+    assert torch.count_nonzero(k1) > 0.99 * k1.numel()
