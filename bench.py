@@ -148,212 +148,227 @@ def time_graph(fn, n: int, reps: int = 10) -> float:
     return e0.elapsed_time(e1) / (reps * n)
 
 
-def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float) -> dict:
-    """Kernel-level rates of the other workloads (not part of `value`)."""
+WORKLOAD_GROUPS = ("gmu_prefill", "gmu_decode", "attention", "ragged", "mamba_decode", "mamba_prefill",
+                   "sambay_prefill", "attn_prefill", "crossdecoder_ex")
+
+
+def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float, only=None) -> dict:
+    """Kernel-level rates of the other workloads (not part of `value`);
+    `only`: a subset of WORKLOAD_GROUPS to run (None: all)."""
     import torch
 
     res = {}
-    # GMU prefill: 4 x 2048 rows, 2560 -> 5120 -> 2560.
-    c = workload.GMU_PREFILL
-    rows = c["batch"] * c["seq"]
-    g = workload.gmu_inputs(rows, c["d_model"], c["d_inner"], seed=1, device=dev)
-    Y = torch.empty(rows, c["d_model"], dtype=torch.bfloat16, device=dev)
-    ms = time_calls(lambda i: sb.gmu_forward(g.M, g.X, g.W1, g.W2, out=Y), 20)
-    flops = 4.0 * rows * c["d_model"] * c["d_inner"]
-    # Context only: the same two products through torch's bf16 matmul (the
-    # vendor BLAS), unfused, with the SiLU·M product as separate elementwise
-    # work — what a caller without this library would run.
-    F = torch.nn.functional
-    ms_lib = time_calls(lambda i: F.linear(g.M * F.silu(F.linear(g.X, g.W1)), g.W2), 20)
-    ms_lib_gemms = time_calls(lambda i: (F.linear(g.X, g.W1), F.linear(g.M, g.W2)), 20)
-    res["gmu_prefill_8192x2560x5120"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
-                                         "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4),
-                                         "frac_of_measured_mfma_loop": round(flops / ms / 1e9 / mfma_tflops, 4),
-                                         "context_torch_gmu_ms": round(ms_lib, 4),
-                                         "context_torch_two_matmuls_ms": round(ms_lib_gemms, 4),
-                                         "context_torch_two_matmuls_tflops": round(flops / ms_lib_gemms / 1e9, 1)}
-    del g, Y
-    # GMU decode: B in {1, 8, 32, 64}, 3072 -> 6144 -> 3072, 8 rotating weight sets (604 MB).
-    c = workload.GMU_DECODE
-    sets = [workload.gmu_inputs(1, c["d_model"], c["d_inner"], seed=2, device=dev, weight_set=k) for k in range(8)]
-    for B in c["batches"]:
-        gi = workload.gmu_inputs(B, c["d_model"], c["d_inner"], seed=3 + B, device=dev)
-        Y = torch.empty(B, c["d_model"], dtype=torch.bfloat16, device=dev)
-        ms = time_calls(lambda i: sb.gmu_forward(gi.M, gi.X, sets[i % 8].W1, sets[i % 8].W2, out=Y), 64)
-        nbytes = 2 * c["d_model"] * c["d_inner"] * 2 + B * (2 * c["d_model"] + c["d_inner"]) * 2
-        gbps = nbytes / ms / 1e6
-        res["gmu_decode_B%d" % B] = {"us_per_call": round(1e3 * ms, 2), "gbps": round(gbps, 1),
-                                     "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
-                                     "frac_of_stream_read": round(gbps / read_gbps, 4)}
-    # Context: two plain streaming reads of the same two weight matrices (the
-    # library's read probe, same rotation), i.e. what a perfect kernel pair
-    # could approach at this size with two launches.
-    def plain_reads(i):
-        sb.probe_stream_read_raw(sets[i % 8].W1)
-        sb.probe_stream_read_raw(sets[i % 8].W2)
+    want = lambda name: only is None or name in only
+    if want("gmu_prefill"):
+        # GMU prefill: 4 x 2048 rows, 2560 -> 5120 -> 2560.
+        c = workload.GMU_PREFILL
+        rows = c["batch"] * c["seq"]
+        g = workload.gmu_inputs(rows, c["d_model"], c["d_inner"], seed=1, device=dev)
+        Y = torch.empty(rows, c["d_model"], dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda i: sb.gmu_forward(g.M, g.X, g.W1, g.W2, out=Y), 20)
+        flops = 4.0 * rows * c["d_model"] * c["d_inner"]
+        # Context only: the same two products through torch's bf16 matmul (the
+        # vendor BLAS), unfused, with the SiLU·M product as separate elementwise
+        # work — what a caller without this library would run.
+        F = torch.nn.functional
+        ms_lib = time_calls(lambda i: F.linear(g.M * F.silu(F.linear(g.X, g.W1)), g.W2), 20)
+        ms_lib_gemms = time_calls(lambda i: (F.linear(g.X, g.W1), F.linear(g.M, g.W2)), 20)
+        res["gmu_prefill_8192x2560x5120"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                                             "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4),
+                                             "frac_of_measured_mfma_loop": round(flops / ms / 1e9 / mfma_tflops, 4),
+                                             "context_torch_gmu_ms": round(ms_lib, 4),
+                                             "context_torch_two_matmuls_ms": round(ms_lib_gemms, 4),
+                                             "context_torch_two_matmuls_tflops": round(flops / ms_lib_gemms / 1e9, 1)}
+        del g, Y
+    if want("gmu_decode"):
+        # GMU decode: B in {1, 8, 32, 64}, 3072 -> 6144 -> 3072, 8 rotating weight sets (604 MB).
+        c = workload.GMU_DECODE
+        sets = [workload.gmu_inputs(1, c["d_model"], c["d_inner"], seed=2, device=dev, weight_set=k) for k in range(8)]
+        for B in c["batches"]:
+            gi = workload.gmu_inputs(B, c["d_model"], c["d_inner"], seed=3 + B, device=dev)
+            Y = torch.empty(B, c["d_model"], dtype=torch.bfloat16, device=dev)
+            ms = time_calls(lambda i: sb.gmu_forward(gi.M, gi.X, sets[i % 8].W1, sets[i % 8].W2, out=Y), 64)
+            nbytes = 2 * c["d_model"] * c["d_inner"] * 2 + B * (2 * c["d_model"] + c["d_inner"]) * 2
+            gbps = nbytes / ms / 1e6
+            res["gmu_decode_B%d" % B] = {"us_per_call": round(1e3 * ms, 2), "gbps": round(gbps, 1),
+                                         "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
+                                         "frac_of_stream_read": round(gbps / read_gbps, 4)}
+        # Context: two plain streaming reads of the same two weight matrices (the
+        # library's read probe, same rotation), i.e. what a perfect kernel pair
+        # could approach at this size with two launches.
+        def plain_reads(i):
+            sb.probe_stream_read_raw(sets[i % 8].W1)
+            sb.probe_stream_read_raw(sets[i % 8].W2)
 
-    pr = time_calls(plain_reads, 64)
-    for B in c["batches"]:
-        res["gmu_decode_B%d" % B]["two_plain_reads_us"] = round(1e3 * pr, 2)
-        res["gmu_decode_B%d" % B]["frac_of_two_plain_reads"] = round(pr / (res["gmu_decode_B%d" % B]["us_per_call"]
-                                                                          / 1e3), 4)
-    del sets
-    # Attention alone: 16 x 24 q heads, 8 KV heads, 34816 positions.
-    c = workload.XATTN_DECODE
-    x = workload.xattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["L"], seed=4, device=dev)
-    out = torch.empty(c["B"], c["Hq"], c["D"], dtype=torch.bfloat16, device=dev)
-    ms = time_calls(lambda i: sb.xattn_decode(x.q, x.K, x.V, out=out), 20)
-    nbytes = c["B"] * c["Hkv"] * c["L"] * c["D"] * 4
-    res["xattn_decode_B16_L34816"] = {"us_per_call": round(1e3 * ms, 1), "gbps": round(nbytes / ms / 1e6, 1),
-                                      "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
-                                      "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
-    # Differential attention on the same cache: both maps in one pass, against
-    # two plain decode passes over it (the cache bytes that an implementation
-    # running one attention pass per map reads).
-    c = workload.DIFFATTN_DECODE
-    gain = workload.diffattn_gain(c["D"], seed=4, device=dev)
-    ms_d = time_calls(lambda i: sb.diffattn_decode(x.q, x.K, x.V, c["lam"], c["lam_init"], gamma=gain,
-                                                   eps=c["eps"], out=out), 20)
+        pr = time_calls(plain_reads, 64)
+        for B in c["batches"]:
+            res["gmu_decode_B%d" % B]["two_plain_reads_us"] = round(1e3 * pr, 2)
+            res["gmu_decode_B%d" % B]["frac_of_two_plain_reads"] = round(pr / (res["gmu_decode_B%d" % B]["us_per_call"]
+                                                                              / 1e3), 4)
+        del sets
+    if want("attention"):
+        # Attention alone: 16 x 24 q heads, 8 KV heads, 34816 positions.
+        c = workload.XATTN_DECODE
+        x = workload.xattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["L"], seed=4, device=dev)
+        out = torch.empty(c["B"], c["Hq"], c["D"], dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda i: sb.xattn_decode(x.q, x.K, x.V, out=out), 20)
+        nbytes = c["B"] * c["Hkv"] * c["L"] * c["D"] * 4
+        res["xattn_decode_B16_L34816"] = {"us_per_call": round(1e3 * ms, 1), "gbps": round(nbytes / ms / 1e6, 1),
+                                          "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                          "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
+        # Differential attention on the same cache: both maps in one pass, against
+        # two plain decode passes over it (the cache bytes that an implementation
+        # running one attention pass per map reads).
+        c = workload.DIFFATTN_DECODE
+        gain = workload.diffattn_gain(c["D"], seed=4, device=dev)
+        ms_d = time_calls(lambda i: sb.diffattn_decode(x.q, x.K, x.V, c["lam"], c["lam_init"], gamma=gain,
+                                                       eps=c["eps"], out=out), 20)
 
-    def two_passes(i):
-        sb.xattn_decode(x.q, x.K, x.V, out=out)
-        sb.xattn_decode(x.q, x.K, x.V, out=out)
+        def two_passes(i):
+            sb.xattn_decode(x.q, x.K, x.V, out=out)
+            sb.xattn_decode(x.q, x.K, x.V, out=out)
 
-    ms_2 = time_calls(two_passes, 10)
-    res["diffattn_decode_B16_L34816"] = {
-        "us_per_call": round(1e3 * ms_d, 1), "gbps": round(nbytes / ms_d / 1e6, 1),
-        "frac_of_hbm_peak": round(nbytes / ms_d / 1e6 / HBM_PEAK_GBS, 4),
-        "frac_of_stream_read": round(nbytes / ms_d / 1e6 / read_gbps, 4),
-        "two_plain_passes_us": round(1e3 * ms_2, 1), "speedup_vs_two_passes": round(ms_2 / ms_d, 3)}
-    del x
-    # Ragged batch: 32 sequences, room for 34816 positions, lengths uniform in [2048, 34816].
-    c = workload.XATTN_VARLEN
-    x = workload.xattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["L"], seed=6, device=dev)
-    lens = workload.ragged_lens(c["B"], c["L"], seed=6, min_len=c["min_len"], device=dev)
-    out = torch.empty(c["B"], c["Hq"], c["D"], dtype=torch.bfloat16, device=dev)
-    ms = time_calls(lambda i: sb.xattn_decode(x.q, x.K, x.V, out=out, lens=lens), 20)
-    nbytes = int(lens.sum().item()) * c["Hkv"] * c["D"] * 4
-    res["xattn_decode_varlen_B32_L34816_ragged"] = {
-        "us_per_call": round(1e3 * ms, 1), "cached_positions": int(lens.sum().item()),
-        "gbps": round(nbytes / ms / 1e6, 1), "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
-        "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
-    # Self-decoder attention steps: the final full-attention layer appends each
-    # sequence's new row to the same cache at position lens - 1 and attends over
-    # lens positions; a sliding-window layer does the same on a 256-slot ring.
-    kn = workload.normal((c["B"], c["Hkv"], c["D"]), seed=60, device=dev)
-    vn = workload.normal((c["B"], c["Hkv"], c["D"]), seed=61, device=dev)
-    pos = (lens - 1).to(torch.int32)
-    ms = time_calls(lambda i: sb.selfattn_decode(x.q, kn, vn, x.K, x.V, pos, out=out), 20)
-    nbytes = int(lens.sum().item()) * c["Hkv"] * c["D"] * 4 + c["B"] * c["Hkv"] * c["D"] * 4
-    res["selfattn_decode_full_B32_L34816_ragged"] = {
-        "us_per_call": round(1e3 * ms, 1), "gbps": round(nbytes / ms / 1e6, 1),
-        "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
-    del x
-    torch.cuda.empty_cache()
-    W = workload.SELFATTN_SWA["window"]
-    r = workload.selfattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], W, seed=62, device=dev)
-    call = lambda i: sb.selfattn_decode(r.q, r.k_new, r.v_new, r.K, r.V, pos, window=W, out=out)
-    ms_eager = time_calls(call, 50)
-    ms = time_graph(call, 20)
-    nbytes = c["B"] * c["Hkv"] * W * c["D"] * 4 + c["B"] * c["Hkv"] * c["D"] * 4
-    res["selfattn_decode_window256_B32"] = {
-        "us_per_call": round(1e3 * ms, 2), "timing": "HIP graph replay of 20 calls",
-        "us_per_call_eager": round(1e3 * ms_eager, 2), "gbps": round(nbytes / ms / 1e6, 1),
-        "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
-    del r
-    # SSM decode step (the Mamba layer producing M): 4 rotating weight sets
-    # (4 x 118 MB, more than the 256 MB last-level cache) so that the weights
-    # stream from HBM as they would layer after layer.
-    c = workload.MAMBA_DECODE
-    dm, di, N, R, K = c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"], c["d_conv"]
-    msets = [workload.mamba_inputs(1, dm, di, N, R, K, seed=70 + k, device=dev).w for k in range(4)]
-    wbytes = (2 * di * dm + (R + 2 * N) * di + di * R + dm * di) * 2 + (di * K + 3 * di + di * N) * 4
-    for B in (1, 32):
-        m = workload.mamba_inputs(B, dm, di, N, R, K, seed=80 + B, device=dev)
-        Mo = torch.empty(B, di, dtype=torch.bfloat16, device=dev)
-        yo = torch.empty(B, dm, dtype=torch.bfloat16, device=dev)
-        ms = time_calls(lambda i: sb.mamba_decode_step(m.x, msets[i % 4], m.conv_state, m.ssm_state, Mo, yo), 40)
-        nbytes = wbytes + B * di * (N + K - 1) * 4 * 2 + B * (2 * dm + di) * 2
-        res["mamba_decode_B%d" % B] = {
-            "us_per_call": round(1e3 * ms, 2), "hbm_bytes": nbytes, "gbps": round(nbytes / ms / 1e6, 1),
-            "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+        ms_2 = time_calls(two_passes, 10)
+        res["diffattn_decode_B16_L34816"] = {
+            "us_per_call": round(1e3 * ms_d, 1), "gbps": round(nbytes / ms_d / 1e6, 1),
+            "frac_of_hbm_peak": round(nbytes / ms_d / 1e6 / HBM_PEAK_GBS, 4),
+            "frac_of_stream_read": round(nbytes / ms_d / 1e6 / read_gbps, 4),
+            "two_plain_passes_us": round(1e3 * ms_2, 1), "speedup_vs_two_passes": round(ms_2 / ms_d, 3)}
+        del x
+    if want("ragged"):
+        # Ragged batch: 32 sequences, room for 34816 positions, lengths uniform in [2048, 34816].
+        c = workload.XATTN_VARLEN
+        x = workload.xattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["L"], seed=6, device=dev)
+        lens = workload.ragged_lens(c["B"], c["L"], seed=6, min_len=c["min_len"], device=dev)
+        out = torch.empty(c["B"], c["Hq"], c["D"], dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda i: sb.xattn_decode(x.q, x.K, x.V, out=out, lens=lens), 20)
+        nbytes = int(lens.sum().item()) * c["Hkv"] * c["D"] * 4
+        res["xattn_decode_varlen_B32_L34816_ragged"] = {
+            "us_per_call": round(1e3 * ms, 1), "cached_positions": int(lens.sum().item()),
+            "gbps": round(nbytes / ms / 1e6, 1), "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
             "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
-        del m
-    del msets
-    # SSM layer over the prompt: 4 x 2048 tokens at the model width.
-    c = workload.MAMBA_DECODE
-    dm, di, N, R, K = c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"], c["d_conv"]
-    Bp, Tp = workload.ATTN_PREFILL["B"], workload.ATTN_PREFILL["T"]
-    m = workload.mamba_inputs(Bp, dm, di, N, R, K, seed=95, device=dev)
-    xs = workload.normal((Bp, Tp, dm), seed=96, device=dev)
-    Mo = torch.empty(Bp, Tp, di, dtype=torch.bfloat16, device=dev)
-    yo = torch.empty(Bp, Tp, dm, dtype=torch.bfloat16, device=dev)
-    ms = time_calls(lambda i: sb.mamba_prefill(xs, m.w, m.conv_state, m.ssm_state, Mo, yo), 10)
-    rows = Bp * Tp
-    flops = 2.0 * rows * (2 * di * dm + ((R + 2 * N + 63) // 64 * 64) * di + di * R + dm * di)
-    res["mamba_prefill_B%d_T%d" % (Bp, Tp)] = {
-        "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
-        "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4)}
-    del m, xs, Mo, yo
-    # YOCO-style prefill of the whole model: 4 x 2048 prompt tokens through the
-    # 16-layer self-decoder, then the 16-layer cross-decoder on the last token;
-    # the self-decoder alone timed beside it (the cross-decoder's share is the
-    # difference).
-    c = workload.SAMBAY_PREFILL
-    yp = workload.sambay_prefill_inputs(c["B"], c["T"], c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"],
-                                        c["d_conv"], c["d_ff"], c["Hq"], c["Hkv"], c["D"], c["window"], c["L"],
-                                        workload.self_layer_kinds(c["n_self"]), workload.layer_kinds(c["n_cross"]),
-                                        seed=97, device=dev)
-    full = sb.SambayPrefill(yp.x, yp.self_layers, yp.cross_layers, yp.kcache, yp.vcache, window=c["window"])
-    selfonly = sb.SambayPrefill(yp.x, yp.self_layers, [], yp.kcache, yp.vcache, window=c["window"])
-    ms_full = time_calls(lambda i: full(), 5, warmup=2)
-    ms_self = time_calls(lambda i: selfonly(), 5, warmup=1)
-    rows = c["B"] * c["T"]
-    res["sambay_prefill_B%d_T%d" % (c["B"], c["T"])] = {
-        "ms": round(ms_full, 3), "prompt_tokens_per_s": round(rows / ms_full * 1e3, 1),
-        "self_decoder_ms": round(ms_self, 3), "cross_decoder_last_token_ms": round(ms_full - ms_self, 3),
-        "layers": "16 self (8 SSM, 7 sliding-window 256, 1 full attention) + 16 cross (8 attention, 8 GMU), "
-                  "SwiGLU d_ff 8192 in every layer"}
-    del yp, full, selfonly
-    # Prefill attention over the prompt: 4 x 2048 tokens, window 256 (the
-    # self-decoder's sliding-window layers), and plain causal at 1 x 2048.
-    c = workload.ATTN_PREFILL
-    for B, W in ((c["B"], c["window"]), (1, 0)):
-        x = workload.prefill_inputs(B, c["T"], c["Hq"], c["Hkv"], c["D"], seed=90 + W, device=dev)
-        o = torch.empty_like(x.q)
-        ms = time_calls(lambda i: sb.attn_prefill(x.q, x.k, x.v, window=W, out=o), 20)
-        T, D = c["T"], c["D"]
-        keys = sum(min(i + 1, W) if W else i + 1 for i in range(T))        # visible (query, key) pairs per head
-        flops = 4.0 * D * keys * c["Hq"] * B
-        nbytes = B * T * (2 * c["Hq"] + 2 * c["Hkv"]) * D * 2
-        res["attn_prefill_B%d_T%d_window%d" % (B, T, W)] = {
-            "us_per_call": round(1e3 * ms, 2), "tflops": round(flops / ms / 1e9, 1),
-            "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4), "gbps": round(nbytes / ms / 1e6, 1),
+        # Self-decoder attention steps: the final full-attention layer appends each
+        # sequence's new row to the same cache at position lens - 1 and attends over
+        # lens positions; a sliding-window layer does the same on a 256-slot ring.
+        kn = workload.normal((c["B"], c["Hkv"], c["D"]), seed=60, device=dev)
+        vn = workload.normal((c["B"], c["Hkv"], c["D"]), seed=61, device=dev)
+        pos = (lens - 1).to(torch.int32)
+        ms = time_calls(lambda i: sb.selfattn_decode(x.q, kn, vn, x.K, x.V, pos, out=out), 20)
+        nbytes = int(lens.sum().item()) * c["Hkv"] * c["D"] * 4 + c["B"] * c["Hkv"] * c["D"] * 4
+        res["selfattn_decode_full_B32_L34816_ragged"] = {
+            "us_per_call": round(1e3 * ms, 1), "gbps": round(nbytes / ms / 1e6, 1),
             "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
-        del x, o
-    # Complete cross-decoder layer step (pre-RMSNorm mixer + pre-RMSNorm SwiGLU MLP, d_ff 8192) on that ragged batch.
-    c = workload.CROSSDECODER_EX
-    x = workload.crossdecoder_ex_inputs(c["B"], c["d_model"], c["d_inner"], c["d_ff"], c["Hq"], c["Hkv"], c["D"],
-                                        c["L"], c["n_layers"], seed=7, device=dev, lens="ragged",
-                                        min_len=c["min_len"])
-    h_in = x.h.clone()
-    step = sb.CrossDecoderStepEx(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+        del x
+        torch.cuda.empty_cache()
+        W = workload.SELFATTN_SWA["window"]
+        r = workload.selfattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], W, seed=62, device=dev)
+        call = lambda i: sb.selfattn_decode(r.q, r.k_new, r.v_new, r.K, r.V, pos, window=W, out=out)
+        ms_eager = time_calls(call, 50)
+        ms = time_graph(call, 20)
+        nbytes = c["B"] * c["Hkv"] * W * c["D"] * 4 + c["B"] * c["Hkv"] * c["D"] * 4
+        res["selfattn_decode_window256_B32"] = {
+            "us_per_call": round(1e3 * ms, 2), "timing": "HIP graph replay of 20 calls",
+            "us_per_call_eager": round(1e3 * ms_eager, 2), "gbps": round(nbytes / ms / 1e6, 1),
+            "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        del r
+    if want("mamba_decode"):
+        # SSM decode step (the Mamba layer producing M): 4 rotating weight sets
+        # (4 x 118 MB, more than the 256 MB last-level cache) so that the weights
+        # stream from HBM as they would layer after layer.
+        c = workload.MAMBA_DECODE
+        dm, di, N, R, K = c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"], c["d_conv"]
+        msets = [workload.mamba_inputs(1, dm, di, N, R, K, seed=70 + k, device=dev).w for k in range(4)]
+        wbytes = (2 * di * dm + (R + 2 * N) * di + di * R + dm * di) * 2 + (di * K + 3 * di + di * N) * 4
+        for B in (1, 32):
+            m = workload.mamba_inputs(B, dm, di, N, R, K, seed=80 + B, device=dev)
+            Mo = torch.empty(B, di, dtype=torch.bfloat16, device=dev)
+            yo = torch.empty(B, dm, dtype=torch.bfloat16, device=dev)
+            ms = time_calls(lambda i: sb.mamba_decode_step(m.x, msets[i % 4], m.conv_state, m.ssm_state, Mo, yo), 40)
+            nbytes = wbytes + B * di * (N + K - 1) * 4 * 2 + B * (2 * dm + di) * 2
+            res["mamba_decode_B%d" % B] = {
+                "us_per_call": round(1e3 * ms, 2), "hbm_bytes": nbytes, "gbps": round(nbytes / ms / 1e6, 1),
+                "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                "frac_of_stream_read": round(nbytes / ms / 1e6 / read_gbps, 4)}
+            del m
+        del msets
+    if want("mamba_prefill"):
+        # SSM layer over the prompt: 4 x 2048 tokens at the model width.
+        c = workload.MAMBA_DECODE
+        dm, di, N, R, K = c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"], c["d_conv"]
+        Bp, Tp = workload.ATTN_PREFILL["B"], workload.ATTN_PREFILL["T"]
+        m = workload.mamba_inputs(Bp, dm, di, N, R, K, seed=95, device=dev)
+        xs = workload.normal((Bp, Tp, dm), seed=96, device=dev)
+        Mo = torch.empty(Bp, Tp, di, dtype=torch.bfloat16, device=dev)
+        yo = torch.empty(Bp, Tp, dm, dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda i: sb.mamba_prefill(xs, m.w, m.conv_state, m.ssm_state, Mo, yo), 10)
+        rows = Bp * Tp
+        flops = 2.0 * rows * (2 * di * dm + ((R + 2 * N + 63) // 64 * 64) * di + di * R + dm * di)
+        res["mamba_prefill_B%d_T%d" % (Bp, Tp)] = {
+            "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+            "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4)}
+        del m, xs, Mo, yo
+    if want("sambay_prefill"):
+        # YOCO-style prefill of the whole model: 4 x 2048 prompt tokens through the
+        # 16-layer self-decoder, then the 16-layer cross-decoder on the last token;
+        # the self-decoder alone timed beside it (the cross-decoder's share is the
+        # difference).
+        c = workload.SAMBAY_PREFILL
+        yp = workload.sambay_prefill_inputs(c["B"], c["T"], c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"],
+                                            c["d_conv"], c["d_ff"], c["Hq"], c["Hkv"], c["D"], c["window"], c["L"],
+                                            workload.self_layer_kinds(c["n_self"]), workload.layer_kinds(c["n_cross"]),
+                                            seed=97, device=dev)
+        full = sb.SambayPrefill(yp.x, yp.self_layers, yp.cross_layers, yp.kcache, yp.vcache, window=c["window"])
+        selfonly = sb.SambayPrefill(yp.x, yp.self_layers, [], yp.kcache, yp.vcache, window=c["window"])
+        ms_full = time_calls(lambda i: full(), 5, warmup=2)
+        ms_self = time_calls(lambda i: selfonly(), 5, warmup=1)
+        rows = c["B"] * c["T"]
+        res["sambay_prefill_B%d_T%d" % (c["B"], c["T"])] = {
+            "ms": round(ms_full, 3), "prompt_tokens_per_s": round(rows / ms_full * 1e3, 1),
+            "self_decoder_ms": round(ms_self, 3), "cross_decoder_last_token_ms": round(ms_full - ms_self, 3),
+            "layers": "16 self (8 SSM, 7 sliding-window 256, 1 full attention) + 16 cross (8 attention, 8 GMU), "
+                      "SwiGLU d_ff 8192 in every layer"}
+        del yp, full, selfonly
+    if want("attn_prefill"):
+        # Prefill attention over the prompt: 4 x 2048 tokens, window 256 (the
+        # self-decoder's sliding-window layers), and plain causal at 1 x 2048.
+        c = workload.ATTN_PREFILL
+        for B, W in ((c["B"], c["window"]), (1, 0)):
+            x = workload.prefill_inputs(B, c["T"], c["Hq"], c["Hkv"], c["D"], seed=90 + W, device=dev)
+            o = torch.empty_like(x.q)
+            ms = time_calls(lambda i: sb.attn_prefill(x.q, x.k, x.v, window=W, out=o), 20)
+            T, D = c["T"], c["D"]
+            keys = sum(min(i + 1, W) if W else i + 1 for i in range(T))        # visible (query, key) pairs per head
+            flops = 4.0 * D * keys * c["Hq"] * B
+            nbytes = B * T * (2 * c["Hq"] + 2 * c["Hkv"]) * D * 2
+            res["attn_prefill_B%d_T%d_window%d" % (B, T, W)] = {
+                "us_per_call": round(1e3 * ms, 2), "tflops": round(flops / ms / 1e9, 1),
+                "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4), "gbps": round(nbytes / ms / 1e6, 1),
+                "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+            del x, o
+    if want("crossdecoder_ex"):
+        # Complete cross-decoder layer step (pre-RMSNorm mixer + pre-RMSNorm SwiGLU MLP, d_ff 8192) on that ragged batch.
+        c = workload.CROSSDECODER_EX
+        x = workload.crossdecoder_ex_inputs(c["B"], c["d_model"], c["d_inner"], c["d_ff"], c["Hq"], c["Hkv"], c["D"],
+                                            c["L"], c["n_layers"], seed=7, device=dev, lens="ragged",
+                                            min_len=c["min_len"])
+        h_in = x.h.clone()
+        step = sb.CrossDecoderStepEx(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
 
-    def run(i):
-        x.h.copy_(h_in)
-        step()
+        def run(i):
+            x.h.copy_(h_in)
+            step()
 
-    ms = time_calls(run, 10)
-    n_x = c["n_layers"] // 2
-    dm, di, dff = c["d_model"], c["d_inner"], c["d_ff"]
-    kv = int(x.lens.sum().item()) * c["Hkv"] * c["D"] * 4
-    nbytes = (n_x * kv + n_x * 2 * dm * dm * 2 + (c["n_layers"] - n_x) * 2 * dm * di * 2
-              + c["n_layers"] * (3 * dm * dff + 2 * dm) * 2)
-    res["crossdecoder_ex_B32_ragged_dff8192"] = {
-        "ms_per_step": round(ms, 4), "tokens_per_s": round(c["B"] / (ms / 1e3), 1), "hbm_bytes_per_step": nbytes,
-        "gbps": round(nbytes / ms / 1e6, 1), "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
-    del step, x
-    torch.cuda.empty_cache()
+        ms = time_calls(run, 10)
+        n_x = c["n_layers"] // 2
+        dm, di, dff = c["d_model"], c["d_inner"], c["d_ff"]
+        kv = int(x.lens.sum().item()) * c["Hkv"] * c["D"] * 4
+        nbytes = (n_x * kv + n_x * 2 * dm * dm * 2 + (c["n_layers"] - n_x) * 2 * dm * di * 2
+                  + c["n_layers"] * (3 * dm * dff + 2 * dm) * 2)
+        res["crossdecoder_ex_B32_ragged_dff8192"] = {
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(c["B"] / (ms / 1e3), 1), "hbm_bytes_per_step": nbytes,
+            "gbps": round(nbytes / ms / 1e6, 1), "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        del step, x
+        torch.cuda.empty_cache()
     return res
 
 
@@ -366,6 +381,8 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle CPU sample")
     ap.add_argument("--all", action="store_true",
                     help="also time the other workloads (GMU prefill, GMU decode per batch, attention alone)")
+    ap.add_argument("--only", default="", metavar="GROUPS",
+                    help="with --all: only these comma-separated workload groups (%s)" % ", ".join(WORKLOAD_GROUPS))
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 5 times (reference for HBM counters) and exit")
     args = ap.parse_args()
@@ -487,7 +504,10 @@ def main():
     if args.all:
         log("bench: timing the other workloads")
         del step
-        workloads = other_workloads(sb, workload, dev, read_gbps, mfma_tf)
+        only = [g for g in args.only.split(",") if g] or None
+        if only and any(g not in WORKLOAD_GROUPS for g in only):
+            raise SystemExit("--only: unknown group in %r (known: %s)" % (args.only, ", ".join(WORKLOAD_GROUPS)))
+        workloads = other_workloads(sb, workload, dev, read_gbps, mfma_tf, only=only)
 
     out = {
         "metric": METRIC,
