@@ -108,6 +108,22 @@ def test_gmu_prefill_full_sampled_rows(sb):
     report("gmu prefill 8192x2560x5120 (%d rows)" % len(idx), err(f64(Y[ii]), ref), TOL_BF16)
 
 
+@pytest.mark.parametrize("rows,d_model,d_inner", [(4000, 1024, 4096), (4000, 1024, 2048)])
+def test_gmu_prefill_wide_tiles(sb, rows, d_model, d_inner):
+    """Shapes whose gate product fills whole rounds of 256 CUs with 256x256
+    tiles (d_inner 4096) or 256x128 tiles (d_inner 2048); 4000 rows leave a
+    ragged last row tile.  The oracle checks 64 sampled rows."""
+    g = workload.gmu_inputs(rows, d_model, d_inner, seed=8, device=DEV)
+    Y = sb.gmu_forward(g.M, g.X, g.W1, g.W2)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    idx = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 3839, 3840, rows - 2, rows - 1],
+                                    rng.choice(rows, 54, replace=False)]))
+    ii = torch.from_numpy(idx).to(DEV)
+    ref = oracle.gmu(cpu(g.M[ii]), cpu(g.X[ii]), cpu(g.W1), cpu(g.W2))
+    report("gmu prefill %dx%dx%d (%d rows)" % (rows, d_model, d_inner, len(idx)), err(f64(Y[ii]), ref), TOL_BF16)
+
+
 def test_gmu_zero_rows_is_noop(sb):
     g = workload.gmu_inputs(1, 64, 128, device=DEV)
     out = torch.full((0, 64), 7.0, dtype=torch.bfloat16, device=DEV)
