@@ -9,8 +9,8 @@
 //  * 128x128 output tile per workgroup, 4 waves in a 2x2 grid, each wave a
 //    64x64 block of 2x2 32x32x16 MFMA tiles (on gfx950 the 32x32x16 bf16 form
 //    measured ~2.4 PFLOP/s in a register-only loop, the 16x16x32 form ~1.4);
-//    256x256 (8 waves of 128x64) and 256x128 (8 waves of 64x64) tiles where
-//    their grid fills whole rounds of the 256 CUs (launch_gemm's rule).
+//    256x256 tiles (8 waves of 128x64) where their grid fills whole rounds
+//    of the 256 CUs (launch_gemm's rule).
 //  * K advances BK = 64 at a time through a two-stage LDS ring filled by direct
 //    global -> LDS loads (global_load_lds_dwordx4): no register staging, and
 //    the next stage's loads run under this stage's MFMAs.  A bare s_barrier
@@ -269,18 +269,15 @@ hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K,
     if (ksplit < 1 || K % (64 * ksplit) != 0 || (ksplit > 1 && epi != EPI_F32)) return hipErrorInvalidValue;
     // Tile shape by how the grid fills the 256 CUs (measured on the prefill
     // shapes, random operands): 256x256 tiles of 8 waves (128x64 each, one
-    // workgroup per CU) read a third less LDS per MFMA and win by 15-17%
+    // workgroup per CU) read a third less LDS per MFMA and win by 15-20%
     // when their tile count is a whole number of 256-wide rounds (8192 x
     // 8192 x 3072: 1071 vs 921 TFLOP/s; 8192 x 12288 x 3072: 1100 vs 937);
-    // 256x128 tiles of 8 waves win on short K when they fill whole rounds
-    // (8192 x 5120 x 2560 with the gate epilogue: 762 vs 708); otherwise the
-    // 128x128 tiles, two workgroups per CU, balance a partial last round best.
+    // otherwise two 128x128 workgroups per CU are best and also balance a
+    // partial last round best (256x128 tiles of 8 waves measured equal or
+    // slower on every prefill shape once the clocks had settled).
     const int64_t t256 = (int64_t)((rows + 255) / 256) * ((N + 255) / 256);
-    const int64_t t256x128 = (int64_t)((rows + 255) / 256) * ((N + 127) / 128);
     if (ksplit == 1 && t256 >= 256 && t256 % 256 == 0)
         return launch_tile<256, 256, 2, 4, 2, 64>(X, W, rows, N, K, epi, out, aux, ksplit, stream);
-    if (ksplit == 1 && K <= 4096 && t256x128 >= 256 && t256x128 % 256 == 0)
-        return launch_tile<256, 128, 4, 2, 2, 64>(X, W, rows, N, K, epi, out, aux, ksplit, stream);
     return launch_tile<128, 128, 2, 2, 2, 64>(X, W, rows, N, K, epi, out, aux, ksplit, stream);
 }
 

@@ -110,9 +110,9 @@ def test_gmu_prefill_full_sampled_rows(sb):
 
 @pytest.mark.parametrize("rows,d_model,d_inner", [(4000, 1024, 4096), (4000, 1024, 2048)])
 def test_gmu_prefill_wide_tiles(sb, rows, d_model, d_inner):
-    """Shapes whose gate product fills whole rounds of 256 CUs with 256x256
-    tiles (d_inner 4096) or 256x128 tiles (d_inner 2048); 4000 rows leave a
-    ragged last row tile.  The oracle checks 64 sampled rows."""
+    """The gate product of d_inner 4096 fills a whole round of 256 CUs with
+    256x256 tiles (d_inner 2048: 128x128 tiles); 4000 rows leave a ragged
+    last row tile.  The oracle checks 64 sampled rows."""
     g = workload.gmu_inputs(rows, d_model, d_inner, seed=8, device=DEV)
     Y = sb.gmu_forward(g.M, g.X, g.W1, g.W2)
     torch.cuda.synchronize()
