@@ -24,6 +24,7 @@
 #include "launch.hpp"
 
 #include <math.h>
+#include <stdlib.h>
 
 namespace sambay {
 
@@ -454,6 +455,12 @@ hipError_t launch_mamba_scan(const float *xz, int ldxz, const float *u, const fl
 // Tokens per scan chunk: 64, halved (to 16 at least) while the scan would
 // have fewer than 8192 waves (32 per CU).
 static int mamba_scan_chunk(int64_t B, int64_t T, int64_t d_inner, int64_t NS) {
+    // SAMBAY_SCAN_CHUNK (a multiple of 8, 8..512) overrides the rule (measurement).
+    const char *env = getenv("SAMBAY_SCAN_CHUNK");
+    if (env && *env) {
+        const int v = atoi(env);
+        if (v >= 8 && v <= 512 && v % 8 == 0) return v;
+    }
     int Lc = 64;
     const int64_t waves = B * d_inner * scan_lanes_per_channel((int)NS) / 64;
     while (Lc > 16 && waves * ((T + Lc - 1) / Lc) < 8192) Lc /= 2;

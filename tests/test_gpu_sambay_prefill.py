@@ -99,6 +99,13 @@ def test_sambay_prefill_small(sb, B, T, W):
          name="small B=%d T=%d W=%d" % (B, T, W))
 
 
+def test_sambay_prefill_cache_written_by_an_earlier_layer(sb):
+    """The full-attention layer first (it is then computed over every token,
+    not finished on the last one), SSM and sliding-window layers after it."""
+    _run(sb, 2, 75, 256, 512, 16, 64, 4, 512, 2, 1, 16, 96, ["attn", "mamba", "swa"], ["xattn", "gmu"], seed=21,
+         name="attention first B=2 T=75")
+
+
 def test_sambay_prefill_without_mlps_or_cross_layers(sb):
     inp = workload.sambay_prefill_inputs(2, 70, 256, 512, 16, 64, 4, 0, 2, 2, 128, 16, 80, ["mamba", "attn"], [],
                                          seed=9, device=DEV, fresh=True, mlp=False, norms=False)
