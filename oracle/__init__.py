@@ -627,3 +627,61 @@ def sambay_prefill(x, self_layers: Sequence, cross_layers: Sequence, Hq: int, Hk
         h_out = crossdecoder_ex(h_last, M_last if M_last is not None else np.zeros((B, 1)), K, V, cross_layers, Hq,
                                 eps=eps, scale=scale, round_bf16=round_h)
     return {"h_out": h_out, "h_last": h_last, "M_last": M_last, "K": K, "V": V, "layers": per_layer}
+
+
+def sambay_decode_step(x, self_layers: Sequence, cross_layers: Sequence, Hq: int, Hkv: int, pos, K, V,
+                       window: int = 0, eps: float = 1e-5, scale: float | None = None, round_h: bool = True) -> dict:
+    """One decode step of the whole model: the new token rows x [B, d_model]
+    at positions pos [B] through the self-decoder's layers, one step each
+    (the layers of sambay_prefill: mamba_step on the layer's states, selfattn
+    on its ring of `window` slots or on the shared cache K, V [B, Hkv, L,
+    D]), then crossdecoder_ex with cache lengths min(pos + 1, L).  Layer
+    dicts as for sambay_prefill, with each SSM layer's conv_state /
+    ssm_state and each sliding-window layer's kring / vring (CPU arrays)
+    as the state before the step.
+
+    Returns a dict: h_out [B, d_model], h_self (after the self-decoder),
+    M_last, K, V (the shared cache after the step), per layer "layers":
+    {conv_state, ssm_state} or {kring, vring} after the step, float64."""
+    h = _f64(x)
+    if h.ndim != 2:
+        raise ValueError("x must be [B, d_model]")
+    B, dm = h.shape
+    D = dm // Hq
+    rnd = round_bf16_array if round_h else (lambda a: a)
+    h = rnd(h)
+    pa = np.ascontiguousarray(np.asarray(pos.cpu() if hasattr(pos, "cpu") else pos), dtype=np.int32)
+    Kc, Vc = _f64(K), _f64(V)
+    L = Kc.shape[2]
+    M_mem, per_layer = None, []
+    for ly in self_layers:
+        kind = ly["kind"]
+        xin = rmsnorm(h, ly["norm1"], eps) if ly.get("norm1") is not None else h
+        if kind == "mamba":
+            M, y, cs, ss = mamba_step(xin, ly["w"], ly["conv_state"], ly["ssm_state"])
+            h = rnd(h + y)
+            M_mem = M
+            per_layer.append({"conv_state": cs, "ssm_state": ss})
+        elif kind in ("swa", "attn"):
+            q = (xin @ _f64(ly["wq"]).T).reshape(B, Hq, D)
+            kn = (xin @ _f64(ly["wk"]).T).reshape(B, Hkv, D)
+            vn = (xin @ _f64(ly["wv"]).T).reshape(B, Hkv, D)
+            if kind == "swa":
+                o, kr, vr = selfattn(q, kn, vn, ly["kring"], ly["vring"], pa, window=window, scale=scale)
+                per_layer.append({"kring": kr, "vring": vr})
+            else:
+                o, Kc, Vc = selfattn(q, kn, vn, Kc, Vc, pa, window=0, scale=scale)
+                per_layer.append({})
+            h = rnd(h + o.reshape(B, dm) @ _f64(ly["wo"]).T)
+        else:
+            raise ValueError("self layer kind must be 'mamba', 'swa' or 'attn'")
+        if ly.get("w_gate") is not None:
+            xm = rmsnorm(h, ly["norm2"], eps) if ly.get("norm2") is not None else h
+            h = rnd(h + swiglu(xm, ly["w_gate"], ly["w_up"], ly["w_down"]))
+    h_self = h
+    h_out = h
+    if cross_layers:
+        lens = np.minimum(np.maximum(pa.astype(np.int64) + 1, 0), L)
+        h_out = crossdecoder_ex(h, M_mem if M_mem is not None else np.zeros((B, 1)), Kc, Vc, cross_layers, Hq,
+                                lens=lens, eps=eps, scale=scale, round_bf16=round_h)
+    return {"h_out": h_out, "h_self": h_self, "M_last": M_mem, "K": Kc, "V": Vc, "layers": per_layer}

@@ -8,9 +8,9 @@ Generation", section 整体框架; Samba's alternation of SSM and sliding-window
 layers, section 消融实验).  The composition is pinned against a different
 computation, the recurrent one:
 - prefill of T - 1 tokens followed by one decode step of the last token
-  through the per-token oracles (mamba_step, selfattn on the ring or the
-  full cache, the norms and MLPs, crossdecoder_ex) equals prefill of T
-  tokens, to fp64 rounding, with every intermediate compared;
+  (oracle.sambay_decode_step: the per-token oracles mamba_step, selfattn on
+  the ring or the full cache, the norms and MLPs, crossdecoder_ex) equals
+  prefill of T tokens, to fp64 rounding, with every intermediate compared;
 - causality: the cache rows of earlier positions do not depend on the last
   token; a window of at least T is plain causal attention;
 - the vectorised bfloat16 rounding used for the residual stream equals the
@@ -51,58 +51,64 @@ def test_round_bf16_array_matches_the_scalar_definition():
     assert np.array_equal(oracle.round_bf16_array(x), oracle.round_bf16(x))
 
 
-def _decode_last_token(inp, pre, xs_last):
-    """The token at position T-1 through the per-token oracles, from the
-    states and cache rows that a prefill of the first T-1 tokens left."""
-    h = _f64(xs_last)
-    M_mem, K_full, V_full, states = None, None, None, {}
-    pos = np.full(B, T - 1, dtype=np.int32)
+def _caches_after_prefill(inp, pre, T_pre):
+    """Ring and shared-cache contents that a prefill of T_pre tokens leaves
+    (from the per-layer keys and values it computed), and the SSM states."""
+    layers = []
+    K = V = None
     for i, ly in enumerate(inp.self_layers):
-        xin = oracle.rmsnorm(h, ly["norm1"]) if ly.get("norm1") is not None else h
-        st = pre["layers"][i]
+        st = dict(ly)
+        r = pre["layers"][i]
         if ly["kind"] == "mamba":
-            M, y, cs, ss = oracle.mamba_step(xin, ly["w"], st["conv_state"], st["ssm_state"])
-            states[i] = (cs, ss)
-            h = h + y
-            M_mem = M
+            st["conv_state"], st["ssm_state"] = r["conv_state"], r["ssm_state"]
+        elif ly["kind"] == "swa":
+            kr, vr = np.zeros((B, HKV, W, D)), np.zeros((B, HKV, W, D))
+            for p in range(max(0, T_pre - W), T_pre):
+                kr[:, :, p % W], vr[:, :, p % W] = r["k"][:, p], r["v"][:, p]
+            st["kring"], st["vring"] = kr, vr
         else:
-            q = (xin @ _f64(ly["wq"]).T).reshape(B, HQ, D)
-            kn = (xin @ _f64(ly["wk"]).T).reshape(B, HKV, D)
-            vn = (xin @ _f64(ly["wv"]).T).reshape(B, HKV, D)
-            kp, vp = st["k"], st["v"]                                  # [B, T-1, Hkv, D]
-            if ly["kind"] == "swa":
-                Kc = np.zeros((B, HKV, W, D))
-                Vc = np.zeros((B, HKV, W, D))
-                for p in range(max(0, T - 1 - W), T - 1):
-                    Kc[:, :, p % W], Vc[:, :, p % W] = kp[:, p], vp[:, p]
-                o, _, _ = oracle.selfattn(q, kn, vn, Kc, Vc, pos, window=W)
-            else:
-                Kc = np.zeros((B, HKV, T, D))
-                Vc = np.zeros((B, HKV, T, D))
-                Kc[:, :, :T - 1] = kp.transpose(0, 2, 1, 3)
-                Vc[:, :, :T - 1] = vp.transpose(0, 2, 1, 3)
-                o, K_full, V_full = oracle.selfattn(q, kn, vn, Kc, Vc, pos, window=0)
-            h = h + o.reshape(B, DM) @ _f64(ly["wo"]).T
-        if ly.get("w_gate") is not None:
-            h = h + oracle.swiglu(oracle.rmsnorm(h, ly["norm2"]), ly["w_gate"], ly["w_up"], ly["w_down"])
-    h_out = oracle.crossdecoder_ex(h, M_mem, K_full, V_full, inp.cross_layers, HQ, round_bf16=False)
-    return h, M_mem, K_full, V_full, h_out, states
+            K, V = np.zeros((B, HKV, T_pre + 1, D)), np.zeros((B, HKV, T_pre + 1, D))
+            K[:, :, :T_pre] = r["k"].transpose(0, 2, 1, 3)
+            V[:, :, :T_pre] = r["v"].transpose(0, 2, 1, 3)
+        layers.append(st)
+    return layers, K, V
 
 
 def test_prefill_equals_prefill_then_one_decode_step():
+    """oracle.sambay_decode_step (per-token oracles, the recurrent form)
+    after a prefill of T - 1 tokens equals a prefill of T tokens."""
     inp = _inputs()
     full = oracle.sambay_prefill(inp.x, inp.self_layers, inp.cross_layers, HQ, HKV, window=W, round_h=False)
     pre = oracle.sambay_prefill(inp.x[:, :T - 1], inp.self_layers, [], HQ, HKV, window=W, round_h=False)
-    h, M, Kf, Vf, h_out, states = _decode_last_token(inp, pre, inp.x[:, T - 1])
-    assert _rel(full["h_last"], h) <= 1e-11
-    assert _rel(full["M_last"], M) <= 1e-11
-    assert _rel(full["K"], Kf) <= 1e-12 and _rel(full["V"], Vf) <= 1e-12
-    assert _rel(full["h_out"], h_out) <= 1e-11
+    layers, K, V = _caches_after_prefill(inp, pre, T - 1)
+    step = oracle.sambay_decode_step(inp.x[:, T - 1], layers, inp.cross_layers, HQ, HKV, np.full(B, T - 1), K, V,
+                                     window=W, round_h=False)
+    assert _rel(full["h_last"], step["h_self"]) <= 1e-11
+    assert _rel(full["M_last"], step["M_last"]) <= 1e-11
+    assert _rel(full["K"], step["K"]) <= 1e-12 and _rel(full["V"], step["V"]) <= 1e-12
+    assert _rel(full["h_out"], step["h_out"]) <= 1e-11
     # the SSM states after the prompt: those after T-1 tokens stepped once more
-    assert len(states) == 2
-    for i, (cs, ss) in states.items():
-        assert _rel(full["layers"][i]["conv_state"], cs) <= 1e-12
-        assert _rel(full["layers"][i]["ssm_state"], ss) <= 1e-11
+    n = 0
+    for i, ly in enumerate(inp.self_layers):
+        if ly["kind"] == "mamba":
+            n += 1
+            assert _rel(full["layers"][i]["conv_state"], step["layers"][i]["conv_state"]) <= 1e-12
+            assert _rel(full["layers"][i]["ssm_state"], step["layers"][i]["ssm_state"]) <= 1e-11
+    assert n == 2
+
+
+def test_decode_step_ring_holds_the_last_window_tokens():
+    """After the step, a sliding-window layer's ring holds the keys of the
+    last `window` tokens (prefill of T tokens), slot = position mod window."""
+    inp = _inputs(seed=12)
+    full = oracle.sambay_prefill(inp.x, inp.self_layers, [], HQ, HKV, window=W, round_h=False)
+    pre = oracle.sambay_prefill(inp.x[:, :T - 1], inp.self_layers, [], HQ, HKV, window=W, round_h=False)
+    layers, K, V = _caches_after_prefill(inp, pre, T - 1)
+    step = oracle.sambay_decode_step(inp.x[:, T - 1], layers, [], HQ, HKV, np.full(B, T - 1), K, V, window=W,
+                                     round_h=False)
+    i = [j for j, ly in enumerate(inp.self_layers) if ly["kind"] == "swa"][0]
+    for p in range(T - W, T):
+        assert _rel(step["layers"][i]["kring"][:, :, p % W], full["layers"][i]["k"][:, p]) <= 1e-12
 
 
 def test_cache_rows_of_earlier_positions_ignore_the_last_token():
