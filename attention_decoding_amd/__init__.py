@@ -36,7 +36,8 @@ EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", 
            "xattn_decode_varlen", "crossdecoder_ex_workspace_bytes", "crossdecoder_step_ex",
            "diffattn_workspace_bytes", "diffattn_decode", "selfattn_workspace_bytes", "selfattn_decode",
            "mamba_workspace_bytes", "mamba_decode_step", "attn_prefill_workspace_bytes", "attn_prefill",
-           "mamba_prefill_workspace_bytes", "mamba_prefill", "sambay_prefill_workspace_bytes", "sambay_prefill")
+           "mamba_prefill_workspace_bytes", "mamba_prefill", "sambay_prefill_workspace_bytes", "sambay_prefill",
+           "sambay_decode_workspace_bytes", "sambay_decode_step")
 SB_TIME_XATTN_SPLIT, SB_TIME_XATTN_MERGE, SB_TIME_SKINNY, SB_TIME_GEMM, SB_TIME_GMU_F32, SB_TIME_PROBE = \
     1, 2, 4, 8, 16, 32
 SB_TIME_DIFF_SPLIT, SB_TIME_DIFF_MERGE, SB_TIME_PREFILL = 64, 128, 256
@@ -128,6 +129,11 @@ def _load() -> ctypes.CDLL:
     lib.sambay_prefill.argtypes = [vp, vp, vp, ctypes.POINTER(SbSelfLayer), i32, ctypes.POINTER(SbLayerEx), i32, vp,
                                    vp] + [i64] * 13 + [ctypes.c_float, ctypes.c_float, vp, sz, vp]
     lib.sambay_prefill.restype = ctypes.c_int
+    lib.sambay_decode_workspace_bytes.argtypes = [i64] * 12
+    lib.sambay_decode_workspace_bytes.restype = sz
+    lib.sambay_decode_step.argtypes = [vp, vp, ctypes.POINTER(SbSelfLayer), i32, ctypes.POINTER(SbLayerEx), i32, vp,
+                                       vp, vp] + [i64] * 12 + [ctypes.c_float, ctypes.c_float, vp, sz, vp]
+    lib.sambay_decode_step.restype = ctypes.c_int
     lib.sb_timing_enable.argtypes = [ctypes.c_uint32]
     lib.sb_timing_enable.restype = ctypes.c_int
     lib.sb_timing_collect.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -648,6 +654,54 @@ def crossdecoder_step_ex(h: torch.Tensor, M: torch.Tensor, kcache: torch.Tensor,
 _SELF_KINDS = {"mamba": SB_SELF_MAMBA, "swa": SB_SELF_SWA, "attn": SB_SELF_ATTN}
 
 
+def _self_layer_array(self_layers: Sequence, cross_layers: Sequence, dev, B: int, d_model: int, Hkv: int, D: int,
+                      window: int):
+    """sb_self_layer descriptors for the self-decoder layer dicts (see
+    SambayPrefill); returns (array, (d_inner, d_state, dt_rank, d_conv), d_ff)."""
+    bf, f32 = torch.bfloat16, torch.float32
+    mamba = [ly for ly in self_layers if ly["kind"] == "mamba"]
+    if mamba:
+        _, d_inner, d_state, dt_rank, d_conv = _mamba_weights(mamba[0]["w"], dev, d_model)
+    else:  # no SSM layer: any supported SSM shape sizes the (unused) memory
+        d_inner, d_state, dt_rank, d_conv = 64, 8, 64, 1
+        for ly in cross_layers:
+            if ly["kind"] == "gmu":
+                d_inner = ly["w_a"].shape[0]
+    d_ff = max(_mlp_width(self_layers), _mlp_width(cross_layers))
+    arr = (SbSelfLayer * max(len(self_layers), 1))()
+    for i, ly in enumerate(self_layers):
+        kind = ly["kind"]
+        if kind not in _SELF_KINDS:
+            raise ValueError("self layer kind must be 'mamba', 'swa' or 'attn'")
+        arr[i].kind = _SELF_KINDS[kind]
+        if kind == "mamba":
+            sw, di, ds, dr, dc = _mamba_weights(ly["w"], dev, d_model)
+            if (di, ds, dr, dc) != (d_inner, d_state, dt_rank, d_conv):
+                raise ValueError("every SSM layer must have the same shape")
+            if ly["ssm_state"].shape != (B, d_inner, d_state) or \
+                    (d_conv > 1 and ly["conv_state"].shape != (B, d_inner, d_conv - 1)):
+                raise ValueError("self layer %d: state shape mismatch" % i)
+            arr[i].mamba = sw
+            arr[i].ssm_state = _dev_ptr(ly["ssm_state"], "ssm_state", f32, dev)
+            if d_conv > 1:
+                arr[i].conv_state = _dev_ptr(ly["conv_state"], "conv_state", f32, dev)
+        else:
+            shapes = {"wq": (d_model, d_model), "wk": (Hkv * D, d_model), "wv": (Hkv * D, d_model),
+                      "wo": (d_model, d_model)}
+            for key, shp in shapes.items():
+                if tuple(ly[key].shape) != shp:
+                    raise ValueError("self layer %d %s has shape %s, expected %s" %
+                                     (i, key, tuple(ly[key].shape), shp))
+                setattr(arr[i], key, _dev_ptr(ly[key], "self layer %d %s" % (i, key), bf, dev))
+            if kind == "swa":
+                for key in ("kring", "vring"):
+                    if tuple(ly[key].shape) != (B, Hkv, window, D):
+                        raise ValueError("self layer %d %s must be [B, Hkv, window, D]" % (i, key))
+                    setattr(arr[i], key, _dev_ptr(ly[key], "self layer %d %s" % (i, key), bf, dev))
+        _set_norms_mlp(arr[i], ly, i, dev, d_model, d_ff, "self layer")
+    return arr, (d_inner, d_state, dt_rank, d_conv), d_ff
+
+
 class SambayPrefill:
     """Prepared YOCO-style prefill: the self-decoder over the prompt x [B, T,
     d_model] (bf16), its final full-attention layer writing the shared cache
@@ -664,7 +718,7 @@ class SambayPrefill:
     def __init__(self, x, self_layers: Sequence, cross_layers: Sequence, kcache, vcache, window: int = 0,
                  eps: float = 1e-5, scale: float | None = None, h_out=None, M_out=None):
         dev = _check_device(x, "x")
-        bf, f32 = torch.bfloat16, torch.float32
+        bf = torch.bfloat16
         if x.dim() != 3 or kcache.dim() != 4 or vcache.shape != kcache.shape:
             raise ValueError("x [B, T, d_model], kcache and vcache [B, Hkv, L, D]")
         B, T, d_model = x.shape
@@ -672,46 +726,8 @@ class SambayPrefill:
         if B2 != B or d_model % D != 0:
             raise ValueError("sambay_prefill shape mismatch")
         Hq = d_model // D
-        mamba = [ly for ly in self_layers if ly["kind"] == "mamba"]
-        if mamba:
-            _, d_inner, d_state, dt_rank, d_conv = _mamba_weights(mamba[0]["w"], dev, d_model)
-        else:  # no SSM layer: any supported SSM shape sizes the (unused) memory
-            d_inner, d_state, dt_rank, d_conv = 64, 8, 64, 1
-            for ly in cross_layers:
-                if ly["kind"] == "gmu":
-                    d_inner = ly["w_a"].shape[0]
-        d_ff = max(_mlp_width(self_layers), _mlp_width(cross_layers))
-        arr = (SbSelfLayer * max(len(self_layers), 1))()
-        for i, ly in enumerate(self_layers):
-            kind = ly["kind"]
-            if kind not in _SELF_KINDS:
-                raise ValueError("self layer kind must be 'mamba', 'swa' or 'attn'")
-            arr[i].kind = _SELF_KINDS[kind]
-            if kind == "mamba":
-                sw, di, ds, dr, dc = _mamba_weights(ly["w"], dev, d_model)
-                if (di, ds, dr, dc) != (d_inner, d_state, dt_rank, d_conv):
-                    raise ValueError("every SSM layer must have the same shape")
-                if ly["ssm_state"].shape != (B, d_inner, d_state) or \
-                        (d_conv > 1 and ly["conv_state"].shape != (B, d_inner, d_conv - 1)):
-                    raise ValueError("self layer %d: state shape mismatch" % i)
-                arr[i].mamba = sw
-                arr[i].ssm_state = _dev_ptr(ly["ssm_state"], "ssm_state", f32, dev)
-                if d_conv > 1:
-                    arr[i].conv_state = _dev_ptr(ly["conv_state"], "conv_state", f32, dev)
-            else:
-                shapes = {"wq": (d_model, d_model), "wk": (Hkv * D, d_model), "wv": (Hkv * D, d_model),
-                          "wo": (d_model, d_model)}
-                for key, shp in shapes.items():
-                    if tuple(ly[key].shape) != shp:
-                        raise ValueError("self layer %d %s has shape %s, expected %s" %
-                                         (i, key, tuple(ly[key].shape), shp))
-                    setattr(arr[i], key, _dev_ptr(ly[key], "self layer %d %s" % (i, key), bf, dev))
-                if kind == "swa":
-                    for key in ("kring", "vring"):
-                        if tuple(ly[key].shape) != (B, Hkv, window, D):
-                            raise ValueError("self layer %d %s must be [B, Hkv, window, D]" % (i, key))
-                        setattr(arr[i], key, _dev_ptr(ly[key], "self layer %d %s" % (i, key), bf, dev))
-            _set_norms_mlp(arr[i], ly, i, dev, d_model, d_ff, "self layer")
+        arr, (d_inner, d_state, dt_rank, d_conv), d_ff = _self_layer_array(self_layers, cross_layers, dev, B, d_model,
+                                                                           Hkv, D, window)
         self.cross = _layer_ex_array(cross_layers, dev, d_model, d_inner, d_ff)
         self.self_arr = arr
         self.h_out = h_out if h_out is not None else torch.empty((B, d_model), dtype=bf, device=dev)
@@ -743,8 +759,59 @@ def sambay_prefill(x, self_layers: Sequence, cross_layers: Sequence, kcache, vca
     return SambayPrefill(x, self_layers, cross_layers, kcache, vcache, window, eps, scale)()
 
 
+class SambayDecodeStep:
+    """Prepared whole-model decode step (after sambay_prefill): h [B, d_model]
+    bf16 holds each sequence's new token row and receives its last hidden
+    state; pos [B] int32 (device) the token positions.  Layers, caches and
+    states as for SambayPrefill (the same dicts).  Calling it returns
+    (h, M_last)."""
+
+    def __init__(self, h, pos, self_layers: Sequence, cross_layers: Sequence, kcache, vcache, window: int = 0,
+                 eps: float = 1e-5, scale: float | None = None, M_out=None):
+        dev = _check_device(h, "h")
+        bf = torch.bfloat16
+        if h.dim() != 2 or kcache.dim() != 4 or vcache.shape != kcache.shape:
+            raise ValueError("h [B, d_model], kcache and vcache [B, Hkv, L, D]")
+        B, d_model = h.shape
+        B2, Hkv, L, D = kcache.shape
+        if B2 != B or d_model % D != 0 or pos.shape != (B,):
+            raise ValueError("sambay_decode_step shape mismatch")
+        Hq = d_model // D
+        arr, (d_inner, d_state, dt_rank, d_conv), d_ff = _self_layer_array(self_layers, cross_layers, dev, B, d_model,
+                                                                           Hkv, D, window)
+        self.cross = _layer_ex_array(cross_layers, dev, d_model, d_inner, d_ff)
+        self.self_arr = arr
+        self.M_out = M_out if M_out is not None else torch.empty((B, d_inner), dtype=bf, device=dev)
+        self.tensors = (h, pos, self_layers, cross_layers, kcache, vcache)
+        self.ptrs = (_dev_ptr(h, "h", bf, dev), _dev_ptr(self.M_out, "M_out", bf, dev))
+        self.kv = (_dev_ptr(kcache, "kcache", bf, dev), _dev_ptr(vcache, "vcache", bf, dev),
+                   _dev_ptr(pos, "pos", torch.int32, dev))
+        self.n = (len(self_layers), len(cross_layers))
+        self.dims = (B, d_model, d_inner, d_state, dt_rank, d_conv, d_ff, Hq, Hkv, D, L)
+        self.window = int(window)
+        self.scale = float(1.0 / math.sqrt(D) if scale is None else scale)
+        self.eps = float(eps)
+        nb = lib.sambay_decode_workspace_bytes(*self.dims, self.window)
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        self.device = dev
+
+    def __call__(self):
+        st = lib.sambay_decode_step(*self.ptrs, self.self_arr, self.n[0], self.cross, self.n[1], *self.kv,
+                                    *self.dims, self.window, self.scale, self.eps, self.ws.data_ptr(),
+                                    self.ws.numel(), _stream(self.device))
+        _check("sambay_decode_step", st)
+        return self.tensors[0], self.M_out
+
+
+def sambay_decode_step(h, pos, self_layers: Sequence, cross_layers: Sequence, kcache, vcache, window: int = 0,
+                       eps: float = 1e-5, scale: float | None = None):
+    """Whole-model decode step (see SambayDecodeStep); returns (h, M_last)."""
+    return SambayDecodeStep(h, pos, self_layers, cross_layers, kcache, vcache, window, eps, scale)()
+
+
 __all__ = ["gmu_forward", "xattn_decode", "diffattn_decode", "selfattn_decode", "mamba_decode_step",
-           "attn_prefill", "mamba_prefill", "sambay_prefill", "SambayPrefill",
+           "attn_prefill", "mamba_prefill", "sambay_prefill", "SambayPrefill", "sambay_decode_step",
+           "SambayDecodeStep",
            "crossdecoder_step", "CrossDecoderStep", "crossdecoder_step_ex",
            "CrossDecoderStepEx", "SambayError", "version", "lib",
            "EXPORTS", "LIB_PATH", "timing_enable", "timing_collect", "probe_stream_read_gbps", "probe_mfma_tflops",

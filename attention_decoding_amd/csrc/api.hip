@@ -486,6 +486,78 @@ bool mamba_dims_ok(int64_t B, int64_t d_model, int64_t d_inner, int64_t N, int64
            R % 8 == 0 && K >= 1 && K <= kMaxConv;
 }
 
+
+// The decode step's launches for B sequences in token groups of <= 64 (the
+// arguments already validated): x may come with a low part x_lo (a bf16
+// hi + lo pair); out_epi EPI_BF16 stores y, EPI_RESID adds it into y_out (h).
+hipError_t run_mamba_step(const bf16_t *x, const bf16_t *x_lo, const sb_mamba_weights *w, float *conv_state,
+                          float *ssm_state, bf16_t *M_out, bf16_t *y_out, Epilogue out_epi, int64_t B,
+                          int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank, int64_t d_conv,
+                          void *workspace, hipStream_t stream) {
+    const MambaLayout lay = mamba_layout(B, d_model, d_inner, d_state, dt_rank);
+    const int64_t P = dt_rank + 2 * d_state;
+    char *ws = reinterpret_cast<char *>(workspace);
+    float *xz = reinterpret_cast<float *>(ws + lay.xz), *u = reinterpret_cast<float *>(ws + lay.u);
+    float *xdbl = reinterpret_cast<float *>(ws + lay.xdbl), *part = reinterpret_cast<float *>(ws + lay.part);
+    bf16_t *u_hi = reinterpret_cast<bf16_t *>(ws + lay.u_hi), *u_lo = reinterpret_cast<bf16_t *>(ws + lay.u_lo);
+    bf16_t *g_hi = reinterpret_cast<bf16_t *>(ws + lay.g_hi), *g_lo = reinterpret_cast<bf16_t *>(ws + lay.g_lo);
+    const int di = (int)d_inner, dm = (int)d_model, Pi = (int)P;
+    hipError_t e = hipSuccess;
+    for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+        const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+        SkinnyArgs a;
+        a.X = x + t0 * d_model;
+        a.X_lo = x_lo ? x_lo + t0 * d_model : nullptr;
+        a.ldx = dm;
+        a.W = (const bf16_t *)w->w_in;
+        a.T = T;
+        a.N = 2 * di;
+        a.K = dm;
+        a.epi = EPI_F32;
+        a.out = xz;
+        a.ldo = 2 * di;
+        const SkinnyPlan p_in = skinny_plan(T, 2 * di, dm, x_lo != nullptr);
+        if (log_enabled() && t0 == 0)
+            fprintf(stderr, "[sambay] SSM step B=%lld d_model=%d d_inner=%d N=%lld R=%lld K=%lld: in-proj %d k-splits\n",
+                    (long long)B, dm, di, (long long)d_state, (long long)dt_rank, (long long)d_conv, p_in.k_splits);
+        e = launch_skinny(a, p_in, part, stream);
+        if (e != hipSuccess) break;
+        e = launch_mamba_conv(xz, 2 * di, conv_state + t0 * d_inner * (d_conv - 1), (const float *)w->conv_w,
+                              (const float *)w->conv_b, u, u_hi, u_lo, T, di, (int)d_conv, stream);
+        if (e != hipSuccess) break;
+        SkinnyArgs b;
+        b.X = u_hi;
+        b.X_lo = u_lo;
+        b.ldx = di;
+        b.W = (const bf16_t *)w->w_x;
+        b.T = T;
+        b.N = Pi;
+        b.K = di;
+        b.epi = EPI_F32;
+        b.out = xdbl;
+        b.ldo = Pi;
+        e = launch_skinny(b, skinny_plan(T, Pi, di, true), part, stream);
+        if (e != hipSuccess) break;
+        e = launch_mamba_scan(xz, 2 * di, u, xdbl, Pi, (int)dt_rank, (const bf16_t *)w->w_dt,
+                              (const float *)w->dt_bias, (const float *)w->a_log, (const float *)w->d_skip,
+                              ssm_state + t0 * d_inner * d_state, M_out + t0 * d_inner, g_hi, g_lo, T, di,
+                              (int)d_state, stream);
+        if (e != hipSuccess) break;
+        SkinnyArgs o;
+        o.X = g_hi;
+        o.X_lo = g_lo;
+        o.ldx = di;
+        o.W = (const bf16_t *)w->w_out;
+        o.T = T;
+        o.N = dm;
+        o.K = di;
+        o.epi = out_epi;
+        o.out = y_out + t0 * d_model;
+        o.ldo = dm;
+        e = launch_skinny(o, skinny_plan(T, dm, di, true), part, stream);
+    }
+    return e;
+}
 }  // namespace
 
 extern "C" size_t mamba_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_state,
@@ -546,66 +618,9 @@ extern "C" sb_status mamba_decode_step(const void *x, const sb_mamba_weights *w,
     for (const Range &r : ins)
         if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
 
-    char *ws = reinterpret_cast<char *>(workspace);
-    float *xz = reinterpret_cast<float *>(ws + lay.xz), *u = reinterpret_cast<float *>(ws + lay.u);
-    float *xdbl = reinterpret_cast<float *>(ws + lay.xdbl), *part = reinterpret_cast<float *>(ws + lay.part);
-    bf16_t *u_hi = reinterpret_cast<bf16_t *>(ws + lay.u_hi), *u_lo = reinterpret_cast<bf16_t *>(ws + lay.u_lo);
-    bf16_t *g_hi = reinterpret_cast<bf16_t *>(ws + lay.g_hi), *g_lo = reinterpret_cast<bf16_t *>(ws + lay.g_lo);
-    const int di = (int)d_inner, dm = (int)d_model, Pi = (int)P;
-    hipError_t e = hipSuccess;
-    for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
-        const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
-        SkinnyArgs a;
-        a.X = (const bf16_t *)x + t0 * d_model;
-        a.ldx = dm;
-        a.W = (const bf16_t *)w->w_in;
-        a.T = T;
-        a.N = 2 * di;
-        a.K = dm;
-        a.epi = EPI_F32;
-        a.out = xz;
-        a.ldo = 2 * di;
-        const SkinnyPlan p_in = skinny_plan(T, 2 * di, dm, false);
-        if (log_enabled() && t0 == 0)
-            fprintf(stderr, "[sambay] %s B=%lld d_model=%d d_inner=%d N=%lld R=%lld K=%lld: in-proj %d k-splits\n",
-                    fn, (long long)B, dm, di, (long long)d_state, (long long)dt_rank, (long long)d_conv,
-                    p_in.k_splits);
-        e = launch_skinny(a, p_in, part, stream);
-        if (e != hipSuccess) break;
-        e = launch_mamba_conv(xz, 2 * di, conv_state + t0 * d_inner * (d_conv - 1), (const float *)w->conv_w,
-                              (const float *)w->conv_b, u, u_hi, u_lo, T, di, (int)d_conv, stream);
-        if (e != hipSuccess) break;
-        SkinnyArgs b;
-        b.X = u_hi;
-        b.X_lo = u_lo;
-        b.ldx = di;
-        b.W = (const bf16_t *)w->w_x;
-        b.T = T;
-        b.N = Pi;
-        b.K = di;
-        b.epi = EPI_F32;
-        b.out = xdbl;
-        b.ldo = Pi;
-        e = launch_skinny(b, skinny_plan(T, Pi, di, true), part, stream);
-        if (e != hipSuccess) break;
-        e = launch_mamba_scan(xz, 2 * di, u, xdbl, Pi, (int)dt_rank, (const bf16_t *)w->w_dt,
-                              (const float *)w->dt_bias, (const float *)w->a_log, (const float *)w->d_skip,
-                              ssm_state + t0 * d_inner * d_state, (bf16_t *)M_out + t0 * d_inner, g_hi, g_lo, T, di,
-                              (int)d_state, stream);
-        if (e != hipSuccess) break;
-        SkinnyArgs o;
-        o.X = g_hi;
-        o.X_lo = g_lo;
-        o.ldx = di;
-        o.W = (const bf16_t *)w->w_out;
-        o.T = T;
-        o.N = dm;
-        o.K = di;
-        o.epi = EPI_BF16;
-        o.out = (bf16_t *)y_out + t0 * d_model;
-        o.ldo = dm;
-        e = launch_skinny(o, skinny_plan(T, dm, di, true), part, stream);
-    }
+    const hipError_t e = run_mamba_step((const bf16_t *)x, nullptr, w, conv_state, ssm_state, (bf16_t *)M_out,
+                                        (bf16_t *)y_out, EPI_BF16, B, d_model, d_inner, d_state, dt_rank, d_conv,
+                                        workspace, stream);
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
 }
@@ -1204,4 +1219,267 @@ extern "C" sb_status sambay_prefill(const void *x, void *h_out, void *M_out, con
     const size_t cbytes = need - round_up(lay.bytes);
     return crossdecoder_step_ex(h_out, m_last, kcache, vcache, lay.lens, cross.data(), (int32_t)cross.size(), B,
                                 d_model, d_inner, d_ff, Hq, Hkv, D, L, scale, eps, cws, cbytes, stream);
+}
+
+// ====================================================== whole-model decode
+
+namespace {
+
+// Workspace of one whole-model decode step: per-layer activations (reused
+// layer to layer), the cache lengths, then the SSM step's, the attention's
+// and the cross-decoder step's own regions.
+struct DecodeLayout {
+    size_t xn, xn_lo, q, kn, vn, o, o_lo, m, lens, lens_ring, hid, hid_lo, part, attn, ssm, cross, total;
+};
+
+DecodeLayout decode_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank,
+                           int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t L, int64_t window) {
+    const int64_t T = B < kSkinnyMaxTokens ? B : kSkinnyMaxTokens;
+    const int t = (int)T, dm = (int)d_model, kvd = (int)(Hkv * kHeadDim), df = (int)d_ff;
+    DecodeLayout l;
+    Carver c{nullptr};
+    l.xn = c.used; c.take((size_t)B * d_model * 2);
+    l.xn_lo = c.used; c.take((size_t)B * d_model * 2);
+    l.q = c.used; c.take((size_t)B * d_model * 2);
+    l.kn = c.used; c.take((size_t)B * kvd * 2);
+    l.vn = c.used; c.take((size_t)B * kvd * 2);
+    l.o = c.used; c.take((size_t)B * d_model * 2);
+    l.o_lo = c.used; c.take((size_t)B * d_model * 2);
+    l.m = c.used; c.take((size_t)B * d_inner * 2);
+    l.lens = c.used; c.take((size_t)B * 4);
+    l.lens_ring = c.used; c.take((size_t)B * 4);
+    l.hid = c.used; c.take((size_t)T * (d_ff > 0 ? d_ff : 1) * 2);
+    l.hid_lo = c.used; c.take((size_t)T * (d_ff > 0 ? d_ff : 1) * 2);
+    size_t part = 0;
+    const int shapes[][2] = {{dm, dm}, {kvd, dm}, {dm, df}};
+    for (const auto &nk : shapes) {
+        if (nk[0] <= 0 || nk[1] <= 0) continue;
+        const size_t v = skinny_partial_bytes_max(t, nk[0], nk[1]);
+        if (v > part) part = v;
+    }
+    if (df > 0) {
+        const size_t v = skinny_partial_bytes_dual(t, df, skinny_plan_dual(t, df, dm));
+        if (v > part) part = v;
+    }
+    l.part = c.used; c.take(part);
+    const int64_t Lmax = L > window ? L : window;
+    l.attn = c.used; c.take(xattn_workspace_need(B, Hq, Hkv, Lmax));
+    l.ssm = c.used; c.take(mamba_layout(B, d_model, d_inner, d_state, dt_rank).total);
+    l.cross = c.used; c.take(ex_layout(B, d_model, d_inner, d_ff, Hq, Hkv, L).total);
+    l.total = c.used;
+    return l;
+}
+
+bool decode_dims_ok(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank, int64_t d_conv,
+                    int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t D, int64_t L) {
+    return B > 0 && D == kHeadDim && Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && Hq * D == d_model && Hq <= 65535 &&
+           L > 0 && L <= kMaxDim && d_ff >= 0 && d_ff % 64 == 0 && d_ff <= kMaxDim &&
+           mamba_dims_ok(B, d_model, d_inner, d_state, dt_rank, d_conv);
+}
+
+}  // namespace
+
+extern "C" size_t sambay_decode_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_state,
+                                                int64_t dt_rank, int64_t d_conv, int64_t d_ff, int64_t Hq,
+                                                int64_t Hkv, int64_t D, int64_t L, int64_t window) {
+    if (!decode_dims_ok(B, d_model, d_inner, d_state, dt_rank, d_conv, d_ff, Hq, Hkv, D, L) || window < 0)
+        return 0;
+    return decode_layout(B, d_model, d_inner, d_state, dt_rank, d_ff, Hq, Hkv, L, window).total;
+}
+
+extern "C" sb_status sambay_decode_step(void *h, void *M_out, const sb_self_layer *self_layers, int32_t n_self,
+                                        const sb_layer_ex *cross_layers, int32_t n_cross, void *kcache, void *vcache,
+                                        const int32_t *pos, int64_t B, int64_t d_model, int64_t d_inner,
+                                        int64_t d_state, int64_t dt_rank, int64_t d_conv, int64_t d_ff, int64_t Hq,
+                                        int64_t Hkv, int64_t D, int64_t L, int64_t window, float scale, float eps,
+                                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "sambay_decode_step";
+    if (B < 0 || d_model < 0 || d_inner < 0 || d_state < 0 || dt_rank < 0 || d_conv < 0 || d_ff < 0 || Hq < 0 ||
+        Hkv < 0 || D < 0 || L < 0 || window < 0 || n_self < 0 || n_cross < 0)
+        return fail(SB_EINVAL, "negative size");
+    if (B == 0) return ok();
+    if (!decode_dims_ok(B, d_model, d_inner, d_state, dt_rank, d_conv, d_ff, Hq, Hkv, D, L))
+        return fail(SB_EUNSUPPORTED,
+                    "unsupported decode shape (D == 128, Hq %% Hkv == 0, Hq*D == d_model; d_model, d_inner, d_ff "
+                    "multiples of 64; d_state in {8, 16, 32, 64}; dt_rank a multiple of 8, <= %d; d_conv <= %d)",
+                    kMaxDtRank, kMaxConv);
+    if (!h || !kcache || !vcache || !pos) return fail(SB_EINVAL, "null tensor pointer");
+    if (n_self > 0 && !self_layers) return fail(SB_EINVAL, "null self-decoder layer array");
+    if (n_cross > 0 && !cross_layers) return fail(SB_EINVAL, "null cross-decoder layer array");
+    if (!aligned16(h) || !aligned16(M_out) || !aligned16(kcache) || !aligned16(vcache))
+        return fail(SB_EINVAL, "tensor base pointers must be 16-byte aligned");
+    if (((uintptr_t)pos & 3u) != 0) return fail(SB_EINVAL, "pos must be 4-byte aligned");
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(SB_EINVAL, "scale must be finite");
+    if (!(eps >= 0.f) || eps == __builtin_inff()) return fail(SB_EINVAL, "eps must be finite and >= 0");
+    const int64_t kvd = Hkv * D;
+    const size_t kvbytes = (size_t)B * Hkv * L * D * 2;
+    std::vector<Range> outs = {rng("h", h, (size_t)B * d_model * 2),
+                               rng("M_out", M_out, M_out ? (size_t)B * d_inner * 2 : 0),
+                               rng("kcache", kcache, kvbytes), rng("vcache", vcache, kvbytes)};
+    std::vector<Range> ins = {rng("pos", pos, (size_t)B * 4)};
+    bool has_attn = false, has_mamba = false, has_swa = false;
+    for (int32_t i = 0; i < n_self; ++i) {
+        const sb_self_layer &ly = self_layers[i];
+        const bool mlp = ly.w_gate != nullptr;
+        if (mlp && (!ly.w_up || !ly.w_down)) return fail(SB_EINVAL, "self layer %d: incomplete MLP", (int)i);
+        if (mlp && d_ff == 0) return fail(SB_EINVAL, "self layer %d has an MLP but d_ff == 0", (int)i);
+        const void *common[] = {ly.norm1, ly.norm2, ly.w_gate, ly.w_up, ly.w_down};
+        for (const void *p : common)
+            if (!aligned16(p)) return fail(SB_EINVAL, "self layer %d: misaligned weight or gain", (int)i);
+        ins.push_back(rng("w_gate", ly.w_gate, mlp ? (size_t)d_ff * d_model * 2 : 0));
+        ins.push_back(rng("w_up", ly.w_up, mlp ? (size_t)d_ff * d_model * 2 : 0));
+        ins.push_back(rng("w_down", ly.w_down, mlp ? (size_t)d_model * d_ff * 2 : 0));
+        if (ly.kind == SB_SELF_MAMBA) {
+            has_mamba = true;
+            const sb_mamba_weights &w = ly.mamba;
+            if (!w.w_in || !w.conv_w || !w.conv_b || !w.w_x || !w.w_dt || !w.dt_bias || !w.a_log || !w.d_skip ||
+                !w.w_out)
+                return fail(SB_EINVAL, "self layer %d: null SSM weight", (int)i);
+            if (!ly.ssm_state || (!ly.conv_state && d_conv > 1))
+                return fail(SB_EINVAL, "self layer %d: null SSM state", (int)i);
+            const void *al[] = {w.w_in, w.conv_w, w.conv_b, w.w_x, w.w_dt, w.dt_bias, w.a_log, w.d_skip, w.w_out,
+                                ly.conv_state, ly.ssm_state};
+            for (const void *p : al)
+                if (!aligned16(p)) return fail(SB_EINVAL, "self layer %d: misaligned SSM tensor", (int)i);
+            outs.push_back(rng("conv_state", ly.conv_state, (size_t)B * d_inner * (d_conv - 1) * 4));
+            outs.push_back(rng("ssm_state", ly.ssm_state, (size_t)B * d_inner * d_state * 4));
+            ins.push_back(rng("w_in", w.w_in, (size_t)2 * d_inner * d_model * 2));
+            ins.push_back(rng("w_out", w.w_out, (size_t)d_model * d_inner * 2));
+        } else if (ly.kind == SB_SELF_SWA || ly.kind == SB_SELF_ATTN) {
+            if (!ly.wq || !ly.wk || !ly.wv || !ly.wo)
+                return fail(SB_EINVAL, "self layer %d: null attention weight", (int)i);
+            const void *al[] = {ly.wq, ly.wk, ly.wv, ly.wo, ly.kring, ly.vring};
+            for (const void *p : al)
+                if (!aligned16(p)) return fail(SB_EINVAL, "self layer %d: misaligned attention tensor", (int)i);
+            ins.push_back(rng("wq", ly.wq, (size_t)d_model * d_model * 2));
+            ins.push_back(rng("wk", ly.wk, (size_t)kvd * d_model * 2));
+            ins.push_back(rng("wv", ly.wv, (size_t)kvd * d_model * 2));
+            ins.push_back(rng("wo", ly.wo, (size_t)d_model * d_model * 2));
+            if (ly.kind == SB_SELF_SWA) {
+                has_swa = true;
+                if (!ly.kring || !ly.vring) return fail(SB_EINVAL, "self layer %d: null ring cache", (int)i);
+                const size_t rb = (size_t)B * Hkv * (window > 0 ? window : 0) * D * 2;
+                outs.push_back(rng("kring", ly.kring, rb));
+                outs.push_back(rng("vring", ly.vring, rb));
+            } else {
+                if (has_attn) return fail(SB_EINVAL, "self layer %d: a second full-attention layer", (int)i);
+                has_attn = true;
+            }
+        } else {
+            return fail(SB_EINVAL, "self layer %d: unknown kind %d", (int)i, (int)ly.kind);
+        }
+    }
+    if (has_swa && (window < 1 || window > kMaxDim))
+        return fail(SB_EUNSUPPORTED, "a sliding-window layer needs 1 <= window < 2^30");
+    for (int32_t i = 0; i < n_cross; ++i) {
+        if (cross_layers[i].kind == SB_LAYER_XATTN && !has_attn)
+            return fail(SB_EINVAL, "cross layer %d attends to a cache no self-decoder layer writes", (int)i);
+        if (cross_layers[i].kind == SB_LAYER_GMU && !has_mamba)
+            return fail(SB_EINVAL, "cross layer %d gates a memory no SSM layer produces", (int)i);
+    }
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlaps(outs[i], outs[j])) return fail(SB_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (const Range &r : ins)
+            if (overlaps(outs[i], r)) return fail(SB_EINVAL, "%s overlaps %s", outs[i].name, r.name);
+    }
+    const DecodeLayout lay = decode_layout(B, d_model, d_inner, d_state, dt_rank, d_ff, Hq, Hkv, L, window);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(SB_EWORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
+                    workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(SB_EINVAL, "workspace must be 16-byte aligned");
+    const Range rw = rng("workspace", workspace, lay.total);
+    for (const Range &r : outs)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+    for (const Range &r : ins)
+        if (overlaps(rw, r)) return fail(SB_EINVAL, "workspace overlaps %s", r.name);
+    if (log_enabled())
+        fprintf(stderr, "[sambay] %s B=%lld self=%d cross=%d d_model=%lld L=%lld window=%lld workspace %zu bytes\n",
+                fn, (long long)B, (int)n_self, (int)n_cross, (long long)d_model, (long long)L, (long long)window,
+                lay.total);
+
+    char *w8 = static_cast<char *>(workspace);
+    bf16_t *xn = reinterpret_cast<bf16_t *>(w8 + lay.xn), *xn_lo = reinterpret_cast<bf16_t *>(w8 + lay.xn_lo);
+    bf16_t *q = reinterpret_cast<bf16_t *>(w8 + lay.q), *kn = reinterpret_cast<bf16_t *>(w8 + lay.kn);
+    bf16_t *vn = reinterpret_cast<bf16_t *>(w8 + lay.vn), *o = reinterpret_cast<bf16_t *>(w8 + lay.o);
+    bf16_t *o_lo = reinterpret_cast<bf16_t *>(w8 + lay.o_lo);
+    bf16_t *mbuf = M_out ? static_cast<bf16_t *>(M_out) : reinterpret_cast<bf16_t *>(w8 + lay.m);
+    int32_t *lens = reinterpret_cast<int32_t *>(w8 + lay.lens);
+    int32_t *lens_ring = reinterpret_cast<int32_t *>(w8 + lay.lens_ring);
+    bf16_t *hid = reinterpret_cast<bf16_t *>(w8 + lay.hid), *hid_lo = reinterpret_cast<bf16_t *>(w8 + lay.hid_lo);
+    float *part = reinterpret_cast<float *>(w8 + lay.part);
+    void *attn_part = w8 + lay.attn, *ssm_ws = w8 + lay.ssm;
+    bf16_t *hb = static_cast<bf16_t *>(h);
+    const int dm = (int)d_model, kvi = (int)kvd, df = (int)d_ff;
+
+    // One weight-streaming product over every token group of <= 64 rows.
+    auto product = [&](const bf16_t *X, const bf16_t *X_lo, const void *W, int N, int K, Epilogue epi,
+                       bf16_t *out) -> hipError_t {
+        hipError_t e = hipSuccess;
+        for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+            const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+            SkinnyArgs a;
+            a.X = X + t0 * K; a.X_lo = X_lo ? X_lo + t0 * K : nullptr; a.ldx = K;
+            a.W = (const bf16_t *)W; a.T = T; a.N = N; a.K = K; a.epi = epi; a.out = out + t0 * N; a.ldo = N;
+            e = launch_skinny(a, skinny_plan(T, N, K, X_lo != nullptr), part, stream);
+        }
+        return e;
+    };
+
+    hipError_t e = hipSuccess;
+    for (int32_t li = 0; li < n_self && e == hipSuccess; ++li) {
+        const sb_self_layer &ly = self_layers[li];
+        const bf16_t *X = hb, *X_lo = nullptr;
+        if (ly.norm1) {
+            if ((e = launch_rmsnorm(hb, (const bf16_t *)ly.norm1, (int)B, dm, eps, xn, xn_lo, stream)) != hipSuccess)
+                break;
+            X = xn; X_lo = xn_lo;
+        }
+        if (ly.kind == SB_SELF_MAMBA) {
+            e = run_mamba_step(X, X_lo, &ly.mamba, ly.conv_state, ly.ssm_state, mbuf, hb, EPI_RESID, B, d_model,
+                               d_inner, d_state, dt_rank, d_conv, ssm_ws, stream);
+        } else {
+            const bool swa = ly.kind == SB_SELF_SWA;
+            const int slots = swa ? (int)window : (int)L;
+            bf16_t *kc = static_cast<bf16_t *>(swa ? ly.kring : kcache);
+            bf16_t *vc = static_cast<bf16_t *>(swa ? ly.vring : vcache);
+            int32_t *ln = swa ? lens_ring : lens;
+            e = product(X, X_lo, ly.wq, dm, dm, EPI_BF16, q);
+            if (e == hipSuccess) e = product(X, X_lo, ly.wk, kvi, dm, EPI_BF16, kn);
+            if (e == hipSuccess) e = product(X, X_lo, ly.wv, kvi, dm, EPI_BF16, vn);
+            if (e == hipSuccess)
+                e = launch_kv_append(kn, vn, kc, vc, pos, ln, (int)B, (int)Hkv, slots, swa ? (int)window : 0,
+                                     stream);
+            if (e == hipSuccess)
+                e = launch_xattn(q, false, kc, vc, ln, o, o_lo, (int)B, (int)Hq, (int)Hkv, slots, scale,
+                                 xattn_plan(B, Hkv, slots, true), attn_part, stream);
+            if (e == hipSuccess) e = product(o, o_lo, ly.wo, dm, dm, EPI_RESID, hb);
+        }
+        if (e != hipSuccess || !ly.w_gate) continue;
+        const bf16_t *Xm = hb, *Xm_lo = nullptr;
+        if (ly.norm2) {
+            if ((e = launch_rmsnorm(hb, (const bf16_t *)ly.norm2, (int)B, dm, eps, xn, xn_lo, stream)) != hipSuccess)
+                break;
+            Xm = xn; Xm_lo = xn_lo;
+        }
+        // Token group by token group: hid = SiLU(x Wg^T) ⊙ (x Wu^T), h += hid Wd^T.
+        for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+            const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+            SkinnyArgs a;
+            a.X = Xm + t0 * dm; a.X_lo = Xm_lo ? Xm_lo + t0 * dm : nullptr; a.ldx = dm;
+            a.W = (const bf16_t *)ly.w_gate; a.W_b = (const bf16_t *)ly.w_up; a.T = T; a.N = df; a.K = dm;
+            a.epi = EPI_SWIGLU; a.out = hid; a.ldo = df; a.out_lo = hid_lo;
+            e = launch_skinny(a, skinny_plan_dual(T, df, dm), part, stream);
+            if (e != hipSuccess) break;
+            SkinnyArgs d;
+            d.X = hid; d.X_lo = hid_lo; d.ldx = df; d.W = (const bf16_t *)ly.w_down; d.T = T; d.N = dm; d.K = df;
+            d.epi = EPI_RESID; d.out = hb + t0 * dm; d.ldo = dm;
+            e = launch_skinny(d, skinny_plan(T, dm, df, true), part, stream);
+        }
+    }
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (n_cross == 0) return ok();
+    return crossdecoder_step_ex(h, mbuf, kcache, vcache, lens, cross_layers, n_cross, B, d_model, d_inner, d_ff, Hq,
+                                Hkv, D, L, scale, eps, w8 + lay.cross, lay.total - lay.cross, stream);
 }

@@ -149,7 +149,7 @@ def time_graph(fn, n: int, reps: int = 10) -> float:
 
 
 WORKLOAD_GROUPS = ("gmu_prefill", "gmu_decode", "attention", "ragged", "mamba_decode", "mamba_prefill",
-                   "sambay_prefill", "attn_prefill", "crossdecoder_ex")
+                   "sambay_prefill", "sambay_decode", "attn_prefill", "crossdecoder_ex")
 
 
 def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float, only=None) -> dict:
@@ -328,6 +328,47 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float, onl
             "layers": "16 self (8 SSM, 7 sliding-window 256, 1 full attention) + 16 cross (8 attention, 8 GMU), "
                       "SwiGLU d_ff 8192 in every layer"}
         del yp, full, selfonly
+    if want("sambay_decode"):
+        # Whole-model decode step: 32 sequences, each at the last of 34,816
+        # cache positions (2K prompt + 32K generated), through the 16-layer
+        # self-decoder (SSM steps, sliding-window ring appends, the shared
+        # cache append) and the 16-layer cross-decoder; the self-decoder alone
+        # timed beside it.
+        c = workload.SAMBAY_PREFILL
+        B, L = 32, c["L"]
+        yd = workload.sambay_prefill_inputs(B, 1, c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"],
+                                            c["d_conv"], c["d_ff"], c["Hq"], c["Hkv"], c["D"], c["window"], L,
+                                            workload.self_layer_kinds(c["n_self"]), workload.layer_kinds(c["n_cross"]),
+                                            seed=98, device=dev, fresh=False)
+        yd.kcache.copy_(workload.normal(tuple(yd.kcache.shape), seed=99, device=dev))
+        yd.vcache.copy_(workload.normal(tuple(yd.vcache.shape), seed=100, device=dev))
+        for ly in yd.self_layers:
+            if ly["kind"] == "swa":
+                ly["kring"].normal_()
+                ly["vring"].normal_()
+        pos = torch.full((B,), L - 1, dtype=torch.int32, device=dev)
+        x0 = workload.normal((B, c["d_model"]), seed=101, device=dev)
+        h = x0.clone()
+        full = sb.SambayDecodeStep(h, pos, yd.self_layers, yd.cross_layers, yd.kcache, yd.vcache, window=c["window"])
+        selfonly = sb.SambayDecodeStep(h, pos, yd.self_layers, [], yd.kcache, yd.vcache, window=c["window"])
+
+        def run_full(i):
+            h.copy_(x0)
+            full()
+
+        def run_self(i):
+            h.copy_(x0)
+            selfonly()
+
+        ms_full = time_calls(run_full, 10)
+        ms_self = time_calls(run_self, 10)
+        res["sambay_decode_B%d_L%d" % (B, L)] = {
+            "ms_per_step": round(ms_full, 4), "tokens_per_s": round(B / ms_full * 1e3, 1),
+            "self_decoder_ms": round(ms_self, 4), "cross_decoder_ms": round(ms_full - ms_self, 4),
+            "layers": "16 self (8 SSM, 7 sliding-window 256, 1 full attention) + 16 cross (8 attention, 8 GMU), "
+                      "SwiGLU d_ff 8192 in every layer"}
+        del yd, full, selfonly
+        torch.cuda.empty_cache()
     if want("attn_prefill"):
         # Prefill attention over the prompt: 4 x 2048 tokens, window 256 (the
         # self-decoder's sliding-window layers), and plain causal at 1 x 2048.

@@ -387,6 +387,39 @@ sb_status sambay_prefill(const void *x, void *h_out, void *M_out, const sb_self_
                          int64_t d_conv, int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t D, int64_t L, int64_t window,
                          float scale, float eps, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------ whole-model decode --
+ * One decode step of the whole model after a prefill: the new token of each
+ * sequence (at position pos[b], the number of tokens before it) through the
+ * self-decoder's layers, each one step of the layer sambay_prefill runs over
+ * the prompt (same norms and MLPs):
+ *   SB_SELF_MAMBA: mamba_decode_step on the normalised x (states in place),
+ *                  h = bf16(h + y); M of the last SSM layer kept for the GMUs
+ *   SB_SELF_SWA:   q, k, v projections of x; k, v stored in ring slot
+ *                  pos % window; attention over the min(pos + 1, window)
+ *                  ring entries; h = bf16(h + o Wo^T)
+ *   SB_SELF_ATTN:  the same on the shared cache [B, Hkv, L, D] at position
+ *                  pos (nothing stored when pos >= L, attention over L then),
+ *                  attention over positions 0 .. pos
+ * then crossdecoder_step_ex(cross_layers) with cache lengths min(pos + 1, L),
+ * in place on h [B, d_model] (bf16: the new token's input row in, its last
+ * hidden state out).  M_out [B, d_inner] (nullable) receives the last SSM
+ * layer's M.  pos [B] int32 on the device; pos[b] < 0 marks an inactive
+ * sequence for the attention layers (nothing stored, zero attention output)
+ * — the other layers still run on its row.  The normalised x, the attention
+ * output, the MLP hidden and the SSM step's inner rows feed their products
+ * as bf16 hi + lo pairs.  At most one SB_SELF_ATTN layer (it writes the
+ * shared cache).  Requirements and errors as sambay_prefill, without T; B
+ * == 0 is a no-op. */
+size_t sambay_decode_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank,
+                                     int64_t d_conv, int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t D, int64_t L,
+                                     int64_t window);
+sb_status sambay_decode_step(void *h, void *M_out, const sb_self_layer *self_layers, int32_t n_self,
+                             const sb_layer_ex *cross_layers, int32_t n_cross, void *kcache, void *vcache,
+                             const int32_t *pos, int64_t B, int64_t d_model, int64_t d_inner, int64_t d_state,
+                             int64_t dt_rank, int64_t d_conv, int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t D,
+                             int64_t L, int64_t window, float scale, float eps, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------ benchmark instrumentation --
  * For measuring kernels inside the calls above (benchmarks and profiling
  * only; not meant for production loops).  While a kind's bit is enabled,

@@ -390,3 +390,34 @@ def test_sambay_prefill_validation(sb):
     assert need > 4 * 2048 * (2 * 3072 + 6144) * 2       # h, x-norm and M rows at least
     assert lib.sambay_prefill_workspace_bytes(4, 0, 3072, 6144, 16, 192, 4, 0, 24, 8, 128, 36864) == 0
     assert lib.sambay_prefill_workspace_bytes(4, 2048, 3072, 6144, 16, 192, 4, 0, 24, 8, 64, 36864) == 0
+
+
+def test_sambay_decode_validation(sb):
+    """Every call here fails validation (or is a no-op); no pointer is touched."""
+    G = 1 << 30
+    mw = sb.SbMambaWeights(*[(i + 60) * G for i in range(9)])
+    mam = sb.SbSelfLayer(kind=sb.SB_SELF_MAMBA, mamba=mw, conv_state=70 * G, ssm_state=71 * G)
+    att = sb.SbSelfLayer(kind=sb.SB_SELF_ATTN, wq=72 * G, wk=73 * G, wv=74 * G, wo=75 * G)
+    swa = sb.SbSelfLayer(kind=sb.SB_SELF_SWA, wq=76 * G, wk=77 * G, wv=78 * G, wo=79 * G, kring=80 * G,
+                         vring=81 * G)
+    cross = (sb.SbLayerEx * 2)()
+    cross[0].kind, cross[0].w_a, cross[0].w_b = sb.SB_LAYER_XATTN, 82 * G, 83 * G
+    cross[1].kind, cross[1].w_a, cross[1].w_b = sb.SB_LAYER_GMU, 84 * G, 85 * G
+
+    def call(layers=(mam, swa, att), pos=5 * G, window=256, wsb=1 << 36, B=32, Hkv=8, kc=20 * G):
+        arr = (sb.SbSelfLayer * max(len(layers), 1))(*layers)
+        return sb.lib.sambay_decode_step(1 * G, 3 * G, arr, len(layers), cross, 2, kc, 30 * G, pos, B, 3072, 6144,
+                                         16, 192, 4, 0, 24, Hkv, 128, 34816, window, 0.088, 1e-5, 100 * G, wsb, None)
+
+    assert call(B=0) == sb.SB_OK
+    assert call(pos=None) == sb.SB_EINVAL
+    assert call(pos=5 * G + 2) == sb.SB_EINVAL            # misaligned positions
+    assert call(layers=(mam, att, att)) == sb.SB_EINVAL   # two layers writing the shared cache
+    assert call(layers=(mam, swa)) == sb.SB_EINVAL        # cross-attention without a cache writer
+    assert call(window=0) == sb.SB_EUNSUPPORTED
+    assert call(Hkv=5) == sb.SB_EUNSUPPORTED              # 24 % 5 != 0
+    assert call(kc=29 * G) == sb.SB_EINVAL                # the caches overlap
+    assert call(wsb=1 << 20) == sb.SB_EWORKSPACE
+    need = sb.lib.sambay_decode_workspace_bytes(32, 3072, 6144, 16, 192, 4, 8192, 24, 8, 128, 34816, 256)
+    assert need > sb.lib.crossdecoder_ex_workspace_bytes(32, 3072, 6144, 8192, 24, 8, 128, 34816)
+    assert sb.lib.sambay_decode_workspace_bytes(32, 3072, 6144, 16, 192, 4, 8192, 24, 8, 64, 34816, 256) == 0

@@ -1,0 +1,144 @@
+"""GPU parity of the whole-model decode step (sambay_decode_step) against
+the oracle's (oracle.sambay_decode_step with the bf16 residual stream),
+started from the caches and states that a GPU prefill left.
+
+Compared: the new token's last hidden state, the memory M the GMUs used,
+the cache row and ring slot the step wrote, the SSM states; the bf16 bar
+(2e-2, max-abs normalised).  Also: prefill of T tokens against prefill of
+T - 1 tokens and one decode step, both on the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 2e-2
+SELF = ["mamba", "swa", "mamba", "attn"]
+CROSS = ["xattn", "gmu"]
+
+
+@pytest.fixture(scope="module")
+def sb():
+    import attention_decoding_amd as sb
+    return sb
+
+
+def err(y, ref):
+    y, ref = np.asarray(y, np.float64), np.asarray(ref, np.float64)
+    return float(np.max(np.abs(y - ref)) / max(float(np.max(np.abs(ref))), 1e-300))
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def report(name, e, tol=TOL):
+    print("%-64s err %.3e (tol %.0e)" % (name, e, tol), flush=True)
+    assert e <= tol, "%s: %.3e > %.0e" % (name, e, tol)
+
+
+def _snapshot(layers):
+    out = []
+    for ly in layers:
+        c = {}
+        for k, v in ly.items():
+            if isinstance(v, torch.Tensor):
+                c[k] = v.detach().cpu().clone()
+            elif isinstance(v, dict):
+                c[k] = {kk: vv.cpu() for kk, vv in v.items()}
+            else:
+                c[k] = v
+        out.append(c)
+    return out
+
+
+def _case(sb, B, T_pre, W, L, pos_list, seed, name, dm=256, di=512, NS=16, R=64, K=4, dff=512, Hq=2, Hkv=1):
+    inp = workload.sambay_prefill_inputs(B, T_pre, dm, di, NS, R, K, dff, Hq, Hkv, 128, W, L, SELF, CROSS,
+                                         seed=seed, device=DEV, fresh=False)
+    sb.sambay_prefill(inp.x, inp.self_layers, inp.cross_layers, inp.kcache, inp.vcache, window=W)
+    torch.cuda.synchronize()
+    before = _snapshot(inp.self_layers)
+    Kb, Vb = inp.kcache.cpu(), inp.vcache.cpu()
+    x_new = workload.normal((B, dm), seed=seed + 500, device=DEV)
+    pos = torch.tensor(pos_list, dtype=torch.int32, device=DEV)
+    print("case %s: B=%d prompt %d, positions %s" % (name, B, T_pre, pos_list), flush=True)
+    h = x_new.clone()
+    h, M = sb.sambay_decode_step(h, pos, inp.self_layers, inp.cross_layers, inp.kcache, inp.vcache, window=W)
+    torch.cuda.synchronize()
+    ref = oracle.sambay_decode_step(x_new.cpu(), before, _snapshot(inp.cross_layers), Hq, Hkv, pos.cpu(), Kb, Vb,
+                                    window=W)
+    report("%s h" % name, err(f64(h), ref["h_out"]))
+    report("%s M_last" % name, err(f64(M), ref["M_last"]))
+    rows = [(b, p) for b, p in enumerate(pos_list) if 0 <= p < L]
+    for b, p in rows:
+        report("%s cache row b=%d p=%d" % (name, b, p),
+               err(f64(inp.kcache[b, :, p]), ref["K"][b, :, p]) + err(f64(inp.vcache[b, :, p]), ref["V"][b, :, p]))
+    for i, ly in enumerate(inp.self_layers):
+        r = ref["layers"][i]
+        if ly["kind"] == "mamba":
+            report("%s layer %d ssm_state" % (name, i), err(f64(ly["ssm_state"]), r["ssm_state"]))
+            report("%s layer %d conv_state" % (name, i), err(f64(ly["conv_state"]), r["conv_state"]))
+        elif ly["kind"] == "swa":
+            report("%s layer %d ring" % (name, i), err(f64(ly["kring"]), r["kring"]) + err(f64(ly["vring"]), r["vring"]))
+
+
+@pytest.mark.parametrize("B,T_pre,W,pos", [
+    (2, 40, 16, [40, 40]),         # the token after a 40-token prompt, the ring wrapped
+    (3, 9, 16, [9, 9, 9]),         # the ring not yet full
+    (2, 40, 16, [40, 33]),         # per-sequence positions
+])
+def test_decode_step_after_prefill(sb, B, T_pre, W, pos):
+    _case(sb, B, T_pre, W, 64, pos, seed=31 + T_pre + pos[-1], name="decode B=%d prompt=%d pos=%s" % (B, T_pre, pos))
+
+
+def test_prefill_then_decode_equals_longer_prefill(sb):
+    """GPU: prefill of T tokens = prefill of T - 1 tokens + one decode step
+    (last token's h, M and the cache row), to the bf16 bar."""
+    B, T, W, L = 2, 50, 16, 64
+    a = workload.sambay_prefill_inputs(B, T, 256, 512, 16, 64, 4, 512, 2, 1, 128, W, L, SELF, CROSS, seed=41,
+                                       device=DEV, fresh=True)
+    h_full, M_full = (t.clone() for t in sb.sambay_prefill(a.x, a.self_layers, a.cross_layers, a.kcache, a.vcache,
+                                                           window=W))
+    b = workload.sambay_prefill_inputs(B, T, 256, 512, 16, 64, 4, 512, 2, 1, 128, W, L, SELF, CROSS, seed=41,
+                                       device=DEV, fresh=True)
+    sb.sambay_prefill(b.x[:, :T - 1].contiguous(), b.self_layers, b.cross_layers, b.kcache, b.vcache, window=W)
+    h = b.x[:, T - 1].contiguous()
+    pos = torch.full((B,), T - 1, dtype=torch.int32, device=DEV)
+    h, M = sb.sambay_decode_step(h, pos, b.self_layers, b.cross_layers, b.kcache, b.vcache, window=W)
+    torch.cuda.synchronize()
+    report("prefill(T) vs prefill(T-1) + step: h", err(f64(h), f64(h_full)))
+    report("prefill(T) vs prefill(T-1) + step: M", err(f64(M), f64(M_full)))
+    report("prefill(T) vs prefill(T-1) + step: cache", err(f64(b.kcache[:, :, :T]), f64(a.kcache[:, :, :T])))
+
+
+def test_decode_step_full_size_properties(sb):
+    """The model at its widths, 32 sequences, 34,816 cached positions: two
+    steps from the same state give the same bits; the outputs are finite."""
+    c = workload.SAMBAY_PREFILL
+    B, L = 32, c["L"]
+    inp = workload.sambay_prefill_inputs(B, 1, c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"], c["d_conv"],
+                                         c["d_ff"], c["Hq"], c["Hkv"], c["D"], c["window"], L,
+                                         workload.self_layer_kinds(c["n_self"]), workload.layer_kinds(c["n_cross"]),
+                                         seed=43, device=DEV, fresh=False)
+    inp.kcache.copy_(workload.normal(tuple(inp.kcache.shape), seed=44, device=DEV))
+    inp.vcache.copy_(workload.normal(tuple(inp.vcache.shape), seed=45, device=DEV))
+    pos = torch.full((B,), L - 1, dtype=torch.int32, device=DEV)
+    x = workload.normal((B, c["d_model"]), seed=46, device=DEV)
+    saved = _snapshot(inp.self_layers)
+    step = sb.SambayDecodeStep(x.clone(), pos, inp.self_layers, inp.cross_layers, inp.kcache, inp.vcache,
+                               window=c["window"])
+    step.tensors[0].copy_(x)
+    h1, m1 = (t.clone() for t in step())
+    for ly, s0 in zip(inp.self_layers, saved):
+        for k in ("conv_state", "ssm_state", "kring", "vring"):
+            if k in ly:
+                ly[k].copy_(s0[k].to(DEV))
+    step.tensors[0].copy_(x)
+    h2, m2 = step()
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2) and torch.equal(m1, m2)
+    assert torch.isfinite(h1.float()).all() and torch.isfinite(m1.float()).all()
