@@ -90,6 +90,7 @@ def _case(sb, B, T_pre, W, L, pos_list, seed, name, dm=256, di=512, NS=16, R=64,
     (2, 40, 16, [40, 40]),         # the token after a 40-token prompt, the ring wrapped
     (3, 9, 16, [9, 9, 9]),         # the ring not yet full
     (2, 40, 16, [40, 33]),         # per-sequence positions
+    (2, 40, 16, [-1, 40]),         # an inactive sequence: no cache writes, zero attention output
 ])
 def test_decode_step_after_prefill(sb, B, T_pre, W, pos):
     _case(sb, B, T_pre, W, 64, pos, seed=31 + T_pre + pos[-1], name="decode B=%d prompt=%d pos=%s" % (B, T_pre, pos))
