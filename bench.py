@@ -165,14 +165,16 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float, onl
         rows = c["batch"] * c["seq"]
         g = workload.gmu_inputs(rows, c["d_model"], c["d_inner"], seed=1, device=dev)
         Y = torch.empty(rows, c["d_model"], dtype=torch.bfloat16, device=dev)
-        ms = time_calls(lambda i: sb.gmu_forward(g.M, g.X, g.W1, g.W2, out=Y), 20)
+        # MFMA-bound: 20 warm-up calls let the clocks settle first (the first
+        # calls of a process read up to ~20% slow).
+        ms = time_calls(lambda i: sb.gmu_forward(g.M, g.X, g.W1, g.W2, out=Y), 20, warmup=20)
         flops = 4.0 * rows * c["d_model"] * c["d_inner"]
         # Context only: the same two products through torch's bf16 matmul (the
         # vendor BLAS), unfused, with the SiLU·M product as separate elementwise
         # work — what a caller without this library would run.
         F = torch.nn.functional
-        ms_lib = time_calls(lambda i: F.linear(g.M * F.silu(F.linear(g.X, g.W1)), g.W2), 20)
-        ms_lib_gemms = time_calls(lambda i: (F.linear(g.X, g.W1), F.linear(g.M, g.W2)), 20)
+        ms_lib = time_calls(lambda i: F.linear(g.M * F.silu(F.linear(g.X, g.W1)), g.W2), 20, warmup=10)
+        ms_lib_gemms = time_calls(lambda i: (F.linear(g.X, g.W1), F.linear(g.M, g.W2)), 20, warmup=10)
         res["gmu_prefill_8192x2560x5120"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
                                              "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500.0, 4),
                                              "frac_of_measured_mfma_loop": round(flops / ms / 1e9 / mfma_tflops, 4),
@@ -300,7 +302,7 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float, onl
         xs = workload.normal((Bp, Tp, dm), seed=96, device=dev)
         Mo = torch.empty(Bp, Tp, di, dtype=torch.bfloat16, device=dev)
         yo = torch.empty(Bp, Tp, dm, dtype=torch.bfloat16, device=dev)
-        ms = time_calls(lambda i: sb.mamba_prefill(xs, m.w, m.conv_state, m.ssm_state, Mo, yo), 10)
+        ms = time_calls(lambda i: sb.mamba_prefill(xs, m.w, m.conv_state, m.ssm_state, Mo, yo), 10, warmup=6)
         rows = Bp * Tp
         flops = 2.0 * rows * (2 * di * dm + ((R + 2 * N + 63) // 64 * 64) * di + di * R + dm * di)
         res["mamba_prefill_B%d_T%d" % (Bp, Tp)] = {
