@@ -65,7 +65,7 @@ def _case(sb, B, T_pre, W, L, pos_list, seed, name, dm=256, di=512, NS=16, R=64,
     Kb, Vb = inp.kcache.cpu(), inp.vcache.cpu()
     x_new = workload.normal((B, dm), seed=seed + 500, device=DEV)
     pos = torch.tensor(pos_list, dtype=torch.int32, device=DEV)
-    print("case %s: B=%d prompt %d, positions %s" % (name, B, T_pre, pos_list), flush=True)
+    print("case %s" % name, flush=True)
     h = x_new.clone()
     h, M = sb.sambay_decode_step(h, pos, inp.self_layers, inp.cross_layers, inp.kcache, inp.vcache, window=W)
     torch.cuda.synchronize()
@@ -91,9 +91,11 @@ def _case(sb, B, T_pre, W, L, pos_list, seed, name, dm=256, di=512, NS=16, R=64,
     (3, 9, 16, [9, 9, 9]),         # the ring not yet full
     (2, 40, 16, [40, 33]),         # per-sequence positions
     (2, 40, 16, [-1, 40]),         # an inactive sequence: no cache writes, zero attention output
+    (70, 5, 16, [5] * 70),         # more sequences than one 64-token group of the products
 ])
 def test_decode_step_after_prefill(sb, B, T_pre, W, pos):
-    _case(sb, B, T_pre, W, 64, pos, seed=31 + T_pre + pos[-1], name="decode B=%d prompt=%d pos=%s" % (B, T_pre, pos))
+    shown = pos if len(pos) <= 4 else "%d x [%d]" % (len(pos), pos[0])
+    _case(sb, B, T_pre, W, 64, pos, seed=31 + T_pre + pos[-1], name="decode B=%d prompt=%d pos=%s" % (B, T_pre, shown))
 
 
 def test_prefill_then_decode_equals_longer_prefill(sb):
