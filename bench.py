@@ -330,6 +330,22 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float, onl
             "layers": "16 self (8 SSM, 7 sliding-window 256, 1 full attention) + 16 cross (8 attention, 8 GMU), "
                       "SwiGLU d_ff 8192 in every layer"}
         del yp, full, selfonly
+        torch.cuda.empty_cache()
+        # One sequence at growing prompt lengths: the prefill stays linear in T
+        # (only windowed attention and the SSM recurrence run over the prompt).
+        scaling = {}
+        for T in (2048, 8192, 32768):
+            ys = workload.sambay_prefill_inputs(1, T, c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"],
+                                                c["d_conv"], c["d_ff"], c["Hq"], c["Hkv"], c["D"], c["window"], T,
+                                                workload.self_layer_kinds(c["n_self"]),
+                                                workload.layer_kinds(c["n_cross"]), seed=102, device=dev)
+            run = sb.SambayPrefill(ys.x, ys.self_layers, ys.cross_layers, ys.kcache, ys.vcache, window=c["window"])
+            ms_t = time_calls(lambda i: run(), 3, warmup=1)
+            scaling["T%d" % T] = {"ms": round(ms_t, 3), "prompt_tokens_per_s": round(T / ms_t * 1e3, 1),
+                                  "us_per_token": round(1e3 * ms_t / T, 3)}
+            del ys, run
+            torch.cuda.empty_cache()
+        res["sambay_prefill_B1_length_scaling"] = scaling
     if want("sambay_decode"):
         # Whole-model decode step: 32 sequences, each at the last of 34,816
         # cache positions (2K prompt + 32K generated), through the 16-layer
