@@ -69,7 +69,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     constexpr int INSTS = ROWS / IROWS;
     constexpr int IPW = INSTS / NWAVES;
     static_assert(IPW * NWAVES == INSTS && FM * 32 == TM && FN * 32 == TN, "tile shape");
-    constexpr int SROW = TN + 4;                  // fp32 per staged epilogue row
+    // Epilogue staging: blocks of 32 rows x SC columns per wave, SC = the
+    // wave's whole width when that fits in LDS and tiles a wave's lanes, else 32.
+    constexpr int SC_FULL = NWAVES * 32 * (TN + 4) * 4 <= 160 * 1024 && TN / 8 <= 64 && 64 % (TN / 8) == 0;
+    constexpr int SC = SC_FULL ? TN : 32;
+    constexpr int NJB = TN / SC;                  // column blocks per 32 rows
+    constexpr int SROW = SC + 4;                  // fp32 per staged epilogue row
     constexpr int RING_BYTES = NS * ROWS * BK * 2, STAGE_BYTES = NWAVES * 32 * SROW * 4;
     constexpr int LDS_BYTES = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -115,20 +120,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // The lane's 8 output columns in the epilogue (the same for every vector
-    // it stores): their softplus biases are loaded before the main loop.
-    constexpr int VPR = TN / 8;                   // 8-column vectors per row
+    // The lane's 8 output columns in each column block of the epilogue (the
+    // same for every vector it stores there): their softplus biases are
+    // loaded before the main loop.
+    constexpr int VPR = SC / 8;                   // 8-column vectors per staged row
     static_assert(64 % VPR == 0, "epilogue columns");
-    const int n_lane = bn + wn * TN + 8 * (lane % VPR);
-    float bias[8];
+    float bias[NJB][8];
     if (EPI == EPI_SOFTPLUS) {
-        f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
-        if (n_lane < N) {
-            b0 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(aux) + n_lane);
-            b1 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(aux) + n_lane + 4);
-        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bias[e] = b0[e], bias[4 + e] = b1[e];
+        for (int jb = 0; jb < NJB; ++jb) {
+            const int n_lane = bn + wn * TN + jb * SC + 8 * (lane % VPR);
+            f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
+            if (n_lane < N) {
+                b0 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(aux) + n_lane);
+                b1 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(aux) + n_lane + 4);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bias[jb][e] = b0[e], bias[jb][4 + e] = b1[e];
+        }
     }
 
     const int KT = Ks / BK;
@@ -165,43 +174,54 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
 
     // Epilogue through LDS: acc[i][j][v] holds row TM·wm + 32·i + 8·(v/4) +
     // 4·half + v%4, col TN·wn + 32·j + l32 of the tile, so each lane owns one
-    // column.  Each wave parks 32 rows of its block in its own LDS area, then
-    // every lane handles 8 consecutive columns: one 16-byte load of M (gate)
-    // and one 16-byte store per vector instead of 2-byte accesses.
-    constexpr int VPL = 32 * VPR / 64;            // vectors per lane per 32 rows
+    // column.  Each wave parks a 32 x SC block of its accumulators in its own
+    // LDS area, then every lane handles 8 consecutive columns: one 16-byte
+    // load of M (gate) or h (residual) and one 16-byte store per vector
+    // instead of 2-byte accesses.  Those loads run PD - 1 blocks ahead (all
+    // blocks when they fit in 64 registers).
+    constexpr int VPL = 32 * VPR / 64;            // vectors per lane per block
     static_assert(VPL * 64 == 32 * VPR, "epilogue shape");
+    constexpr int NB = FM * NJB;                  // blocks per wave
+    constexpr int PD = NB * VPL <= 16 ? NB : 2;
+    constexpr bool AUX = EPI == EPI_GATE || EPI == EPI_RESID;
     float *stage = reinterpret_cast<float *>(lds_raw) + wave * 32 * SROW;
-    u32x4 mv[FM][VPL];
-    if (EPI == EPI_GATE || EPI == EPI_RESID) {  // M (gate) or the residual h itself (out)
+    u32x4 mv[PD][VPL];
+    auto load_aux = [&](int blk) {  // M (gate) or the residual h itself (out)
         const bf16_t *src = EPI == EPI_GATE ? aux : out;
+        const int i = blk / NJB, jb = blk % NJB;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int u = 0; u < VPL; ++u) {
+            const int idx = u * 64 + lane, r = idx / VPR, c8 = idx % VPR;
+            const int m = bm + wm * TM + 32 * i + r, n = bn + wn * TN + jb * SC + 8 * c8;
+            mv[blk % PD][u] = (m < rows && n < N) ? ld16(src + (size_t)m * N + n) : (u32x4){0u, 0u, 0u, 0u};
+        }
+    };
+    if (AUX) {
 #pragma unroll
-            for (int u = 0; u < VPL; ++u) {
-                const int idx = u * 64 + lane, r = idx / VPR, c8 = idx % VPR;
-                const int m = bm + wm * TM + 32 * i + r, n = bn + wn * TN + 8 * c8;
-                mv[i][u] = (m < rows && n < N) ? ld16(src + (size_t)m * N + n) : (u32x4){0u, 0u, 0u, 0u};
-            }
+        for (int blk = 0; blk < PD - 1; ++blk) load_aux(blk);
     }
     __syncthreads();  // every wave is done with the operand ring
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int blk = 0; blk < NB; ++blk) {
+        const int i = blk / NJB, jb = blk % NJB;
+        if (AUX && blk + PD - 1 < NB) load_aux(blk + PD - 1);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int jj = 0; jj < SC / 32; ++jj)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) stage[(8 * (v / 4) + 4 * half + (v % 4)) * SROW + 32 * j + l32] = acc[i][j][v];
+            for (int v = 0; v < 16; ++v)
+                stage[(8 * (v / 4) + 4 * half + (v % 4)) * SROW + 32 * jj + l32] = acc[i][jb * (SC / 32) + jj][v];
         wave_lds_fence();
 #pragma unroll
         for (int u = 0; u < VPL; ++u) {
             const int idx = u * 64 + lane, r = idx / VPR, c8 = idx % VPR;
-            const int m = bm + wm * TM + 32 * i + r, n = bn + wn * TN + 8 * c8;
+            const int m = bm + wm * TM + 32 * i + r, n = bn + wn * TN + jb * SC + 8 * c8;
             const f32x4 lo = *reinterpret_cast<const f32x4 *>(&stage[r * SROW + 8 * c8]);
             const f32x4 hi = *reinterpret_cast<const f32x4 *>(&stage[r * SROW + 8 * c8 + 4]);
             float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             if (EPI == EPI_GATE) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t w = mv[i][u][e / 2];
+                    const uint32_t w = mv[blk % PD][u][e / 2];
                     const float mm = (e & 1) ? hi_bf16(w) : lo_bf16(w);
                     x[e] = mm * (x[e] / (1.f + expf(-x[e])));
                 }
@@ -209,14 +229,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
             if (EPI == EPI_RESID) {  // h = bf16(h + acc)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t w = mv[i][u][e / 2];
+                    const uint32_t w = mv[blk % PD][u][e / 2];
                     x[e] += (e & 1) ? hi_bf16(w) : lo_bf16(w);
                 }
             }
             if (EPI == EPI_SOFTPLUS) {  // softplus(acc + bias[n]), the SSM layer's step sizes
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float a = x[e] + bias[e];
+                    const float a = x[e] + bias[jb][e];
                     // log(1 + e^a) with the hardware exp/log: exact enough where it matters (|a| <= 20);
                     // a itself above, e^a below -15 (1 + e^a would round to 1).
                     x[e] = a > 20.f ? a : (a < -15.f ? __expf(a) : __logf(1.f + __expf(a)));
@@ -267,18 +287,40 @@ hipError_t launch_tile(const bf16_t *X, const bf16_t *W, int rows, int N, int K,
 hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
                        const bf16_t *aux, hipStream_t stream, int ksplit) {
     if (ksplit < 1 || K % (64 * ksplit) != 0 || (ksplit > 1 && epi != EPI_F32)) return hipErrorInvalidValue;
-    // Tile shape by how the grid fills the 256 CUs (measured on the prefill
-    // shapes, random operands): 256x256 tiles of 8 waves (128x64 each, one
-    // workgroup per CU) read a third less LDS per MFMA and win by 15-20%
-    // when their tile count is a whole number of 256-wide rounds (8192 x
-    // 8192 x 3072: 1071 vs 921 TFLOP/s; 8192 x 12288 x 3072: 1100 vs 937);
-    // otherwise two 128x128 workgroups per CU are best and also balance a
-    // partial last round best (256x128 tiles of 8 waves measured equal or
-    // slower on every prefill shape once the clocks had settled).
-    const int64_t t256 = (int64_t)((rows + 255) / 256) * ((N + 255) / 256);
-    if (ksplit == 1 && t256 >= 256 && t256 % 256 == 0)
-        return launch_tile<256, 256, 2, 4, 2, 64>(X, W, rows, N, K, epi, out, aux, ksplit, stream);
-    return launch_tile<128, 128, 2, 2, 2, 64>(X, W, rows, N, K, epi, out, aux, ksplit, stream);
+    // Tile shape by how the grid fills the 256 CUs.  The large tiles (8
+    // waves, one workgroup per CU) read less LDS per MFMA; two 128x128
+    // workgroups per CU fill 512 slots per round.  Each shape is priced as
+    // its rounds of tiles times a round's area over the shape's rate, a last
+    // partial round at 0.4 + 0.6 x its fill (a part-filled chip runs each
+    // tile faster).  Rates per unit of tile area, measured on MI355X over
+    // 2048-32768 rows and the prefill products (random operands): 256x320
+    // and 256x256 1.0, 256x192 0.9, 128x128 0.8; the rule's choice was
+    // within 0.7% of the fastest shape in all 24 measured cases (e.g. the
+    // GMU products at 8192 rows on 256x320 tiles, 5120 x 2560: 253 vs 284
+    // us with 128x128; 2560 x 5120: 203 vs 255 us; 3072-wide outputs at
+    // 8192 rows on 256x192, 3072 x 6144: 325 vs 340 us).  All shapes add
+    // the same products in the same order (identical bits).  The softplus
+    // epilogue keeps 320-wide tiles out (its 5 bias vectors spill).
+    if (ksplit > 1) return launch_tile<128, 128, 2, 2, 2, 64>(X, W, rows, N, K, epi, out, aux, ksplit, stream);
+    struct Shape { int bm, bn, per_cu; double rate; };
+    const Shape shapes[] = {{256, 320, 1, 1.0}, {256, 256, 1, 1.0}, {256, 192, 1, 0.9}, {128, 128, 2, 0.8}};
+    int best = -1;
+    double best_t = 0.0;
+    for (int i = 0; i < 4; ++i) {
+        const Shape &c = shapes[i];
+        if (c.bn == 320 && epi == EPI_SOFTPLUS) continue;
+        const int64_t tiles = (int64_t)((rows + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        const int64_t slots = 256LL * c.per_cu, full = tiles / slots, rem = tiles % slots;
+        const double rounds = (double)full + (rem ? 0.4 + 0.6 * (double)rem / (double)slots : 0.0);
+        const double t = rounds * c.bm * c.bn * c.per_cu / c.rate;
+        if (best < 0 || t < best_t) best = i, best_t = t;
+    }
+    switch (best) {
+        case 0: return launch_tile<256, 320, 4, 2, 2, 64>(X, W, rows, N, K, epi, out, aux, ksplit, stream);
+        case 1: return launch_tile<256, 256, 2, 4, 2, 64>(X, W, rows, N, K, epi, out, aux, ksplit, stream);
+        case 2: return launch_tile<256, 192, 4, 2, 2, 64>(X, W, rows, N, K, epi, out, aux, ksplit, stream);
+        default: return launch_tile<128, 128, 2, 2, 2, 64>(X, W, rows, N, K, epi, out, aux, ksplit, stream);
+    }
 }
 
 }  // namespace sambay

@@ -108,11 +108,14 @@ def test_gmu_prefill_full_sampled_rows(sb):
     report("gmu prefill 8192x2560x5120 (%d rows)" % len(idx), err(f64(Y[ii]), ref), TOL_BF16)
 
 
-@pytest.mark.parametrize("rows,d_model,d_inner", [(4000, 1024, 4096), (4000, 1024, 2048)])
+@pytest.mark.parametrize("rows,d_model,d_inner", [(4000, 1024, 4096), (4000, 1024, 2048), (4000, 1024, 4992),
+                                                  (4000, 3008, 1024)])
 def test_gmu_prefill_wide_tiles(sb, rows, d_model, d_inner):
-    """The gate product of d_inner 4096 fills a whole round of 256 CUs with
-    256x256 tiles (d_inner 2048: 128x128 tiles); 4000 rows leave a ragged
-    last row tile.  The oracle checks 64 sampled rows."""
+    """Each GEMM tile shape: the gate product of d_inner 4096 runs on 256x256
+    tiles, d_inner 2048 on 128x128, d_inner 4992 on 256x320 (last column
+    tile 192 wide) and the output product of d_model 3008 on 256x192 (last
+    column tile 128 wide); 4000 rows leave a ragged last row tile.  The
+    oracle checks 64 sampled rows."""
     g = workload.gmu_inputs(rows, d_model, d_inner, seed=8, device=DEV)
     Y = sb.gmu_forward(g.M, g.X, g.W1, g.W2)
     torch.cuda.synchronize()
