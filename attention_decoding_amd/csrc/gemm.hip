@@ -69,11 +69,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     constexpr int INSTS = ROWS / IROWS;
     constexpr int IPW = INSTS / NWAVES;
     static_assert(IPW * NWAVES == INSTS && FM * 32 == TM && FN * 32 == TN, "tile shape");
+    // EPI_SWIGLU: the W tile interleaves, per 64 rows, 32 gate rows (W) and
+    // the 32 up rows (aux) of the same output columns, so a wave's fragment
+    // pair (2p, 2p + 1) holds g and u of one 32-column block and the tile
+    // covers BN / 2 output columns.
+    constexpr bool PAIR = EPI == EPI_SWIGLU;
+    static_assert(!PAIR || FN % 2 == 0, "paired gate/up fragments");
+    constexpr int OBN = PAIR ? BN / 2 : BN, OTN = PAIR ? TN / 2 : TN;  // output columns per tile / wave
     // Epilogue staging: blocks of 32 rows x SC columns per wave, SC = the
     // wave's whole width when that fits in LDS and tiles a wave's lanes, else 32.
-    constexpr int SC_FULL = NWAVES * 32 * (TN + 4) * 4 <= 160 * 1024 && TN / 8 <= 64 && 64 % (TN / 8) == 0;
-    constexpr int SC = SC_FULL ? TN : 32;
-    constexpr int NJB = TN / SC;                  // column blocks per 32 rows
+    constexpr int SC_FULL = NWAVES * 32 * (OTN + 4) * 4 <= 160 * 1024 && OTN / 8 <= 64 && 64 % (OTN / 8) == 0;
+    constexpr int SC = SC_FULL ? OTN : 32;
+    constexpr int NJB = OTN / SC;                 // column blocks per 32 rows
     constexpr int SROW = SC + 4;                  // fp32 per staged epilogue row
     constexpr int RING_BYTES = NS * ROWS * BK * 2, STAGE_BYTES = NWAVES * 32 * SROW * 4;
     constexpr int LDS_BYTES = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
@@ -81,7 +88,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     __shared__ __attribute__((aligned(1024))) char lds_raw[LDS_BYTES];
     bf16_t(*lds)[ROWS * BK] = reinterpret_cast<bf16_t(*)[ROWS * BK]>(lds_raw);
 
-    const int tiles_m = (rows + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int tiles_m = (rows + BM - 1) / BM, tiles_n = (N + OBN - 1) / OBN;
     const int ntiles = tiles_m * tiles_n;
     // Split K (EPI_F32 only): slice blockIdx.x / ntiles of K / ksplit, its
     // partial sums to the slice's own [rows, N] block of out.
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     const int gsize = min(tiles_m - first_m, kGroupM);
     const int tm = first_m + (pid % (kGroupM * tiles_n)) % gsize;
     const int tn = (pid % (kGroupM * tiles_n)) / gsize;
-    const int bm = tm * BM, bn = tn * BN;
+    const int bm = tm * BM, bn = tn * OBN;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
     const int wm = wave / WGN, wn = wave % WGN;
@@ -103,8 +110,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     for (int q = 0; q < IPW; ++q) {
         const int r = (wave * IPW + q) * IROWS + lane / CPR;
         const int logical = swz<BK>(r, lane % CPR);
-        const bf16_t *base = r < BM ? X + (size_t)min(bm + r, rows - 1) * K
-                                    : W + (size_t)min(bn + r - BM, N - 1) * K;
+        const bf16_t *base;
+        if (r < BM) {
+            base = X + (size_t)min(bm + r, rows - 1) * K;
+        } else if (PAIR) {
+            const int rw = r - BM, n = bn + 32 * (rw / 64) + (rw & 31);
+            base = ((rw & 32) ? aux : W) + (size_t)min(n, N - 1) * K;
+        } else {
+            base = W + (size_t)min(bn + r - BM, N - 1) * K;
+        }
         src[q] = base + (size_t)kslice * Ks + 8 * logical;
     }
     auto issue = [&](int kt, int slot) {
@@ -129,7 +143,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
     if (EPI == EPI_SOFTPLUS) {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-            const int n_lane = bn + wn * TN + jb * SC + 8 * (lane % VPR);
+            const int n_lane = bn + wn * OTN + jb * SC + 8 * (lane % VPR);
             f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
             if (n_lane < N) {
                 b0 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(aux) + n_lane);
@@ -192,7 +206,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
 #pragma unroll
         for (int u = 0; u < VPL; ++u) {
             const int idx = u * 64 + lane, r = idx / VPR, c8 = idx % VPR;
-            const int m = bm + wm * TM + 32 * i + r, n = bn + wn * TN + jb * SC + 8 * c8;
+            const int m = bm + wm * TM + 32 * i + r, n = bn + wn * OTN + jb * SC + 8 * c8;
             mv[blk % PD][u] = (m < rows && n < N) ? ld16(src + (size_t)m * N + n) : (u32x4){0u, 0u, 0u, 0u};
         }
     };
@@ -206,15 +220,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
         const int i = blk / NJB, jb = blk % NJB;
         if (AUX && blk + PD - 1 < NB) load_aux(blk + PD - 1);
 #pragma unroll
-        for (int jj = 0; jj < SC / 32; ++jj)
+        for (int jj = 0; jj < SC / 32; ++jj) {
+            const int q = jb * (SC / 32) + jj;
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                stage[(8 * (v / 4) + 4 * half + (v % 4)) * SROW + 32 * jj + l32] = acc[i][jb * (SC / 32) + jj][v];
+            for (int v = 0; v < 16; ++v) {
+                float val;
+                if constexpr (PAIR) {  // SiLU(g) · u
+                    const float g = acc[i][2 * q][v];
+                    val = (g / (1.f + expf(-g))) * acc[i][2 * q + 1][v];
+                } else {
+                    val = acc[i][q][v];
+                }
+                stage[(8 * (v / 4) + 4 * half + (v % 4)) * SROW + 32 * jj + l32] = val;
+            }
+        }
         wave_lds_fence();
 #pragma unroll
         for (int u = 0; u < VPL; ++u) {
             const int idx = u * 64 + lane, r = idx / VPR, c8 = idx % VPR;
-            const int m = bm + wm * TM + 32 * i + r, n = bn + wn * TN + jb * SC + 8 * c8;
+            const int m = bm + wm * TM + 32 * i + r, n = bn + wn * OTN + jb * SC + 8 * c8;
             const f32x4 lo = *reinterpret_cast<const f32x4 *>(&stage[r * SROW + 8 * c8]);
             const f32x4 hi = *reinterpret_cast<const f32x4 *>(&stage[r * SROW + 8 * c8 + 4]);
             float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -262,7 +286,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
 template <int BM, int BN, int WGM, int WGN, int NS, int BK>
 hipError_t launch_tile(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
                      const bf16_t *aux, int ksplit, hipStream_t stream) {
-    const int tiles = ((rows + BM - 1) / BM) * ((N + BN - 1) / BN) * ksplit;
+    const int obn = epi == EPI_SWIGLU ? BN / 2 : BN;
+    const int tiles = ((rows + BM - 1) / BM) * ((N + obn - 1) / obn) * ksplit;
     TimingScope ts(kTimeGemm, stream);
     if (epi == EPI_GATE)
         hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_GATE>), dim3(tiles), dim3(64 * WGM * WGN), 0,
@@ -273,6 +298,13 @@ hipError_t launch_tile(const bf16_t *X, const bf16_t *W, int rows, int N, int K,
     else if (epi == EPI_RESID)
         hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_RESID>), dim3(tiles), dim3(64 * WGM * WGN), 0,
                            stream, X, W, rows, N, K, out, aux, ksplit);
+    else if (epi == EPI_SWIGLU) {
+        if constexpr ((BN / WGN / 32) % 2 == 0)
+            hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_SWIGLU>), dim3(tiles), dim3(64 * WGM * WGN),
+                               0, stream, X, W, rows, N, K, out, aux, ksplit);
+        else
+            return hipErrorInvalidValue;  // the paired form needs fragment pairs per wave
+    }
     else if (epi == EPI_SOFTPLUS)
         hipLaunchKernelGGL((gemm32_kernel<BM, BN, WGM, WGN, NS, BK, EPI_SOFTPLUS>), dim3(tiles),
                            dim3(64 * WGM * WGN), 0, stream, X, W, rows, N, K, out, aux, ksplit);
@@ -309,7 +341,11 @@ hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K,
     for (int i = 0; i < 4; ++i) {
         const Shape &c = shapes[i];
         if (c.bn == 320 && epi == EPI_SOFTPLUS) continue;
-        const int64_t tiles = (int64_t)((rows + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        // The paired SwiGLU form needs an even number of 32-column fragments
+        // per wave (256x256 and 128x128); its tiles cover bn / 2 outputs.
+        if (epi == EPI_SWIGLU && (c.bn == 320 || c.bn == 192)) continue;
+        const int obn = epi == EPI_SWIGLU ? c.bn / 2 : c.bn;
+        const int64_t tiles = (int64_t)((rows + c.bm - 1) / c.bm) * ((N + obn - 1) / obn);
         const int64_t slots = 256LL * c.per_cu, full = tiles / slots, rem = tiles % slots;
         const double rounds = (double)full + (rem ? 0.4 + 0.6 * (double)rem / (double)slots : 0.0);
         const double t = rounds * c.bm * c.bn * c.per_cu / c.rate;

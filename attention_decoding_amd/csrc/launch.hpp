@@ -155,7 +155,9 @@ size_t skinny_partial_bytes_dual(int T, int N, const SkinnyPlan &p);
 // out[r, n] = epi( Σ_k X[r, k] · W[n, k] ), any row count, N % 8 == 0, K % 64 == 0.
 // epi: EPI_BF16, EPI_GATE (aux = M), EPI_RESID (out = bf16(out + acc), in
 // place), EPI_F32 or EPI_SOFTPLUS (out is then a float array; EPI_SOFTPLUS
-// reads its fp32 bias [N] through aux).  ksplit > 1
+// reads its fp32 bias [N] through aux), EPI_SWIGLU (out = bf16(SiLU(X W^T) ·
+// (X aux^T)): W the gate and aux the up weights, both [N, K]; the hidden
+// activation of a SwiGLU MLP in one pass).  ksplit > 1
 // (EPI_F32 only, K % (64·ksplit) == 0): slice s of K writes its partial sums
 // to out + s·rows·N.
 hipError_t launch_gemm(const bf16_t *X, const bf16_t *W, int rows, int N, int K, Epilogue epi, bf16_t *out,
@@ -189,7 +191,7 @@ struct SelfDecoderLayout {
     int32_t *lens;
     bf16_t *m_last;                      // [B, d_inner]: M at position T-1 when the caller keeps none
     void *scratch;                       // shared by the attention, MLP and SSM layers in turn
-    bf16_t *q, *k, *v, *o, *up, *hid;    // views into scratch
+    bf16_t *q, *k, *v, *o, *hid;         // views into scratch
     void *attn_ws;
     size_t bytes;
 };

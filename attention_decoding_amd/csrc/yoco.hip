@@ -6,10 +6,10 @@
 // Generation", section 整体框架; the Samba self-decoder alternates Mamba and
 // sliding-window attention, section 消融实验).
 //
-// Every product is the MFMA GEMM over the B·T prompt rows (residual adds and
-// the SwiGLU gate fused into its epilogues), the SSM layers are the chunked
-// prefill of mamba.hip, the attention layers the prefill kernel of
-// prefill.hip.  This file adds the cache stores and the last-row gathers.
+// Every product is the MFMA GEMM over the B·T prompt rows (residual adds
+// fused into its epilogues, the MLP's gate and up products paired in one),
+// the SSM layers are the chunked prefill of mamba.hip, the attention layers
+// the prefill kernel of prefill.hip.  This file adds the cache stores and the last-row gathers.
 // Nothing after the final full-attention layer looks at earlier positions,
 // so when that layer is the last one only its keys and values are computed
 // for every token here; its attention, output projection and MLP run on the
@@ -85,7 +85,7 @@ SelfDecoderLayout self_decoder_layout(void *base, int64_t B, int64_t T, int64_t 
     // layers' own workspace.
     const size_t attn = r256((size_t)rows * Hq * D * 2) * 2 + r256((size_t)rows * Hkv * D * 2) * 2 +
                         r256(attn_prefill_workspace_need(B, T, Hkv));
-    const size_t mlp = d_ff > 0 ? r256((size_t)rows * d_ff * 2) * 2 : 0;
+    const size_t mlp = d_ff > 0 ? r256((size_t)rows * d_ff * 2) : 0;
     const size_t ssm = r256(mamba_prefill_workspace_need(B, T, d_inner, d_state, dt_rank));
     size_t shared = attn > mlp ? attn : mlp;
     if (ssm > shared) shared = ssm;
@@ -96,8 +96,7 @@ SelfDecoderLayout self_decoder_layout(void *base, int64_t B, int64_t T, int64_t 
     L.v = reinterpret_cast<bf16_t *>(s ? (char *)L.k + r256((size_t)rows * Hkv * D * 2) : nullptr);
     L.o = reinterpret_cast<bf16_t *>(s ? (char *)L.v + r256((size_t)rows * Hkv * D * 2) : nullptr);
     L.attn_ws = s ? (char *)L.o + r256((size_t)rows * Hq * D * 2) : nullptr;
-    L.up = reinterpret_cast<bf16_t *>(s);
-    L.hid = reinterpret_cast<bf16_t *>(s && d_ff > 0 ? s + r256((size_t)rows * d_ff * 2) : nullptr);
+    L.hid = reinterpret_cast<bf16_t *>(s);
     L.bytes = off;
     return L;
 }
@@ -156,10 +155,9 @@ hipError_t launch_self_decoder(const SelfDecoderArgs &a, const SelfDecoderLayout
                 return e;
             xm = L.xn;
         }
-        // hid = (x W_up^T) ⊙ SiLU(x W_gate^T), then h += hid W_down^T.
-        e = launch_gemm(xm, (const bf16_t *)ly.w_up, rows, a.d_ff, dm, EPI_BF16, L.up, nullptr, stream);
-        if (e == hipSuccess)
-            e = launch_gemm(xm, (const bf16_t *)ly.w_gate, rows, a.d_ff, dm, EPI_GATE, L.hid, L.up, stream);
+        // hid = SiLU(x W_gate^T) ⊙ (x W_up^T) in one paired product, then h += hid W_down^T.
+        e = launch_gemm(xm, (const bf16_t *)ly.w_gate, rows, a.d_ff, dm, EPI_SWIGLU, L.hid,
+                        (const bf16_t *)ly.w_up, stream);
         if (e == hipSuccess)
             e = launch_gemm(L.hid, (const bf16_t *)ly.w_down, rows, dm, a.d_ff, EPI_RESID, L.h, nullptr, stream);
     }
