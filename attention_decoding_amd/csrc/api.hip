@@ -200,7 +200,7 @@ extern "C" sb_status gmu_forward(const void *M, const void *X, const void *W1, c
                     (long long)rows, (long long)d_model, (long long)d_inner, p1.rows_per_wg, p1.k_splits,
                     p2.rows_per_wg, p2.k_splits);
         } else {
-            fprintf(stderr, "[sambay] gmu_forward rows=%lld %lldx%lld bf16 -> prefill GEMMs (128x128 tiles)\n",
+            fprintf(stderr, "[sambay] gmu_forward rows=%lld %lldx%lld bf16 -> prefill GEMMs (MFMA tiles)\n",
                     (long long)rows, (long long)d_model, (long long)d_inner);
         }
     }

@@ -6,11 +6,12 @@
 //   Y = H W2^T.
 //
 // Design (compute-bound at prefill sizes):
-//  * 128x128 output tile per workgroup, 4 waves in a 2x2 grid, each wave a
-//    64x64 block of 2x2 32x32x16 MFMA tiles (on gfx950 the 32x32x16 bf16 form
-//    measured ~2.4 PFLOP/s in a register-only loop, the 16x16x32 form ~1.4);
-//    256x256 tiles (8 waves of 128x64) where their grid fills whole rounds
-//    of the 256 CUs (launch_gemm's rule).
+//  * Workgroup tiles of 32x32x16 MFMA blocks (on gfx950 the 32x32x16 bf16
+//    form measured ~2.4 PFLOP/s in a register-only loop, the 16x16x32 form
+//    ~1.4): 256x320, 256x256 and 256x192 tiles of 8 waves (64x160, 128x64,
+//    64x96 per wave; one workgroup per CU) and 128x128 tiles of 4 waves
+//    (64x64 each; two per CU), chosen per call by how whole rounds of the
+//    256 CUs fill (launch_gemm's rule).
 //  * K advances BK = 64 at a time through a two-stage LDS ring filled by direct
 //    global -> LDS loads (global_load_lds_dwordx4): no register staging, and
 //    the next stage's loads run under this stage's MFMAs.  A bare s_barrier
@@ -18,20 +19,19 @@
 //    would also wait for the stage still in flight).  16-byte chunks of each
 //    128-byte LDS row are XOR-swizzled by (row / 2): the 16 lanes of an
 //    operand read hit 16 distinct bank groups (no bank conflicts counted).
-//  * Two workgroups per CU; workgroup ids are remapped so each XCD (ids
-//    round-robin over 8) works on a contiguous band of tiles, grouped 8
-//    row-tiles at a time.
+//  * Workgroup ids are remapped so each XCD (ids round-robin over 8) works
+//    on a contiguous band of tiles, grouped 8 row-tiles at a time.
 //  * The epilogue parks each wave's accumulators in LDS (the ring is free by
 //    then) so that M (or, for the residual add, h itself) is read and the
-//    output written as 16-byte vectors.
-//  * Measured at 8192 x 2560 x 5120 (both GMU products, random data): ~250 us
-//    for the gate product and ~227 us for the output product (850-950
-//    TFLOP/s).  A 3-5 deep ring (BK 64 or 32), 256-wide tiles with 8 or 16
-//    waves, 128x160 tiles (whole tile rounds on the output product), 64x128
-//    or 128x128 blocks per wave, and reading a whole slice's
-//    fragments before its MFMAs (forced with scheduling barriers) all
-//    measured equal or slower; MFMA busy stays near a third, LDS bank
-//    conflicts are zero.
+//    output written as 16-byte vectors.  The paired form (EPI_SWIGLU) loads
+//    gate and up weight rows into one W tile and forms SiLU(g)·u there.
+//  * Measured at 8192 x 2560 x 5120 (both GMU products on 256x320 tiles,
+//    random data): ~243 us for the gate product and ~193 us for the output
+//    product (885 and 1112 TFLOP/s).  A 3-5 deep ring (BK 64 or 32), 16-wave
+//    tiles, 128x160 tiles, 4 waves of 128x128 per 256x256 tile, and reading
+//    a whole slice's fragments before its MFMAs (forced with scheduling
+//    barriers) all measured equal or slower; MFMA busy stays under half,
+//    LDS bank conflicts are zero.
 #include "device.hpp"
 #include "launch.hpp"
 
