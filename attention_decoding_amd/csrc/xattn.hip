@@ -11,17 +11,20 @@
 //  * One workgroup per (chunk s, KV head g, sequence b); its four waves take
 //    32-position blocks of the chunk round-robin.  All G query heads of the
 //    group share every K/V byte loaded, so the cache is read exactly once.
+//  * K and V stream into per-wave LDS buffers by direct global -> LDS copies
+//    of whole rows with the non-temporal policy (the next block's copies in
+//    flight while the wave computes on the current one).
 //  * Scores: one 16x16x32 MFMA tile per 16 positions and 32 dims, K rows as
-//    the A operand straight from HBM (each lane streams 64 contiguous bytes of
-//    one row), the group's queries as the B operand (padded to 16 heads).
+//    the A operand read from LDS, the group's queries as the B operand
+//    (padded to 16 heads).
 //    The query is pre-scaled by scale·log2(e) and split into bf16 hi + lo
 //    parts, so q·k keeps ~16 significant bits with exact bf16 keys.
 //  * Online softmax in the log2 domain per lane (each lane owns one head of
 //    8 positions); the block max is shared across the 4 lane groups.
 //  * P·V: the score tile's accumulator layout is already the B operand of
 //    the second product (each lane holds 8 probabilities of one head), so P
-//    never moves.  V is staged through a per-wave LDS tile and read back
-//    transposed (position-major per lane) as the A operand.
+//    never moves.  V is read back from its LDS buffer transposed
+//    (position-major per lane) as the A operand.
 //  * Partials (m, l, o) per (b, head, chunk) in fp32; a merge kernel combines
 //    the chunks by log-sum-exp in a fixed order (deterministic, no atomics)
 //    and stores bf16 (plus, on request, the bf16 low part of the fp32 value).
@@ -59,13 +62,16 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kVStride = kHeadDim + 8;  // bf16 per staged V row: 272-byte rows spread the transposed reads over banks
+constexpr int kBlockElems = kKeyBlock * kHeadDim;  // bf16 per 32-position K or V block (8 KB)
+constexpr int kWaitLds = 0xc07f;  // lgkmcnt(0): this wave's LDS reads have returned
+
+// Copy policy of the cache streams: non-temporal (each byte is read once).
+constexpr int kStreamPolicy = 2;
 
 template <bool QF32, bool DIFF>
-// Three waves per SIMD (12 per CU) keep enough block loads in flight; a
-// register-level prefetch of the next block measured slower (it forces one
-// wave per SIMD or spills).
-__global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__restrict__ qv,
+// Two workgroups per CU (64 KB of K and V buffers each); every wave keeps the
+// next block's copies in flight while it computes on the current one.
+__global__ __launch_bounds__(kThreads, 2) void xattn_split_kernel(const void *__restrict__ qv,
                                                                const bf16_t *__restrict__ K,
                                                                const bf16_t *__restrict__ V,
                                                                float2 *__restrict__ part_ml,
@@ -74,7 +80,8 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
                                                                int B, int Hq, int Hkv, int L,
                                                                const int32_t *__restrict__ lens, int chunk, int S,
                                                                float qscale) {
-    __shared__ __attribute__((aligned(16))) bf16_t vs[kWaves][kKeyBlock][kVStride];
+    __shared__ __attribute__((aligned(16))) bf16_t kbuf[kWaves][kBlockElems];
+    __shared__ __attribute__((aligned(16))) bf16_t vbuf[kWaves][kBlockElems];
     __shared__ float red_m[kWaves][kMaxGroup];
     __shared__ float red_l[kWaves][kMaxGroup];
 
@@ -91,7 +98,7 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
         // the empty chunks); workgroups past the last item exit.  Each thread
         // counts the items of a contiguous run of sequences, a scan over the
         // runs locates the sequence of this workgroup's item.
-        int *runs = reinterpret_cast<int *>(&vs[0][0][0]);  // kThreads ints, free until the first block
+        int *runs = reinterpret_cast<int *>(&kbuf[0][0]);  // kThreads ints, free until the first block
         // Chunks of sequence i: those holding positions, at least one (an empty
         // item still writes the sequence's zero result).
         auto chunks_of = [&](int i) { return max(1, (min(max(lens[i], 0), L) + chunk - 1) / chunk); };
@@ -171,55 +178,73 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
     f32x4 acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    bf16_t(*vw)[kVStride] = vs[wave];
+    bf16_t *kw = kbuf[wave], *vw = vbuf[wave];
 
-    // One 32-position block in registers: rows base + col (k0/v0) and base + 16 + col
-    // (k1/v1), 16 bytes per MFMA k-step.  For each k-step the 4 lane groups of a
-    // row read 64 contiguous bytes (one full 64-byte memory request per row; a
-    // 16-byte-per-64 pattern measured 1.7x slower).
-    struct Blk {
-        u32x4 k0[4], k1[4], v0[4], v1[4];
-    };
-    auto load_block = [&](int blk, Blk &r) {
+    // One 32-position block of K or V into this wave's LDS buffer by direct
+    // global -> LDS copies: 8 instructions of 1 KB, each 4 whole 256-byte
+    // rows, so every request reads whole cache lines (register loads in the
+    // MFMA operand layout read 64 bytes of each of 16 rows per instruction,
+    // and the non-temporal policy then fetches lines twice).  Lane i copies
+    // 16-byte chunk (i % 16) ^ swz(row) of row 4j + i / 16 into slot i % 16:
+    // K rows swizzle by row % 16 (16 rows read at one chunk), V rows by
+    // 2 · ((row / 4) % 4) (4 rows read at one dimension), so the reads below
+    // hit distinct LDS banks.  Rows past the chunk end are clamped to its
+    // last row (in bounds) and masked later.
+    auto issue_block = [&](const bf16_t *src, bf16_t *dst, int blk, bool is_v) {
         const int base = j0 + blk * kKeyBlock;
-        // Rows past the chunk end are clamped to its last row (in bounds) and masked later.
-        const int ra = min(base + col, j1 - 1), rb = min(base + 16 + col, j1 - 1);
-        const bf16_t *kpa = Kb + (size_t)ra * kHeadDim + 8 * grp;
-        const bf16_t *kpb = Kb + (size_t)rb * kHeadDim + 8 * grp;
-        const bf16_t *vpa = Vb + (size_t)ra * kHeadDim + 8 * grp;
-        const bf16_t *vpb = Vb + (size_t)rb * kHeadDim + 8 * grp;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            r.k0[t] = ld16(kpa + 32 * t);
-            r.k1[t] = ld16(kpb + 32 * t);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            r.v0[t] = ld16(vpa + 32 * t);
-            r.v1[t] = ld16(vpb + 32 * t);
+        for (int j = 0; j < 8; ++j) {
+            const int r = 4 * j + (lane >> 4), slot = lane & 15;
+            const int c = slot ^ (is_v ? 2 * ((r >> 2) & 3) : (r & 15));
+            const int row = min(base + r, j1 - 1);
+            __builtin_amdgcn_global_load_lds(src + (size_t)row * kHeadDim + 8 * c,
+                                             (__attribute__((address_space(3))) void *)(dst + 512 * j), 16, 0,
+                                             kStreamPolicy);
         }
     };
 
-    auto process_block = [&](int blk, const Blk &r) {
+    // A block is read from LDS into registers whole (K fragments and the
+    // transposed V operand) before the next block's copies are issued: a read
+    // of LDS waits for every copy issued before it, so the copies of block
+    // blk + 4 fly while the wave computes on block blk.
+    auto process_block = [&](int blk, bool next) {
         const int base = j0 + blk * kKeyBlock;
+        // K fragments: rows col (k0) and 16 + col (k1), dims 32·t + 8·grp .. +7 (chunk 4t + grp).
+        u32x4 k0[4], k1[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int sl = (4 * t + grp) ^ col;
+            k0[t] = *reinterpret_cast<const u32x4 *>(&kw[col * kHeadDim + 8 * sl]);
+            k1[t] = *reinterpret_cast<const u32x4 *>(&kw[(16 + col) * kHeadDim + 8 * sl]);
+        }
+        // V^T operand: dim 16·db + col at positions 4·grp + i and 16 + 4·grp + i, whose
+        // rows all carry swizzle 2·grp.
+        u32x4 va[8];
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const int e = 8 * (2 * (db ^ grp) + (col >> 3)) + (col & 7);
+            const bf16_t *v0 = vw + (4 * grp) * kHeadDim + e, *v1 = vw + (16 + 4 * grp) * kHeadDim + e;
+            va[db][0] = (uint32_t)v0[0] | ((uint32_t)v0[kHeadDim] << 16);
+            va[db][1] = (uint32_t)v0[2 * kHeadDim] | ((uint32_t)v0[3 * kHeadDim] << 16);
+            va[db][2] = (uint32_t)v1[0] | ((uint32_t)v1[kHeadDim] << 16);
+            va[db][3] = (uint32_t)v1[2 * kHeadDim] | ((uint32_t)v1[3 * kHeadDim] << 16);
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLds);  // the buffers are free
+        if (next) {
+            issue_block(Kb, kw, blk + kWaves, false);
+            issue_block(Vb, vw, blk + kWaves, true);
+        }
         // Scores of positions base + 4·grp + i (s0) and base + 16 + 4·grp + i (s1) for head col.
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            s0 = mfma16x16x32(r.k0[t], qhi[t], s0);
-            s1 = mfma16x16x32(r.k1[t], qhi[t], s1);
+            s0 = mfma16x16x32(k0[t], qhi[t], s0);
+            s1 = mfma16x16x32(k1[t], qhi[t], s1);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            s0 = mfma16x16x32(r.k0[t], qlo[t], s0);
-            s1 = mfma16x16x32(r.k1[t], qlo[t], s1);
-        }
-
-        wave_lds_fence();  // the previous block's transposed reads are done
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            *reinterpret_cast<u32x4 *>(&vw[col][32 * t + 8 * grp]) = r.v0[t];
-            *reinterpret_cast<u32x4 *>(&vw[16 + col][32 * t + 8 * grp]) = r.v1[t];
+            s0 = mfma16x16x32(k0[t], qlo[t], s0);
+            s1 = mfma16x16x32(k1[t], qlo[t], s1);
         }
 
 #pragma unroll
@@ -245,27 +270,17 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
         for (int i = 0; i < 8; ++i) acc[i] *= alpha;
         const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                           pack_bf16x2(p[6], p[7])};
-
-        wave_lds_fence();  // the staged V rows are visible to every lane
-        // O^T[dim][head] += V^T[dim][pos] · P^T[pos][head]; lane reads dim 16·db + col at its 8 positions.
+        // O^T[dim][head] += V^T[dim][pos] · P^T[pos][head].
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-            const int d = 16 * db + col;
-            u32x4 va;
-            va[0] = (uint32_t)vw[4 * grp + 0][d] | ((uint32_t)vw[4 * grp + 1][d] << 16);
-            va[1] = (uint32_t)vw[4 * grp + 2][d] | ((uint32_t)vw[4 * grp + 3][d] << 16);
-            va[2] = (uint32_t)vw[16 + 4 * grp + 0][d] | ((uint32_t)vw[16 + 4 * grp + 1][d] << 16);
-            va[3] = (uint32_t)vw[16 + 4 * grp + 2][d] | ((uint32_t)vw[16 + 4 * grp + 3][d] << 16);
-            acc[db] = mfma16x16x32(va, pb, acc[db]);
-        }
+        for (int db = 0; db < 8; ++db) acc[db] = mfma16x16x32(va[db], pb, acc[db]);
     };
 
     const int nblk = (j1 - j0 + kKeyBlock - 1) / kKeyBlock;
-    for (int blk = wave; blk < nblk; blk += kWaves) {
-        Blk r;
-        load_block(blk, r);
-        process_block(blk, r);
+    if (wave < nblk) {
+        issue_block(Kb, kw, wave, false);
+        issue_block(Vb, vw, wave, true);
     }
+    for (int blk = wave; blk < nblk; blk += kWaves) process_block(blk, blk + kWaves < nblk);
 
     // Row sums: each lane group summed different positions of the same head.
     l_run += __shfl_xor(l_run, 16);
@@ -273,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 3) void xattn_split_kernel(const void *__
 
     // Combine the four waves' (m, l, o) in LDS, then write this chunk's partial.
     __syncthreads();
-    float *ow = reinterpret_cast<float *>(&vs[0][0][0]);  // [kWaves][16 heads][128 dims] fp32 = 32 KB
+    float *ow = reinterpret_cast<float *>(&kbuf[0][0]);  // [kWaves][16 heads][128 dims] fp32 = 32 KB
     if (grp == 0) {
         red_m[wave][col] = m_run;
         red_l[wave][col] = l_run;
