@@ -60,8 +60,10 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// Data read once per call (KV cache, weights) uses plain loads too: the
-// non-temporal hint measured ~8% slower on the attention kernel.
+// Register loads in MFMA operand layouts (64 bytes of each of 16 rows per
+// instruction) stay plain: the non-temporal hint measured ~8% slower there.
+// Whole-row streams copied into LDS (the attention kernel's K and V) take
+// it: 6.9-7.0 against 6.0-6.3 TB/s in a read probe of the same block walk.
 
 // 16-byte global -> LDS copy (gfx950 global_load_lds_dwordx4): lane i's 16
 // bytes land at lds_base + 16·i; lds_base must be wave-uniform.  Completion

@@ -18,7 +18,9 @@ constexpr int kReadThreads = 256, kReadInFlight = 8;
 int read_wgs(size_t bytes) { return bytes < ((size_t)256 << 20) ? 1024 : 256; }
 
 // Grid-stride read: each workgroup reads 32 KB contiguous per step (eight 16-byte
-// loads in flight per thread), the grid sweeps memory linearly.
+// loads in flight per thread), the grid sweeps memory linearly.  Non-temporal
+// loads: on MI355X they read a 4 GiB buffer at ~7.0-7.4 TB/s against
+// ~6.2-6.4 TB/s for plain loads (256-4096 workgroups).
 __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4 *__restrict__ p, size_t n,
                                                                    unsigned *__restrict__ sink) {
     u32x4 acc = {0u, 0u, 0u, 0u};
@@ -28,7 +30,7 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4 *
 #pragma unroll
         for (int u = 0; u < kReadInFlight; ++u) {
             const size_t i = base + (size_t)u * kReadThreads;
-            v[u] = i < n ? p[i] : (u32x4){0u, 0u, 0u, 0u};
+            v[u] = i < n ? __builtin_nontemporal_load(p + i) : (u32x4){0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < kReadInFlight; ++u) acc ^= v[u];
