@@ -195,7 +195,7 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float, onl
             res["gmu_decode_B%d" % B] = {"us_per_call": round(1e3 * ms, 2), "gbps": round(gbps, 1),
                                          "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
                                          "frac_of_stream_read": round(gbps / read_gbps, 4)}
-        # Context: two plain streaming reads of the same two weight matrices (the
+        # Context: two streaming reads of the same two weight matrices (the
         # library's read probe, same rotation), i.e. what a perfect kernel pair
         # could approach at this size with two launches.
         def plain_reads(i):
