@@ -81,8 +81,8 @@ __device__ __forceinline__ void store_swiglu(float g, float v, int t, int n, voi
 // X arrives as a bf16 hi + lo pair (two MFMAs per operand pair).  DUAL: the
 // first RT/2 row tiles come from W, the other RT/2 from W_b at the same rows
 // (the SwiGLU gate and up products); partials then hold [slice][T][2N].
-template <int RT, int TB, int U, int EPI, bool XLO, bool DUAL = false>
-__global__ __launch_bounds__(kThreads) void skinny_kernel(const bf16_t *__restrict__ X,
+template <int RT, int TB, int U, int EPI, bool XLO, bool DUAL = false, int MINB = 1>
+__global__ __launch_bounds__(kThreads, MINB) void skinny_kernel(const bf16_t *__restrict__ X,
                                                           const bf16_t *__restrict__ X_lo, int ldx,
                                                           const bf16_t *__restrict__ W,
                                                           const bf16_t *__restrict__ W_b, int T, int N, int K, int R,
@@ -406,10 +406,16 @@ hipError_t launch_gemv(const SkinnyArgs &a, hipStream_t stream) {
 template <int RT, int TB, int EPI, bool XLO, bool DUAL = false>
 hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
     // Chunks in flight per wave: operand registers U·8·(RT + TB·(1 + XLO)) <= ~160.
-    constexpr int U = 20 / (RT + TB * (XLO ? 2 : 1)) < 1 ? 1 : 20 / (RT + TB * (XLO ? 2 : 1));
+    // The dual SwiGLU pass keeps one chunk in flight and two workgroups per
+    // CU instead (at 32 tokens: 122 registers against 185, its 512
+    // workgroups in one round instead of two; 34.9 -> ~30.5 us per 100.7 MB
+    // launch, the whole-model decode step 10.19 -> 10.04 ms).
+    constexpr int U0 = 20 / (RT + TB * (XLO ? 2 : 1)) < 1 ? 1 : 20 / (RT + TB * (XLO ? 2 : 1));
+    constexpr int U = DUAL ? 1 : U0;
+    constexpr int MINB = DUAL ? 2 : 1;
     const dim3 grid((a.N + p.rows_per_wg - 1) / p.rows_per_wg, p.k_splits);
     TimingScope ts(kTimeSkinny, stream);
-    hipLaunchKernelGGL((skinny_kernel<RT, TB, U, EPI, XLO, DUAL>), grid, dim3(kThreads), 0, stream, a.X, a.X_lo, a.ldx,
+    hipLaunchKernelGGL((skinny_kernel<RT, TB, U, EPI, XLO, DUAL, MINB>), grid, dim3(kThreads), 0, stream, a.X, a.X_lo, a.ldx,
                        a.W, a.W_b, a.T, a.N, a.K, p.rows_per_wg, p.k_slice, a.out, a.ldo, a.out_lo, a.aux, a.ldaux, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.k_splits == 1) return e;
