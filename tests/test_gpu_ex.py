@@ -2,13 +2,12 @@
 layer against the fp64 oracle (through the C ABI), plus the invariants that
 tie them to the plain entry points.
 
-Tolerance: the bf16 bar, max |gpu - oracle| / max |oracle| <= 2e-2, except
-for whole multi-layer complete steps at full size, whose residual stream is
-rounded to bf16 at R = 2 points per layer: two implementations that agree to
-fp32 before each rounding can land one bf16 step (2^-8 relative) apart at any
-of them, and those disagreements add up along the stream like a random walk,
-so the bar there is 2·sqrt(R)·2^-8 (R = 32: 4.4e-2); every single layer is
-still held to 2e-2 (teacher-forced).
+Tolerance: the bf16 bar, max |gpu - oracle| / max |oracle| <= 2e-2, for
+every case, the whole 16-layer complete step at full size included (its
+residual stream is rounded to bf16 at 32 points; the oracle's own rounded
+stream sits 1.7e-2 from the unrounded one on that input, and the library is
+held to the same 2e-2 bar as everywhere else); every single layer is also
+checked alone, teacher-forced, at 2e-2.
 """
 import numpy as np
 import pytest
@@ -20,10 +19,6 @@ import workload
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL_BF16 = 2e-2
-
-
-def tol_stream(roundings: int) -> float:
-    return 2.0 * np.sqrt(roundings) * 2.0 ** -8
 
 
 @pytest.fixture(scope="module")
@@ -189,7 +184,7 @@ def test_step_ex_full_size_sampled(sb):
     h0 = x.h.clone()
     sb.crossdecoder_step_ex(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
     torch.cuda.synchronize()
-    report("step_ex full size, 3 sampled sequences", err(f64(x.h[rows]), ref), tol_stream(2 * c["n_layers"]))
+    report("step_ex full size, 3 sampled sequences", err(f64(x.h[rows]), ref), TOL_BF16)
     # Teacher-forced: every layer alone, from the GPU's own input to it.
     h = h0.clone()
     worst = 0.0

@@ -18,6 +18,7 @@ import pytest
 import torch
 
 import oracle
+import torch_model as tm
 import workload
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")))
@@ -163,40 +164,12 @@ def test_ex_without_norms_mlp_or_lengths_is_the_plain_step():
 
 
 def _torch_ex(x, Hq, eps=1e-5):
-    """Layer-by-layer composition from torch fp64 operations, h rounded to
-    bf16 by the (separately pinned) oracle rounding after every residual add."""
-    h = x.h.double()
-    M = x.M.double()
-    B, d_model = h.shape
-    Hkv, L, D = x.K.shape[1], x.K.shape[2], x.K.shape[3]
-    G = Hq // Hkv
-    lens = [L] * B if x.lens is None else [int(v) for v in x.lens]
-
-    def rms(t, g):
-        if g is None:
-            return t
-        return t / torch.sqrt((t * t).mean(-1, keepdim=True) + eps) * g.double()
-
-    for ly in x.layers:
-        t = rms(h, ly["norm1"])
-        if ly["kind"] == "xattn":
-            q = (t @ ly["w_a"].double().T).view(B, Hq, D)
-            o = torch.zeros(B, Hq, D, dtype=torch.float64)
-            for b in range(B):
-                if lens[b] == 0:
-                    continue
-                k = x.K[b, :, :lens[b]].double().repeat_interleave(G, 0)
-                v = x.V[b, :, :lens[b]].double().repeat_interleave(G, 0)
-                o[b] = torch.nn.functional.scaled_dot_product_attention(q[b].unsqueeze(1), k, v).squeeze(1)
-            y = o.view(B, d_model) @ ly["w_b"].double().T
-        else:
-            y = (M * torch.nn.functional.silu(t @ ly["w_a"].double().T)) @ ly["w_b"].double().T
-        h = torch.from_numpy(oracle.round_bf16((h + y).numpy()))
-        if ly.get("w_gate") is not None:
-            t = rms(h, ly["norm2"])
-            u = torch.nn.functional.silu(t @ ly["w_gate"].double().T) * (t @ ly["w_up"].double().T)
-            h = torch.from_numpy(oracle.round_bf16((h + u @ ly["w_down"].double().T).numpy()))
-    return h.numpy()
+    """Layer-by-layer composition from torch fp64 operations (tests/torch_model.py),
+    h rounded to bf16 by the (separately pinned) oracle rounding after every
+    residual add."""
+    L = x.K.shape[2]
+    lens = [L] * x.h.shape[0] if x.lens is None else [int(v) for v in x.lens]
+    return tm.cross_decoder(x.h, x.M, x.K, x.V, lens, x.layers, Hq, eps=eps).numpy()
 
 
 @pytest.mark.parametrize("kinds", [("xattn", "gmu", "xattn", "gmu"), ("gmu", "xattn"), ("xattn", "xattn")])

@@ -31,6 +31,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
+import torch_model as tm
 import workload
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")))
@@ -50,34 +51,8 @@ def _f64(a):
 
 
 def _parallel(xs, w, conv0, s0):
-    """T steps of one sequence in parallel form: xs [T, d_model], conv0
-    [d_inner, K-1], s0 [d_inner, N].  Returns M [T, d_inner], y [T, d_model],
-    final conv window [d_inner, K-1], final state [d_inner, N]."""
-    W = {k: _t64(v) for k, v in w.items()}
-    xs, conv0, s0 = _t64(xs), _t64(conv0), _t64(s0)
-    T = xs.shape[0]
-    d_inner, K = W["conv_w"].shape
-    N = W["A_log"].shape[1]
-    R = W["W_dt"].shape[1]
-    xz = F.linear(xs, W["W_in"])                                       # [T, 2 d_inner]
-    xi, z = xz[:, :d_inner], xz[:, d_inner:]
-    hist = torch.cat([conv0, xi.T], dim=1)                             # [d_inner, K-1+T], oldest first
-    u = F.silu(F.conv1d(hist[None], W["conv_w"][:, None, :], W["conv_b"], groups=d_inner)[0].T)   # [T, d_inner]
-    xd = F.linear(u, W["W_x"])
-    delta, Bv, Cv = xd[:, :R], xd[:, R:R + N], xd[:, R + N:]
-    dt = F.softplus(F.linear(delta, W["W_dt"]) + W["dt_bias"])          # [T, d_inner]
-    A = -torch.exp(W["A_log"])                                          # [d_inner, N]
-    la = dt[:, :, None] * A[None]                                       # log decay per step [T, d_inner, N]
-    cum = torch.cumsum(la, dim=0)                                       # Σ_{k<=t} log a_k
-    # mixing: L[t, j] = exp(cum[t] - cum[j]) for j <= t (the decay from step j+1 to t)
-    Lmix = torch.exp(cum[:, None] - cum[None, :])                       # [T, T, d_inner, N]
-    causal = torch.ones(T, T, dtype=torch.bool).tril()
-    Lmix = torch.where(causal[:, :, None, None], Lmix, torch.zeros(()))
-    inp = dt[:, :, None] * Bv[:, None, :] * u[:, :, None]               # Δ_j B_j u_j  [T, d_inner, N]
-    S = torch.einsum("tjcn,jcn->tcn", Lmix, inp) + torch.exp(cum) * s0[None]
-    M = torch.einsum("tcn,tn->tc", S, Cv) + W["D"][None] * u
-    y = F.linear(M * F.silu(z), W["W_out"])
-    return M.numpy(), y.numpy(), hist[:, T:].numpy(), S[-1].numpy()
+    """T steps of one sequence in parallel form (tests/torch_model.py)."""
+    return tm.mamba_parallel(xs, w, conv0, s0)
 
 
 def _inputs(B, seed, d_model=64, d_inner=128, N=16, R=64, K=4, T=1):

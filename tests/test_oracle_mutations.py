@@ -1,10 +1,13 @@
 """The oracle's pins must catch plausible mistakes.
 
 Each case below plants one mistake (a dropped term, a wrong sign, a swapped
-operand, a wrong index or stride) in a private copy of oracle.c, rebuilds it
-in a temporary directory and runs the pin file that should catch it; the
-case passes only if that pin run fails.  Nothing here touches the product
-library or a GPU.
+operand, a wrong index or stride) in a private copy of oracle.c, or (the
+whole-model compositions: a skipped norm, the memory of the wrong SSM layer,
+the shared cache written by the wrong layer, a ring slot or a visible length
+off by one) in a private copy of the oracle's Python module, rebuilds it in
+a temporary directory and runs the pin file that should catch it; the case
+passes only if that pin run fails.  Nothing here touches the product library
+or a GPU.
 """
 import os
 import shutil
@@ -104,20 +107,62 @@ MUTANTS = [
 ]
 
 
+# Mistakes in the oracle's Python compositions (oracle/__init__.py).
+PY_MUTANTS = [
+    ("prefill_mlp_skips_norm2", "test_oracle_composition.py",
+     'xm = rmsnorm(h.reshape(B * T, dm), ly["norm2"], eps) if ly.get("norm2") is not None \\',
+     'xm = h.reshape(B * T, dm) if ly.get("norm2") is not None \\'),
+    ("decode_mlp_skips_norm2", "test_oracle_composition.py",
+     'xm = rmsnorm(h, ly["norm2"], eps) if ly.get("norm2") is not None else h', "xm = h"),
+    ("prefill_mixer_skips_norm1", "test_oracle_composition.py",
+     'xin = rmsnorm(h.reshape(B * T, dm), ly["norm1"], eps).reshape(B, T, dm) if ly.get("norm1") is not None else h',
+     "xin = h"),
+    ("prefill_memory_from_first_ssm", "test_oracle_composition.py",
+     '            M_mem = M\n            per_layer.append({"conv_state": conv, "ssm_state": ssm})',
+     '            M_mem = M if M_mem is None else M_mem\n            per_layer.append({"conv_state": conv, "ssm_state": ssm})'),
+    ("decode_memory_from_first_ssm", "test_oracle_composition.py",
+     '            M_mem = M\n            per_layer.append({"conv_state": cs, "ssm_state": ss})',
+     '            M_mem = M if M_mem is None else M_mem\n            per_layer.append({"conv_state": cs, "ssm_state": ss})'),
+    ("prefill_cache_from_window_layer", "test_oracle_composition.py",
+     '            if kind == "attn":\n                K, V =', '            if kind == "swa":\n                K, V ='),
+    ("decode_window_layer_writes_shared_cache", "test_oracle_composition.py",
+     'o, kr, vr = selfattn(q, kn, vn, ly["kring"], ly["vring"], pa, window=window, scale=scale)',
+     'o, Kc, Vc = selfattn(q, kn, vn, Kc, Vc, pa, window=0, scale=scale); kr, vr = ly["kring"], ly["vring"]'),
+    ("decode_ring_slot_off_by_one", "test_oracle_composition.py",
+     'selfattn(q, kn, vn, ly["kring"], ly["vring"], pa, window=window',
+     'selfattn(q, kn, vn, ly["kring"], ly["vring"], pa + 1, window=window'),
+    ("decode_cross_lengths_exclude_new_token", "test_oracle_composition.py",
+     "lens = np.minimum(np.maximum(pa.astype(np.int64) + 1, 0), L)",
+     "lens = np.minimum(np.maximum(pa.astype(np.int64), 0), L)"),
+    ("prefill_window_ignored", "test_oracle_composition.py",
+     'o = attn_prefill(q, k, v, window if kind == "swa" else 0, scale)', "o = attn_prefill(q, k, v, 0, scale)"),
+    ("decode_ssm_residual_dropped", "test_oracle_composition.py",
+     '            h = rnd(h + y)\n            M_mem = M\n            per_layer.append({"conv_state": cs',
+     '            h = rnd(y)\n            M_mem = M\n            per_layer.append({"conv_state": cs'),
+    ("prefill_cross_decoder_on_first_token", "test_oracle_composition.py",
+     "h_last = np.ascontiguousarray(h[:, T - 1])", "h_last = np.ascontiguousarray(h[:, 0])"),
+    ("mamba_prefill_state_not_carried", "test_oracle_mamba.py",
+     "M, y, conv, ssm = mamba_step(np.ascontiguousarray(xa[:, t]), w, conv, ssm)",
+     "M, y, _, _ = mamba_step(np.ascontiguousarray(xa[:, t]), w, conv, ssm)"),
+]
+
+CASES = [("oracle.c",) + m for m in MUTANTS] + [("__init__.py",) + m for m in PY_MUTANTS]
+
+
 @pytest.fixture(scope="module")
-def source():
-    with open(os.path.join(ROOT, "oracle", "oracle.c")) as f:
-        return f.read()
+def sources():
+    return {f: open(os.path.join(ROOT, "oracle", f)).read() for f in ("oracle.c", "__init__.py")}
 
 
-@pytest.mark.parametrize("name,pins,orig,planted", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_planted_mistake(tmp_path, source, name, pins, orig, planted):
-    assert source.count(orig) >= 1, "mutation site for %s not found in oracle.c" % name
+@pytest.mark.parametrize("target,name,pins,orig,planted", CASES, ids=[c[1] for c in CASES])
+def test_pins_catch_planted_mistake(tmp_path, sources, target, name, pins, orig, planted):
+    source = sources[target]
+    assert source.count(orig) >= 1, "mutation site for %s not found in %s" % (name, target)
     for d in ("oracle", "workload", "tests"):
         shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
                         ignore=shutil.ignore_patterns("*.so", "__pycache__", "*.tmp*"))
     shutil.copy(os.path.join(ROOT, "pytest.ini"), tmp_path)
-    (tmp_path / "oracle" / "oracle.c").write_text(source.replace(orig, planted, 1))
+    (tmp_path / "oracle" / target).write_text(source.replace(orig, planted, 1))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-m", "not gpu", "-p", "no:cacheprovider",
                         os.path.join("tests", pins)], cwd=tmp_path, capture_output=True, text=True, timeout=600)
     assert r.returncode == 1, "planted mistake %r survived %s:\n%s" % (name, pins, r.stdout[-2000:])
