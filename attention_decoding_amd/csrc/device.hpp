@@ -60,6 +60,11 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// Non-temporal 16-byte load (streamed weights: read once per step).
+__device__ __forceinline__ u32x4 ld16_nt(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
 // Register loads in MFMA operand layouts (64 bytes of each of 16 rows per
 // instruction) stay plain: the non-temporal hint measured ~8% slower there.
 // Whole-row streams copied into LDS (the attention kernel's K and V) take

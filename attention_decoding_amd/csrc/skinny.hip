@@ -197,6 +197,124 @@ __global__ __launch_bounds__(kThreads, MINB) void skinny_kernel(const bf16_t *__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Weight streaming through LDS (decode products of 2-32 tokens).  Every
+// workgroup (16 waves, one per CU) copies its whole block of weight rows
+// [n0, n0 + R) x K-slice into LDS with direct global -> LDS copies of
+// contiguous row segments (non-temporal policy), all issued at once; the
+// token operand goes to registers underneath that latency.  Then each wave
+// multiplies its own K part (16x16x32 MFMA: A = weight rows read from LDS,
+// B = tokens) and the 16 partial tiles are summed through LDS in wave
+// order (deterministic).  Measured on the memory side (37.7 MB, 256
+// workgroups): 6.8-6.9 us, level with a plain streaming read of the same
+// bytes, against 11-12 us for register loads in the MFMA operand layout
+// (64 bytes of each of 16 rows per instruction) and 7.0-7.9 us with 8 waves
+// or without the non-temporal policy.
+constexpr int kStreamWaves = 16;
+constexpr int kStreamThreads = 64 * kStreamWaves;
+constexpr int kStreamCopyPolicy = 2;               // non-temporal
+constexpr size_t kStreamLdsMax = 160 * 1024;
+
+// Wave w's LDS region holds its R x KW block as R rows of CPR 16-byte
+// chunks; global chunk g of row r sits in slot (g & ~(SW-1)) | ((g ^ r) &
+// (SW-1)), SW the largest of 16, 8, 4 dividing CPR, so that the 16 rows of an
+// MFMA operand read land in distinct banks (SW 16 and 8: conflict-free).
+__host__ __device__ constexpr int stream_swizzle_width(int cpr) { return cpr % 16 == 0 ? 16 : (cpr % 8 == 0 ? 8 : 4); }
+
+// KS: 32-wide k-steps per wave (K slice = 512·KS).  Rows past R or N read a
+// valid row and are never stored; token slots past T read token T-1.
+template <int RT, int TB, int KS, int EPI, bool XLO>
+__global__ __launch_bounds__(kStreamThreads) void stream_kernel(const bf16_t *__restrict__ X,
+                                                                const bf16_t *__restrict__ X_lo, int ldx,
+                                                                const bf16_t *__restrict__ W, int T, int N, int K,
+                                                                int R, void *out, int ldo, bf16_t *out_lo,
+                                                                const bf16_t *__restrict__ aux, int ldaux,
+                                                                float *__restrict__ partials) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int KW = KS * 32, CPR = KW / 8, SW = stream_swizzle_width(CPR), TT = 16 * TB;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+    const int n0 = blockIdx.x * R;
+    // Wave w takes K part (w + blockIdx.x) % 16: neighbouring workgroups (on
+    // the same XCD, which all read the same token rows from its L2) read
+    // different lines of them at any moment.
+    const int kpart = (wave + blockIdx.x) & (kStreamWaves - 1);
+    const int kw0 = blockIdx.y * (KW * kStreamWaves) + kpart * KW;
+    const int units = R * CPR, instr = (units + 63) / 64;
+    unsigned char *wl = smem + (size_t)wave * instr * 1024;
+
+    u32x4 xf[KS][TB], xl[XLO ? KS : 1][TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const size_t xo = (size_t)min(16 * tb + col, T - 1) * ldx + kw0 + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            xf[ks][tb] = ld16(X + xo + 32 * ks);
+            if (XLO) xl[XLO ? ks : 0][tb] = ld16(X_lo + xo + 32 * ks);
+        }
+    }
+    for (int i = 0; i < instr; ++i) {
+        const int u = min(i * 64 + lane, units - 1), r = u / CPR, c = u % CPR;
+        const int g = (c & ~(SW - 1)) | ((c ^ r) & (SW - 1));
+        const int row = min(n0 + r, N - 1);
+        __builtin_amdgcn_global_load_lds(W + (size_t)row * K + kw0 + 8 * g,
+                                         (__attribute__((address_space(3))) void *)(wl + (size_t)i * 1024), 16, 0,
+                                         kStreamCopyPolicy);
+    }
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's copies and token loads have landed
+    __builtin_amdgcn_wave_barrier();
+
+    f32x4 acc[RT][TB];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int r = min(16 * rt + col, R - 1), g = 4 * ks + grp;
+            const int c = (g & ~(SW - 1)) | ((g ^ r) & (SW - 1));
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(wl + ((size_t)r * CPR + c) * 16);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                acc[rt][tb] = mfma16x16x32(a, xf[ks][tb], acc[rt][tb]);
+                if (XLO) acc[rt][tb] = mfma16x16x32(a, xl[XLO ? ks : 0][tb], acc[rt][tb]);
+            }
+        }
+
+    // acc[rt][tb][q] = partial of row 16·rt + 4·grp + q, token 16·tb + col.
+    __syncthreads();  // every wave is done with its weights: the region becomes the reduction buffer
+    float *red = reinterpret_cast<float *>(smem);
+    constexpr int RS = TT + 4;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                red[(wave * 16 * RT + 16 * rt + 4 * grp + q) * RS + 16 * tb + col] = acc[rt][tb][q];
+    __syncthreads();
+    const int total = R * T;
+    for (int idx = threadIdx.x; idx < total; idx += kStreamThreads) {
+        const int t = idx / R, rl = idx % R, n = n0 + rl;
+        if (n >= N) continue;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kStreamWaves; ++w) v += red[(w * 16 * RT + rl) * RS + t];
+        if (gridDim.y == 1)
+            apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, ldaux);
+        else
+            partials[((size_t)blockIdx.y * T + t) * N + n] = v;
+    }
+}
+
+size_t stream_lds_bytes(int R, int KS, int RT, int TB) {
+    const size_t units = (size_t)R * KS * 4, instr = (units + 63) / 64;
+    const size_t copy = (size_t)kStreamWaves * instr * 1024;
+    const size_t red = (size_t)kStreamWaves * 16 * RT * (16 * TB + 4) * sizeof(float);
+    return copy > red ? copy : red;
+}
+
 __global__ __launch_bounds__(256) void swiglu_finish_kernel(const float *__restrict__ partials, int splits, int T,
                                                             int N, void *out, int ldo, bf16_t *out_lo) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -287,88 +405,72 @@ __global__ __launch_bounds__(256) void resid_norm_finish_kernel(const float *__r
 }
 
 // One-token products (batch-1 decode): a plain VALU dot product, lanes along
-// K.  Each wave reads whole weight rows, 1 KB contiguous per load
-// instruction (lane l holds elements 512·s + 8·l .. +7 of segment s), keeps
-// the token row in registers, and reduces each row across the wave in a fixed
-// order.  No token padding, no LDS.  Measured against the MFMA product at one
-// token (3072/6144-wide, random data, weights from HBM): 8.3 vs 9.2 us
-// (6144 x 3072) and 8.3 vs 10.4 us (3072 x 6144); at 4 tokens it is slower
-// (register pressure), so it serves T == 1 only.
-template <int KS, int RPW, int EPI, bool XLO>
+// K.  Each wave reads one whole weight row, 1 KB contiguous per load
+// instruction (lane l holds elements 512·s + 8·l .. +7 of segment s), with
+// the non-temporal policy; the token row (and the epilogue's own input) is
+// read by every wave from L2.  The code is straight-line: no loop and no
+// branch sits between the loads, so all of a wave's loads are in flight
+// together (a guarded load, or a loop over rows, made the compiler wait for
+// the token row before issuing the weight loads, and for each row's loads
+// before the next row's: 8.1-8.7 against 7.4 us for 37.7 MB).  Rows past N
+// read row N-1 and store nothing.  Each row is reduced across the wave in a
+// fixed order.  No token padding, no LDS.
+template <int KS, int EPI, bool XLO>
 __global__ __launch_bounds__(256) void gemv_kernel(const bf16_t *__restrict__ X, const bf16_t *__restrict__ X_lo,
                                                    const bf16_t *__restrict__ W, int N, void *out, bf16_t *out_lo,
                                                    const bf16_t *__restrict__ aux) {
     constexpr int K = KS * 512;
     const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6), nw = gridDim.x * 4;
-    u32x4 xr[KS], xl[XLO ? KS : 1];
+    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nr = min(n, N - 1);
+    u32x4 xr[KS], xl[XLO ? KS : 1], wr[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         xr[s] = ld16(X + s * 512 + 8 * lane);
         if (XLO) xl[XLO ? s : 0] = ld16(X_lo + s * 512 + 8 * lane);
     }
-    for (int n0 = gw * RPW; n0 < N; n0 += nw * RPW) {
-        u32x4 wr[RPW][KS];
 #pragma unroll
-        for (int r = 0; r < RPW; ++r)
+    for (int s = 0; s < KS; ++s) wr[s] = ld16_nt(W + (size_t)nr * K + s * 512 + 8 * lane);
+    // The epilogue's own input (M for the gate, h for the residual add), fetched
+    // with the weights so that its latency overlaps theirs.
+    float pre = 0.f;
+    if (EPI == EPI_GATE) pre = bf16_to_f32(aux[nr]);
+    if (EPI == EPI_RESID) pre = bf16_to_f32(reinterpret_cast<const bf16_t *>(out)[nr]);
+    float acc = 0.f;
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                wr[r][s] = n0 + r < N ? ld16(W + (size_t)(n0 + r) * K + s * 512 + 8 * lane) : (u32x4){0u, 0u, 0u, 0u};
-        // The epilogue's own input (M for the gate, h for the residual add) is
-        // fetched together with the weights so its latency overlaps theirs.
-        float pre[RPW];
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            pre[r] = 0.f;
-            if ((EPI == EPI_GATE || EPI == EPI_RESID) && lane == 0 && n0 + r < N)
-                pre[r] = bf16_to_f32(EPI == EPI_GATE ? aux[n0 + r] : reinterpret_cast<const bf16_t *>(out)[n0 + r]);
+        for (int e = 0; e < 4; ++e) {
+            acc += lo_bf16(wr[s][e]) * lo_bf16(xr[s][e]) + hi_bf16(wr[s][e]) * hi_bf16(xr[s][e]);
+            if (XLO)
+                acc += lo_bf16(wr[s][e]) * lo_bf16(xl[XLO ? s : 0][e]) + hi_bf16(wr[s][e]) * hi_bf16(xl[XLO ? s : 0][e]);
         }
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc += lo_bf16(wr[r][s][e]) * lo_bf16(xr[s][e]) + hi_bf16(wr[r][s][e]) * hi_bf16(xr[s][e]);
-                    if (XLO)
-                        acc += lo_bf16(wr[r][s][e]) * lo_bf16(xl[XLO ? s : 0][e]) +
-                               hi_bf16(wr[r][s][e]) * hi_bf16(xl[XLO ? s : 0][e]);
-                }
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-            if (lane != 0 || n0 + r >= N) continue;
-            const int n = n0 + r;
-            if (EPI == EPI_F32) {
-                reinterpret_cast<float *>(out)[n] = acc;
-            } else if (EPI == EPI_BF16) {
-                reinterpret_cast<bf16_t *>(out)[n] = f32_to_bf16(acc);
-            } else if (EPI == EPI_GATE) {
-                const float g = pre[r] * (acc / (1.f + expf(-acc)));
-                const bf16_t hi = f32_to_bf16(g);
-                reinterpret_cast<bf16_t *>(out)[n] = hi;
-                if (out_lo) out_lo[n] = f32_to_bf16(g - bf16_to_f32(hi));
-            } else {
-                reinterpret_cast<bf16_t *>(out)[n] = f32_to_bf16(pre[r] + acc);
-            }
-        }
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane != 0 || n >= N) return;
+    if (EPI == EPI_F32) {
+        reinterpret_cast<float *>(out)[n] = acc;
+    } else if (EPI == EPI_BF16) {
+        reinterpret_cast<bf16_t *>(out)[n] = f32_to_bf16(acc);
+    } else if (EPI == EPI_GATE) {
+        const float g = pre * (acc / (1.f + expf(-acc)));
+        const bf16_t hi = f32_to_bf16(g);
+        reinterpret_cast<bf16_t *>(out)[n] = hi;
+        if (out_lo) out_lo[n] = f32_to_bf16(g - bf16_to_f32(hi));
+    } else {
+        reinterpret_cast<bf16_t *>(out)[n] = f32_to_bf16(pre + acc);
     }
 }
 
 template <int KS, int EPI, bool XLO>
 hipError_t launch_gemv3(const SkinnyArgs &a, hipStream_t stream) {
-    constexpr int RPW = KS >= 12 ? 1 : 2;  // rows in flight per wave (measured)
-    // Up to 3072 waves (3 per SIMD): one wave per RPW rows, so that every
-    // wave issues all its loads at once and none runs a second, dependent
-    // round (the 6144 x 3072 gate product: 11.3 -> 10.7 us).  Larger
-    // products and the hi + lo operand form keep 512 workgroups, which
-    // measured faster for them (12288 x 3072: 15.6 vs 16.2 us; 3072 x 6144
-    // with a hi + lo token: 11.6 vs 13.0 us).
-    const int waves = (a.N + RPW - 1) / RPW;
-    const int wgs = (!XLO && waves <= 3072) ? (waves + 3) / 4 : 512;
+    // One wave per weight row, four per workgroup (measured against 2 and 4
+    // rows per wave and 8 or 16 waves per workgroup on 6144 x 3072 and
+    // 3072 x 6144: the single-row wave is fastest or level).
+    const int wgs = (a.N + 3) / 4;
     TimingScope ts(kTimeSkinny, stream);
-    hipLaunchKernelGGL((gemv_kernel<KS, RPW, EPI, XLO>), dim3(wgs), dim3(256), 0, stream, a.X, a.X_lo, a.W, a.N,
-                       a.out, a.out_lo, a.aux);
+    hipLaunchKernelGGL((gemv_kernel<KS, EPI, XLO>), dim3(wgs), dim3(256), 0, stream, a.X, a.X_lo, a.W, a.N, a.out,
+                       a.out_lo, a.aux);
     return hipGetLastError();
 }
 
@@ -403,6 +505,105 @@ hipError_t launch_gemv(const SkinnyArgs &a, hipStream_t stream) {
     }
 }
 
+// The finishing pass of a K-split product (fp32 partials [slice][T][N]).
+template <int EPI>
+hipError_t launch_finish(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    if (EPI == EPI_RESID && skinny_fuses_norm(a, p)) {
+        hipLaunchKernelGGL(resid_norm_finish_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, partials, p.k_splits,
+                           a.T, a.N, static_cast<bf16_t *>(a.out), a.ldo, a.next_norm, a.eps, a.next_x,
+                           a.next_x_lo);
+        return hipGetLastError();
+    }
+    const size_t total = (size_t)a.T * a.N;
+    hipLaunchKernelGGL((skinny_finish_kernel<EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       partials, p.k_splits, a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.ldaux);
+    return hipGetLastError();
+}
+
+template <int RT, int TB, int KS, int EPI, bool XLO>
+hipError_t launch_stream4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    const size_t lds = stream_lds_bytes(p.rows_per_wg, KS, RT, TB);
+    static const hipError_t attr = hipFuncSetAttribute((const void *)stream_kernel<RT, TB, KS, EPI, XLO>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax);
+    if (attr != hipSuccess) return attr;
+    const dim3 grid((a.N + p.rows_per_wg - 1) / p.rows_per_wg, p.k_splits);
+    {
+        TimingScope ts(kTimeSkinny, stream);
+        hipLaunchKernelGGL((stream_kernel<RT, TB, KS, EPI, XLO>), grid, dim3(kStreamThreads), lds, stream, a.X, a.X_lo,
+                           a.ldx, a.W, a.T, a.N, a.K, p.rows_per_wg, a.out, a.ldo, a.out_lo, a.aux, a.ldaux, partials);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.k_splits == 1) return e;
+    return launch_finish<EPI>(a, p, partials, stream);
+}
+
+template <int RT, int TB, int KS, int EPI>
+hipError_t launch_stream3(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    if constexpr (KS * TB * 2 <= 24) {  // the hi + lo token operand doubles the token registers
+        if (a.X_lo) return launch_stream4<RT, TB, KS, EPI, true>(a, p, partials, stream);
+    }
+    if constexpr (KS * TB <= 24) {
+        if (!a.X_lo) return launch_stream4<RT, TB, KS, EPI, false>(a, p, partials, stream);
+    }
+    return hipErrorInvalidValue;  // never dispatched (stream_fit)
+}
+
+template <int RT, int TB, int KS>
+hipError_t launch_stream2(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    switch (a.epi) {
+        case EPI_F32: return launch_stream3<RT, TB, KS, EPI_F32>(a, p, partials, stream);
+        case EPI_BF16: return launch_stream3<RT, TB, KS, EPI_BF16>(a, p, partials, stream);
+        case EPI_GATE: return launch_stream3<RT, TB, KS, EPI_GATE>(a, p, partials, stream);
+        default: return launch_stream3<RT, TB, KS, EPI_RESID>(a, p, partials, stream);
+    }
+}
+
+// Shapes the LDS-streaming product takes: 2-32 tokens, no SwiGLU pairing, a K
+// slice of 1536, 3072 or 6144 elements, at most 32 rows per workgroup, the
+// token operand within 24 registers of 16 bytes per lane, the block within
+// the LDS of one CU.
+int stream_tb(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
+
+// The K steps per wave for which the LDS-streaming product takes a shape
+// (0: it does not): a K slice of 1536, 3072 or 6144 elements, at most 32
+// rows per workgroup, the token operand within 24 registers of 16 bytes per
+// lane, the block within the LDS of one CU.
+int stream_fit(int T, int R, int k_slice, bool xlo) {
+    if (T < 2 || T > kSkinnyMaxTokens || R > 32 || k_slice % (32 * kStreamWaves) != 0) return 0;
+    const int KS = k_slice / (32 * kStreamWaves);
+    if (KS != 3 && KS != 6 && KS != 12) return 0;
+    const int TB = stream_tb(T), RT = R <= 16 ? 1 : 2;
+    if (KS * TB * (xlo ? 2 : 1) > 24) return 0;
+    if (stream_lds_bytes(R, KS, RT, TB) > kStreamLdsMax) return 0;
+    return KS;
+}
+
+int stream_ks(const SkinnyArgs &a, const SkinnyPlan &p) {
+    if (a.epi == EPI_SWIGLU || a.ldx % 8 != 0 || a.K % 8 != 0) return 0;
+    return stream_fit(a.T, p.rows_per_wg, p.k_slice, a.X_lo != nullptr);
+}
+
+template <int RT, int TB>
+hipError_t launch_stream1(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream, int KS) {
+    if (KS == 3) return launch_stream2<RT, TB, 3>(a, p, partials, stream);
+    if (KS == 6) return launch_stream2<RT, TB, 6>(a, p, partials, stream);
+    return launch_stream2<RT, TB, 12>(a, p, partials, stream);
+}
+
+template <int RT>
+hipError_t launch_stream0(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream, int KS) {
+    switch (stream_tb(a.T)) {
+        case 1: return launch_stream1<RT, 1>(a, p, partials, stream, KS);
+        case 2: return launch_stream1<RT, 2>(a, p, partials, stream, KS);
+        default: return launch_stream1<RT, 4>(a, p, partials, stream, KS);
+    }
+}
+
+hipError_t launch_stream(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream, int KS) {
+    return p.rows_per_wg > 16 ? launch_stream0<2>(a, p, partials, stream, KS)
+                              : launch_stream0<1>(a, p, partials, stream, KS);
+}
+
 template <int RT, int TB, int EPI, bool XLO, bool DUAL = false>
 hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
     // Chunks in flight per wave: operand registers U·8·(RT + TB·(1 + XLO)) <= ~160.
@@ -425,16 +626,7 @@ hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hi
                            p.k_splits, a.T, a.N, a.out, a.ldo, a.out_lo);
         return hipGetLastError();
     }
-    if (EPI == EPI_RESID && skinny_fuses_norm(a, p)) {
-        hipLaunchKernelGGL(resid_norm_finish_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, partials, p.k_splits,
-                           a.T, a.N, static_cast<bf16_t *>(a.out), a.ldo, a.next_norm, a.eps, a.next_x,
-                           a.next_x_lo);
-        return hipGetLastError();
-    }
-    const size_t total = (size_t)a.T * a.N;
-    hipLaunchKernelGGL((skinny_finish_kernel<EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       partials, p.k_splits, a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.ldaux);
-    return hipGetLastError();
+    return launch_finish<EPI>(a, p, partials, stream);
 }
 
 template <int RT, int TB, int EPI>
@@ -471,6 +663,25 @@ hipError_t launch1(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hi
 }  // namespace
 
 SkinnyPlan skinny_plan(int T, int N, int K, bool xlo) {
+    // The LDS-streaming product (2-64 tokens) first: the smallest K split
+    // (1, 2, 4) at which it takes the shape, about 256 workgroups.
+    static const bool no_stream = [] {
+        const char *e = getenv("SAMBAY_NO_STREAM");
+        return e && *e && *e != '0';
+    }();
+    if (T >= 2 && !no_stream) {
+        for (int ks = 1; ks <= 4; ks *= 2) {
+            if (K % ks != 0) break;
+            const int R = (int)(((int64_t)N * ks + kTargetWGs - 1) / kTargetWGs);
+            if (stream_fit(T, R, K / ks, xlo)) {
+                SkinnyPlan p;
+                p.rows_per_wg = R;
+                p.k_splits = ks;
+                p.k_slice = K / ks;
+                return p;
+            }
+        }
+    }
     // Every workgroup reads the K slice of the token operand from L2: T·K·2
     // bytes without a K split (twice that for a hi + lo pair).  Measured on
     // MI355X (N, K in {3072, 6144}, 1-64 tokens, all epilogues): below ~190
@@ -504,9 +715,16 @@ SkinnyPlan skinny_plan(int T, int N, int K, bool xlo) {
 }
 
 size_t skinny_partial_bytes_max(int T, int N, int K) {
-    const size_t a = skinny_partial_bytes(T, N, skinny_plan(T, N, K, false));
-    const size_t b = skinny_partial_bytes(T, N, skinny_plan(T, N, K, true));
-    return a > b ? a : b;
+    // Over both operand kinds and every token group up to T (the products of a
+    // batch run in groups of at most T tokens, the last one smaller, and the
+    // plan's K split is chosen per group).
+    size_t m = 0;
+    for (int t = 1; t <= T; ++t)
+        for (int xlo = 0; xlo < 2; ++xlo) {
+            const size_t b = skinny_partial_bytes(t, N, skinny_plan(t, N, K, xlo != 0));
+            if (b > m) m = b;
+        }
+    return m;
 }
 
 SkinnyPlan skinny_plan_dual(int T, int N, int K) {
@@ -544,6 +762,7 @@ size_t skinny_partial_bytes(int T, int N, const SkinnyPlan &p) {
 hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *partials, hipStream_t stream) {
     const int R = plan.rows_per_wg;
     if (gemv_eligible(a) && plan.k_splits == 1) return launch_gemv(a, stream);
+    if (const int ks = stream_ks(a, plan)) return launch_stream(a, plan, partials, stream, ks);
     if (a.epi == EPI_SWIGLU) {  // dual: row tiles in pairs, R <= 32 (skinny_plan_dual)
         if (!a.W_b || R > 32) return hipErrorInvalidValue;
         return R <= 16 ? launch1<2>(a, plan, partials, stream) : launch1<4>(a, plan, partials, stream);
