@@ -154,6 +154,21 @@ def version() -> str:
     return lib.sb_version().decode()
 
 
+def built_source_hash() -> str:
+    """The source hash the loaded library was built from (from its version string)."""
+    return version().rsplit(" ", 1)[-1]
+
+
+def current_source_hash() -> str:
+    """The hash of the kernel and header sources as they are on disk now."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("sambay_build", os.path.join(os.path.dirname(__file__), "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.source_hash()
+
+
 def timing_enable(mask: int) -> None:
     """Bracket later launches of the kernel kinds in `mask` (SB_TIME_* bits)
     with HIP events on their own stream; 0 turns recording off."""

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -26,6 +27,21 @@ ARCH = os.environ.get("SAMBAY_OFFLOAD_ARCH", "gfx950")
 # Packed-fp32 VALU forms are disabled for all device code.
 COMMON_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I" + INCLUDE, "-I" + CSRC]
+
+
+def source_hash() -> str:
+    """First 16 hex digits of the SHA-256 of every kernel and header source
+    (csrc/*.hip, csrc/*.hpp, include/*.h), names included; built into the
+    library's version string so that a loaded binary can be tied to the
+    sources it came from."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")) +
+                   glob.glob(os.path.join(INCLUDE, "*.h")))
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def hipcc() -> str:
@@ -48,6 +64,7 @@ def build(extra_flags=(), jobs: int | None = None, verbose: bool = False) -> str
     """Compile all csrc/*.hip for gfx950 and link libsambay.so.  Always rebuilds."""
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    extra_flags = list(extra_flags) + ['-DSAMBAY_SOURCE_HASH="%s"' % source_hash()]
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra_flags), srcs))

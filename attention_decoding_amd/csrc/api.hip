@@ -146,7 +146,10 @@ size_t xattn_ws(int64_t B, int64_t Hq, int64_t Hkv, int64_t L) {
 
 extern "C" const char *sb_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" const char *sb_version(void) { return "sambay-mi355x 0.1 (gfx950)"; }
+#ifndef SAMBAY_SOURCE_HASH
+#define SAMBAY_SOURCE_HASH "unknown"
+#endif
+extern "C" const char *sb_version(void) { return "sambay-mi355x 0.2 (gfx950) sources " SAMBAY_SOURCE_HASH; }
 
 extern "C" size_t gmu_workspace_bytes(int64_t rows, int64_t d_model, int64_t d_inner, sb_dtype dt) {
     return gmu_ws(rows, d_model, d_inner, dt);

@@ -21,8 +21,19 @@ Also reported on the same JSON line:
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
                 (a few whole sequences through all 16 layers), on the host.
   kernels       per-kernel-kind times and rates from a short extra pass.
+  graph_replay  the same step replayed from a captured HIP graph (host launch
+                cost removed), checked bitwise against the eager step.
+  configs       the other workloads in compact form: the tiny fp32 GMU against
+                the oracle, GMU prefill (TFLOP/s), GMU decode at 1/8/32/64
+                tokens and the 16-sequence cross-attention decode (GB/s).
+  library       the version string of the loaded library, with the hash of
+                the sources it was built from and of the sources present.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+The timed steps carry no instrumentation; the split kernel's launch time for
+`roofline` comes from the same number of steps run again with the library's
+HIP-event brackets on that kernel.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs] [--all]
 """
 from __future__ import annotations
 
@@ -38,6 +49,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "cross-decoder decode tokens/s @34K ctx; GMU & XA achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "xattn_split_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_decoding_amd", "csrc", f) for f in ("xattn.hip", "device.hpp")]
 
@@ -431,12 +443,67 @@ def other_workloads(sb, workload, dev, read_gbps: float, mfma_tflops: float, onl
     return res
 
 
+def configs_block(sb, workload, dev, oracle_ok: bool) -> dict:
+    """The five workloads of this path, compact: the tiny fp32 GMU against the
+    oracle (correctness only), GMU prefill (TFLOP/s and fraction of the bf16
+    MFMA peak), GMU decode per batch size (8 rotating weight sets, so every
+    call reads its weights from HBM; us per call and fraction of 8 TB/s),
+    and the cross-attention decode alone (us and fraction of 8 TB/s).  The
+    16-layer step is the headline value itself."""
+    import torch
+
+    out = {}
+    if oracle_ok:
+        import numpy as np
+
+        import oracle
+
+        t = workload.tiny_gmu(seed=0)
+        Y = sb.gmu_forward(t.M.to(dev), t.X.to(dev), t.W1.to(dev), t.W2.to(dev))
+        torch.cuda.synchronize()
+        ref = oracle.gmu(t.M, t.X, t.W1, t.W2)
+        err = float(np.max(np.abs(Y.double().cpu().numpy() - ref)) / np.max(np.abs(ref)))
+        out["tiny_gmu_fp32_T64_64x128"] = {"rel_err_vs_oracle": err, "tolerance": 1e-5, "pass": err <= 1e-5}
+    c = workload.GMU_PREFILL
+    rows = c["batch"] * c["seq"]
+    g = workload.gmu_inputs(rows, c["d_model"], c["d_inner"], seed=1, device=dev)
+    Y = torch.empty(rows, c["d_model"], dtype=torch.bfloat16, device=dev)
+    ms = time_calls(lambda i: sb.gmu_forward(g.M, g.X, g.W1, g.W2, out=Y), 20, warmup=20)
+    tf = 4.0 * rows * c["d_model"] * c["d_inner"] / ms / 1e9
+    out["gmu_prefill_B4_T2048_2560x5120"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                                              "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    del g, Y
+    c = workload.GMU_DECODE
+    sets = [workload.gmu_inputs(1, c["d_model"], c["d_inner"], seed=2, device=dev, weight_set=k) for k in range(8)]
+    for B in c["batches"]:
+        gi = workload.gmu_inputs(B, c["d_model"], c["d_inner"], seed=3 + B, device=dev)
+        Y = torch.empty(B, c["d_model"], dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda i: sb.gmu_forward(gi.M, gi.X, sets[i % 8].W1, sets[i % 8].W2, out=Y), 64)
+        nbytes = 2 * c["d_model"] * c["d_inner"] * 2 + B * (2 * c["d_model"] + c["d_inner"]) * 2
+        out["gmu_decode_B%d_3072x6144" % B] = {"us": round(1e3 * ms, 2), "gbps": round(nbytes / ms / 1e6, 1),
+                                               "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        del gi, Y
+    del sets
+    torch.cuda.empty_cache()
+    c = workload.XATTN_DECODE
+    x = workload.xattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["L"], seed=4, device=dev)
+    o = torch.empty(c["B"], c["Hq"], c["D"], dtype=torch.bfloat16, device=dev)
+    ms = time_calls(lambda i: sb.xattn_decode(x.q, x.K, x.V, out=o), 20)
+    nbytes = c["B"] * c["Hkv"] * c["L"] * c["D"] * 4 + 2 * c["B"] * c["Hq"] * c["D"] * 2
+    out["xattn_decode_B16_L34816_24q8kv"] = {"us": round(1e3 * ms, 1), "gbps": round(nbytes / ms / 1e6, 1),
+                                             "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del x, o
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the compact per-workload block")
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle CPU sample")
     ap.add_argument("--all", action="store_true",
                     help="also time the other workloads (GMU prefill, GMU decode per batch, attention alone)")
@@ -487,7 +554,7 @@ def main():
     torch.cuda.synchronize()
     log("bench: warmup done, timing %d steps" % args.steps)
 
-    sb.timing_enable(sb.SB_TIME_XATTN_SPLIT)
+    # The timed steps: no per-kernel instrumentation.
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -497,8 +564,6 @@ def main():
         evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sb.timing_enable(0)
-    n_split, ms_split = sb.timing_collect(sb.SB_TIME_XATTN_SPLIT)
     ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
     per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
 
@@ -506,10 +571,61 @@ def main():
         return per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
     ms_step = max(ms_step, 1e3 * wall / args.steps)
     tokens_per_s = c["B"] / (ms_step / 1e3)
+
+    # The same number of steps again with the split kernel's launches bracketed
+    # by HIP events that the library records on the launch's own stream: its
+    # mean launch duration, for the roofline entry.
+    sb.timing_enable(sb.SB_TIME_XATTN_SPLIT)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        run_step()
+    e1.record()
+    torch.cuda.synchronize()
+    sb.timing_enable(0)
+    ms_step_instr = e0.elapsed_time(e1) / args.steps
+    n_split, ms_split = sb.timing_collect(sb.SB_TIME_XATTN_SPLIT)
     split_ms = ms_split / max(n_split, 1)
     achieved = nbytes["kv_per_layer"] / (split_ms / 1e3) / 1e9
     log("bench: %.3f ms/step, %.0f tokens/s; split kernel %.1f us/launch over %d launches" %
         (ms_step, tokens_per_s, 1e3 * split_ms, n_split))
+
+    # The step replayed from a HIP graph (the input refresh and every launch of
+    # the step captured once): what the host's launch cost is worth.
+    h_eager = None
+    graph = None
+    try:
+        run_step()
+        torch.cuda.synchronize()
+        h_eager = x.h.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            run_step()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                run_step()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(x.h, h_eager))
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_g = e0.elapsed_time(e1) / args.steps
+        graph = {"ms_per_step": round(ms_g, 4), "tokens_per_s": round(c["B"] / (ms_g / 1e3), 1),
+                 "eager_over_graph": round(ms_step / ms_g, 4), "bitwise_equal_to_eager": same}
+        del g
+        log("bench: graph replay %.3f ms/step (eager %.3f)" % (ms_g, ms_step))
+    except Exception as exc:  # a failed capture is reported, not fatal
+        graph = {"error": str(exc)[:200]}
 
     # Per-kernel breakdown on a few extra steps (not part of the timed value).
     kinds = {"xattn_split": sb.SB_TIME_XATTN_SPLIT, "xattn_merge": sb.SB_TIME_XATTN_MERGE,
@@ -536,6 +652,15 @@ def main():
     read_gbps = sb.probe_stream_read_gbps(x.K)
     mfma_tf = sb.probe_mfma_tflops(dev, iters=10000)
     log("bench: probes: streaming read %.0f GB/s, bf16 MFMA loop %.0f TFLOP/s" % (read_gbps, mfma_tf))
+
+    configs = None
+    if not args.no_configs:
+        log("bench: timing the per-workload block")
+        configs = configs_block(sb, workload, dev, oracle_ok=not args.no_cpu_baseline)
+        configs["crossdecoder_step_B32_L34816_16_layers"] = {"ms": round(ms_step, 4),
+                                                             "tokens_per_s": round(tokens_per_s, 1),
+                                                             "frac_of_hbm_peak": round(nbytes["total"] / (ms_step / 1e3)
+                                                                                       / 1e9 / HBM_PEAK_GBS, 4)}
 
     cpu = parity = None
     if not args.no_cpu_baseline:
@@ -596,9 +721,15 @@ def main():
                      "traffic": traffic_for_current_kernel()},
         "measured_ceilings": {"stream_read_gbps": round(read_gbps, 1), "bf16_mfma_tflops": round(mfma_tf, 1),
                               "split_frac_of_stream_read": round(achieved / read_gbps, 4)},
+        "ms_per_step_with_split_events": round(ms_step_instr, 4),
+        "graph_replay": graph,
         "kernels": kern,
+        "configs": configs,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
+        "library": {"version": sb.version(), "built_from_sources": sb.built_source_hash(),
+                    "sources_now": sb.current_source_hash(),
+                    "matches": sb.built_source_hash() == sb.current_source_hash()},
     }
     if workloads is not None:
         out["workloads"] = workloads

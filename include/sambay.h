@@ -72,7 +72,9 @@ typedef struct {
 /* Text describing the last non-SB_OK status returned on this thread ("" if none). */
 const char *sb_last_error(void);
 
-/* Library version string. */
+/* Library version string: "sambay-mi355x <version> (gfx950) sources <hash>", where <hash> is the
+ * first 16 hex digits of the SHA-256 over the kernel and header sources the library was built from
+ * (attention_decoding_amd/build.py, source_hash()).  Static storage; never null. */
 const char *sb_version(void);
 
 /* ------------------------------------------------------------------ GMU --
