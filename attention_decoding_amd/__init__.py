@@ -37,7 +37,7 @@ EXPORTS = ("sb_last_error", "sb_version", "gmu_workspace_bytes", "gmu_forward", 
            "diffattn_workspace_bytes", "diffattn_decode", "selfattn_workspace_bytes", "selfattn_decode",
            "mamba_workspace_bytes", "mamba_decode_step", "attn_prefill_workspace_bytes", "attn_prefill",
            "mamba_prefill_workspace_bytes", "mamba_prefill", "sambay_prefill_workspace_bytes", "sambay_prefill",
-           "sambay_decode_workspace_bytes", "sambay_decode_step")
+           "sambay_decode_workspace_bytes", "sambay_decode_step", "xattn_decode_noalloc")
 SB_TIME_XATTN_SPLIT, SB_TIME_XATTN_MERGE, SB_TIME_SKINNY, SB_TIME_GEMM, SB_TIME_GMU_F32, SB_TIME_PROBE = \
     1, 2, 4, 8, 16, 32
 SB_TIME_DIFF_SPLIT, SB_TIME_DIFF_MERGE, SB_TIME_PREFILL = 64, 128, 256
@@ -88,6 +88,8 @@ def _load() -> ctypes.CDLL:
     lib.xattn_workspace_bytes.restype = sz
     lib.xattn_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, sz, vp]
     lib.xattn_decode.restype = ctypes.c_int
+    lib.xattn_decode_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp]
+    lib.xattn_decode_noalloc.restype = ctypes.c_int
     lib.crossdecoder_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64]
     lib.crossdecoder_workspace_bytes.restype = sz
     lib.crossdecoder_step.argtypes = [vp, vp, vp, vp, ctypes.POINTER(SbLayer), i32, i64, i64, i64, i64, i64, i64,
@@ -325,6 +327,29 @@ def xattn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, ou
             raise ValueError("lens must have shape [B]")
         lp = _dev_ptr(lens, "lens", torch.int32, dev)
         _check("xattn_decode_varlen", lib.xattn_decode_varlen(*args, lp, _dev_ptr(out, "out", bf, dev), *tail))
+    return out
+
+
+def xattn_decode_noalloc(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, out: torch.Tensor,
+                         scale: float | None = None) -> torch.Tensor:
+    """xattn_decode whose partials live in the library's own per-GPU scratch
+    array: the call allocates nothing (the caller passes out).  Calls that
+    overlap on one GPU race (one array per GPU)."""
+    dev = _check_device(q, "q")
+    bf = torch.bfloat16
+    if q.dim() != 3 or kcache.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and kcache [B, Hkv, L, D]")
+    B, Hq, D = q.shape
+    B2, Hkv, L, D2 = kcache.shape
+    if B2 != B or D2 != D or vcache.shape != kcache.shape or out.shape != (B, Hq, D):
+        raise ValueError("xattn_decode_noalloc shape mismatch: q %s k %s v %s out %s" %
+                         (tuple(q.shape), tuple(kcache.shape), tuple(vcache.shape), tuple(out.shape)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check("xattn_decode_noalloc",
+           lib.xattn_decode_noalloc(_dev_ptr(q, "q", bf, dev), _dev_ptr(kcache, "kcache", bf, dev),
+                                    _dev_ptr(vcache, "vcache", bf, dev), _dev_ptr(out, "out", bf, dev), B, Hq, Hkv, D,
+                                    L, float(scale), _stream(dev)))
     return out
 
 

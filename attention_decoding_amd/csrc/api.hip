@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "launch.hpp"
@@ -279,6 +280,58 @@ extern "C" sb_status xattn_decode(const void *q, const void *kcache, const void 
                                   size_t workspace_bytes, hipStream_t stream) {
     return xattn_decode_impl("xattn_decode", q, kcache, vcache, nullptr, out, B, Hq, Hkv, D, L, scale, workspace,
                              workspace_bytes, stream);
+}
+
+// ---------------------------------------------------- no-allocation entry
+// The partials of xattn_decode_noalloc live in this file-scope device array:
+// one copy per GPU the library runs on, held until the process ends.  On the
+// host its name is only a stand-in: the device address is looked up once per
+// device with hipGetSymbolAddress (with that device current), and only that
+// address is ever passed on.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+sb_status scratch_for_current_device(const char *fn, void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (dev < 0 || dev >= kMaxDevices) return fail(SB_EUNSUPPORTED, "%s: device %d (at most %d)", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return SB_OK;
+}
+
+}  // namespace
+
+extern "C" sb_status xattn_decode_noalloc(const void *q, const void *kcache, const void *vcache, void *out, int64_t B,
+                                          int64_t Hq, int64_t Hkv, int64_t D, int64_t L, float scale,
+                                          hipStream_t stream) {
+    const char *fn = "xattn_decode_noalloc";
+    if (B < 0 || Hq < 0 || Hkv < 0 || D < 0 || L < 0) return fail(SB_EINVAL, "negative size");
+    if (B == 0) return ok();
+    const sb_status st = check_xattn_shape(B, Hq, Hkv, D, L);
+    if (st != SB_OK) return st;
+    const size_t need = xattn_ws(B, Hq, Hkv, L);
+    if (need > kNoAllocScratchBytes)
+        return fail(SB_EWORKSPACE, "%s: %zu bytes of partials needed, the library's scratch holds %zu", fn, need,
+                    kNoAllocScratchBytes);
+    void *ws = nullptr;
+    const sb_status sst = scratch_for_current_device(fn, &ws);
+    if (sst != SB_OK) return sst;
+    return xattn_decode_impl(fn, q, kcache, vcache, nullptr, out, B, Hq, Hkv, D, L, scale, ws, kNoAllocScratchBytes,
+                             stream);
 }
 
 extern "C" sb_status xattn_decode_varlen(const void *q, const void *kcache, const void *vcache, const int32_t *lens,

@@ -117,6 +117,18 @@ sb_status xattn_decode(const void *q, const void *kcache, const void *vcache, vo
                        int64_t Hkv, int64_t D, int64_t L, float scale, void *workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* xattn_decode without a workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same computation, kernels
+ * and results as xattn_decode, with the split partials kept in a file-scope device array of the
+ * library (16 MiB per GPU, allocated when the library is loaded, held until the process ends).  The
+ * partials take xattn_workspace_bytes(B, Hq, Hkv, D, L) bytes; a larger request returns
+ * SB_EWORKSPACE before anything is enqueued (e.g. B = 32, 24q/8kv heads, any L: 3.2 MB).  Every call
+ * on one GPU uses that GPU's one array, which keeps the last call's contents: calls that overlap on
+ * one GPU (other streams, other host threads) race and must be ordered by the caller.  Allocates
+ * and frees nothing; errors as xattn_decode. */
+sb_status xattn_decode_noalloc(const void *q, const void *kcache, const void *vcache, void *out, int64_t B,
+                               int64_t Hq, int64_t Hkv, int64_t D, int64_t L, float scale, hipStream_t stream);
+
 /* ---------------------------------------------------- cross-decoder step --
  * One decode step of the cross-decoder ([Notes] section 整体框架): for each
  * layer in array order, a residual branch on the bf16 stream h [B, d_model]:

@@ -421,3 +421,19 @@ def test_sambay_decode_validation(sb):
     need = sb.lib.sambay_decode_workspace_bytes(32, 3072, 6144, 16, 192, 4, 8192, 24, 8, 128, 34816, 256)
     assert need > sb.lib.crossdecoder_ex_workspace_bytes(32, 3072, 6144, 8192, 24, 8, 128, 34816)
     assert sb.lib.sambay_decode_workspace_bytes(32, 3072, 6144, 16, 192, 4, 8192, 24, 8, 64, 34816, 256) == 0
+
+
+def test_noalloc_attention_rejects_requests_beyond_its_scratch(sb):
+    """xattn_decode_noalloc checks shapes and its 16 MiB scratch limit before
+    it touches the device: 4096 sequences x 128 query heads need 545 MB of
+    partials."""
+    lib = sb.lib
+    assert lib.xattn_decode_noalloc(_addr(0), _addr(1), _addr(2), _addr(3), 4096, 128, 16, 128, 34816, 0.088,
+                                    None) == sb.SB_EWORKSPACE
+    assert "scratch" in lib.sb_last_error().decode()
+    assert lib.xattn_decode_noalloc(_addr(0), _addr(1), _addr(2), _addr(3), 2, 24, 8, 64, 100, 0.1,
+                                    None) == sb.SB_EUNSUPPORTED          # D != 128
+    assert lib.xattn_decode_noalloc(_addr(0), _addr(1), _addr(2), _addr(3), -1, 24, 8, 128, 100, 0.1,
+                                    None) == sb.SB_EINVAL
+    assert lib.xattn_decode_noalloc(_addr(0), _addr(1), _addr(2), _addr(3), 0, 24, 8, 128, 100, 0.1,
+                                    None) == sb.SB_OK                    # nothing to do
