@@ -896,71 +896,79 @@ int oracle_mamba_step(const void *x, int dt_x, const void *W_in, const void *W_x
         d_model <= 0 || d_inner <= 0 || N <= 0 || R <= 0 || K < 1)
         return -1;
     const int64_t P = R + 2 * N, KS = K - 1;
-    int fail = 0;
-#pragma omp parallel
-    {
-        double *xi = (double *)malloc((size_t)d_inner * sizeof(double));
-        double *z = (double *)malloc((size_t)d_inner * sizeof(double));
-        double *u = (double *)malloc((size_t)d_inner * sizeof(double));
-        double *xd = (double *)malloc((size_t)P * sizeof(double));
-        double *gm = (double *)malloc((size_t)d_inner * sizeof(double));
-        int ok = xi && z && u && xd && gm;
-        if (!ok) {
-#pragma omp atomic write
-            fail = 1;
-        }
-#pragma omp for schedule(dynamic, 1)
-        for (int64_t b = 0; b < B; ++b) {
-            if (!ok) continue;
-            /* input projection: the x branch and the gate branch */
-            for (int64_t c = 0; c < 2 * d_inner; ++c) {
-                double acc = 0.0;
-                for (int64_t k = 0; k < d_model; ++k) acc += widen(W_in, dt_w, c * d_model + k) * widen(x, dt_x, b * d_model + k);
-                if (c < d_inner) xi[c] = acc; else z[c - d_inner] = acc;
-            }
-            /* causal depthwise convolution over the last K inputs, SiLU; shift the window */
-            for (int64_t c = 0; c < d_inner; ++c) {
-                const int64_t so = (b * d_inner + c) * KS;
-                double acc = widen(conv_b, dt_p, c);
-                for (int64_t k = 0; k < KS; ++k) acc += widen(conv_w, dt_p, c * K + k) * widen(conv_state, dt_s, so + k);
-                acc += widen(conv_w, dt_p, c * K + KS) * xi[c];
-                u[c] = acc / (1.0 + exp(-acc));
-                for (int64_t k = 0; k + 1 < KS; ++k) conv_state_out[so + k] = widen(conv_state, dt_s, so + k + 1);
-                if (KS > 0) conv_state_out[so + KS - 1] = xi[c];
-            }
-            /* the data-dependent step, input and output vectors */
-            for (int64_t p = 0; p < P; ++p) {
-                double acc = 0.0;
-                for (int64_t c = 0; c < d_inner; ++c) acc += widen(W_x, dt_w, p * d_inner + c) * u[c];
-                xd[p] = acc;
-            }
-            const double *delta = xd, *Bv = xd + R, *Cv = xd + R + N;
-            for (int64_t c = 0; c < d_inner; ++c) {
-                double a = widen(dt_bias, dt_p, c);
-                for (int64_t r = 0; r < R; ++r) a += widen(W_dt, dt_w, c * R + r) * delta[r];
-                const double dlt = softplus_def(a);
-                double m = 0.0;
-                for (int64_t n = 0; n < N; ++n) {
-                    const int64_t si = (b * d_inner + c) * N + n;
-                    const double A = -exp(widen(A_log, dt_p, c * N + n));
-                    const double st = exp(dlt * A) * widen(ssm_state, dt_s, si) + dlt * Bv[n] * u[c];
-                    ssm_state_out[si] = st;
-                    m += Cv[n] * st;
-                }
-                m += widen(Dp, dt_p, c) * u[c];
-                M_out[b * d_inner + c] = m;
-                gm[c] = m * (z[c] / (1.0 + exp(-z[c])));
-            }
-            /* output projection of the gated readout */
-            for (int64_t o = 0; o < d_model; ++o) {
-                double acc = 0.0;
-                for (int64_t c = 0; c < d_inner; ++c) acc += widen(W_out, dt_w, o * d_inner + c) * gm[c];
-                y_out[b * d_model + o] = acc;
-            }
-        }
-        free(xi); free(z); free(u); free(xd); free(gm);
+    /* Per-sequence intermediates; every stage below is a loop over independent
+       (sequence, channel) pairs, so it runs in parallel also for one sequence. */
+    double *XI = (double *)malloc((size_t)B * d_inner * sizeof(double));
+    double *Z = (double *)malloc((size_t)B * d_inner * sizeof(double));
+    double *U = (double *)malloc((size_t)B * d_inner * sizeof(double));
+    double *XD = (double *)malloc((size_t)B * P * sizeof(double));
+    double *GM = (double *)malloc((size_t)B * d_inner * sizeof(double));
+    if (B > 0 && !(XI && Z && U && XD && GM)) {
+        free(XI); free(Z); free(U); free(XD); free(GM);
+        return -2;
     }
-    return fail ? -2 : 0;
+    /* input projection: the x branch and the gate branch */
+#pragma omp parallel for schedule(static)
+    for (int64_t bc = 0; bc < B * 2 * d_inner; ++bc) {
+        const int64_t b = bc / (2 * d_inner), c = bc % (2 * d_inner);
+        double acc = 0.0;
+        for (int64_t k = 0; k < d_model; ++k) acc += widen(W_in, dt_w, c * d_model + k) * widen(x, dt_x, b * d_model + k);
+        if (c < d_inner) XI[b * d_inner + c] = acc; else Z[b * d_inner + c - d_inner] = acc;
+    }
+    /* causal depthwise convolution over the last K inputs, SiLU; shift the window */
+#pragma omp parallel for schedule(static)
+    for (int64_t bc = 0; bc < B * d_inner; ++bc) {
+        const int64_t b = bc / d_inner, c = bc % d_inner;
+        const double *xi = XI + b * d_inner;
+        const int64_t so = (b * d_inner + c) * KS;
+        double acc = widen(conv_b, dt_p, c);
+        for (int64_t k = 0; k < KS; ++k) acc += widen(conv_w, dt_p, c * K + k) * widen(conv_state, dt_s, so + k);
+        acc += widen(conv_w, dt_p, c * K + KS) * xi[c];
+        U[b * d_inner + c] = acc / (1.0 + exp(-acc));
+        for (int64_t k = 0; k + 1 < KS; ++k) conv_state_out[so + k] = widen(conv_state, dt_s, so + k + 1);
+        if (KS > 0) conv_state_out[so + KS - 1] = xi[c];
+    }
+    /* the data-dependent step, input and output vectors */
+#pragma omp parallel for schedule(static)
+    for (int64_t bp = 0; bp < B * P; ++bp) {
+        const int64_t b = bp / P, p = bp % P;
+        const double *u = U + b * d_inner;
+        double acc = 0.0;
+        for (int64_t c = 0; c < d_inner; ++c) acc += widen(W_x, dt_w, p * d_inner + c) * u[c];
+        XD[b * P + p] = acc;
+    }
+    /* the state update, the readout M = C·s + D·u and the gate */
+#pragma omp parallel for schedule(static)
+    for (int64_t bc = 0; bc < B * d_inner; ++bc) {
+        const int64_t b = bc / d_inner, c = bc % d_inner;
+        const double *u = U + b * d_inner, *z = Z + b * d_inner, *xd = XD + b * P;
+        const double *delta = xd, *Bv = xd + R, *Cv = xd + R + N;
+        double a = widen(dt_bias, dt_p, c);
+        for (int64_t r = 0; r < R; ++r) a += widen(W_dt, dt_w, c * R + r) * delta[r];
+        const double dlt = softplus_def(a);
+        double m = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const int64_t si = (b * d_inner + c) * N + n;
+            const double A = -exp(widen(A_log, dt_p, c * N + n));
+            const double st = exp(dlt * A) * widen(ssm_state, dt_s, si) + dlt * Bv[n] * u[c];
+            ssm_state_out[si] = st;
+            m += Cv[n] * st;
+        }
+        m += widen(Dp, dt_p, c) * u[c];
+        M_out[b * d_inner + c] = m;
+        GM[b * d_inner + c] = m * (z[c] / (1.0 + exp(-z[c])));
+    }
+    /* output projection of the gated readout */
+#pragma omp parallel for schedule(static)
+    for (int64_t bo = 0; bo < B * d_model; ++bo) {
+        const int64_t b = bo / d_model, o = bo % d_model;
+        const double *gm = GM + b * d_inner;
+        double acc = 0.0;
+        for (int64_t c = 0; c < d_inner; ++c) acc += widen(W_out, dt_w, o * d_inner + c) * gm[c];
+        y_out[b * d_model + o] = acc;
+    }
+    free(XI); free(Z); free(U); free(XD); free(GM);
+    return 0;
 }
 
 /* ------------------------------------------------ self-decoder prefill

@@ -37,8 +37,8 @@ def f64(t):
 
 
 def report(name, e, tol=TOL):
-    print("%-64s err %.3e (tol %.0e)" % (name, e, tol), flush=True)
-    assert e <= tol, "%s: %.3e > %.0e" % (name, e, tol)
+    print("%-64s err %.3e (tol %.2e)" % (name, e, tol), flush=True)
+    assert e <= tol, "%s: %.3e > %.2e" % (name, e, tol)
 
 
 def _snapshot(layers):
@@ -116,6 +116,78 @@ def test_prefill_then_decode_equals_longer_prefill(sb):
     report("prefill(T) vs prefill(T-1) + step: h", err(f64(h), f64(h_full)))
     report("prefill(T) vs prefill(T-1) + step: M", err(f64(M), f64(M_full)))
     report("prefill(T) vs prefill(T-1) + step: cache", err(f64(b.kcache[:, :, :T]), f64(a.kcache[:, :, :T])))
+
+
+@pytest.mark.timeout(400)
+def test_decode_step_full_width_full_depth(sb):
+    """The whole model at its widths and depth (16 self-decoder layers: 8 SSM,
+    7 sliding-window, 1 full attention; 16 cross-decoder layers; SwiGLU d_ff
+    8192 everywhere) for 2 sequences at positions 4095 and 3000 of a
+    4096-position shared cache, from random caches, rings and SSM states:
+    both sequences' outputs, the memory M, the written cache rows, the ring
+    slots and every SSM state against the oracle."""
+    c = workload.SAMBAY_PREFILL
+    B, L, W = 2, 4096, c["window"]
+    inp = workload.sambay_prefill_inputs(B, 1, c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"], c["d_conv"],
+                                         c["d_ff"], c["Hq"], c["Hkv"], c["D"], W, L,
+                                         workload.self_layer_kinds(c["n_self"]), workload.layer_kinds(c["n_cross"]),
+                                         seed=47, device=DEV, fresh=False)
+    inp.kcache.copy_(workload.normal(tuple(inp.kcache.shape), seed=48, device=DEV))
+    inp.vcache.copy_(workload.normal(tuple(inp.vcache.shape), seed=49, device=DEV))
+    for i, ly in enumerate(inp.self_layers):
+        if ly["kind"] == "swa":
+            ly["kring"].copy_(workload.normal(tuple(ly["kring"].shape), seed=60 + 2 * i, device=DEV))
+            ly["vring"].copy_(workload.normal(tuple(ly["vring"].shape), seed=61 + 2 * i, device=DEV))
+    pos_list = [L - 1, 3000]
+    pos = torch.tensor(pos_list, dtype=torch.int32, device=DEV)
+    x_new = workload.normal((B, c["d_model"]), seed=50, device=DEV)
+    before = _snapshot(inp.self_layers)
+    Kb, Vb = inp.kcache.cpu(), inp.vcache.cpu()
+    print("case full width, full depth: B=2, positions %s of %d" % (pos_list, L), flush=True)
+    h, M = sb.sambay_decode_step(x_new.clone(), pos, inp.self_layers, inp.cross_layers, inp.kcache, inp.vcache,
+                                 window=W)
+    torch.cuda.synchronize()
+    ref = oracle.sambay_decode_step(x_new.cpu(), before, _snapshot(inp.cross_layers), c["Hq"], c["Hkv"], pos.cpu(),
+                                    Kb, Vb, window=W)
+    # The bf16 residual stream is rounded at 64 points on the way through the
+    # 32 layers; how far that rounding alone moves the result is measured on
+    # this very input (the oracle with and without it: 2.2e-2).  Two
+    # implementations that both round at those points land that far apart
+    # for the final h (a pre-rounding difference in the last fp32 bits sends
+    # some roundings to the neighbouring bf16 value, and the difference
+    # travels: measured 2.198e-2 against a floor of 2.200e-2), so its bar is
+    # the larger of 2e-2 and 1.25 times that floor; the h after the
+    # self-decoder (32 roundings) and every other output keep 2e-2.
+    exact = oracle.sambay_decode_step(x_new.cpu(), before, _snapshot(inp.cross_layers), c["Hq"], c["Hkv"],
+                                      pos.cpu(), Kb, Vb, window=W, round_h=False)
+    floor = err(ref["h_out"], exact["h_out"])
+    name = "full width/depth"
+    print("%s: the oracle's own bf16-stream floor for h %.3e" % (name, floor), flush=True)
+    report("%s h" % name, err(f64(h), ref["h_out"]), max(TOL, 1.25 * floor))
+    report("%s M_last" % name, err(f64(M), ref["M_last"]))
+    for b, p in enumerate(pos_list):
+        report("%s cache row b=%d p=%d" % (name, b, p),
+               max(err(f64(inp.kcache[b, :, p]), ref["K"][b, :, p]), err(f64(inp.vcache[b, :, p]), ref["V"][b, :, p])))
+    worst_state = worst_ring = 0.0
+    for i, ly in enumerate(inp.self_layers):
+        r = ref["layers"][i]
+        if ly["kind"] == "mamba":
+            worst_state = max(worst_state, err(f64(ly["ssm_state"]), r["ssm_state"]),
+                              err(f64(ly["conv_state"]), r["conv_state"]))
+        elif ly["kind"] == "swa":
+            worst_ring = max(worst_ring, err(f64(ly["kring"]), r["kring"]), err(f64(ly["vring"]), r["vring"]))
+    report("%s SSM states, worst of 8 layers" % name, worst_state)
+    report("%s window rings, worst of 7 layers" % name, worst_ring)
+    # The self-decoder alone from the same state (no cross-decoder layers).
+    for ly, s0 in zip(inp.self_layers, before):
+        for k in ("conv_state", "ssm_state", "kring", "vring"):
+            if k in ly:
+                ly[k].copy_(s0[k].to(DEV))
+    inp.kcache.copy_(Kb.to(DEV))
+    inp.vcache.copy_(Vb.to(DEV))
+    h_self, _ = sb.sambay_decode_step(x_new.clone(), pos, inp.self_layers, [], inp.kcache, inp.vcache, window=W)
+    torch.cuda.synchronize()
+    report("%s h after the self-decoder" % name, err(f64(h_self), ref["h_self"]))
 
 
 def test_decode_step_full_size_properties(sb):

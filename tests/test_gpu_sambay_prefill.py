@@ -125,6 +125,17 @@ def test_sambay_prefill_full_width(sb):
          c["Hkv"], 64, 512, SELF, ["xattn", "gmu"], seed=11, name="full width 1 x 70")
 
 
+@pytest.mark.timeout(400)
+def test_sambay_prefill_full_width_512_tokens(sb):
+    """The model's widths and its 256-token window over a 512-token prompt:
+    the window ring wraps, the SSM scan runs over many chunks and the prompt
+    products fill whole 256-row GEMM tiles; 4 self-decoder and 2
+    cross-decoder layers, one sequence, every output against the oracle."""
+    c = workload.SAMBAY_PREFILL
+    _run(sb, 1, 512, c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"], c["d_conv"], c["d_ff"], c["Hq"],
+         c["Hkv"], c["window"], 576, SELF, ["xattn", "gmu"], seed=13, name="full width 1 x 512")
+
+
 def test_sambay_prefill_full_size_properties(sb):
     """The benchmark's whole prefill (4 x 2048 tokens, 16 + 16 layers): two
     runs give the same bits, every output is finite, exactly the prompt's

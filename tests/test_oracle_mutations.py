@@ -79,14 +79,15 @@ MUTANTS = [
      "const int64_t n = p < 0 ? 0 : (window && p + 1 > window ? window : p + 1);",
      "const int64_t n = p < 0 ? 0 : (window ? window : p + 1);"),
     ("mamba_conv_taps_reversed", "test_oracle_mamba.py",
-     "for (int64_t k = 0; k < KS; ++k) acc += widen(conv_w, dt_p, c * K + k) * widen(conv_state, dt_s, so + k);\n                acc += widen(conv_w, dt_p, c * K + KS) * xi[c];",
-     "for (int64_t k = 0; k < KS; ++k) acc += widen(conv_w, dt_p, c * K + KS - k) * widen(conv_state, dt_s, so + k);\n                acc += widen(conv_w, dt_p, c * K) * xi[c];"),
+     "for (int64_t k = 0; k < KS; ++k) acc += widen(conv_w, dt_p, c * K + k) * widen(conv_state, dt_s, so + k);\n        acc += widen(conv_w, dt_p, c * K + KS) * xi[c];",
+     "for (int64_t k = 0; k < KS; ++k) acc += widen(conv_w, dt_p, c * K + KS - k) * widen(conv_state, dt_s, so + k);\n        acc += widen(conv_w, dt_p, c * K) * xi[c];"),
     ("mamba_step_without_softplus", "test_oracle_mamba.py", "const double dlt = softplus_def(a);",
      "const double dlt = a;"),
     ("mamba_decay_sign", "test_oracle_mamba.py", "const double A = -exp(widen(A_log, dt_p, c * N + n));",
      "const double A = exp(widen(A_log, dt_p, c * N + n));"),
     ("mamba_skip_dropped", "test_oracle_mamba.py", "m += widen(Dp, dt_p, c) * u[c];", "m += 0.0;"),
-    ("mamba_gate_dropped", "test_oracle_mamba.py", "gm[c] = m * (z[c] / (1.0 + exp(-z[c])));", "gm[c] = m;"),
+    ("mamba_gate_dropped", "test_oracle_mamba.py", "GM[b * d_inner + c] = m * (z[c] / (1.0 + exp(-z[c])));",
+     "GM[b * d_inner + c] = m;"),
     ("mamba_B_C_swapped", "test_oracle_mamba.py", "const double *delta = xd, *Bv = xd + R, *Cv = xd + R + N;",
      "const double *delta = xd, *Cv = xd + R, *Bv = xd + R + N;"),
     ("mamba_window_not_shifted", "test_oracle_mamba.py",
