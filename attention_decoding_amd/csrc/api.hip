@@ -80,13 +80,21 @@ bool log_enabled() {
 
 // ----------------------------------------------------------------- GMU
 
+// Elements of the GMU's gated hidden H for a group of T decode tokens: above
+// 16 tokens it travels in the 16-token tiled layout (whole tiles), below it
+// row-major.
+size_t gmu_hidden_elems(int T, int d_inner) {
+    return T > 16 ? tiled_elems(T, d_inner) : (size_t)T * d_inner;
+}
+
 size_t gmu_ws(int64_t rows, int64_t d_model, int64_t d_inner, sb_dtype dt) {
     if (rows <= 0 || d_model <= 0 || d_inner <= 0) return 0;
     if (dt == SB_F32) return round_up((size_t)rows * d_inner * sizeof(float));
-    // bf16 H [rows, d_inner] (decode: a hi + lo pair, plus room for k-split partials).
+    // bf16 H [rows, d_inner] (decode: a hi + lo pair in whole 16-token tiles,
+    // plus room for k-split partials).
     size_t bytes = round_up((size_t)rows * d_inner * sizeof(bf16_t));
     if (rows <= kSkinnyMaxTokens) {
-        bytes *= 2;
+        bytes = 2 * round_up(gmu_hidden_elems((int)rows, (int)d_inner) * sizeof(bf16_t));
         size_t part = skinny_partial_bytes_max((int)rows, (int)d_inner, (int)d_model);
         const size_t part2 = skinny_partial_bytes_max((int)rows, (int)d_model, (int)d_inner);
         if (part2 > part) part = part2;
@@ -102,8 +110,8 @@ size_t gmu_ws(int64_t rows, int64_t d_model, int64_t d_inner, sb_dtype dt) {
 hipError_t gmu_decode_bf16(const bf16_t *M, const bf16_t *X, const bf16_t *X_lo, int ldx, const bf16_t *W1,
                            const bf16_t *W2, void *Y, Epilogue out_epi, int T, int d_model, int d_inner, bool h_lo,
                            Carver &ws, hipStream_t stream) {
-    bf16_t *H = static_cast<bf16_t *>(ws.take((size_t)T * d_inner * sizeof(bf16_t)));
-    bf16_t *H_lo = static_cast<bf16_t *>(ws.take((size_t)T * d_inner * sizeof(bf16_t)));
+    bf16_t *H = static_cast<bf16_t *>(ws.take(gmu_hidden_elems(T, d_inner) * sizeof(bf16_t)));
+    bf16_t *H_lo = static_cast<bf16_t *>(ws.take(gmu_hidden_elems(T, d_inner) * sizeof(bf16_t)));
     if (!h_lo) H_lo = nullptr;
     const SkinnyPlan p1 = skinny_plan(T, d_inner, d_model, X_lo != nullptr);
     const SkinnyPlan p2 = skinny_plan(T, d_model, d_inner, H_lo != nullptr);
@@ -113,11 +121,19 @@ hipError_t gmu_decode_bf16(const bf16_t *M, const bf16_t *X, const bf16_t *X_lo,
     SkinnyArgs a1;
     a1.X = X; a1.X_lo = X_lo; a1.ldx = ldx; a1.W = W1; a1.T = T; a1.N = d_inner; a1.K = d_model; a1.epi = EPI_GATE;
     a1.out = H; a1.ldo = d_inner; a1.out_lo = H_lo; a1.aux = M; a1.ldaux = d_inner;
-    hipError_t e = launch_skinny(a1, p1, partials, stream);
-    if (e != hipSuccess) return e;
     SkinnyArgs a2;
     a2.X = H; a2.X_lo = H_lo; a2.ldx = d_inner; a2.W = W2; a2.T = T; a2.N = d_model; a2.K = d_inner;
     a2.epi = out_epi; a2.out = Y; a2.ldo = d_model;
+    // Above 16 tokens H travels in the 16-token tiled layout when both
+    // products stream through LDS: each token-operand load then reads 1 KB
+    // contiguous (a 32-token product of 37.7 MB: 11.4 -> 10.0 us; at 8
+    // tokens no gain).
+    if (T > 16 && p1.k_splits == 1 && skinny_streams(a1, p1) && skinny_streams(a2, p2)) {
+        a1.out_tiled = true;
+        a2.x_tiled = true;
+    }
+    hipError_t e = launch_skinny(a1, p1, partials, stream);
+    if (e != hipSuccess) return e;
     return launch_skinny(a2, p2, partials, stream);
 }
 
@@ -772,7 +788,7 @@ StepLayout step_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t Hq, 
                             skinny_partial_bytes_max((int)T, (int)d_model, (int)d_model)};
     for (size_t c : cands)
         if (c > part) part = c;
-    s.gmu = 2 * round_up((size_t)T * d_inner * sizeof(bf16_t)) + round_up(part);
+    s.gmu = 2 * round_up(gmu_hidden_elems((int)T, (int)d_inner) * sizeof(bf16_t)) + round_up(part);
     s.partials = round_up(xattn_partial_bytes(B, Hq, xattn_plan(B, Hkv, L).splits));
     s.total = s.q + s.o + s.gmu + s.partials;
     return s;
@@ -857,7 +873,7 @@ extern "C" sb_status crossdecoder_step(void *h, const void *M, const void *kcach
             // Projection partials share the GMU region's partial space (after the H pair).
             const int64_t Tm = B < kSkinnyMaxTokens ? B : kSkinnyMaxTokens;
             float *proj_partials =
-                reinterpret_cast<float *>(gmu_ws_base + 2 * round_up((size_t)Tm * di * sizeof(bf16_t)));
+                reinterpret_cast<float *>(gmu_ws_base + 2 * round_up(gmu_hidden_elems((int)Tm, di) * sizeof(bf16_t)));
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
                 SkinnyArgs aq;

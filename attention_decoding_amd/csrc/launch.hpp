@@ -145,7 +145,22 @@ struct SkinnyArgs {
     const bf16_t *next_norm = nullptr;
     bf16_t *next_x = nullptr, *next_x_lo = nullptr;
     float eps = 0.f;
+    // The 16-token tiled layout of a token operand [T, K] (element (t, k) at
+    // tiled_index(t, k, ceil(T / 16)); tiled_elems(T, K) elements, tokens past
+    // T undefined): one load instruction of the MFMA token operand reads 1 KB
+    // contiguous instead of 64 bytes of 16 rows.  For operands the library
+    // produces and consumes itself (the GMU's gated hidden H); only the
+    // LDS-streaming product takes it (skinny_streams).
+    bool x_tiled = false;    // X (and X_lo) in the tiled layout (ldx unused)
+    bool out_tiled = false;  // EPI_GATE: out (and out_lo) written in the tiled layout, K = N (ldo unused)
 };
+__host__ __device__ inline size_t tiled_index(int t, int k, int ntiles) {
+    return ((size_t)(k >> 5) * ntiles + (t >> 4)) * 512 + ((k >> 3) & 3) * 128 + (t & 15) * 8 + (k & 7);
+}
+inline size_t tiled_elems(int T, int K) { return (size_t)((T + 15) / 16) * 16 * K; }
+// Whether launch_skinny runs this product on the LDS-streaming kernel (the
+// only one that reads or writes the tiled layout).
+bool skinny_streams(const SkinnyArgs &a, const SkinnyPlan &plan);
 hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *partials, hipStream_t stream);
 bool skinny_fuses_norm(const SkinnyArgs &a, const SkinnyPlan &plan);
 SkinnyPlan skinny_plan_dual(int T, int N, int K);

@@ -223,13 +223,15 @@ __host__ __device__ constexpr int stream_swizzle_width(int cpr) { return cpr % 1
 
 // KS: 32-wide k-steps per wave (K slice = 512·KS).  Rows past R or N read a
 // valid row and are never stored; token slots past T read token T-1.
-template <int RT, int TB, int KS, int EPI, bool XLO>
+// XT: the token operand in the 16-token tiled layout; otiled (EPI_GATE): the
+// output in that layout.
+template <int RT, int TB, int KS, int EPI, bool XLO, bool XT>
 __global__ __launch_bounds__(kStreamThreads) void stream_kernel(const bf16_t *__restrict__ X,
                                                                 const bf16_t *__restrict__ X_lo, int ldx,
                                                                 const bf16_t *__restrict__ W, int T, int N, int K,
                                                                 int R, void *out, int ldo, bf16_t *out_lo,
                                                                 const bf16_t *__restrict__ aux, int ldaux,
-                                                                float *__restrict__ partials) {
+                                                                float *__restrict__ partials, int otiled) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int KW = KS * 32, CPR = KW / 8, SW = stream_swizzle_width(CPR), TT = 16 * TB;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
@@ -243,13 +245,18 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(const bf16_t *__
     unsigned char *wl = smem + (size_t)wave * instr * 1024;
 
     u32x4 xf[KS][TB], xl[XLO ? KS : 1][TB];
+    const int ntiles = (T + 15) / 16;
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
         const size_t xo = (size_t)min(16 * tb + col, T - 1) * ldx + kw0 + 8 * grp;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            xf[ks][tb] = ld16(X + xo + 32 * ks);
-            if (XLO) xl[XLO ? ks : 0][tb] = ld16(X_lo + xo + 32 * ks);
+            // Tiled: lane l's 16 bytes of k-step (kw0 / 32 + ks), token tile tb,
+            // are bytes 16 l .. 16 l + 15 of one contiguous 1 KB block.
+            const size_t xi = XT ? ((size_t)((kw0 >> 5) + ks) * ntiles + min(tb, ntiles - 1)) * 512 + lane * 8
+                                 : xo + 32 * ks;
+            xf[ks][tb] = ld16(X + xi);
+            if (XLO) xl[XLO ? ks : 0][tb] = ld16(X_lo + xi);
         }
     }
     for (int i = 0; i < instr; ++i) {
@@ -301,10 +308,18 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(const bf16_t *__
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < kStreamWaves; ++w) v += red[(w * 16 * RT + rl) * RS + t];
-        if (gridDim.y == 1)
-            apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, ldaux);
-        else
+        if (gridDim.y > 1) {
             partials[((size_t)blockIdx.y * T + t) * N + n] = v;
+        } else if (EPI == EPI_GATE && otiled) {
+            const float m = bf16_to_f32(aux[(size_t)t * ldaux + n]);
+            const float gv = m * (v / (1.f + expf(-v)));
+            const bf16_t hi = f32_to_bf16(gv);
+            const size_t o = tiled_index(t, n, ntiles);
+            reinterpret_cast<bf16_t *>(out)[o] = hi;
+            if (out_lo) out_lo[o] = f32_to_bf16(gv - bf16_to_f32(hi));
+        } else {
+            apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, ldaux);
+        }
     }
 }
 
@@ -520,20 +535,28 @@ hipError_t launch_finish(const SkinnyArgs &a, const SkinnyPlan &p, float *partia
     return hipGetLastError();
 }
 
-template <int RT, int TB, int KS, int EPI, bool XLO>
-hipError_t launch_stream4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+template <int RT, int TB, int KS, int EPI, bool XLO, bool XT>
+hipError_t launch_stream5(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
     const size_t lds = stream_lds_bytes(p.rows_per_wg, KS, RT, TB);
-    static const hipError_t attr = hipFuncSetAttribute((const void *)stream_kernel<RT, TB, KS, EPI, XLO>,
+    static const hipError_t attr = hipFuncSetAttribute((const void *)stream_kernel<RT, TB, KS, EPI, XLO, XT>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax);
     if (attr != hipSuccess) return attr;
     const dim3 grid((a.N + p.rows_per_wg - 1) / p.rows_per_wg, p.k_splits);
+    TimingScope ts(kTimeSkinny, stream);
+    hipLaunchKernelGGL((stream_kernel<RT, TB, KS, EPI, XLO, XT>), grid, dim3(kStreamThreads), lds, stream, a.X, a.X_lo,
+                       a.ldx, a.W, a.T, a.N, a.K, p.rows_per_wg, a.out, a.ldo, a.out_lo, a.aux, a.ldaux, partials,
+                       a.out_tiled ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <int RT, int TB, int KS, int EPI, bool XLO>
+hipError_t launch_stream4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
     {
-        TimingScope ts(kTimeSkinny, stream);
-        hipLaunchKernelGGL((stream_kernel<RT, TB, KS, EPI, XLO>), grid, dim3(kStreamThreads), lds, stream, a.X, a.X_lo,
-                           a.ldx, a.W, a.T, a.N, a.K, p.rows_per_wg, a.out, a.ldo, a.out_lo, a.aux, a.ldaux, partials);
+        const hipError_t e0 = a.x_tiled ? launch_stream5<RT, TB, KS, EPI, XLO, true>(a, p, partials, stream)
+                                        : launch_stream5<RT, TB, KS, EPI, XLO, false>(a, p, partials, stream);
+        if (e0 != hipSuccess) return e0;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.k_splits == 1) return e;
+    if (p.k_splits == 1) return hipSuccess;
     return launch_finish<EPI>(a, p, partials, stream);
 }
 
@@ -759,8 +782,16 @@ size_t skinny_partial_bytes(int T, int N, const SkinnyPlan &p) {
     return p.k_splits > 1 ? (size_t)p.k_splits * T * N * sizeof(float) : 0;
 }
 
+bool skinny_streams(const SkinnyArgs &a, const SkinnyPlan &plan) {
+    return !(gemv_eligible(a) && plan.k_splits == 1) && stream_ks(a, plan) != 0;
+}
+
 hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *partials, hipStream_t stream) {
     const int R = plan.rows_per_wg;
+    // The tiled token layout exists only in the LDS-streaming product; a
+    // tiled output only from its unsplit gate epilogue.
+    if ((a.x_tiled || a.out_tiled) && !skinny_streams(a, plan)) return hipErrorInvalidValue;
+    if (a.out_tiled && (a.epi != EPI_GATE || plan.k_splits != 1)) return hipErrorInvalidValue;
     if (gemv_eligible(a) && plan.k_splits == 1) return launch_gemv(a, stream);
     if (const int ks = stream_ks(a, plan)) return launch_stream(a, plan, partials, stream, ks);
     if (a.epi == EPI_SWIGLU) {  // dual: row tiles in pairs, R <= 32 (skinny_plan_dual)
