@@ -125,10 +125,10 @@ hipError_t gmu_decode_bf16(const bf16_t *M, const bf16_t *X, const bf16_t *X_lo,
     a2.X = H; a2.X_lo = H_lo; a2.ldx = d_inner; a2.W = W2; a2.T = T; a2.N = d_model; a2.K = d_inner;
     a2.epi = out_epi; a2.out = Y; a2.ldo = d_model;
     // Above 16 tokens H travels in the 16-token tiled layout when both
-    // products stream through LDS: each token-operand load then reads 1 KB
+    // products' kernels take it: each token-operand load then reads 1 KB
     // contiguous (a 32-token product of 37.7 MB: 11.4 -> 10.0 us; at 8
     // tokens no gain).
-    if (T > 16 && p1.k_splits == 1 && skinny_streams(a1, p1) && skinny_streams(a2, p2)) {
+    if (T > 16 && p1.k_splits == 1 && skinny_tiles(a1, p1) && skinny_tiles(a2, p2)) {
         a1.out_tiled = true;
         a2.x_tiled = true;
     }

@@ -119,6 +119,7 @@ struct SkinnyPlan {
     int rows_per_wg;   // weight rows per workgroup
     int k_splits;      // workgroups along K (1 = epilogue fused)
     int k_slice;       // K elements per split (multiple of 64)
+    int slab_rtw = 0;  // > 0: the slab product, 128 x slab_rtw weight rows per workgroup (k_splits > 1 always)
 };
 // xlo: the token operand is a bf16 hi + lo pair (twice the bytes per workgroup).
 SkinnyPlan skinny_plan(int T, int N, int K, bool xlo);
@@ -150,7 +151,7 @@ struct SkinnyArgs {
     // T undefined): one load instruction of the MFMA token operand reads 1 KB
     // contiguous instead of 64 bytes of 16 rows.  For operands the library
     // produces and consumes itself (the GMU's gated hidden H); only the
-    // LDS-streaming product takes it (skinny_streams).
+    // LDS-streaming product takes it (skinny_tiles).
     bool x_tiled = false;    // X (and X_lo) in the tiled layout (ldx unused)
     bool out_tiled = false;  // EPI_GATE: out (and out_lo) written in the tiled layout, K = N (ldo unused)
 };
@@ -160,7 +161,10 @@ __host__ __device__ inline size_t tiled_index(int t, int k, int ntiles) {
 inline size_t tiled_elems(int T, int K) { return (size_t)((T + 15) / 16) * 16 * K; }
 // Whether launch_skinny runs this product on the LDS-streaming kernel (the
 // only one that reads or writes the tiled layout).
-bool skinny_streams(const SkinnyArgs &a, const SkinnyPlan &plan);
+// Whether the plan's kernel takes the 16-token tiled layout for this
+// product's token operand (x_tiled) and, for the gate epilogue, its output
+// (out_tiled).
+bool skinny_tiles(const SkinnyArgs &a, const SkinnyPlan &plan);
 hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *partials, hipStream_t stream);
 bool skinny_fuses_norm(const SkinnyArgs &a, const SkinnyPlan &plan);
 SkinnyPlan skinny_plan_dual(int T, int N, int K);

@@ -18,19 +18,37 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Up to kMaxVec 8-element vectors of a row per thread (rows up to 8192).
+constexpr int kMaxVec = 4;
+
 __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const bf16_t *__restrict__ h, const bf16_t *__restrict__ g,
                                                            int d, float eps, bf16_t *__restrict__ out_hi,
                                                            bf16_t *__restrict__ out_lo) {
     __shared__ float red[kThreads / 64];
     const size_t row = (size_t)blockIdx.x * d;
     const int nvec = d / 8;
-    float ss = 0.f;
-    for (int v = threadIdx.x; v < nvec; v += kThreads) {
-        const u32x4 x = ld16(h + row + 8 * v);
+    // The row and the gains are requested at once and kept in registers for
+    // the scaling (one round trip to memory; same arithmetic order as a
+    // strided loop over the vectors).
+    u32x4 xs[kMaxVec], gs[kMaxVec];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float a = lo_bf16(x[e]), b = hi_bf16(x[e]);
-            ss += a * a + b * b;
+    for (int i = 0; i < kMaxVec; ++i) {
+        const int v = threadIdx.x + i * kThreads;
+        if (v < nvec) {
+            xs[i] = ld16(h + row + 8 * v);
+            gs[i] = ld16(g + 8 * v);
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxVec; ++i) {
+        const int v = threadIdx.x + i * kThreads;
+        if (v < nvec) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = lo_bf16(xs[i][e]), b = hi_bf16(xs[i][e]);
+                ss += a * a + b * b;
+            }
         }
     }
 #pragma unroll
@@ -41,8 +59,11 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const bf16_t *__restr
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
     const float r = 1.f / sqrtf(tot / (float)d + eps);
-    for (int v = threadIdx.x; v < nvec; v += kThreads) {
-        const u32x4 x = ld16(h + row + 8 * v), gv = ld16(g + 8 * v);
+#pragma unroll
+    for (int i = 0; i < kMaxVec; ++i) {
+        const int v = threadIdx.x + i * kThreads;
+        if (v >= nvec) break;
+        const u32x4 x = xs[i], gv = gs[i];
         u32x4 hi, lo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -62,6 +83,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const bf16_t *__restr
 hipError_t launch_rmsnorm(const bf16_t *h, const bf16_t *g, int rows, int d, float eps, bf16_t *out_hi,
                           bf16_t *out_lo, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
+    if (d % 8 != 0 || d > 8 * kThreads * kMaxVec) return hipErrorInvalidValue;
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(kThreads), 0, stream, h, g, d, eps, out_hi, out_lo);
     return hipGetLastError();
 }

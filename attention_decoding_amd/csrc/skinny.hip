@@ -323,6 +323,237 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(const bf16_t *__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Slab product (decode products of 17-64 tokens).  Every workgroup streams its
+// weight bytes and, from L2, the token operand of its K range; measured on
+// MI355X, one CU moves these at ~36-40 GB/s together, a token byte costing as
+// much as a weight byte.  With 32 tokens as a hi + lo pair the whole token
+// operand of a K = 3072 product is 393 KB, five times a workgroup's share of
+// an 18.9 MB weight matrix.  So here a workgroup takes few columns and many
+// rows: 128 x RTW weight rows by a K slab of 64 x KC columns (K split in
+// K / (64 KC) slabs, fp32 partials summed by a finishing pass).  The token
+// slab is copied into LDS once (direct global -> LDS copies) and read by all
+// 8 waves; wave w streams its own 16 x RTW rows through a private ring of NS
+// LDS stages of 16 rows x 64 columns (8 rows x 128 B per copy instruction,
+// which streams at full rate; 16 rows x 64 B loses ~25%), NS - 1 stages
+// ahead.  No wave waits for another after the token slab has landed, and
+// each wave's accumulators hold finished partial rows (no reduction across
+// waves).
+constexpr int kSlabWaves = 8;
+constexpr int kSlabThreads = 64 * kSlabWaves;
+constexpr size_t kSlabLdsMax = 160 * 1024;
+constexpr int kSlabMaxSplits = 16;  // K slabs (the finishing passes hold one partial per slab in registers)
+
+__host__ __device__ constexpr size_t slab_token_bytes(int TB, int KC, bool xlo) {
+    return (size_t)16 * TB * 64 * KC * 2 * (xlo ? 2 : 1);
+}
+// Ring stages per wave (2 KB each): what the token slab leaves of the LDS, at most 8.
+__host__ __device__ constexpr int slab_stages(int TB, int KC, bool xlo) {
+    return slab_token_bytes(TB, KC, xlo) >= kSlabLdsMax
+               ? 0
+               : ((kSlabLdsMax - slab_token_bytes(TB, KC, xlo)) / (kSlabWaves * 2048) > 8
+                      ? 8
+                      : (int)((kSlabLdsMax - slab_token_bytes(TB, KC, xlo)) / (kSlabWaves * 2048)));
+}
+
+// s_waitcnt vmcnt(n) for an n known after unrolling (the switch folds away).
+__device__ __forceinline__ void slab_wait(int n) {
+#define SLAB_WAIT_CASE(c) \
+    case c: __builtin_amdgcn_s_waitcnt(0x3f70 | ((c) & 0xf) | (((c) >> 4) << 14)); break;
+    switch (n) {
+        SLAB_WAIT_CASE(0) SLAB_WAIT_CASE(2) SLAB_WAIT_CASE(4) SLAB_WAIT_CASE(6) SLAB_WAIT_CASE(8)
+        SLAB_WAIT_CASE(10) SLAB_WAIT_CASE(12) SLAB_WAIT_CASE(14)
+        default: __builtin_amdgcn_s_waitcnt(0x3f70); break;
+    }
+#undef SLAB_WAIT_CASE
+}
+
+__device__ __forceinline__ void slab_copy(const bf16_t *g, unsigned char *lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, kStreamCopyPolicy);
+}
+
+// Rows [0, Na) of the Nrows come from W, rows [Na, Nrows) from W_b (the
+// SwiGLU pair: gate then up).  partials: fp32 [K / KR][T][Nrows].
+template <int RTW, int TB, int KC, bool XLO>
+__global__ __launch_bounds__(kSlabThreads) void slab_kernel(const bf16_t *__restrict__ X,
+                                                            const bf16_t *__restrict__ X_lo, int ldx,
+                                                            const bf16_t *__restrict__ W,
+                                                            const bf16_t *__restrict__ W_b, int Na, int Nrows, int K,
+                                                            int T, float *__restrict__ partials) {
+    constexpr int KR = 64 * KC, CPR = KR / 8, T16 = 16 * TB;
+    constexpr int NS = slab_stages(TB, KC, XLO);
+    constexpr int S = RTW * KC;  // ring stages per wave
+    constexpr size_t SLAB = slab_token_bytes(TB, KC, XLO);
+    constexpr int NJ = (int)(SLAB / 1024);  // token copy instructions per workgroup
+    constexpr int NJW = (NJ + kSlabWaves - 1) / kSlabWaves;
+    static_assert(NS >= 3 && 2 * (NS - 1) <= 14, "ring depth");
+    static_assert(CPR % 16 == 0 && SLAB % 1024 == 0, "slab rows of whole 16-chunk groups");
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+    const int k0 = blockIdx.y * KR;
+    const int row0 = blockIdx.x * (128 * RTW) + wave * 16 * RTW;  // this wave's first row
+    unsigned char *ring = smem + SLAB + (size_t)wave * NS * 2048;
+
+    // Token slab: row t (tokens past T repeat token T - 1), chunk g of the
+    // slab's 64 KC columns at slot (g & ~15) | ((g ^ t) & 15); the lo half
+    // after the hi half.  Copy instruction j fills slab bytes [1 KB j, 1 KB j + 1 KB).
+#pragma unroll
+    for (int jj = 0; jj < NJW; ++jj) {
+        const int j = min(wave + kSlabWaves * jj, NJ - 1);  // the last instruction may be repeated (same bytes)
+        const int u = j * 64 + lane, part = u / (T16 * CPR), rem = u % (T16 * CPR), t = rem / CPR, slot = rem % CPR;
+        const int g = (slot & ~15) | ((slot ^ t) & 15);
+        slab_copy((part ? X_lo : X) + (size_t)min(t, T - 1) * ldx + k0 + 8 * g, smem + (size_t)j * 1024);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the token copies stay ahead of the ring's (the waits count them)
+    // Ring stage s: this wave's row tile s / KC, columns 64 (s % KC) .. + 63;
+    // row r's eight chunks at r·128 + 16·(g ^ ((r >> 1) & 7)).
+    auto issue = [&](int s) {
+        const int rt = s / KC, kc = s % KC;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 8 * i + (lane >> 3), g = (lane & 7) ^ ((r >> 1) & 7);
+            const int row = min(row0 + 16 * rt + r, Nrows - 1);
+            const bf16_t *src = row < Na ? W + (size_t)row * K : W_b + (size_t)(row - Na) * K;
+            slab_copy(src + k0 + 64 * kc + 8 * g, ring + (size_t)(s % NS) * 2048 + i * 1024);
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < S) {
+            issue(s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    slab_wait(2 * (NS - 1 < S ? NS - 1 : S));  // this wave's token copies have landed
+    __builtin_amdgcn_s_barrier();               // ... and every wave's
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int aslot = col * 128;                          // + 16 * (g ^ ((col >> 1) & 7))
+    const unsigned char *bbase = smem + (size_t)col * KR * 2;  // token row col of tile 0
+    f32x4 acc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int after = (NS - 2 < S - 1 - s) ? NS - 2 : S - 1 - s;
+        slab_wait(2 * after);  // stage s has landed
+        __builtin_amdgcn_wave_barrier();
+        if (s + NS - 1 < S) issue(s + NS - 1);  // into the slot stage s - 1 used
+        const unsigned char *st = ring + (size_t)(s % NS) * 2048 + aslot;
+        const int kc = s % KC;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int g = 4 * (2 * kc + q) + grp;
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(st + 16 * ((4 * q + grp) ^ ((col >> 1) & 7)));
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int t = 16 * tb + col;
+                const size_t bo = (size_t)tb * 16 * KR * 2 + 16 * ((g & ~15) | ((g ^ t) & 15));
+                acc[tb] = mfma16x16x32(a, *reinterpret_cast<const u32x4 *>(bbase + bo), acc[tb]);
+                if (XLO) acc[tb] = mfma16x16x32(a, *reinterpret_cast<const u32x4 *>(bbase + SLAB / 2 + bo), acc[tb]);
+            }
+        }
+        if (kc == KC - 1) {
+            // acc[tb][e] = partial of row 16·rt + 4·grp + e, token 16·tb + col.
+            const int grow = row0 + 16 * (s / KC) + 4 * grp;
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int t = 16 * tb + col;
+                if (t < T && grow < Nrows)
+                    *reinterpret_cast<f32x4 *>(partials + ((size_t)blockIdx.y * T + t) * Nrows + grow) = acc[tb];
+                acc[tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Finishing passes of the slab product: four outputs per thread (16-byte
+// partial loads), the slabs summed in slab order.
+template <int EPI>
+__global__ __launch_bounds__(256) void slab_finish_kernel(const float *__restrict__ partials, int ks, int T, int N,
+                                                          void *out, int ldo, bf16_t *out_lo,
+                                                          const bf16_t *__restrict__ aux, int ldaux) {
+    const int n4 = N / 4;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)T * n4) return;
+    const int t = (int)(idx / n4), n = 4 * (int)(idx % n4);
+    // Every slab's partial is requested before the first is used (one round
+    // trip to wherever the slab kernel's writes went, not one per slab).
+    f32x4 pv[kSlabMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kSlabMaxSplits; ++s)
+        if (s < ks) pv[s] = *reinterpret_cast<const f32x4 *>(partials + ((size_t)s * T + t) * N + n);
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSlabMaxSplits; ++s)
+        if (s < ks) v += pv[s];
+    const size_t o = (size_t)t * ldo + n;
+    if (EPI == EPI_F32) {
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + o) = v;
+    } else if (EPI == EPI_BF16) {
+        *reinterpret_cast<u32x2 *>(reinterpret_cast<bf16_t *>(out) + o) = (u32x2){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    } else if (EPI == EPI_GATE) {
+        const u32x2 m = *reinterpret_cast<const u32x2 *>(aux + (size_t)t * ldaux + n);
+        const float mm[4] = {lo_bf16(m[0]), hi_bf16(m[0]), lo_bf16(m[1]), hi_bf16(m[1])};
+        bf16_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float g = mm[e] * (v[e] / (1.f + expf(-v[e])));
+            hi[e] = f32_to_bf16(g);
+            lo[e] = f32_to_bf16(g - bf16_to_f32(hi[e]));
+        }
+        *reinterpret_cast<u32x2 *>(reinterpret_cast<bf16_t *>(out) + o) =
+            (u32x2){(uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16)};
+        if (out_lo)
+            *reinterpret_cast<u32x2 *>(out_lo + o) =
+                (u32x2){(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
+    } else {
+        bf16_t *h = reinterpret_cast<bf16_t *>(out);
+        const u32x2 hv = *reinterpret_cast<const u32x2 *>(h + o);
+        *reinterpret_cast<u32x2 *>(h + o) =
+            (u32x2){(uint32_t)f32_to_bf16(lo_bf16(hv[0]) + v[0]) | ((uint32_t)f32_to_bf16(hi_bf16(hv[0]) + v[1]) << 16),
+                    (uint32_t)f32_to_bf16(lo_bf16(hv[1]) + v[2]) | ((uint32_t)f32_to_bf16(hi_bf16(hv[1]) + v[3]) << 16)};
+    }
+}
+
+// SwiGLU: partials [ks][T][2N], gate columns then up columns.
+__global__ __launch_bounds__(256) void slab_swiglu_finish_kernel(const float *__restrict__ partials, int ks, int T,
+                                                                 int N, bf16_t *__restrict__ out, int ldo,
+                                                                 bf16_t *__restrict__ out_lo) {
+    const int n4 = N / 4;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)T * n4) return;
+    const int t = (int)(idx / n4), n = 4 * (int)(idx % n4);
+    f32x4 pg[kSlabMaxSplits], pu[kSlabMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kSlabMaxSplits; ++s)
+        if (s < ks) {
+            const float *p = partials + ((size_t)s * T + t) * 2 * N + n;
+            pg[s] = *reinterpret_cast<const f32x4 *>(p);
+            pu[s] = *reinterpret_cast<const f32x4 *>(p + N);
+        }
+    f32x4 g = {0.f, 0.f, 0.f, 0.f}, v = g;
+#pragma unroll
+    for (int s = 0; s < kSlabMaxSplits; ++s)
+        if (s < ks) {
+            g += pg[s];
+            v += pu[s];
+        }
+    bf16_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float u = (g[e] / (1.f + expf(-g[e]))) * v[e];
+        hi[e] = f32_to_bf16(u);
+        lo[e] = f32_to_bf16(u - bf16_to_f32(hi[e]));
+    }
+    const size_t o = (size_t)t * ldo + n;
+    *reinterpret_cast<u32x2 *>(out + o) =
+        (u32x2){(uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16)};
+    if (out_lo)
+        *reinterpret_cast<u32x2 *>(out_lo + o) =
+            (u32x2){(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
+}
+
 size_t stream_lds_bytes(int R, int KS, int RT, int TB) {
     const size_t units = (size_t)R * KS * 4, instr = (units + 63) / 64;
     const size_t copy = (size_t)kStreamWaves * instr * 1024;
@@ -335,8 +566,19 @@ __global__ __launch_bounds__(256) void swiglu_finish_kernel(const float *__restr
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)T * N) return;
     const int t = (int)(idx / N), n = (int)(idx % N);
+    // The first 16 splits' partials are requested at once (one round trip).
+    float pg[16], pu[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+        if (s < splits) {
+            pg[s] = partials[((size_t)s * T + t) * 2 * N + n];
+            pu[s] = partials[((size_t)s * T + t) * 2 * N + N + n];
+        }
     float g = 0.f, v = 0.f;
-    for (int s = 0; s < splits; ++s) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+        if (s < splits) g += pg[s], v += pu[s];
+    for (int s = 16; s < splits; ++s) {
         g += partials[((size_t)s * T + t) * 2 * N + n];
         v += partials[((size_t)s * T + t) * 2 * N + N + n];
     }
@@ -350,8 +592,16 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(const float *__restr
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)T * N) return;
     const int t = (int)(idx / N), n = (int)(idx % N);
+    // The first 16 splits' partials are requested at once (one round trip).
+    float pv[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+        if (s < splits) pv[s] = partials[((size_t)s * T + t) * N + n];
     float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += partials[((size_t)s * T + t) * N + n];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+        if (s < splits) v += pv[s];
+    for (int s = 16; s < splits; ++s) v += partials[((size_t)s * T + t) * N + n];
     apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, ldaux);
 }
 
@@ -627,6 +877,124 @@ hipError_t launch_stream(const SkinnyArgs &a, const SkinnyPlan &p, float *partia
                               : launch_stream0<1>(a, p, partials, stream, KS);
 }
 
+template <int RTW, int TB, int KC, bool XLO>
+hipError_t launch_slab4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    const bool dual = a.epi == EPI_SWIGLU;
+    const int Nrows = dual ? 2 * a.N : a.N;
+    const size_t lds = slab_token_bytes(TB, KC, XLO) + (size_t)kSlabWaves * slab_stages(TB, KC, XLO) * 2048;
+    static const hipError_t attr = hipFuncSetAttribute((const void *)slab_kernel<RTW, TB, KC, XLO>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSlabLdsMax);
+    if (attr != hipSuccess) return attr;
+    const dim3 grid((Nrows + 128 * RTW - 1) / (128 * RTW), p.k_splits);
+    {
+        TimingScope ts(kTimeSkinny, stream);
+        hipLaunchKernelGGL((slab_kernel<RTW, TB, KC, XLO>), grid, dim3(kSlabThreads), lds, stream, a.X, a.X_lo, a.ldx,
+                           a.W, dual ? a.W_b : a.W, a.N, Nrows, a.K, a.T, partials);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned blocks = (unsigned)(((size_t)a.T * (a.N / 4) + 255) / 256);
+    switch (a.epi) {
+        case EPI_SWIGLU:
+            hipLaunchKernelGGL(slab_swiglu_finish_kernel, dim3(blocks), dim3(256), 0, stream, partials, p.k_splits, a.T,
+                               a.N, static_cast<bf16_t *>(a.out), a.ldo, a.out_lo);
+            break;
+        case EPI_F32:
+            hipLaunchKernelGGL(slab_finish_kernel<EPI_F32>, dim3(blocks), dim3(256), 0, stream, partials, p.k_splits,
+                               a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.ldaux);
+            break;
+        case EPI_BF16:
+            hipLaunchKernelGGL(slab_finish_kernel<EPI_BF16>, dim3(blocks), dim3(256), 0, stream, partials, p.k_splits,
+                               a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.ldaux);
+            break;
+        case EPI_GATE:
+            hipLaunchKernelGGL(slab_finish_kernel<EPI_GATE>, dim3(blocks), dim3(256), 0, stream, partials, p.k_splits,
+                               a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.ldaux);
+            break;
+        default:
+            hipLaunchKernelGGL(slab_finish_kernel<EPI_RESID>, dim3(blocks), dim3(256), 0, stream, partials, p.k_splits,
+                               a.T, a.N, a.out, a.ldo, a.out_lo, a.aux, a.ldaux);
+            break;
+    }
+    return hipGetLastError();
+}
+
+template <int RTW, int TB, int KC>
+hipError_t launch_slab3(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    if (a.X_lo) {
+        if constexpr (slab_stages(TB, KC, true) >= 3) return launch_slab4<RTW, TB, KC, true>(a, p, partials, stream);
+        return hipErrorInvalidValue;
+    }
+    return launch_slab4<RTW, TB, KC, false>(a, p, partials, stream);
+}
+
+template <int TB>
+hipError_t launch_slab2(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    const int kc = p.k_slice / 64;
+    if (p.slab_rtw == 1 && kc == 6) return launch_slab3<1, TB, 6>(a, p, partials, stream);
+    if (p.slab_rtw == 2 && kc == 6) return launch_slab3<2, TB, 6>(a, p, partials, stream);
+    if (p.slab_rtw == 2 && kc == 8) return launch_slab3<2, TB, 8>(a, p, partials, stream);
+    if (p.slab_rtw == 2 && kc == 12) return launch_slab3<2, TB, 12>(a, p, partials, stream);
+    if (p.slab_rtw == 1 && kc == 12) return launch_slab3<1, TB, 12>(a, p, partials, stream);
+    return hipErrorInvalidValue;
+}
+
+// The slab shapes (rows per wave in 16-row tiles, K slab in 64-column chunks)
+// the plan chooses from.
+struct SlabShape {
+    int rtw, kc;
+};
+constexpr SlabShape kSlabShapes[] = {{1, 6}, {2, 6}, {2, 8}, {2, 12}, {1, 12}};
+
+bool slab_fits(int T, int Nrows, int K, int ldx, bool x_tiled, const SkinnyPlan &p) {
+    return T > 16 && T <= kSkinnyMaxTokens && Nrows % 4 == 0 && !x_tiled && ldx % 8 == 0 && p.k_splits >= 2 &&
+           p.k_splits <= kSlabMaxSplits &&
+           (int64_t)p.k_slice * p.k_splits == K;
+}
+
+hipError_t launch_slab(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    const bool dual = a.epi == EPI_SWIGLU;
+    if (a.out_tiled || (dual && !a.W_b) || !slab_fits(a.T, dual ? 2 * a.N : a.N, a.K, a.ldx, a.x_tiled, p) ||
+        a.N % 4 != 0 || a.ldo % 4 != 0 || (a.epi == EPI_GATE && a.ldaux % 4 != 0))
+        return hipErrorInvalidValue;
+    return stream_tb(a.T) == 2 ? launch_slab2<2>(a, p, partials, stream) : launch_slab2<4>(a, p, partials, stream);
+}
+
+// The slab plan of least modelled time: per workgroup, its weights, its token
+// slab (16-token tiles, hi + lo) and its partial rows at ~38 GB/s per CU (in
+// rounds of 256 workgroups), against all weights at ~6 TB/s, plus the
+// partials written and read again at ~6 TB/s.  Taken for a hi + lo token
+// operand above 16 tokens and for any operand above 32 (a plain bf16 one at
+// 17-32 tokens measured faster in the LDS-streaming product, whose gate
+// output needs no finishing pass); none for outputs whose rows are not a
+// multiple of 4.  SAMBAY_NO_SLAB=1 turns it off.
+bool slab_plan(int T, int Nrows, int K, bool xlo, SkinnyPlan &p) {
+    static const bool off = [] {
+        const char *e = getenv("SAMBAY_NO_SLAB");
+        return e && *e && *e != '0';
+    }();
+    if (off || T <= 16 || (!xlo && T <= 32) || T > kSkinnyMaxTokens || Nrows % 4 != 0) return false;
+    const int TB = stream_tb(T);
+    double best = 1e30;
+    for (const SlabShape &sh : kSlabShapes) {
+        const int KR = 64 * sh.kc;
+        if (K % KR != 0 || K / KR < 2 || K / KR > kSlabMaxSplits || slab_stages(TB, sh.kc, xlo) < 3) continue;
+        const int ks = K / KR, R = 128 * sh.rtw;
+        const double wgs = (double)((Nrows + R - 1) / R) * ks, rounds = (double)(int)((wgs + kTargetWGs - 1) / kTargetWGs);
+        const double per_wg = (double)R * KR * 2 + 16.0 * TB * KR * 2 * (xlo ? 2 : 1) + (double)T * R * 4;
+        const double t_cu = rounds * per_wg / 38e3, t_hbm = (double)Nrows * K * 2 / 6e6;
+        const double t = (t_cu > t_hbm ? t_cu : t_hbm) + 2.0 * ks * T * Nrows * 4 / 6e6;
+        if (t < best) {
+            best = t;
+            p.rows_per_wg = R;
+            p.k_splits = ks;
+            p.k_slice = KR;
+            p.slab_rtw = sh.rtw;
+        }
+    }
+    return best < 1e30;
+}
+
 template <int RT, int TB, int EPI, bool XLO, bool DUAL = false>
 hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
     // Chunks in flight per wave: operand registers U·8·(RT + TB·(1 + XLO)) <= ~160.
@@ -692,6 +1060,10 @@ SkinnyPlan skinny_plan(int T, int N, int K, bool xlo) {
         const char *e = getenv("SAMBAY_NO_STREAM");
         return e && *e && *e != '0';
     }();
+    {
+        SkinnyPlan p;
+        if (slab_plan(T, N, K, xlo, p)) return p;
+    }
     if (T >= 2 && !no_stream) {
         for (int ks = 1; ks <= 4; ks *= 2) {
             if (K % ks != 0) break;
@@ -751,6 +1123,10 @@ size_t skinny_partial_bytes_max(int T, int N, int K) {
 }
 
 SkinnyPlan skinny_plan_dual(int T, int N, int K) {
+    {
+        SkinnyPlan p;  // the pair's token operand is a hi + lo pair in the layer stack
+        if (slab_plan(T, 2 * N, K, true, p)) return p;
+    }
     // The 2N weight rows are planned together (a 2-way K split above 16
     // tokens), then each workgroup takes R/2 output rows (R/2 rows of each
     // matrix).
@@ -774,7 +1150,7 @@ bool skinny_fuses_norm(const SkinnyArgs &a, const SkinnyPlan &p) {
     // SAMBAY_NO_NORM_FUSION=1 selects the separate RMSNorm launch instead (same bits).
     const char *env = getenv("SAMBAY_NO_NORM_FUSION");
     const bool off = env && *env && *env != '0';
-    return !off && a.epi == EPI_RESID && p.k_splits > 1 && a.next_norm && a.next_x && a.next_x_lo &&
+    return !off && a.epi == EPI_RESID && p.k_splits > 1 && p.slab_rtw == 0 && a.next_norm && a.next_x && a.next_x_lo &&
            a.ldo == a.N && a.N % 8 == 0;
 }
 
@@ -782,7 +1158,8 @@ size_t skinny_partial_bytes(int T, int N, const SkinnyPlan &p) {
     return p.k_splits > 1 ? (size_t)p.k_splits * T * N * sizeof(float) : 0;
 }
 
-bool skinny_streams(const SkinnyArgs &a, const SkinnyPlan &plan) {
+bool skinny_tiles(const SkinnyArgs &a, const SkinnyPlan &plan) {
+    if (plan.slab_rtw > 0) return false;
     return !(gemv_eligible(a) && plan.k_splits == 1) && stream_ks(a, plan) != 0;
 }
 
@@ -790,8 +1167,9 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *par
     const int R = plan.rows_per_wg;
     // The tiled token layout exists only in the LDS-streaming product; a
     // tiled output only from its unsplit gate epilogue.
-    if ((a.x_tiled || a.out_tiled) && !skinny_streams(a, plan)) return hipErrorInvalidValue;
+    if ((a.x_tiled || a.out_tiled) && !skinny_tiles(a, plan)) return hipErrorInvalidValue;
     if (a.out_tiled && (a.epi != EPI_GATE || plan.k_splits != 1)) return hipErrorInvalidValue;
+    if (plan.slab_rtw > 0) return launch_slab(a, plan, partials, stream);
     if (gemv_eligible(a) && plan.k_splits == 1) return launch_gemv(a, stream);
     if (const int ks = stream_ks(a, plan)) return launch_stream(a, plan, partials, stream, ks);
     if (a.epi == EPI_SWIGLU) {  // dual: row tiles in pairs, R <= 32 (skinny_plan_dual)

@@ -197,6 +197,20 @@ def test_step_ex_full_size_sampled(sb):
     report("step_ex full size, teacher-forced, worst of 16 layers", worst, TOL_BF16)
 
 
+@pytest.mark.parametrize("B", [17, 33, 64])
+def test_step_ex_token_tile_edges(sb, B):
+    """d_model 768, d_inner 1536, d_ff 1536: every product of the layer at 17
+    (one token past a 16-token tile), 33 and 64 tokens splits K in slabs of
+    384 or 768 columns (hi + lo token operands) with a finishing pass; all
+    sequences checked."""
+    x = workload.crossdecoder_ex_inputs(B, 768, 1536, 1536, 6, 2, 128, 300, 2, seed=40 + B, device=DEV,
+                                        lens="ragged")
+    ref = _oracle_ex(x)
+    sb.crossdecoder_step_ex(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+    torch.cuda.synchronize()
+    report("step_ex B=%d 768/1536/1536" % B, err(f64(x.h), ref), TOL_BF16)
+
+
 def test_step_ex_prepared_replays_identically(sb):
     x = _ex_inputs(3, 2, [5, 300, 77], seed=35)
     h0 = x.h.clone()

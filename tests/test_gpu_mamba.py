@@ -48,6 +48,7 @@ def _cpu_w(m):
 def _run(sb, m, name, rows=None):
     B = m.x.shape[0]
     rows = list(range(B)) if rows is None else rows
+    assert 0 <= min(rows) and max(rows) < B, "sampled rows outside the batch"  # checked before any GPU gather
     idx = torch.tensor(rows, device=DEV)
     conv0, ssm0 = m.conv_state[idx].cpu(), m.ssm_state[idx].cpu()
     M, y = sb.mamba_decode_step(m.x, m.w, m.conv_state, m.ssm_state)
@@ -72,14 +73,15 @@ def test_mamba_small(sb, B, dm, di, N, R, K):
     _run(sb, m, "mamba B=%d %dx%d N=%d R=%d K=%d" % (B, dm, di, N, R, K))
 
 
-@pytest.mark.parametrize("B", [1, 32, 70])
+@pytest.mark.parametrize("B", [1, 17, 32, 33, 70])
 def test_mamba_full_width(sb, B):
     """d_model 3072, d_inner 6144, 16 states, rank 192, 4 taps: one token (the
-    one-token product path), the 32-sequence batch, two token groups."""
+    one-token product path), 17 and 33 tokens (one past a 16-token tile), the
+    32-sequence batch, two token groups."""
     c = workload.MAMBA_DECODE
     m = workload.mamba_inputs(B, c["d_model"], c["d_inner"], c["d_state"], c["dt_rank"], c["d_conv"], seed=B,
                               device=DEV)
-    rows = None if B <= 32 else [0, 31, 63, 64, 69]
+    rows = None if B <= 33 else [0, 31, 63, 64, B - 1]   # every row up to 33; sampled across both groups above
     _run(sb, m, "mamba full width B=%d" % B, rows)
 
 
