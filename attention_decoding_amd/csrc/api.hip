@@ -12,6 +12,7 @@
 #include <string>
 
 #include "launch.hpp"
+#include "norm_order.hpp"
 
 #include <vector>
 
@@ -910,7 +911,7 @@ namespace {
 
 // Workspace of one complete-layer step (all reused layer to layer).
 struct ExLayout {
-    size_t q, o, xn, gmu, mlp_u, part, attn, total;
+    size_t q, o, xn, gmu, mlp_u, part, attn, stats, total;
 };
 
 ExLayout ex_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_ff, int64_t Hq, int64_t Hkv, int64_t L) {
@@ -935,7 +936,8 @@ ExLayout ex_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_ff, in
     }
     s.part = round_up(part);
     s.attn = round_up(xattn_workspace_need(B, Hq, Hkv, L));
-    s.total = s.q + s.o + s.xn + s.gmu + s.mlp_u + s.part + s.attn;
+    s.stats = round_up((size_t)B * norm_stats_stride(dm) * sizeof(float));
+    s.total = s.q + s.o + s.xn + s.gmu + s.mlp_u + s.part + s.attn + s.stats;
     return s;
 }
 
@@ -1025,6 +1027,8 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
     float *part = reinterpret_cast<float *>(p);
     p += lay.part;
     void *attn_part = p;
+    p += lay.attn;
+    float *stats = reinterpret_cast<float *>(p);
     const XattnPlan plan = xattn_plan(B, Hkv, L, lens != nullptr);
     if (log_enabled())
         fprintf(stderr, "[sambay] crossdecoder_step_ex B=%lld layers=%d d_model=%lld d_inner=%lld d_ff=%lld L=%lld%s "
@@ -1034,35 +1038,65 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
     bf16_t *hb = static_cast<bf16_t *>(h);
     const int dm = (int)d_model, di = (int)d_inner, df = (int)d_ff;
 
-    // One weight-streaming product of a token group of T <= 64 rows (pointers
-    // already at the group's first row).
-    auto product = [&](const bf16_t *X, const bf16_t *X_lo, int ldx, const void *W, int N, int K, Epilogue epi,
-                       void *out, int ldo, int T) -> hipError_t {
-        SkinnyArgs a;
-        a.X = X; a.X_lo = X_lo; a.ldx = ldx; a.W = (const bf16_t *)W; a.T = T; a.N = N; a.K = K; a.epi = epi;
-        a.out = out; a.ldo = ldo;
-        return launch_skinny(a, skinny_plan(T, N, K, X_lo != nullptr), part, stream);
+    // A sublayer's input RMSNorm(h; g) is either materialised in xn (hi + lo)
+    // or deferred: the residual product that last wrote h left each token's
+    // chunk sums of squares in `stats`, and the products that read the input
+    // normalise their own K slab while staging it (the slab product; same
+    // bits as the RMSNorm kernel).  Deferred per token group of <= 64 rows
+    // when the residual product and every consumer of the input run as slab
+    // products; never for the first layer's input.
+    const int sstride = norm_stats_stride(dm);
+    constexpr int kMaxGroups = 64;
+    bool deferred[kMaxGroups] = {};
+    const bool may_defer = (B + kSkinnyMaxTokens - 1) / kSkinnyMaxTokens <= kMaxGroups;
+    auto group = [](int64_t t0) { return (int)(t0 / kSkinnyMaxTokens); };
+    // The operand of a product of group t0 whose input is RMSNorm(h; g) (g
+    // null: h itself).
+    auto operand = [&](SkinnyArgs &a, int64_t t0, const void *g) {
+        a.ldx = dm;
+        if (g && deferred[group(t0)]) {
+            a.X = hb + t0 * dm; a.X_lo = nullptr;
+            a.norm_g = (const bf16_t *)g; a.norm_stats = stats + t0 * sstride; a.norm_eps = eps;
+        } else if (g) {
+            a.X = xn + t0 * dm; a.X_lo = xn_lo + t0 * dm;
+        } else {
+            a.X = hb + t0 * dm; a.X_lo = nullptr;
+        }
+    };
+    auto plan_of = [](const SkinnyArgs &a) { return skinny_plan(a.T, a.N, a.K, a.X_lo != nullptr || a.norm_g != nullptr); };
+    // Whether the mixer of layer i (if any) reads its normalised input through the slab product at T tokens.
+    auto mixer_takes = [&](int32_t i, int T) {
+        if (i >= n_layers || !layers[i].norm1) return false;
+        return layers[i].kind == SB_LAYER_XATTN ? slab_norm_ok(T, dm, dm) : slab_norm_ok(T, di, dm);
     };
     // The residual product of a group; when `next_norm` is set the group's
-    // rows of the next sublayer's input RMSNorm(h; next_norm) are produced
-    // too, inside the K-split finishing pass or by a separate launch.
+    // rows of the next sublayer's input RMSNorm(h; next_norm) are prepared
+    // too: deferred (statistics from this product's finishing pass) when
+    // `defer` allows and this product runs as the slab product, else
+    // materialised in xn inside the K-split finishing pass or by a separate
+    // launch.
     auto residual = [&](const bf16_t *X, const bf16_t *X_lo, int ldx, const void *W, int K, int64_t t0, int T,
-                        const void *next_norm) -> hipError_t {
+                        const void *next_norm, bool defer) -> hipError_t {
         SkinnyArgs a;
         a.X = X; a.X_lo = X_lo; a.ldx = ldx; a.W = (const bf16_t *)W; a.T = T; a.N = dm; a.K = K;
         a.epi = EPI_RESID; a.out = hb + t0 * dm; a.ldo = dm;
+        const SkinnyPlan plan_r = plan_of(a);
+        const bool d = next_norm && defer && may_defer && plan_r.slab_rtw > 0;
+        deferred[group(t0)] = d;
+        if (d) {
+            a.stats_out = stats + t0 * sstride;
+            return launch_skinny(a, plan_r, part, stream);
+        }
         a.next_norm = (const bf16_t *)next_norm; a.next_x = xn + t0 * dm; a.next_x_lo = xn_lo + t0 * dm;
         a.eps = eps;
-        const SkinnyPlan plan_r = skinny_plan(T, dm, K, X_lo != nullptr);
         hipError_t e = launch_skinny(a, plan_r, part, stream);
         if (e == hipSuccess && next_norm && !skinny_fuses_norm(a, plan_r))
             e = launch_rmsnorm(hb + t0 * dm, (const bf16_t *)next_norm, T, dm, eps, xn + t0 * dm, xn_lo + t0 * dm,
                                stream);
         return e;
     };
-    auto rows = [](const bf16_t *p, int64_t t0, int ld) { return p ? p + t0 * ld : nullptr; };
 
-    // xn holds RMSNorm(h) for the sublayer about to run whenever its gain is set.
+    // xn holds RMSNorm(h) for the first sublayer when its gain is set.
     hipError_t e0 = layers[0].norm1
                         ? launch_rmsnorm(hb, (const bf16_t *)layers[0].norm1, (int)B, dm, eps, xn, xn_lo, stream)
                         : hipSuccess;
@@ -1073,41 +1107,42 @@ extern "C" sb_status crossdecoder_step_ex(void *h, const void *M, const void *kc
         const void *after_mixer = mlp ? ly.norm2 : (li + 1 < n_layers ? layers[li + 1].norm1 : nullptr);
         const void *after_mlp = li + 1 < n_layers ? layers[li + 1].norm1 : nullptr;
         hipError_t e = hipSuccess;
-        // Mixer input: RMSNorm(h) as a bf16 hi + lo pair, or h itself.
-        const bf16_t *X = ly.norm1 ? xn : hb, *X_lo = ly.norm1 ? xn_lo : nullptr;
-        if (ly.kind == SB_LAYER_XATTN) {
-            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
-                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
-                e = product(rows(X, t0, dm), rows(X_lo, t0, dm), dm, ly.w_a, dm, dm, EPI_F32, q + t0 * dm, dm, T);
-            }
-            if (e == hipSuccess)
-                e = launch_xattn(q, true, (const bf16_t *)kcache, (const bf16_t *)vcache, lens, o, o_lo, (int)B,
-                                 (int)Hq, (int)Hkv, (int)L, scale, plan, attn_part, stream);
-            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
-                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
-                e = residual(o + t0 * dm, o_lo + t0 * dm, dm, ly.w_b, dm, t0, T, after_mixer);
-            }
-        } else {
-            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
-                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+        for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+            const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+            const bool defer_mixer = mlp ? slab_norm_ok(T, 2 * df, dm) : mixer_takes(li + 1, T);
+            if (ly.kind == SB_LAYER_XATTN) {
+                SkinnyArgs a;
+                operand(a, t0, ly.norm1);
+                a.W = (const bf16_t *)ly.w_a; a.T = T; a.N = dm; a.K = dm; a.epi = EPI_F32; a.out = q + t0 * dm;
+                a.ldo = dm;
+                e = launch_skinny(a, plan_of(a), part, stream);
+            } else {
                 SkinnyArgs a1;
-                a1.X = rows(X, t0, dm); a1.X_lo = rows(X_lo, t0, dm); a1.ldx = dm;
+                operand(a1, t0, ly.norm1);
                 a1.W = (const bf16_t *)ly.w_a; a1.T = T; a1.N = di; a1.K = dm; a1.epi = EPI_GATE;
                 a1.out = H; a1.ldo = di; a1.out_lo = H_lo; a1.aux = (const bf16_t *)M + t0 * di; a1.ldaux = di;
-                e = launch_skinny(a1, skinny_plan(T, di, dm, a1.X_lo != nullptr), part, stream);
-                if (e == hipSuccess) e = residual(H, H_lo, di, ly.w_b, di, t0, T, after_mixer);
+                e = launch_skinny(a1, plan_of(a1), part, stream);
+                if (e == hipSuccess) e = residual(H, H_lo, di, ly.w_b, di, t0, T, after_mixer, defer_mixer);
+            }
+        }
+        if (e == hipSuccess && ly.kind == SB_LAYER_XATTN) {
+            e = launch_xattn(q, true, (const bf16_t *)kcache, (const bf16_t *)vcache, lens, o, o_lo, (int)B, (int)Hq,
+                             (int)Hkv, (int)L, scale, plan, attn_part, stream);
+            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+                const bool defer_mixer = mlp ? slab_norm_ok(T, 2 * df, dm) : mixer_takes(li + 1, T);
+                e = residual(o + t0 * dm, o_lo + t0 * dm, dm, ly.w_b, dm, t0, T, after_mixer, defer_mixer);
             }
         }
         if (e == hipSuccess && mlp) {
-            const bf16_t *X2 = ly.norm2 ? xn : hb, *X2_lo = ly.norm2 ? xn_lo : nullptr;
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
                 SkinnyArgs a;  // gate and up weights streamed in one pass
-                a.X = rows(X2, t0, dm); a.X_lo = rows(X2_lo, t0, dm); a.ldx = dm;
+                operand(a, t0, ly.norm2);
                 a.W = (const bf16_t *)ly.w_gate; a.W_b = (const bf16_t *)ly.w_up; a.T = T; a.N = df; a.K = dm;
                 a.epi = EPI_SWIGLU; a.out = U; a.ldo = df; a.out_lo = U_lo;
                 e = launch_skinny(a, skinny_plan_dual(T, df, dm), part, stream);
-                if (e == hipSuccess) e = residual(U, U_lo, df, ly.w_down, df, t0, T, after_mlp);
+                if (e == hipSuccess) e = residual(U, U_lo, df, ly.w_down, df, t0, T, after_mlp, mixer_takes(li + 1, T));
             }
         }
         if (e != hipSuccess) return hip_fail("crossdecoder_step_ex launch", e);

@@ -154,6 +154,16 @@ struct SkinnyArgs {
     // LDS-streaming product takes it (skinny_tiles).
     bool x_tiled = false;    // X (and X_lo) in the tiled layout (ldx unused)
     bool out_tiled = false;  // EPI_GATE: out (and out_lo) written in the tiled layout, K = N (ldo unused)
+    // The deferred RMSNorm (slab product only, slab_norm_ok): X is the
+    // residual stream h (X_lo null) and the operand is RMSNorm(h; norm_g),
+    // from the chunk sums of squares norm_stats [T][norm_stats_stride(K)]
+    // that the residual product which last wrote h left (stats_out).
+    const bf16_t *norm_g = nullptr;
+    const float *norm_stats = nullptr;
+    float norm_eps = 0.f;
+    // EPI_RESID, slab product only: also write those chunk sums of h_new
+    // ([T][norm_stats_stride(N)]) for the next sublayer's deferred norm.
+    float *stats_out = nullptr;
 };
 __host__ __device__ inline size_t tiled_index(int t, int k, int ntiles) {
     return ((size_t)(k >> 5) * ntiles + (t >> 4)) * 512 + ((k >> 3) & 3) * 128 + (t & 15) * 8 + (k & 7);
@@ -161,6 +171,13 @@ __host__ __device__ inline size_t tiled_index(int t, int k, int ntiles) {
 inline size_t tiled_elems(int T, int K) { return (size_t)((T + 15) / 16) * 16 * K; }
 // Whether launch_skinny runs this product on the LDS-streaming kernel (the
 // only one that reads or writes the tiled layout).
+// Whether a product of T tokens, Nrows weight rows (the SwiGLU pair: both
+// matrices' rows) and K columns runs as the slab product with a hi + lo
+// operand: then its operand may be a deferred RMSNorm, and a residual
+// product of that shape may leave the statistics for one.
+bool slab_norm_ok(int T, int Nrows, int K);
+// SAMBAY_NO_NORM_FUSION=1: every RMSNorm by its own launch (same bits).
+bool norm_fusion_off();
 // Whether the plan's kernel takes the 16-token tiled layout for this
 // product's token operand (x_tiled) and, for the gate epilogue, its output
 // (out_tiled).

@@ -57,7 +57,11 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 // K block slots: piece c (dims 8c .. 8c+7) of key row r, XOR-swizzled so the
 // 16 rows an MFMA operand reads at one piece index fall on distinct banks.
-__device__ __forceinline__ int kslot(int r, int c) { return 16 * r + (c ^ (r & 15)); }
+// A score tile reads rows 8(l/4) + l%4 (+ 4 for the second tile) for l < 16:
+// (r & 3) | ((r >> 3) << 2) is l itself on both sets.  (r & 15 repeats on
+// them: rows 0 and 16 shared banks, ~2x the LDS cycles of the key reads.)
+__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 3) << 2); }
+__device__ __forceinline__ int kslot(int r, int c) { return 16 * r + (c ^ kswz(r)); }
 // V^T block slots: keys 8s .. 8s+7 of dim row d (64-byte rows), swizzled so
 // that 16 consecutive dims at one s fall on distinct banks.
 __device__ __forceinline__ int vslot(int d, int s) { return 4 * d + (s ^ ((d >> 2) & 3)); }
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(kPThreads, 2) void attn_prefill_kernel(const bf16_t
         for (int e = 0; e < 4; ++e) {
             const int slot = threadIdx.x + kPThreads * e, sl = slot & (kPSlots - 1);
             if (e < 2) {
-                const int row = sl >> 4, c = (sl & 15) ^ (row & 15);
+                const int row = sl >> 4, c = (sl & 15) ^ kswz(row);
                 const int j = min(kb * kPKeys + row, T - 1);  // rows past T: any valid row, masked later
                 r[e] = ld16(kbase + (size_t)j * Hkv * kHeadDim + 8 * c);
             } else {

@@ -34,6 +34,7 @@
 //    go through a small finishing kernel (skinny_plan gives the measured rule).
 #include "device.hpp"
 #include "launch.hpp"
+#include "norm_order.hpp"
 
 #include <math.h>
 #include <stdlib.h>
@@ -374,12 +375,21 @@ __device__ __forceinline__ void slab_copy(const bf16_t *g, unsigned char *lds) {
 
 // Rows [0, Na) of the Nrows come from W, rows [Na, Nrows) from W_b (the
 // SwiGLU pair: gate then up).  partials: fp32 [K / KR][T][Nrows].
-template <int RTW, int TB, int KC, bool XLO>
+// NORM: X is the residual stream h and the operand is RMSNorm(h; g): the
+// h slab is copied in, together with the slab's gains and the tokens' chunk
+// sums of squares (stats [T][stride], left by the residual product that
+// wrote h), and turned into the bf16 hi + lo pair in LDS, with the
+// arithmetic of norm_order.hpp (the same bits as the RMSNorm kernel).
+template <int RTW, int TB, int KC, bool XLO, bool NORM = false>
 __global__ __launch_bounds__(kSlabThreads) void slab_kernel(const bf16_t *__restrict__ X,
                                                             const bf16_t *__restrict__ X_lo, int ldx,
                                                             const bf16_t *__restrict__ W,
                                                             const bf16_t *__restrict__ W_b, int Na, int Nrows, int K,
-                                                            int T, float *__restrict__ partials) {
+                                                            int T, float *__restrict__ partials,
+                                                            const bf16_t *__restrict__ norm_g,
+                                                            const float *__restrict__ norm_stats, int stats_stride,
+                                                            float eps) {
+    static_assert(!NORM || XLO, "the normalised operand is a hi + lo pair");
     constexpr int KR = 64 * KC, CPR = KR / 8, T16 = 16 * TB;
     constexpr int NS = slab_stages(TB, KC, XLO);
     constexpr int S = RTW * KC;  // ring stages per wave
@@ -397,12 +407,34 @@ __global__ __launch_bounds__(kSlabThreads) void slab_kernel(const bf16_t *__rest
     // Token slab: row t (tokens past T repeat token T - 1), chunk g of the
     // slab's 64 KC columns at slot (g & ~15) | ((g ^ t) & 15); the lo half
     // after the hi half.  Copy instruction j fills slab bytes [1 KB j, 1 KB j + 1 KB).
+    constexpr int NJC = NORM ? NJ / 2 : NJ;  // NORM: only the hi half is copied (h)
+    constexpr int NJCW = (NJC + kSlabWaves - 1) / kSlabWaves;
+    unsigned char *lo_half = smem + SLAB / 2;
 #pragma unroll
-    for (int jj = 0; jj < NJW; ++jj) {
-        const int j = min(wave + kSlabWaves * jj, NJ - 1);  // the last instruction may be repeated (same bytes)
+    for (int jj = 0; jj < NJCW; ++jj) {
+        const int j = min(wave + kSlabWaves * jj, NJC - 1);  // the last instruction may be repeated (same bytes)
         const int u = j * 64 + lane, part = u / (T16 * CPR), rem = u % (T16 * CPR), t = rem / CPR, slot = rem % CPR;
         const int g = (slot & ~15) | ((slot ^ t) & 15);
         slab_copy((part ? X_lo : X) + (size_t)min(t, T - 1) * ldx + k0 + 8 * g, smem + (size_t)j * 1024);
+    }
+    if (NORM) {
+        // The gains of the slab's columns (lo half, bytes 0 .. 2 KB) and the
+        // tokens' chunk sums (lo half, bytes 2 KB .. 4 KB), until the lo half
+        // is written below.
+        if (wave == 0) {
+#pragma unroll
+            for (int i = 0; i < (KR * 2 + 1023) / 1024; ++i)
+                slab_copy(norm_g + k0 + 8 * min(64 * i + lane, CPR - 1), lo_half + 1024 * i);
+        } else if (wave == 1) {
+            const int per_tok = stats_stride / 4;  // 16-byte pieces per token
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int q = 64 * i + lane, tq = q / per_tok, pq = q % per_tok;
+                if (i * 64 < T16 * per_tok)
+                    slab_copy(reinterpret_cast<const bf16_t *>(norm_stats + (size_t)min(tq, T - 1) * stats_stride + 4 * pq),
+                              lo_half + 2048 + 1024 * i);
+            }
+        }
     }
     __builtin_amdgcn_sched_barrier(0);  // the token copies stay ahead of the ring's (the waits count them)
     // Ring stage s: this wave's row tile s / KC, columns 64 (s % KC) .. + 63;
@@ -426,6 +458,57 @@ __global__ __launch_bounds__(kSlabThreads) void slab_kernel(const bf16_t *__rest
     slab_wait(2 * (NS - 1 < S ? NS - 1 : S));  // this wave's token copies have landed
     __builtin_amdgcn_s_barrier();               // ... and every wave's
     __builtin_amdgcn_sched_barrier(0);
+    if (NORM) {
+        // h -> RMSNorm(h; g) as hi (in place) + lo.  The gains and scales of
+        // this thread's slots are read before any lo store (they live
+        // there); every LDS read of a phase is issued before the first use.
+        constexpr int SLOTS = T16 * CPR, PER = (SLOTS + kSlabThreads - 1) / kSlabThreads;
+        const int nch = norm_chunks(K);
+        const unsigned char *stb = lo_half + 2048;
+        u32x4 gv[PER];
+        f32x4 s0[PER], s1[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int j = min((int)threadIdx.x + kSlabThreads * m, SLOTS - 1), t = j / CPR, sl = j % CPR;
+            const int g = (sl & ~15) | ((sl ^ t) & 15);
+            gv[m] = *reinterpret_cast<const u32x4 *>(lo_half + 16 * g);
+            // chunk sums 0-3 and 4-7 (with 4 per token the second read is the
+            // next token's and unused)
+            s0[m] = *reinterpret_cast<const f32x4 *>(stb + (size_t)t * stats_stride * 4);
+            s1[m] = *reinterpret_cast<const f32x4 *>(stb + (size_t)t * stats_stride * 4 + 16);
+        }
+        float rv[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            float tot = 0.f;
+#pragma unroll
+            for (int c = 0; c < kNormMaxChunks; ++c)
+                if (c < nch) tot += c < 4 ? s0[m][c] : s1[m][c - 4];
+            rv[m] = norm_scale(tot, K, eps);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        u32x4 xv[PER];
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int j = min((int)threadIdx.x + kSlabThreads * m, SLOTS - 1);
+            xv[m] = *reinterpret_cast<const u32x4 *>(smem + (size_t)(j / CPR) * KR * 2 + 16 * (j % CPR));
+        }
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int j = (int)threadIdx.x + kSlabThreads * m;
+            if (j >= SLOTS) break;
+            const size_t off = (size_t)(j / CPR) * KR * 2 + 16 * (j % CPR);
+            u32x2 h0, l0, h1, l1;
+            norm_apply4((u32x2){xv[m][0], xv[m][1]}, (u32x2){gv[m][0], gv[m][1]}, rv[m], h0, l0);
+            norm_apply4((u32x2){xv[m][2], xv[m][3]}, (u32x2){gv[m][2], gv[m][3]}, rv[m], h1, l1);
+            *reinterpret_cast<u32x4 *>(smem + off) = (u32x4){h0[0], h0[1], h1[0], h1[1]};
+            *reinterpret_cast<u32x4 *>(lo_half + off) = (u32x4){l0[0], l0[1], l1[0], l1[1]};
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the pair is in LDS before any wave reads it
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     const int aslot = col * 128;                          // + 16 * (g ^ ((col >> 1) & 7))
     const unsigned char *bbase = smem + (size_t)col * KR * 2;  // token row col of tile 0
@@ -554,6 +637,37 @@ __global__ __launch_bounds__(256) void slab_swiglu_finish_kernel(const float *__
             (u32x2){(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
 }
 
+// The residual finishing pass of the slab product that also leaves the next
+// sublayer's RMSNorm statistics: one workgroup per (1024-column chunk, token
+// row); h_new = bf16(h + Σ partials) as in slab_finish_kernel, and the
+// chunk's sum of squares of h_new (order of norm_order.hpp) in
+// stats[t · stride + chunk].
+__global__ __launch_bounds__(kNormThreads) void slab_resid_stats_kernel(const float *__restrict__ partials, int ks,
+                                                                        int T, int N, bf16_t *__restrict__ h, int ldo,
+                                                                        float *__restrict__ stats, int stride) {
+    __shared__ float red[kNormThreads / 64];
+    const int c = blockIdx.x, t = blockIdx.y, n = kNormChunk * c + 4 * threadIdx.x;
+    float ss = 0.f;
+    if (n < N) {
+        f32x4 pv[kSlabMaxSplits];
+#pragma unroll
+        for (int s = 0; s < kSlabMaxSplits; ++s)
+            if (s < ks) pv[s] = *reinterpret_cast<const f32x4 *>(partials + ((size_t)s * T + t) * N + n);
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kSlabMaxSplits; ++s)
+            if (s < ks) v += pv[s];
+        bf16_t *hp = h + (size_t)t * ldo + n;
+        const u32x2 hv = *reinterpret_cast<const u32x2 *>(hp);
+        const u32x2 hn = {(uint32_t)f32_to_bf16(lo_bf16(hv[0]) + v[0]) | ((uint32_t)f32_to_bf16(hi_bf16(hv[0]) + v[1]) << 16),
+                          (uint32_t)f32_to_bf16(lo_bf16(hv[1]) + v[2]) | ((uint32_t)f32_to_bf16(hi_bf16(hv[1]) + v[3]) << 16)};
+        *reinterpret_cast<u32x2 *>(hp) = hn;
+        ss = norm_sq4(hn);
+    }
+    const float cs = norm_chunk_sum(ss, red);
+    if (threadIdx.x == 0) stats[(size_t)t * stride + c] = cs;
+}
+
 size_t stream_lds_bytes(int R, int KS, int RT, int TB) {
     const size_t units = (size_t)R * KS * 4, instr = (units + 63) / 64;
     const size_t copy = (size_t)kStreamWaves * instr * 1024;
@@ -607,65 +721,42 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(const float *__restr
 
 // K-split finishing of a residual product fused with the next sublayer's
 // RMSNorm: one workgroup per token row sums the slices in slice order, stores
-// h_new = bf16(h + Σ) and writes RMSNorm(h_new; g) as a bf16 hi + lo pair.
-// The norm's loop structure and reduction order are those of the standalone
-// RMSNorm kernel, so both give the same bits.
-__global__ __launch_bounds__(256) void resid_norm_finish_kernel(const float *__restrict__ partials, int splits,
-                                                                 int T, int N, bf16_t *__restrict__ h, int ldo,
-                                                                 const bf16_t *__restrict__ g, float eps,
-                                                                 bf16_t *__restrict__ xn, bf16_t *__restrict__ xn_lo) {
-    __shared__ float red[4];
-    const int t = blockIdx.x;
+// h_new = bf16(h + Σ) and writes RMSNorm(h_new; g) as a bf16 hi + lo pair,
+// the sum of squares in the order of norm_order.hpp (the same bits as the
+// standalone RMSNorm kernel).  Four columns per thread per 1024-column chunk.
+__global__ __launch_bounds__(kNormThreads) void resid_norm_finish_kernel(
+    const float *__restrict__ partials, int splits, int T, int N, bf16_t *__restrict__ h, int ldo,
+    const bf16_t *__restrict__ g, float eps, bf16_t *__restrict__ xn, bf16_t *__restrict__ xn_lo) {
+    __shared__ float red[kNormThreads / 64];
+    const int t = blockIdx.x, nch = norm_chunks(N);
     bf16_t *hr = h + (size_t)t * ldo;
-    const int nvec = N / 8;
-    float ss = 0.f;
-    for (int v = threadIdx.x; v < nvec; v += 256) {
-        const int n = 8 * v;
-        float acc[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-        for (int sl = 0; sl < splits; ++sl) {
-            const float *p = partials + ((size_t)sl * T + t) * N + n;
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[e] += a[e];
-                acc[4 + e] += b[e];
-            }
-        }
-        const u32x4 hv = ld16(hr + n);
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bf16_t h0 = f32_to_bf16(lo_bf16(hv[e]) + acc[2 * e]);
-            const bf16_t h1 = f32_to_bf16(hi_bf16(hv[e]) + acc[2 * e + 1]);
-            o[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            const float a = bf16_to_f32(h0), b = bf16_to_f32(h1);
-            ss += a * a + b * b;
-        }
-        *reinterpret_cast<u32x4 *>(hr + n) = o;
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
+    u32x2 hn[kNormMaxChunks];
     float tot = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) tot += red[w];
-    const float r = 1.f / sqrtf(tot / (float)N + eps);
-    for (int v = threadIdx.x; v < nvec; v += 256) {
-        const u32x4 x = ld16(hr + 8 * v), gv = ld16(g + 8 * v);  // this thread's own stores above
-        u32x4 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float y0 = lo_bf16(x[e]) * r * lo_bf16(gv[e]);
-            const float y1 = hi_bf16(x[e]) * r * hi_bf16(gv[e]);
-            const bf16_t h0 = f32_to_bf16(y0), h1 = f32_to_bf16(y1);
-            hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lo[e] = pack_bf16x2(y0 - bf16_to_f32(h0), y1 - bf16_to_f32(h1));
+    for (int c = 0; c < kNormMaxChunks; ++c) {
+        if (c >= nch) break;
+        const int n = kNormChunk * c + 4 * threadIdx.x;
+        float ss = 0.f;
+        if (n < N) {
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            for (int sl = 0; sl < splits; ++sl) v += *reinterpret_cast<const f32x4 *>(partials + ((size_t)sl * T + t) * N + n);
+            const u32x2 hv = *reinterpret_cast<const u32x2 *>(hr + n);
+            hn[c] = (u32x2){(uint32_t)f32_to_bf16(lo_bf16(hv[0]) + v[0]) | ((uint32_t)f32_to_bf16(hi_bf16(hv[0]) + v[1]) << 16),
+                            (uint32_t)f32_to_bf16(lo_bf16(hv[1]) + v[2]) | ((uint32_t)f32_to_bf16(hi_bf16(hv[1]) + v[3]) << 16)};
+            *reinterpret_cast<u32x2 *>(hr + n) = hn[c];
+            ss = norm_sq4(hn[c]);
         }
-        *reinterpret_cast<u32x4 *>(xn + (size_t)t * ldo + 8 * v) = hi;
-        *reinterpret_cast<u32x4 *>(xn_lo + (size_t)t * ldo + 8 * v) = lo;
+        tot += norm_chunk_sum(ss, red);
+    }
+    const float r = norm_scale(tot, N, eps);
+#pragma unroll
+    for (int c = 0; c < kNormMaxChunks; ++c) {
+        const int n = kNormChunk * c + 4 * threadIdx.x;
+        if (c >= nch || n >= N) continue;
+        u32x2 hi, lo;
+        norm_apply4(hn[c], *reinterpret_cast<const u32x2 *>(g + n), r, hi, lo);
+        *reinterpret_cast<u32x2 *>(xn + (size_t)t * ldo + n) = hi;
+        *reinterpret_cast<u32x2 *>(xn_lo + (size_t)t * ldo + n) = lo;
     }
 }
 
@@ -774,7 +865,7 @@ hipError_t launch_gemv(const SkinnyArgs &a, hipStream_t stream) {
 template <int EPI>
 hipError_t launch_finish(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
     if (EPI == EPI_RESID && skinny_fuses_norm(a, p)) {
-        hipLaunchKernelGGL(resid_norm_finish_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, partials, p.k_splits,
+        hipLaunchKernelGGL(resid_norm_finish_kernel, dim3((unsigned)a.T), dim3(kNormThreads), 0, stream, partials, p.k_splits,
                            a.T, a.N, static_cast<bf16_t *>(a.out), a.ldo, a.next_norm, a.eps, a.next_x,
                            a.next_x_lo);
         return hipGetLastError();
@@ -877,22 +968,29 @@ hipError_t launch_stream(const SkinnyArgs &a, const SkinnyPlan &p, float *partia
                               : launch_stream0<1>(a, p, partials, stream, KS);
 }
 
-template <int RTW, int TB, int KC, bool XLO>
+template <int RTW, int TB, int KC, bool XLO, bool NORM = false>
 hipError_t launch_slab4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
     const bool dual = a.epi == EPI_SWIGLU;
     const int Nrows = dual ? 2 * a.N : a.N;
     const size_t lds = slab_token_bytes(TB, KC, XLO) + (size_t)kSlabWaves * slab_stages(TB, KC, XLO) * 2048;
-    static const hipError_t attr = hipFuncSetAttribute((const void *)slab_kernel<RTW, TB, KC, XLO>,
+    static const hipError_t attr = hipFuncSetAttribute((const void *)slab_kernel<RTW, TB, KC, XLO, NORM>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSlabLdsMax);
     if (attr != hipSuccess) return attr;
     const dim3 grid((Nrows + 128 * RTW - 1) / (128 * RTW), p.k_splits);
     {
         TimingScope ts(kTimeSkinny, stream);
-        hipLaunchKernelGGL((slab_kernel<RTW, TB, KC, XLO>), grid, dim3(kSlabThreads), lds, stream, a.X, a.X_lo, a.ldx,
-                           a.W, dual ? a.W_b : a.W, a.N, Nrows, a.K, a.T, partials);
+        hipLaunchKernelGGL((slab_kernel<RTW, TB, KC, XLO, NORM>), grid, dim3(kSlabThreads), lds, stream, a.X, a.X_lo,
+                           a.ldx, a.W, dual ? a.W_b : a.W, a.N, Nrows, a.K, a.T, partials, a.norm_g, a.norm_stats,
+                           norm_stats_stride(a.K), a.norm_eps);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.epi == EPI_RESID && a.stats_out) {
+        hipLaunchKernelGGL(slab_resid_stats_kernel, dim3((unsigned)norm_chunks(a.N), (unsigned)a.T), dim3(kNormThreads),
+                           0, stream, partials, p.k_splits, a.T, a.N, static_cast<bf16_t *>(a.out), a.ldo, a.stats_out,
+                           norm_stats_stride(a.N));
+        return hipGetLastError();
+    }
     const unsigned blocks = (unsigned)(((size_t)a.T * (a.N / 4) + 255) / 256);
     switch (a.epi) {
         case EPI_SWIGLU:
@@ -921,6 +1019,10 @@ hipError_t launch_slab4(const SkinnyArgs &a, const SkinnyPlan &p, float *partial
 
 template <int RTW, int TB, int KC>
 hipError_t launch_slab3(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
+    if (a.norm_g) {
+        if constexpr (slab_stages(TB, KC, true) >= 3) return launch_slab4<RTW, TB, KC, true, true>(a, p, partials, stream);
+        return hipErrorInvalidValue;
+    }
     if (a.X_lo) {
         if constexpr (slab_stages(TB, KC, true) >= 3) return launch_slab4<RTW, TB, KC, true>(a, p, partials, stream);
         return hipErrorInvalidValue;
@@ -957,17 +1059,22 @@ hipError_t launch_slab(const SkinnyArgs &a, const SkinnyPlan &p, float *partials
     if (a.out_tiled || (dual && !a.W_b) || !slab_fits(a.T, dual ? 2 * a.N : a.N, a.K, a.ldx, a.x_tiled, p) ||
         a.N % 4 != 0 || a.ldo % 4 != 0 || (a.epi == EPI_GATE && a.ldaux % 4 != 0))
         return hipErrorInvalidValue;
+    if (a.norm_g && (a.X_lo || !a.norm_stats || a.K % 4 != 0 || norm_chunks(a.K) > kNormMaxChunks))
+        return hipErrorInvalidValue;
+    if (a.stats_out && (a.epi != EPI_RESID || norm_chunks(a.N) > kNormMaxChunks)) return hipErrorInvalidValue;
     return stream_tb(a.T) == 2 ? launch_slab2<2>(a, p, partials, stream) : launch_slab2<4>(a, p, partials, stream);
 }
 
 // The slab plan of least modelled time: per workgroup, its weights, its token
 // slab (16-token tiles, hi + lo) and its partial rows at ~38 GB/s per CU (in
 // rounds of 256 workgroups), against all weights at ~6 TB/s, plus the
-// partials written and read again at ~6 TB/s.  Taken for a hi + lo token
-// operand above 16 tokens and for any operand above 32 (a plain bf16 one at
-// 17-32 tokens measured faster in the LDS-streaming product, whose gate
-// output needs no finishing pass); none for outputs whose rows are not a
-// multiple of 4.  SAMBAY_NO_SLAB=1 turns it off.
+// partials written and read again at ~6 TB/s.  Taken above 16 tokens for a
+// hi + lo token operand and for any operand above 32 tokens: a plain bf16
+// operand at 17-32 tokens measured faster in the LDS-streaming product (the
+// 32-token GMU: 23.7 us against 26.3 us with the slab product taking its
+// K = 6144 output product, the hidden then no longer in the tiled layout);
+// none for outputs whose rows are not a multiple of 4.  SAMBAY_NO_SLAB=1
+// turns it off.
 bool slab_plan(int T, int Nrows, int K, bool xlo, SkinnyPlan &p) {
     static const bool off = [] {
         const char *e = getenv("SAMBAY_NO_SLAB");
@@ -1052,6 +1159,11 @@ hipError_t launch1(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hi
 }
 
 }  // namespace
+
+bool slab_norm_ok(int T, int Nrows, int K) {
+    SkinnyPlan p;
+    return !norm_fusion_off() && K % 4 == 0 && norm_chunks(K) <= kNormMaxChunks && slab_plan(T, Nrows, K, true, p);
+}
 
 SkinnyPlan skinny_plan(int T, int N, int K, bool xlo) {
     // The LDS-streaming product (2-64 tokens) first: the smallest K split
@@ -1146,12 +1258,15 @@ size_t skinny_partial_bytes_dual(int T, int N, const SkinnyPlan &p) {
     return p.k_splits > 1 ? (size_t)p.k_splits * T * 2 * N * sizeof(float) : 0;
 }
 
-bool skinny_fuses_norm(const SkinnyArgs &a, const SkinnyPlan &p) {
+bool norm_fusion_off() {
     // SAMBAY_NO_NORM_FUSION=1 selects the separate RMSNorm launch instead (same bits).
     const char *env = getenv("SAMBAY_NO_NORM_FUSION");
-    const bool off = env && *env && *env != '0';
-    return !off && a.epi == EPI_RESID && p.k_splits > 1 && p.slab_rtw == 0 && a.next_norm && a.next_x && a.next_x_lo &&
-           a.ldo == a.N && a.N % 8 == 0;
+    return env && *env && *env != '0';
+}
+
+bool skinny_fuses_norm(const SkinnyArgs &a, const SkinnyPlan &p) {
+    return !norm_fusion_off() && a.epi == EPI_RESID && p.k_splits > 1 && p.slab_rtw == 0 && a.next_norm && a.next_x && a.next_x_lo &&
+           a.ldo == a.N && a.N % 4 == 0 && norm_chunks(a.N) <= kNormMaxChunks;
 }
 
 size_t skinny_partial_bytes(int T, int N, const SkinnyPlan &p) {
@@ -1170,6 +1285,7 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *par
     if ((a.x_tiled || a.out_tiled) && !skinny_tiles(a, plan)) return hipErrorInvalidValue;
     if (a.out_tiled && (a.epi != EPI_GATE || plan.k_splits != 1)) return hipErrorInvalidValue;
     if (plan.slab_rtw > 0) return launch_slab(a, plan, partials, stream);
+    if (a.norm_g || a.stats_out) return hipErrorInvalidValue;  // the deferred norm exists only in the slab product
     if (gemv_eligible(a) && plan.k_splits == 1) return launch_gemv(a, stream);
     if (const int ks = stream_ks(a, plan)) return launch_stream(a, plan, partials, stream, ks);
     if (a.epi == EPI_SWIGLU) {  // dual: row tiles in pairs, R <= 32 (skinny_plan_dual)

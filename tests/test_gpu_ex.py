@@ -223,6 +223,24 @@ def test_step_ex_prepared_replays_identically(sb):
     assert torch.equal(first, x.h)
 
 
+@pytest.mark.parametrize("B", [17, 40])
+def test_step_ex_deferred_norm_matches_separate_norm(sb, monkeypatch, B):
+    """d_model 768: above 16 tokens the residual products leave each token's
+    chunk sums of squares and the next sublayer's products normalise their
+    own K slab while staging it (no RMSNorm launch); the result must be the
+    same bits as materialising every RMSNorm by its own launch."""
+    x = workload.crossdecoder_ex_inputs(B, 768, 1536, 1536, 6, 2, 128, 300, 4, seed=60 + B, device=DEV,
+                                        lens="ragged")
+    h0 = x.h.clone()
+    sb.crossdecoder_step_ex(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+    fused = x.h.clone()
+    x.h.copy_(h0)
+    monkeypatch.setenv("SAMBAY_NO_NORM_FUSION", "1")
+    sb.crossdecoder_step_ex(x.h, x.M, x.K, x.V, x.layers, lens=x.lens)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, x.h)
+
+
 def test_step_ex_fused_norm_matches_separate_norm(sb, monkeypatch):
     """Above 16 tokens the next sublayer's RMSNorm is fused into the residual
     product's finishing pass; it must give the same bits as the separate
