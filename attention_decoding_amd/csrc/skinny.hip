@@ -1089,6 +1089,9 @@ bool slab_plan(int T, int Nrows, int K, bool xlo, SkinnyPlan &p) {
         const int ks = K / KR, R = 128 * sh.rtw;
         const double wgs = (double)((Nrows + R - 1) / R) * ks, rounds = (double)(int)((wgs + kTargetWGs - 1) / kTargetWGs);
         const double per_wg = (double)R * KR * 2 + 16.0 * TB * KR * 2 * (xlo ? 2 : 1) + (double)T * R * 4;
+        // (Bounding a CU's rate by the bytes its ring keeps in flight too
+        // picked deeper rings with twice the slabs: slower everywhere, e.g.
+        // the 64-token GMU 32.0 -> 40.5 us.)
         const double t_cu = rounds * per_wg / 38e3, t_hbm = (double)Nrows * K * 2 / 6e6;
         const double t = (t_cu > t_hbm ? t_cu : t_hbm) + 2.0 * ks * T * Nrows * 4 / 6e6;
         if (t < best) {
@@ -1106,9 +1109,11 @@ template <int RT, int TB, int EPI, bool XLO, bool DUAL = false>
 hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
     // Chunks in flight per wave: operand registers U·8·(RT + TB·(1 + XLO)) <= ~160.
     // The dual SwiGLU pass keeps one chunk in flight and two workgroups per
-    // CU instead (at 32 tokens: 122 registers against 185, its 512
-    // workgroups in one round instead of two; 34.9 -> ~30.5 us per 100.7 MB
-    // launch, the whole-model decode step 10.19 -> 10.04 ms).
+    // CU instead.  That was measured at 32 tokens (122 registers against
+    // 185, its 512 workgroups in one round instead of two; 34.9 -> ~30.5 us
+    // per 100.7 MB launch), where the slab product has since taken over;
+    // here it serves 2-16 tokens (one token tile, fewer registers still),
+    // where the choice was kept without a separate measurement.
     constexpr int U0 = 20 / (RT + TB * (XLO ? 2 : 1)) < 1 ? 1 : 20 / (RT + TB * (XLO ? 2 : 1));
     constexpr int U = DUAL ? 1 : U0;
     constexpr int MINB = DUAL ? 2 : 1;
