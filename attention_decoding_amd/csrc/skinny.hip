@@ -437,10 +437,12 @@ __global__ __launch_bounds__(kSlabThreads) void slab_kernel(const bf16_t *__rest
         }
     }
     __builtin_amdgcn_sched_barrier(0);  // the token copies stay ahead of the ring's (the waits count them)
-    // Ring stage s: this wave's row tile s / KC, columns 64 (s % KC) .. + 63;
-    // row r's eight chunks at r·128 + 16·(g ^ ((r >> 1) & 7)).
+    // Ring stage s: this wave's row tile s % RTW, columns 64 (s / RTW) .. + 63
+    // (row tiles fastest, so the token operands of a 64-column step are read
+    // from LDS once for all of the wave's row tiles); row r's eight chunks at
+    // r·128 + 16·(g ^ ((r >> 1) & 7)).
     auto issue = [&](int s) {
-        const int rt = s / KC, kc = s % KC;
+        const int rt = s % RTW, kc = s / RTW;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int r = 8 * i + (lane >> 3), g = (lane & 7) ^ ((r >> 1) & 7);
@@ -512,9 +514,12 @@ __global__ __launch_bounds__(kSlabThreads) void slab_kernel(const bf16_t *__rest
 
     const int aslot = col * 128;                          // + 16 * (g ^ ((col >> 1) & 7))
     const unsigned char *bbase = smem + (size_t)col * KR * 2;  // token row col of tile 0
-    f32x4 acc[TB];
+    f32x4 acc[RTW][TB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) acc[tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    u32x4 bh[2][TB], bl[2][XLO ? TB : 1];  // the current 64-column step's token operands
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int after = (NS - 2 < S - 1 - s) ? NS - 2 : S - 1 - s;
@@ -522,31 +527,41 @@ __global__ __launch_bounds__(kSlabThreads) void slab_kernel(const bf16_t *__rest
         __builtin_amdgcn_wave_barrier();
         if (s + NS - 1 < S) issue(s + NS - 1);  // into the slot stage s - 1 used
         const unsigned char *st = ring + (size_t)(s % NS) * 2048 + aslot;
-        const int kc = s % KC;
+        const int rt = s % RTW, kc = s / RTW;
+        if (rt == 0) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int g = 4 * (2 * kc + q) + grp;
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const int t = 16 * tb + col;
+                    const size_t bo = (size_t)tb * 16 * KR * 2 + 16 * ((g & ~15) | ((g ^ t) & 15));
+                    bh[q][tb] = *reinterpret_cast<const u32x4 *>(bbase + bo);
+                    if (XLO) bl[q][XLO ? tb : 0] = *reinterpret_cast<const u32x4 *>(bbase + SLAB / 2 + bo);
+                }
+            }
+        }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int g = 4 * (2 * kc + q) + grp;
             const u32x4 a = *reinterpret_cast<const u32x4 *>(st + 16 * ((4 * q + grp) ^ ((col >> 1) & 7)));
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
-                const int t = 16 * tb + col;
-                const size_t bo = (size_t)tb * 16 * KR * 2 + 16 * ((g & ~15) | ((g ^ t) & 15));
-                acc[tb] = mfma16x16x32(a, *reinterpret_cast<const u32x4 *>(bbase + bo), acc[tb]);
-                if (XLO) acc[tb] = mfma16x16x32(a, *reinterpret_cast<const u32x4 *>(bbase + SLAB / 2 + bo), acc[tb]);
-            }
-        }
-        if (kc == KC - 1) {
-            // acc[tb][e] = partial of row 16·rt + 4·grp + e, token 16·tb + col.
-            const int grow = row0 + 16 * (s / KC) + 4 * grp;
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const int t = 16 * tb + col;
-                if (t < T && grow < Nrows)
-                    *reinterpret_cast<f32x4 *>(partials + ((size_t)blockIdx.y * T + t) * Nrows + grow) = acc[tb];
-                acc[tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                acc[rt][tb] = mfma16x16x32(a, bh[q][tb], acc[rt][tb]);
+                if (XLO) acc[rt][tb] = mfma16x16x32(a, bl[q][XLO ? tb : 0], acc[rt][tb]);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+    }
+    // acc[rt][tb][e] = partial of row 16·rt + 4·grp + e of the wave's rows, token 16·tb + col.
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        const int grow = row0 + 16 * rt + 4 * grp;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int t = 16 * tb + col;
+            if (t < T && grow < Nrows)
+                *reinterpret_cast<f32x4 *>(partials + ((size_t)blockIdx.y * T + t) * Nrows + grow) = acc[rt][tb];
+        }
     }
 }
 
