@@ -32,7 +32,8 @@ namespace {
 
 constexpr int kConvThreads = 256;
 constexpr int kScanChannels = 64;  // channels per workgroup (one per lane)
-constexpr int kScanWaves = 4;      // tokens per workgroup (one per wave) from 4 tokens up
+constexpr int kScanWaves = 4;      // tokens per workgroup (one per wave) from 4 tokens up,
+constexpr int kScanWavesWide = 8;  // ... and from 8 tokens up
 constexpr int kMaxStates = 64;
 
 __device__ __forceinline__ float silu(float v) { return v / (1.f + expf(-v)); }
@@ -82,10 +83,12 @@ __global__ __launch_bounds__(kConvThreads) void mamba_conv_kernel(const float *_
 // 64 rows of W_dt are staged too, transposed to [pair of ranks][channel] so
 // that the lanes' reads of one rank pair hit consecutive banks (each row
 // serves 4 tokens); with TW = 1 (one token, no reuse) each lane reads its
-// own row from memory.  Every staging load of a thread is issued before its
-// first LDS store.  Then Δ from the row and δ; the NS states of (token,
-// channel) are updated in registers and written back; M (bf16) and
-// g = M·SiLU(z) (bf16 hi + lo).
+// own row from memory.  A thread's state, input and gate are loaded first,
+// so that their latency overlaps the staging and the step projection (every
+// workgroup is resident at once and runs the same phases); every staging
+// load of a thread is issued before its first LDS store.  Then Δ from the
+// row and δ; the NS states of (token, channel) are updated in registers and
+// written back; M (bf16) and g = M·SiLU(z) (bf16 hi + lo).
 template <int NS, int TW>
 __global__ __launch_bounds__(64 * TW) void mamba_scan_kernel(
     const float *__restrict__ xz, int ldxz, const float *__restrict__ u, const float *__restrict__ xdbl, int P, int R,
@@ -100,23 +103,43 @@ __global__ __launch_bounds__(64 * TW) void mamba_scan_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c0 = blockIdx.x * kScanChannels, t0 = blockIdx.y * TW;
     const int nchunk = R / 8;  // 8 ranks (16 bytes) per chunk
+    const int c = c0 + lane, t = t0 + wave;
+    // Every global load first, with indices clamped to valid elements instead
+    // of conditions (threads past the last channel or token store nothing).
+    const int cc = min(c, d_inner - 1);
+    const size_t tc = (size_t)min(t, T - 1) * d_inner + cc;
+    f32x4 sv[NS / 4], alv[TW > 1 ? 1 : NS / 4];
+    {
+        const f32x4 *sp = reinterpret_cast<const f32x4 *>(ssm_state + tc * NS);
+#pragma unroll
+        for (int q = 0; q < NS / 4; ++q) sv[q] = sp[q];
+        if (TW == 1) {
+            const f32x4 *ap = reinterpret_cast<const f32x4 *>(A_log + (size_t)cc * NS);
+#pragma unroll
+            for (int q = 0; q < NS / 4; ++q) alv[q] = ap[q];
+        }
+    }
+    const float uu = u[tc];
+    const float zz = xz[(size_t)min(t, T - 1) * ldxz + d_inner + cc];
+    const float dtb = dt_bias[cc], dpc = Dp[cc];
     {
         constexpr int kX = (TW * kMaxP + kThreads - 1) / kThreads;
         float xv[kX];
 #pragma unroll
         for (int k = 0; k < kX; ++k) {
             const int i = threadIdx.x + k * kThreads, tt = i / P, j = i - tt * P;
-            xv[k] = i < TW * P && t0 + tt < T ? xdbl[(size_t)(t0 + tt) * P + j] : 0.f;
+            xv[k] = xdbl[(size_t)min(t0 + tt, T - 1) * P + j];
         }
         if (TW > 1) {
             constexpr int kW = kMaxDtRank / 8 / TW;  // chunks per lane: chunk j = wave + TW·k of row lane
+            constexpr int kA = (NS + TW - 1) / TW;   // decay rates per lane: state wave + TW·k of channel lane
             u32x4 wv[kW];
-            const bf16_t *row = W_dt + (size_t)(c0 + lane) * R;
+            float al[kA];
+            const bf16_t *row = W_dt + (size_t)cc * R;
 #pragma unroll
-            for (int k = 0; k < kW; ++k) {
-                const int j = wave + TW * k;
-                wv[k] = j < nchunk && c0 + lane < d_inner ? ld16(row + 8 * j) : (u32x4){0u, 0u, 0u, 0u};
-            }
+            for (int k = 0; k < kW; ++k) wv[k] = ld16(row + 8 * min(wave + TW * k, nchunk - 1));
+#pragma unroll
+            for (int k = 0; k < kA; ++k) al[k] = A_log[(size_t)cc * NS + min(wave + TW * k, NS - 1)];
 #pragma unroll
             for (int k = 0; k < kW; ++k) {
                 const int j = wave + TW * k;
@@ -124,9 +147,9 @@ __global__ __launch_bounds__(64 * TW) void mamba_scan_kernel(
 #pragma unroll
                     for (int e = 0; e < 4; ++e) wdt[4 * j + e][lane] = wv[k][e];
             }
-            // The decay rates, once per workgroup: wave w takes states w, w + TW, ...
-            if (c0 + lane < d_inner)
-                for (int n = wave; n < NS; n += TW) a2s[n][lane] = -expf(A_log[(size_t)(c0 + lane) * NS + n]) * kLog2e;
+#pragma unroll
+            for (int k = 0; k < kA; ++k)
+                if (wave + TW * k < NS) a2s[wave + TW * k][lane] = -expf(al[k]) * kLog2e;
         }
 #pragma unroll
         for (int k = 0; k < kX; ++k) {
@@ -135,11 +158,10 @@ __global__ __launch_bounds__(64 * TW) void mamba_scan_kernel(
         }
     }
     __syncthreads();
-    const int c = c0 + lane, t = t0 + wave;
     if (c >= d_inner || t >= T) return;  // no barrier below
 
     const float *xd = xds[wave];  // δ [R] | B [NS] | C [NS]
-    float a = dt_bias[c];
+    float a = dtb;
     if (TW > 1) {
         for (int r = 0; r < R / 2; ++r) {
             const uint32_t w = wdt[r][lane];
@@ -151,7 +173,7 @@ __global__ __launch_bounds__(64 * TW) void mamba_scan_kernel(
         for (int j0 = 0; j0 < nchunk; j0 += 8) {  // 8 chunks in flight
             u32x4 v[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = j0 + k < nchunk ? ld16(row + 8 * (j0 + k)) : (u32x4){0u, 0u, 0u, 0u};
+            for (int k = 0; k < 8; ++k) v[k] = ld16(row + 8 * min(j0 + k, nchunk - 1));
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 if (j0 + k < nchunk)
@@ -163,13 +185,10 @@ __global__ __launch_bounds__(64 * TW) void mamba_scan_kernel(
         }
     }
     const float dlt = a > 20.f ? a : log1pf(expf(a));  // softplus
-    const size_t tc = (size_t)t * d_inner + c;
-    const float uu = u[tc];
     float s[NS];
-    const f32x4 *sp = reinterpret_cast<const f32x4 *>(ssm_state + tc * NS);
 #pragma unroll
     for (int q = 0; q < NS / 4; ++q) {
-        const f32x4 v = sp[q];
+        const f32x4 v = sv[q];
         s[4 * q] = v[0];
         s[4 * q + 1] = v[1];
         s[4 * q + 2] = v[2];
@@ -179,16 +198,16 @@ __global__ __launch_bounds__(64 * TW) void mamba_scan_kernel(
     float m = 0.f;
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
-        const float a2 = TW > 1 ? a2s[n][lane] : -expf(A_log[(size_t)c * NS + n]) * kLog2e;
+        const float a2 = TW > 1 ? a2s[n][lane] : -expf(alv[TW > 1 ? 0 : n / 4][n % 4]) * kLog2e;
         s[n] = exp2_fast(dlt * a2) * s[n] + du * xd[R + n];  // exp(Δ·A) as 2^(Δ·A·log2 e)
         m += xd[R + NS + n] * s[n];
     }
     f32x4 *so = reinterpret_cast<f32x4 *>(ssm_state + tc * NS);
 #pragma unroll
     for (int q = 0; q < NS / 4; ++q) so[q] = (f32x4){s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
-    m += Dp[c] * uu;
+    m += dpc * uu;
     M_out[tc] = f32_to_bf16(m);
-    store_pair(g_hi, g_lo, tc, m * silu(xz[(size_t)t * ldxz + d_inner + c]));
+    store_pair(g_hi, g_lo, tc, m * silu(zz));
 }
 
 // ------------------------------------------------------------------ prefill
@@ -430,15 +449,17 @@ hipError_t launch_mamba_scan(const float *xz, int ldxz, const float *u, const fl
                              const bf16_t *W_dt, const float *dt_bias, const float *A_log, const float *Dp,
                              float *ssm_state, bf16_t *M_out, bf16_t *g_hi, bf16_t *g_lo, int T, int d_inner, int NS,
                              hipStream_t stream) {
-    // Four tokens per workgroup share its staged W_dt rows; below four tokens
-    // one wave per workgroup reads its rows directly.
-    const int TW = T >= kScanWaves ? kScanWaves : 1;
+    // Eight (from 8 tokens) or four (from 4) tokens per workgroup share its
+    // staged W_dt rows; below four tokens one wave per workgroup reads its
+    // rows directly.
+    const int TW = T >= kScanWavesWide ? kScanWavesWide : T >= kScanWaves ? kScanWaves : 1;
     const dim3 grid((unsigned)((d_inner + kScanChannels - 1) / kScanChannels), (unsigned)((T + TW - 1) / TW));
 #define SB_SCAN(N_, TW_)                                                                                             \
     hipLaunchKernelGGL((mamba_scan_kernel<N_, TW_>), grid, dim3(64 * TW_), 0, stream, xz, ldxz, u, xdbl, P, R, W_dt, \
                        dt_bias, A_log, Dp, ssm_state, M_out, g_hi, g_lo, T, d_inner)
-#define SB_SCAN_TW(N_)                    \
-    if (TW == kScanWaves) SB_SCAN(N_, 4); \
+#define SB_SCAN_TW(N_)                         \
+    if (TW == kScanWavesWide) SB_SCAN(N_, 8);  \
+    else if (TW == kScanWaves) SB_SCAN(N_, 4); \
     else SB_SCAN(N_, 1);
     switch (NS) {
         case 8: SB_SCAN_TW(8); break;
