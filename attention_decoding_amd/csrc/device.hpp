@@ -28,16 +28,26 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
-// Round to nearest, ties to even (NaN stays a quiet NaN).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
-}
+typedef __attribute__((ext_vector_type(2))) float f32x2v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+
+// Round to nearest, ties to even (NaN stays a NaN), by gfx950's packed
+// conversion (v_cvt_pk_bf16_f32): for every finite fp32 value it gives the
+// bits of the integer rounding u + 0x7fff + ((u >> 16) & 1) >> 16 (checked
+// over all 2^32 patterns), in one instruction per pair.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
+}
+
+// The low part of y's bf16 hi + lo pair: bf16(y - hi), hi = bf16(y), y as
+// rounded to fp32.  No multiply-add contraction here: fusing the subtraction
+// with the multiply that produced y would form lo from the unrounded product
+// in some kernels and not in others.
+__device__ __forceinline__ bf16_t split_lo(float y, bf16_t hi) {
+#pragma clang fp contract(off)
+    return f32_to_bf16(y - bf16_to_f32(hi));
 }
 
 // Low / high bf16 of a packed pair, widened to fp32.

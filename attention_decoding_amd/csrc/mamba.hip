@@ -41,7 +41,7 @@ __device__ __forceinline__ float silu(float v) { return v / (1.f + expf(-v)); }
 __device__ __forceinline__ void store_pair(bf16_t *hi, bf16_t *lo, size_t i, float v) {
     const bf16_t h = f32_to_bf16(v);
     hi[i] = h;
-    lo[i] = f32_to_bf16(v - bf16_to_f32(h));
+    lo[i] = split_lo(v, h);
 }
 
 // One thread per (token, channel): u = SiLU(conv_b + Σ_k conv_w[k]·window[k]),

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const bf16_t *__r
         const int n = kNormChunk * c + 4 * threadIdx.x;
         tot += norm_chunk_sum(n < d ? norm_sq4(xs[c]) : 0.f, red);
     }
-    const float r = norm_scale(tot, d, eps);
+    const float r = norm_scale(tot, 1.f / (float)d, eps);
 #pragma unroll
     for (int c = 0; c < kNormMaxChunks; ++c) {
         const int n = kNormChunk * c + 4 * threadIdx.x;

@@ -7,7 +7,8 @@
 //  * the 64 lanes of a wave are summed by an xor butterfly, the four waves
 //    of the chunk in wave order;
 //  * the row's total adds the chunk sums in chunk order, from zero;
-//  * r = 1 / sqrt(total / d + eps), and x = (h · r) · g per column, stored
+//  * r = rsqrt(total · (1 / d) + eps) by the hardware reciprocal square
+//    root (v_rsq_f32, within 1 ulp), and x = (h · r) · g per column, stored
 //    as a bf16 hi + lo pair.
 #pragma once
 
@@ -46,11 +47,17 @@ __device__ __forceinline__ float norm_chunk_sum(float ss, float *red) {
     return c;
 }
 
-__device__ __forceinline__ float norm_scale(float total, int d, float eps) { return 1.f / sqrtf(total / (float)d + eps); }
+__device__ __forceinline__ float norm_scale(float total, float inv_d, float eps) {
+    return __builtin_amdgcn_rsqf(total * inv_d + eps);
+}
 
 // Four columns (two packed bf16 pairs of h and of the gain) normalised and
-// split into bf16 hi + lo pairs.
+// split into bf16 hi + lo pairs: y = (h · r) · g rounded to fp32, hi = bf16(y),
+// lo = bf16(y - hi).  No multiply-add contraction here: a fused
+// (h · r) · g - hi would form lo from the unrounded product in some kernels
+// and not in others.
 __device__ __forceinline__ void norm_apply4(u32x2 x, u32x2 g, float r, u32x2 &hi, u32x2 &lo) {
+#pragma clang fp contract(off)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const float y0 = lo_bf16(x[e]) * r * lo_bf16(g[e]);

@@ -61,7 +61,7 @@ __device__ __forceinline__ void apply_epilogue(float v, int t, int n, void *out,
         const float g = m * (v / (1.f + expf(-v)));
         const bf16_t hi = f32_to_bf16(g);
         reinterpret_cast<bf16_t *>(out)[o] = hi;
-        if (out_lo) out_lo[o] = f32_to_bf16(g - bf16_to_f32(hi));
+        if (out_lo) out_lo[o] = split_lo(g, hi);
     } else {
         bf16_t *h = reinterpret_cast<bf16_t *>(out);
         h[o] = f32_to_bf16(bf16_to_f32(h[o]) + v);
@@ -75,7 +75,7 @@ __device__ __forceinline__ void store_swiglu(float g, float v, int t, int n, voi
     const float u = (g / (1.f + expf(-g))) * v;
     const bf16_t hi = f32_to_bf16(u);
     reinterpret_cast<bf16_t *>(out)[o] = hi;
-    if (out_lo) out_lo[o] = f32_to_bf16(u - bf16_to_f32(hi));
+    if (out_lo) out_lo[o] = split_lo(u, hi);
 }
 
 // RT row tiles of 16, TB token tiles of 16, U chunks in flight per wave; XLO:
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(const bf16_t *__
             const bf16_t hi = f32_to_bf16(gv);
             const size_t o = tiled_index(t, n, ntiles);
             reinterpret_cast<bf16_t *>(out)[o] = hi;
-            if (out_lo) out_lo[o] = f32_to_bf16(gv - bf16_to_f32(hi));
+            if (out_lo) out_lo[o] = split_lo(gv, hi);
         } else {
             apply_epilogue<EPI>(v, t, n, out, ldo, out_lo, aux, ldaux);
         }
@@ -480,13 +480,14 @@ __global__ __launch_bounds__(kSlabThreads) void slab_kernel(const bf16_t *__rest
             s1[m] = *reinterpret_cast<const f32x4 *>(stb + (size_t)t * stats_stride * 4 + 16);
         }
         float rv[PER];
+        const float inv_k = 1.f / (float)K;
 #pragma unroll
         for (int m = 0; m < PER; ++m) {
             float tot = 0.f;
 #pragma unroll
             for (int c = 0; c < kNormMaxChunks; ++c)
                 if (c < nch) tot += c < 4 ? s0[m][c] : s1[m][c - 4];
-            rv[m] = norm_scale(tot, K, eps);
+            rv[m] = norm_scale(tot, inv_k, eps);
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(256) void slab_finish_kernel(const float *__restric
         for (int e = 0; e < 4; ++e) {
             const float g = mm[e] * (v[e] / (1.f + expf(-v[e])));
             hi[e] = f32_to_bf16(g);
-            lo[e] = f32_to_bf16(g - bf16_to_f32(hi[e]));
+            lo[e] = split_lo(g, hi[e]);
         }
         *reinterpret_cast<u32x2 *>(reinterpret_cast<bf16_t *>(out) + o) =
             (u32x2){(uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16)};
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(256) void slab_swiglu_finish_kernel(const float *__
     for (int e = 0; e < 4; ++e) {
         const float u = (g[e] / (1.f + expf(-g[e]))) * v[e];
         hi[e] = f32_to_bf16(u);
-        lo[e] = f32_to_bf16(u - bf16_to_f32(hi[e]));
+        lo[e] = split_lo(u, hi[e]);
     }
     const size_t o = (size_t)t * ldo + n;
     *reinterpret_cast<u32x2 *>(out + o) =
@@ -763,7 +764,7 @@ __global__ __launch_bounds__(kNormThreads) void resid_norm_finish_kernel(
         }
         tot += norm_chunk_sum(ss, red);
     }
-    const float r = norm_scale(tot, N, eps);
+    const float r = norm_scale(tot, 1.f / (float)N, eps);
 #pragma unroll
     for (int c = 0; c < kNormMaxChunks; ++c) {
         const int n = kNormChunk * c + 4 * threadIdx.x;
@@ -827,7 +828,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const bf16_t *__restrict__ X,
         const float g = pre * (acc / (1.f + expf(-acc)));
         const bf16_t hi = f32_to_bf16(g);
         reinterpret_cast<bf16_t *>(out)[n] = hi;
-        if (out_lo) out_lo[n] = f32_to_bf16(g - bf16_to_f32(hi));
+        if (out_lo) out_lo[n] = split_lo(g, hi);
     } else {
         reinterpret_cast<bf16_t *>(out)[n] = f32_to_bf16(pre + acc);
     }

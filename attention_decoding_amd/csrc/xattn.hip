@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 2) void xattn_split_kernel(const void *__
             for (int e = 0; e < 4; ++e) {
                 const bf16_t h0 = f32_to_bf16(f[2 * e]), h1 = f32_to_bf16(f[2 * e + 1]);
                 hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                lo[e] = pack_bf16x2(f[2 * e] - bf16_to_f32(h0), f[2 * e + 1] - bf16_to_f32(h1));
+                lo[e] = (uint32_t)split_lo(f[2 * e], h0) | ((uint32_t)split_lo(f[2 * e + 1], h1) << 16);
             }
             qhi[t] = (u32x4){hi[0], hi[1], hi[2], hi[3]};
             qlo[t] = (u32x4){lo[0], lo[1], lo[2], lo[3]};
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 2) void xattn_split_kernel(const void *__
             const size_t oi = ((size_t)b * Hq + (size_t)g * G + hh) * kHeadDim + d;
             const bf16_t hi = f32_to_bf16(v);
             out[oi] = hi;
-            if (out_lo) out_lo[oi] = f32_to_bf16(v - bf16_to_f32(hi));
+            if (out_lo) out_lo[oi] = split_lo(v, hi);
         } else {
             const size_t pi = ((size_t)b * (DIFF ? 2 * Hq : Hq) + (size_t)g * NC + hh) * S + s;
             part_o[pi * kHeadDim + d] = o;
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(kHeadDim) void xattn_merge_kernel(const float2 *__r
     const float v = merge_column(part_ml + bh * S, part_o + bh * S * kHeadDim, Sb, d);
     const bf16_t hi = f32_to_bf16(v);
     out[bh * kHeadDim + d] = hi;
-    if (out_lo) out_lo[bh * kHeadDim + d] = f32_to_bf16(v - bf16_to_f32(hi));
+    if (out_lo) out_lo[bh * kHeadDim + d] = split_lo(v, hi);
 }
 
 // Differential attention, one workgroup per (sequence, query head): merge the
