@@ -560,13 +560,30 @@ bool mamba_dims_ok(int64_t B, int64_t d_model, int64_t d_inner, int64_t N, int64
 }
 
 
+// Deferred RMSNorms of the whole-model step, per token group of
+// kSkinnyMaxTokens rows.  in_deferred[g]: the group's input is RMSNorm(h;
+// norm_in) and the input product normalises its own K slab from h and the
+// chunk sums of squares in stats (no RMSNorm launch).  out_defer[g]: the
+// output product (a residual add into h) leaves the group's chunk sums in
+// stats for the next sublayer's norm.  stats: [token][stride] floats.
+struct DeferredNorms {
+    const bf16_t *h = nullptr;
+    const bf16_t *norm_in = nullptr;
+    const bool *in_deferred = nullptr;
+    const bool *out_defer = nullptr;
+    float *stats = nullptr;
+    int stride = 0;
+    float eps = 0.f;
+};
+
 // The decode step's launches for B sequences in token groups of <= 64 (the
 // arguments already validated): x may come with a low part x_lo (a bf16
-// hi + lo pair); out_epi EPI_BF16 stores y, EPI_RESID adds it into y_out (h).
+// hi + lo pair); out_epi EPI_BF16 stores y, EPI_RESID adds it into y_out (h);
+// dn (optional) defers the input's and the next sublayer's RMSNorm.
 hipError_t run_mamba_step(const bf16_t *x, const bf16_t *x_lo, const sb_mamba_weights *w, float *conv_state,
                           float *ssm_state, bf16_t *M_out, bf16_t *y_out, Epilogue out_epi, int64_t B,
                           int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank, int64_t d_conv,
-                          void *workspace, hipStream_t stream) {
+                          void *workspace, hipStream_t stream, const DeferredNorms *dn = nullptr) {
     const MambaLayout lay = mamba_layout(B, d_model, d_inner, d_state, dt_rank);
     const int64_t P = dt_rank + 2 * d_state;
     char *ws = reinterpret_cast<char *>(workspace);
@@ -578,9 +595,17 @@ hipError_t run_mamba_step(const bf16_t *x, const bf16_t *x_lo, const sb_mamba_we
     hipError_t e = hipSuccess;
     for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
         const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+        const int grp = (int)(t0 / kSkinnyMaxTokens);
         SkinnyArgs a;
         a.X = x + t0 * d_model;
         a.X_lo = x_lo ? x_lo + t0 * d_model : nullptr;
+        if (dn && dn->in_deferred && dn->in_deferred[grp]) {
+            a.X = dn->h + t0 * d_model;
+            a.X_lo = nullptr;
+            a.norm_g = dn->norm_in;
+            a.norm_stats = dn->stats + t0 * dn->stride;
+            a.norm_eps = dn->eps;
+        }
         a.ldx = dm;
         a.W = (const bf16_t *)w->w_in;
         a.T = T;
@@ -589,7 +614,7 @@ hipError_t run_mamba_step(const bf16_t *x, const bf16_t *x_lo, const sb_mamba_we
         a.epi = EPI_F32;
         a.out = xz;
         a.ldo = 2 * di;
-        const SkinnyPlan p_in = skinny_plan(T, 2 * di, dm, x_lo != nullptr);
+        const SkinnyPlan p_in = skinny_plan(T, 2 * di, dm, a.X_lo != nullptr || a.norm_g != nullptr);
         if (log_enabled() && t0 == 0)
             fprintf(stderr, "[sambay] SSM step B=%lld d_model=%d d_inner=%d N=%lld R=%lld K=%lld: in-proj %d k-splits\n",
                     (long long)B, dm, di, (long long)d_state, (long long)dt_rank, (long long)d_conv, p_in.k_splits);
@@ -627,6 +652,7 @@ hipError_t run_mamba_step(const bf16_t *x, const bf16_t *x_lo, const sb_mamba_we
         o.epi = out_epi;
         o.out = y_out + t0 * d_model;
         o.ldo = dm;
+        if (dn && dn->out_defer && dn->out_defer[grp]) o.stats_out = dn->stats + t0 * dn->stride;
         e = launch_skinny(o, skinny_plan(T, dm, di, true), part, stream);
     }
     return e;
@@ -1336,7 +1362,7 @@ namespace {
 // layer to layer), the cache lengths, then the SSM step's, the attention's
 // and the cross-decoder step's own regions.
 struct DecodeLayout {
-    size_t xn, xn_lo, q, kn, vn, o, o_lo, m, lens, lens_ring, hid, hid_lo, part, attn, ssm, cross, total;
+    size_t xn, xn_lo, q, kn, vn, o, o_lo, m, lens, lens_ring, hid, hid_lo, stats, part, attn, ssm, cross, total;
 };
 
 DecodeLayout decode_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank,
@@ -1357,6 +1383,7 @@ DecodeLayout decode_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t 
     l.lens_ring = c.used; c.take((size_t)B * 4);
     l.hid = c.used; c.take((size_t)T * (d_ff > 0 ? d_ff : 1) * 2);
     l.hid_lo = c.used; c.take((size_t)T * (d_ff > 0 ? d_ff : 1) * 2);
+    l.stats = c.used; c.take((size_t)B * norm_stats_stride(dm) * 4);
     size_t part = 0;
     const int shapes[][2] = {{dm, dm}, {kvd, dm}, {dm, df}};
     for (const auto &nk : shapes) {
@@ -1520,61 +1547,130 @@ extern "C" sb_status sambay_decode_step(void *h, void *M_out, const sb_self_laye
     bf16_t *hb = static_cast<bf16_t *>(h);
     const int dm = (int)d_model, kvi = (int)kvd, df = (int)d_ff;
 
-    // One weight-streaming product over every token group of <= 64 rows.
-    auto product = [&](const bf16_t *X, const bf16_t *X_lo, const void *W, int N, int K, Epilogue epi,
-                       bf16_t *out) -> hipError_t {
+    // A sublayer's input RMSNorm(h; g) is materialised in xn (hi + lo) by an
+    // RMSNorm launch, or deferred: the residual product that last wrote the
+    // group's rows of h left their chunk sums of squares in `stats`, and each
+    // product that reads the input normalises its own K slab while staging
+    // it (the slab product; the same bits as the RMSNorm kernel).  Deferred
+    // per token group of <= 64 rows when the residual product and every
+    // consumer of the input run as slab products; never for the first
+    // layer's input or the cross-decoder's.
+    float *stats = reinterpret_cast<float *>(w8 + lay.stats);
+    const int sstride = norm_stats_stride(dm), di = (int)d_inner;
+    constexpr int kMaxGroups = 64;
+    const int ngroups = (int)((B + kSkinnyMaxTokens - 1) / kSkinnyMaxTokens);
+    const bool may_defer = ngroups <= kMaxGroups;
+    bool deferred[kMaxGroups] = {};  // the pending norm's sums are in stats for the group
+    bool out_defer[kMaxGroups] = {};
+    auto group_T = [&](int gi) {
+        const int64_t t0 = (int64_t)gi * kSkinnyMaxTokens;
+        return (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+    };
+    // Whether every consumer of layer i's first (second) norm takes it deferred at T tokens.
+    auto takes_norm1 = [&](int32_t i, int T) {
+        if (i >= n_self || !self_layers[i].norm1) return false;
+        if (self_layers[i].kind == SB_SELF_MAMBA) return slab_norm_ok(T, 2 * di, dm);
+        return slab_norm_ok(T, dm, dm) && slab_norm_ok(T, kvi, dm);
+    };
+    auto takes_norm2 = [&](int32_t i, int T) {
+        return self_layers[i].w_gate && self_layers[i].norm2 && slab_norm_ok(T, 2 * df, dm);
+    };
+    // out_defer for a residual product of K columns whose next norm is taken when `takes` says so.
+    auto plan_defer = [&](int K, auto takes) {
+        for (int gi = 0; gi < ngroups; ++gi) {
+            const int T = group_T(gi);
+            out_defer[gi] = may_defer && takes(T) && skinny_plan(T, dm, K, true).slab_rtw > 0;
+        }
+    };
+    // RMSNorm(h; g) into xn for the groups whose norm is not deferred (one
+    // launch when none is).
+    auto materialise = [&](const void *g) -> hipError_t {
+        bool any = false;
+        for (int gi = 0; gi < ngroups; ++gi) any = any || deferred[gi];
+        if (!any) return launch_rmsnorm(hb, (const bf16_t *)g, (int)B, dm, eps, xn, xn_lo, stream);
         hipError_t e = hipSuccess;
-        for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
-            const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
-            SkinnyArgs a;
-            a.X = X + t0 * K; a.X_lo = X_lo ? X_lo + t0 * K : nullptr; a.ldx = K;
-            a.W = (const bf16_t *)W; a.T = T; a.N = N; a.K = K; a.epi = epi; a.out = out + t0 * N; a.ldo = N;
-            e = launch_skinny(a, skinny_plan(T, N, K, X_lo != nullptr), part, stream);
+        for (int gi = 0; gi < ngroups && e == hipSuccess; ++gi) {
+            const int64_t t0 = (int64_t)gi * kSkinnyMaxTokens;
+            if (!deferred[gi])
+                e = launch_rmsnorm(hb + t0 * dm, (const bf16_t *)g, group_T(gi), dm, eps, xn + t0 * dm,
+                                   xn_lo + t0 * dm, stream);
         }
         return e;
     };
+    // The operand of a product of group t0 whose input is RMSNorm(h; g) (g null: h itself).
+    auto operand = [&](SkinnyArgs &a, int64_t t0, const void *g) {
+        a.ldx = dm;
+        if (g && deferred[t0 / kSkinnyMaxTokens]) {
+            a.X = hb + t0 * dm; a.X_lo = nullptr;
+            a.norm_g = (const bf16_t *)g; a.norm_stats = stats + t0 * sstride; a.norm_eps = eps;
+        } else if (g) {
+            a.X = xn + t0 * dm; a.X_lo = xn_lo + t0 * dm;
+        } else {
+            a.X = hb + t0 * dm; a.X_lo = nullptr;
+        }
+    };
+    auto plan_of = [](const SkinnyArgs &a) { return skinny_plan(a.T, a.N, a.K, a.X_lo != nullptr || a.norm_g != nullptr); };
 
     hipError_t e = hipSuccess;
     for (int32_t li = 0; li < n_self && e == hipSuccess; ++li) {
         const sb_self_layer &ly = self_layers[li];
-        const bf16_t *X = hb, *X_lo = nullptr;
-        if (ly.norm1) {
-            if ((e = launch_rmsnorm(hb, (const bf16_t *)ly.norm1, (int)B, dm, eps, xn, xn_lo, stream)) != hipSuccess)
-                break;
-            X = xn; X_lo = xn_lo;
-        }
+        const bool mlp = ly.w_gate != nullptr;
+        if (ly.norm1 && (e = materialise(ly.norm1)) != hipSuccess) break;
+        // The sublayer after the mixer: the MLP's norm2, else the next layer's norm1.
+        auto takes_after_mixer = [&](int T) { return mlp ? takes_norm2(li, T) : takes_norm1(li + 1, T); };
         if (ly.kind == SB_SELF_MAMBA) {
-            e = run_mamba_step(X, X_lo, &ly.mamba, ly.conv_state, ly.ssm_state, mbuf, hb, EPI_RESID, B, d_model,
-                               d_inner, d_state, dt_rank, d_conv, ssm_ws, stream);
+            plan_defer(di, takes_after_mixer);
+            DeferredNorms dn;
+            dn.h = hb; dn.norm_in = (const bf16_t *)ly.norm1; dn.in_deferred = ly.norm1 ? deferred : nullptr;
+            dn.out_defer = out_defer; dn.stats = stats; dn.stride = sstride; dn.eps = eps;
+            e = run_mamba_step(ly.norm1 ? xn : hb, ly.norm1 ? xn_lo : nullptr, &ly.mamba, ly.conv_state,
+                               ly.ssm_state, mbuf, hb, EPI_RESID, B, d_model, d_inner, d_state, dt_rank, d_conv,
+                               ssm_ws, stream, &dn);
         } else {
             const bool swa = ly.kind == SB_SELF_SWA;
             const int slots = swa ? (int)window : (int)L;
             bf16_t *kc = static_cast<bf16_t *>(swa ? ly.kring : kcache);
             bf16_t *vc = static_cast<bf16_t *>(swa ? ly.vring : vcache);
             int32_t *ln = swa ? lens_ring : lens;
-            e = product(X, X_lo, ly.wq, dm, dm, EPI_BF16, q);
-            if (e == hipSuccess) e = product(X, X_lo, ly.wk, kvi, dm, EPI_BF16, kn);
-            if (e == hipSuccess) e = product(X, X_lo, ly.wv, kvi, dm, EPI_BF16, vn);
+            // q, k and v of every token group (each product normalises its own slab when deferred).
+            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+                const void *ws[3] = {ly.wq, ly.wk, ly.wv};
+                bf16_t *outs[3] = {q, kn, vn};
+                const int ns[3] = {dm, kvi, kvi};
+                for (int j = 0; j < 3 && e == hipSuccess; ++j) {
+                    SkinnyArgs a;
+                    operand(a, t0, ly.norm1);
+                    a.W = (const bf16_t *)ws[j]; a.T = T; a.N = ns[j]; a.K = dm; a.epi = EPI_BF16;
+                    a.out = outs[j] + t0 * ns[j]; a.ldo = ns[j];
+                    e = launch_skinny(a, plan_of(a), part, stream);
+                }
+            }
             if (e == hipSuccess)
                 e = launch_kv_append(kn, vn, kc, vc, pos, ln, (int)B, (int)Hkv, slots, swa ? (int)window : 0,
                                      stream);
             if (e == hipSuccess)
                 e = launch_xattn(q, false, kc, vc, ln, o, o_lo, (int)B, (int)Hq, (int)Hkv, slots, scale,
                                  xattn_plan(B, Hkv, slots, true), attn_part, stream);
-            if (e == hipSuccess) e = product(o, o_lo, ly.wo, dm, dm, EPI_RESID, hb);
+            plan_defer(dm, takes_after_mixer);
+            for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
+                const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+                SkinnyArgs a;
+                a.X = o + t0 * dm; a.X_lo = o_lo + t0 * dm; a.ldx = dm; a.W = (const bf16_t *)ly.wo; a.T = T;
+                a.N = dm; a.K = dm; a.epi = EPI_RESID; a.out = hb + t0 * dm; a.ldo = dm;
+                if (out_defer[t0 / kSkinnyMaxTokens]) a.stats_out = stats + t0 * sstride;
+                e = launch_skinny(a, skinny_plan(T, dm, dm, true), part, stream);
+            }
         }
-        if (e != hipSuccess || !ly.w_gate) continue;
-        const bf16_t *Xm = hb, *Xm_lo = nullptr;
-        if (ly.norm2) {
-            if ((e = launch_rmsnorm(hb, (const bf16_t *)ly.norm2, (int)B, dm, eps, xn, xn_lo, stream)) != hipSuccess)
-                break;
-            Xm = xn; Xm_lo = xn_lo;
-        }
+        for (int gi = 0; gi < ngroups; ++gi) deferred[gi] = out_defer[gi];
+        if (e != hipSuccess || !mlp) continue;
+        if (ly.norm2 && (e = materialise(ly.norm2)) != hipSuccess) break;
+        plan_defer(df, [&](int T) { return takes_norm1(li + 1, T); });
         // Token group by token group: hid = SiLU(x Wg^T) ⊙ (x Wu^T), h += hid Wd^T.
         for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
             const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
             SkinnyArgs a;
-            a.X = Xm + t0 * dm; a.X_lo = Xm_lo ? Xm_lo + t0 * dm : nullptr; a.ldx = dm;
+            operand(a, t0, ly.norm2);
             a.W = (const bf16_t *)ly.w_gate; a.W_b = (const bf16_t *)ly.w_up; a.T = T; a.N = df; a.K = dm;
             a.epi = EPI_SWIGLU; a.out = hid; a.ldo = df; a.out_lo = hid_lo;
             e = launch_skinny(a, skinny_plan_dual(T, df, dm), part, stream);
@@ -1582,8 +1678,10 @@ extern "C" sb_status sambay_decode_step(void *h, void *M_out, const sb_self_laye
             SkinnyArgs d;
             d.X = hid; d.X_lo = hid_lo; d.ldx = df; d.W = (const bf16_t *)ly.w_down; d.T = T; d.N = dm; d.K = df;
             d.epi = EPI_RESID; d.out = hb + t0 * dm; d.ldo = dm;
+            if (out_defer[t0 / kSkinnyMaxTokens]) d.stats_out = stats + t0 * sstride;
             e = launch_skinny(d, skinny_plan(T, dm, df, true), part, stream);
         }
+        for (int gi = 0; gi < ngroups; ++gi) deferred[gi] = out_defer[gi];
     }
     if (e != hipSuccess) return hip_fail(fn, e);
     if (n_cross == 0) return ok();

@@ -217,3 +217,52 @@ def test_decode_step_full_size_properties(sb):
     torch.cuda.synchronize()
     assert torch.equal(h1, h2) and torch.equal(m1, m2)
     assert torch.isfinite(h1.float()).all() and torch.isfinite(m1.float()).all()
+
+
+@pytest.mark.parametrize("B", [17, 40])
+def test_decode_step_deferred_norms_match_separate_norms(sb, monkeypatch, B):
+    """d_model 768, d_inner 1536, d_ff 1536, 6/2 heads: above 16 tokens the
+    self-decoder's residual products leave each token's chunk sums of
+    squares and the next sublayer's products (the SSM input projection, q, k
+    and v, the SwiGLU pair) normalise their own K slab (no RMSNorm launch).
+    The step must give the same bits as with every RMSNorm launched on its
+    own (SAMBAY_NO_NORM_FUSION=1): h, M, the cache rows, the rings and the
+    SSM states."""
+    W, L = 16, 64
+    inp = workload.sambay_prefill_inputs(B, 5, 768, 1536, 16, 64, 4, 1536, 6, 2, 128, W, L, SELF, CROSS,
+                                         seed=70 + B, device=DEV, fresh=False)
+    sb.sambay_prefill(inp.x, inp.self_layers, inp.cross_layers, inp.kcache, inp.vcache, window=W)
+    torch.cuda.synchronize()
+    saved = _snapshot(inp.self_layers)
+    Kb, Vb = inp.kcache.clone(), inp.vcache.clone()
+    x_new = workload.normal((B, 768), seed=80 + B, device=DEV)
+    pos = torch.full((B,), 5, dtype=torch.int32, device=DEV)
+
+    def run():
+        for ly, s0 in zip(inp.self_layers, saved):
+            for k in ("conv_state", "ssm_state", "kring", "vring"):
+                if k in ly:
+                    ly[k].copy_(s0[k].to(DEV))
+        inp.kcache.copy_(Kb)
+        inp.vcache.copy_(Vb)
+        h, M = sb.sambay_decode_step(x_new.clone(), pos, inp.self_layers, inp.cross_layers, inp.kcache, inp.vcache,
+                                     window=W)
+        torch.cuda.synchronize()
+        states = [ly[k].clone() for ly in inp.self_layers for k in ("conv_state", "ssm_state", "kring", "vring")
+                  if k in ly]
+        return [h.clone(), M.clone(), inp.kcache.clone(), inp.vcache.clone()] + states
+
+    print("case deferred norms B=%d" % B, flush=True)
+    fused = run()
+    monkeypatch.setenv("SAMBAY_NO_NORM_FUSION", "1")
+    separate = run()
+    assert len(fused) == len(separate)
+    for i, (a, b) in enumerate(zip(fused, separate)):
+        assert torch.equal(a, b), "output %d differs" % i
+
+
+def test_decode_step_deferred_norms_against_oracle(sb):
+    """17 sequences at d_model 768 (the deferred-norm path of the self- and
+    cross-decoder) against the oracle, to the bf16 bar."""
+    _case(sb, 17, 5, 16, 64, [5] * 17, seed=91, name="decode B=17 d_model 768 (deferred norms)", dm=768, di=1536,
+          dff=1536, Hq=6, Hkv=2)
