@@ -1385,7 +1385,7 @@ DecodeLayout decode_layout(int64_t B, int64_t d_model, int64_t d_inner, int64_t 
     l.hid_lo = c.used; c.take((size_t)T * (d_ff > 0 ? d_ff : 1) * 2);
     l.stats = c.used; c.take((size_t)B * norm_stats_stride(dm) * 4);
     size_t part = 0;
-    const int shapes[][2] = {{dm, dm}, {kvd, dm}, {dm, df}};
+    const int shapes[][2] = {{dm, dm}, {kvd, dm}, {dm + 2 * kvd, dm}, {dm, df}};
     for (const auto &nk : shapes) {
         if (nk[0] <= 0 || nk[1] <= 0) continue;
         const size_t v = skinny_partial_bytes_max(t, nk[0], nk[1]);
@@ -1570,7 +1570,7 @@ extern "C" sb_status sambay_decode_step(void *h, void *M_out, const sb_self_laye
     auto takes_norm1 = [&](int32_t i, int T) {
         if (i >= n_self || !self_layers[i].norm1) return false;
         if (self_layers[i].kind == SB_SELF_MAMBA) return slab_norm_ok(T, 2 * di, dm);
-        return slab_norm_ok(T, dm, dm) && slab_norm_ok(T, kvi, dm);
+        return slab_norm_ok(T, dm + 2 * kvi, dm);  // q, k and v as one stacked product
     };
     auto takes_norm2 = [&](int32_t i, int T) {
         return self_layers[i].w_gate && self_layers[i].norm2 && slab_norm_ok(T, 2 * df, dm);
@@ -1632,9 +1632,23 @@ extern "C" sb_status sambay_decode_step(void *h, void *M_out, const sb_self_laye
             bf16_t *kc = static_cast<bf16_t *>(swa ? ly.kring : kcache);
             bf16_t *vc = static_cast<bf16_t *>(swa ? ly.vring : vcache);
             int32_t *ln = swa ? lens_ring : lens;
-            // q, k and v of every token group (each product normalises its own slab when deferred).
+            // q, k and v of every token group: one stacked pass over the three
+            // weight matrices when the slab product takes it (the deferred
+            // norm only then), else three products.
             for (int64_t t0 = 0; t0 < B && e == hipSuccess; t0 += kSkinnyMaxTokens) {
                 const int T = (int)(B - t0 < kSkinnyMaxTokens ? B - t0 : kSkinnyMaxTokens);
+                SkinnyArgs s3;
+                operand(s3, t0, ly.norm1);
+                s3.W = (const bf16_t *)ly.wq; s3.W_b = (const bf16_t *)ly.wk; s3.W_c = (const bf16_t *)ly.wv;
+                s3.T = T; s3.N = dm + 2 * kvi; s3.K = dm; s3.epi = EPI_BF16;
+                s3.na = dm; s3.nb = dm + kvi;
+                s3.out = q + t0 * dm; s3.ldo = dm; s3.out_b = kn + t0 * kvi; s3.ldo_b = kvi;
+                s3.out_c = vn + t0 * kvi; s3.ldo_c = kvi;
+                const SkinnyPlan p3 = plan_of(s3);
+                if (p3.slab_rtw > 0 && kvi % 4 == 0) {
+                    e = launch_skinny(s3, p3, part, stream);
+                    continue;
+                }
                 const void *ws[3] = {ly.wq, ly.wk, ly.wv};
                 bf16_t *outs[3] = {q, kn, vn};
                 const int ns[3] = {dm, kvi, kvi};

@@ -131,8 +131,8 @@ struct SkinnyArgs {
     const bf16_t *X_lo = nullptr;  // optional low part: the product uses X + X_lo (a bf16 hi + lo pair)
     int ldx = 0;
     const bf16_t *W = nullptr;     // [N, K] bf16
-    const bf16_t *W_b = nullptr;   // EPI_SWIGLU only: the up weights [N, K]; W is then the gate (one pass, plan
-                                   // with skinny_plan_dual)
+    const bf16_t *W_b = nullptr;   // EPI_SWIGLU: the up weights [N, K]; W is then the gate (one pass, plan
+                                   // with skinny_plan_dual).  Stacked products: below
     int T = 0, N = 0, K = 0;
     Epilogue epi = EPI_F32;
     void *out = nullptr;           // [T, ldo]
@@ -164,6 +164,15 @@ struct SkinnyArgs {
     // EPI_RESID, slab product only: also write those chunk sums of h_new
     // ([T][norm_stats_stride(N)]) for the next sublayer's deferred norm.
     float *stats_out = nullptr;
+    // Stacked products (EPI_BF16, slab product only; na > 0): several
+    // products of one operand in one pass.  Output rows [0, na) come from W
+    // into out [T, ldo], rows [na, nb) from W_b (row n - na) into out_b
+    // [T, ldo_b], rows [nb, N) from W_c (row n - nb) into out_c [T, ldo_c];
+    // na, nb, the leading dimensions multiples of 4.
+    const bf16_t *W_c = nullptr;
+    int na = 0, nb = 0;
+    bf16_t *out_b = nullptr, *out_c = nullptr;
+    int ldo_b = 0, ldo_c = 0;
 };
 __host__ __device__ inline size_t tiled_index(int t, int k, int ntiles) {
     return ((size_t)(k >> 5) * ntiles + (t >> 4)) * 512 + ((k >> 3) & 3) * 128 + (t & 15) * 8 + (k & 7);

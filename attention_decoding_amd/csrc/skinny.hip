@@ -373,8 +373,10 @@ __device__ __forceinline__ void slab_copy(const bf16_t *g, unsigned char *lds) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, kStreamCopyPolicy);
 }
 
-// Rows [0, Na) of the Nrows come from W, rows [Na, Nrows) from W_b (the
-// SwiGLU pair: gate then up).  partials: fp32 [K / KR][T][Nrows].
+// Rows [0, Na) of the Nrows come from W, rows [Na, Nb) from W_b (row
+// n - Na), rows [Nb, Nrows) from W_c (row n - Nb): the SwiGLU pair (gate
+// then up; Nb = Nrows) or a stacked product (the attention layer's q, k and
+// v).  partials: fp32 [K / KR][T][Nrows].
 // NORM: X is the residual stream h and the operand is RMSNorm(h; g): the
 // h slab is copied in, together with the slab's gains and the tokens' chunk
 // sums of squares (stats [T][stride], left by the residual product that
@@ -384,7 +386,9 @@ template <int RTW, int TB, int KC, bool XLO, bool NORM = false>
 __global__ __launch_bounds__(kSlabThreads) void slab_kernel(const bf16_t *__restrict__ X,
                                                             const bf16_t *__restrict__ X_lo, int ldx,
                                                             const bf16_t *__restrict__ W,
-                                                            const bf16_t *__restrict__ W_b, int Na, int Nrows, int K,
+                                                            const bf16_t *__restrict__ W_b,
+                                                            const bf16_t *__restrict__ W_c, int Na, int Nb, int Nrows,
+                                                            int K,
                                                             int T, float *__restrict__ partials,
                                                             const bf16_t *__restrict__ norm_g,
                                                             const float *__restrict__ norm_stats, int stats_stride,
@@ -447,7 +451,9 @@ __global__ __launch_bounds__(kSlabThreads) void slab_kernel(const bf16_t *__rest
         for (int i = 0; i < 2; ++i) {
             const int r = 8 * i + (lane >> 3), g = (lane & 7) ^ ((r >> 1) & 7);
             const int row = min(row0 + 16 * rt + r, Nrows - 1);
-            const bf16_t *src = row < Na ? W + (size_t)row * K : W_b + (size_t)(row - Na) * K;
+            const bf16_t *src = row < Na   ? W + (size_t)row * K
+                                : row < Nb ? W_b + (size_t)(row - Na) * K
+                                           : W_c + (size_t)(row - Nb) * K;
             slab_copy(src + k0 + 64 * kc + 8 * g, ring + (size_t)(s % NS) * 2048 + i * 1024);
         }
     };
@@ -613,6 +619,30 @@ __global__ __launch_bounds__(256) void slab_finish_kernel(const float *__restric
             (u32x2){(uint32_t)f32_to_bf16(lo_bf16(hv[0]) + v[0]) | ((uint32_t)f32_to_bf16(hi_bf16(hv[0]) + v[1]) << 16),
                     (uint32_t)f32_to_bf16(lo_bf16(hv[1]) + v[2]) | ((uint32_t)f32_to_bf16(hi_bf16(hv[1]) + v[3]) << 16)};
     }
+}
+
+// Stacked products (bf16 outputs): the slabs summed as above, output rows
+// [0, na) into out, [na, nb) into out_b, [nb, N) into out_c (na and nb
+// multiples of 4, so a thread's four outputs share one destination).
+__global__ __launch_bounds__(256) void slab_stacked_finish_kernel(const float *__restrict__ partials, int ks, int T,
+                                                                  int N, int na, int nb, bf16_t *__restrict__ out,
+                                                                  int ldo, bf16_t *__restrict__ out_b, int ldo_b,
+                                                                  bf16_t *__restrict__ out_c, int ldo_c) {
+    const int n4 = N / 4;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)T * n4) return;
+    const int t = (int)(idx / n4), n = 4 * (int)(idx % n4);
+    f32x4 pv[kSlabMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kSlabMaxSplits; ++s)
+        if (s < ks) pv[s] = *reinterpret_cast<const f32x4 *>(partials + ((size_t)s * T + t) * N + n);
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSlabMaxSplits; ++s)
+        if (s < ks) v += pv[s];
+    bf16_t *dst = n < na ? out + (size_t)t * ldo + n
+                         : n < nb ? out_b + (size_t)t * ldo_b + (n - na) : out_c + (size_t)t * ldo_c + (n - nb);
+    *reinterpret_cast<u32x2 *>(dst) = (u32x2){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
 // SwiGLU: partials [ks][T][2N], gate columns then up columns.
@@ -986,8 +1016,11 @@ hipError_t launch_stream(const SkinnyArgs &a, const SkinnyPlan &p, float *partia
 
 template <int RTW, int TB, int KC, bool XLO, bool NORM = false>
 hipError_t launch_slab4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hipStream_t stream) {
-    const bool dual = a.epi == EPI_SWIGLU;
+    const bool dual = a.epi == EPI_SWIGLU, stacked = a.na > 0;
     const int Nrows = dual ? 2 * a.N : a.N;
+    // Row ranges of the weight sources: [0, na) W, [na, nb) W_b, [nb, Nrows) W_c.
+    const int na = dual ? a.N : stacked ? a.na : a.N, nb = dual || !stacked ? Nrows : a.nb;
+    const bf16_t *wb = dual || stacked ? a.W_b : a.W, *wc = stacked && a.W_c ? a.W_c : wb;
     const size_t lds = slab_token_bytes(TB, KC, XLO) + (size_t)kSlabWaves * slab_stages(TB, KC, XLO) * 2048;
     static const hipError_t attr = hipFuncSetAttribute((const void *)slab_kernel<RTW, TB, KC, XLO, NORM>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSlabLdsMax);
@@ -996,7 +1029,7 @@ hipError_t launch_slab4(const SkinnyArgs &a, const SkinnyPlan &p, float *partial
     {
         TimingScope ts(kTimeSkinny, stream);
         hipLaunchKernelGGL((slab_kernel<RTW, TB, KC, XLO, NORM>), grid, dim3(kSlabThreads), lds, stream, a.X, a.X_lo,
-                           a.ldx, a.W, dual ? a.W_b : a.W, a.N, Nrows, a.K, a.T, partials, a.norm_g, a.norm_stats,
+                           a.ldx, a.W, wb, wc, na, nb, Nrows, a.K, a.T, partials, a.norm_g, a.norm_stats,
                            norm_stats_stride(a.K), a.norm_eps);
     }
     hipError_t e = hipGetLastError();
@@ -1008,6 +1041,11 @@ hipError_t launch_slab4(const SkinnyArgs &a, const SkinnyPlan &p, float *partial
         return hipGetLastError();
     }
     const unsigned blocks = (unsigned)(((size_t)a.T * (a.N / 4) + 255) / 256);
+    if (stacked) {
+        hipLaunchKernelGGL(slab_stacked_finish_kernel, dim3(blocks), dim3(256), 0, stream, partials, p.k_splits, a.T,
+                           a.N, a.na, a.nb, static_cast<bf16_t *>(a.out), a.ldo, a.out_b, a.ldo_b, a.out_c, a.ldo_c);
+        return hipGetLastError();
+    }
     switch (a.epi) {
         case EPI_SWIGLU:
             hipLaunchKernelGGL(slab_swiglu_finish_kernel, dim3(blocks), dim3(256), 0, stream, partials, p.k_splits, a.T,
@@ -1078,6 +1116,9 @@ hipError_t launch_slab(const SkinnyArgs &a, const SkinnyPlan &p, float *partials
     if (a.norm_g && (a.X_lo || !a.norm_stats || a.K % 4 != 0 || norm_chunks(a.K) > kNormMaxChunks))
         return hipErrorInvalidValue;
     if (a.stats_out && (a.epi != EPI_RESID || norm_chunks(a.N) > kNormMaxChunks)) return hipErrorInvalidValue;
+    if (a.na > 0 && (a.epi != EPI_BF16 || a.na % 4 != 0 || a.nb % 4 != 0 || a.nb < a.na || a.nb > a.N || !a.W_b ||
+                     !a.out_b || a.ldo_b % 4 != 0 || (a.nb < a.N && (!a.W_c || !a.out_c || a.ldo_c % 4 != 0))))
+        return hipErrorInvalidValue;
     return stream_tb(a.T) == 2 ? launch_slab2<2>(a, p, partials, stream) : launch_slab2<4>(a, p, partials, stream);
 }
 
@@ -1306,7 +1347,8 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, float *par
     if ((a.x_tiled || a.out_tiled) && !skinny_tiles(a, plan)) return hipErrorInvalidValue;
     if (a.out_tiled && (a.epi != EPI_GATE || plan.k_splits != 1)) return hipErrorInvalidValue;
     if (plan.slab_rtw > 0) return launch_slab(a, plan, partials, stream);
-    if (a.norm_g || a.stats_out) return hipErrorInvalidValue;  // the deferred norm exists only in the slab product
+    // The deferred norm and the stacked products exist only in the slab product.
+    if (a.norm_g || a.stats_out || a.na > 0) return hipErrorInvalidValue;
     if (gemv_eligible(a) && plan.k_splits == 1) return launch_gemv(a, stream);
     if (const int ks = stream_ks(a, plan)) return launch_stream(a, plan, partials, stream, ks);
     if (a.epi == EPI_SWIGLU) {  // dual: row tiles in pairs, R <= 32 (skinny_plan_dual)
