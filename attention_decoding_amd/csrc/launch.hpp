@@ -73,6 +73,8 @@ hipError_t launch_kv_append(const bf16_t *k_new, const bf16_t *v_new, bf16_t *K,
 // window > 0).  Grid (ceil(T / 64), Hq, B).
 // workspace: attn_prefill_workspace_need(B, T, Hkv) bytes (V transposed).
 size_t attn_prefill_workspace_need(int64_t B, int64_t T, int64_t Hkv);
+// Query heads that one prefill-attention workgroup takes (1 to 4, a divisor of Hq / Hkv).
+int attn_prefill_heads(int64_t B, int64_t T, int64_t Hq, int64_t Hkv);
 hipError_t launch_attn_prefill(const bf16_t *q, const bf16_t *k, const bf16_t *v, bf16_t *out, int B, int T, int Hq,
                                int Hkv, int window, float scale, void *workspace, hipStream_t stream);
 

@@ -8,8 +8,13 @@
 // W > 0, j > i - W; no positional encoding.
 //
 // Design (flash attention with the score tile transposed, as in the decode
-// kernel): one workgroup per (sequence, query head, 64 queries); its four
-// waves take 16 queries each as the 16 columns of a 16x16x32 MFMA tile.
+// kernel): one workgroup per (sequence, NH query heads of one KV head, 64
+// queries); its four waves take 16 queries each as the 16 columns of a
+// 16x16x32 MFMA tile, one tile per head: every K and V^T operand read from
+// LDS serves the NH heads (their visible keys are the same), and a block's
+// loads, stores and barrier serve NH times the work.  NH is 3 or 2 of the
+// group when that leaves the grid at least two workgroups per CU, else 1 (a
+// causal batch-1 prompt, whose longest tiles would then bound the call).
 //  * Keys come in 32-position blocks (16 KB of K and V^T, pieces of each
 //    row XOR-swizzled against bank conflicts) through a register-to-LDS
 //    pipeline: while block n is processed from one LDS stage, blocks n + 1
@@ -36,6 +41,7 @@
 #include "launch.hpp"
 
 #include <math.h>
+#include <stdlib.h>
 
 namespace sambay {
 
@@ -96,6 +102,7 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const bf16_t *__restri
     }
 }
 
+template <int NH>
 __global__ __launch_bounds__(kPThreads, 2) void attn_prefill_kernel(const bf16_t *__restrict__ Q,
                                                                     const bf16_t *__restrict__ K,
                                                                     const bf16_t *__restrict__ VT,
@@ -106,8 +113,8 @@ __global__ __launch_bounds__(kPThreads, 2) void attn_prefill_kernel(const bf16_t
 
     const int ntiles = (T + kPQueries - 1) / kPQueries;
     const int tile = ntiles - 1 - (int)blockIdx.x;  // longest key ranges first (causal: late tiles)
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int g = h / (Hq / Hkv);
+    const int h0 = blockIdx.y * NH, b = blockIdx.z;   // heads h0 .. h0 + NH - 1, one KV head
+    const int g = h0 / (Hq / Hkv);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
     const int i0 = tile * kPQueries;
     const int qi = i0 + 16 * wave + col;  // this lane's query (column)
@@ -115,11 +122,12 @@ __global__ __launch_bounds__(kPThreads, 2) void attn_prefill_kernel(const bf16_t
     const int jlo = window > 0 ? max(0, i0 - window + 1) : 0;
     const int kb0 = jlo / kPKeys, kb1 = qlast / kPKeys;
 
-    u32x4 qb[4];
-    {
-        const size_t qrow = (((size_t)b * T + min(qi, T - 1)) * Hq + h) * kHeadDim + 8 * grp;
+    u32x4 qb[NH][4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) qb[t] = ld16(Q + qrow + 32 * t);
+    for (int j = 0; j < NH; ++j) {
+        const size_t qrow = (((size_t)b * T + min(qi, T - 1)) * Hq + h0 + j) * kHeadDim + 8 * grp;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) qb[j][t] = ld16(Q + qrow + 32 * t);
     }
     // The queries are complete before the block pipeline starts, so that no
     // wait inside the loop has to count them among the loads in flight.
@@ -148,10 +156,15 @@ __global__ __launch_bounds__(kPThreads, 2) void attn_prefill_kernel(const bf16_t
         for (int e = 0; e < 4; ++e) stage[buf][threadIdx.x + kPThreads * e] = r[e];
     };
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 acc[8];
+    float m_run[NH], l_run[NH];
+    f32x4 acc[NH][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NH; ++j) {
+        m_run[j] = -INFINITY;
+        l_run[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[j][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
 
     // Score tile rows: tile 0 row r holds key 8(r/4) + r%4, tile 1 row r key
     // 8(r/4) + 4 + r%4, so that lane group grp ends up with keys 8grp .. 8grp+7
@@ -161,41 +174,55 @@ __global__ __launch_bounds__(kPThreads, 2) void attn_prefill_kernel(const bf16_t
         const u32x4 *kr = stage[buf];
         const u32x4 *vr = kr + kPSlots;
         const int j0 = kb * kPKeys;
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 s0[NH], s1[NH];
+#pragma unroll
+        for (int j = 0; j < NH; ++j) s0[j] = s1[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            s0 = mfma16x16x32(kr[kslot(r0, 4 * t + grp)], qb[t], s0);
-            s1 = mfma16x16x32(kr[kslot(r1, 4 * t + grp)], qb[t], s1);
-        }
-        // s0[i]: key j0 + 8grp + i, s1[i]: key j0 + 8grp + 4 + i, for query qi.
-        const int jmin = window > 0 ? qi - window + 1 : 0;  // visible keys: jmin <= j <= qi
+            const u32x4 k0 = kr[kslot(r0, 4 * t + grp)], k1 = kr[kslot(r1, 4 * t + grp)];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ja = j0 + 8 * grp + i, jb = ja + 4;
-            s0[i] = ja <= qi && ja >= jmin ? s0[i] * qscale : -INFINITY;
-            s1[i] = jb <= qi && jb >= jmin ? s1[i] * qscale : -INFINITY;
+            for (int j = 0; j < NH; ++j) {
+                s0[j] = mfma16x16x32(k0, qb[j][t], s0[j]);
+                s1[j] = mfma16x16x32(k1, qb[j][t], s1[j]);
+            }
         }
-        float bm = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                         fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float m_new = fmaxf(m_run, bm);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no visible key yet: nothing to rescale
-        const float alpha = exp2_fast(m_run - m_use);
-        m_run = m_new;
-        float p[8];
+        // s0[j][i]: key j0 + 8grp + i, s1[j][i]: key j0 + 8grp + 4 + i, for query qi of head h0 + j.
+        const int jmin = window > 0 ? qi - window + 1 : 0;  // visible keys: jmin <= key <= qi
+        u32x4 pb[NH];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[i] = exp2_fast(s0[i] - m_use);
-            p[4 + i] = exp2_fast(s1[i] - m_use);
+        for (int j = 0; j < NH; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ja = j0 + 8 * grp + i, jb = ja + 4;
+                s0[j][i] = ja <= qi && ja >= jmin ? s0[j][i] * qscale : -INFINITY;
+                s1[j][i] = jb <= qi && jb >= jmin ? s1[j][i] * qscale : -INFINITY;
+            }
+            float bm = fmaxf(fmaxf(fmaxf(s0[j][0], s0[j][1]), fmaxf(s0[j][2], s0[j][3])),
+                             fmaxf(fmaxf(s1[j][0], s1[j][1]), fmaxf(s1[j][2], s1[j][3])));
+            bm = fmaxf(bm, __shfl_xor(bm, 16));
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            const float m_new = fmaxf(m_run[j], bm);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no visible key yet: nothing to rescale
+            const float alpha = exp2_fast(m_run[j] - m_use);
+            m_run[j] = m_new;
+            float p[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = exp2_fast(s0[j][i] - m_use);
+                p[4 + i] = exp2_fast(s1[j][i] - m_use);
+            }
+            l_run[j] = l_run[j] * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] *= alpha;
+            pb[j] = (u32x4){pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
         }
-        l_run = l_run * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] *= alpha;
-        const u32x4 pb = {pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
         // O^T[dim][query] += V^T[dim][key] · P^T[key][query]: lane reads keys 8grp .. 8grp+7 of dim 16·db + col.
 #pragma unroll
-        for (int db = 0; db < 8; ++db) acc[db] = mfma16x16x32(vr[vslot(16 * db + col, grp)], pb, acc[db]);
+        for (int db = 0; db < 8; ++db) {
+            const u32x4 v = vr[vslot(16 * db + col, grp)];
+#pragma unroll
+            for (int j = 0; j < NH; ++j) acc[j][db] = mfma16x16x32(v, pb[j], acc[j][db]);
+        }
     };
 
     // Pipeline: block kb is processed from one stage while block kb + 1 waits
@@ -223,21 +250,42 @@ __global__ __launch_bounds__(kPThreads, 2) void attn_prefill_kernel(const bf16_t
     }
 
     // Row sums: the four lane groups summed different keys of the same query.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (qi >= T) return;
-    const float inv = 1.f / l_run;  // every query sees at least itself
-    bf16_t *o = out + (((size_t)b * T + qi) * Hq + h) * kHeadDim;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-        const int d = 16 * db + 4 * grp;
-        const uint32_t w0 = pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv);
-        const uint32_t w1 = pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv);
-        *reinterpret_cast<u32x2 *>(o + d) = (u32x2){w0, w1};
+    for (int j = 0; j < NH; ++j) {
+        l_run[j] += __shfl_xor(l_run[j], 16);
+        l_run[j] += __shfl_xor(l_run[j], 32);
+    }
+    if (qi >= T) return;
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+        const float inv = 1.f / l_run[j];  // every query sees at least itself
+        bf16_t *o = out + (((size_t)b * T + qi) * Hq + h0 + j) * kHeadDim;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const int d = 16 * db + 4 * grp;
+            const uint32_t w0 = pack_bf16x2(acc[j][db][0] * inv, acc[j][db][1] * inv);
+            const uint32_t w1 = pack_bf16x2(acc[j][db][2] * inv, acc[j][db][3] * inv);
+            *reinterpret_cast<u32x2 *>(o + d) = (u32x2){w0, w1};
+        }
     }
 }
 
 }  // namespace
+
+// Query heads per workgroup: 3 or 2 heads of a KV head's group (G = Hq /
+// Hkv divisible by them; 4 would not fit the registers) when that still
+// gives >= 512 workgroups (two per CU), else 1.  SAMBAY_PREFILL_HEADS (1-3,
+// a divisor of G) overrides the rule.
+int attn_prefill_heads(int64_t B, int64_t T, int64_t Hq, int64_t Hkv) {
+    const int64_t G = Hq / Hkv;
+    if (const char *env = getenv("SAMBAY_PREFILL_HEADS")) {
+        const int v = atoi(env);
+        if (v >= 1 && v <= 3 && G % v == 0) return v;
+    }
+    const int nh = G % 3 == 0 ? 3 : G % 2 == 0 ? 2 : 1;
+    const int64_t tiles = (T + kPQueries - 1) / kPQueries;
+    return tiles * B * (Hq / nh) < 512 ? 1 : nh;
+}
 
 size_t attn_prefill_workspace_need(int64_t B, int64_t T, int64_t Hkv) {
     const int64_t Tp = (T + kPKeys - 1) / kPKeys * kPKeys;
@@ -252,10 +300,20 @@ hipError_t launch_attn_prefill(const bf16_t *q, const bf16_t *k, const bf16_t *v
                        stream, v, vt, T, Tp, Hkv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)((T + kPQueries - 1) / kPQueries), (unsigned)Hq, (unsigned)B);
+    const int tiles = (T + kPQueries - 1) / kPQueries, G = Hq / Hkv;
+    int nh = attn_prefill_heads(B, T, Hq, Hkv);
+    if (nh < 1 || nh > 3 || G % nh != 0) nh = 1;
+    const dim3 grid((unsigned)tiles, (unsigned)(Hq / nh), (unsigned)B);
     TimingScope ts(kTimePrefill, stream);
-    hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(kPThreads), 0, stream, q, k, vt, out, T, Tp, Hq, Hkv, window,
-                       scale * kLog2e);
+#define SB_PREFILL(NH_)                                                                                              \
+    hipLaunchKernelGGL(attn_prefill_kernel<NH_>, grid, dim3(kPThreads), 0, stream, q, k, vt, out, T, Tp, Hq, Hkv,   \
+                       window, scale * kLog2e)
+    switch (nh) {
+        case 2: SB_PREFILL(2); break;
+        case 3: SB_PREFILL(3); break;
+        default: SB_PREFILL(1); break;
+    }
+#undef SB_PREFILL
     return hipGetLastError();
 }
 

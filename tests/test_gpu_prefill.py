@@ -83,3 +83,33 @@ def test_prefill_window_beyond_prompt_equals_causal(sb):
     c = sb.attn_prefill(x.q, x.k, x.v, window=10000)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
+
+
+@pytest.mark.parametrize("heads", [1, 2, 3])
+@pytest.mark.parametrize("B,T,Hq,Hkv,W", [
+    (2, 100, 6, 2, 0),        # causal, a ragged last tile
+    (1, 300, 24, 8, 64),      # window shorter than the tile span
+    (3, 130, 12, 2, 0),       # six query heads per KV head
+])
+def test_prefill_heads_per_workgroup(sb, monkeypatch, heads, B, T, Hq, Hkv, W):
+    """One workgroup serving 1, 2 or 3 query heads of a KV head (forced by
+    SAMBAY_PREFILL_HEADS where the group size allows it), against the oracle."""
+    if (Hq // Hkv) % heads:
+        pytest.skip("%d heads do not divide the group of %d" % (heads, Hq // Hkv))
+    monkeypatch.setenv("SAMBAY_PREFILL_HEADS", str(heads))
+    x = workload.prefill_inputs(B, T, Hq, Hkv, 128, seed=7 * T + W + heads, device=DEV)
+    out = sb.attn_prefill(x.q, x.k, x.v, window=W)
+    torch.cuda.synchronize()
+    ref = oracle.attn_prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), W)
+    report("prefill %d heads/wg B=%d T=%d %d/%d W=%d" % (heads, B, T, Hq, Hkv, W), err(f64(out), ref), TOL_BF16)
+
+
+def test_prefill_full_size_causal_three_heads(sb, monkeypatch):
+    """The 2048-token causal prompt with three query heads per workgroup."""
+    monkeypatch.setenv("SAMBAY_PREFILL_HEADS", "3")
+    c = workload.ATTN_PREFILL
+    x = workload.prefill_inputs(1, c["T"], c["Hq"], c["Hkv"], c["D"], seed=8, device=DEV)
+    out = sb.attn_prefill(x.q, x.k, x.v, window=0)
+    torch.cuda.synchronize()
+    ref = oracle.attn_prefill(x.q.cpu(), x.k.cpu(), x.v.cpu(), 0)
+    report("prefill 1 x 2048 causal, 3 heads per workgroup", err(f64(out), ref), TOL_BF16)
