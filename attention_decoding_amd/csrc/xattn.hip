@@ -85,59 +85,71 @@ __global__ __launch_bounds__(kThreads, 2) void xattn_split_kernel(const void *__
     __shared__ float red_m[kWaves][kMaxGroup];
     __shared__ float red_l[kWaves][kMaxGroup];
 
-    __shared__ int item[2];
-    int s, g, b;
+    __shared__ int item[3];  // ragged batches: sequence, item index in it, its length
+    int s, g, b, Lb;
     if (!lens) {
         // Full caches: grid (S, Hkv, B), a head's chunks in consecutive workgroups.
         s = blockIdx.x;
         g = blockIdx.y;
         b = blockIdx.z;
+        Lb = L;
     } else {
         // Ragged batches: a 1-D grid over the (sequence, KV head, chunk) items
         // that hold positions, in that order (the same order as above, without
         // the empty chunks); workgroups past the last item exit.  Each thread
-        // counts the items of a contiguous run of sequences, a scan over the
-        // runs locates the sequence of this workgroup's item.
-        int *runs = reinterpret_cast<int *>(&kbuf[0][0]);  // kThreads ints, free until the first block
-        // Chunks of sequence i: those holding positions, at least one (an empty
-        // item still writes the sequence's zero result).
-        auto chunks_of = [&](int i) { return max(1, (min(max(lens[i], 0), L) + chunk - 1) / chunk); };
+        // counts the items of a contiguous run of sequences (reading each
+        // length once), a prefix sum over the threads (a scan inside each
+        // wave, the wave totals through LDS) gives each run's first item, and
+        // the thread whose run holds this workgroup's item publishes it.
+        int *wsum = reinterpret_cast<int *>(&kbuf[0][0]);  // wave totals, free until the first block
+        // Sequence i's length (clamped to [0, L]) and chunks: those holding
+        // positions, at least one (an empty item still writes its zero result).
+        auto len_of = [&](int i) { return min(max(lens[i], 0), L); };
+        auto chunks = [&](int len) { return max(1, (len + chunk - 1) / chunk); };
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int per = (B + kThreads - 1) / kThreads;
         const int lo = min(B, (int)threadIdx.x * per), hi = min(B, lo + per);
+        const int len_lo = lo < hi ? len_of(lo) : 0;
         int cnt = 0;
-        for (int i = lo; i < hi; ++i) cnt += Hkv * chunks_of(i);
-        runs[threadIdx.x] = cnt;
+        for (int i = lo; i < hi; ++i) cnt += Hkv * chunks(i == lo ? len_lo : len_of(i));
+        int incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        if (threadIdx.x == 0) item[0] = -1;
         __syncthreads();
-        if (threadIdx.x == 0) {
-            int acc = 0, t = 0;
-            const int w = (int)blockIdx.x;
-            while (t < kThreads && acc + runs[t] <= w) acc += runs[t++];
-            item[0] = -1;
-            if (t < kThreads) {
-                for (int i = min(B, t * per); i < min(B, t * per + per); ++i) {
-                    const int n = Hkv * chunks_of(i);
-                    if (w < acc + n) {
-                        item[0] = i;
-                        item[1] = w - acc;
-                        break;
-                    }
-                    acc += n;
+        int start = incl - cnt;
+        for (int w2 = 0; w2 < wave; ++w2) start += wsum[w2];
+        const int w = (int)blockIdx.x;
+        if (w >= start && w < start + cnt) {  // at most one thread
+            int acc = start;
+            for (int i = lo; i < hi; ++i) {
+                const int len = i == lo ? len_lo : len_of(i), n = Hkv * chunks(len);
+                if (w < acc + n) {
+                    item[0] = i;
+                    item[1] = w - acc;
+                    item[2] = len;
+                    break;
                 }
+                acc += n;
             }
         }
         __syncthreads();
         if (item[0] < 0) return;  // uniform across the workgroup
         b = item[0];
-        const int nch = chunks_of(b);
+        Lb = item[2];
+        const int nch = chunks(Lb);
         g = item[1] / nch;
-        s = item[1] % nch;
+        s = item[1] % nch;  // (wsum's region is read only before the second barrier)
     }
     const int G = Hq / Hkv;
     const int NC = DIFF ? 2 * G : G;  // score columns of this group
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
-    // Ragged batch: sequence b uses its first lens[b] positions (clamped to
-    // [0, L]); chunks past that end are empty and write an empty partial.
-    const int Lb = lens ? min(max(lens[b], 0), L) : L;
+    // Ragged batch: sequence b uses its first Lb = lens[b] positions (clamped
+    // to [0, L]); chunks past that end are empty and write an empty partial.
     const int j0 = s * chunk;
     const int j1 = max(j0, min(Lb, j0 + chunk));
     const size_t kv0 = ((size_t)b * Hkv + g) * (size_t)L * kHeadDim;
