@@ -39,6 +39,10 @@ constexpr int kMaxSplits = 64;
 struct XattnPlan {
     int splits;  // number of key chunks per (sequence, KV head)
     int chunk;   // keys per chunk, a multiple of kKeyBlock; every chunk is non-empty
+    // Lengths batches: keys per chunk when every length is within one chunk
+    // of L (decided on the device, where the lengths are): the full plan's
+    // chunk, twice `chunk` when the plan halved it for ragged lengths.
+    int chunk_full;
 };
 
 // ragged: a lengths array limits each sequence to a prefix of the L positions.

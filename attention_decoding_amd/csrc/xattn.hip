@@ -78,21 +78,22 @@ __global__ __launch_bounds__(kThreads, 2) void xattn_split_kernel(const void *__
                                                                float *__restrict__ part_o,
                                                                bf16_t *__restrict__ out, bf16_t *__restrict__ out_lo,
                                                                int B, int Hq, int Hkv, int L,
-                                                               const int32_t *__restrict__ lens, int chunk, int S,
-                                                               float qscale) {
+                                                               const int32_t *__restrict__ lens, int chunk,
+                                                               int chunk_full, int S, float qscale) {
     __shared__ __attribute__((aligned(16))) bf16_t kbuf[kWaves][kBlockElems];
     __shared__ __attribute__((aligned(16))) bf16_t vbuf[kWaves][kBlockElems];
     __shared__ float red_m[kWaves][kMaxGroup];
     __shared__ float red_l[kWaves][kMaxGroup];
 
     __shared__ int item[3];  // ragged batches: sequence, item index in it, its length
-    int s, g, b, Lb;
+    int s, g, b, Lb, ck;      // ck: positions per chunk
     if (!lens) {
         // Full caches: grid (S, Hkv, B), a head's chunks in consecutive workgroups.
         s = blockIdx.x;
         g = blockIdx.y;
         b = blockIdx.z;
         Lb = L;
+        ck = chunk;
     } else {
         // Ragged batches: a 1-D grid over the (sequence, KV head, chunk) items
         // that hold positions, in that order (the same order as above, without
@@ -101,33 +102,56 @@ __global__ __launch_bounds__(kThreads, 2) void xattn_split_kernel(const void *__
         // length once), a prefix sum over the threads (a scan inside each
         // wave, the wave totals through LDS) gives each run's first item, and
         // the thread whose run holds this workgroup's item publishes it.
-        int *wsum = reinterpret_cast<int *>(&kbuf[0][0]);  // wave totals, free until the first block
+        // Chunks hold chunk_full positions when every length is within one
+        // chunk of L (a uniform batch: fewer, longer workgroups, as the full
+        // plan), else chunk; both counts are formed in the same pass, and the
+        // batch's shortest length picks one.
+        int *wsum = reinterpret_cast<int *>(&kbuf[0][0]);  // [0, 4) / [4, 8) wave totals, [8, 12) wave minima
         // Sequence i's length (clamped to [0, L]) and chunks: those holding
         // positions, at least one (an empty item still writes its zero result).
         auto len_of = [&](int i) { return min(max(lens[i], 0), L); };
-        auto chunks = [&](int len) { return max(1, (len + chunk - 1) / chunk); };
+        auto chunks = [&](int len, int c) { return max(1, (len + c - 1) / c); };
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int per = (B + kThreads - 1) / kThreads;
         const int lo = min(B, (int)threadIdx.x * per), hi = min(B, lo + per);
         const int len_lo = lo < hi ? len_of(lo) : 0;
-        int cnt = 0;
-        for (int i = lo; i < hi; ++i) cnt += Hkv * chunks(i == lo ? len_lo : len_of(i));
-        int incl = cnt;
+        int cnt_s = 0, cnt_f = 0, mn = L;
+        for (int i = lo; i < hi; ++i) {
+            const int len = i == lo ? len_lo : len_of(i);
+            cnt_s += Hkv * chunks(len, chunk);
+            cnt_f += Hkv * chunks(len, chunk_full);
+            mn = min(mn, len);
+        }
+        int incl_s = cnt_s, incl_f = cnt_f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(incl, off);
-            if (lane >= off) incl += v;
+            const int vs = __shfl_up(incl_s, off), vf = __shfl_up(incl_f, off);
+            if (lane >= off) {
+                incl_s += vs;
+                incl_f += vf;
+            }
         }
-        if (lane == 63) wsum[wave] = incl;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mn = min(mn, __shfl_xor(mn, off));
+        if (lane == 63) {
+            wsum[wave] = incl_s;
+            wsum[kWaves + wave] = incl_f;
+            wsum[2 * kWaves + wave] = mn;
+        }
         if (threadIdx.x == 0) item[0] = -1;
         __syncthreads();
-        int start = incl - cnt;
-        for (int w2 = 0; w2 < wave; ++w2) start += wsum[w2];
+        int bmin = L;
+        for (int w2 = 0; w2 < kWaves; ++w2) bmin = min(bmin, wsum[2 * kWaves + w2]);
+        const bool uniform = bmin >= L - chunk;
+        ck = uniform ? chunk_full : chunk;
+        const int cnt = uniform ? cnt_f : cnt_s;
+        int start = (uniform ? incl_f : incl_s) - cnt;
+        for (int w2 = 0; w2 < wave; ++w2) start += wsum[(uniform ? kWaves : 0) + w2];
         const int w = (int)blockIdx.x;
         if (w >= start && w < start + cnt) {  // at most one thread
             int acc = start;
             for (int i = lo; i < hi; ++i) {
-                const int len = i == lo ? len_lo : len_of(i), n = Hkv * chunks(len);
+                const int len = i == lo ? len_lo : len_of(i), n = Hkv * chunks(len, ck);
                 if (w < acc + n) {
                     item[0] = i;
                     item[1] = w - acc;
@@ -141,7 +165,7 @@ __global__ __launch_bounds__(kThreads, 2) void xattn_split_kernel(const void *__
         if (item[0] < 0) return;  // uniform across the workgroup
         b = item[0];
         Lb = item[2];
-        const int nch = chunks(Lb);
+        const int nch = chunks(Lb, ck);
         g = item[1] / nch;
         s = item[1] % nch;  // (wsum's region is read only before the second barrier)
     }
@@ -150,8 +174,8 @@ __global__ __launch_bounds__(kThreads, 2) void xattn_split_kernel(const void *__
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
     // Ragged batch: sequence b uses its first Lb = lens[b] positions (clamped
     // to [0, L]); chunks past that end are empty and write an empty partial.
-    const int j0 = s * chunk;
-    const int j1 = max(j0, min(Lb, j0 + chunk));
+    const int j0 = s * ck;
+    const int j1 = max(j0, min(Lb, j0 + ck));
     const size_t kv0 = ((size_t)b * Hkv + g) * (size_t)L * kHeadDim;
     const bf16_t *Kb = K + kv0;
     const bf16_t *Vb = V + kv0;
@@ -356,15 +380,32 @@ __device__ __forceinline__ float merge_column(const float2 *__restrict__ ml, con
 }
 
 // One workgroup per (sequence, query head): the merge, then the bf16 store.
+// Ragged batches: the chunk length the split kernel used (chunk_full when
+// every length of the batch is within one chunk of L, else chunk), from the
+// batch's shortest length; every thread of the workgroup gets it.
+__device__ __forceinline__ int lens_chunk(const int32_t *__restrict__ lens, int B, int L, int chunk, int chunk_full,
+                                          int *red) {
+    int mn = L;
+    for (int i = threadIdx.x; i < B; i += blockDim.x) mn = min(mn, min(max(lens[i], 0), L));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mn = min(mn, __shfl_xor(mn, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mn;
+    __syncthreads();
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) mn = min(mn, red[w]);
+    return mn >= L - chunk ? chunk_full : chunk;
+}
+
 __global__ __launch_bounds__(kHeadDim) void xattn_merge_kernel(const float2 *__restrict__ part_ml,
                                                                const float *__restrict__ part_o,
                                                                bf16_t *__restrict__ out, bf16_t *__restrict__ out_lo,
                                                                int S, int Hq, int L, const int32_t *__restrict__ lens,
-                                                               int chunk) {
+                                                               int chunk, int chunk_full) {
+    __shared__ int red[kHeadDim / 64];
     const size_t bh = blockIdx.x;
     const int d = threadIdx.x;
     // Ragged batches: only the chunks that hold positions were written.
-    const int Sb = lens ? (min(max(lens[bh / Hq], 0), L) + chunk - 1) / chunk : S;
+    const int ck = lens ? lens_chunk(lens, (int)(gridDim.x / Hq), L, chunk, chunk_full, red) : chunk;
+    const int Sb = lens ? (min(max(lens[bh / Hq], 0), L) + ck - 1) / ck : S;
     const float v = merge_column(part_ml + bh * S, part_o + bh * S * kHeadDim, Sb, d);
     const bf16_t hi = f32_to_bf16(v);
     out[bh * kHeadDim + d] = hi;
@@ -380,14 +421,17 @@ __global__ __launch_bounds__(kHeadDim) void diffattn_merge_kernel(const float2 *
                                                                   const bf16_t *__restrict__ gamma,
                                                                   bf16_t *__restrict__ out, int S, int Hq, int G,
                                                                   int L, const int32_t *__restrict__ lens, int chunk,
-                                                                  float lam, float lam_init, float eps) {
+                                                                  int chunk_full, float lam, float lam_init,
+                                                                  float eps) {
     __shared__ float red[kHeadDim / 64];
+    __shared__ int ired[kHeadDim / 64];
     const size_t bh = blockIdx.x;
     const int d = threadIdx.x;
     const size_t b = bh / Hq;
     const int h = (int)(bh % Hq), g = h / G;
     const size_t c1 = b * 2 * Hq + (size_t)g * 2 * G + (h - g * G), c2 = c1 + G;  // map 1 and map 2 columns
-    const int Sb = lens ? (min(max(lens[b], 0), L) + chunk - 1) / chunk : S;
+    const int ck = lens ? lens_chunk(lens, (int)(gridDim.x / Hq), L, chunk, chunk_full, ired) : chunk;
+    const int Sb = lens ? (min(max(lens[b], 0), L) + ck - 1) / ck : S;
     const float y = merge_column(part_ml + c1 * S, part_o + c1 * S * kHeadDim, Sb, d) -
                     lam * merge_column(part_ml + c2 * S, part_o + c2 * S * kHeadDim, Sb, d);
     float ss = y * y;
@@ -416,6 +460,7 @@ XattnPlan xattn_plan(int64_t B, int64_t Hkv, int64_t L, bool ragged) {
     // unless that leaves fewer than ~2 workgroups per CU (256 CUs); never more
     // than ~8 per CU.
     int64_t S = env_splits();
+    bool halved = false;  // ragged: chunks half as long as the full plan's
     if (S == 0) {
         const int64_t fill = (512 + pairs - 1) / pairs, cap = (2048 + pairs - 1) / pairs;
         const int64_t by_len = L / 4096 > 1 ? L / 4096 : 1;
@@ -431,7 +476,10 @@ XattnPlan xattn_plan(int64_t B, int64_t Hkv, int64_t L, bool ragged) {
         // Ragged batches hold fewer positions than L per sequence: chunks half
         // as long keep the workgroup count up and the tail short (measured on
         // lengths uniform in [2048, 34816]: 8 -> 16 chunks, 5.1 -> 5.4 TB/s).
-        if (ragged && nblk / (2 * S) >= 16) S *= 2;
+        if (ragged && nblk / (2 * S) >= 16) {
+            halved = true;
+            S *= 2;
+        }
     }
     if (S > kMaxSplits) S = kMaxSplits;
     if (S > nblk) S = nblk;
@@ -440,6 +488,8 @@ XattnPlan xattn_plan(int64_t B, int64_t Hkv, int64_t L, bool ragged) {
     XattnPlan p;
     p.chunk = (int)(per * kKeyBlock);
     p.splits = (int)((L + p.chunk - 1) / p.chunk);  // every chunk non-empty
+    const int64_t S_full = halved ? S / 2 : S, per_full = (nblk + S_full - 1) / S_full;
+    p.chunk_full = halved ? (int)(per_full * kKeyBlock) : p.chunk;
     return p;
 }
 
@@ -467,16 +517,16 @@ hipError_t launch_xattn(const void *q, bool q_f32, const bf16_t *K, const bf16_t
     TimingScope ts(kTimeXattnSplit, stream);
     if (q_f32)
         hipLaunchKernelGGL((xattn_split_kernel<true, false>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po, out,
-                           out_lo, B, Hq, Hkv, L, lens, plan.chunk, plan.splits, qscale);
+                           out_lo, B, Hq, Hkv, L, lens, plan.chunk, plan.chunk_full, plan.splits, qscale);
     else
         hipLaunchKernelGGL((xattn_split_kernel<false, false>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po, out,
-                           out_lo, B, Hq, Hkv, L, lens, plan.chunk, plan.splits, qscale);
+                           out_lo, B, Hq, Hkv, L, lens, plan.chunk, plan.chunk_full, plan.splits, qscale);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;  // one chunk: the split kernel stored the output
     TimingScope ts(kTimeXattnMerge, stream);
     hipLaunchKernelGGL(xattn_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kHeadDim), 0, stream, ml, po, out, out_lo,
-                       plan.splits, Hq, L, lens, plan.chunk);
+                       plan.splits, Hq, L, lens, plan.chunk, plan.chunk_full);
     return hipGetLastError();
 }
 
@@ -491,13 +541,14 @@ hipError_t launch_diffattn(const bf16_t *q, const bf16_t *K, const bf16_t *V, co
     {
         TimingScope ts(kTimeDiffSplit, stream);
         hipLaunchKernelGGL((xattn_split_kernel<false, true>), grid, dim3(kThreads), 0, stream, q, K, V, ml, po,
-                           nullptr, nullptr, B, Hq, Hkv, L, lens, plan.chunk, plan.splits, scale * kLog2e);
+                           nullptr, nullptr, B, Hq, Hkv, L, lens, plan.chunk, plan.chunk_full, plan.splits,
+                           scale * kLog2e);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     TimingScope ts(kTimeDiffMerge, stream);
     hipLaunchKernelGGL(diffattn_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kHeadDim), 0, stream, ml, po, gamma, out,
-                       plan.splits, Hq, Hq / Hkv, L, lens, plan.chunk, lam, lam_init, eps);
+                       plan.splits, Hq, Hq / Hkv, L, lens, plan.chunk, plan.chunk_full, lam, lam_init, eps);
     return hipGetLastError();
 }
 
