@@ -81,6 +81,43 @@ def test_xattn_varlen_full_size_sampled(sb):
     report("xattn varlen 32x34816 ragged (%d sequences)" % len(pick), err(f64(out[idx.to(DEV)]), ref), TOL_BF16)
 
 
+def test_xattn_varlen_full_size_full_lengths_take_the_full_plan(sb):
+    """32 sequences at full length (34816): the lengths path sees on the device
+    that every length is within one chunk of L and takes the full plan's
+    chunks (8 per head rather than the 16 of ragged batches), so its result is
+    bit-identical to the plain path's."""
+    c = workload.XATTN_VARLEN
+    x = workload.xattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["L"], seed=9, device=DEV)
+    lens = torch.full((c["B"],), c["L"], dtype=torch.int32, device=DEV)
+    a = sb.xattn_decode(x.q, x.K, x.V)
+    b = sb.xattn_decode(x.q, x.K, x.V, lens=lens)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("spread", [2177, 2178])
+def test_xattn_varlen_full_size_near_full_lengths(sb, spread):
+    """Lengths in [L - spread + 1, L] at 32 x 34816, the shortest exactly
+    L - spread + 1.  The ragged plan's chunk is 2176 positions: with spread
+    2177 the shortest length is L - 2176, still within one chunk of L, so the
+    long chunks are taken (their last ones partial); with 2178 it is one
+    position lower and the short chunks are taken.  The oracle checks 4
+    sequences, the shortest among them."""
+    c = workload.XATTN_VARLEN
+    L = c["L"]
+    x = workload.xattn_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], L, seed=10, device=DEV)
+    g = torch.Generator().manual_seed(spread)
+    ln = L - torch.randint(0, spread - 1, (c["B"],), generator=g, dtype=torch.int32)
+    ln[3] = L - spread + 1
+    lens = ln.to(DEV)
+    out = sb.xattn_decode(x.q, x.K, x.V, lens=lens)
+    torch.cuda.synchronize()
+    pick = [0, 3, 17, 31]
+    idx = torch.tensor(pick)
+    ref = oracle.xattn_varlen(cpu(x.q)[idx], cpu(x.K)[idx], cpu(x.V)[idx], ln.numpy()[pick])
+    report("xattn varlen 32x%d, lengths >= L - %d" % (L, spread - 1), err(f64(out[idx.to(DEV)]), ref), TOL_BF16)
+
+
 def test_xattn_varlen_full_lengths_equal_plain(sb, monkeypatch):
     """Every sequence at full length: with the same chunking the ragged path is
     bit-identical to the plain one; with the default plans (ragged batches use
