@@ -339,7 +339,9 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(const bf16_t *__
 // which streams at full rate; 16 rows x 64 B loses ~25%), NS - 1 stages
 // ahead.  No wave waits for another after the token slab has landed, and
 // each wave's accumulators hold finished partial rows (no reduction across
-// waves).
+// waves).  The rows may come from up to three weight matrices stacked one
+// after another (the SwiGLU gate and up pair; an attention layer's q, k and
+// v), with one finishing pass for all of them.
 constexpr int kSlabWaves = 8;
 constexpr int kSlabThreads = 64 * kSlabWaves;
 constexpr size_t kSlabLdsMax = 160 * 1024;
