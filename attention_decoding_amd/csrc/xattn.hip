@@ -64,6 +64,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockElems = kKeyBlock * kHeadDim;  // bf16 per 32-position K or V block (8 KB)
 constexpr int kWaitLds = 0xc07f;  // lgkmcnt(0): this wave's LDS reads have returned
+constexpr int kWaitVm = 0x3f70;   // vmcnt(0): this wave's loads and direct-to-LDS copies have landed
 
 // Copy policy of the cache streams: non-temporal (each byte is read once).
 constexpr int kStreamPolicy = 2;
@@ -180,40 +181,6 @@ __global__ __launch_bounds__(kThreads, 2) void xattn_split_kernel(const void *__
     const bf16_t *Kb = K + kv0;
     const bf16_t *Vb = V + kv0;
 
-    // B operand of the score product: head `col` of this group (differential:
-    // map col / G of head col % G, the other map's half zeroed); MFMA k-step t
-    // covers dims 32·t .. 32·t+31, lane group grp holding dims 32·t + 8·grp + e.
-    u32x4 qhi[4], qlo[4];
-    {
-        const int map = DIFF && col >= G ? 1 : 0;
-        const int h = g * G + col - map * G;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float f[8];
-            const bool live = col < NC && (!DIFF || (t >> 1) == map);
-            const size_t off = ((size_t)b * Hq + h) * kHeadDim + 32 * t + 8 * grp;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = 0.f;
-                if (live) x = QF32 ? ((const float *)qv)[off + e] : bf16_to_f32(((const bf16_t *)qv)[off + e]);
-                f[e] = x * qscale;
-            }
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bf16_t h0 = f32_to_bf16(f[2 * e]), h1 = f32_to_bf16(f[2 * e + 1]);
-                hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                lo[e] = (uint32_t)split_lo(f[2 * e], h0) | ((uint32_t)split_lo(f[2 * e + 1], h1) << 16);
-            }
-            qhi[t] = (u32x4){hi[0], hi[1], hi[2], hi[3]};
-            qlo[t] = (u32x4){lo[0], lo[1], lo[2], lo[3]};
-        }
-    }
-
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
     bf16_t *kw = kbuf[wave], *vw = vbuf[wave];
 
     // One 32-position block of K or V into this wave's LDS buffer by direct
@@ -239,12 +206,68 @@ __global__ __launch_bounds__(kThreads, 2) void xattn_split_kernel(const void *__
         }
     };
 
+    // B operand of the score product: head `col` of this group (differential:
+    // map col / G of head col % G, the other map's half zeroed); MFMA k-step t
+    // covers dims 32·t .. 32·t+31, lane group grp holding dims 32·t + 8·grp + e.
+    // The query rows are loaded first (16-byte loads; dead columns read a
+    // clamped row and are zeroed), then the first block's copies go out, and
+    // only then is the query converted: its latency and the first block's
+    // overlap instead of adding up.
+    const int q_map = DIFF && col >= G ? 1 : 0;
+    const int q_head = min(g * G + col - q_map * G, Hq - 1);
+    constexpr int QV = QF32 ? 2 : 1;  // 16-byte loads per 8 dims
+    u32x4 qraw[4][QV];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const size_t off = ((size_t)b * Hq + q_head) * kHeadDim + 32 * t + 8 * grp;
+#pragma unroll
+        for (int v = 0; v < QV; ++v)
+            qraw[t][v] = QF32 ? ld16((const float *)qv + off + 4 * v) : ld16((const bf16_t *)qv + off);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int nblk = (j1 - j0 + kKeyBlock - 1) / kKeyBlock;
+    if (wave < nblk) {
+        issue_block(Kb, kw, wave, false);
+        issue_block(Vb, vw, wave, true);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 qhi[4], qlo[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float f[8];
+        const bool live = col < NC && (!DIFF || (t >> 1) == q_map);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = QF32 ? __uint_as_float(qraw[t][QF32 ? e / 4 : 0][e % 4])
+                                 : ((e & 1) ? hi_bf16(qraw[t][0][e / 2]) : lo_bf16(qraw[t][0][e / 2]));
+            f[e] = (live ? x : 0.f) * qscale;
+        }
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bf16_t h0 = f32_to_bf16(f[2 * e]), h1 = f32_to_bf16(f[2 * e + 1]);
+            hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lo[e] = (uint32_t)split_lo(f[2 * e], h0) | ((uint32_t)split_lo(f[2 * e + 1], h1) << 16);
+        }
+        qhi[t] = (u32x4){hi[0], hi[1], hi[2], hi[3]};
+        qlo[t] = (u32x4){lo[0], lo[1], lo[2], lo[3]};
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
     // A block is read from LDS into registers whole (K fragments and the
-    // transposed V operand) before the next block's copies are issued: a read
-    // of LDS waits for every copy issued before it, so the copies of block
-    // blk + 4 fly while the wave computes on block blk.
+    // transposed V operand) before the next block's copies are issued, so the
+    // copies of block blk + 4 fly while the wave computes on block blk.  The
+    // wave has one block of copies in flight at a time: an explicit vmcnt(0)
+    // before the LDS reads waits for exactly that block (the compiler's own
+    // tracking of direct-to-LDS copies does not insert this wait on every
+    // path through the loop).
     auto process_block = [&](int blk, bool next) {
         const int base = j0 + blk * kKeyBlock;
+        __builtin_amdgcn_s_waitcnt(kWaitVm);  // this wave's copies of block blk have landed
         // K fragments: rows col (k0) and 16 + col (k1), dims 32·t + 8·grp .. +7 (chunk 4t + grp).
         u32x4 k0[4], k1[4];
 #pragma unroll
@@ -311,11 +334,6 @@ __global__ __launch_bounds__(kThreads, 2) void xattn_split_kernel(const void *__
         for (int db = 0; db < 8; ++db) acc[db] = mfma16x16x32(va[db], pb, acc[db]);
     };
 
-    const int nblk = (j1 - j0 + kKeyBlock - 1) / kKeyBlock;
-    if (wave < nblk) {
-        issue_block(Kb, kw, wave, false);
-        issue_block(Vb, vw, wave, true);
-    }
     for (int blk = wave; blk < nblk; blk += kWaves) process_block(blk, blk + kWaves < nblk);
 
     // Row sums: each lane group summed different positions of the same head.

@@ -85,17 +85,18 @@ def test_prefill_window_beyond_prompt_equals_causal(sb):
     assert torch.equal(a, b) and torch.equal(a, c)
 
 
-@pytest.mark.parametrize("heads", [1, 2, 3])
-@pytest.mark.parametrize("B,T,Hq,Hkv,W", [
+# Heads per workgroup that divide each case's group of query heads.
+_HEADS_CASES = [(heads,) + case for case in [
     (2, 100, 6, 2, 0),        # causal, a ragged last tile
     (1, 300, 24, 8, 64),      # window shorter than the tile span
     (3, 130, 12, 2, 0),       # six query heads per KV head
-])
+] for heads in (1, 2, 3) if (case[2] // case[3]) % heads == 0]
+
+
+@pytest.mark.parametrize("heads,B,T,Hq,Hkv,W", _HEADS_CASES)
 def test_prefill_heads_per_workgroup(sb, monkeypatch, heads, B, T, Hq, Hkv, W):
     """One workgroup serving 1, 2 or 3 query heads of a KV head (forced by
-    SAMBAY_PREFILL_HEADS where the group size allows it), against the oracle."""
-    if (Hq // Hkv) % heads:
-        pytest.skip("%d heads do not divide the group of %d" % (heads, Hq // Hkv))
+    SAMBAY_PREFILL_HEADS), against the oracle."""
     monkeypatch.setenv("SAMBAY_PREFILL_HEADS", str(heads))
     x = workload.prefill_inputs(B, T, Hq, Hkv, 128, seed=7 * T + W + heads, device=DEV)
     out = sb.attn_prefill(x.q, x.k, x.v, window=W)
