@@ -72,12 +72,13 @@ def test_gmu_decode_bf16_small(sb, rows, dm, di):
     report("gmu bf16 rows=%d %dx%d" % (rows, dm, di), err(f64(Y), ref), TOL_BF16)
 
 
-@pytest.mark.parametrize("B", workload.GMU_DECODE["batches"] + (17, 20, 33, 40, 50))
+@pytest.mark.parametrize("B", workload.GMU_DECODE["batches"] + (2, 5, 17, 20, 33, 40, 50))
 def test_gmu_decode_full_width(sb, B):
     """One decode step of B sequences at d_model 3072, d_inner 6144 (all rows
-    checked); 17, 20, 33, 40 and 50 tokens end in a part-filled 16-token tile
-    (of the hidden's tiled layout up to 32 tokens, of the K-slab product's
-    token slab above)."""
+    checked); 2 and 5 tokens leave most of the 16 token columns of the
+    LDS-streaming product's tile to the repeated last token; 17, 20, 33, 40
+    and 50 tokens end in a part-filled 16-token tile (of the hidden's tiled
+    layout up to 32 tokens, of the K-slab product's token slab above)."""
     c = workload.GMU_DECODE
     g = workload.gmu_inputs(B, c["d_model"], c["d_inner"], seed=100 + B, device=DEV)
     Y = sb.gmu_forward(g.M, g.X, g.W1, g.W2)
