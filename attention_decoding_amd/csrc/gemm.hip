@@ -25,13 +25,20 @@
 //    then) so that M (or, for the residual add, h itself) is read and the
 //    output written as 16-byte vectors.  The paired form (EPI_SWIGLU) loads
 //    gate and up weight rows into one W tile and forms SiLU(g)·u there.
-//  * Measured at 8192 x 2560 x 5120 (both GMU products on 256x320 tiles,
-//    random data): ~243 us for the gate product and ~193 us for the output
-//    product (885 and 1112 TFLOP/s).  A 3-5 deep ring (BK 64 or 32), 16-wave
-//    tiles, 128x160 tiles, 4 waves of 128x128 per 256x256 tile, and reading
-//    a whole slice's fragments before its MFMAs (forced with scheduling
-//    barriers) all measured equal or slower; MFMA busy stays under half,
-//    LDS bank conflicts are zero.
+//  * Inside a stage, the fragments of 16-deep k-step ks + 1 are read into a
+//    second register set while k-step ks multiplies, one LDS read placed
+//    between two MFMAs (scheduling group barriers); only the first k-step
+//    of a stage waits for its reads.  The GMU pair at 8192 x 2560 x 5120:
+//    0.409-0.412 against 0.425-0.428 ms with the reads of each k-step ahead
+//    of its own MFMAs (same box, alternating runs).
+//  * Measured at 8192 x 2560 x 5120 before that change (both GMU products
+//    on 256x320 tiles, random data): ~243 us for the gate product and ~193
+//    us for the output product (885 and 1112 TFLOP/s).  A 3-5 deep ring (BK
+//    64 or 32), 16-wave tiles, 128x160 tiles, 4 waves of 128x128 per 256x256
+//    tile, 4 waves of 128x160 per 256x320 tile, reading a whole slice's
+//    fragments before its MFMAs (forced with scheduling barriers) and a
+//    raised wave priority around the MFMA clusters all measured equal or
+//    slower; MFMA busy stays under 70%, LDS bank conflicts are zero.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -166,23 +173,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm32_kernel(const bf16_t *__
         if (kt + NS - 1 < KT) issue(kt + NS - 1, (kt + NS - 1) % NS);
         const bf16_t *sA = lds[slot];
         const bf16_t *sB = lds[slot] + BM * BK;
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            u32x4 fa[FM], fb[FN];
+        // Fragments of k-step ks + 1 are read while k-step ks multiplies (two
+        // register sets), one read between two MFMAs.
+        u32x4 fa[2][FM], fb[2][FN];
+        auto read_frags = [&](int ks, int b) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int r = wm * TM + 32 * i + l32;
-                fa[i] = *reinterpret_cast<const u32x4 *>(&sA[r * BK + 8 * swz<BK>(r, 2 * ks + half)]);
+                fa[b][i] = *reinterpret_cast<const u32x4 *>(&sA[r * BK + 8 * swz<BK>(r, 2 * ks + half)]);
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int r = wn * TN + 32 * j + l32;
-                fb[j] = *reinterpret_cast<const u32x4 *>(&sB[r * BK + 8 * swz<BK>(BM + r, 2 * ks + half)]);
+                fb[b][j] = *reinterpret_cast<const u32x4 *>(&sB[r * BK + 8 * swz<BK>(BM + r, 2 * ks + half)]);
             }
+        };
+        read_frags(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int b = ks & 1;
+            if (ks + 1 < BK / 16) read_frags(ks + 1, b ^ 1);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[b][i], fb[b][j], acc[i][j]);
+            if (ks + 1 < BK / 16) {
+                constexpr int NR = FM + FN, NM = FM * FN;
+#pragma unroll
+                for (int q = 0; q < (NR < NM ? NR : NM); ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                }
+                if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM > NR ? NM - NR : 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
