@@ -1171,8 +1171,10 @@ hipError_t launch4(const SkinnyArgs &a, const SkinnyPlan &p, float *partials, hi
     // CU instead.  That was measured at 32 tokens (122 registers against
     // 185, its 512 workgroups in one round instead of two; 34.9 -> ~30.5 us
     // per 100.7 MB launch), where the slab product has since taken over;
-    // here it serves 2-16 tokens (one token tile, fewer registers still),
-    // where the choice was kept without a separate measurement.
+    // here it serves 2-16 tokens (one token tile).  Measured there too: the
+    // 16-layer complete step at 4 / 8 / 16 tokens (2,048 cached positions)
+    // 1.122 / 1.205 / 1.434 ms against 1.142 / 1.232 / 1.472 ms with the
+    // chunks in flight and one workgroup per CU of the other products.
     constexpr int U0 = 20 / (RT + TB * (XLO ? 2 : 1)) < 1 ? 1 : 20 / (RT + TB * (XLO ? 2 : 1));
     constexpr int U = DUAL ? 1 : U0;
     constexpr int MINB = DUAL ? 2 : 1;
