@@ -189,6 +189,29 @@ def test_xattn_full_sampled_sequences(sb):
     torch.cuda.empty_cache()
 
 
+def test_xattn_cache_past_2_31_elements(sb):
+    """64 sequences at 34816 cached positions: the K and V caches hold 2.28 G
+    elements each (9.1 GB together), so the last sequences' rows sit past
+    2^31 elements; the plain and the lengths path against the oracle on the
+    first and the last two sequences."""
+    B, Hq, Hkv, D, L = 64, 24, 8, 128, 34816
+    assert B * Hkv * L * D > 2 ** 31
+    x = workload.xattn_inputs(B, Hq, Hkv, D, L, seed=12, device=DEV)
+    out = sb.xattn_decode(x.q, x.K, x.V)
+    lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    lens[B - 1] = L - 1000
+    out_l = sb.xattn_decode(x.q, x.K, x.V, lens=lens)
+    torch.cuda.synchronize()
+    for b in (0, B - 2, B - 1):
+        ref = oracle.xattn(cpu(x.q[b:b + 1]), cpu(x.K[b:b + 1]), cpu(x.V[b:b + 1]))
+        report("xattn 64 x 34816 seq %d" % b, err(f64(out[b:b + 1]), ref), TOL_BF16)
+        n = int(lens[b])
+        ref_l = oracle.xattn_varlen(cpu(x.q[b:b + 1]), cpu(x.K[b:b + 1]), cpu(x.V[b:b + 1]), [n])
+        report("xattn lengths 64 x 34816 seq %d (%d positions)" % (b, n), err(f64(out_l[b:b + 1]), ref_l), TOL_BF16)
+    del x, out, out_l
+    torch.cuda.empty_cache()
+
+
 # -------------------------------------------------------- cross-decoder
 
 def _step_inputs(B, Hq, Hkv, L, d_inner, n_layers, seed, first="xattn", D=128):
